@@ -1,0 +1,145 @@
+/*
+ * hysparse.h -- C ABI of the HySparse / HySparse2 attention hot path on MI355X (gfx950).
+ *
+ * Sources (web pages) cited below:
+ *   [P1] "HySparse2: Hybrid Sparse Attention with Two-Level KV Sharing", reading notes,
+ *        qqtang-code.github.io.
+ *   [P2] "HySparse hybrid sparse attention (part 1): full attention as the oracle",
+ *        pinghaoyang.com.cn.
+ *   [P4] "HySparse: A Hybrid Sparse Attention Architecture with Oracle Token Selection and KV
+ *        Cache Sharing", papercache.org summary of arXiv:2602.03560.
+ *   [P5] "HySparse2: Hybrid Sparse Attention with Two-Level KV Sharing", picx.dev summary.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE memory owned by the caller (e.g. torch tensors).  The
+ *     library never allocates, frees or synchronizes; every call enqueues its kernels on
+ *     `stream` (a hipStream_t, NULL = the default stream) and returns.  Device faults surface at
+ *     the caller's next synchronization.
+ *   - Layouts are contiguous, head_dim fastest:
+ *       Q, Q', O : [B, q_len, Hq, d]        K, V, K', V' : [B, kv_len, Hkv, d]
+ *       LSE      : [B, Hq, q_len] fp32 (natural log)
+ *     Query row j sits at absolute position t = q_offset + j and sees keys 0..t (causal).
+ *     Query head h reads KV head u = h / g, g = Hq / Hkv.
+ *   - Arguments are validated on the host before anything is enqueued.  An invalid call returns
+ *     HS_ERR_INVALID_ARG or HS_ERR_UNSUPPORTED, enqueues nothing and leaves every output
+ *     untouched; hs_last_error() then describes the problem.  A failed launch returns HS_ERR_HIP.
+ *   - Outputs are fully overwritten (padding included).  The library keeps no state between
+ *     calls: the caller keeps K, V and the index sets alive across the sparse layers that reuse
+ *     them [P2 engineering constraint 6: producer/consumer lifetime].
+ *   - Workspace: every call takes a caller-owned device scratch buffer of at least
+ *     hs_workspace_size(...) bytes (16-byte aligned); a smaller one returns HS_ERR_WORKSPACE.
+ *   - Supported: head_dim in {64, 128}; g = Hq/Hkv integral; in_dtype bf16 or fp32; out_dtype
+ *     bf16 or fp32.  Index-set selection (hs_oracle_topk, hs_block_score_topk) needs g in
+ *     {4, 8, 16}.
+ */
+#ifndef HYSPARSE_H
+#define HYSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARG = -1,
+  HS_ERR_UNSUPPORTED = -2,
+  HS_ERR_WORKSPACE = -3,
+  HS_ERR_HIP = -4
+} hs_status;
+
+typedef enum { HS_BF16 = 0, HS_F32 = 1 } hs_dtype;
+
+typedef enum { HS_IDX_TOKEN = 0, HS_IDX_BLOCK = 1 } hs_index_kind;
+
+typedef enum {
+  HS_OP_FULL_ATTN = 0,   /* p0, p1 unused */
+  HS_OP_ORACLE_TOPK = 1, /* p0 = k_global, p1 = window */
+  HS_OP_BLOCK_TOPK = 2,  /* p0 = block, p1 = n_blocks */
+  HS_OP_SPARSE_ATTN = 3  /* p0 = number of keys per index set (token cap, or n_blocks*block);
+                            p1 = SWA window (0: no SWA branch) */
+} hs_op;
+
+typedef struct {
+  int32_t batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim;
+  int64_t q_offset;   /* absolute position of query row 0; -1 means kv_len - q_len */
+  hs_dtype in_dtype;  /* element type of Q, K, V (and K', V') */
+  hs_dtype out_dtype; /* element type of O */
+} hs_attn_desc;
+
+/* Sliding-window branch of a HySparse sparse layer: the layer's own local keys and values and
+ * the two gate logits per query head [P2 "Same query, two memories" and "Two sigmoid gates";
+ * P4 section 3.3]. */
+typedef struct {
+  const void* k_local;      /* [B, kv_len, Hkv, d], in_dtype; position-indexed */
+  const void* v_local;      /* [B, kv_len, Hkv, d], in_dtype */
+  const float* gate_logits; /* [B, q_len, Hq, 2] fp32: (zG, zL); sigmoid applied inside */
+  int32_t window;           /* w >= 1: positions max(0, t-w+1) .. t */
+} hs_swa_branch;
+
+/* Full causal GQA attention, the full-attention layer of a hybrid block:
+ *   a_{t,i} = q_t.k_i / sqrt(d),  O_t = sum_{i<=t} softmax_i(a) v_i,  LSE_t = ln sum_{i<=t} e^a
+ * [P2 "Extracting block scores from exact attention", attention equations; P4 section 3.2].
+ * q, k, v: in_dtype.  o: [B, q_len, Hq, d] out_dtype.  lse: [B, Hq, q_len] fp32, required (the
+ * index-selection calls normalize logits with it). */
+hs_status hs_full_attn_fwd(const hs_attn_desc* desc, const void* q, const void* k, const void* v,
+                           void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Token-level oracle index of HySparse2 [P1 section 4.2 changes 1 and 2; P5 "KV Reuse (Inner
+ * Level)"].  Per (b, t, u): score s_i = max over the group's heads h of exp(a^h_{t,i} - LSE^h_t)
+ * (the group maximum of [P2 "GQA: the group shares one index set"] applied to tokens); the set is
+ * the forced window {max(0,t-w+1)..t} plus the k_global best candidates among 0..t-w ranked by
+ * (score desc, position asc).  Exact: no candidate is dropped by an approximation.
+ * lse: output of hs_full_attn_fwd.  idx: [B, q_len, Hkv, k_global + window] int32, ascending,
+ * padded with -1.  count: [B, q_len, Hkv] int32 = min(t+1, k_global + window). */
+hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k, const float* lse,
+                         int32_t k_global, int32_t window, int32_t* idx, int32_t* count, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Block-level oracle index of HySparse [P2 "Extracting block scores from exact attention",
+ * block-score and TopK equations; P2 "GQA: the group shares one index set"; P4 section 3.2 and
+ * Algorithm 1 with the exp its line 14 omits].  Per (b, t, u): S_r = max over heads h and keys
+ * i in [rB, min(rB+B-1, t)] of exp(a^h_{t,i} - LSE^h_t), for the causal blocks r <= t/B; the
+ * n_blocks best by (S desc, r asc).  blk_idx: [B, q_len, Hkv, n_blocks] int32 ascending, -1
+ * padded; count: [B, q_len, Hkv] = min(n_blocks, t/B + 1). */
+hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const void* k,
+                              const float* lse, int32_t block, int32_t n_blocks,
+                              int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Sparse layer over the full layer's K, V and index set, with the layer's own queries q
+ * [P2 "Cross-layer KV cache reuse", gather equations; P2 "Same query, two memories";
+ * P4 section 3.3].
+ *   kind == HS_IDX_TOKEN: idx [B, q_len, Hkv, idx_cap] token positions (ascending or not), the
+ *     first count[b,j,u] entries valid; attention over exactly those keys.
+ *   kind == HS_IDX_BLOCK: idx [B, q_len, Hkv, idx_cap] block ids, count valid; attention over
+ *     the keys of those blocks (size `block`), masked causally inside a block that crosses t
+ *     [P2 engineering constraint 4].
+ *   swa != NULL (HySparse): adds the sliding-window branch over swa->k_local/v_local and returns
+ *     sigmoid(zG) * o_glob + sigmoid(zL) * o_loc.  swa == NULL (HySparse2): returns o_glob.
+ * Entries must lie in 0..t (tokens) or 0..t/block (blocks); entries outside are masked out.
+ * o: [B, q_len, Hq, d] out_dtype.  lse_opt (nullable): [B, Hq, q_len] LSE of the global branch. */
+hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const void* k_full,
+                                const void* v_full, hs_index_kind kind, const int32_t* idx,
+                                const int32_t* count, int32_t idx_cap, int32_t block,
+                                const hs_swa_branch* swa, void* o, float* lse_opt, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Bytes of workspace the call `op` needs for `desc` (p0, p1 as documented on hs_op).  Returns 0
+ * for an invalid description (hs_last_error() says why). */
+size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t p1);
+
+const char* hs_status_string(hs_status s);
+
+/* Thread-local description of the last non-OK return on this thread ("" if none). */
+const char* hs_last_error(void);
+
+/* Library version string. */
+const char* hs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -2,17 +2,14 @@
 
 The compute lives in the HIP library ``libhysparse.so`` (C ABI in include/hysparse.h).  The
 binding in ``oracle_top_kv_amd.hs`` only marshals torch tensors into pointers and sizes; it is
-loaded lazily so that ``oracle_top_kv_amd.inputs`` can be used without the GPU library.
+imported lazily so that ``oracle_top_kv_amd.inputs`` can be used without the GPU library.
 """
+import importlib
 
-__all__ = ["hs", "inputs"]
+__all__ = ["hs", "inputs", "costs"]
 
 
 def __getattr__(name):
-    if name == "hs":
-        from . import hs as _hs
-        return _hs
-    if name == "inputs":
-        from . import inputs as _inputs
-        return _inputs
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

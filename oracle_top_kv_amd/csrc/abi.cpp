@@ -1,0 +1,420 @@
+// abi.cpp -- the C ABI (include/hysparse.h): host-side validation, workspace layout and the
+// choice of launch geometry.  No kernel is enqueued before every argument has been checked.
+#include "../../include/hysparse.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "hs_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hs_status fail(hs_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hs_status ok() {
+  g_err[0] = 0;
+  return HS_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Resolved shape of a call.
+struct Shape {
+  int B, Tq, Tk, Hq, Hkv, D, g;
+  long long q_off;
+  bool in_f32, out_f32;
+};
+
+hs_status check_desc(const hs_attn_desc* d, Shape* s) {
+  if (!d) return fail(HS_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1 || d->q_len < 1 || d->kv_len < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(HS_ERR_INVALID_ARG, "batch, q_len, kv_len and head counts must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(HS_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                d->n_q_heads, d->n_kv_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(HS_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if ((d->in_dtype != HS_BF16 && d->in_dtype != HS_F32) ||
+      (d->out_dtype != HS_BF16 && d->out_dtype != HS_F32))
+    return fail(HS_ERR_INVALID_ARG, "unknown dtype");
+  long long q_off = d->q_offset == -1 ? (long long)d->kv_len - d->q_len : d->q_offset;
+  if (q_off < 0 || q_off + d->q_len > d->kv_len)
+    return fail(HS_ERR_INVALID_ARG, "q_offset %lld with q_len %d does not fit kv_len %d", q_off,
+                d->q_len, d->kv_len);
+  const int g = d->n_q_heads / d->n_kv_heads;
+  if (g > 16)
+    return fail(HS_ERR_UNSUPPORTED, "GQA group of %d query heads per KV head (at most 16)", g);
+  // 32-bit position arithmetic inside the kernels
+  if ((long long)d->kv_len > (1LL << 30))
+    return fail(HS_ERR_UNSUPPORTED, "kv_len %d too large", d->kv_len);
+  s->B = d->batch;
+  s->Tq = d->q_len;
+  s->Tk = d->kv_len;
+  s->Hq = d->n_q_heads;
+  s->Hkv = d->n_kv_heads;
+  s->D = d->head_dim;
+  s->g = g;
+  s->q_off = q_off;
+  s->in_f32 = d->in_dtype == HS_F32;
+  s->out_f32 = d->out_dtype == HS_F32;
+  return HS_OK;
+}
+
+// ---- row-attention geometry ----------------------------------------------------------------
+constexpr int kStepKeys = 32;
+constexpr int kTargetWorkgroups = 2048;
+
+struct RaGeom {
+  int q_per_set, sets_per_bu, n_sets, n_split, steps_per_split;
+};
+
+RaGeom ra_geom(const Shape& s, bool per_query, long long max_keys, int min_steps_per_split) {
+  RaGeom g;
+  g.q_per_set = per_query ? 1 : (16 / s.g > 0 ? 16 / s.g : 1);
+  g.sets_per_bu = (s.Tq + g.q_per_set - 1) / g.q_per_set;
+  g.n_sets = s.B * s.Hkv * g.sets_per_bu;
+  const long long steps = (max_keys + kStepKeys - 1) / kStepKeys;
+  long long want = (kTargetWorkgroups + g.n_sets - 1) / g.n_sets;
+  long long most = (steps + min_steps_per_split - 1) / min_steps_per_split;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  g.steps_per_split = (int)((steps + want - 1) / want);
+  if (g.steps_per_split < 1) g.steps_per_split = 1;
+  g.n_split = (int)((steps + g.steps_per_split - 1) / g.steps_per_split);
+  if (g.n_split < 1) g.n_split = 1;
+  return g;
+}
+
+size_t partial_bytes(const RaGeom& g, int D) {
+  const size_t rows = (size_t)g.n_split * g.n_sets * 16;
+  return align_up(rows * 4, 256) + align_up(rows * 8, 256) + align_up(rows * 4 * D, 256);
+}
+
+void carve_partials(void* base, const RaGeom& g, int D, float** m, double** l, float** o) {
+  const size_t rows = (size_t)g.n_split * g.n_sets * 16;
+  char* p = (char*)base;
+  *m = (float*)p;
+  p += align_up(rows * 4, 256);
+  *l = (double*)p;
+  p += align_up(rows * 8, 256);
+  *o = (float*)p;
+}
+
+hs::RowAttnParams ra_params(const Shape& s, const RaGeom& g) {
+  hs::RowAttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = s.B;
+  p.Tq = s.Tq;
+  p.Tk = s.Tk;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.g;
+  p.q_off = s.q_off;
+  p.q_per_set = g.q_per_set;
+  p.sets_per_bu = g.sets_per_bu;
+  p.n_split = g.n_split;
+  p.steps_per_split = g.steps_per_split;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  p.out_f32 = s.out_f32;
+  return p;
+}
+
+hs::CombineParams combine_params(const Shape& s, const RaGeom& g, void* o, float* lse) {
+  hs::CombineParams c;
+  memset(&c, 0, sizeof(c));
+  c.B = s.B;
+  c.Tq = s.Tq;
+  c.Hq = s.Hq;
+  c.Hkv = s.Hkv;
+  c.g = s.g;
+  c.q_per_set = g.q_per_set;
+  c.sets_per_bu = g.sets_per_bu;
+  c.o = o;
+  c.lse = lse;
+  c.out_f32 = s.out_f32;
+  return c;
+}
+
+hs_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(HS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ---- full attention ------------------------------------------------------------------------
+size_t full_attn_ws(const Shape& s) {
+  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8);
+  return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+}
+
+// ---- token top-k ---------------------------------------------------------------------------
+struct TkGeom {
+  int q_per_set, sets_per_bu, n_split, keys_per_split;
+  size_t rows;
+};
+
+TkGeom tk_geom(const Shape& s) {
+  TkGeom t;
+  t.q_per_set = 16 / s.g;
+  t.sets_per_bu = (s.Tq + t.q_per_set - 1) / t.q_per_set;
+  const long long n_sets = (long long)s.B * s.Hkv * t.sets_per_bu;
+  long long want = (kTargetWorkgroups + n_sets - 1) / n_sets;
+  const long long most = (s.Tk + 255) / 256;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  long long kps = (s.Tk + want - 1) / want;
+  kps = (kps + 63) / 64 * 64;
+  t.keys_per_split = (int)kps;
+  t.n_split = (int)((s.Tk + kps - 1) / kps);
+  t.rows = (size_t)s.B * s.Tq * s.Hkv;
+  return t;
+}
+
+size_t tk_ws(const Shape& s, const TkGeom& t) {
+  return align_up(t.rows * (size_t)s.Tk * 4, 256) + align_up(3 * t.rows * 2048 * 4, 256) +
+         align_up(t.rows * (size_t)t.n_split * 2 * 4, 256);
+}
+
+// ---- sparse attention ----------------------------------------------------------------------
+struct SparseGeom {
+  RaGeom glob, loc;
+  bool combine;
+};
+
+SparseGeom sparse_geom(const Shape& s, long long keys_per_set, int window) {
+  SparseGeom g;
+  g.glob = ra_geom(s, true, keys_per_set, 4);
+  g.loc = ra_geom(s, true, window > 0 ? window : 1, 4);
+  g.combine = window > 0 || g.glob.n_split > 1;
+  return g;
+}
+
+size_t sparse_ws(const Shape& s, const SparseGeom& g, int window) {
+  if (!g.combine) return 0;
+  size_t b = partial_bytes(g.glob, s.D);
+  if (window > 0) b += partial_bytes(g.loc, s.D);
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hs_version(void) { return "hysparse-gfx950 0.1"; }
+
+const char* hs_last_error(void) { return g_err; }
+
+const char* hs_status_string(hs_status s) {
+  switch (s) {
+    case HS_OK: return "ok";
+    case HS_ERR_INVALID_ARG: return "invalid argument";
+    case HS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HS_ERR_WORKSPACE: return "workspace too small";
+    case HS_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t p1) {
+  Shape s;
+  if (check_desc(desc, &s) != HS_OK) return 0;
+  switch (op) {
+    case HS_OP_FULL_ATTN: return full_attn_ws(s);
+    case HS_OP_ORACLE_TOPK: {
+      if (s.g != 4 && s.g != 8 && s.g != 16) return 0;
+      return tk_ws(s, tk_geom(s));
+    }
+    case HS_OP_BLOCK_TOPK: return 0;
+    case HS_OP_SPARSE_ATTN: {
+      if (p0 < 1 || p1 < 0) return 0;
+      return sparse_ws(s, sparse_geom(s, p0, p1), p1);
+    }
+  }
+  fail(HS_ERR_INVALID_ARG, "unknown op %d", (int)op);
+  return 0;
+}
+
+hs_status hs_full_attn_fwd(const hs_attn_desc* desc, const void* q, const void* k, const void* v,
+                           void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  if (!q || !k || !v || !o || !lse) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8);
+  const size_t need = g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hs::RowAttnParams p = ra_params(s, g);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.final_direct = g.n_split == 1;
+  if (!p.final_direct) carve_partials(ws, g, s.D, &p.part_m, &p.part_l, &p.part_o);
+  hipStream_t hst = (hipStream_t)stream;
+  hipError_t e = hs::launch_row_attn(p, s.D, s.in_f32, hs::SRC_RANGE, hst);
+  if (e != hipSuccess) return hip_status(e, "full attention kernel");
+  if (!p.final_direct) {
+    hs::CombineParams c = combine_params(s, g, o, lse);
+    c.n_branch = 1;
+    c.m[0] = p.part_m;
+    c.l[0] = p.part_l;
+    c.po[0] = p.part_o;
+    c.n_split[0] = g.n_split;
+    e = hs::launch_combine(c, s.D, hst);
+    if (e != hipSuccess) return hip_status(e, "combine kernel");
+  }
+  return ok();
+}
+
+hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k, const float* lse,
+                         int32_t k_global, int32_t window, int32_t* idx, int32_t* count, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  if (!q || !k || !lse || !idx || !count) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (k_global < 0 || window < 0) return fail(HS_ERR_INVALID_ARG, "k_global and window must be >= 0");
+  if ((long long)k_global + window < 1) return fail(HS_ERR_INVALID_ARG, "k_global + window must be >= 1");
+  if (s.g != 4 && s.g != 8 && s.g != 16)
+    return fail(HS_ERR_UNSUPPORTED, "token selection needs a GQA group of 4, 8 or 16 (got %d)", s.g);
+  const TkGeom t = tk_geom(s);
+  const size_t need = tk_ws(s, t);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hs::TopkDecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.lse = lse;
+  p.B = s.B;
+  p.Tq = s.Tq;
+  p.Tk = s.Tk;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.g;
+  p.q_off = s.q_off;
+  p.k_global = k_global;
+  p.window = window;
+  p.q_per_set = t.q_per_set;
+  p.sets_per_bu = t.sets_per_bu;
+  p.n_split = t.n_split;
+  p.keys_per_split = t.keys_per_split;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  char* w = (char*)ws;
+  p.keys = (uint32_t*)w;
+  w += align_up(t.rows * (size_t)s.Tk * 4, 256);
+  p.hist = (uint32_t*)w;
+  w += align_up(3 * t.rows * 2048 * 4, 256);
+  p.counts = (uint32_t*)w;
+  p.idx = idx;
+  p.cnt = count;
+  p.cap = k_global + window;
+  return hip_status(hs::launch_topk_decode(p, s.D, s.in_f32, (hipStream_t)stream),
+                    "token top-k kernels");
+}
+
+hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const void* k,
+                              const float* lse, int32_t block, int32_t n_blocks,
+                              int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
+                              void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  (void)q; (void)k; (void)lse; (void)block; (void)n_blocks; (void)blk_idx; (void)count;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return fail(HS_ERR_UNSUPPORTED, "block score top-k not built yet");
+}
+
+hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const void* k_full,
+                                const void* v_full, hs_index_kind kind, const int32_t* idx,
+                                const int32_t* count, int32_t idx_cap, int32_t block,
+                                const hs_swa_branch* swa, void* o, float* lse_opt, void* ws,
+                                size_t ws_bytes, void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  if (!q || !k_full || !v_full || !idx || !count || !o)
+    return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (kind != HS_IDX_TOKEN && kind != HS_IDX_BLOCK) return fail(HS_ERR_INVALID_ARG, "unknown index kind");
+  if (idx_cap < 1) return fail(HS_ERR_INVALID_ARG, "idx_cap must be >= 1");
+  if (kind == HS_IDX_BLOCK && block < 1) return fail(HS_ERR_INVALID_ARG, "block must be >= 1");
+  const long long keys = kind == HS_IDX_TOKEN ? idx_cap : (long long)idx_cap * block;
+  if (keys > (1LL << 30)) return fail(HS_ERR_UNSUPPORTED, "index set too large");
+  int window = 0;
+  if (swa) {
+    if (!swa->k_local || !swa->v_local || !swa->gate_logits)
+      return fail(HS_ERR_INVALID_ARG, "NULL pointer in the sliding-window branch");
+    if (swa->window < 1) return fail(HS_ERR_INVALID_ARG, "sliding window must be >= 1");
+    window = swa->window;
+  }
+  const SparseGeom g = sparse_geom(s, keys, window);
+  const size_t need = sparse_ws(s, g, window);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hipStream_t hst = (hipStream_t)stream;
+
+  hs::RowAttnParams pg = ra_params(s, g.glob);
+  pg.q = q;
+  pg.k = k_full;
+  pg.v = v_full;
+  pg.idx = idx;
+  pg.cnt = count;
+  pg.idx_cap = idx_cap;
+  pg.block = block;
+  pg.o = o;
+  pg.lse = lse_opt;
+  pg.final_direct = !g.combine;
+  char* w = (char*)ws;
+  if (g.combine) {
+    carve_partials(w, g.glob, s.D, &pg.part_m, &pg.part_l, &pg.part_o);
+    w += partial_bytes(g.glob, s.D);
+  }
+  hipError_t e = hs::launch_row_attn(pg, s.D, s.in_f32,
+                                     kind == HS_IDX_TOKEN ? hs::SRC_TOKEN : hs::SRC_BLOCK, hst);
+  if (e != hipSuccess) return hip_status(e, "sparse attention kernel");
+  hs::RowAttnParams pl;
+  if (window > 0) {
+    pl = ra_params(s, g.loc);
+    pl.q = q;
+    pl.k = swa->k_local;
+    pl.v = swa->v_local;
+    pl.window = window;
+    pl.final_direct = 0;
+    carve_partials(w, g.loc, s.D, &pl.part_m, &pl.part_l, &pl.part_o);
+    e = hs::launch_row_attn(pl, s.D, s.in_f32, hs::SRC_RANGE, hst);
+    if (e != hipSuccess) return hip_status(e, "sliding-window kernel");
+  }
+  if (g.combine) {
+    hs::CombineParams c = combine_params(s, g.glob, o, lse_opt);
+    c.n_branch = window > 0 ? 2 : 1;
+    c.m[0] = pg.part_m;
+    c.l[0] = pg.part_l;
+    c.po[0] = pg.part_o;
+    c.n_split[0] = g.glob.n_split;
+    if (window > 0) {
+      c.m[1] = pl.part_m;
+      c.l[1] = pl.part_l;
+      c.po[1] = pl.part_o;
+      c.n_split[1] = g.loc.n_split;
+      c.gate = swa->gate_logits;
+    }
+    e = hs::launch_combine(c, s.D, hst);
+    if (e != hipSuccess) return hip_status(e, "combine kernel");
+  }
+  return ok();
+}
+
+}  // extern "C"

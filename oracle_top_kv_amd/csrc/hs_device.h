@@ -1,0 +1,91 @@
+// hs_device.h -- device-side building blocks for gfx950 (CDNA4): MFMA operand types, LDS
+// transpose reads, bf16 conversion, order-preserving float keys and wave reductions.
+//
+// MFMA lane layouts used throughout (wave64, l = lane id):
+//   v_mfma_f32_16x16x32_bf16  A[16x32]: lane l holds row l%16, k = 8*(l/16) .. +7
+//                             B[32x16]: lane l holds col l%16, k = 8*(l/16) .. +7
+//                             C[16x16]: lane l holds col l%16, rows 4*(l/16) .. +3
+//   v_mfma_f32_16x16x4_f32    A: row l%16, k = l/16;  B: col l%16, k = l/16;  C as above.
+// ds_read_b64_tr_b16 (per 16-lane group): lane r supplies the address of a 4-element row R_r;
+// lane i receives { R_{i/4 + 4e}[i%4] : e = 0..3 }.  With lane r pointing at
+// tile[kb + r/4][c0 + 4*(r%4)] of a row-major [key][d] tile, lane i receives
+// tile[kb + e][c0 + i], e = 0..3: four consecutive keys of one column, which is the MFMA operand
+// layout for a contraction over keys.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.6931471805599453;
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read of four 16-bit elements (see the layout note above).
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)(p)));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(const s16x4& lo, const s16x4& hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// float -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
+  typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+  u16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; i++) v[i] = f2bf(x[i]);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key; -0 < +0 is fine here).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// max / sum over the 4 lanes {n, n+16, n+32, n+48} (one MFMA row spread over 4 lane groups)
+__device__ __forceinline__ float max4groups(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  return fmaxf(v, shfl_xor_f(v, 32));
+}
+__device__ __forceinline__ float sum4groups(float v) {
+  v += shfl_xor_f(v, 16);
+  return v + shfl_xor_f(v, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Kahan-compensated accumulation (s, c): s + c carries the sum.
+__device__ __forceinline__ void kahan_add(float& s, float& c, float x) {
+  const float y = x - c;
+  const float t = s + y;
+  c = (t - s) - y;
+  s = t;
+}
+
+}  // namespace hs

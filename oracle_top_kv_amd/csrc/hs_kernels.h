@@ -1,0 +1,85 @@
+// hs_kernels.h -- launch interface between the C ABI layer (abi.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+// Where the keys of one row-set come from.
+enum KeySrc : int {
+  SRC_RANGE = 0,  // contiguous positions lo..hi (full attention, sliding window)
+  SRC_TOKEN = 1,  // token positions from an index list
+  SRC_BLOCK = 2   // whole blocks of `block` positions from a block-id list
+};
+
+// One launch of the row-attention kernel.  A row-set is a group of at most 16 (query, head)
+// rows that share one KV head and one key list; its rows are packed in the MFMA M dimension.
+struct RowAttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;  // list modes: [B, Tq, Hkv, idx_cap]
+  const int32_t* cnt;  // list modes: [B, Tq, Hkv]
+  int idx_cap, block;
+  int window;  // range mode: > 0 restricts each row to positions t-window+1 .. t
+  int B, Tq, Tk, Hq, Hkv, g;
+  long long q_off;
+  int q_per_set;    // queries per row-set (range mode may pack several; list modes: 1)
+  int sets_per_bu;  // row-sets per (b, u) = ceil(Tq / q_per_set)
+  int n_split;      // splits of the key list per row-set (grid.x)
+  int steps_per_split;  // 32-key steps per split
+  float scale_log2;     // log2(e) / sqrt(d)
+  // final output (when final_direct) or partials (otherwise)
+  void* o;
+  float* lse;
+  int out_f32;
+  int final_direct;
+  float* part_m;   // [n_split][n_sets][16]
+  double* part_l;  // [n_split][n_sets][16]
+  float* part_o;   // [n_split][n_sets][16][D]
+};
+
+// Merge of split partials (one or two branches) into O and LSE; with two branches the sigmoid
+// gates combine them.
+struct CombineParams {
+  const float* m[2];
+  const double* l[2];
+  const float* po[2];
+  int n_split[2];
+  int n_branch;
+  const float* gate;  // [B, Tq, Hq, 2] (two branches)
+  int B, Tq, Hq, Hkv, g;
+  int q_per_set, sets_per_bu;
+  void* o;
+  float* lse;  // nullable; LSE of branch 0
+  int out_f32;
+};
+
+hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
+                           hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
+
+// ---- token top-k for row groups of at most 16 (query, head) rows (decode) ----------------
+struct TopkDecodeParams {
+  const void* q;
+  const void* k;
+  const float* lse;
+  int B, Tq, Tk, Hq, Hkv, g;
+  long long q_off;
+  int k_global, window;
+  int q_per_set, sets_per_bu;   // query rows packed per score workgroup (q_per_set * g <= 16)
+  int n_split, keys_per_split;  // key chunk per workgroup (multiple of 64)
+  float scale_log2;
+  // workspace
+  uint32_t* keys;    // [rows][Tk]   rows = B * Tq * Hkv
+  uint32_t* hist;    // [3][rows][2048]
+  uint32_t* counts;  // [rows][n_split][2]
+  // outputs
+  int32_t* idx;  // [B, Tq, Hkv, cap]
+  int32_t* cnt;  // [B, Tq, Hkv]
+  int cap;
+};
+hipError_t launch_topk_decode(const TopkDecodeParams& p, int head_dim, bool in_f32,
+                              hipStream_t stream);
+
+}  // namespace hs

@@ -1,0 +1,205 @@
+"""Thin ctypes binding of libhysparse.so (C ABI: include/hysparse.h).
+
+Argument marshalling only: shapes and dtypes are read off torch tensors, outputs and workspace are
+allocated with torch on the tensors' device, and the call is enqueued on torch's current stream.
+Every step of the computation runs in the library's HIP kernels; there is no fallback.  Loading
+fails loudly when the library has not been built.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhysparse.so")
+
+HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE, HS_ERR_HIP = 0, -1, -2, -3, -4
+HS_BF16, HS_F32 = 0, 1
+HS_IDX_TOKEN, HS_IDX_BLOCK = 0, 1
+HS_OP_FULL_ATTN, HS_OP_ORACLE_TOPK, HS_OP_BLOCK_TOPK, HS_OP_SPARSE_ATTN = 0, 1, 2, 3
+
+EXPORTS = ["hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk", "hs_sparse_attn_gather",
+           "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("q_offset", ctypes.c_int64),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+
+
+class SwaBranch(ctypes.Structure):
+    _fields_ = [("k_local", ctypes.c_void_p), ("v_local", ctypes.c_void_p),
+                ("gate_logits", ctypes.c_void_p), ("window", ctypes.c_int32)]
+
+
+class HsError(RuntimeError):
+    def __init__(self, status, what, detail):
+        super().__init__(f"{what}: status {status} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        pd = ctypes.POINTER(AttnDesc)
+        L.hs_full_attn_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.hs_oracle_topk.argtypes = [pd, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.hs_block_score_topk.argtypes = [pd, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.hs_sparse_attn_gather.argtypes = [pd, vp, vp, vp, ctypes.c_int, vp, vp, i32, i32,
+                                            ctypes.POINTER(SwaBranch), vp, vp, vp, sz, vp]
+        L.hs_workspace_size.argtypes = [ctypes.c_int, pd, i32, i32]
+        L.hs_workspace_size.restype = sz
+        L.hs_status_string.restype = ctypes.c_char_p
+        L.hs_status_string.argtypes = [ctypes.c_int]
+        L.hs_last_error.restype = ctypes.c_char_p
+        L.hs_version.restype = ctypes.c_char_p
+        for f in ("hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk",
+                  "hs_sparse_attn_gather"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != HS_OK:
+        raise HsError(status, what, lib().hs_last_error().decode())
+
+
+def _dtype_code(t):
+    if t == torch.bfloat16:
+        return HS_BF16
+    if t == torch.float32:
+        return HS_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, device, dtype=None, shape=None):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def make_desc(q, k, q_offset=None, out_dtype=None):
+    B, Tq, Hq, d = q.shape
+    Bk, Tk, Hkv, dk = k.shape
+    if B != Bk or d != dk:
+        raise ValueError("q and k shapes disagree")
+    out = q.dtype if out_dtype is None else out_dtype
+    return AttnDesc(B, Tq, Tk, Hq, Hkv, d, -1 if q_offset is None else int(q_offset),
+                    _dtype_code(q.dtype), _dtype_code(out))
+
+
+def workspace(op, desc, p0=0, p1=0, device=None):
+    n = lib().hs_workspace_size(op, ctypes.byref(desc), int(p0), int(p1))
+    if n == 0:
+        return None, 0
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def full_attn_fwd(q, k, v, q_offset=None, out_dtype=None):
+    """Full causal GQA attention. Returns (o [B,Tq,Hq,d], lse fp32 [B,Hq,Tq])."""
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dev, dtype=q.dtype)
+    desc = make_desc(q, k, q_offset, out_dtype)
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
+    ws, n = workspace(HS_OP_FULL_ATTN, desc, device=dev)
+    _check(lib().hs_full_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(lse), _ptr(ws), n, _stream(dev)), "hs_full_attn_fwd")
+    return o, lse
+
+
+def oracle_topk(q, k, lse, k_global, window, q_offset=None):
+    """Forced window plus top-k_global tokens. Returns (idx int32 [B,Tq,Hkv,k+w], count)."""
+    dev = q.device
+    _need(q, "q", dev)
+    _need(k, "k", dev, dtype=q.dtype)
+    _need(lse, "lse", dev, dtype=torch.float32, shape=(q.shape[0], q.shape[2], q.shape[1]))
+    desc = make_desc(q, k, q_offset)
+    B, Tq, Hkv = q.shape[0], q.shape[1], k.shape[2]
+    idx = torch.empty((B, Tq, Hkv, k_global + window), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
+    ws, n = workspace(HS_OP_ORACLE_TOPK, desc, k_global, window, device=dev)
+    _check(lib().hs_oracle_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), int(k_global),
+                                int(window), _ptr(idx), _ptr(cnt), _ptr(ws), n, _stream(dev)),
+           "hs_oracle_topk")
+    return idx, cnt
+
+
+def block_score_topk(q, k, lse, block, n_blocks, q_offset=None):
+    """Top n_blocks causal blocks. Returns (blk_idx int32 [B,Tq,Hkv,n_blocks], count)."""
+    dev = q.device
+    _need(q, "q", dev)
+    _need(k, "k", dev, dtype=q.dtype)
+    _need(lse, "lse", dev, dtype=torch.float32, shape=(q.shape[0], q.shape[2], q.shape[1]))
+    desc = make_desc(q, k, q_offset)
+    B, Tq, Hkv = q.shape[0], q.shape[1], k.shape[2]
+    idx = torch.empty((B, Tq, Hkv, n_blocks), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
+    ws, n = workspace(HS_OP_BLOCK_TOPK, desc, block, n_blocks, device=dev)
+    _check(lib().hs_block_score_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), int(block),
+                                     int(n_blocks), _ptr(idx), _ptr(cnt), _ptr(ws), n,
+                                     _stream(dev)), "hs_block_score_topk")
+    return idx, cnt
+
+
+def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_offset=None,
+                       out_dtype=None, want_lse=False):
+    """Sparse layer over the shared K, V and index set with the layer's own q.
+    swa = (k_local, v_local, gate_logits fp32 [B,Tq,Hq,2], window) adds the gated sliding-window
+    branch.  Returns (o, lse or None)."""
+    dev = q.device
+    _need(q, "q", dev)
+    _need(k, "k", dev, dtype=q.dtype)
+    _need(v, "v", dev, dtype=q.dtype)
+    _need(idx, "idx", dev, dtype=torch.int32)
+    _need(count, "count", dev, dtype=torch.int32, shape=idx.shape[:3])
+    desc = make_desc(q, k, q_offset, out_dtype)
+    kind_code = HS_IDX_TOKEN if kind == "token" else HS_IDX_BLOCK
+    cap = idx.shape[-1]
+    keys = cap if kind_code == HS_IDX_TOKEN else cap * block
+    sw = None
+    window = 0
+    keep = []
+    if swa is not None:
+        kl, vl, gate, window = swa
+        _need(kl, "k_local", dev, dtype=q.dtype, shape=k.shape)
+        _need(vl, "v_local", dev, dtype=q.dtype, shape=k.shape)
+        _need(gate, "gate_logits", dev, dtype=torch.float32, shape=tuple(q.shape[:3]) + (2,))
+        sw = SwaBranch(kl.data_ptr(), vl.data_ptr(), gate.data_ptr(), int(window))
+        keep = [kl, vl, gate]
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    lse = (torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
+           if want_lse else None)
+    ws, n = workspace(HS_OP_SPARSE_ATTN, desc, keys, window, device=dev)
+    _check(lib().hs_sparse_attn_gather(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), kind_code,
+                                       _ptr(idx), _ptr(count), int(cap), int(block),
+                                       ctypes.byref(sw) if sw is not None else None, _ptr(o),
+                                       _ptr(lse), _ptr(ws), n, _stream(dev)),
+           "hs_sparse_attn_gather")
+    del keep
+    return o, lse

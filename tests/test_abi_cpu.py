@@ -1,0 +1,108 @@
+"""The C ABI library without a GPU: it loads, exports every symbol include/hysparse.h declares,
+and rejects invalid calls on the host before anything is enqueued (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle_top_kv_amd import hs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hysparse.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = hs.lib()
+    names = declared_functions()
+    assert set(names) == set(hs.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.hs_version().decode().startswith("hysparse")
+
+
+def desc(**kw):
+    base = dict(batch=1, q_len=1, kv_len=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                q_offset=-1, in_dtype=hs.HS_BF16, out_dtype=hs.HS_BF16)
+    base.update(kw)
+    return hs.AttnDesc(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), hs.HS_ERR_UNSUPPORTED),
+    (dict(n_q_heads=6, n_kv_heads=4), hs.HS_ERR_INVALID_ARG),
+    (dict(q_len=0), hs.HS_ERR_INVALID_ARG),
+    (dict(q_offset=1024), hs.HS_ERR_INVALID_ARG),
+    (dict(q_len=4, q_offset=1021), hs.HS_ERR_INVALID_ARG),
+    (dict(n_q_heads=64, n_kv_heads=1), hs.HS_ERR_UNSUPPORTED),
+    (dict(in_dtype=7), hs.HS_ERR_INVALID_ARG),
+])
+def test_full_attn_rejects_bad_descriptions(kw, status):
+    d = desc(**kw)
+    rc = hs.lib().hs_full_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                  None)
+    assert rc == status
+    assert hs.lib().hs_last_error().decode()
+
+
+def test_null_pointers_rejected():
+    d = desc()
+    assert hs.lib().hs_full_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == \
+        hs.HS_ERR_INVALID_ARG
+    assert hs.lib().hs_full_attn_fwd(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                    None) == hs.HS_ERR_INVALID_ARG
+    assert hs.lib().hs_full_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, 0,
+                                    None) == hs.HS_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_is_reported():
+    d = desc(batch=8, kv_len=32768, n_q_heads=32, n_kv_heads=8)
+    need = hs.lib().hs_workspace_size(hs.HS_OP_FULL_ATTN, ctypes.byref(d), 0, 0)
+    assert need > 0
+    rc = hs.lib().hs_full_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                  None)
+    assert rc == hs.HS_ERR_WORKSPACE
+    need_tk = hs.lib().hs_workspace_size(hs.HS_OP_ORACLE_TOPK, ctypes.byref(d), 1024, 128)
+    rc = hs.lib().hs_oracle_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 1024, 128, FAKE, FAKE, FAKE,
+                                 need_tk - 1, None)
+    assert rc == hs.HS_ERR_WORKSPACE
+
+
+def test_topk_argument_checks():
+    d = desc()
+    L = hs.lib()
+    assert L.hs_oracle_topk(ctypes.byref(d), FAKE, FAKE, FAKE, -1, 128, FAKE, FAKE, FAKE, 1 << 40,
+                            None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_oracle_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, 1 << 40,
+                            None) == hs.HS_ERR_INVALID_ARG
+    d3 = desc(n_q_heads=6, n_kv_heads=2)  # g = 3
+    assert L.hs_oracle_topk(ctypes.byref(d3), FAKE, FAKE, FAKE, 16, 4, FAKE, FAKE, FAKE, 1 << 40,
+                            None) == hs.HS_ERR_UNSUPPORTED
+
+
+def test_sparse_argument_checks():
+    d = desc()
+    L = hs.lib()
+    assert L.hs_sparse_attn_gather(ctypes.byref(d), FAKE, FAKE, FAKE, 5, FAKE, FAKE, 8, 64, None,
+                                   FAKE, None, FAKE, 1 << 40, None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_sparse_attn_gather(ctypes.byref(d), FAKE, FAKE, FAKE, hs.HS_IDX_BLOCK, FAKE, FAKE,
+                                   16, 0, None, FAKE, None, FAKE, 1 << 40, None) == \
+        hs.HS_ERR_INVALID_ARG
+    bad = hs.SwaBranch(0x1000, 0x1000, 0x1000, 0)
+    assert L.hs_sparse_attn_gather(ctypes.byref(d), FAKE, FAKE, FAKE, hs.HS_IDX_BLOCK, FAKE, FAKE,
+                                   16, 64, ctypes.byref(bad), FAKE, None, FAKE, 1 << 40,
+                                   None) == hs.HS_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    L = hs.lib()
+    for s in (0, -1, -2, -3, -4):
+        assert L.hs_status_string(s).decode()

@@ -1,0 +1,182 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded inputs.
+
+Sizes here are ones the oracle finishes in seconds while still spanning many tiles, several
+splits and ragged tails.  Index sets follow the near-tie rule of parity_utils; outputs are
+compared with identical (oracle) index sets.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle_top_kv_amd.inputs import Workload, make_inputs, to_numpy_f32
+from parity_utils import (TOL_BF16, TOL_F32, check_block_sets, check_token_sets, max_abs)
+
+pytestmark = pytest.mark.gpu
+
+
+def hs():
+    from oracle_top_kv_amd import hs as _hs
+    return _hs
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(x):
+    if isinstance(x, list):
+        return [t.cuda() for t in x]
+    return x.cuda() if torch.is_tensor(x) else x
+
+
+# ---- full attention ----------------------------------------------------------------------
+
+FULL_CASES = [
+    # name, workload
+    ("tiny_f32_prefill", Workload("tiny", 1, 512, 512, 4, 1, 64, "f32", seed=101)),
+    ("decode_bf16_g4", Workload("dec", 2, 1, 5000, 32, 8, 128, "bf16", needles=4, seed=11)),
+    ("decode_bf16_g16", Workload("dec16", 2, 1, 3001, 64, 4, 128, "bf16", seed=12)),
+    ("short_block_bf16_d64", Workload("sb", 2, 3, 777, 8, 2, 64, "bf16", seed=13)),
+    ("prefill_bf16_g4_ragged", Workload("pf", 1, 200, 1100, 8, 2, 128, "bf16", seed=14)),
+]
+
+
+@pytest.mark.parametrize("name,wl", FULL_CASES, ids=[c[0] for c in FULL_CASES])
+def test_full_attn_matches_oracle(name, wl):
+    say(f"[full_attn] {name} {wl}")
+    x = make_inputs(wl)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = hs().full_attn_fwd(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.full_attention(to_numpy_f32(x["q"]), to_numpy_f32(x["k"]),
+                                           to_numpy_f32(x["v"]))
+    tol = TOL_F32 if wl.dtype == "f32" else TOL_BF16
+    eo = max_abs(o.cpu().numpy(), o_ref)
+    el = max_abs(lse.cpu().numpy(), lse_ref)
+    say(f"  max|dO| = {eo:.3e}  max|dLSE| = {el:.3e}")
+    assert eo <= tol
+    assert el <= 2e-6
+    # bf16 output path: within max(1e-2, one bf16 ulp) of the rounded oracle
+    if wl.dtype == "bf16":
+        ob, _ = hs().full_attn_fwd(q, k, v)
+        ref_b = torch.from_numpy(o_ref).to(torch.bfloat16).float().numpy()
+        diff = np.abs(ob.float().cpu().numpy() - ref_b)
+        ulp = np.abs(ref_b) * 2.0 ** -7
+        assert (diff <= np.maximum(TOL_BF16, ulp)).all()
+
+
+# ---- token top-k -------------------------------------------------------------------------
+
+TOPK_CASES = [
+    ("tiny_f32_prefill", Workload("tiny", 1, 512, 512, 4, 1, 64, "f32", k_global=64, window=16,
+                                  seed=101)),
+    ("decode_g4_needles", Workload("dec", 2, 1, 9000, 32, 8, 128, "bf16", k_global=1024,
+                                   window=128, needles=16, seed=21)),
+    ("decode_g16_short", Workload("dec16", 1, 1, 1500, 64, 4, 128, "bf16", k_global=1024,
+                                  window=128, seed=22)),
+    ("decode_g8_two_queries", Workload("g8", 2, 2, 4000, 16, 2, 64, "bf16", k_global=100,
+                                       window=20, seed=23)),
+    ("prefill_g4_cross_cap", Workload("pfx", 1, 48, 1200, 8, 2, 128, "bf16", k_global=1024,
+                                      window=128, seed=24)),
+]
+
+
+@pytest.mark.parametrize("name,wl", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_oracle_topk_matches_oracle(name, wl):
+    say(f"[topk] {name} {wl}")
+    x = make_inputs(wl)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    _, lse = hs().full_attn_fwd(q, k, v, out_dtype=torch.float32)
+    idx, cnt = hs().oracle_topk(q, k, lse, wl.k_global, wl.window)
+    torch.cuda.synchronize()
+    qn, kn = to_numpy_f32(x["q"]), to_numpy_f32(x["k"])
+    _, lse_ref = oracle.full_attention(qn, kn, to_numpy_f32(x["v"]))
+    oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
+    excused = check_token_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, qn, kn, lse_ref,
+                               wl.k_global, wl.window, wl.q_offset)
+    say(f"  near-tie differences excused: {excused}")
+    if wl.needles:
+        for b in range(wl.batch):
+            for u in range(wl.n_kv_heads):
+                sel = set(idx[b, -1, u, :cnt[b, -1, u]].cpu().tolist())
+                assert set(x["needle_pos"][b, u].tolist()) <= sel
+
+
+# ---- sparse attention over the oracle's index sets ----------------------------------------
+
+SPARSE_CASES = [
+    ("tiny_f32_token", Workload("tiny", 1, 512, 512, 4, 1, 64, "f32", k_global=64, window=16,
+                                seed=101)),
+    ("decode_g4_token", Workload("dec", 3, 1, 6000, 32, 8, 128, "bf16", needles=8, seed=31)),
+    ("decode_g16_token", Workload("d16", 2, 1, 2500, 64, 4, 128, "bf16", seed=32)),
+    ("prefill_g4_token", Workload("pf", 1, 40, 1500, 8, 2, 128, "bf16", seed=33)),
+]
+
+
+@pytest.mark.parametrize("name,wl", SPARSE_CASES, ids=[c[0] for c in SPARSE_CASES])
+def test_sparse_token_matches_oracle(name, wl):
+    say(f"[sparse token] {name} {wl}")
+    x = make_inputs(wl, n_sparse=2)
+    qn, kn, vn = (to_numpy_f32(x[n]) for n in ("q", "k", "v"))
+    oi, oc = oracle.token_topk(qn, kn, None, wl.k_global, wl.window)
+    k, v = to_dev(x["k"]), to_dev(x["v"])
+    idx = torch.from_numpy(oi).cuda()
+    cnt = torch.from_numpy(oc).cuda()
+    tol = TOL_F32 if wl.dtype == "f32" else TOL_BF16
+    for layer, qs in enumerate(x["q_sparse"]):
+        o, lse = hs().sparse_attn_gather(to_dev(qs), k, v, idx, cnt, kind="token",
+                                         out_dtype=torch.float32, want_lse=True)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.masked_attention(to_numpy_f32(qs), kn, vn, oi, oc)
+        eo, el = max_abs(o.cpu().numpy(), o_ref), max_abs(lse.cpu().numpy(), lse_ref)
+        say(f"  layer {layer}: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+        assert eo <= tol and el <= 2e-6
+
+
+def test_sparse_token_budget_covering_prefix_equals_full_attention():
+    """k + w >= t + 1: the sparse layer must reproduce full attention with the same Q'."""
+    wl = Workload("cov", 1, 64, 64, 8, 2, 128, "bf16", k_global=48, window=16, seed=34)
+    say(f"[sparse cover] {wl}")
+    x = make_inputs(wl)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    qs = to_dev(x["q_sparse"][0])
+    _, lse = hs().full_attn_fwd(q, k, v)
+    idx, cnt = hs().oracle_topk(q, k, lse, wl.k_global, wl.window)
+    o_s, _ = hs().sparse_attn_gather(qs, k, v, idx, cnt, out_dtype=torch.float32)
+    o_f, _ = hs().full_attn_fwd(qs, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert max_abs(o_s.cpu().numpy(), o_f.cpu().numpy()) <= 1e-5
+
+
+GATED_CASES = [
+    ("decode_g4", Workload("gd", 2, 1, 5000, 32, 8, 128, "bf16", block=64, n_blocks=16,
+                           window=128, seed=41)),
+    ("prefill_g4_ragged", Workload("gp", 1, 70, 900, 8, 2, 128, "bf16", block=64, n_blocks=4,
+                                   window=32, seed=42)),
+    ("tiny_f32", Workload("gt", 1, 128, 512, 4, 1, 64, "f32", block=16, n_blocks=5, window=16,
+                          seed=43)),
+]
+
+
+@pytest.mark.parametrize("name,wl", GATED_CASES, ids=[c[0] for c in GATED_CASES])
+def test_block_sparse_gated_swa_matches_oracle(name, wl):
+    say(f"[block+swa] {name} {wl}")
+    x = make_inputs(wl, block_variant=True)
+    a = {n: to_numpy_f32(x[n]) for n in ("q", "k", "v", "k_loc", "v_loc", "gate")}
+    qs = x["q_sparse"][0]
+    bi, bc = oracle.block_topk(a["q"], a["k"], None, wl.block, wl.n_blocks)
+    o_ref, _, _ = oracle.gated_block_swa(to_numpy_f32(qs), a["k"], a["v"], bi, bc, wl.block,
+                                         a["k_loc"], a["v_loc"], wl.window, a["gate"])
+    o, _ = hs().sparse_attn_gather(
+        to_dev(qs), to_dev(x["k"]), to_dev(x["v"]), torch.from_numpy(bi).cuda(),
+        torch.from_numpy(bc).cuda(), kind="block", block=wl.block,
+        swa=(to_dev(x["k_loc"]), to_dev(x["v_loc"]), to_dev(x["gate"]), wl.window),
+        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tol = TOL_F32 if wl.dtype == "f32" else TOL_BF16
+    eo = max_abs(o.cpu().numpy(), o_ref)
+    say(f"  max|dO| = {eo:.3e}")
+    assert eo <= tol
