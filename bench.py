@@ -1,0 +1,186 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = one pass of every stage of the hot path over one batch of the 7B-shaped decode
+workload (batch 8, 32768-token context, 32 query / 8 KV heads, d = 128, bf16, 16 needles per KV
+head):
+  full attention with LSE -> token oracle top-k (1024 + window 128) -> 3 token-sparse layers
+  (each with its own Q') -> block scores + top-16 blocks -> a block-sparse layer with its gated
+  sliding-window branch (own K', V').
+Inputs are generated on the GPU before timing and stay resident in HBM.
+
+Prints ONE JSON line.  `value` is the step's algorithmic HBM bytes (what the method must read: K
+and V once for full attention, K once for each scoring pass, the index-set rows of K and V for
+each sparse layer) divided by the step time.  Per-stage times come from HIP events recorded on
+the stream the library launches on.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn gathered KV GB/s + full-attn+topk prefill TFLOP/s, % of roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_7b_32k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from oracle_top_kv_amd import costs, hs
+    from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(wl, device=dev, block_variant=True)
+    q, k, v = x["q"], x["k"], x["v"]
+    qs = x["q_sparse"]
+    kl, vl, gate = x["k_loc"], x["v_loc"], x["gate"]
+    torch.cuda.synchronize()
+
+    stages = ["full_attn", "token_topk", "sparse_token", "block_topk", "sparse_block_swa"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        o, lse = hs.full_attn_fwd(q, k, v)
+        mark(1)
+        idx, cnt = hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+        mark(2)
+        for l in range(wl.n_sparse):
+            hs.sparse_attn_gather(qs[l], k, v, idx, cnt, kind="token")
+        mark(3)
+        bidx, bcnt = hs.block_score_topk(q, k, lse, wl.block, wl.n_blocks)
+        mark(4)
+        hs.sparse_attn_gather(qs[0], k, v, bidx, bcnt, kind="block", block=wl.block,
+                              swa=(kl, vl, gate, wl.window))
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, bracketed by synchronization, with per-stage events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, name in enumerate(stages)}
+
+    # algorithmic bytes per stage
+    b_full = costs.full_attn_kv_bytes(wl)                 # K and V read once
+    b_score = costs.score_k_bytes(wl)                     # K read once per scoring pass
+    b_tok = costs.token_gather_bytes(wl)                  # per sparse layer
+    b_blk = costs.block_gather_bytes(wl)                  # per block-sparse + SWA layer
+    stage_bytes = {"full_attn": b_full, "token_topk": b_score,
+                   "sparse_token": wl.n_sparse * b_tok, "block_topk": b_score,
+                   "sparse_block_swa": b_blk}
+    total_bytes = sum(stage_bytes.values())
+    value = total_bytes / (ms_step * 1e-3) / 1e9
+
+    stages_out = {}
+    for n in stages:
+        gbs = stage_bytes[n] / (stage_ms[n] * 1e-3) / 1e9
+        stages_out[n] = {"ms": round(stage_ms[n], 4), "GB_per_s": round(gbs, 1),
+                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
+    stages_out["sparse_token"]["per_layer_gathered_bytes"] = b_tok
+    dom = "full_attn"
+    achieved = stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "kv_len": wl.kv_len,
+                   "q_len": wl.q_len, "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "k_global": wl.k_global, "window": wl.window,
+                   "sparse_layers": wl.n_sparse, "block": wl.block, "n_blocks": wl.n_blocks,
+                   "needles_per_kv_head": wl.needles, "step_bytes": total_bytes},
+        "stages": stages_out,
+        "roofline": {"bound": "hbm", "kernel": "full-attention decode (row_attn_kernel + combine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, x, budget_s):
+    """The oracle, as it is, on the host cores over whole batch entries of the same workload
+    (full layer, token top-k, the sparse layers, block top-k and the gated layer), taken one batch
+    entry at a time until about `budget_s` seconds have passed; scaled to GB/s of the same
+    algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+    from oracle_top_kv_amd import costs
+
+    def host(t, b):
+        return t[b:b + 1].float().cpu().numpy()
+
+    done, t_used = 0, 0.0
+    for b in range(wl.batch):
+        q, k, v = host(x["q"], b), host(x["k"], b), host(x["v"], b)
+        qs = [host(t, b) for t in x["q_sparse"]]
+        kl, vl, gate = host(x["k_loc"], b), host(x["v_loc"], b), host(x["gate"], b)
+        t0 = time.perf_counter()
+        _, lse = oracle.full_attention(q, k, v)
+        idx, cnt = oracle.token_topk(q, k, lse, wl.k_global, wl.window)
+        for l in range(wl.n_sparse):
+            oracle.masked_attention(qs[l], k, v, idx, cnt)
+        bi, bc = oracle.block_topk(q, k, lse, wl.block, wl.n_blocks)
+        oracle.gated_block_swa(qs[0], k, v, bi, bc, wl.block, kl, vl, wl.window, gate)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= budget_s:
+            break
+    per_b = (costs.full_attn_kv_bytes(wl) + 2 * costs.score_k_bytes(wl) +
+             wl.n_sparse * costs.token_gather_bytes(wl) + costs.block_gather_bytes(wl)) / wl.batch
+    return {"value": round(done * per_b / t_used / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done} of {wl.batch} batch entries, every stage, {t_used:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -186,6 +186,46 @@ size_t tk_ws(const Shape& s, const TkGeom& t) {
          align_up(t.rows * (size_t)t.n_split * 2 * 4, 256);
 }
 
+// ---- block top-k ---------------------------------------------------------------------------
+struct BkGeom {
+  int q_per_set, sets_per_bu, n_split, blocks_per_split;
+  size_t rows;
+};
+
+BkGeom bk_geom(const Shape& s, int block, int n_blocks) {
+  BkGeom t;
+  t.q_per_set = 16 / s.g;
+  t.sets_per_bu = (s.Tq + t.q_per_set - 1) / t.q_per_set;
+  const long long n_sets = (long long)s.B * s.Hkv * t.sets_per_bu;
+  const long long nblk = (s.Tk + block - 1) / block;
+  long long want = (kTargetWorkgroups + n_sets - 1) / n_sets;
+  const long long most = (nblk + 3) / 4;
+  if (want > most) want = most;
+  const long long least = (nblk + 255) / 256;  // at most 256 blocks per workgroup
+  if (want < least) want = least;
+  if (want < 1) want = 1;
+  long long bps = (nblk + want - 1) / want;
+  t.blocks_per_split = (int)bps;
+  t.n_split = (int)((nblk + bps - 1) / bps);
+  t.rows = (size_t)s.B * s.Tq * s.Hkv;
+  return t;
+}
+
+hs_status bk_check(const Shape& s, int block, int n_blocks, BkGeom* g) {
+  if (block < 16 || block % 16) return fail(HS_ERR_UNSUPPORTED, "block %d: must be a multiple of 16", block);
+  if (n_blocks < 1 || n_blocks > 64) return fail(HS_ERR_UNSUPPORTED, "n_blocks %d: must be 1..64", n_blocks);
+  if (s.g != 4 && s.g != 8 && s.g != 16)
+    return fail(HS_ERR_UNSUPPORTED, "block selection needs a GQA group of 4, 8 or 16 (got %d)", s.g);
+  *g = bk_geom(s, block, n_blocks);
+  if ((long long)g->n_split * n_blocks > 4096)
+    return fail(HS_ERR_UNSUPPORTED, "context too long for the block merge (%d splits)", g->n_split);
+  return HS_OK;
+}
+
+size_t bk_ws(const BkGeom& g, int n_blocks) {
+  return align_up(g.rows * (size_t)g.n_split * n_blocks * 8, 256);
+}
+
 // ---- sparse attention ----------------------------------------------------------------------
 struct SparseGeom {
   RaGeom glob, loc;
@@ -235,7 +275,11 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
       if (s.g != 4 && s.g != 8 && s.g != 16) return 0;
       return tk_ws(s, tk_geom(s));
     }
-    case HS_OP_BLOCK_TOPK: return 0;
+    case HS_OP_BLOCK_TOPK: {
+      BkGeom g;
+      if (bk_check(s, p0, p1, &g) != HS_OK) return 0;
+      return bk_ws(g, p1);
+    }
     case HS_OP_SPARSE_ATTN: {
       if (p0 < 1 || p1 < 0) return 0;
       return sparse_ws(s, sparse_geom(s, p0, p1), p1);
@@ -333,9 +377,37 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
-  (void)q; (void)k; (void)lse; (void)block; (void)n_blocks; (void)blk_idx; (void)count;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return fail(HS_ERR_UNSUPPORTED, "block score top-k not built yet");
+  if (!q || !k || !lse || !blk_idx || !count) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  BkGeom g;
+  st = bk_check(s, block, n_blocks, &g);
+  if (st != HS_OK) return st;
+  const size_t need = bk_ws(g, n_blocks);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hs::BlockTopkParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.lse = lse;
+  p.B = s.B;
+  p.Tq = s.Tq;
+  p.Tk = s.Tk;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.g;
+  p.q_off = s.q_off;
+  p.block = block;
+  p.n_blocks = n_blocks;
+  p.q_per_set = g.q_per_set;
+  p.sets_per_bu = g.sets_per_bu;
+  p.n_split = g.n_split;
+  p.blocks_per_split = g.blocks_per_split;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  p.cand = (unsigned long long*)ws;
+  p.blk_idx = blk_idx;
+  p.cnt = count;
+  return hip_status(hs::launch_block_topk(p, s.D, s.in_f32, (hipStream_t)stream),
+                    "block top-k kernels");
 }
 
 hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const void* k_full,

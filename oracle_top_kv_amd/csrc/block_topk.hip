@@ -1,0 +1,196 @@
+// block_topk.hip -- HySparse block-level oracle index [P2 "Extracting block scores from exact
+// attention", block-score and TopK equations; P2 "GQA: the group shares one index set";
+// P4 section 3.2 and Algorithm 1, with the exp that its line 14 omits].
+//
+// Block score of causal block r for query row (b, t, u):
+//   S_r = max_{h in group u} max_{i in [rB, min(rB+B-1, t)]} exp(a^h_{t,i} - LSE^h_t),
+// ranked in the log2 domain as max(a * log2(e) - (LSE * log2(e) - C)) like the token scores.
+// The logits are recomputed (MFMA, S = Q K^T) rather than stored per tile, so no T x T/B score
+// matrix exists anywhere.
+//
+// Two kernels:
+//   1. per (key split, row-set): every block of the split is scored; the split's exact top-n
+//      blocks per query (n = n_blocks) are written as 64-bit keys (score key << 32 | ~block id),
+//      so larger key = better and equal scores prefer the lower block id;
+//   2. per query row: the top-n of the union of the splits' candidates (exact: the global top-n
+//      is contained in the union of per-split top-n), written in ascending block order.
+#include "hs_device.h"
+#include "hs_kernels.h"
+
+namespace hs {
+namespace {
+
+constexpr int kMaxRange = 256;  // blocks per split (per workgroup)
+
+template <int D, bool F32>
+__global__ __launch_bounds__(256) void blk_score_kernel(BlockTopkParams p) {
+  __shared__ unsigned long long bkey[4][kMaxRange];  // per query of the set, per block of the split
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rn = lane & 15, jg = lane >> 4;
+  const int split = blockIdx.x;
+  const int set = blockIdx.y;
+  const int sq = set % p.sets_per_bu;
+  const int bu = set / p.sets_per_bu;
+  const int u = bu % p.Hkv, b = bu / p.Hkv;
+  const int j0 = sq * p.q_per_set;
+  const int nq = min(p.q_per_set, p.Tq - j0);
+  const int nrows = nq * p.g;
+  const int G = p.g / 4;
+
+  const long long blk_begin = (long long)split * p.blocks_per_split;
+  const long long t_last = p.q_off + j0 + nq - 1;
+  long long blk_end = blk_begin + p.blocks_per_split;
+  if (blk_end > t_last / p.block + 1) blk_end = t_last / p.block + 1;
+  const int n_range = blk_end > blk_begin ? (int)(blk_end - blk_begin) : 0;
+  for (int i = threadIdx.x; i < 4 * kMaxRange; i += 256) (&bkey[0][0])[i] = 0ull;
+
+  constexpr int KK = F32 ? D / 4 : D / 32;
+  const bool row_ok = rn < nrows;
+  const int jq_r = row_ok ? rn / p.g : 0, hh_r = row_ok ? rn % p.g : 0;
+  bf16x8 qa[F32 ? 1 : KK];
+  float qf[F32 ? KK : 1];
+  {
+    const size_t qoff = (((size_t)b * p.Tq + j0 + jq_r) * p.Hq + u * p.g + hh_r) * D;
+    if constexpr (!F32) {
+      const uint16_t* qp = (const uint16_t*)p.q + qoff;
+#pragma unroll
+      for (int kk = 0; kk < KK; kk++) {
+        u32x4 raw = row_ok ? *(const u32x4*)(qp + 32 * kk + 8 * jg) : u32x4{0, 0, 0, 0};
+        qa[kk] = __builtin_bit_cast(bf16x8, raw);
+      }
+    } else {
+      const float* qp = (const float*)p.q + qoff + jg * KK;
+#pragma unroll
+      for (int s = 0; s < KK; s++) qf[s] = row_ok ? qp[s] : 0.f;
+    }
+  }
+  float delta[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int r = 4 * jg + e;
+    if (r < nrows) {
+      const int j = j0 + r / p.g, hh = r % p.g;
+      const double l2 = (double)p.lse[((size_t)b * p.Hq + u * p.g + hh) * p.Tq + j] * 1.4426950408889634;
+      const double C = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
+      delta[e] = (float)(l2 - C);
+    } else {
+      delta[e] = INFINITY;
+    }
+  }
+  const int jq_own = jg / G;
+  const bool owner = (jg % G) == 0 && jq_own < nq;
+  const long long t_own = p.q_off + j0 + jq_own;
+  __syncthreads();
+
+  const size_t kv_row_stride = (size_t)p.Hkv * D;
+  const size_t kv_base = ((size_t)b * p.Tk * p.Hkv + u) * D;
+  const int groups = p.block / 16;  // 16-key MFMA groups per block
+  for (int rb = wave; rb < n_range; rb += 4) {
+    const long long blk = blk_begin + rb;
+    float best = -INFINITY;  // running max for this lane's query over the block
+    for (int gi = 0; gi < groups; gi++) {
+      const long long pos = blk * p.block + 16 * gi + rn;
+      const long long pc = pos < p.Tk ? pos : 0;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!F32) {
+        const uint16_t* kp = (const uint16_t*)p.k + kv_base + (size_t)pc * kv_row_stride;
+#pragma unroll
+        for (int kk = 0; kk < KK; kk++) {
+          u32x4 raw = *(const u32x4*)(kp + 32 * kk + 8 * jg);
+          acc = mfma_bf16(qa[kk], __builtin_bit_cast(bf16x8, raw), acc);
+        }
+      } else {
+        const float* kp = (const float*)p.k + kv_base + (size_t)pc * kv_row_stride + jg * KK;
+#pragma unroll
+        for (int s = 0; s < KK; s++) acc = mfma_f32(qf[s], kp[s], acc);
+      }
+      float v = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[e], p.scale_log2, -delta[e]));
+      if (G >= 2) v = fmaxf(v, __shfl_xor(v, 16, 64));
+      if (G >= 4) v = fmaxf(v, __shfl_xor(v, 32, 64));
+      // causal: keys after this lane's query position do not count
+      if (pos > t_own || pos >= p.Tk) v = -INFINITY;
+      // max over the 16 keys of the group (lanes of one 16-lane row)
+      v = fmaxf(v, __shfl_xor(v, 1, 64));
+      v = fmaxf(v, __shfl_xor(v, 2, 64));
+      v = fmaxf(v, __shfl_xor(v, 4, 64));
+      v = fmaxf(v, __shfl_xor(v, 8, 64));
+      best = fmaxf(best, v);
+    }
+    if (owner && rn == 0 && blk <= t_own / p.block)
+      bkey[jq_own][rb] = ((unsigned long long)float_key(best) << 32) |
+                         (unsigned long long)(0xFFFFFFFFu - (uint32_t)blk);
+  }
+  __syncthreads();
+  // exact local top-n per query: rank = number of strictly larger keys (keys are distinct)
+  for (int jq = 0; jq < nq; jq++) {
+    const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
+    unsigned long long* out = p.cand + ((size_t)row * p.n_split + split) * p.n_blocks;
+    for (int c = threadIdx.x; c < n_range; c += 256) {
+      const unsigned long long kc = bkey[jq][c];
+      if (kc == 0ull) continue;
+      int rank = 0;
+      for (int o = 0; o < n_range; o++) rank += bkey[jq][o] > kc;
+      if (rank < p.n_blocks) out[rank] = kc;
+    }
+    // fill the unused slots with 0 (no candidate)
+    int valid = 0;
+    for (int c = 0; c < n_range; c++) valid += bkey[jq][c] != 0ull;
+    for (int s = valid + threadIdx.x; s < p.n_blocks; s += 256) out[s] = 0ull;
+  }
+}
+
+__global__ __launch_bounds__(256) void blk_merge_kernel(BlockTopkParams p) {
+  extern __shared__ unsigned long long cand[];  // n_split * n_blocks
+  __shared__ int sel_ids[64];
+  const int row = blockIdx.x;
+  const int j = (row / p.Hkv) % p.Tq;
+  const long long t = p.q_off + j;
+  const long long nb = t / p.block + 1;
+  const int n_take = (int)(nb < p.n_blocks ? nb : p.n_blocks);
+  const int R = p.n_split * p.n_blocks;
+  const unsigned long long* src = p.cand + (size_t)row * R;
+  for (int i = threadIdx.x; i < R; i += 256) cand[i] = src[i];
+  __syncthreads();
+  for (int c = threadIdx.x; c < R; c += 256) {
+    const unsigned long long kc = cand[c];
+    if (kc == 0ull) continue;
+    int rank = 0;
+    for (int o = 0; o < R; o++) rank += cand[o] > kc;
+    if (rank < n_take) sel_ids[rank] = (int)(0xFFFFFFFFu - (uint32_t)(kc & 0xFFFFFFFFull));
+  }
+  __syncthreads();
+  // ascending block ids
+  int32_t* out = p.blk_idx + (size_t)row * p.n_blocks;
+  for (int s = threadIdx.x; s < p.n_blocks; s += 256) {
+    if (s < n_take) {
+      const int id = sel_ids[s];
+      int pos = 0;
+      for (int o = 0; o < n_take; o++) pos += sel_ids[o] < id;
+      out[pos] = id;
+    } else {
+      out[s] = -1;
+    }
+  }
+  if (threadIdx.x == 0) p.cnt[row] = n_take;
+}
+
+template <int D, bool F32>
+hipError_t launch_blk(const BlockTopkParams& p, hipStream_t stream) {
+  blk_score_kernel<D, F32><<<dim3(p.n_split, p.B * p.Hkv * p.sets_per_bu), 256, 0, stream>>>(p);
+  const size_t rows = (size_t)p.B * p.Tq * p.Hkv;
+  const size_t smem = (size_t)p.n_split * p.n_blocks * sizeof(unsigned long long);
+  blk_merge_kernel<<<dim3((unsigned)rows), 256, smem, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_block_topk(const BlockTopkParams& p, int head_dim, bool in_f32,
+                             hipStream_t stream) {
+  if (head_dim == 128) return in_f32 ? launch_blk<128, true>(p, stream) : launch_blk<128, false>(p, stream);
+  return in_f32 ? launch_blk<64, true>(p, stream) : launch_blk<64, false>(p, stream);
+}
+
+}  // namespace hs

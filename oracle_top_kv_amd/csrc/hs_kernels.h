@@ -82,4 +82,22 @@ struct TopkDecodeParams {
 hipError_t launch_topk_decode(const TopkDecodeParams& p, int head_dim, bool in_f32,
                               hipStream_t stream);
 
+// ---- block scores + top-n blocks ----------------------------------------------------------
+struct BlockTopkParams {
+  const void* q;
+  const void* k;
+  const float* lse;
+  int B, Tq, Tk, Hq, Hkv, g;
+  long long q_off;
+  int block, n_blocks;
+  int q_per_set, sets_per_bu;
+  int n_split, blocks_per_split;
+  float scale_log2;
+  unsigned long long* cand;  // workspace [rows][n_split][n_blocks]
+  int32_t* blk_idx;          // [B, Tq, Hkv, n_blocks]
+  int32_t* cnt;              // [B, Tq, Hkv]
+};
+hipError_t launch_block_topk(const BlockTopkParams& p, int head_dim, bool in_f32,
+                             hipStream_t stream);
+
 }  // namespace hs

@@ -105,6 +105,35 @@ def test_oracle_topk_matches_oracle(name, wl):
                 assert set(x["needle_pos"][b, u].tolist()) <= sel
 
 
+# ---- block scores + top-n blocks ----------------------------------------------------------
+
+BLOCK_CASES = [
+    ("tiny_f32_b16", Workload("tb", 1, 512, 512, 4, 1, 64, "f32", block=16, n_blocks=5, seed=51)),
+    ("decode_g4_b64", Workload("bd", 2, 1, 9000, 32, 8, 128, "bf16", block=64, n_blocks=16,
+                               needles=8, seed=52)),
+    ("decode_g16_b64", Workload("bd16", 1, 1, 4100, 64, 4, 128, "bf16", block=64, n_blocks=16,
+                                seed=53)),
+    ("prefill_g8_b32", Workload("bp", 1, 37, 2000, 16, 2, 64, "bf16", block=32, n_blocks=7,
+                                seed=54)),
+]
+
+
+@pytest.mark.parametrize("name,wl", BLOCK_CASES, ids=[c[0] for c in BLOCK_CASES])
+def test_block_topk_matches_oracle(name, wl):
+    say(f"[block topk] {name} {wl}")
+    x = make_inputs(wl)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    _, lse = hs().full_attn_fwd(q, k, v)
+    bi, bc = hs().block_score_topk(q, k, lse, wl.block, wl.n_blocks)
+    torch.cuda.synchronize()
+    qn, kn = to_numpy_f32(x["q"]), to_numpy_f32(x["k"])
+    _, lse_ref = oracle.full_attention(qn, kn, to_numpy_f32(x["v"]))
+    oi, oc = oracle.block_topk(qn, kn, lse_ref, wl.block, wl.n_blocks)
+    excused = check_block_sets(bi.cpu().numpy(), bc.cpu().numpy(), oi, oc, qn, kn, lse_ref,
+                               wl.block, wl.q_offset)
+    say(f"  near-tie differences excused: {excused}")
+
+
 # ---- sparse attention over the oracle's index sets ----------------------------------------
 
 SPARSE_CASES = [
