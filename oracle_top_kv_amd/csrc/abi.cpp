@@ -1,6 +1,6 @@
 // abi.cpp -- the C ABI (include/hysparse.h): host-side validation, workspace layout and the
 // choice of launch geometry.  No kernel is enqueued before every argument has been checked.
-#include "../../include/hysparse.h"
+#include "hysparse.h"
 
 #include <hip/hip_runtime.h>
 
@@ -80,15 +80,20 @@ struct RaGeom {
   int q_per_set, sets_per_bu, n_sets, n_split, steps_per_split;
 };
 
-RaGeom ra_geom(const Shape& s, bool per_query, long long max_keys, int min_steps_per_split) {
+// Splits of each row-set's key list: enough workgroups to fill the GPU (`target`), no split
+// shorter than `min_steps` 32-key steps, none longer than `max_steps`.
+RaGeom ra_geom(const Shape& s, bool per_query, long long max_keys, int min_steps_per_split,
+               long long target = kTargetWorkgroups, long long max_steps = 1LL << 40) {
   RaGeom g;
   g.q_per_set = per_query ? 1 : (16 / s.g > 0 ? 16 / s.g : 1);
   g.sets_per_bu = (s.Tq + g.q_per_set - 1) / g.q_per_set;
   g.n_sets = s.B * s.Hkv * g.sets_per_bu;
   const long long steps = (max_keys + kStepKeys - 1) / kStepKeys;
-  long long want = (kTargetWorkgroups + g.n_sets - 1) / g.n_sets;
+  long long want = (target + g.n_sets - 1) / g.n_sets;
   long long most = (steps + min_steps_per_split - 1) / min_steps_per_split;
   if (want > most) want = most;
+  const long long least = (steps + max_steps - 1) / max_steps;
+  if (want < least) want = least;
   if (want < 1) want = 1;
   g.steps_per_split = (int)((steps + want - 1) / want);
   if (g.steps_per_split < 1) g.steps_per_split = 1;
@@ -153,14 +158,16 @@ hs_status hip_status(hipError_t e, const char* what) {
 }
 
 // ---- full attention ------------------------------------------------------------------------
+constexpr long long kResidentWorkgroups = 512;  // 256 CUs x 2 workgroups of this kernel
+
 size_t full_attn_ws(const Shape& s) {
-  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8);
+  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
   return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
 }
 
 // ---- token top-k ---------------------------------------------------------------------------
 struct TkGeom {
-  int q_per_set, sets_per_bu, n_split, keys_per_split;
+  int q_per_set, sets_per_bu, n_split, keys_per_split, sel_split, keys_per_sel;
   size_t rows;
 };
 
@@ -169,7 +176,7 @@ TkGeom tk_geom(const Shape& s) {
   t.q_per_set = 16 / s.g;
   t.sets_per_bu = (s.Tq + t.q_per_set - 1) / t.q_per_set;
   const long long n_sets = (long long)s.B * s.Hkv * t.sets_per_bu;
-  long long want = (kTargetWorkgroups + n_sets - 1) / n_sets;
+  long long want = (kResidentWorkgroups + n_sets - 1) / n_sets;  // one round of the score pass
   const long long most = (s.Tk + 255) / 256;
   if (want > most) want = most;
   if (want < 1) want = 1;
@@ -178,13 +185,39 @@ TkGeom tk_geom(const Shape& s) {
   t.keys_per_split = (int)kps;
   t.n_split = (int)((s.Tk + kps - 1) / kps);
   t.rows = (size_t)s.B * s.Tq * s.Hkv;
+  // selection passes: chunks of at least 8192 keys, enough chunks to fill the GPU
+  long long ks = 8192;
+  while (ks > 1024 && (long long)t.rows * ((s.Tk + ks - 1) / ks) < 512) ks /= 2;
+  while ((s.Tk + ks - 1) / ks > 4096) ks *= 2;
+  t.keys_per_sel = (int)ks;
+  t.sel_split = (int)((s.Tk + ks - 1) / ks);
   return t;
 }
 
-size_t tk_ws(const Shape& s, const TkGeom& t) {
-  return align_up(t.rows * (size_t)s.Tk * 4, 256) + align_up(3 * t.rows * 2048 * 4, 256) +
-         align_up(t.rows * (size_t)t.n_split * 2 * 4, 256);
+struct TkLayout {
+  size_t keys, hist, blist, above, counts, state, total;
+};
+
+TkLayout tk_layout(const Shape& s, const TkGeom& t) {
+  TkLayout L;
+  size_t o = 0;
+  L.keys = o;
+  o += align_up(t.rows * (size_t)s.Tk * 4, 256);
+  L.hist = o;  // histograms, then the boundary counters (zeroed together)
+  o += align_up((t.rows * 2048 + t.rows) * 4, 256);
+  L.blist = o;
+  o += align_up(t.rows * (size_t)s.Tk * 8, 256);
+  L.above = o;
+  o += align_up(t.rows * (size_t)t.sel_split * 4, 256);
+  L.counts = o;
+  o += align_up(t.rows * (size_t)t.sel_split * 4, 256);
+  L.state = o;
+  o += align_up(t.rows * 2 * 4, 256);
+  L.total = o;
+  return L;
 }
+
+size_t tk_ws(const Shape& s, const TkGeom& t) { return tk_layout(s, t).total; }
 
 // ---- block top-k ---------------------------------------------------------------------------
 struct BkGeom {
@@ -198,7 +231,8 @@ BkGeom bk_geom(const Shape& s, int block, int n_blocks) {
   t.sets_per_bu = (s.Tq + t.q_per_set - 1) / t.q_per_set;
   const long long n_sets = (long long)s.B * s.Hkv * t.sets_per_bu;
   const long long nblk = (s.Tk + block - 1) / block;
-  long long want = (kTargetWorkgroups + n_sets - 1) / n_sets;
+  // fewer, longer splits than the token path: the merge cost grows with splits * n_blocks
+  long long want = (kResidentWorkgroups + n_sets - 1) / n_sets;
   const long long most = (nblk + 3) / 4;
   if (want > most) want = most;
   const long long least = (nblk + 255) / 256;  // at most 256 blocks per workgroup
@@ -234,7 +268,7 @@ struct SparseGeom {
 
 SparseGeom sparse_geom(const Shape& s, long long keys_per_set, int window) {
   SparseGeom g;
-  g.glob = ra_geom(s, true, keys_per_set, 4);
+  g.glob = ra_geom(s, true, keys_per_set, 4, kTargetWorkgroups, 64);
   g.loc = ra_geom(s, true, window > 0 ? window : 1, 4);
   g.combine = window > 0 || g.glob.n_split > 1;
   return g;
@@ -295,7 +329,7 @@ hs_status hs_full_attn_fwd(const hs_attn_desc* desc, const void* q, const void* 
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
   if (!q || !k || !v || !o || !lse) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
-  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8);
+  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
   const size_t need = g.n_split > 1 ? partial_bytes(g, s.D) : 0;
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
@@ -356,13 +390,18 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
   p.sets_per_bu = t.sets_per_bu;
   p.n_split = t.n_split;
   p.keys_per_split = t.keys_per_split;
+  p.sel_split = t.sel_split;
+  p.keys_per_sel = t.keys_per_sel;
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  const TkLayout lay = tk_layout(s, t);
   char* w = (char*)ws;
-  p.keys = (uint32_t*)w;
-  w += align_up(t.rows * (size_t)s.Tk * 4, 256);
-  p.hist = (uint32_t*)w;
-  w += align_up(3 * t.rows * 2048 * 4, 256);
-  p.counts = (uint32_t*)w;
+  p.keys = (uint32_t*)(w + lay.keys);
+  p.hist = (uint32_t*)(w + lay.hist);
+  p.bcount = p.hist + t.rows * 2048;
+  p.blist = (unsigned long long*)(w + lay.blist);
+  p.above = (uint32_t*)(w + lay.above);
+  p.counts = (uint32_t*)(w + lay.counts);
+  p.state = (uint32_t*)(w + lay.state);
   p.idx = idx;
   p.cnt = count;
   p.cap = k_global + window;
@@ -466,7 +505,7 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
     pl.window = window;
     pl.final_direct = 0;
     carve_partials(w, g.loc, s.D, &pl.part_m, &pl.part_l, &pl.part_o);
-    e = hs::launch_row_attn(pl, s.D, s.in_f32, hs::SRC_RANGE, hst);
+    e = hs::launch_row_attn(pl, s.D, s.in_f32, hs::SRC_WINDOW, hst);
     if (e != hipSuccess) return hip_status(e, "sliding-window kernel");
   }
   if (g.combine) {

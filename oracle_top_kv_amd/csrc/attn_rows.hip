@@ -20,6 +20,8 @@
 //   O^T += V^T P^T : B = P^T is exactly the S^T output (no shuffle), A = V^T read from a
 //                 row-major LDS tile with ds_read_b64_tr_b16.
 // Every per-row statistic (running max, sum) lives in the 4 lanes of that row.
+#include <type_traits>
+
 #include "hs_device.h"
 #include "hs_kernels.h"
 
@@ -28,6 +30,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kStep = 32;  // keys per wave step
+constexpr int kMaxListEntries = 2048;  // list-mode entries staged per workgroup (64 steps)
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -51,7 +54,7 @@ template <int SRC>
 __device__ __forceinline__ int entry_pos(const RowAttnParams& p, int e, int L, long long lo,
                                          long long t_last, const int32_t* list) {
   if (e >= L) return -1;
-  if (SRC == SRC_RANGE) return (int)(lo + e);
+  if (SRC == SRC_RANGE || SRC == SRC_WINDOW) return (int)(lo + e);
   if (SRC == SRC_TOKEN) {
     const int x = list[e];
     return (x >= 0 && x <= t_last) ? x : -1;
@@ -66,18 +69,21 @@ template <int D, bool F32, int SRC>
 __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
   using Cfg = RaCfg<D, F32>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::kSmem];
-  __shared__ int pos_lds[kWaves][kStep];
+  __shared__ int pos_all[kMaxListEntries];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rn = lane & 15;   // MFMA row / column index of this lane
   const int jg = lane >> 4;   // lane group 0..3
-  const int split = blockIdx.x;
-  const int set = blockIdx.y;
-  const int sq = set % p.sets_per_bu;
-  const int bu = set / p.sets_per_bu;
-  const int u = bu % p.Hkv;
-  const int b = bu / p.Hkv;
+  // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
+  // workgroups reading the same positions of the Hkv interleaved heads run together (whole
+  // [Hkv, d] rows of K and V are then consumed close in time).
+  const int u = blockIdx.x % p.Hkv;
+  const int split = (blockIdx.x / p.Hkv) % p.n_split;
+  const int bq = blockIdx.x / (p.Hkv * p.n_split);
+  const int sq = bq % p.sets_per_bu;
+  const int b = bq / p.sets_per_bu;
+  const int set = (b * p.Hkv + u) * p.sets_per_bu + sq;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);
   const int nrows = nq * p.g;
@@ -87,8 +93,8 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
   int L;
   long long lo = 0;
   const int32_t* list = nullptr;
-  if (SRC == SRC_RANGE) {
-    lo = (p.window > 0) ? (t_first - p.window + 1 > 0 ? t_first - p.window + 1 : 0) : 0;
+  if (SRC == SRC_RANGE || SRC == SRC_WINDOW) {
+    lo = (SRC == SRC_WINDOW) ? (t_first - p.window + 1 > 0 ? t_first - p.window + 1 : 0) : 0;
     L = (int)(t_last - lo + 1);
   } else {
     const long long row = ((long long)b * p.Tq + j0) * p.Hkv + u;
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
   const int hh = row_ok ? rn % p.g : 0;
   const long long t_row = p.q_off + j0 + jq;
   const int h = u * p.g + hh;
-  const long long lo_row = (SRC == SRC_RANGE && p.window > 0) ? t_row - p.window + 1 : 0;
+  const long long lo_row = (SRC == SRC_WINDOW) ? t_row - p.window + 1 : 0;
 
   const size_t kv_row_stride = (size_t)p.Hkv * D;  // elements between consecutive positions
   const size_t kv_base = ((size_t)b * p.Tk * p.Hkv + u) * D;
@@ -140,61 +146,91 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
   const int step_begin = split * p.steps_per_split;
   const int step_end = min(step_begin + p.steps_per_split, n_steps);
   unsigned char* vtile = smem + wave * Cfg::kVTileBytes;
-  int* pos_w = pos_lds[wave];
 
-  for (int step = step_begin + wave; step < step_end; step += kWaves) {
-    if (lane < kStep) pos_w[lane] = entry_pos<SRC>(p, step * kStep + lane, L, lo, t_last, list);
-    wave_lds_sync();
+  // Positions of this split's key-list entries.  List modes stage them in LDS once (so the
+  // K/V loads of the next step can be issued without waiting on an index load); range modes
+  // compute them.
+  constexpr bool kList = (SRC == SRC_TOKEN || SRC == SRC_BLOCK);
+  if constexpr (kList) {
+    const int n_e = (step_end - step_begin) * kStep;
+    for (int i = threadIdx.x; i < n_e; i += 256)
+      pos_all[i] = entry_pos<SRC>(p, step_begin * kStep + i, L, lo, t_last, list);
+    __syncthreads();
+  }
+  auto pos_of = [&](int step, int i) -> int {
+    if constexpr (kList) {
+      return pos_all[(step - step_begin) * kStep + i];
+    } else {
+      const int e = step * kStep + i;
+      return e < L ? (int)(lo + e) : -1;
+    }
+  };
 
-    // K operand for the two 16-key blocks (straight from HBM)
-    const int pk0 = pos_w[rn], pk1 = pos_w[16 + rn];
-    f32x4 sacc[2];
+  // Software pipeline: the K and V rows of a wave's next step are requested before the current
+  // step is computed.  K goes to registers in MFMA operand layout, V to registers and then to
+  // this wave's LDS tile.
+  constexpr int VL = Cfg::kVLoads;
+  using KReg = typename std::conditional<F32, float, u32x4>::type;
+  auto load_step = [&](int step, KReg (&k0)[KK], KReg (&k1)[KK], u32x4 (&vr)[VL]) {
+    const int pk0 = pos_of(step, rn), pk1 = pos_of(step, 16 + rn);
     if constexpr (!F32) {
-      const uint16_t* kp0 = (const uint16_t*)p.k + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride;
-      const uint16_t* kp1 = (const uint16_t*)p.k + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride;
-      u32x4 ka0[KK], ka1[KK];
+      const uint16_t* kp0 = (const uint16_t*)p.k + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + 8 * jg;
+      const uint16_t* kp1 = (const uint16_t*)p.k + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + 8 * jg;
 #pragma unroll
       for (int kk = 0; kk < KK; kk++) {
-        ka0[kk] = *(const u32x4*)(kp0 + 32 * kk + 8 * jg);
-        ka1[kk] = *(const u32x4*)(kp1 + 32 * kk + 8 * jg);
+        k0[kk] = *(const u32x4*)(kp0 + 32 * kk);
+        k1[kk] = *(const u32x4*)(kp1 + 32 * kk);
       }
-      // V rows -> LDS tile (row-major [key][d], padded rows)
+    } else {
+      const float* kp0 = (const float*)p.k + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + jg * KK;
+      const float* kp1 = (const float*)p.k + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + jg * KK;
 #pragma unroll
-      for (int n = 0; n < Cfg::kVLoads; n++) {
-        const int c = n * 64 + lane;
-        const int e = c / Cfg::kChunksPerRow, qc = c % Cfg::kChunksPerRow;
-        const int pv = pos_w[e];
-        const uint16_t* vp = (const uint16_t*)p.v + kv_base + (size_t)(pv < 0 ? 0 : pv) * kv_row_stride + qc * 8;
-        *(u32x4*)((uint16_t*)vtile + e * Cfg::kVStride + qc * 8) = *(const u32x4*)vp;
+      for (int s2 = 0; s2 < KK; s2++) {
+        k0[s2] = kp0[s2];
+        k1[s2] = kp1[s2];
       }
-      sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int n = 0; n < VL; n++) {
+      const int c = n * 64 + lane;
+      const int e = c / Cfg::kChunksPerRow, qc = c % Cfg::kChunksPerRow;
+      const int pv = pos_of(step, e);
+      const unsigned char* vp = (const unsigned char*)p.v +
+          (kv_base + (size_t)(pv < 0 ? 0 : pv) * kv_row_stride) * Cfg::kElem + qc * 16;
+      vr[n] = ld_stream(vp);
+    }
+  };
+
+  KReg ka0[KK], ka1[KK];
+  u32x4 va[VL];
+  int step = step_begin + wave;
+  if (step < step_end) load_step(step, ka0, ka1, va);
+  for (; step < step_end; step += kWaves) {
+    KReg kn0[KK], kn1[KK];
+    u32x4 vn[VL];
+    if (step + kWaves < step_end) load_step(step + kWaves, kn0, kn1, vn);
+
+    // V rows of this step -> LDS tile (row-major [key][d], padded rows)
+#pragma unroll
+    for (int n = 0; n < VL; n++) {
+      const int c = n * 64 + lane;
+      const int e = c / Cfg::kChunksPerRow, qc = c % Cfg::kChunksPerRow;
+      *(u32x4*)(vtile + (e * Cfg::kVStride) * Cfg::kElem + qc * 16) = va[n];
+    }
+
+    // S^T = K Q^T for the two 16-key blocks
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (!F32) {
 #pragma unroll
       for (int kk = 0; kk < KK; kk++) {
         sacc[0] = mfma_bf16(__builtin_bit_cast(bf16x8, ka0[kk]), qb[kk], sacc[0]);
         sacc[1] = mfma_bf16(__builtin_bit_cast(bf16x8, ka1[kk]), qb[kk], sacc[1]);
       }
     } else {
-      const float* kp0 = (const float*)p.k + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + jg * KK;
-      const float* kp1 = (const float*)p.k + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + jg * KK;
-      float ka0[KK], ka1[KK];
 #pragma unroll
-      for (int s = 0; s < KK; s++) {
-        ka0[s] = kp0[s];
-        ka1[s] = kp1[s];
-      }
-#pragma unroll
-      for (int n = 0; n < Cfg::kVLoads; n++) {
-        const int c = n * 64 + lane;
-        const int e = c / Cfg::kChunksPerRow, qc = c % Cfg::kChunksPerRow;
-        const int pv = pos_w[e];
-        const float* vp = (const float*)p.v + kv_base + (size_t)(pv < 0 ? 0 : pv) * kv_row_stride + qc * 4;
-        *(u32x4*)((float*)vtile + e * Cfg::kVStride + qc * 4) = *(const u32x4*)vp;
-      }
-      sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KK; s++) {
-        sacc[0] = mfma_f32(ka0[s], qf[s], sacc[0]);
-        sacc[1] = mfma_f32(ka1[s], qf[s], sacc[1]);
+      for (int s2 = 0; s2 < KK; s2++) {
+        sacc[0] = mfma_f32(ka0[s2], qf[s2], sacc[0]);
+        sacc[1] = mfma_f32(ka1[s2], qf[s2], sacc[1]);
       }
     }
 
@@ -205,7 +241,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
     for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const int pos = pos_w[16 * kb + 4 * jg + e];
+        const int pos = pos_of(step, 16 * kb + 4 * jg + e);
         const bool ok = row_ok && pos >= 0 && pos <= t_row && pos >= lo_row;
         const float x = ok ? sacc[kb][e] * p.scale_log2 : -INFINITY;
         sv[kb][e] = x;
@@ -242,8 +278,8 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
       for (int db = 0; db < D / 16; db++) {
         const uint16_t* a0 = vt + (4 * jg + (rn >> 2)) * Cfg::kVStride + 16 * db + 4 * (rn & 3);
         const uint16_t* a1 = a0 + 16 * Cfg::kVStride;
-        const bf16x8 va = join_tr(lds_read_tr16(a0), lds_read_tr16(a1));
-        oacc[db] = mfma_bf16(va, pb, oacc[db]);
+        const bf16x8 vop = join_tr(lds_read_tr16(a0), lds_read_tr16(a1));
+        oacc[db] = mfma_bf16(vop, pb, oacc[db]);
       }
     } else {
       const float* vt = (const float*)vtile;
@@ -253,11 +289,19 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
           for (int e = 0; e < 4; e++) {
-            const float va = vt[(16 * kb + 4 * jg + e) * Cfg::kVStride + 16 * db + rn];
-            oacc[db] = mfma_f32(va, pv8[4 * kb + e], oacc[db]);
+            const float vop = vt[(16 * kb + 4 * jg + e) * Cfg::kVStride + 16 * db + rn];
+            oacc[db] = mfma_f32(vop, pv8[4 * kb + e], oacc[db]);
           }
     }
     wave_lds_sync();  // tile reads done before the next step overwrites it
+
+#pragma unroll
+    for (int kk = 0; kk < KK; kk++) {
+      ka0[kk] = kn0[kk];
+      ka1[kk] = kn1[kk];
+    }
+#pragma unroll
+    for (int n = 0; n < VL; n++) va[n] = vn[n];
   }
 
   // ---- merge the 4 waves of this workgroup ----
@@ -319,7 +363,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
       p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] =
           (Ls > 0.0) ? (float)(((double)M + log2(Ls)) * kLn2) : -INFINITY;
   } else {
-    const size_t n_sets = gridDim.y;
+    const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu;
     const size_t prow = ((size_t)split * n_sets + set) * 16 + r;
     if (c0 == 0) {
       p.part_m[prow] = M;
@@ -331,72 +375,93 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
 }
 
 // ---- split / branch combine ---------------------------------------------------------------
+// One workgroup per (row-set, row).  Threads = SP split lanes x D/4 column chunks; each thread
+// folds every SP-th split of its 4 columns with weights 2^(m_s - M), then the split lanes are
+// summed in LDS.  Row sums are combined in fp64.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  constexpr int CPT = D / 16;
-  const int set = blockIdx.x;
-  const size_t n_sets = gridDim.x;
-  const int r = threadIdx.x >> 4;
-  const int c0 = (threadIdx.x & 15) * CPT;
+  constexpr int NC = D / 4;         // column chunks of 4
+  constexpr int SP = 256 / NC;      // split lanes
+  __shared__ float red[SP][D];
+  __shared__ double redl[SP];
+  const int set = blockIdx.x / 16;
+  const int r = blockIdx.x % 16;
+  const size_t n_sets = gridDim.x / 16;
   const int sq = set % p.sets_per_bu;
   const int bu = set / p.sets_per_bu;
   const int u = bu % p.Hkv;
   const int b = bu / p.Hkv;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);
-  if (r >= nq * p.g) return;
+  if (r >= nq * p.g) return;  // whole workgroup leaves together
   const int jr = j0 + r / p.g;
   const int hr = u * p.g + r % p.g;
+  const int c = threadIdx.x % NC;
+  const int sl = threadIdx.x / NC;
 
-  double out[CPT];
+  float out[4] = {0.f, 0.f, 0.f, 0.f};
   double lse0 = -INFINITY;
-#pragma unroll
-  for (int c = 0; c < CPT; c++) out[c] = 0.0;
   for (int br = 0; br < p.n_branch; br++) {
+    const int ns = p.n_split[br];
+    const float* m = p.m[br];
+    // row maximum over splits (every thread, redundantly; ns is small)
     float M = -INFINITY;
-    for (int s = 0; s < p.n_split[br]; s++) M = fmaxf(M, p.m[br][((size_t)s * n_sets + set) * 16 + r]);
-    double Ls = 0.0, acc[CPT];
-#pragma unroll
-    for (int c = 0; c < CPT; c++) acc[c] = 0.0;
+    for (int s = 0; s < ns; s++) M = fmaxf(M, m[((size_t)s * n_sets + set) * 16 + r]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    double lacc = 0.0;
     if (M != -INFINITY) {
-      for (int s = 0; s < p.n_split[br]; s++) {
+      for (int s = sl; s < ns; s += SP) {
         const size_t prow = ((size_t)s * n_sets + set) * 16 + r;
-        const float ms = p.m[br][prow];
+        const float ms = m[prow];
         if (ms == -INFINITY) continue;
-        const double f = exp2((double)ms - (double)M);
-        Ls += f * p.l[br][prow];
-#pragma unroll
-        for (int c = 0; c < CPT; c++) acc[c] += f * (double)p.po[br][prow * D + c0 + c];
+        const float f = fast_exp2(ms - M);
+        const f32x4 o4 = *(const f32x4*)(p.po[br] + prow * D + 4 * c);
+        acc += f * o4;
+        if (c == 0) lacc += exp2((double)ms - (double)M) * p.l[br][prow];
       }
     }
-    double wgt = 1.0;
-    if (p.n_branch == 2) {
-      const float z = p.gate[(((size_t)b * p.Tq + jr) * p.Hq + hr) * 2 + br];
-      wgt = 1.0 / (1.0 + exp(-(double)z));
-    }
-    const double inv = Ls > 0.0 ? wgt / Ls : 0.0;
+    *(f32x4*)&red[sl][4 * c] = acc;
+    if (c == 0) redl[sl] = lacc;
+    __syncthreads();
+    if (sl == 0) {
+      double L = 0.0;
+      for (int q = 0; q < SP; q++) L += redl[q];
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < SP; q++)
 #pragma unroll
-    for (int c = 0; c < CPT; c++) out[c] += acc[c] * inv;
-    if (br == 0) lse0 = Ls > 0.0 ? ((double)M + log2(Ls)) * kLn2 : -INFINITY;
+        for (int e = 0; e < 4; e++) sum[e] += red[q][4 * c + e];
+      float wgt = 1.f;
+      if (p.n_branch == 2) {
+        const float z = p.gate[(((size_t)b * p.Tq + jr) * p.Hq + hr) * 2 + br];
+        wgt = (float)(1.0 / (1.0 + exp(-(double)z)));
+      }
+      const float inv = L > 0.0 ? (float)(wgt / L) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; e++) out[e] += sum[e] * inv;
+      if (br == 0 && c == 0) lse0 = L > 0.0 ? ((double)M + log2(L)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
   }
-  const size_t ooff = (((size_t)b * p.Tq + jr) * p.Hq + hr) * D + c0;
+  if (sl != 0) return;
+  const size_t ooff = (((size_t)b * p.Tq + jr) * p.Hq + hr) * D + 4 * c;
   if (p.out_f32) {
 #pragma unroll
-    for (int c = 0; c < CPT; c++) ((float*)p.o)[ooff + c] = (float)out[c];
+    for (int e = 0; e < 4; e++) ((float*)p.o)[ooff + e] = out[e];
   } else {
 #pragma unroll
-    for (int c = 0; c < CPT; c++) ((uint16_t*)p.o)[ooff + c] = f2bf((float)out[c]);
+    for (int e = 0; e < 4; e++) ((uint16_t*)p.o)[ooff + e] = f2bf(out[e]);
   }
-  if (p.lse && c0 == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = (float)lse0;
+  if (p.lse && c == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = (float)lse0;
 }
 
 template <int D, bool F32>
 hipError_t launch_ra(const RowAttnParams& p, KeySrc src, hipStream_t stream) {
-  const dim3 grid(p.n_split, p.B * p.Hkv * p.sets_per_bu);
+  const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu);
   switch (src) {
     case SRC_RANGE: row_attn_kernel<D, F32, SRC_RANGE><<<grid, 256, 0, stream>>>(p); break;
     case SRC_TOKEN: row_attn_kernel<D, F32, SRC_TOKEN><<<grid, 256, 0, stream>>>(p); break;
     case SRC_BLOCK: row_attn_kernel<D, F32, SRC_BLOCK><<<grid, 256, 0, stream>>>(p); break;
+    case SRC_WINDOW: row_attn_kernel<D, F32, SRC_WINDOW><<<grid, 256, 0, stream>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -410,7 +475,7 @@ hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, Ke
 }
 
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.B * p.Hkv * p.sets_per_bu);
+  const dim3 grid(p.B * p.Hkv * p.sets_per_bu * 16);
   if (head_dim == 128)
     combine_kernel<128><<<grid, 256, 0, stream>>>(p);
   else

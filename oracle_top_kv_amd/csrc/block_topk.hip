@@ -16,6 +16,7 @@
 //      is contained in the union of per-split top-n), written in ascending block order.
 #include "hs_device.h"
 #include "hs_kernels.h"
+#include "score_common.h"
 
 namespace hs {
 namespace {
@@ -25,13 +26,15 @@ constexpr int kMaxRange = 256;  // blocks per split (per workgroup)
 template <int D, bool F32>
 __global__ __launch_bounds__(256) void blk_score_kernel(BlockTopkParams p) {
   __shared__ unsigned long long bkey[4][kMaxRange];  // per query of the set, per block of the split
+  __shared__ uint32_t bmax[4][kMaxRange];             // running block maxima (order-preserving keys)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rn = lane & 15, jg = lane >> 4;
-  const int split = blockIdx.x;
-  const int set = blockIdx.y;
-  const int sq = set % p.sets_per_bu;
-  const int bu = set / p.sets_per_bu;
-  const int u = bu % p.Hkv, b = bu / p.Hkv;
+  // KV head fastest, then split, then (batch, query chunk): see the row-attention kernel
+  const int u = blockIdx.x % p.Hkv;
+  const int split = (blockIdx.x / p.Hkv) % p.n_split;
+  const int bq = blockIdx.x / (p.Hkv * p.n_split);
+  const int sq = bq % p.sets_per_bu;
+  const int b = bq / p.sets_per_bu;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);
   const int nrows = nq * p.g;
@@ -42,9 +45,12 @@ __global__ __launch_bounds__(256) void blk_score_kernel(BlockTopkParams p) {
   long long blk_end = blk_begin + p.blocks_per_split;
   if (blk_end > t_last / p.block + 1) blk_end = t_last / p.block + 1;
   const int n_range = blk_end > blk_begin ? (int)(blk_end - blk_begin) : 0;
-  for (int i = threadIdx.x; i < 4 * kMaxRange; i += 256) (&bkey[0][0])[i] = 0ull;
+  for (int i = threadIdx.x; i < 4 * kMaxRange; i += 256) {
+    (&bkey[0][0])[i] = 0ull;
+    (&bmax[0][0])[i] = 0u;
+  }
 
-  constexpr int KK = F32 ? D / 4 : D / 32;
+  constexpr int KK = KTile<D, F32>::KK;
   const bool row_ok = rn < nrows;
   const int jq_r = row_ok ? rn / p.g : 0, hh_r = row_ok ? rn % p.g : 0;
   bf16x8 qa[F32 ? 1 : KK];
@@ -84,43 +90,47 @@ __global__ __launch_bounds__(256) void blk_score_kernel(BlockTopkParams p) {
 
   const size_t kv_row_stride = (size_t)p.Hkv * D;
   const size_t kv_base = ((size_t)b * p.Tk * p.Hkv + u) * D;
-  const int groups = p.block / 16;  // 16-key MFMA groups per block
-  for (int rb = wave; rb < n_range; rb += 4) {
-    const long long blk = blk_begin + rb;
-    float best = -INFINITY;  // running max for this lane's query over the block
-    for (int gi = 0; gi < groups; gi++) {
-      const long long pos = blk * p.block + 16 * gi + rn;
-      const long long pc = pos < p.Tk ? pos : 0;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (!F32) {
-        const uint16_t* kp = (const uint16_t*)p.k + kv_base + (size_t)pc * kv_row_stride;
+  // keys of this split's blocks, in 64-key tiles interleaved over the waves; every 16-key
+  // group's maximum is folded into its block with an LDS atomicMax on order-preserving keys
+  const long long key_begin = blk_begin * p.block;
+  long long key_end = blk_end * p.block;
+  if (key_end > t_last + 1) key_end = t_last + 1;
+  KTile<D, F32> cur, nxt;
+  long long tile = key_begin + 64LL * wave;
+  if (tile < key_end) load_k_tile<D, F32>(cur, p.k, kv_base, kv_row_stride, tile, p.Tk, rn, jg);
+  for (; tile < key_end; tile += 64LL * 4) {
+    if (tile + 256 < key_end)
+      load_k_tile<D, F32>(nxt, p.k, kv_base, kv_row_stride, tile + 256, p.Tk, rn, jg);
 #pragma unroll
-        for (int kk = 0; kk < KK; kk++) {
-          u32x4 raw = *(const u32x4*)(kp + 32 * kk + 8 * jg);
-          acc = mfma_bf16(qa[kk], __builtin_bit_cast(bf16x8, raw), acc);
-        }
-      } else {
-        const float* kp = (const float*)p.k + kv_base + (size_t)pc * kv_row_stride + jg * KK;
-#pragma unroll
-        for (int s = 0; s < KK; s++) acc = mfma_f32(qf[s], kp[s], acc);
-      }
+    for (int kb = 0; kb < 4; kb++) {
+      const long long g0 = tile + 16 * kb;  // first key of the group
+      const long long pos = g0 + rn;
+      const f32x4 acc = score_block<D, F32>(cur, kb, qa, qf);
       float v = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[e], p.scale_log2, -delta[e]));
       if (G >= 2) v = fmaxf(v, __shfl_xor(v, 16, 64));
       if (G >= 4) v = fmaxf(v, __shfl_xor(v, 32, 64));
       // causal: keys after this lane's query position do not count
-      if (pos > t_own || pos >= p.Tk) v = -INFINITY;
+      if (pos > t_own || pos >= key_end) v = -INFINITY;
       // max over the 16 keys of the group (lanes of one 16-lane row)
       v = fmaxf(v, __shfl_xor(v, 1, 64));
       v = fmaxf(v, __shfl_xor(v, 2, 64));
       v = fmaxf(v, __shfl_xor(v, 4, 64));
       v = fmaxf(v, __shfl_xor(v, 8, 64));
-      best = fmaxf(best, v);
+      const long long blk = g0 / p.block;
+      if (owner && rn == 0 && g0 < key_end && g0 <= t_own)
+        atomicMax(&bmax[jq_own][blk - blk_begin], float_key(v));
     }
-    if (owner && rn == 0 && blk <= t_own / p.block)
-      bkey[jq_own][rb] = ((unsigned long long)float_key(best) << 32) |
-                         (unsigned long long)(0xFFFFFFFFu - (uint32_t)blk);
+    cur = nxt;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 4 * n_range; i += 256) {
+    const int jq = i / n_range, rb = i % n_range;
+    const long long blk = blk_begin + rb;
+    if (jq < nq && blk <= (p.q_off + j0 + jq) / p.block)
+      bkey[jq][rb] = ((unsigned long long)bmax[jq][rb] << 32) |
+                     (unsigned long long)(0xFFFFFFFFu - (uint32_t)blk);
   }
   __syncthreads();
   // exact local top-n per query: rank = number of strictly larger keys (keys are distinct)
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(256) void blk_merge_kernel(BlockTopkParams p) {
 
 template <int D, bool F32>
 hipError_t launch_blk(const BlockTopkParams& p, hipStream_t stream) {
-  blk_score_kernel<D, F32><<<dim3(p.n_split, p.B * p.Hkv * p.sets_per_bu), 256, 0, stream>>>(p);
+  blk_score_kernel<D, F32><<<dim3(p.n_split * p.B * p.Hkv * p.sets_per_bu), 256, 0, stream>>>(p);
   const size_t rows = (size_t)p.B * p.Tq * p.Hkv;
   const size_t smem = (size_t)p.n_split * p.n_blocks * sizeof(unsigned long long);
   blk_merge_kernel<<<dim3((unsigned)rows), 256, smem, stream>>>(p);

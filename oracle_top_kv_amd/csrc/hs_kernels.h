@@ -9,7 +9,8 @@ namespace hs {
 enum KeySrc : int {
   SRC_RANGE = 0,  // contiguous positions lo..hi (full attention, sliding window)
   SRC_TOKEN = 1,  // token positions from an index list
-  SRC_BLOCK = 2   // whole blocks of `block` positions from a block-id list
+  SRC_BLOCK = 2,  // whole blocks of `block` positions from a block-id list
+  SRC_WINDOW = 3  // contiguous positions t-window+1 .. t (sliding window over own K', V')
 };
 
 // One launch of the row-attention kernel.  A row-set is a group of at most 16 (query, head)
@@ -21,7 +22,7 @@ struct RowAttnParams {
   const int32_t* idx;  // list modes: [B, Tq, Hkv, idx_cap]
   const int32_t* cnt;  // list modes: [B, Tq, Hkv]
   int idx_cap, block;
-  int window;  // range mode: > 0 restricts each row to positions t-window+1 .. t
+  int window;  // window mode: each row sees positions t-window+1 .. t
   int B, Tq, Tk, Hq, Hkv, g;
   long long q_off;
   int q_per_set;    // queries per row-set (range mode may pack several; list modes: 1)
@@ -68,12 +69,17 @@ struct TopkDecodeParams {
   long long q_off;
   int k_global, window;
   int q_per_set, sets_per_bu;   // query rows packed per score workgroup (q_per_set * g <= 16)
-  int n_split, keys_per_split;  // key chunk per workgroup (multiple of 64)
+  int n_split, keys_per_split;  // score pass: key chunk per workgroup (multiple of 64)
+  int sel_split, keys_per_sel;  // selection passes: key chunk per workgroup
   float scale_log2;
   // workspace
-  uint32_t* keys;    // [rows][Tk]   rows = B * Tq * Hkv
-  uint32_t* hist;    // [3][rows][2048]
-  uint32_t* counts;  // [rows][n_split][2]
+  uint32_t* keys;               // [rows][Tk]   rows = B * Tq * Hkv
+  uint32_t* hist;               // [rows][2048] top-11-bit histograms, followed by `bcount`
+  uint32_t* bcount;             // [rows] boundary-list lengths
+  unsigned long long* blist;    // [rows][Tk] boundary list (key << 32 | ~position)
+  uint32_t* above;              // [rows][sel_split] keys above the boundary bin, per chunk
+  uint32_t* counts;             // [rows][sel_split] keys taken per chunk
+  uint32_t* state;              // [rows][2] key threshold T, last position taken at T
   // outputs
   int32_t* idx;  // [B, Tq, Hkv, cap]
   int32_t* cnt;  // [B, Tq, Hkv]

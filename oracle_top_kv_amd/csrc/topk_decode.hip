@@ -14,14 +14,19 @@
 //   1. score: recompute the logits (MFMA, S = Q K^T so a key's g head values sit in one lane or
 //      one lane row), write the order-preserving 32-bit key per candidate and a histogram of its
 //      top 11 bits;
-//   2. radix passes on bits 20..10 and 9..0 among the keys that match the prefix found so far;
-//   3. the exact k-th key value T and how many keys equal to T are taken (lowest positions
-//      first: the tie rule is position ascending);
-//   4. ordered compaction per chunk (keys > T, and the first keys == T) into the index list,
-//      which is therefore ascending; the window positions follow; -1 padding to the cap.
+//   2. collect: the bin b1 holding the k-th key is found from the histogram; keys above b1 are
+//      counted per chunk (all of them are taken), keys inside b1 go to a boundary list with
+//      their positions;
+//   3. finalize: radix passes over the boundary list's 64-bit values (key << 32 | ~position)
+//      give the exact k1-th value V*, i.e. the key threshold T and the last position taken at
+//      T (ties go to the lower position); per-chunk counts of taken keys follow;
+//   4. write: ordered compaction per chunk (key > T, or key == T at a position <= the cut)
+//      into the index list, which is therefore ascending; the window positions follow; -1
+//      padding to the cap.
 // All steps are exact: nothing is dropped by an approximation.
 #include "hs_device.h"
 #include "hs_kernels.h"
+#include "score_common.h"
 
 namespace hs {
 namespace {
@@ -39,11 +44,12 @@ __global__ __launch_bounds__(256) void tk_score_kernel(TopkDecodeParams p) {
   __shared__ uint32_t hist[4][kBins];  // one per query row of the set (q_per_set * g <= 16, g >= 4)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rn = lane & 15, jg = lane >> 4;
-  const int split = blockIdx.x;
-  const int set = blockIdx.y;
-  const int sq = set % p.sets_per_bu;
-  const int bu = set / p.sets_per_bu;
-  const int u = bu % p.Hkv, b = bu / p.Hkv;
+  // KV head fastest, then split, then (batch, query chunk): see the row-attention kernel
+  const int u = blockIdx.x % p.Hkv;
+  const int split = (blockIdx.x / p.Hkv) % p.n_split;
+  const int bq = blockIdx.x / (p.Hkv * p.n_split);
+  const int sq = bq % p.sets_per_bu;
+  const int b = bq / p.sets_per_bu;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);
   const int nrows = nq * p.g;
@@ -52,7 +58,7 @@ __global__ __launch_bounds__(256) void tk_score_kernel(TopkDecodeParams p) {
   for (int i = threadIdx.x; i < 4 * kBins; i += 256) (&hist[0][0])[i] = 0u;
 
   // A operand: Q rows (row r = jq * g + hh)
-  constexpr int KK = F32 ? D / 4 : D / 32;  // MFMA steps over d
+  constexpr int KK = KTile<D, F32>::KK;
   const bool row_ok = rn < nrows;
   const int jq_r = row_ok ? rn / p.g : 0, hh_r = row_ok ? rn % p.g : 0;
   bf16x8 qa[F32 ? 1 : KK];
@@ -102,24 +108,16 @@ __global__ __launch_bounds__(256) void tk_score_kernel(TopkDecodeParams p) {
   const size_t kv_row_stride = (size_t)p.Hkv * D;
   const size_t kv_base = ((size_t)b * p.Tk * p.Hkv + u) * D;
 
-  for (long long tile = k_begin + 64LL * wave; tile < k_end; tile += 64LL * 4) {
+  KTile<D, F32> cur, nxt;
+  long long tile = k_begin + 64LL * wave;
+  if (tile < k_end) load_k_tile<D, F32>(cur, p.k, kv_base, kv_row_stride, tile, p.Tk, rn, jg);
+  for (; tile < k_end; tile += 64LL * 4) {
+    if (tile + 256 < k_end)
+      load_k_tile<D, F32>(nxt, p.k, kv_base, kv_row_stride, tile + 256, p.Tk, rn, jg);
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
       const long long pos = tile + 16 * kb + rn;
-      const long long pc = pos < p.Tk ? pos : 0;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (!F32) {
-        const uint16_t* kp = (const uint16_t*)p.k + kv_base + (size_t)pc * kv_row_stride;
-#pragma unroll
-        for (int kk = 0; kk < KK; kk++) {
-          u32x4 raw = *(const u32x4*)(kp + 32 * kk + 8 * jg);
-          acc = mfma_bf16(qa[kk], __builtin_bit_cast(bf16x8, raw), acc);
-        }
-      } else {
-        const float* kp = (const float*)p.k + kv_base + (size_t)pc * kv_row_stride + jg * KK;
-#pragma unroll
-        for (int s = 0; s < KK; s++) acc = mfma_f32(qf[s], kp[s], acc);
-      }
+      const f32x4 acc = score_block<D, F32>(cur, kb, qa, qf);
       // lane (key rn, group jg) holds rows 4jg..4jg+3 for key `pos`
       float v = -INFINITY;
 #pragma unroll
@@ -132,10 +130,11 @@ __global__ __launch_bounds__(256) void tk_score_kernel(TopkDecodeParams p) {
         atomicAdd(&hist[jq_own][key >> 21], 1u);
       }
     }
+    cur = nxt;
   }
   __syncthreads();
   for (int jq = 0; jq < nq; jq++) {
-    uint32_t* gh = p.hist + ((size_t)((b * p.Tq + j0 + jq) * p.Hkv + u)) * kBins;
+    uint32_t* gh = p.hist + ((size_t)(b * p.Tq + j0 + jq) * p.Hkv + u) * kBins;
     for (int i = threadIdx.x; i < kBins; i += 256) {
       const uint32_t c = hist[jq][i];
       if (c) atomicAdd(&gh[i], c);
@@ -143,41 +142,7 @@ __global__ __launch_bounds__(256) void tk_score_kernel(TopkDecodeParams p) {
   }
 }
 
-// Find, scanning bins from the top, the bin holding the k-th largest element; returns the bin
-// and the rank k' of that element within the bin (1-based).  All 256 threads call it.
-__device__ void find_bin(const uint32_t* h, int k, int* bin_out, int* k_out) {
-  __shared__ uint32_t part[256];
-  // thread i owns bins [8*(255-i), 8*(255-i)+8): thread 0 owns the top bins
-  const int base = 8 * (255 - threadIdx.x);
-  uint32_t s = 0;
-#pragma unroll
-  for (int q = 0; q < 8; q++) s += h[base + q];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  // inclusive prefix over threads (top-down order) by a simple log-step scan
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t x = threadIdx.x >= off ? part[threadIdx.x - off] : 0u;
-    __syncthreads();
-    part[threadIdx.x] += x;
-    __syncthreads();
-  }
-  const uint32_t incl = part[threadIdx.x];
-  const uint32_t excl = incl - s;
-  if ((int)excl < k && k <= (int)incl) {
-    uint32_t cum = excl;
-    for (int q = 7; q >= 0; q--) {
-      const uint32_t c = h[base + q];
-      if ((int)(cum + c) >= k) {
-        *bin_out = base + q;
-        *k_out = k - (int)cum;
-        break;
-      }
-      cum += c;
-    }
-  }
-  __syncthreads();
-}
-
+// ---- selection ----------------------------------------------------------------------------
 struct RowSel {
   int k_eff;  // number of candidates to take
   long long n_cand;
@@ -194,101 +159,159 @@ __device__ __forceinline__ RowSel row_sel(const TopkDecodeParams& p, int row) {
   return r;
 }
 
-// ---- 2. radix passes on the lower digits ---------------------------------------------------
-// PASS 1: digit bits 20..10 among keys whose bits 31..21 match; PASS 2: bits 9..0.
-template <int PASS>
-__global__ __launch_bounds__(256) void tk_pass_kernel(TopkDecodeParams p) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ int sel[4];
-  const int split = blockIdx.x, row = blockIdx.y;
-  if (threadIdx.x < 4) sel[threadIdx.x] = 0;
-  const RowSel rs = row_sel(p, row);
-  if (rs.k_eff == 0) return;
-  const size_t nrows = (size_t)p.B * p.Tq * p.Hkv;
-  const uint32_t* h0 = p.hist + (size_t)row * kBins;
-  const uint32_t* h1 = p.hist + (nrows + row) * kBins;
-  for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = 0u;
-  find_bin(h0, rs.k_eff, &sel[0], &sel[1]);
-  if (PASS == 2) find_bin(h1, sel[1], &sel[2], &sel[3]);
-  __syncthreads();
-  const uint32_t b1 = sel[0];
-  const uint32_t b2 = PASS == 2 ? (uint32_t)sel[2] : 0u;
-  const long long k_begin = (long long)split * p.keys_per_split;
-  long long k_end = k_begin + p.keys_per_split;
-  if (k_end > rs.n_cand) k_end = rs.n_cand;
-  const uint32_t* keys = p.keys + (size_t)row * p.Tk;
-  for (long long i = k_begin + threadIdx.x; i < k_end; i += 256) {
-    const uint32_t key = keys[i];
-    if ((key >> 21) != b1) continue;
-    if (PASS == 1) {
-      atomicAdd(&hist[(key >> 10) & 2047u], 1u);
-    } else if (((key >> 10) & 2047u) == b2) {
-      atomicAdd(&hist[key & 1023u], 1u);
+// Scanning a 2048-bin histogram from the top bin down, find the bin that holds the k-th largest
+// element and the rank (1-based) of that element inside the bin.  Wave 0 does the scan with
+// lane shuffles; every thread of the workgroup must call it (it synchronizes).
+__device__ void find_bin(const uint32_t* h, int k, int* bin_out, int* k_out) {
+  __shared__ int res[2];
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int top = kBins - 32 * lane;  // lane owns bins [top-32, top), lane 0 the highest
+    uint32_t s = 0;
+    for (int q = 1; q <= 32; q++) s += h[top - q];
+    uint32_t incl = s;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t x = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += x;
+    }
+    const uint32_t excl = incl - s;
+    if ((long long)excl < k && (long long)k <= (long long)incl) {
+      uint32_t cum = excl;
+      for (int q = 1; q <= 32; q++) {
+        const uint32_t c = h[top - q];
+        if ((long long)cum + c >= k) {
+          res[0] = top - q;
+          res[1] = k - (int)cum;
+          break;
+        }
+        cum += c;
+      }
     }
   }
   __syncthreads();
-  uint32_t* gh = p.hist + ((PASS == 1 ? nrows : 2 * nrows) + row) * kBins;
-  for (int i = threadIdx.x; i < kBins; i += 256)
-    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+  *bin_out = res[0];
+  *k_out = res[1];
+  __syncthreads();
 }
 
-// ---- 3. exact threshold, per-chunk counts ------------------------------------------------
-__device__ void threshold(const TopkDecodeParams& p, int row, int k_eff, uint32_t* T, int* k_eq) {
-  __shared__ int sel[6];
-  const size_t nrows = (size_t)p.B * p.Tq * p.Hkv;
-  if (threadIdx.x < 6) sel[threadIdx.x] = 0;
-  __syncthreads();
-  find_bin(p.hist + (size_t)row * kBins, k_eff, &sel[0], &sel[1]);
-  find_bin(p.hist + (nrows + row) * kBins, sel[1], &sel[2], &sel[3]);
-  find_bin(p.hist + (2 * nrows + row) * kBins, sel[3], &sel[4], &sel[5]);
-  __syncthreads();
-  *T = ((uint32_t)sel[0] << 21) | ((uint32_t)sel[2] << 10) | (uint32_t)sel[4];
-  *k_eq = sel[5];
-}
-
-__global__ __launch_bounds__(256) void tk_count_kernel(TopkDecodeParams p) {
-  __shared__ uint32_t tot[2];
+// ---- 2. collect: per chunk, count keys above the boundary bin b1 (all taken) and append the
+// keys inside it, with their positions, to the row's boundary list --------------------------
+__global__ __launch_bounds__(256) void tk_collect_kernel(TopkDecodeParams p) {
+  __shared__ uint32_t scan[256];
+  __shared__ uint32_t base_sh, above_sh;
   const int split = blockIdx.x, row = blockIdx.y;
   const RowSel rs = row_sel(p, row);
-  uint32_t* cnt = p.counts + ((size_t)row * p.n_split + split) * 2;
-  if (rs.k_eff == 0) {
-    if (threadIdx.x == 0) cnt[0] = cnt[1] = 0u;
-    return;
-  }
-  uint32_t T;
-  int k_eq;
-  threshold(p, row, rs.k_eff, &T, &k_eq);
-  if (threadIdx.x < 2) tot[threadIdx.x] = 0u;
-  __syncthreads();
-  const long long k_begin = (long long)split * p.keys_per_split;
-  long long k_end = k_begin + p.keys_per_split;
+  if (rs.k_eff == 0) return;
+  int b1, k1;
+  find_bin(p.hist + (size_t)row * kBins, rs.k_eff, &b1, &k1);
+  const long long k_begin = (long long)split * p.keys_per_sel;
+  long long k_end = k_begin + p.keys_per_sel;
   if (k_end > rs.n_cand) k_end = rs.n_cand;
   const uint32_t* keys = p.keys + (size_t)row * p.Tk;
-  uint32_t gt = 0, eq = 0;
+  // pass 1: per-thread counts of keys above b1 and inside b1
+  uint32_t above = 0, inside = 0;
   for (long long i = k_begin + threadIdx.x; i < k_end; i += 256) {
-    const uint32_t key = keys[i];
-    gt += key > T;
-    eq += key == T;
+    const uint32_t d = keys[i] >> 21;
+    above += d > (uint32_t)b1;
+    inside += d == (uint32_t)b1;
   }
-  atomicAdd(&tot[0], gt);
-  atomicAdd(&tot[1], eq);
+  // exclusive scan of `inside` over the workgroup; one global reservation per workgroup
+  scan[threadIdx.x] = inside;
+  if (threadIdx.x == 0) above_sh = 0u;
   __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t x = threadIdx.x >= off ? scan[threadIdx.x - off] : 0u;
+    __syncthreads();
+    scan[threadIdx.x] += x;
+    __syncthreads();
+  }
+  atomicAdd(&above_sh, above);
+  if (threadIdx.x == 255) base_sh = scan[255] ? atomicAdd(p.bcount + row, scan[255]) : 0u;
+  __syncthreads();
+  // pass 2: write this thread's boundary entries (key << 32 | ~position)
+  unsigned long long* bl = p.blist + (size_t)row * p.Tk;
+  uint32_t slot = base_sh + scan[threadIdx.x] - inside;
+  for (long long i = k_begin + threadIdx.x; i < k_end && inside; i += 256) {
+    const uint32_t key = keys[i];
+    if ((key >> 21) == (uint32_t)b1) {
+      bl[slot++] = ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
+      inside--;
+    }
+  }
+  if (threadIdx.x == 0) p.above[(size_t)row * p.sel_split + split] = above_sh;
+}
+
+// ---- 3. finalize: exact k1-th largest of the boundary list, by radix passes over the 64-bit
+// value (key << 32 | ~position), so that ties in the key go to the lower position ------------
+__global__ __launch_bounds__(256) void tk_finalize_kernel(TopkDecodeParams p) {
+  constexpr int kStage = 4096;  // boundary entries staged in LDS when they fit
+  __shared__ uint32_t hist[kBins];
+  __shared__ unsigned long long stage[kStage];
+  extern __shared__ uint32_t chunk_sel[];  // sel_split counters
+  const int row = blockIdx.x;
+  const RowSel rs = row_sel(p, row);
+  if (rs.k_eff == 0) return;
+  int b1, k1;
+  find_bin(p.hist + (size_t)row * kBins, rs.k_eff, &b1, &k1);
+  const int m = (int)p.bcount[row];
+  const unsigned long long* bl = p.blist + (size_t)row * p.Tk;
+  if (m <= kStage) {
+    for (int i = threadIdx.x; i < m; i += 256) stage[i] = bl[i];
+    bl = stage;
+  }
+  // digits of V below the common 11-bit prefix: bits 52..42, 41..32, 31..21, 20..10, 9..0
+  const int shifts[5] = {42, 32, 21, 10, 0};
+  const int widths[5] = {11, 10, 11, 11, 10};
+  unsigned long long prefix = (unsigned long long)b1 << 53, pmask = 0x7FFull << 53;
+  int k = k1;
+  for (int d = 0; d < 5; d++) {
+    for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = 0u;
+    __syncthreads();
+    const unsigned long long dmask = (1ull << widths[d]) - 1ull;
+    for (int i = threadIdx.x; i < m; i += 256) {
+      const unsigned long long v = bl[i];
+      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shifts[d]) & dmask], 1u);
+    }
+    __syncthreads();
+    int bin, kr;
+    find_bin(hist, k, &bin, &kr);
+    const bool all_taken = hist[bin] == (uint32_t)kr;
+    prefix |= (unsigned long long)bin << shifts[d];
+    pmask |= dmask << shifts[d];
+    k = kr;
+    // every entry with this prefix is taken: V >= prefix (lower bits 0) selects exactly them
+    if (all_taken) break;
+  }
+  const unsigned long long vstar = prefix;
+  for (int c = threadIdx.x; c < p.sel_split; c += 256) chunk_sel[c] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < m; i += 256) {
+    const unsigned long long v = bl[i];
+    if (v >= vstar) {
+      const uint32_t pos = 0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull);
+      atomicAdd(&chunk_sel[pos / p.keys_per_sel], 1u);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < p.sel_split; c += 256)
+    p.counts[(size_t)row * p.sel_split + c] = p.above[(size_t)row * p.sel_split + c] + chunk_sel[c];
   if (threadIdx.x == 0) {
-    cnt[0] = tot[0];
-    cnt[1] = tot[1];
+    // selection rule for every key: V >= V*, i.e. key > T, or key == T at position <= pos*
+    p.state[2 * (size_t)row] = (uint32_t)(vstar >> 32);                              // T
+    p.state[2 * (size_t)row + 1] = 0xFFFFFFFFu - (uint32_t)(vstar & 0xFFFFFFFFull);   // pos*
   }
 }
 
 // ---- 4. ordered compaction + window + padding ----------------------------------------------
 __global__ __launch_bounds__(256) void tk_write_kernel(TopkDecodeParams p) {
-  __shared__ uint32_t wsum[2][4];
-  __shared__ long long base_sh[2];
+  __shared__ uint32_t wsum[4];
+  __shared__ long long base_sh;
   const int split = blockIdx.x, row = blockIdx.y;
   const RowSel rs = row_sel(p, row);
   int32_t* out = p.idx + (size_t)row * p.cap;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  if (split == p.n_split - 1) {
+  if (split == p.sel_split - 1) {
     // window positions after the k_eff selected candidates, then padding and the count
     const long long w0 = rs.t - p.window + 1 > 0 ? rs.t - p.window + 1 : 0;
     const int n_win = (int)(rs.t - w0 + 1);
@@ -297,59 +320,36 @@ __global__ __launch_bounds__(256) void tk_write_kernel(TopkDecodeParams p) {
     if (threadIdx.x == 0) p.cnt[row] = rs.k_eff + n_win;
   }
   if (rs.k_eff == 0) return;
-
-  uint32_t T;
-  int k_eq;
-  threshold(p, row, rs.k_eff, &T, &k_eq);
-  // offsets from the chunks before this one
+  const uint32_t T = p.state[2 * (size_t)row];
+  const uint32_t pos_star = p.state[2 * (size_t)row + 1];
   if (threadIdx.x == 0) {
-    long long off = 0, eq_before = 0;
-    const uint32_t* c = p.counts + (size_t)row * p.n_split * 2;
-    for (int s = 0; s < split; s++) {
-      const long long gt = c[2 * s], eq = c[2 * s + 1];
-      long long take = k_eq - eq_before;
-      take = take < 0 ? 0 : (take > eq ? eq : take);
-      off += gt + take;
-      eq_before += eq;
-    }
-    base_sh[0] = off;
-    base_sh[1] = eq_before;
+    long long off = 0;
+    const uint32_t* c = p.counts + (size_t)row * p.sel_split;
+    for (int s2 = 0; s2 < split; s2++) off += c[s2];
+    base_sh = off;
   }
   __syncthreads();
-  long long off = base_sh[0], eq_seen = base_sh[1];
-  const long long k_begin = (long long)split * p.keys_per_split;
-  long long k_end = k_begin + p.keys_per_split;
+  long long off = base_sh;
+  const long long k_begin = (long long)split * p.keys_per_sel;
+  long long k_end = k_begin + p.keys_per_sel;
   if (k_end > rs.n_cand) k_end = rs.n_cand;
   const uint32_t* keys = p.keys + (size_t)row * p.Tk;
+  const unsigned long long lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (long long i0 = k_begin; i0 < k_end; i0 += 256) {
     const long long i = i0 + threadIdx.x;
     const uint32_t key = i < k_end ? keys[i] : 0u;
-    const bool is_gt = i < k_end && key > T;
-    const bool is_eq = i < k_end && key == T;
-    // block-wide exclusive prefix of equal keys, in position order
-    const unsigned long long beq = __ballot(is_eq);
-    const unsigned long long lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const uint32_t eq_in_wave = __popcll(beq & lower);
-    if (lane == 0) wsum[1][wave] = __popcll(beq);
-    __syncthreads();
-    uint32_t eq_prev = 0;
-    for (int w = 0; w < wave; w++) eq_prev += wsum[1][w];
-    const long long eq_rank = eq_seen + eq_prev + eq_in_wave;
-    const bool take = is_gt || (is_eq && eq_rank < k_eq);
+    const bool take = i < k_end && (key > T || (key == T && (uint32_t)i <= pos_star));
     const unsigned long long bt = __ballot(take);
-    const uint32_t t_in_wave = __popcll(bt & lower);
-    if (lane == 0) wsum[0][wave] = __popcll(bt);
+    if (lane == 0) wsum[wave] = __popcll(bt);
     __syncthreads();
-    uint32_t t_prev = 0, t_all = 0, eq_all = 0;
+    uint32_t t_prev = 0, t_all = 0;
     for (int w = 0; w < 4; w++) {
-      if (w < wave) t_prev += wsum[0][w];
-      t_all += wsum[0][w];
-      eq_all += wsum[1][w];
+      if (w < wave) t_prev += wsum[w];
+      t_all += wsum[w];
     }
-    const long long slot = off + t_prev + t_in_wave;
+    const long long slot = off + t_prev + __popcll(bt & lower);
     if (take && slot < rs.k_eff) out[slot] = (int32_t)i;
     off += t_all;
-    eq_seen += eq_all;
     __syncthreads();
   }
 }
@@ -357,13 +357,12 @@ __global__ __launch_bounds__(256) void tk_write_kernel(TopkDecodeParams p) {
 template <int D, bool F32>
 hipError_t launch_tk(const TopkDecodeParams& p, hipStream_t stream) {
   const size_t rows = (size_t)p.B * p.Tq * p.Hkv;
-  const size_t hist_words = 3 * rows * kBins;
-  zero_u32_kernel<<<(unsigned)((hist_words + 255) / 256 < 1024 ? (hist_words + 255) / 256 : 1024), 256, 0, stream>>>(p.hist, hist_words);
-  tk_score_kernel<D, F32><<<dim3(p.n_split, p.B * p.Hkv * p.sets_per_bu), 256, 0, stream>>>(p);
-  tk_pass_kernel<1><<<dim3(p.n_split, rows), 256, 0, stream>>>(p);
-  tk_pass_kernel<2><<<dim3(p.n_split, rows), 256, 0, stream>>>(p);
-  tk_count_kernel<<<dim3(p.n_split, rows), 256, 0, stream>>>(p);
-  tk_write_kernel<<<dim3(p.n_split, rows), 256, 0, stream>>>(p);
+  const size_t zero_words = rows * kBins + rows;  // first histograms, then boundary counters
+  zero_u32_kernel<<<(unsigned)((zero_words + 255) / 256 < 1024 ? (zero_words + 255) / 256 : 1024), 256, 0, stream>>>(p.hist, zero_words);
+  tk_score_kernel<D, F32><<<dim3(p.n_split * p.B * p.Hkv * p.sets_per_bu), 256, 0, stream>>>(p);
+  tk_collect_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
+  tk_finalize_kernel<<<dim3((unsigned)rows), 256, p.sel_split * sizeof(uint32_t), stream>>>(p);
+  tk_write_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
