@@ -160,7 +160,13 @@ hs_status hip_status(hipError_t e, const char* what) {
 // ---- full attention ------------------------------------------------------------------------
 constexpr long long kResidentWorkgroups = 512;  // 256 CUs x 2 workgroups of this kernel
 
+// Many queries per KV head (bf16): the LDS-tiled prefill kernel; otherwise the row kernel.
+bool use_prefill_kernel(const Shape& s) {
+  return !s.in_f32 && (long long)s.Tq * s.g > 16 && 128 % s.g == 0;
+}
+
 size_t full_attn_ws(const Shape& s) {
+  if (use_prefill_kernel(s)) return 0;
   const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
   return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
 }
@@ -329,6 +335,25 @@ hs_status hs_full_attn_fwd(const hs_attn_desc* desc, const void* q, const void* 
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
   if (!q || !k || !v || !o || !lse) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (use_prefill_kernel(s)) {
+    hs::PrefillParams pp;
+    memset(&pp, 0, sizeof(pp));
+    pp.q = q;
+    pp.k = k;
+    pp.v = v;
+    pp.B = s.B;
+    pp.Tq = s.Tq;
+    pp.Tk = s.Tk;
+    pp.Hq = s.Hq;
+    pp.Hkv = s.Hkv;
+    pp.g = s.g;
+    pp.q_off = s.q_off;
+    pp.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+    pp.o = o;
+    pp.lse = lse;
+    pp.out_f32 = s.out_f32;
+    return hip_status(hs::launch_prefill_attn(pp, s.D, (hipStream_t)stream), "prefill attention kernel");
+  }
   const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
   const size_t need = g.n_split > 1 ? partial_bytes(g, s.D) : 0;
   if (need > 0 && (!ws || ws_bytes < need))

@@ -58,6 +58,21 @@ struct CombineParams {
 
 hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
                            hipStream_t stream);
+
+// Full causal attention for many queries per KV head (bf16): 128 (query, head) rows per
+// workgroup sharing LDS-staged K/V tiles.
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int B, Tq, Tk, Hq, Hkv, g;
+  long long q_off;
+  float scale_log2;
+  void* o;
+  float* lse;
+  int out_f32;
+};
+hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 
 // ---- token top-k for row groups of at most 16 (query, head) rows (decode) ----------------

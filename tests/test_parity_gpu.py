@@ -41,6 +41,9 @@ FULL_CASES = [
     ("decode_bf16_g16", Workload("dec16", 2, 1, 3001, 64, 4, 128, "bf16", seed=12)),
     ("short_block_bf16_d64", Workload("sb", 2, 3, 777, 8, 2, 64, "bf16", seed=13)),
     ("prefill_bf16_g4_ragged", Workload("pf", 1, 200, 1100, 8, 2, 128, "bf16", seed=14)),
+    ("prefill_bf16_g16_chunk", Workload("pf16", 1, 77, 3000, 32, 2, 128, "bf16", seed=15)),
+    ("prefill_bf16_g8_d64_causal", Workload("pf8", 2, 300, 300, 16, 2, 64, "bf16", seed=16)),
+    ("prefill_bf16_g4_causal_long", Workload("pf4", 1, 700, 700, 8, 2, 128, "bf16", seed=17)),
 ]
 
 
