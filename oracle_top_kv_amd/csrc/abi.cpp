@@ -162,7 +162,7 @@ constexpr long long kResidentWorkgroups = 512;  // 256 CUs x 2 workgroups of thi
 
 // Many queries per KV head (bf16): the LDS-tiled prefill kernel; otherwise the row kernel.
 bool use_prefill_kernel(const Shape& s) {
-  return !s.in_f32 && (long long)s.Tq * s.g > 16 && 128 % s.g == 0;
+  return !s.in_f32 && (long long)s.Tq * s.g > 16 && 256 % s.g == 0;
 }
 
 size_t full_attn_ws(const Shape& s) {

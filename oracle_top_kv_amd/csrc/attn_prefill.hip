@@ -2,9 +2,10 @@
 // O and LSE [P2 "Extracting block scores from exact attention", attention equations;
 // P4 section 3.2, the tiled loop of Algorithm 1 without its score output].
 //
-// A workgroup owns 128 (query, head) rows of one KV head: 128/g consecutive queries times the
-// g heads of the group, so every K/V tile staged in LDS serves all heads of the group.  Each of
-// the 4 waves owns 32 rows (two 16-row MFMA blocks).  Per 64-key tile:
+// A workgroup owns 256 (query, head) rows of one KV head: 256/g consecutive queries times the
+// g heads of the group, so every K/V tile staged in LDS serves all heads of the group (256 rows
+// per 64-key tile: 128 flop per byte of K/V moved from L2).  Each of the 8 waves owns 32 rows
+// (two 16-row MFMA blocks).  Per 64-key tile:
 //   S^T = K Q^T   A = K from LDS (ds_read_b128), B = Q^T resident in registers
 //   online softmax in the log2 domain; the row state lives in the 4 lanes of the row
 //   O^T += V^T P^T  B = P^T straight from the S^T accumulator (bf16), A = V^T from the
@@ -18,7 +19,8 @@
 namespace hs {
 namespace {
 
-constexpr int kRowsWG = 128;
+constexpr int kRowsWG = 256;
+constexpr int kThreads = 512;
 constexpr int kBN = 64;
 
 template <int D>
@@ -28,11 +30,11 @@ struct PfCfg {
   static constexpr int KK = D / 32;     // MFMA steps over d
   static constexpr int DB = D / 16;     // 16-wide d blocks of O
   static constexpr int CPR = D / 8;     // 16-byte chunks per row
-  static constexpr int LPT = kBN * CPR / 256;  // chunks per thread per tile (each of K and V)
+  static constexpr int LPT = kBN * CPR / kThreads;  // chunks per thread per tile (each of K and V)
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void pf_attn_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   using C = PfCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBN * C::KStr];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][kBN * C::VStr];
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(PrefillParams p) {
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < C::LPT; i++) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + kThreads * i;
       const int row = c / C::CPR, ch = c % C::CPR;
       long long key = (long long)t * kBN + row;
       if (key > t_max) key = t_max;  // rows past the last query are loaded but masked
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(PrefillParams p) {
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::LPT; i++) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + kThreads * i;
       const int row = c / C::CPR, ch = c % C::CPR;
       *(u32x4*)(&ks[buf][row * C::KStr + ch * 8]) = kreg[i];
       *(u32x4*)(&vs[buf][row * C::VStr + ch * 8]) = vreg[i];
@@ -162,8 +164,10 @@ __global__ __launch_bounds__(256, 2) void pf_attn_kernel(PrefillParams p) {
       l_c[rb] *= alpha;
       kahan_add(l_s[rb], l_c[rb], psum);
       m_run[rb] = m_new;
+      if (__ballot(alpha != 1.f)) {  // rescale only when some row maximum moved
 #pragma unroll
-      for (int db = 0; db < C::DB; db++) oacc[rb][db] *= alpha;
+        for (int db = 0; db < C::DB; db++) oacc[rb][db] *= alpha;
+      }
 #pragma unroll
       for (int s = 0; s < 2; s++) {
         const float x8[8] = {pv[2 * s][0], pv[2 * s][1], pv[2 * s][2], pv[2 * s][3],
@@ -220,9 +224,9 @@ hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t
   const int n_qt = (p.Tq + qpw - 1) / qpw;
   const dim3 grid(p.B * p.Hkv * n_qt);
   if (head_dim == 128)
-    pf_attn_kernel<128><<<grid, 256, 0, stream>>>(p);
+    pf_attn_kernel<128><<<grid, kThreads, 0, stream>>>(p);
   else
-    pf_attn_kernel<64><<<grid, 256, 0, stream>>>(p);
+    pf_attn_kernel<64><<<grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -52,12 +52,11 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// Eight floats -> bf16x8, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
-  typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-  u16x8 v;
-#pragma unroll
-  for (int i = 0; i < 8; i++) v[i] = f2bf(x[i]);
-  return __builtin_bit_cast(bf16x8, v);
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
 }
 
 // Order-preserving map float -> uint32 (larger float -> larger key; -0 < +0 is fine here).
