@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 80B-shaped prefill leg (full attention + token top-k)")
     return ap.parse_args()
 
 
@@ -141,9 +143,52 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }
+    if not args.no_prefill:
+        del x, q, k, v, qs, kl, vl, gate
+        torch.cuda.empty_cache()
+        out["prefill"] = prefill_leg(args)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, make_inputs(wl, device=dev, block_variant=True),
+                                           args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def prefill_leg(args):
+    """Full attention + token top-k on the 80B-shaped prefill chunk (4096 queries appended to a
+    131072-token cache, 64/4 heads, d 128, bf16): TFLOP/s of the full-attention flops plus the
+    score-recompute flops over the two calls' time, and of the full-attention flops alone."""
+    import torch
+
+    from oracle_top_kv_amd import costs, hs
+    from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["prefill_80b_128k"]
+    x = make_inputs(wl, device=torch.device("cuda:0"), n_sparse=0)
+    q, k, v = x["q"], x["k"], x["v"]
+    for _ in range(2):
+        _, lse = hs.full_attn_fwd(q, k, v)
+        hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+    torch.cuda.synchronize()
+    reps = 3
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record()
+        _, lse = hs.full_attn_fwd(q, k, v)
+        ev[r][1].record()
+        hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+        ev[r][2].record()
+    torch.cuda.synchronize()
+    t_fa = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    t_tk = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    f_fa, f_sc = costs.full_attn_flops(wl), costs.score_flops(wl)
+    tot = (f_fa + f_sc) / ((t_fa + t_tk) * 1e-3) / 1e12
+    return {"workload": wl.name, "full_attn_ms": round(t_fa, 3), "topk_ms": round(t_tk, 3),
+            "full_attn_tflops": round(f_fa / (t_fa * 1e-3) / 1e12, 1),
+            "topk_score_tflops": round(f_sc / (t_tk * 1e-3) / 1e12, 1),
+            "full_attn_plus_topk_tflops": round(tot, 1),
+            "useful_tflops": round(f_fa / ((t_fa + t_tk) * 1e-3) / 1e12, 1),
+            "mfma_frac_full_attn": round(f_fa / (t_fa * 1e-3) / 2.5e15, 4),
+            "peak_tflops": 2500.0, "reps": reps}
 
 
 def cpu_baseline(wl, x, budget_s):

@@ -225,6 +225,33 @@ TkLayout tk_layout(const Shape& s, const TkGeom& t) {
 
 size_t tk_ws(const Shape& s, const TkGeom& t) { return tk_layout(s, t).total; }
 
+// Many query rows per KV head: selection streams over K tiles and stores no per-key score.
+bool use_prefill_select(const Shape& s, int k_global) {
+  return (long long)s.Tq * s.g > 16 && k_global <= hs::prefill_select_max_k();
+}
+
+size_t tk_prefill_ws(const Shape& s) {
+  return align_up((size_t)s.B * s.Tq * s.Hkv * hs::prefill_select_buffer_cap() * 8, 256);
+}
+
+hs::PrefillSelectParams select_params(const Shape& s, const void* q, const void* k,
+                                      const float* lse) {
+  hs::PrefillSelectParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.lse = lse;
+  p.B = s.B;
+  p.Tq = s.Tq;
+  p.Tk = s.Tk;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.g;
+  p.q_off = s.q_off;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  return p;
+}
+
 // ---- block top-k ---------------------------------------------------------------------------
 struct BkGeom {
   int q_per_set, sets_per_bu, n_split, blocks_per_split;
@@ -260,6 +287,11 @@ hs_status bk_check(const Shape& s, int block, int n_blocks, BkGeom* g) {
   if ((long long)g->n_split * n_blocks > 4096)
     return fail(HS_ERR_UNSUPPORTED, "context too long for the block merge (%d splits)", g->n_split);
   return HS_OK;
+}
+
+// Many query rows per KV head and blocks that tile 64 keys: streamed running top-n.
+bool use_prefill_blocks(const Shape& s, int block) {
+  return (long long)s.Tq * s.g > 16 && 64 % block == 0;
 }
 
 size_t bk_ws(const BkGeom& g, int n_blocks) {
@@ -313,11 +345,13 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
     case HS_OP_FULL_ATTN: return full_attn_ws(s);
     case HS_OP_ORACLE_TOPK: {
       if (s.g != 4 && s.g != 8 && s.g != 16) return 0;
+      if (use_prefill_select(s, p0)) return tk_prefill_ws(s);
       return tk_ws(s, tk_geom(s));
     }
     case HS_OP_BLOCK_TOPK: {
       BkGeom g;
       if (bk_check(s, p0, p1, &g) != HS_OK) return 0;
+      if (use_prefill_blocks(s, p0)) return 0;
       return bk_ws(g, p1);
     }
     case HS_OP_SPARSE_ATTN: {
@@ -393,6 +427,20 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
   if ((long long)k_global + window < 1) return fail(HS_ERR_INVALID_ARG, "k_global + window must be >= 1");
   if (s.g != 4 && s.g != 8 && s.g != 16)
     return fail(HS_ERR_UNSUPPORTED, "token selection needs a GQA group of 4, 8 or 16 (got %d)", s.g);
+  if (use_prefill_select(s, k_global)) {
+    const size_t need = tk_prefill_ws(s);
+    if (!ws || ws_bytes < need)
+      return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    hs::PrefillSelectParams p = select_params(s, q, k, lse);
+    p.k_global = k_global;
+    p.window = window;
+    p.cap = k_global + window;
+    p.tbuf = (unsigned long long*)ws;
+    p.idx = idx;
+    p.cnt = count;
+    return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, false, (hipStream_t)stream),
+                      "token selection kernel");
+  }
   const TkGeom t = tk_geom(s);
   const size_t need = tk_ws(s, t);
   if (!ws || ws_bytes < need)
@@ -445,6 +493,15 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
   BkGeom g;
   st = bk_check(s, block, n_blocks, &g);
   if (st != HS_OK) return st;
+  if (use_prefill_blocks(s, block)) {
+    hs::PrefillSelectParams p = select_params(s, q, k, lse);
+    p.block = block;
+    p.n_blocks = n_blocks;
+    p.idx = blk_idx;
+    p.cnt = count;
+    return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, true, (hipStream_t)stream),
+                      "block selection kernel");
+  }
   const size_t need = bk_ws(g, n_blocks);
   if (!ws || ws_bytes < need)
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);

@@ -121,4 +121,26 @@ struct BlockTopkParams {
 hipError_t launch_block_topk(const BlockTopkParams& p, int head_dim, bool in_f32,
                              hipStream_t stream);
 
+// ---- selection for many queries per KV head (prefill), streamed tile by tile -----------------
+struct PrefillSelectParams {
+  const void* q;
+  const void* k;
+  const float* lse;
+  int B, Tq, Tk, Hq, Hkv, g;
+  long long q_off;
+  float scale_log2;
+  // token mode
+  int k_global, window, cap;
+  unsigned long long* tbuf;  // workspace [rows][prefill_select_buffer_cap()]
+  // block mode
+  int block, n_blocks;
+  // outputs
+  int32_t* idx;
+  int32_t* cnt;
+};
+int prefill_select_buffer_cap();
+int prefill_select_max_k();
+hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
+                                 bool block_mode, hipStream_t stream);
+
 }  // namespace hs

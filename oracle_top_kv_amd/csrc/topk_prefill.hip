@@ -1,0 +1,467 @@
+// topk_prefill.hip -- exact token and block selection for many queries per KV head (prefill),
+// without storing any per-key score: scores are recomputed tile by tile and selected on the fly.
+//
+// Scores [P2 "Extracting block scores from exact attention"; P2 "GQA: the group shares one index
+// set"; P4 section 3.2]:
+//   token  s_i = max_{h in group} exp(a^h_i - LSE^h)            (HySparse2, P1 section 4.2; P5)
+//   block  S_r = max over the block's keys i <= t of s_i        (HySparse, P2 TopK equation)
+// ranked in the log2 domain as max_h(a^h * tau * log2 e - (LSE^h * log2 e - C)) with a per-query
+// integer C, exactly as in the decode kernels, and compared as 64-bit values
+// V = (order-preserving score bits << 32) | ~position (or ~block id): equal scores prefer the
+// lower position.
+//
+// Tiling: a workgroup owns 256 (query, head) rows of one KV head (256/g queries, all g heads),
+// 8 waves of 32 rows; 64-key K tiles are double-buffered in LDS and shared by all rows.
+// S = Q K^T on MFMA (A = Q rows resident, B = K^T from LDS) leaves the g head values of one key
+// in one lane row, so the group maximum is an in-lane max plus at most two shuffles.
+//
+// Token mode: each query keeps a candidate buffer (2048 entries) in the workspace.  A key enters
+// it if it is a candidate (position <= t - w) and V >= theta, the query's running threshold.
+// When the buffer is nearly full, the query's wave compacts it exactly: a radix select (8-bit
+// digits; entries in registers, histogram in LDS) finds the k-th largest V, theta becomes that
+// value (or the lower bound of a bin taken whole), and only entries >= theta stay.  Every key
+// dropped is below k kept keys, so the final top-k is exact.  At the end the k positions are
+// sorted (bitonic, in LDS) and the forced window is appended.
+// Block mode (blocks of 16, 32 or 64 keys): each query keeps its best n blocks in LDS; a block
+// replaces the current minimum when its V is larger.
+#include "hs_device.h"
+#include "hs_kernels.h"
+
+namespace hs {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kRowsWG = 256;
+constexpr int kBN = 64;
+constexpr int kBufCap = 2048;          // token candidates per query
+constexpr int kNPL = kBufCap / 64;     // buffer entries per lane during a compaction
+constexpr int kSortCap = 1024;         // largest k_global of the token mode
+constexpr int kMaxBlocks = 64;         // largest n_blocks
+
+template <int D, bool F32>
+struct PsCfg {
+  static constexpr int Elem = F32 ? 4 : 2;
+  static constexpr int KStr = F32 ? D + 4 : D + 8;  // K tile row stride (elements)
+  static constexpr int KK = F32 ? D / 4 : D / 32;   // MFMA steps over d
+  static constexpr int CPR = D * Elem / 16;         // 16-byte chunks per row
+  static constexpr int LPT = kBN * CPR / kThreads;  // chunks per thread per tile
+};
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Loads of data this kernel wrote earlier (candidate buffers): agent-scope atomic loads do not
+// return stale copies from the per-CU cache.  Callers first complete their own stores with a
+// workgroup-scope release fence.
+__device__ __forceinline__ unsigned long long ld_coherent(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-wide: scanning 256 LDS bins from the top, the bin holding the k-th largest element, the
+// rank of that element inside the bin, and the bin's count.
+__device__ __forceinline__ void wave_find_bin(const uint32_t* h, int k, int lane, int* bin,
+                                              int* kr, uint32_t* bin_count) {
+  uint32_t c[4], s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    c[q] = h[255 - 4 * lane - q];  // lane 0 owns the highest bins
+    s += c[q];
+  }
+  uint32_t incl = s;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += x;
+  }
+  const uint32_t excl = incl - s;
+  int my_bin = -1, my_kr = 0;
+  uint32_t my_cnt = 0;
+  if ((long long)excl < k && (long long)k <= (long long)incl) {
+    uint32_t cum = excl;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      if (my_bin < 0 && (long long)cum + c[q] >= k) {
+        my_bin = 255 - 4 * lane - q;
+        my_kr = k - (int)cum;
+        my_cnt = c[q];
+      }
+      cum += c[q];
+    }
+  }
+  const unsigned long long who = __ballot(my_bin >= 0);
+  const int src = who ? (__ffsll((long long)who) - 1) : 0;
+  *bin = __shfl(my_bin, src, 64);
+  *kr = __shfl(my_kr, src, 64);
+  *bin_count = __shfl(my_cnt, src, 64);
+}
+
+// Keep exactly the k largest of the n (> k) entries of `buf`; returns the new threshold theta
+// (entries >= theta are the ones kept, compacted to buf[0..k)).  Wave-wide.  If `sorted_pos`
+// is given, the kept positions (~low word) are also written there, unordered.
+__device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k, int lane,
+                                           uint32_t* hist, int* kept_pos) {
+  unsigned long long v[kNPL];
+#pragma unroll
+  for (int i = 0; i < kNPL; i++) {
+    const int idx = lane + 64 * i;
+    v[i] = idx < n ? ld_coherent(buf + idx) : 0ull;
+  }
+  unsigned long long prefix = 0ull, pmask = 0ull;
+  int kk = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) hist[4 * lane + q] = 0u;
+    wave_sync_lds();
+#pragma unroll
+    for (int i = 0; i < kNPL; i++)
+      if (v[i] != 0ull && (v[i] & pmask) == prefix) atomicAdd(&hist[(v[i] >> shift) & 255ull], 1u);
+    wave_sync_lds();
+    int bin, kr;
+    uint32_t cnt;
+    wave_find_bin(hist, kk, lane, &bin, &kr, &cnt);
+    prefix |= (unsigned long long)bin << shift;
+    pmask |= 255ull << shift;
+    kk = kr;
+    wave_sync_lds();
+    if (cnt == (uint32_t)kr) break;  // the bin is taken whole: V >= prefix selects exactly k
+  }
+  const unsigned long long theta = prefix;
+  int base = 0;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < kNPL; i++) {
+    const bool keep = v[i] != 0ull && v[i] >= theta;
+    const unsigned long long bm = __ballot(keep);
+    const int slot = base + __popcll(bm & below);
+    if (keep) {
+      buf[slot] = v[i];
+      if (kept_pos) kept_pos[slot] = (int)(0xFFFFFFFFu - (uint32_t)(v[i] & 0xFFFFFFFFull));
+    }
+    base += __popcll(bm);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // stores complete before reloads
+  return theta;
+}
+
+// Ascending bitonic sort of M (a power of two) ints in this wave's LDS area.
+__device__ void wave_bitonic_sort(int* a, int M, int lane) {
+  for (int kk = 2; kk <= M; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int i = lane; i < M; i += 64) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const int x = a[i], y = a[ixj];
+          const bool up = (i & kk) == 0;
+          if ((x > y) == up) {
+            a[i] = y;
+            a[ixj] = x;
+          }
+        }
+      }
+      wave_sync_lds();
+    }
+  }
+}
+
+template <int D, bool F32, bool BLOCK>
+__global__ __launch_bounds__(kThreads, 1) void pf_select_kernel(PrefillSelectParams p) {
+  using C = PsCfg<D, F32>;
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kBN * C::KStr * C::Elem];
+  __shared__ uint32_t whist[8][256];
+  __shared__ unsigned long long qtheta[8][8];  // token mode: running threshold per query
+  __shared__ int qcount[8][8];                 // token: buffer fill; block: list fill
+  __shared__ unsigned long long blist[BLOCK ? 64 : 1][BLOCK ? kMaxBlocks : 1];
+  __shared__ int sortbuf[BLOCK ? 1 : 8][BLOCK ? 1 : kSortCap];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rn = lane & 15, jg = lane >> 4;
+  const int G = p.g / 4;          // lane groups per query (g = 4, 8, 16)
+  const int QR = 4 / G;           // queries per 16-row block
+  const int qpw = kRowsWG / p.g;  // queries per workgroup
+  const int n_qt = (p.Tq + qpw - 1) / qpw;
+  const int u = blockIdx.x % p.Hkv;
+  const int qt = n_qt - 1 - (int)((blockIdx.x / p.Hkv) % n_qt);
+  const int b = blockIdx.x / (p.Hkv * n_qt);
+  const int j0 = qt * qpw;
+  const int nq = min(qpw, p.Tq - j0);
+  const long long t_max = p.q_off + j0 + nq - 1;
+
+  // Q rows (A operand) and the per-row shift delta = LSE * log2 e - C
+  constexpr int KK = C::KK;
+  bf16x8 qa[2][F32 ? 1 : KK];
+  float qf[2][F32 ? KK : 1];
+  float delta[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++) {
+    const int r = wave * 32 + rb * 16 + rn;
+    const int jq = r / p.g, hh = r % p.g;
+    const bool ok = jq < nq;
+    const size_t qoff = (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + u * p.g + hh) * D;
+    if constexpr (!F32) {
+      const uint16_t* qp = (const uint16_t*)p.q + qoff;
+#pragma unroll
+      for (int kk = 0; kk < KK; kk++) {
+        u32x4 raw = ok ? *(const u32x4*)(qp + 32 * kk + 8 * jg) : u32x4{0, 0, 0, 0};
+        qa[rb][kk] = __builtin_bit_cast(bf16x8, raw);
+      }
+    } else {
+      const float* qp = (const float*)p.q + qoff + jg * KK;
+#pragma unroll
+      for (int s = 0; s < KK; s++) qf[rb][s] = ok ? qp[s] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int r2 = wave * 32 + rb * 16 + 4 * jg + e;
+      const int jq2 = r2 / p.g, hh2 = r2 % p.g;
+      if (jq2 < nq) {
+        const int j = j0 + jq2;
+        const double l2 = (double)p.lse[((size_t)b * p.Hq + u * p.g + hh2) * p.Tq + j] * 1.4426950408889634;
+        const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
+        delta[rb][e] = (float)(l2 - Cq);
+      } else {
+        delta[rb][e] = INFINITY;  // rows past the last query never win the max
+      }
+    }
+  }
+  // this lane's query in each row block: workgroup query index, position, candidate limit
+  int qj[2];
+  long long t_q[2];
+  bool q_ok[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++) {
+    qj[rb] = (wave * 32 + rb * 16) / p.g + jg / G;
+    q_ok[rb] = qj[rb] < nq;
+    t_q[rb] = p.q_off + j0 + qj[rb];
+  }
+  if (lane < 2 * QR) {
+    qtheta[wave][lane] = 0ull;
+    qcount[wave][lane] = 0;
+  }
+
+  const size_t kv_row_stride = (size_t)p.Hkv * D;
+  const unsigned char* kbase =
+      (const unsigned char*)p.k + ((size_t)b * p.Tk * p.Hkv + u) * D * C::Elem;
+  const long long key_last = BLOCK ? t_max : t_max - p.window;  // last key any query needs
+  const int n_tiles = key_last < 0 ? 0 : (int)(key_last / kBN + 1);
+  u32x4 kreg[C::LPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < C::LPT; i++) {
+      const int c = threadIdx.x + kThreads * i;
+      const int row = c / C::CPR, ch = c % C::CPR;
+      long long key = (long long)t * kBN + row;
+      if (key > key_last) key = key_last;
+      kreg[i] = *(const u32x4*)(kbase + ((size_t)key * kv_row_stride) * C::Elem + ch * 16);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::LPT; i++) {
+      const int c = threadIdx.x + kThreads * i;
+      const int row = c / C::CPR, ch = c % C::CPR;
+      *(u32x4*)(&ktile[buf][(row * C::KStr) * C::Elem + ch * 16]) = kreg[i];
+    }
+  };
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // lanes of this lane's query inside a 16-row block: all (g=16), a half (g=8), a quarter (g=4)
+  const unsigned long long qmask =
+      (G == 4) ? ~0ull : ((G == 2) ? (0xFFFFFFFFull << (32 * (jg / 2))) : (0xFFFFull << (16 * jg)));
+  const bool q_leader = (jg % G) == 0 && rn == 0;
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t++) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const long long key0 = (long long)t * kBN;
+
+    if constexpr (!BLOCK) {
+      // make room: compact every nearly full buffer of this wave's queries
+      for (int wq = 0; wq < 2 * QR; wq++) {
+        const int jq = wave * 2 * QR + wq;
+        if (jq < nq && qcount[wave][wq] > kBufCap - kBN) {
+          const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
+          const unsigned long long th = wave_compact(p.tbuf + (size_t)row * kBufCap,
+                                                     qcount[wave][wq], p.k_global, lane,
+                                                     whist[wave], nullptr);
+          wave_sync_lds();
+          if (lane == 0) {
+            qtheta[wave][wq] = th;
+            qcount[wave][wq] = p.k_global;
+          }
+          wave_sync_lds();
+        }
+      }
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) {
+      const int wq = rb * QR + jg / G;  // this lane's query within the wave
+      float group_best = -INFINITY;     // block mode: running max over the current block
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!F32) {
+          const uint16_t* kt = (const uint16_t*)ktile[buf];
+#pragma unroll
+          for (int kk = 0; kk < KK; kk++) {
+            const bf16x8 kbv = *(const bf16x8*)(kt + (16 * kb + rn) * C::KStr + 32 * kk + 8 * jg);
+            acc = mfma_bf16(qa[rb][kk], kbv, acc);
+          }
+        } else {
+          const float* kt = (const float*)ktile[buf];
+#pragma unroll
+          for (int s = 0; s < KK; s++) acc = mfma_f32(qf[rb][s], kt[(16 * kb + rn) * C::KStr + jg * KK + s], acc);
+        }
+        float v = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[e], p.scale_log2, -delta[rb][e]));
+        if (G >= 2) v = fmaxf(v, __shfl_xor(v, 16, 64));
+        if (G >= 4) v = fmaxf(v, __shfl_xor(v, 32, 64));
+        const long long g0 = key0 + 16 * kb;  // first key of this 16-key group
+        const long long pos = g0 + rn;
+        if constexpr (!BLOCK) {
+          // lane (key, group) owns key blocks kb with kb % G == jg % G of its query
+          bool take = false;
+          unsigned long long V = 0ull;
+          if ((kb % G) == (jg % G) && q_ok[rb] && pos <= t_q[rb] - p.window) {
+            V = ((unsigned long long)float_key(v) << 32) |
+                (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
+            take = V >= qtheta[wave][wq];
+          }
+          const unsigned long long bm = __ballot(take);
+          if (bm) {
+            if (take) {
+              const long long row = ((long long)b * p.Tq + j0 + qj[rb]) * p.Hkv + u;
+              const int slot = qcount[wave][wq] + __popcll(bm & qmask & below);
+              p.tbuf[(size_t)row * kBufCap + slot] = V;
+            }
+            wave_sync_lds();
+            if (q_leader) qcount[wave][wq] += __popcll(bm & qmask);
+            wave_sync_lds();
+          }
+        } else {
+          // max over the group's 16 keys (masked past the query), folded into the block
+          float bv = (q_ok[rb] && pos <= t_q[rb]) ? v : -INFINITY;
+          bv = fmaxf(bv, __shfl_xor(bv, 1, 64));
+          bv = fmaxf(bv, __shfl_xor(bv, 2, 64));
+          bv = fmaxf(bv, __shfl_xor(bv, 4, 64));
+          bv = fmaxf(bv, __shfl_xor(bv, 8, 64));
+          group_best = fmaxf(group_best, bv);
+          const bool live = q_ok[rb] && g0 <= t_q[rb];
+          const bool block_end = ((g0 + 16) % p.block) == 0 || g0 + 15 >= t_q[rb];
+          if (live && block_end) {
+            if (q_leader) {
+              const long long blk = g0 / p.block;
+              const unsigned long long V = ((unsigned long long)float_key(group_best) << 32) |
+                                           (unsigned long long)(0xFFFFFFFFu - (uint32_t)blk);
+              unsigned long long* L = blist[wave * 8 + wq];
+              const int n = qcount[wave][wq];
+              if (n < p.n_blocks) {
+                L[n] = V;
+                qcount[wave][wq] = n + 1;
+              } else {
+                int mi = 0;
+                for (int i = 1; i < p.n_blocks; i++)
+                  if (L[i] < L[mi]) mi = i;
+                if (V > L[mi]) L[mi] = V;
+              }
+            }
+          }
+          if (block_end) group_best = -INFINITY;
+        }
+      }
+    }
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- outputs, one query at a time per wave ----
+  for (int wq = 0; wq < 2 * QR; wq++) {
+    const int jq = wave * 2 * QR + wq;
+    if (jq >= nq) break;
+    const long long t = p.q_off + j0 + jq;
+    const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
+    if constexpr (!BLOCK) {
+      const long long n_cand = t - p.window + 1 > 0 ? t - p.window + 1 : 0;
+      const int k_eff = (int)(n_cand < p.k_global ? n_cand : p.k_global);
+      unsigned long long* bufq = p.tbuf + (size_t)row * kBufCap;
+      int* sb = sortbuf[wave];
+      const int n = qcount[wave][wq];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // appends complete before reloads
+      if (n > k_eff) {
+        wave_compact(bufq, n, k_eff, lane, whist[wave], sb);
+      } else {
+        for (int i = lane; i < n; i += 64)
+          sb[i] = (int)(0xFFFFFFFFu - (uint32_t)(ld_coherent(bufq + i) & 0xFFFFFFFFull));
+      }
+      int M = 1;
+      while (M < k_eff) M <<= 1;
+      for (int i = k_eff + lane; i < M; i += 64) sb[i] = 0x7FFFFFFF;
+      wave_sync_lds();
+      wave_bitonic_sort(sb, M, lane);
+      int32_t* out = p.idx + (size_t)row * p.cap;
+      const long long w0 = t - p.window + 1 > 0 ? t - p.window + 1 : 0;
+      const int n_win = (int)(t - w0 + 1);
+      for (int i = lane; i < p.cap; i += 64) {
+        int32_t val = -1;
+        if (i < k_eff) val = sb[i];
+        else if (i < k_eff + n_win) val = (int32_t)(w0 + (i - k_eff));
+        out[i] = val;
+      }
+      if (lane == 0) p.cnt[row] = k_eff + n_win;
+      wave_sync_lds();
+    } else {
+      const long long nb = t / p.block + 1;
+      const int n_take = (int)(nb < p.n_blocks ? nb : p.n_blocks);
+      const unsigned long long* L = blist[wave * 8 + wq];
+      int32_t* out = p.idx + (size_t)row * p.n_blocks;
+      if (lane < p.n_blocks) {
+        if (lane < n_take) {
+          const int id = (int)(0xFFFFFFFFu - (uint32_t)(L[lane] & 0xFFFFFFFFull));
+          int rank = 0;
+          for (int o = 0; o < n_take; o++)
+            rank += (int)(0xFFFFFFFFu - (uint32_t)(L[o] & 0xFFFFFFFFull)) < id;
+          out[rank] = id;
+        } else {
+          out[lane] = -1;
+        }
+      }
+      if (lane == 0) p.cnt[row] = n_take;
+    }
+  }
+}
+
+}  // namespace
+
+int prefill_select_buffer_cap() { return kBufCap; }
+int prefill_select_max_k() { return kSortCap; }
+
+hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
+                                 bool block_mode, hipStream_t stream) {
+  const int qpw = kRowsWG / p.g;
+  const int n_qt = (p.Tq + qpw - 1) / qpw;
+  const dim3 grid(p.B * p.Hkv * n_qt);
+#define HS_LAUNCH(D, F, BL) pf_select_kernel<D, F, BL><<<grid, kThreads, 0, stream>>>(p)
+  if (head_dim == 128) {
+    if (in_f32) {
+      if (block_mode) HS_LAUNCH(128, true, true); else HS_LAUNCH(128, true, false);
+    } else {
+      if (block_mode) HS_LAUNCH(128, false, true); else HS_LAUNCH(128, false, false);
+    }
+  } else {
+    if (in_f32) {
+      if (block_mode) HS_LAUNCH(64, true, true); else HS_LAUNCH(64, true, false);
+    } else {
+      if (block_mode) HS_LAUNCH(64, false, true); else HS_LAUNCH(64, false, false);
+    }
+  }
+#undef HS_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace hs

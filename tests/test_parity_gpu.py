@@ -84,6 +84,11 @@ TOPK_CASES = [
                                        window=20, seed=23)),
     ("prefill_g4_cross_cap", Workload("pfx", 1, 48, 1200, 8, 2, 128, "bf16", k_global=1024,
                                       window=128, seed=24)),
+    # prefill selection: more than 2048 candidates per query forces buffer compactions
+    ("prefill_g16_compactions", Workload("pfc", 1, 40, 6000, 32, 2, 128, "bf16",
+                                         k_global=1024, window=128, seed=25)),
+    ("prefill_g8_d64_small_k", Workload("pf8", 2, 100, 3000, 16, 2, 64, "bf16", k_global=50,
+                                        window=10, seed=26)),
 ]
 
 
@@ -108,6 +113,37 @@ def test_oracle_topk_matches_oracle(name, wl):
                 assert set(x["needle_pos"][b, u].tolist()) <= sel
 
 
+@pytest.mark.parametrize("q_len", [1, 33])
+def test_token_selection_exact_ties_prefer_lower_position(q_len):
+    """Exactly equal scores: both selection paths (few and many query rows) must keep the lower
+    positions, as the oracle does."""
+    wl = Workload("ties", 1, q_len, 3000, 8, 2, 128, "bf16", k_global=50, window=16, seed=61)
+    say(f"[topk ties] q_len={q_len}")
+    x = make_inputs(wl)
+    k = x["k"].clone()
+    # one needle for head 0 of KV head 0 copied to 81 positions (500, 1000..1079): each copy gets
+    # p ~ 1/81, above every other key of the group, so the 50 selected candidates are all copies
+    # and the tie rule alone decides which (the lowest positions)
+    qh = x["q"][0, -1, 0].float()
+    k[0, 500, 0] = (8.0 * 128 ** 0.5 * qh / (qh * qh).sum()).to(k.dtype)
+    k[0, 1000:1080, 0] = k[0, 500, 0]
+    k[0, 100:700, 1] = k[0, 1000:1600, 1]  # scattered ties for KV head 1
+    qn, kn = to_numpy_f32(x["q"]), to_numpy_f32(k)
+    q_d, k_d, v_d = to_dev(x["q"]), to_dev(k), to_dev(x["v"])
+    _, lse = hs().full_attn_fwd(q_d, k_d, v_d)
+    idx, cnt = hs().oracle_topk(q_d, k_d, lse, wl.k_global, wl.window)
+    torch.cuda.synchronize()
+    _, lse_ref = oracle.full_attention(qn, kn, to_numpy_f32(x["v"]))
+    oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    want = np.array([500] + list(range(1000, 1049)))
+    assert np.array_equal(oi[0, -1, 0, :50], want)
+    assert np.array_equal(gi[0, -1, 0, :50], want)
+    excused = check_token_sets(gi, gc, oi, oc, qn, kn, lse_ref, wl.k_global, wl.window,
+                               wl.q_offset)
+    say(f"  near-tie differences excused: {excused}")
+
+
 # ---- block scores + top-n blocks ----------------------------------------------------------
 
 BLOCK_CASES = [
@@ -118,6 +154,12 @@ BLOCK_CASES = [
                                 seed=53)),
     ("prefill_g8_b32", Workload("bp", 1, 37, 2000, 16, 2, 64, "bf16", block=32, n_blocks=7,
                                 seed=54)),
+    ("prefill_g16_b64", Workload("bp16", 1, 50, 4000, 32, 2, 128, "bf16", block=64,
+                                 n_blocks=16, seed=55)),
+    ("prefill_g4_b64_causal", Workload("bp4", 2, 300, 300, 8, 2, 128, "bf16", block=64,
+                                       n_blocks=3, seed=56)),
+    ("prefill_g4_b128_generic", Workload("bpg", 1, 30, 1500, 8, 2, 128, "bf16", block=128,
+                                         n_blocks=5, seed=57)),
 ]
 
 
