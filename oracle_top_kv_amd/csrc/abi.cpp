@@ -227,7 +227,8 @@ size_t tk_ws(const Shape& s, const TkGeom& t) { return tk_layout(s, t).total; }
 
 // Many query rows per KV head: selection streams over K tiles and stores no per-key score.
 bool use_prefill_select(const Shape& s, int k_global) {
-  return (long long)s.Tq * s.g > 16 && k_global <= hs::prefill_select_max_k();
+  return (long long)s.Tq * s.g > 16 && (s.g == 4 || s.g == 8 || s.g == 16) &&
+         k_global <= hs::prefill_select_max_k();
 }
 
 size_t tk_prefill_ws(const Shape& s) {

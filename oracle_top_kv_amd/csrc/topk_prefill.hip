@@ -11,9 +11,10 @@
 // lower position.
 //
 // Tiling: a workgroup owns 256 (query, head) rows of one KV head (256/g queries, all g heads),
-// 8 waves of 32 rows; 64-key K tiles are double-buffered in LDS and shared by all rows.
-// S = Q K^T on MFMA (A = Q rows resident, B = K^T from LDS) leaves the g head values of one key
-// in one lane row, so the group maximum is an in-lane max plus at most two shuffles.
+// 4 waves of 64 rows; 64-key K tiles are double-buffered in LDS and shared by all rows.
+// S = Q K^T on MFMA (A = Q rows resident, B = K^T from LDS).  Rows are packed so that a lane
+// holds, for one key, four heads of one query in each of the g/4 MFMA blocks of that query:
+// the group maximum over the heads is taken inside the lane, with no cross-lane traffic.
 //
 // Token mode: each query keeps a candidate buffer (2048 entries) in the workspace.  A key enters
 // it if it is a candidate (position <= t - w) and V >= theta, the query's running threshold.
@@ -30,7 +31,7 @@
 namespace hs {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;  // 4 waves of 64 rows
 constexpr int kRowsWG = 256;
 constexpr int kBN = 64;
 constexpr int kBufCap = 2048;          // token candidates per query
@@ -164,21 +165,32 @@ __device__ void wave_bitonic_sort(int* a, int M, int lane) {
   }
 }
 
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 template <int D, bool F32, bool BLOCK>
-__global__ __launch_bounds__(kThreads, 1) void pf_select_kernel(PrefillSelectParams p) {
+__global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectParams p) {
   using C = PsCfg<D, F32>;
+  constexpr int NW = kThreads / 64;      // waves
+  constexpr int QMAX = 16;               // queries per wave at most (g = 4)
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kBN * C::KStr * C::Elem];
-  __shared__ uint32_t whist[8][256];
-  __shared__ unsigned long long qtheta[8][8];  // token mode: running threshold per query
-  __shared__ int qcount[8][8];                 // token: buffer fill; block: list fill
-  __shared__ unsigned long long blist[BLOCK ? 64 : 1][BLOCK ? kMaxBlocks : 1];
-  __shared__ int sortbuf[BLOCK ? 1 : 8][BLOCK ? 1 : kSortCap];
+  __shared__ uint32_t whist[NW][256];
+  __shared__ unsigned long long qtheta[NW][QMAX];  // token: running threshold per query
+  __shared__ int qcount[NW][QMAX];                 // token: buffer fill; block: list fill
+  __shared__ unsigned long long blist[BLOCK ? NW * QMAX : 1][BLOCK ? kMaxBlocks : 1];
+  __shared__ int sortbuf[BLOCK ? 1 : NW][BLOCK ? 1 : kSortCap];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rn = lane & 15, jg = lane >> 4;
-  const int G = p.g / 4;          // lane groups per query (g = 4, 8, 16)
-  const int QR = 4 / G;           // queries per 16-row block
-  const int qpw = kRowsWG / p.g;  // queries per workgroup
+  // Row packing, head-quarter major: the wave's 64 rows are 4 MFMA blocks; block rb holds heads
+  // 4hq..4hq+3 of the 4 queries of query group qg (rb = qg * HQ + hq), MFMA row 4j+e being
+  // query 4qg+j, head 4hq+e.  The S = Q K^T output then gives lane (key, j) heads 4hq..4hq+3 of
+  // query 4qg+j in every block of the group: the group maximum over all g heads is in-lane.
+  const int HQ = p.g / 4;          // head quarters per query (g = 4, 8, 16)
+  const int QG = 4 / HQ;           // query groups per wave
+  const int QW = 4 * QG;           // queries per wave (64 / g)
+  const int qpw = NW * QW;         // queries per workgroup (256 / g)
   const int n_qt = (p.Tq + qpw - 1) / qpw;
   const int u = blockIdx.x % p.Hkv;
   const int qt = n_qt - 1 - (int)((blockIdx.x / p.Hkv) % n_qt);
@@ -186,58 +198,64 @@ __global__ __launch_bounds__(kThreads, 1) void pf_select_kernel(PrefillSelectPar
   const int j0 = qt * qpw;
   const int nq = min(qpw, p.Tq - j0);
   const long long t_max = p.q_off + j0 + nq - 1;
+  const int wq0 = wave * QW;  // first workgroup query of this wave
 
-  // Q rows (A operand) and the per-row shift delta = LSE * log2 e - C
   constexpr int KK = C::KK;
-  bf16x8 qa[2][F32 ? 1 : KK];
-  float qf[2][F32 ? KK : 1];
-  float delta[2][4];
+  bf16x8 qa[4][F32 ? 1 : KK];
+  float qf[4][F32 ? KK : 1];
+  float delta[4][4];
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
-    const int r = wave * 32 + rb * 16 + rn;
-    const int jq = r / p.g, hh = r % p.g;
-    const bool ok = jq < nq;
-    const size_t qoff = (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + u * p.g + hh) * D;
-    if constexpr (!F32) {
-      const uint16_t* qp = (const uint16_t*)p.q + qoff;
+  for (int rb = 0; rb < 4; rb++) {
+    const int qg = rb / HQ, hq = rb % HQ;
+    {  // A operand: lane row rn = 4j + e -> query 4qg + j, head 4hq + e
+      const int jq = wq0 + 4 * qg + rn / 4;
+      const int hh = 4 * hq + rn % 4;
+      const bool ok = jq < nq;
+      const size_t qoff = (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + u * p.g + hh) * D;
+      if constexpr (!F32) {
+        const uint16_t* qp = (const uint16_t*)p.q + qoff;
 #pragma unroll
-      for (int kk = 0; kk < KK; kk++) {
-        u32x4 raw = ok ? *(const u32x4*)(qp + 32 * kk + 8 * jg) : u32x4{0, 0, 0, 0};
-        qa[rb][kk] = __builtin_bit_cast(bf16x8, raw);
-      }
-    } else {
-      const float* qp = (const float*)p.q + qoff + jg * KK;
-#pragma unroll
-      for (int s = 0; s < KK; s++) qf[rb][s] = ok ? qp[s] : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const int r2 = wave * 32 + rb * 16 + 4 * jg + e;
-      const int jq2 = r2 / p.g, hh2 = r2 % p.g;
-      if (jq2 < nq) {
-        const int j = j0 + jq2;
-        const double l2 = (double)p.lse[((size_t)b * p.Hq + u * p.g + hh2) * p.Tq + j] * 1.4426950408889634;
-        const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
-        delta[rb][e] = (float)(l2 - Cq);
+        for (int kk = 0; kk < KK; kk++) {
+          u32x4 raw = ok ? *(const u32x4*)(qp + 32 * kk + 8 * jg) : u32x4{0, 0, 0, 0};
+          qa[rb][kk] = __builtin_bit_cast(bf16x8, raw);
+        }
       } else {
-        delta[rb][e] = INFINITY;  // rows past the last query never win the max
+        const float* qp = (const float*)p.q + qoff + jg * KK;
+#pragma unroll
+        for (int s2 = 0; s2 < KK; s2++) qf[rb][s2] = ok ? qp[s2] : 0.f;
+      }
+    }
+    {  // output rows of lane group jg: query 4qg + jg, heads 4hq + e
+      const int jq = wq0 + 4 * qg + jg;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        if (jq < nq) {
+          const int j = j0 + jq, hh = 4 * hq + e;
+          const double l2 = (double)p.lse[((size_t)b * p.Hq + u * p.g + hh) * p.Tq + j] * 1.4426950408889634;
+          const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
+          delta[rb][e] = (float)(l2 - Cq);
+        } else {
+          delta[rb][e] = INFINITY;  // queries past the last one never score
+        }
       }
     }
   }
-  // this lane's query in each row block: workgroup query index, position, candidate limit
-  int qj[2];
-  long long t_q[2];
-  bool q_ok[2];
+  // this lane's query in each query group
+  long long t_q[4];
+  bool q_ok[4];
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
-    qj[rb] = (wave * 32 + rb * 16) / p.g + jg / G;
-    q_ok[rb] = qj[rb] < nq;
-    t_q[rb] = p.q_off + j0 + qj[rb];
+  for (int qg = 0; qg < 4; qg++) {
+    const int jq = wq0 + 4 * qg + jg;
+    q_ok[qg] = qg < QG && jq < nq;
+    t_q[qg] = p.q_off + j0 + jq;
   }
-  if (lane < 2 * QR) {
+  if (lane < QW) {
     qtheta[wave][lane] = 0ull;
     qcount[wave][lane] = 0;
   }
+  // token mode: this lane's copy of its queries' thresholds (exact 64-bit and a float filter)
+  unsigned long long th[4] = {0ull, 0ull, 0ull, 0ull};
+  float thf[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 
   const size_t kv_row_stride = (size_t)p.Hkv * D;
   const unsigned char* kbase =
@@ -264,10 +282,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_select_kernel(PrefillSelectPar
     }
   };
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // lanes of this lane's query inside a 16-row block: all (g=16), a half (g=8), a quarter (g=4)
-  const unsigned long long qmask =
-      (G == 4) ? ~0ull : ((G == 2) ? (0xFFFFFFFFull << (32 * (jg / 2))) : (0xFFFFull << (16 * jg)));
-  const bool q_leader = (jg % G) == 0 && rn == 0;
+  const unsigned long long qmask = 0xFFFFull << (16 * jg);  // lanes of this lane's query
+  float bmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // block mode running maxima
 
   if (n_tiles > 0) {
     load_tile(0);
@@ -281,85 +297,111 @@ __global__ __launch_bounds__(kThreads, 1) void pf_select_kernel(PrefillSelectPar
 
     if constexpr (!BLOCK) {
       // make room: compact every nearly full buffer of this wave's queries
-      for (int wq = 0; wq < 2 * QR; wq++) {
-        const int jq = wave * 2 * QR + wq;
+      bool any = false;
+      for (int wq = 0; wq < QW; wq++) {
+        const int jq = wq0 + wq;
         if (jq < nq && qcount[wave][wq] > kBufCap - kBN) {
           const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
-          const unsigned long long th = wave_compact(p.tbuf + (size_t)row * kBufCap,
-                                                     qcount[wave][wq], p.k_global, lane,
-                                                     whist[wave], nullptr);
+          const unsigned long long tnew = wave_compact(p.tbuf + (size_t)row * kBufCap,
+                                                       qcount[wave][wq], p.k_global, lane,
+                                                       whist[wave], nullptr);
           wave_sync_lds();
           if (lane == 0) {
-            qtheta[wave][wq] = th;
+            qtheta[wave][wq] = tnew;
             qcount[wave][wq] = p.k_global;
           }
           wave_sync_lds();
+          any = true;
+        }
+      }
+      if (any) {
+#pragma unroll
+        for (int qg = 0; qg < 4; qg++) {
+          if (qg < QG) {
+            th[qg] = qtheta[wave][4 * qg + jg];
+            const uint32_t hi = (uint32_t)(th[qg] >> 32);
+            thf[qg] = hi ? key_to_float(hi) : -INFINITY;
+          }
         }
       }
     }
 
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
-      const int wq = rb * QR + jg / G;  // this lane's query within the wave
-      float group_best = -INFINITY;     // block mode: running max over the current block
+    for (int kb = 0; kb < 4; kb++) {
+      f32x4 acc[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; kb++) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (!F32) {
-          const uint16_t* kt = (const uint16_t*)ktile[buf];
+      for (int rb = 0; rb < 4; rb++) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (!F32) {
+        const uint16_t* kt = (const uint16_t*)ktile[buf];
 #pragma unroll
-          for (int kk = 0; kk < KK; kk++) {
-            const bf16x8 kbv = *(const bf16x8*)(kt + (16 * kb + rn) * C::KStr + 32 * kk + 8 * jg);
-            acc = mfma_bf16(qa[rb][kk], kbv, acc);
-          }
-        } else {
-          const float* kt = (const float*)ktile[buf];
+        for (int kk = 0; kk < KK; kk++) {
+          const bf16x8 kbv = *(const bf16x8*)(kt + (16 * kb + rn) * C::KStr + 32 * kk + 8 * jg);
 #pragma unroll
-          for (int s = 0; s < KK; s++) acc = mfma_f32(qf[rb][s], kt[(16 * kb + rn) * C::KStr + jg * KK + s], acc);
+          for (int rb = 0; rb < 4; rb++) acc[rb] = mfma_bf16(qa[rb][kk], kbv, acc[rb]);
         }
+      } else {
+        const float* kt = (const float*)ktile[buf];
+#pragma unroll
+        for (int s2 = 0; s2 < KK; s2++) {
+          const float kv = kt[(16 * kb + rn) * C::KStr + jg * KK + s2];
+#pragma unroll
+          for (int rb = 0; rb < 4; rb++) acc[rb] = mfma_f32(qf[rb][s2], kv, acc[rb]);
+        }
+      }
+      const long long g0 = key0 + 16 * kb;
+      const long long pos = g0 + rn;
+#pragma unroll
+      for (int qg = 0; qg < 4; qg++) {
+        if (qg >= QG) break;
         float v = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[e], p.scale_log2, -delta[rb][e]));
-        if (G >= 2) v = fmaxf(v, __shfl_xor(v, 16, 64));
-        if (G >= 4) v = fmaxf(v, __shfl_xor(v, 32, 64));
-        const long long g0 = key0 + 16 * kb;  // first key of this 16-key group
-        const long long pos = g0 + rn;
+        for (int hq = 0; hq < 4; hq++) {
+          if (hq >= HQ) break;
+          const int rb = qg * HQ + hq;
+#pragma unroll
+          for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[rb][e], p.scale_log2, -delta[rb][e]));
+        }
         if constexpr (!BLOCK) {
-          // lane (key, group) owns key blocks kb with kb % G == jg % G of its query
           bool take = false;
-          unsigned long long V = 0ull;
-          if ((kb % G) == (jg % G) && q_ok[rb] && pos <= t_q[rb] - p.window) {
-            V = ((unsigned long long)float_key(v) << 32) |
-                (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
-            take = V >= qtheta[wave][wq];
+          if (q_ok[qg] && pos <= t_q[qg] - p.window && v >= thf[qg]) {
+            if (v > thf[qg]) {
+              take = true;
+            } else {  // equal to the float filter: decide on the exact 64-bit value
+              const unsigned long long V = ((unsigned long long)float_key(v) << 32) |
+                                           (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
+              take = V >= th[qg];
+            }
           }
           const unsigned long long bm = __ballot(take);
           if (bm) {
+            const int wq = 4 * qg + jg;
             if (take) {
-              const long long row = ((long long)b * p.Tq + j0 + qj[rb]) * p.Hkv + u;
+              const long long row = ((long long)b * p.Tq + j0 + wq0 + wq) * p.Hkv + u;
               const int slot = qcount[wave][wq] + __popcll(bm & qmask & below);
-              p.tbuf[(size_t)row * kBufCap + slot] = V;
+              p.tbuf[(size_t)row * kBufCap + slot] =
+                  ((unsigned long long)float_key(v) << 32) |
+                  (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
             }
             wave_sync_lds();
-            if (q_leader) qcount[wave][wq] += __popcll(bm & qmask);
+            if (rn == 0) qcount[wave][wq] += __popcll(bm & qmask);
             wave_sync_lds();
           }
         } else {
-          // max over the group's 16 keys (masked past the query), folded into the block
-          float bv = (q_ok[rb] && pos <= t_q[rb]) ? v : -INFINITY;
-          bv = fmaxf(bv, __shfl_xor(bv, 1, 64));
-          bv = fmaxf(bv, __shfl_xor(bv, 2, 64));
-          bv = fmaxf(bv, __shfl_xor(bv, 4, 64));
-          bv = fmaxf(bv, __shfl_xor(bv, 8, 64));
-          group_best = fmaxf(group_best, bv);
-          const bool live = q_ok[rb] && g0 <= t_q[rb];
-          const bool block_end = ((g0 + 16) % p.block) == 0 || g0 + 15 >= t_q[rb];
-          if (live && block_end) {
-            if (q_leader) {
-              const long long blk = g0 / p.block;
-              const unsigned long long V = ((unsigned long long)float_key(group_best) << 32) |
+          // running maximum of the current block (keys past the query are masked)
+          bmax[qg] = fmaxf(bmax[qg], (q_ok[qg] && pos <= t_q[qg]) ? v : -INFINITY);
+          if (((g0 + 16) % p.block) == 0) {  // block boundary: same for every lane
+            float bv = bmax[qg];
+            bv = fmaxf(bv, __shfl_xor(bv, 1, 64));
+            bv = fmaxf(bv, __shfl_xor(bv, 2, 64));
+            bv = fmaxf(bv, __shfl_xor(bv, 4, 64));
+            bv = fmaxf(bv, __shfl_xor(bv, 8, 64));
+            const long long bstart = g0 + 16 - p.block;
+            if (rn == 0 && q_ok[qg] && bstart <= t_q[qg]) {
+              const long long blk = bstart / p.block;
+              const unsigned long long V = ((unsigned long long)float_key(bv) << 32) |
                                            (unsigned long long)(0xFFFFFFFFu - (uint32_t)blk);
-              unsigned long long* L = blist[wave * 8 + wq];
+              const int wq = 4 * qg + jg;
+              unsigned long long* L = blist[wave * QMAX + wq];
               const int n = qcount[wave][wq];
               if (n < p.n_blocks) {
                 L[n] = V;
@@ -371,8 +413,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_select_kernel(PrefillSelectPar
                 if (V > L[mi]) L[mi] = V;
               }
             }
+            bmax[qg] = -INFINITY;
           }
-          if (block_end) group_best = -INFINITY;
         }
       }
     }
@@ -381,8 +423,8 @@ __global__ __launch_bounds__(kThreads, 1) void pf_select_kernel(PrefillSelectPar
   }
 
   // ---- outputs, one query at a time per wave ----
-  for (int wq = 0; wq < 2 * QR; wq++) {
-    const int jq = wave * 2 * QR + wq;
+  for (int wq = 0; wq < QW; wq++) {
+    const int jq = wq0 + wq;
     if (jq >= nq) break;
     const long long t = p.q_off + j0 + jq;
     const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
@@ -418,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_select_kernel(PrefillSelectPar
     } else {
       const long long nb = t / p.block + 1;
       const int n_take = (int)(nb < p.n_blocks ? nb : p.n_blocks);
-      const unsigned long long* L = blist[wave * 8 + wq];
+      const unsigned long long* L = blist[wave * QMAX + wq];
       int32_t* out = p.idx + (size_t)row * p.n_blocks;
       if (lane < p.n_blocks) {
         if (lane < n_take) {
@@ -443,7 +485,7 @@ int prefill_select_max_k() { return kSortCap; }
 
 hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
                                  bool block_mode, hipStream_t stream) {
-  const int qpw = kRowsWG / p.g;
+  const int qpw = kRowsWG / p.g;  // queries per workgroup
   const int n_qt = (p.Tq + qpw - 1) / qpw;
   const dim3 grid(p.B * p.Hkv * n_qt);
 #define HS_LAUNCH(D, F, BL) pf_select_kernel<D, F, BL><<<grid, kThreads, 0, stream>>>(p)
