@@ -302,14 +302,16 @@ size_t bk_ws(const BkGeom& g, int n_blocks) {
 // ---- sparse attention ----------------------------------------------------------------------
 struct SparseGeom {
   RaGeom glob, loc;
-  bool combine;
+  bool combine;  // split partials merged by the combine kernel
+  bool fused;    // gated layer with unsplit branches: both in one workgroup, no partials
 };
 
 SparseGeom sparse_geom(const Shape& s, long long keys_per_set, int window) {
   SparseGeom g;
   g.glob = ra_geom(s, true, keys_per_set, 4, kTargetWorkgroups, 64);
   g.loc = ra_geom(s, true, window > 0 ? window : 1, 4);
-  g.combine = window > 0 || g.glob.n_split > 1;
+  g.fused = window > 0 && g.glob.n_split == 1 && g.loc.n_split == 1;
+  g.combine = !g.fused && (window > 0 || g.glob.n_split > 1);
   return g;
 }
 
@@ -571,13 +573,22 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
   pg.o = o;
   pg.lse = lse_opt;
   pg.final_direct = !g.combine;
+  const hs::KeySrc src = kind == HS_IDX_TOKEN ? hs::SRC_TOKEN : hs::SRC_BLOCK;
+  if (g.fused) {
+    pg.k2 = swa->k_local;
+    pg.v2 = swa->v_local;
+    pg.window = window;
+    pg.gate = swa->gate_logits;
+    hipError_t e = hs::launch_row_attn(pg, s.D, s.in_f32, src, hst, true);
+    if (e != hipSuccess) return hip_status(e, "gated sparse attention kernel");
+    return ok();
+  }
   char* w = (char*)ws;
   if (g.combine) {
     carve_partials(w, g.glob, s.D, &pg.part_m, &pg.part_l, &pg.part_o);
     w += partial_bytes(g.glob, s.D);
   }
-  hipError_t e = hs::launch_row_attn(pg, s.D, s.in_f32,
-                                     kind == HS_IDX_TOKEN ? hs::SRC_TOKEN : hs::SRC_BLOCK, hst);
+  hipError_t e = hs::launch_row_attn(pg, s.D, s.in_f32, src, hst);
   if (e != hipSuccess) return hip_status(e, "sparse attention kernel");
   hs::RowAttnParams pl;
   if (window > 0) {

@@ -65,27 +65,29 @@ __device__ __forceinline__ int entry_pos(const RowAttnParams& p, int e, int L, l
   return x <= t_last ? (int)x : -1;
 }
 
-template <int D, bool F32, int SRC>
-__global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
-  using Cfg = RaCfg<D, F32>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::kSmem];
-  __shared__ int pos_all[kMaxListEntries];
+// Result of one pass over a key source, as held by the merge thread of row r, columns
+// c0 .. c0 + D/16 - 1 (r = threadIdx.x / 16, c0 = (threadIdx.x % 16) * D/16): the row maximum
+// M (log2 domain), the row sum L relative to M and the unnormalized output columns.
+template <int D>
+struct PassOut {
+  float M;
+  double L;
+  float ov[D / 16];
+};
 
+// One split of one row-set over one key source (K, V given explicitly so that the gated layer
+// can run its window branch over K', V' in the same workgroup).  Ends with the four waves
+// merged; `smem` and `pos_all` are free again once the caller has synchronized.
+template <int D, bool F32, int SRC>
+__device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* kmat,
+                                            const void* vmat, int split, int steps_per_split,
+                                            int b, int u, int j0, int nq, unsigned char* smem,
+                                            int* pos_all, PassOut<D>& out) {
+  using Cfg = RaCfg<D, F32>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rn = lane & 15;   // MFMA row / column index of this lane
   const int jg = lane >> 4;   // lane group 0..3
-  // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
-  // workgroups reading the same positions of the Hkv interleaved heads run together (whole
-  // [Hkv, d] rows of K and V are then consumed close in time).
-  const int u = blockIdx.x % p.Hkv;
-  const int split = (blockIdx.x / p.Hkv) % p.n_split;
-  const int bq = blockIdx.x / (p.Hkv * p.n_split);
-  const int sq = bq % p.sets_per_bu;
-  const int b = bq / p.sets_per_bu;
-  const int set = (b * p.Hkv + u) * p.sets_per_bu + sq;
-  const int j0 = sq * p.q_per_set;
-  const int nq = min(p.q_per_set, p.Tq - j0);
   const int nrows = nq * p.g;
   const long long t_first = p.q_off + j0;
   const long long t_last = p.q_off + j0 + nq - 1;
@@ -143,8 +145,8 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
   for (int db = 0; db < D / 16; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int n_steps = (L + kStep - 1) / kStep;
-  const int step_begin = split * p.steps_per_split;
-  const int step_end = min(step_begin + p.steps_per_split, n_steps);
+  const int step_begin = split * steps_per_split;
+  const int step_end = min(step_begin + steps_per_split, n_steps);
   unsigned char* vtile = smem + wave * Cfg::kVTileBytes;
 
   // Positions of this split's key-list entries.  List modes stage them in LDS once (so the
@@ -174,16 +176,16 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
   auto load_step = [&](int step, KReg (&k0)[KK], KReg (&k1)[KK], u32x4 (&vr)[VL]) {
     const int pk0 = pos_of(step, rn), pk1 = pos_of(step, 16 + rn);
     if constexpr (!F32) {
-      const uint16_t* kp0 = (const uint16_t*)p.k + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + 8 * jg;
-      const uint16_t* kp1 = (const uint16_t*)p.k + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + 8 * jg;
+      const uint16_t* kp0 = (const uint16_t*)kmat + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + 8 * jg;
+      const uint16_t* kp1 = (const uint16_t*)kmat + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + 8 * jg;
 #pragma unroll
       for (int kk = 0; kk < KK; kk++) {
         k0[kk] = *(const u32x4*)(kp0 + 32 * kk);
         k1[kk] = *(const u32x4*)(kp1 + 32 * kk);
       }
     } else {
-      const float* kp0 = (const float*)p.k + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + jg * KK;
-      const float* kp1 = (const float*)p.k + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + jg * KK;
+      const float* kp0 = (const float*)kmat + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + jg * KK;
+      const float* kp1 = (const float*)kmat + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + jg * KK;
 #pragma unroll
       for (int s2 = 0; s2 < KK; s2++) {
         k0[s2] = kp0[s2];
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
       const int c = n * 64 + lane;
       const int e = c / Cfg::kChunksPerRow, qc = c % Cfg::kChunksPerRow;
       const int pv = pos_of(step, e);
-      const unsigned char* vp = (const unsigned char*)p.v +
+      const unsigned char* vp = (const unsigned char*)vmat +
           (kv_base + (size_t)(pv < 0 ? 0 : pv) * kv_row_stride) * Cfg::kElem + qc * 16;
       vr[n] = ld_stream(vp);
     }
@@ -336,42 +338,94 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
     f[w] = (mw == -INFINITY) ? 0.f : (float)exp2((double)mw - (double)M);
     Ls += (mw == -INFINITY) ? 0.0 : exp2((double)mw - (double)M) * cL[w * 16 + r];
   }
-  float ov[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; c++) {
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; w++) acc += f[w] * cO[(w * 16 + r) * D + c0 + c];
-    ov[c] = acc;
+    out.ov[c] = acc;
   }
-  if (r >= nrows) return;
+  out.M = M;
+  out.L = Ls;
+}
+
+template <int D>
+__device__ __forceinline__ float lse_of(const PassOut<D>& a) {
+  return (a.L > 0.0) ? (float)(((double)a.M + log2(a.L)) * kLn2) : -INFINITY;
+}
+
+// GATED: the HySparse sparse layer in one workgroup when neither branch is split -- the block
+// (or token) branch over K, V, then the sliding-window branch over K', V' (p.k2, p.v2), each
+// normalized on its own and weighted by its sigmoid gate [P2 "Same query, two memories"].
+template <int D, bool F32, int SRC, bool GATED>
+__global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
+  using Cfg = RaCfg<D, F32>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::kSmem];
+  __shared__ int pos_all[kMaxListEntries];
+
+  // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
+  // workgroups reading the same positions of the Hkv interleaved heads run together (whole
+  // [Hkv, d] rows of K and V are then consumed close in time).
+  const int u = blockIdx.x % p.Hkv;
+  const int split = (blockIdx.x / p.Hkv) % p.n_split;
+  const int bq = blockIdx.x / (p.Hkv * p.n_split);
+  const int sq = bq % p.sets_per_bu;
+  const int b = bq / p.sets_per_bu;
+  const int set = (b * p.Hkv + u) * p.sets_per_bu + sq;
+  const int j0 = sq * p.q_per_set;
+  const int nq = min(p.q_per_set, p.Tq - j0);
+  const int nrows = nq * p.g;
+
+  PassOut<D> a;
+  attend_pass<D, F32, SRC>(p, p.k, p.v, split, p.steps_per_split, b, u, j0, nq, smem, pos_all, a);
+
+  constexpr int CPT = D / 16;  // columns per merge thread
+  const int r = threadIdx.x >> 4;
+  const int c0 = (threadIdx.x & 15) * CPT;
   const int jr = j0 + r / p.g;
   const int hr = u * p.g + r % p.g;
-  if (p.final_direct) {
-    const float inv = (Ls > 0.0) ? (float)(1.0 / Ls) : 0.f;
-    const size_t ooff = (((size_t)b * p.Tq + jr) * p.Hq + hr) * D + c0;
-    if (p.out_f32) {
-      float* op = (float*)p.o + ooff;
+  const size_t ooff = (((size_t)b * p.Tq + jr) * p.Hq + hr) * D + c0;
+  float res[CPT];
+  float inv = 0.f;
+  if constexpr (GATED) {
+    __syncthreads();  // merge buffers are reused by the window pass
+    PassOut<D> w;
+    attend_pass<D, F32, SRC_WINDOW>(p, p.k2, p.v2, 0, 1 << 30, b, u, j0, nq, smem, pos_all, w);
+    if (r >= nrows) return;
+    const float* z = p.gate + (((size_t)b * p.Tq + jr) * p.Hq + hr) * 2;
+    const double sg = 1.0 / (1.0 + exp(-(double)z[0]));
+    const double sl = 1.0 / (1.0 + exp(-(double)z[1]));
+    const float fg = a.L > 0.0 ? (float)(sg / a.L) : 0.f;
+    const float fl = w.L > 0.0 ? (float)(sl / w.L) : 0.f;
 #pragma unroll
-      for (int c = 0; c < CPT; c++) op[c] = ov[c] * inv;
-    } else {
-      uint16_t* op = (uint16_t*)p.o + ooff;
-#pragma unroll
-      for (int c = 0; c < CPT; c++) op[c] = f2bf(ov[c] * inv);
-    }
-    if (p.lse && c0 == 0)
-      p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] =
-          (Ls > 0.0) ? (float)(((double)M + log2(Ls)) * kLn2) : -INFINITY;
+    for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * fg + w.ov[c] * fl;
   } else {
-    const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu;
-    const size_t prow = ((size_t)split * n_sets + set) * 16 + r;
-    if (c0 == 0) {
-      p.part_m[prow] = M;
-      p.part_l[prow] = Ls;
-    }
+    if (r >= nrows) return;
+    if (!p.final_direct) {
+      const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu;
+      const size_t prow = ((size_t)split * n_sets + set) * 16 + r;
+      if (c0 == 0) {
+        p.part_m[prow] = a.M;
+        p.part_l[prow] = a.L;
+      }
 #pragma unroll
-    for (int c = 0; c < CPT; c++) p.part_o[prow * D + c0 + c] = ov[c];
+      for (int c = 0; c < CPT; c++) p.part_o[prow * D + c0 + c] = a.ov[c];
+      return;
+    }
+    inv = (a.L > 0.0) ? (float)(1.0 / a.L) : 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * inv;
   }
+  if (p.out_f32) {
+    float* op = (float*)p.o + ooff;
+#pragma unroll
+    for (int c = 0; c < CPT; c++) op[c] = res[c];
+  } else {
+    uint16_t* op = (uint16_t*)p.o + ooff;
+#pragma unroll
+    for (int c = 0; c < CPT; c++) op[c] = f2bf(res[c]);
+  }
+  if (p.lse && c0 == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = lse_of(a);
 }
 
 // ---- split / branch combine ---------------------------------------------------------------
@@ -455,13 +509,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }
 
 template <int D, bool F32>
-hipError_t launch_ra(const RowAttnParams& p, KeySrc src, hipStream_t stream) {
+hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
   const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu);
+  if (gated) {
+    if (src == SRC_TOKEN)
+      row_attn_kernel<D, F32, SRC_TOKEN, true><<<grid, 256, 0, stream>>>(p);
+    else
+      row_attn_kernel<D, F32, SRC_BLOCK, true><<<grid, 256, 0, stream>>>(p);
+    return hipGetLastError();
+  }
   switch (src) {
-    case SRC_RANGE: row_attn_kernel<D, F32, SRC_RANGE><<<grid, 256, 0, stream>>>(p); break;
-    case SRC_TOKEN: row_attn_kernel<D, F32, SRC_TOKEN><<<grid, 256, 0, stream>>>(p); break;
-    case SRC_BLOCK: row_attn_kernel<D, F32, SRC_BLOCK><<<grid, 256, 0, stream>>>(p); break;
-    case SRC_WINDOW: row_attn_kernel<D, F32, SRC_WINDOW><<<grid, 256, 0, stream>>>(p); break;
+    case SRC_RANGE: row_attn_kernel<D, F32, SRC_RANGE, false><<<grid, 256, 0, stream>>>(p); break;
+    case SRC_TOKEN: row_attn_kernel<D, F32, SRC_TOKEN, false><<<grid, 256, 0, stream>>>(p); break;
+    case SRC_BLOCK: row_attn_kernel<D, F32, SRC_BLOCK, false><<<grid, 256, 0, stream>>>(p); break;
+    case SRC_WINDOW: row_attn_kernel<D, F32, SRC_WINDOW, false><<<grid, 256, 0, stream>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -469,9 +530,12 @@ hipError_t launch_ra(const RowAttnParams& p, KeySrc src, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
-                           hipStream_t stream) {
-  if (head_dim == 128) return in_f32 ? launch_ra<128, true>(p, src, stream) : launch_ra<128, false>(p, src, stream);
-  return in_f32 ? launch_ra<64, true>(p, src, stream) : launch_ra<64, false>(p, src, stream);
+                           hipStream_t stream, bool gated) {
+  if (head_dim == 128)
+    return in_f32 ? launch_ra<128, true>(p, src, gated, stream)
+                  : launch_ra<128, false>(p, src, gated, stream);
+  return in_f32 ? launch_ra<64, true>(p, src, gated, stream)
+                : launch_ra<64, false>(p, src, gated, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream) {

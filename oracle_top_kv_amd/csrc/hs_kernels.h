@@ -38,6 +38,10 @@ struct RowAttnParams {
   float* part_m;   // [n_split][n_sets][16]
   double* part_l;  // [n_split][n_sets][16]
   float* part_o;   // [n_split][n_sets][16][D]
+  // gated layer in one pass (no splits): the window branch's own K', V' and the gate logits
+  const void* k2;
+  const void* v2;
+  const float* gate;  // [B, Tq, Hq, 2]
 };
 
 // Merge of split partials (one or two branches) into O and LSE; with two branches the sigmoid
@@ -56,10 +60,12 @@ struct CombineParams {
   int out_f32;
 };
 
+// gated: list source (token or block) then the window branch over k2, v2 in one workgroup,
+// combined with the sigmoid gates (requires n_split == 1).
 hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
-                           hipStream_t stream);
+                           hipStream_t stream, bool gated = false);
 
-// Full causal attention for many queries per KV head (bf16): 128 (query, head) rows per
+// Full causal attention for many queries per KV head (bf16): 256 (query, head) rows per
 // workgroup sharing LDS-staged K/V tiles.
 struct PrefillParams {
   const void* q;

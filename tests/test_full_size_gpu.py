@@ -1,0 +1,241 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The GPU runs every stage over the whole workload; the oracle recomputes sampled query rows (and,
+for the long-context workloads, sampled batch entries) one by one.  Sampled rows cover the first
+and last queries, tile and workgroup boundaries and a few seeded random rows.  For the sparse
+stages the oracle's own index sets are written into the sampled rows of the GPU's index input,
+so both sides attend over identical sets and no oracle input comes from the GPU.
+
+Workloads (sizes of the pages' two model families):
+  decode_7b_32k     batch 8, 32768 keys, 32/8 heads, d 128, needles     every output compared
+  prefill_80b_128k  4096 queries after 131072 cached keys, 64/4 heads    12 sampled rows
+  decode_80b_1m     batch 4, 2^20 keys, 64/4 heads, clustered needles    batch entries 0 and 3
+  block_7b_64k      batch 4, 65536-query causal prefill, 32/8 heads      sampled (b, row) pairs
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs, to_numpy_f32
+from parity_utils import TOL_BF16, check_block_sets, check_token_sets, max_abs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+LSE_TOL = 2e-6
+
+
+def hs():
+    from oracle_top_kv_amd import hs as _hs
+    return _hs
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sample_rows(q_len, seed, extra=4):
+    fixed = [0, 1, 15, 16, 255, 256, q_len // 2 - 1, q_len // 2, q_len - 2, q_len - 1]
+    rng = np.random.default_rng(seed)
+    rnd = rng.integers(0, q_len, size=extra).tolist()
+    return sorted({j for j in fixed + rnd if 0 <= j < q_len})
+
+
+class Timer:
+    """Prints the GPU time of each stage (information only, not a pass criterion)."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def __enter__(self):
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
+        self.e0.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.e1.record()
+        torch.cuda.synchronize()
+        say(f"  [{self.name}] {self.e0.elapsed_time(self.e1):.2f} ms")
+
+
+def host(t, b=None):
+    return to_numpy_f32(t if b is None else t[b:b + 1])
+
+
+def test_decode_7b_32k_every_stage_full_size():
+    wl = WORKLOADS["decode_7b_32k"]
+    say(f"[full size] {wl}")
+    x = make_inputs(wl, device="cuda", block_variant=True)
+    q, k, v = x["q"], x["k"], x["v"]
+    o, lse = hs().full_attn_fwd(q, k, v, out_dtype=torch.float32)
+    idx, cnt = hs().oracle_topk(q, k, lse, wl.k_global, wl.window)
+    bidx, bcnt = hs().block_score_topk(q, k, lse, wl.block, wl.n_blocks)
+    torch.cuda.synchronize()
+    qn, kn, vn = host(q), host(k), host(v)
+    o_ref, lse_ref = oracle.full_attention(qn, kn, vn)
+    eo, el = max_abs(o.cpu().numpy(), o_ref), max_abs(lse.cpu().numpy(), lse_ref)
+    say(f"  full attention: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+    assert eo <= TOL_BF16 and el <= LSE_TOL
+
+    oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
+    ex = check_token_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, qn, kn, lse_ref,
+                          wl.k_global, wl.window, wl.q_offset)
+    say(f"  token sets: near-tie differences excused {ex}")
+    sel = idx.cpu().numpy()
+    for b in range(wl.batch):
+        for u in range(wl.n_kv_heads):
+            assert set(x["needle_pos"][b, u].tolist()) <= set(sel[b, 0, u].tolist())
+
+    bi, bc = oracle.block_topk(qn, kn, lse_ref, wl.block, wl.n_blocks)
+    ex = check_block_sets(bidx.cpu().numpy(), bcnt.cpu().numpy(), bi, bc, qn, kn, lse_ref,
+                          wl.block, wl.q_offset)
+    say(f"  block sets: near-tie differences excused {ex}")
+
+    # sparse layers over the oracle's index sets
+    oi_d, oc_d = torch.from_numpy(oi).cuda(), torch.from_numpy(oc).cuda()
+    for layer, qs in enumerate(x["q_sparse"]):
+        os_, ls_ = hs().sparse_attn_gather(qs, k, v, oi_d, oc_d, kind="token",
+                                           out_dtype=torch.float32, want_lse=True)
+        torch.cuda.synchronize()
+        r_o, r_l = oracle.masked_attention(host(qs), kn, vn, oi, oc)
+        eo, el = max_abs(os_.cpu().numpy(), r_o), max_abs(ls_.cpu().numpy(), r_l)
+        say(f"  sparse layer {layer}: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+        assert eo <= TOL_BF16 and el <= LSE_TOL
+
+    qs = x["q_sparse"][0]
+    og, _ = hs().sparse_attn_gather(
+        qs, k, v, torch.from_numpy(bi).cuda(), torch.from_numpy(bc).cuda(), kind="block",
+        block=wl.block, swa=(x["k_loc"], x["v_loc"], x["gate"], wl.window),
+        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    r_o, _, _ = oracle.gated_block_swa(host(qs), kn, vn, bi, bc, wl.block, host(x["k_loc"]),
+                                       host(x["v_loc"]), wl.window, host(x["gate"]))
+    eo = max_abs(og.cpu().numpy(), r_o)
+    say(f"  block-sparse + gated SWA: max|dO| = {eo:.3e}")
+    assert eo <= TOL_BF16
+
+
+def test_prefill_80b_128k_sampled_rows():
+    wl = WORKLOADS["prefill_80b_128k"]
+    say(f"[full size] {wl}")
+    x = make_inputs(wl, device="cuda", n_sparse=2)
+    q, k, v = x["q"], x["k"], x["v"]
+    o, lse = hs().full_attn_fwd(q, k, v, out_dtype=torch.float32)
+    idx, cnt = hs().oracle_topk(q, k, lse, wl.k_global, wl.window)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.q_len, seed=wl.seed)
+    say(f"  sampled rows {rows}")
+    qn, kn, vn = host(q), host(k), host(v)
+    o_ref, lse_ref = oracle.full_attention(qn, kn, vn, rows=rows)
+    o_g, lse_g = o.cpu().numpy(), lse.cpu().numpy()
+    eo = max_abs(o_g[:, rows], o_ref[:, rows])
+    el = max_abs(lse_g[:, :, rows], lse_ref[:, :, rows])
+    say(f"  full attention: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+    assert eo <= TOL_BF16 and el <= LSE_TOL
+
+    oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window, rows=rows)
+    ex = check_token_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, qn, kn, lse_ref,
+                          wl.k_global, wl.window, wl.q_offset, rows=rows)
+    say(f"  token sets: near-tie differences excused {ex}")
+
+    # sparse layers: the sampled rows carry the oracle's sets in the GPU's index input
+    idx_in, cnt_in = idx.clone(), cnt.clone()
+    r = torch.tensor(rows, device="cuda")
+    idx_in[:, r] = torch.from_numpy(oi[:, rows]).cuda()
+    cnt_in[:, r] = torch.from_numpy(oc[:, rows]).cuda()
+    for layer, qs in enumerate(x["q_sparse"]):
+        os_, ls_ = hs().sparse_attn_gather(qs, k, v, idx_in, cnt_in, kind="token",
+                                           out_dtype=torch.float32, want_lse=True)
+        torch.cuda.synchronize()
+        r_o, r_l = oracle.masked_attention(host(qs), kn, vn, oi, oc, rows=rows)
+        eo = max_abs(os_.cpu().numpy()[:, rows], r_o[:, rows])
+        el = max_abs(ls_.cpu().numpy()[:, :, rows], r_l[:, :, rows])
+        say(f"  sparse layer {layer}: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+        assert eo <= TOL_BF16 and el <= LSE_TOL
+
+
+def test_decode_80b_1m_sampled_batch_entries():
+    wl = WORKLOADS["decode_80b_1m"]
+    say(f"[full size] {wl}")
+    x = make_inputs(wl, device="cuda", n_sparse=1)
+    q, k, v = x["q"], x["k"], x["v"]
+    with Timer("full attention"):
+        o, lse = hs().full_attn_fwd(q, k, v, out_dtype=torch.float32)
+    with Timer("token top-k"):
+        idx, cnt = hs().oracle_topk(q, k, lse, wl.k_global, wl.window)
+    qs = x["q_sparse"][0]
+    o_g, lse_g, idx_g, cnt_g = (t.cpu().numpy() for t in (o, lse, idx, cnt))
+    idx_in, cnt_in = idx.clone(), cnt.clone()
+    refs = {}
+    for b in (0, wl.batch - 1):
+        qn, kn, vn = host(q, b), host(k, b), host(v, b)
+        o_ref, lse_ref = oracle.full_attention(qn, kn, vn)
+        eo, el = max_abs(o_g[b:b + 1], o_ref), max_abs(lse_g[b:b + 1], lse_ref)
+        say(f"  b={b} full attention: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+        assert eo <= TOL_BF16 and el <= LSE_TOL
+        oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
+        ex = check_token_sets(idx_g[b:b + 1], cnt_g[b:b + 1], oi, oc, qn, kn, lse_ref,
+                              wl.k_global, wl.window, wl.q_offset)
+        say(f"  b={b} token sets: near-tie differences excused {ex}")
+        for u in range(wl.n_kv_heads):
+            assert set(x["needle_pos"][b, u].tolist()) <= set(idx_g[b, 0, u].tolist())
+        idx_in[b] = torch.from_numpy(oi[0]).cuda()
+        cnt_in[b] = torch.from_numpy(oc[0]).cuda()
+        refs[b] = (oi, oc)
+    with Timer("sparse layer"):
+        os_, ls_ = hs().sparse_attn_gather(qs, k, v, idx_in, cnt_in, kind="token",
+                                           out_dtype=torch.float32, want_lse=True)
+    os_g, ls_g = os_.cpu().numpy(), ls_.cpu().numpy()
+    for b, (oi, oc) in refs.items():
+        r_o, r_l = oracle.masked_attention(host(qs, b), host(k, b), host(v, b), oi, oc)
+        eo, el = max_abs(os_g[b:b + 1], r_o), max_abs(ls_g[b:b + 1], r_l)
+        say(f"  b={b} sparse layer: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+        assert eo <= TOL_BF16 and el <= LSE_TOL
+
+
+def test_block_7b_64k_sampled_rows():
+    wl = WORKLOADS["block_7b_64k"]
+    say(f"[full size] {wl}")
+    x = make_inputs(wl, device="cuda", block_variant=True)
+    q, k, v = x["q"], x["k"], x["v"]
+    with Timer("full attention"):
+        _, lse = hs().full_attn_fwd(q, k, v)
+    with Timer("block scores + top-16"):
+        bidx, bcnt = hs().block_score_topk(q, k, lse, wl.block, wl.n_blocks)
+    rows = sample_rows(wl.q_len, seed=wl.seed)
+    rows = sorted(set(rows) | {63, 64, 1023, 1024})
+    say(f"  sampled rows {rows}")
+    lse_g = lse.cpu().numpy()
+    bidx_g, bcnt_g = bidx.cpu().numpy(), bcnt.cpu().numpy()
+    bidx_in, bcnt_in = bidx.clone(), bcnt.clone()
+    r = torch.tensor(rows, device="cuda")
+    refs = {}
+    for b in (0, wl.batch - 1):
+        qn, kn, vn = host(q, b), host(k, b), host(v, b)
+        _, lse_ref = oracle.full_attention(qn, kn, vn, rows=rows)
+        el = max_abs(lse_g[b:b + 1][:, :, rows], lse_ref[:, :, rows])
+        say(f"  b={b} full attention: max|dLSE| = {el:.3e}")
+        assert el <= LSE_TOL
+        bi, bc = oracle.block_topk(qn, kn, lse_ref, wl.block, wl.n_blocks, rows=rows)
+        ex = check_block_sets(bidx_g[b:b + 1], bcnt_g[b:b + 1], bi, bc, qn, kn, lse_ref,
+                              wl.block, wl.q_offset, rows=rows)
+        say(f"  b={b} block sets: near-tie differences excused {ex}")
+        bidx_in[b, r] = torch.from_numpy(bi[0, rows]).cuda()
+        bcnt_in[b, r] = torch.from_numpy(bc[0, rows]).cuda()
+        refs[b] = (bi, bc)
+    qs = x["q_sparse"][0]
+    with Timer("block-sparse + gated SWA"):
+        og, _ = hs().sparse_attn_gather(
+            qs, k, v, bidx_in, bcnt_in, kind="block", block=wl.block,
+            swa=(x["k_loc"], x["v_loc"], x["gate"], wl.window), out_dtype=torch.float32)
+    og_g = og.cpu().numpy()
+    for b, (bi, bc) in refs.items():
+        r_o, _, _ = oracle.gated_block_swa(host(qs, b), host(k, b), host(v, b), bi, bc,
+                                           wl.block, host(x["k_loc"], b), host(x["v_loc"], b),
+                                           wl.window, host(x["gate"], b), rows=rows)
+        eo = max_abs(og_g[b:b + 1][:, rows], r_o[:, rows])
+        say(f"  b={b} block-sparse + gated SWA: max|dO| = {eo:.3e}")
+        assert eo <= TOL_BF16

@@ -238,6 +238,11 @@ GATED_CASES = [
                                    window=32, seed=42)),
     ("tiny_f32", Workload("gt", 1, 128, 512, 4, 1, 64, "f32", block=16, n_blocks=5, window=16,
                           seed=43)),
+    # at least 2048 (query, KV head) sets: both branches unsplit, run in one workgroup
+    ("prefill_fused_g4", Workload("gf", 1, 600, 1200, 16, 4, 128, "bf16", block=64, n_blocks=4,
+                                  window=32, seed=44)),
+    ("prefill_fused_f32_d64", Workload("gf32", 1, 520, 600, 16, 4, 64, "f32", block=16,
+                                       n_blocks=6, window=20, seed=45)),
 ]
 
 
