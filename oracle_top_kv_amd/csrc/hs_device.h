@@ -77,6 +77,32 @@ __device__ __forceinline__ float sum4groups(float v) {
   return v + shfl_xor_f(v, 32);
 }
 
+// Lane exchanges inside a 16-lane row with DPP (no LDS crossbar): quad_perm [1,0,3,2] and
+// [2,3,0,1], then the half-row and row mirrors.  After the four steps of max16 / min16_u64 every
+// lane of the row holds the row's maximum / minimum.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x141>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp_u32<0x140>(__float_as_uint(v))));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long min_dpp_u64(unsigned long long v) {
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)v), hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+  const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+  return o < v ? o : v;
+}
+__device__ __forceinline__ unsigned long long min16_u64(unsigned long long v) {
+  v = min_dpp_u64<0xB1>(v);
+  v = min_dpp_u64<0x4E>(v);
+  v = min_dpp_u64<0x141>(v);
+  return min_dpp_u64<0x140>(v);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Streaming loads for data read once per step (V rows): fetched non-temporally (measured on

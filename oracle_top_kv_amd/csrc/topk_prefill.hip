@@ -23,8 +23,9 @@
 // value (or the lower bound of a bin taken whole), and only entries >= theta stay.  Every key
 // dropped is below k kept keys, so the final top-k is exact.  At the end the k positions are
 // sorted (bitonic, in LDS) and the forced window is appended.
-// Block mode (blocks of 16, 32 or 64 keys): each query keeps its best n blocks in LDS; a block
-// replaces the current minimum when its V is larger.
+// Block mode (blocks of 16, 32 or 64 keys): each query keeps its best n blocks in registers,
+// spread over the 16 lanes that hold its keys; at each block boundary the block's V replaces
+// the list minimum (found with four lane exchanges) when it is larger.
 #include "hs_device.h"
 #include "hs_kernels.h"
 
@@ -169,16 +170,18 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-template <int D, bool F32, bool BLOCK>
+// G: query heads per KV head (4, 8 or 16).  NE: block-list entries per lane (n_blocks <= 16 NE).
+template <int D, bool F32, bool BLOCK, int G, int NE>
 __global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectParams p) {
   using C = PsCfg<D, F32>;
-  constexpr int NW = kThreads / 64;      // waves
-  constexpr int QMAX = 16;               // queries per wave at most (g = 4)
+  constexpr int NW = kThreads / 64;  // waves
+  constexpr int HQ = G / 4;          // head quarters per query
+  constexpr int QG = 4 / HQ;         // query groups per wave
+  constexpr int QW = 4 * QG;         // queries per wave (64 / G)
+  constexpr int QPW = NW * QW;       // queries per workgroup (256 / G)
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kBN * C::KStr * C::Elem];
-  __shared__ uint32_t whist[NW][256];
-  __shared__ unsigned long long qtheta[NW][QMAX];  // token: running threshold per query
-  __shared__ int qcount[NW][QMAX];                 // token: buffer fill; block: list fill
-  __shared__ unsigned long long blist[BLOCK ? NW * QMAX : 1][BLOCK ? kMaxBlocks : 1];
+  __shared__ uint32_t whist[BLOCK ? 1 : NW][256];
+  __shared__ unsigned long long blist[BLOCK ? NW * QW : 1][BLOCK ? 16 * NE : 1];
   __shared__ int sortbuf[BLOCK ? 1 : NW][BLOCK ? 1 : kSortCap];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -186,32 +189,30 @@ __global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectPar
   // Row packing, head-quarter major: the wave's 64 rows are 4 MFMA blocks; block rb holds heads
   // 4hq..4hq+3 of the 4 queries of query group qg (rb = qg * HQ + hq), MFMA row 4j+e being
   // query 4qg+j, head 4hq+e.  The S = Q K^T output then gives lane (key, j) heads 4hq..4hq+3 of
-  // query 4qg+j in every block of the group: the group maximum over all g heads is in-lane.
-  const int HQ = p.g / 4;          // head quarters per query (g = 4, 8, 16)
-  const int QG = 4 / HQ;           // query groups per wave
-  const int QW = 4 * QG;           // queries per wave (64 / g)
-  const int qpw = NW * QW;         // queries per workgroup (256 / g)
-  const int n_qt = (p.Tq + qpw - 1) / qpw;
+  // query 4qg+j in every block of the group: the group maximum over all G heads is in-lane.
+  const int n_qt = (p.Tq + QPW - 1) / QPW;
   const int u = blockIdx.x % p.Hkv;
   const int qt = n_qt - 1 - (int)((blockIdx.x / p.Hkv) % n_qt);
   const int b = blockIdx.x / (p.Hkv * n_qt);
-  const int j0 = qt * qpw;
-  const int nq = min(qpw, p.Tq - j0);
-  const long long t_max = p.q_off + j0 + nq - 1;
+  const int j0 = qt * QPW;
+  const int nq = min(QPW, p.Tq - j0);
+  const int tq0 = (int)p.q_off + j0;  // positions fit in 31 bits
+  const int t_max = tq0 + nq - 1;
   const int wq0 = wave * QW;  // first workgroup query of this wave
 
   constexpr int KK = C::KK;
   bf16x8 qa[4][F32 ? 1 : KK];
   float qf[4][F32 ? KK : 1];
-  float delta[4][4];
+  // A operand: lane row rn = 4j + e of block rb -> query 4qg + j, head 4hq + e.  Reloaded after
+  // buffer compactions, which then need no registers of their own for it.
+  auto load_q = [&]() {
 #pragma unroll
-  for (int rb = 0; rb < 4; rb++) {
-    const int qg = rb / HQ, hq = rb % HQ;
-    {  // A operand: lane row rn = 4j + e -> query 4qg + j, head 4hq + e
+    for (int rb = 0; rb < 4; rb++) {
+      const int qg = rb / HQ, hq = rb % HQ;
       const int jq = wq0 + 4 * qg + rn / 4;
       const int hh = 4 * hq + rn % 4;
       const bool ok = jq < nq;
-      const size_t qoff = (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + u * p.g + hh) * D;
+      const size_t qoff = (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + u * G + hh) * D;
       if constexpr (!F32) {
         const uint16_t* qp = (const uint16_t*)p.q + qoff;
 #pragma unroll
@@ -225,14 +226,20 @@ __global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectPar
         for (int s2 = 0; s2 < KK; s2++) qf[rb][s2] = ok ? qp[s2] : 0.f;
       }
     }
+  };
+  load_q();
+  float delta[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; rb++) {
+    const int qg = rb / HQ, hq = rb % HQ;
     {  // output rows of lane group jg: query 4qg + jg, heads 4hq + e
       const int jq = wq0 + 4 * qg + jg;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         if (jq < nq) {
           const int j = j0 + jq, hh = 4 * hq + e;
-          const double l2 = (double)p.lse[((size_t)b * p.Hq + u * p.g + hh) * p.Tq + j] * 1.4426950408889634;
-          const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
+          const double l2 = (double)p.lse[((size_t)b * p.Hq + u * G + hh) * p.Tq + j] * 1.4426950408889634;
+          const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * G) * p.Tq + j] * 1.4426950408889634);
           delta[rb][e] = (float)(l2 - Cq);
         } else {
           delta[rb][e] = INFINITY;  // queries past the last one never score
@@ -241,35 +248,50 @@ __global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectPar
     }
   }
   // this lane's query in each query group
-  long long t_q[4];
-  bool q_ok[4];
+  int t_q[QG];
+  bool q_ok[QG];
 #pragma unroll
-  for (int qg = 0; qg < 4; qg++) {
+  for (int qg = 0; qg < QG; qg++) {
     const int jq = wq0 + 4 * qg + jg;
-    q_ok[qg] = qg < QG && jq < nq;
-    t_q[qg] = p.q_off + j0 + jq;
+    q_ok[qg] = jq < nq;
+    t_q[qg] = tq0 + jq;
   }
-  if (lane < QW) {
-    qtheta[wave][lane] = 0ull;
-    qcount[wave][lane] = 0;
+
+  // token mode: buffer fill and threshold of this lane's queries (the same in its 16 lanes)
+  int cnt[QG];
+  unsigned long long th[QG];
+  float thf[QG];
+  // block mode: running block maxima and the best-n list, slot e*16 + rn in L[qg][e]; an empty
+  // slot holds its own index (below every real entry, so empties fill in slot order), slots past
+  // n_blocks hold ~0 and are never replaced.
+  float bmax[QG];
+  unsigned long long L[QG][NE];
+#pragma unroll
+  for (int qg = 0; qg < QG; qg++) {
+    cnt[qg] = 0;
+    th[qg] = 0ull;
+    thf[qg] = -INFINITY;
+    bmax[qg] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < NE; e++) {
+      const int slot = 16 * e + rn;
+      L[qg][e] = slot < p.n_blocks ? (unsigned long long)slot : ~0ull;
+    }
   }
-  // token mode: this lane's copy of its queries' thresholds (exact 64-bit and a float filter)
-  unsigned long long th[4] = {0ull, 0ull, 0ull, 0ull};
-  float thf[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  const int bshift = BLOCK ? __ffs(p.block) - 1 : 0;  // blocks of 16, 32 or 64 keys
 
   const size_t kv_row_stride = (size_t)p.Hkv * D;
   const unsigned char* kbase =
       (const unsigned char*)p.k + ((size_t)b * p.Tk * p.Hkv + u) * D * C::Elem;
-  const long long key_last = BLOCK ? t_max : t_max - p.window;  // last key any query needs
-  const int n_tiles = key_last < 0 ? 0 : (int)(key_last / kBN + 1);
+  const int key_last = BLOCK ? t_max : t_max - p.window;  // last key any query needs
+  const int n_tiles = key_last < 0 ? 0 : key_last / kBN + 1;
   u32x4 kreg[C::LPT];
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int i = 0; i < C::LPT; i++) {
       const int c = threadIdx.x + kThreads * i;
       const int row = c / C::CPR, ch = c % C::CPR;
-      long long key = (long long)t * kBN + row;
-      if (key > key_last) key = key_last;
+      const int key = min(t * kBN + row, key_last);
       kreg[i] = *(const u32x4*)(kbase + ((size_t)key * kv_row_stride) * C::Elem + ch * 16);
     }
   };
@@ -283,48 +305,50 @@ __global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectPar
   };
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const unsigned long long qmask = 0xFFFFull << (16 * jg);  // lanes of this lane's query
-  float bmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // block mode running maxima
+  auto buf_of = [&](int wq) {
+    return p.tbuf + ((size_t)((size_t)b * p.Tq + j0 + wq0 + wq) * p.Hkv + u) * kBufCap;
+  };
 
   if (n_tiles > 0) {
     load_tile(0);
     store_tile(0);
   }
   __syncthreads();
+  // Complete every load issued so far (the resident Q operand among them) here: otherwise the
+  // first use of Q inside the loop leaves a wait for all loads in every iteration, and the next
+  // K tile's loads would never overlap the current tile's work.
+  __builtin_amdgcn_s_waitcnt(0);
   for (int t = 0; t < n_tiles; t++) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    const long long key0 = (long long)t * kBN;
+    const int key0 = t * kBN;
 
-    if constexpr (!BLOCK) {
+    if constexpr (!BLOCK) {  // before the next tile's loads: their registers are free here
       // make room: compact every nearly full buffer of this wave's queries
-      bool any = false;
-      for (int wq = 0; wq < QW; wq++) {
-        const int jq = wq0 + wq;
-        if (jq < nq && qcount[wave][wq] > kBufCap - kBN) {
-          const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
-          const unsigned long long tnew = wave_compact(p.tbuf + (size_t)row * kBufCap,
-                                                       qcount[wave][wq], p.k_global, lane,
-                                                       whist[wave], nullptr);
-          wave_sync_lds();
-          if (lane == 0) {
-            qtheta[wave][wq] = tnew;
-            qcount[wave][wq] = p.k_global;
-          }
-          wave_sync_lds();
-          any = true;
-        }
-      }
-      if (any) {
+      bool full = false;
 #pragma unroll
-        for (int qg = 0; qg < 4; qg++) {
-          if (qg < QG) {
-            th[qg] = qtheta[wave][4 * qg + jg];
-            const uint32_t hi = (uint32_t)(th[qg] >> 32);
-            thf[qg] = hi ? key_to_float(hi) : -INFINITY;
+      for (int qg = 0; qg < QG; qg++) full |= cnt[qg] > kBufCap - kBN;
+      if (__ballot(full)) {
+#pragma unroll
+        for (int qg = 0; qg < QG; qg++) {
+          for (int jj = 0; jj < 4; jj++) {
+            const int n = __shfl(cnt[qg], 16 * jj, 64);
+            if (n > kBufCap - kBN) {
+              const unsigned long long tnew =
+                  wave_compact(buf_of(4 * qg + jj), n, p.k_global, lane, whist[wave], nullptr);
+              if (jg == jj) {
+                cnt[qg] = p.k_global;
+                th[qg] = tnew;
+                const uint32_t hi = (uint32_t)(tnew >> 32);
+                thf[qg] = hi ? key_to_float(hi) : -INFINITY;
+              }
+            }
           }
         }
+        load_q();
+        __builtin_amdgcn_s_waitcnt(0);
       }
     }
+    if (t + 1 < n_tiles) load_tile(t + 1);
 
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
@@ -348,15 +372,13 @@ __global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectPar
           for (int rb = 0; rb < 4; rb++) acc[rb] = mfma_f32(qf[rb][s2], kv, acc[rb]);
         }
       }
-      const long long g0 = key0 + 16 * kb;
-      const long long pos = g0 + rn;
+      const int g0 = key0 + 16 * kb;
+      const int pos = g0 + rn;
 #pragma unroll
-      for (int qg = 0; qg < 4; qg++) {
-        if (qg >= QG) break;
+      for (int qg = 0; qg < QG; qg++) {
         float v = -INFINITY;
 #pragma unroll
-        for (int hq = 0; hq < 4; hq++) {
-          if (hq >= HQ) break;
+        for (int hq = 0; hq < HQ; hq++) {
           const int rb = qg * HQ + hq;
 #pragma unroll
           for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[rb][e], p.scale_log2, -delta[rb][e]));
@@ -374,44 +396,30 @@ __global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectPar
           }
           const unsigned long long bm = __ballot(take);
           if (bm) {
-            const int wq = 4 * qg + jg;
             if (take) {
-              const long long row = ((long long)b * p.Tq + j0 + wq0 + wq) * p.Hkv + u;
-              const int slot = qcount[wave][wq] + __popcll(bm & qmask & below);
-              p.tbuf[(size_t)row * kBufCap + slot] =
-                  ((unsigned long long)float_key(v) << 32) |
-                  (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
+              const int slot = cnt[qg] + __popcll(bm & qmask & below);
+              buf_of(4 * qg + jg)[slot] = ((unsigned long long)float_key(v) << 32) |
+                                          (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
             }
-            wave_sync_lds();
-            if (rn == 0) qcount[wave][wq] += __popcll(bm & qmask);
-            wave_sync_lds();
+            cnt[qg] += __popcll(bm & qmask);
           }
         } else {
           // running maximum of the current block (keys past the query are masked)
           bmax[qg] = fmaxf(bmax[qg], (q_ok[qg] && pos <= t_q[qg]) ? v : -INFINITY);
-          if (((g0 + 16) % p.block) == 0) {  // block boundary: same for every lane
-            float bv = bmax[qg];
-            bv = fmaxf(bv, __shfl_xor(bv, 1, 64));
-            bv = fmaxf(bv, __shfl_xor(bv, 2, 64));
-            bv = fmaxf(bv, __shfl_xor(bv, 4, 64));
-            bv = fmaxf(bv, __shfl_xor(bv, 8, 64));
-            const long long bstart = g0 + 16 - p.block;
-            if (rn == 0 && q_ok[qg] && bstart <= t_q[qg]) {
-              const long long blk = bstart / p.block;
-              const unsigned long long V = ((unsigned long long)float_key(bv) << 32) |
-                                           (unsigned long long)(0xFFFFFFFFu - (uint32_t)blk);
-              const int wq = 4 * qg + jg;
-              unsigned long long* L = blist[wave * QMAX + wq];
-              const int n = qcount[wave][wq];
-              if (n < p.n_blocks) {
-                L[n] = V;
-                qcount[wave][wq] = n + 1;
-              } else {
-                int mi = 0;
-                for (int i = 1; i < p.n_blocks; i++)
-                  if (L[i] < L[mi]) mi = i;
-                if (V > L[mi]) L[mi] = V;
-              }
+          if (((g0 + 16) & (p.block - 1)) == 0) {  // block boundary: the same for every lane
+            const float bv = max16(bmax[qg]);
+            const int bstart = g0 + 16 - p.block;
+            const unsigned long long V = ((unsigned long long)float_key(bv) << 32) |
+                                         (unsigned long long)(0xFFFFFFFFu - (uint32_t)(bstart >> bshift));
+            // minimum of the query's list (16 lanes x NE entries, all distinct)
+            unsigned long long mn = L[qg][0];
+#pragma unroll
+            for (int e = 1; e < NE; e++) mn = L[qg][e] < mn ? L[qg][e] : mn;
+            const unsigned long long gmn = min16_u64(mn);
+            if (q_ok[qg] && bstart <= t_q[qg] && V > gmn && mn == gmn) {
+#pragma unroll
+              for (int e = 0; e < NE; e++)
+                if (L[qg][e] == gmn) L[qg][e] = V;
             }
             bmax[qg] = -INFINITY;
           }
@@ -423,59 +431,96 @@ __global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectPar
   }
 
   // ---- outputs, one query at a time per wave ----
-  for (int wq = 0; wq < QW; wq++) {
-    const int jq = wq0 + wq;
-    if (jq >= nq) break;
-    const long long t = p.q_off + j0 + jq;
-    const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
-    if constexpr (!BLOCK) {
-      const long long n_cand = t - p.window + 1 > 0 ? t - p.window + 1 : 0;
-      const int k_eff = (int)(n_cand < p.k_global ? n_cand : p.k_global);
-      unsigned long long* bufq = p.tbuf + (size_t)row * kBufCap;
-      int* sb = sortbuf[wave];
-      const int n = qcount[wave][wq];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // appends complete before reloads
-      if (n > k_eff) {
-        wave_compact(bufq, n, k_eff, lane, whist[wave], sb);
-      } else {
-        for (int i = lane; i < n; i += 64)
-          sb[i] = (int)(0xFFFFFFFFu - (uint32_t)(ld_coherent(bufq + i) & 0xFFFFFFFFull));
-      }
-      int M = 1;
-      while (M < k_eff) M <<= 1;
-      for (int i = k_eff + lane; i < M; i += 64) sb[i] = 0x7FFFFFFF;
-      wave_sync_lds();
-      wave_bitonic_sort(sb, M, lane);
-      int32_t* out = p.idx + (size_t)row * p.cap;
-      const long long w0 = t - p.window + 1 > 0 ? t - p.window + 1 : 0;
-      const int n_win = (int)(t - w0 + 1);
-      for (int i = lane; i < p.cap; i += 64) {
-        int32_t val = -1;
-        if (i < k_eff) val = sb[i];
-        else if (i < k_eff + n_win) val = (int32_t)(w0 + (i - k_eff));
-        out[i] = val;
-      }
-      if (lane == 0) p.cnt[row] = k_eff + n_win;
-      wave_sync_lds();
-    } else {
-      const long long nb = t / p.block + 1;
-      const int n_take = (int)(nb < p.n_blocks ? nb : p.n_blocks);
-      const unsigned long long* L = blist[wave * QMAX + wq];
-      int32_t* out = p.idx + (size_t)row * p.n_blocks;
-      if (lane < p.n_blocks) {
-        if (lane < n_take) {
-          const int id = (int)(0xFFFFFFFFu - (uint32_t)(L[lane] & 0xFFFFFFFFull));
-          int rank = 0;
-          for (int o = 0; o < n_take; o++)
-            rank += (int)(0xFFFFFFFFu - (uint32_t)(L[o] & 0xFFFFFFFFull)) < id;
-          out[rank] = id;
+  if constexpr (BLOCK) {
+#pragma unroll
+    for (int qg = 0; qg < QG; qg++)
+#pragma unroll
+      for (int e = 0; e < NE; e++) blist[wave * QW + 4 * qg + jg][16 * e + rn] = L[qg][e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+#pragma unroll
+  for (int qg = 0; qg < QG; qg++) {
+    for (int jj = 0; jj < 4; jj++) {
+      const int wq = 4 * qg + jj;
+      const int jq = wq0 + wq;
+      if (jq >= nq) break;
+      const int t = tq0 + jq;
+      const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
+      if constexpr (!BLOCK) {
+        const int n_cand = max(t - p.window + 1, 0);
+        const int k_eff = min(n_cand, p.k_global);
+        unsigned long long* bufq = buf_of(wq);
+        int* sb = sortbuf[wave];
+        const int n = __shfl(cnt[qg], 16 * jj, 64);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // appends complete before reloads
+        if (n > k_eff) {
+          wave_compact(bufq, n, k_eff, lane, whist[wave], sb);
         } else {
-          out[lane] = -1;
+          for (int i = lane; i < n; i += 64)
+            sb[i] = (int)(0xFFFFFFFFu - (uint32_t)(ld_coherent(bufq + i) & 0xFFFFFFFFull));
         }
+        int M = 1;
+        while (M < k_eff) M <<= 1;
+        for (int i = k_eff + lane; i < M; i += 64) sb[i] = 0x7FFFFFFF;
+        wave_sync_lds();
+        wave_bitonic_sort(sb, M, lane);
+        int32_t* out = p.idx + (size_t)row * p.cap;
+        const int w0 = max(t - p.window + 1, 0);
+        const int n_win = t - w0 + 1;
+        for (int i = lane; i < p.cap; i += 64) {
+          int32_t val = -1;
+          if (i < k_eff) val = sb[i];
+          else if (i < k_eff + n_win) val = w0 + (i - k_eff);
+          out[i] = val;
+        }
+        if (lane == 0) p.cnt[row] = k_eff + n_win;
+        wave_sync_lds();
+      } else {
+        const int n_take = min((t >> bshift) + 1, p.n_blocks);
+        const unsigned long long* Lq = blist[wave * QW + wq];
+        int32_t* out = p.idx + (size_t)row * p.n_blocks;
+        // real entries occupy slots 0 .. n_take-1 (empties are replaced in slot order)
+        if (lane < p.n_blocks) {
+          if (lane < n_take) {
+            const int id = (int)(0xFFFFFFFFu - (uint32_t)(Lq[lane] & 0xFFFFFFFFull));
+            int rank = 0;
+            for (int o = 0; o < n_take; o++)
+              rank += (int)(0xFFFFFFFFu - (uint32_t)(Lq[o] & 0xFFFFFFFFull)) < id;
+            out[rank] = id;
+          } else {
+            out[lane] = -1;
+          }
+        }
+        if (lane == 0) p.cnt[row] = n_take;
       }
-      if (lane == 0) p.cnt[row] = n_take;
     }
   }
+}
+
+template <int D, bool F32, bool BLOCK, int G>
+void launch_g(const PrefillSelectParams& p, dim3 grid, hipStream_t stream) {
+  if constexpr (BLOCK) {
+    if (p.n_blocks > 16) {
+      pf_select_kernel<D, F32, BLOCK, G, 4><<<grid, kThreads, 0, stream>>>(p);
+      return;
+    }
+  }
+  pf_select_kernel<D, F32, BLOCK, G, 1><<<grid, kThreads, 0, stream>>>(p);
+}
+
+template <int D, bool F32, bool BLOCK>
+void launch_dfb(const PrefillSelectParams& p, hipStream_t stream) {
+  const int qpw = kRowsWG / p.g;  // queries per workgroup
+  const int n_qt = (p.Tq + qpw - 1) / qpw;
+  const dim3 grid(p.B * p.Hkv * n_qt);
+  if (p.g == 4)
+    launch_g<D, F32, BLOCK, 4>(p, grid, stream);
+  else if (p.g == 8)
+    launch_g<D, F32, BLOCK, 8>(p, grid, stream);
+  else
+    launch_g<D, F32, BLOCK, 16>(p, grid, stream);
 }
 
 }  // namespace
@@ -485,24 +530,23 @@ int prefill_select_max_k() { return kSortCap; }
 
 hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
                                  bool block_mode, hipStream_t stream) {
-  const int qpw = kRowsWG / p.g;  // queries per workgroup
-  const int n_qt = (p.Tq + qpw - 1) / qpw;
-  const dim3 grid(p.B * p.Hkv * n_qt);
-#define HS_LAUNCH(D, F, BL) pf_select_kernel<D, F, BL><<<grid, kThreads, 0, stream>>>(p)
+  if (p.g != 4 && p.g != 8 && p.g != 16) return hipErrorInvalidValue;
+  if (block_mode && (p.block < 16 || p.block > 64 || (p.block & (p.block - 1)) ||
+                     p.n_blocks < 1 || p.n_blocks > kMaxBlocks))
+    return hipErrorInvalidValue;
   if (head_dim == 128) {
     if (in_f32) {
-      if (block_mode) HS_LAUNCH(128, true, true); else HS_LAUNCH(128, true, false);
+      if (block_mode) launch_dfb<128, true, true>(p, stream); else launch_dfb<128, true, false>(p, stream);
     } else {
-      if (block_mode) HS_LAUNCH(128, false, true); else HS_LAUNCH(128, false, false);
+      if (block_mode) launch_dfb<128, false, true>(p, stream); else launch_dfb<128, false, false>(p, stream);
     }
   } else {
     if (in_f32) {
-      if (block_mode) HS_LAUNCH(64, true, true); else HS_LAUNCH(64, true, false);
+      if (block_mode) launch_dfb<64, true, true>(p, stream); else launch_dfb<64, true, false>(p, stream);
     } else {
-      if (block_mode) HS_LAUNCH(64, false, true); else HS_LAUNCH(64, false, false);
+      if (block_mode) launch_dfb<64, false, true>(p, stream); else launch_dfb<64, false, false>(p, stream);
     }
   }
-#undef HS_LAUNCH
   return hipGetLastError();
 }
 
