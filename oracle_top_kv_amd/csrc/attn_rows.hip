@@ -203,15 +203,9 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
     }
   };
 
-  KReg ka0[KK], ka1[KK];
-  u32x4 va[VL];
-  int step = step_begin + wave;
-  if (step < step_end) load_step(step, ka0, ka1, va);
-  for (; step < step_end; step += kWaves) {
-    KReg kn0[KK], kn1[KK];
-    u32x4 vn[VL];
-    if (step + kWaves < step_end) load_step(step + kWaves, kn0, kn1, vn);
-
+  // One 32-key step of this wave on K rows (ka0, ka1) and V rows (va) already in registers.
+  auto compute_step = [&](int step, const KReg (&ka0)[KK], const KReg (&ka1)[KK],
+                          const u32x4 (&va)[VL]) {
     // V rows of this step -> LDS tile (row-major [key][d], padded rows)
 #pragma unroll
     for (int n = 0; n < VL; n++) {
@@ -296,7 +290,19 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
           }
     }
     wave_lds_sync();  // tile reads done before the next step overwrites it
+  };
 
+  // The loop always prefetches (its last step is peeled off below): a conditional prefetch
+  // would make the compiler wait for the first prefetched load before every step.
+  KReg ka0[KK], ka1[KK];
+  u32x4 va[VL];
+  int step = step_begin + wave;
+  if (step < step_end) load_step(step, ka0, ka1, va);
+  for (; step + kWaves < step_end; step += kWaves) {
+    KReg kn0[KK], kn1[KK];
+    u32x4 vn[VL];
+    load_step(step + kWaves, kn0, kn1, vn);
+    compute_step(step, ka0, ka1, va);
 #pragma unroll
     for (int kk = 0; kk < KK; kk++) {
       ka0[kk] = kn0[kk];
@@ -305,6 +311,7 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
 #pragma unroll
     for (int n = 0; n < VL; n++) va[n] = vn[n];
   }
+  if (step < step_end) compute_step(step, ka0, ka1, va);
 
   // ---- merge the 4 waves of this workgroup ----
   __syncthreads();
