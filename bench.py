@@ -37,7 +37,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 80B-shaped prefill leg (full attention + token top-k)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (calibrates the "
+                         "HBM byte counters of a profiler) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size: reads and writes exactly `mib` MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 5}), flush=True)
 
 
 def main():
@@ -46,6 +63,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
 
@@ -139,9 +160,11 @@ def main():
                    "sparse_layers": wl.n_sparse, "block": wl.block, "n_blocks": wl.n_blocks,
                    "needles_per_kv_head": wl.needles, "step_bytes": total_bytes},
         "stages": stages_out,
-        "roofline": {"bound": "hbm", "kernel": "full-attention decode (row_attn_kernel + combine)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "full-attention decode call (row_attn_kernel + combine_kernel)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": b_full, "traffic": counter_traffic(wl.name)},
     }
     if not args.no_prefill:
         del x, q, k, v, qs, kl, vl, gate
@@ -151,6 +174,28 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, make_inputs(wl, device=dev, block_variant=True),
                                            args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def counter_traffic(workload):
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading); None when that summary
+    is missing, covers another workload, or any kernel source it lists has changed since."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    meta = json.loads(m.group(1))
+    if meta.get("workload") != workload:
+        return None
+    for rel, digest in meta["sources_sha256"].items():
+        src = os.path.join(ROOT, rel)
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != digest:
+            return None
+    return meta["traffic_bytes_per_launch"]
 
 
 def prefill_leg(args):
