@@ -4,12 +4,14 @@
 //
 // A workgroup owns 256 (query, head) rows of one KV head: 256/g consecutive queries times the
 // g heads of the group, so every K/V tile staged in LDS serves all heads of the group (256 rows
-// per 64-key tile: 128 flop per byte of K/V moved from L2).  Each of the 8 waves owns 32 rows
-// (two 16-row MFMA blocks).  Per 64-key tile:
-//   S^T = K Q^T   A = K from LDS (ds_read_b128), B = Q^T resident in registers
-//   online softmax in the log2 domain; the row state lives in the 4 lanes of the row
+// per 64-key tile: 128 flop per byte of K/V moved from L2).  Each of the 8 waves owns 32 rows,
+// one column block of v_mfma_f32_32x32x16_bf16.  Per 64-key tile:
+//   S^T = K Q^T   A = K (32 keys x 16 d) from LDS, B = Q^T resident in registers; lane l then
+//                 holds row l%32 for 32 of the tile's keys, the other 32 sit in lane l^32
+//   online softmax in the log2 domain (scale folded into the exponent's FMA); the row maximum is
+//                 an in-lane max3 chain plus one v_permlane32_swap
 //   O^T += V^T P^T  B = P^T straight from the S^T accumulator (bf16), A = V^T from the
-//                   row-major LDS tile with ds_read_b64_tr_b16
+//                 row-major LDS tile with ds_read_b64_tr_b16 (keys in the accumulator's order)
 // K/V tiles are double-buffered: the next tile's rows are loaded into registers while the
 // current tile is computed, then stored to the other buffer; one barrier per tile.  Only tiles
 // that reach past the earliest query position of the workgroup apply the causal mask.
@@ -23,16 +25,31 @@ constexpr int kRowsWG = 256;
 constexpr int kThreads = 512;
 constexpr int kBN = 64;
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// max over lanes l and l ^ 32 (the two halves of the wave)
+__device__ __forceinline__ float max_halves(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 template <int D>
 struct PfCfg {
   static constexpr int KStr = D + 8;    // K tile row stride (elements): conflict-free ds_read_b128
   static constexpr int VStr = D + 16;   // V tile row stride: conflict-free transpose reads
-  static constexpr int KK = D / 32;     // MFMA steps over d
-  static constexpr int DB = D / 16;     // 16-wide d blocks of O
+  static constexpr int KK = D / 16;     // MFMA steps over d
+  static constexpr int DB = D / 32;     // 32-wide d blocks of O
   static constexpr int CPR = D / 8;     // 16-byte chunks per row
   static constexpr int LPT = kBN * CPR / kThreads;  // chunks per thread per tile (each of K and V)
 };
 
+// 32x32x16 layouts (wave64, lane l, h = l / 32):
+//   A[32 x 16]: row l % 32, k = 8h .. 8h + 7;   B[16 x 32]: column l % 32, k = 8h .. 8h + 7
+//   C[32 x 32]: column l % 32, register 4g + e holds row 8g + 4h + e (g, e = 0..3)
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   using C = PfCfg<D>;
@@ -40,7 +57,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][kBN * C::VStr];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rn = lane & 15, jg = lane >> 4;
+  const int rj = lane & 31, h = lane >> 5;
   const int qpw = kRowsWG / p.g;  // queries per workgroup
   const int n_qt = (p.Tq + qpw - 1) / qpw;
   // KV head fastest, then query tile (latest, i.e. longest, first), then batch
@@ -49,42 +66,38 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   const int b = blockIdx.x / (p.Hkv * n_qt);
   const int j0 = qt * qpw;
   const int nq = min(qpw, p.Tq - j0);
-  const long long t_min = p.q_off + j0;
-  const long long t_max = p.q_off + j0 + nq - 1;
+  const int t_min = (int)p.q_off + j0;  // positions fit in 31 bits
+  const int t_max = t_min + nq - 1;
 
-  // this lane's two rows (one per 16-row block)
-  bool row_ok[2];
-  long long t_row[2];
-  int j_row[2], h_row[2];
-  bf16x8 qb[2][C::KK];
-#pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
-    const int r = wave * 32 + rb * 16 + rn;
-    const int jq = r / p.g, hh = r % p.g;
-    row_ok[rb] = jq < nq;
-    j_row[rb] = j0 + (row_ok[rb] ? jq : 0);
-    h_row[rb] = u * p.g + hh;
-    t_row[rb] = p.q_off + j_row[rb];
-    const uint16_t* qp = (const uint16_t*)p.q + (((size_t)b * p.Tq + j_row[rb]) * p.Hq + h_row[rb]) * D;
+  // this lane's row: column rj of the wave's S^T / O^T blocks
+  const int r = wave * 32 + rj;
+  const int jq = r / p.g, hh = r % p.g;
+  const bool row_ok = jq < nq;
+  const int j_row = j0 + (row_ok ? jq : 0);
+  const int h_row = u * p.g + hh;
+  const int t_row = t_min + jq;
+  bf16x8 qb[C::KK];
+  {
+    const uint16_t* qp = (const uint16_t*)p.q + (((size_t)b * p.Tq + j_row) * p.Hq + h_row) * D;
 #pragma unroll
     for (int kk = 0; kk < C::KK; kk++) {
-      u32x4 raw = row_ok[rb] ? *(const u32x4*)(qp + 32 * kk + 8 * jg) : u32x4{0, 0, 0, 0};
-      qb[rb][kk] = __builtin_bit_cast(bf16x8, raw);
+      u32x4 raw = row_ok ? *(const u32x4*)(qp + 16 * kk + 8 * h) : u32x4{0, 0, 0, 0};
+      qb[kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
 
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_s[2] = {0.f, 0.f}, l_c[2] = {0.f, 0.f};
-  f32x4 oacc[2][C::DB];
+  float m_run = -INFINITY;  // running row maximum, log2 domain (scaled)
+  float l_s = 0.f, l_c = 0.f;
+  f32x16 oacc[C::DB];
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++)
+  for (int db = 0; db < C::DB; db++)
 #pragma unroll
-    for (int db = 0; db < C::DB; db++) oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; i++) oacc[db][i] = 0.f;
 
   const size_t kv_row_stride = (size_t)p.Hkv * D;
   const uint16_t* kbase = (const uint16_t*)p.k + ((size_t)b * p.Tk * p.Hkv + u) * D;
   const uint16_t* vbase = (const uint16_t*)p.v + ((size_t)b * p.Tk * p.Hkv + u) * D;
-  const int n_tiles = (int)((t_max + kBN) / kBN);  // tiles covering keys 0..t_max
+  const int n_tiles = (t_max + kBN) / kBN;  // tiles covering keys 0..t_max
 
   u32x4 kreg[C::LPT], vreg[C::LPT];
   auto load_tile = [&](int t) {
@@ -92,8 +105,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
     for (int i = 0; i < C::LPT; i++) {
       const int c = threadIdx.x + kThreads * i;
       const int row = c / C::CPR, ch = c % C::CPR;
-      long long key = (long long)t * kBN + row;
-      if (key > t_max) key = t_max;  // rows past the last query are loaded but masked
+      const int key = min(t * kBN + row, t_max);  // rows past the last query are loaded but masked
       kreg[i] = *(const u32x4*)(kbase + (size_t)key * kv_row_stride + ch * 8);
       vreg[i] = ld_stream(vbase + (size_t)key * kv_row_stride + ch * 8);
     }
@@ -111,80 +123,82 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   load_tile(0);
   store_tile(0);
   __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);  // Q loads done here, not inside the loop
   for (int t = 0; t < n_tiles; t++) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
-    const long long key0 = (long long)t * kBN;
+    const int key0 = t * kBN;
     const bool need_mask = key0 + kBN - 1 > t_min;
 
-    // S^T for 4 key blocks x 2 row blocks
-    f32x4 sacc[4][2];
+    // S^T for the two 32-key blocks: register 4g + e of sacc[kb] is key key0 + 32kb + 8g + 4h + e
+    f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
-      sacc[kb][0] = sacc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) sacc[kb][i] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < C::KK; kk++) {
-        const bf16x8 ka = *(const bf16x8*)(&ks[buf][(16 * kb + rn) * C::KStr + 32 * kk + 8 * jg]);
-        sacc[kb][0] = mfma_bf16(ka, qb[0][kk], sacc[kb][0]);
-        sacc[kb][1] = mfma_bf16(ka, qb[1][kk], sacc[kb][1]);
+        const bf16x8 ka = *(const bf16x8*)(&ks[buf][(32 * kb + rj) * C::KStr + 16 * kk + 8 * h]);
+        sacc[kb] = mfma32(ka, qb[kk], sacc[kb]);
       }
     }
 
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * h + (i % 4);
+          if (!row_ok || key > t_row) sacc[kb][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx * p.scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
     bf16x8 pb[2][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
-      float sv[4][4];
-      float mx = -INFINITY;
+    for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
-      for (int kb = 0; kb < 4; kb++)
+      for (int s2 = 0; s2 < 2; s2++) {
+        float x8[8];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          float x = sacc[kb][rb][e] * p.scale_log2;
-          if (need_mask) {
-            const long long key = key0 + 16 * kb + 4 * jg + e;
-            if (!row_ok[rb] || key > t_row[rb]) x = -INFINITY;
-          }
-          sv[kb][e] = x;
-          mx = fmaxf(mx, x);
+        for (int i = 0; i < 8; i++) {
+          x8[i] = fast_exp2(__builtin_fmaf(sacc[kb][8 * s2 + i], p.scale_log2, -m_use));
+          psum += x8[i];
         }
-      mx = max4groups(mx);
-      const float m_new = fmaxf(m_run[rb], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[rb] - m_use);
-      float pv[4][4];
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          pv[kb][e] = fast_exp2(sv[kb][e] - m_use);
-          psum += pv[kb][e];
-        }
-      l_s[rb] *= alpha;
-      l_c[rb] *= alpha;
-      kahan_add(l_s[rb], l_c[rb], psum);
-      m_run[rb] = m_new;
-      if (__ballot(alpha != 1.f)) {  // rescale only when some row maximum moved
-#pragma unroll
-        for (int db = 0; db < C::DB; db++) oacc[rb][db] *= alpha;
-      }
-#pragma unroll
-      for (int s = 0; s < 2; s++) {
-        const float x8[8] = {pv[2 * s][0], pv[2 * s][1], pv[2 * s][2], pv[2 * s][3],
-                             pv[2 * s + 1][0], pv[2 * s + 1][1], pv[2 * s + 1][2], pv[2 * s + 1][3]};
-        pb[rb][s] = pack_bf16x8(x8);
+        pb[kb][s2] = pack_bf16x8(x8);
       }
     }
+    l_s *= alpha;
+    l_c *= alpha;
+    kahan_add(l_s, l_c, psum);
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {  // rescale only when some row maximum moved
+#pragma unroll
+      for (int db = 0; db < C::DB; db++) oacc[db] *= alpha;
+    }
 
-    // O^T += V^T P^T over the two 32-key halves of the tile
+    // O^T += V^T P^T over four 16-key steps; step (kb, s2) covers keys key0 + 32kb + 16s2 + {4h+e,
+    // 8+4h+e}, the order in which pb[kb][s2] holds them
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
+    for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
-      for (int db = 0; db < C::DB; db++) {
-        const uint16_t* a0 = &vs[buf][(32 * s + 4 * jg + (rn >> 2)) * C::VStr + 16 * db + 4 * (rn & 3)];
-        const bf16x8 va = join_tr(lds_read_tr16(a0), lds_read_tr16(a0 + 16 * C::VStr));
-        oacc[0][db] = mfma_bf16(va, pb[0][s], oacc[0][db]);
-        oacc[1][db] = mfma_bf16(va, pb[1][s], oacc[1][db]);
+      for (int s2 = 0; s2 < 2; s2++) {
+        const int kbase_row = 32 * kb + 16 * s2 + 4 * h;
+#pragma unroll
+        for (int db = 0; db < C::DB; db++) {
+          const int c0 = 32 * db + 16 * ((lane >> 4) & 1);
+          const uint16_t* a0 = &vs[buf][(kbase_row + ((lane & 15) >> 2)) * C::VStr + c0 + 4 * (lane & 3)];
+          const bf16x8 va = join_tr(lds_read_tr16(a0), lds_read_tr16(a0 + 8 * C::VStr));
+          oacc[db] = mfma32(va, pb[kb][s2], oacc[db]);
+        }
       }
     }
     if (t + 1 < n_tiles) store_tile(buf ^ 1);
@@ -192,29 +206,31 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   }
 
   // epilogue: normalize and write O and LSE
+  // lanes l and l ^ 32 hold the row's sums over different keys (with the same maximum)
+  double ld = (double)l_s - (double)l_c;
+  ld += __shfl_xor(ld, 32, 64);
+  if (!row_ok) return;
+  const float inv = ld > 0.0 ? (float)(1.0 / ld) : 0.f;
+  const size_t orow = (((size_t)b * p.Tq + j_row) * p.Hq + h_row) * D;
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
-    double ld = (double)l_s[rb] - (double)l_c[rb];
-    ld += __shfl_xor(ld, 16, 64);
-    ld += __shfl_xor(ld, 32, 64);
-    if (!row_ok[rb]) continue;
-    const float inv = ld > 0.0 ? (float)(1.0 / ld) : 0.f;
-    const size_t ooff = (((size_t)b * p.Tq + j_row[rb]) * p.Hq + h_row[rb]) * D + 4 * jg;
+  for (int db = 0; db < C::DB; db++) {
 #pragma unroll
-    for (int db = 0; db < C::DB; db++) {
-      const f32x4 o4 = oacc[rb][db] * inv;
+    for (int g = 0; g < 4; g++) {
+      const size_t ooff = orow + 32 * db + 8 * g + 4 * h;
+      const f32x4 o4 = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                        oacc[db][4 * g + 3] * inv};
       if (p.out_f32) {
-        *(f32x4*)((float*)p.o + ooff + 16 * db) = o4;
+        *(f32x4*)((float*)p.o + ooff) = o4;
       } else {
         typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
         u16x4 h4 = {f2bf(o4[0]), f2bf(o4[1]), f2bf(o4[2]), f2bf(o4[3])};
-        *(u16x4*)((uint16_t*)p.o + ooff + 16 * db) = h4;
+        *(u16x4*)((uint16_t*)p.o + ooff) = h4;
       }
     }
-    if (jg == 0)
-      p.lse[((size_t)b * p.Hq + h_row[rb]) * p.Tq + j_row[rb]] =
-          ld > 0.0 ? (float)(((double)m_run[rb] + log2(ld)) * kLn2) : -INFINITY;
   }
+  if (h == 0)
+    p.lse[((size_t)b * p.Hq + h_row) * p.Tq + j_row] =
+        ld > 0.0 ? (float)(((double)m_run + log2(ld)) * kLn2) : -INFINITY;
 }
 
 }  // namespace
