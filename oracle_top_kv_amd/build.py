@@ -16,7 +16,10 @@ SO = os.path.join(HERE, "libhysparse.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
-HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+# -fno-honor-nans: no kernel produces or tests for NaN (masked scores are -inf, never NaN), and
+# without it every fmaxf operand straight from an MFMA is first re-canonicalized by an extra
+# v_max_f32.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fno-honor-nans",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 

@@ -15,6 +15,8 @@
 // K/V tiles are double-buffered: the next tile's rows are loaded into registers while the
 // current tile is computed, then stored to the other buffer; one barrier per tile.  Only tiles
 // that reach past the earliest query position of the workgroup apply the causal mask.
+#include <type_traits>
+
 #include "hs_device.h"
 #include "hs_kernels.h"
 
@@ -124,26 +126,29 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   store_tile(0);
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0);  // Q loads done here, not inside the loop
-  for (int t = 0; t < n_tiles; t++) {
+  // One 64-key tile; MASK: the tile reaches past the workgroup's first query position.
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
     const int key0 = t * kBN;
-    const bool need_mask = key0 + kBN - 1 > t_min;
 
     // S^T for the two 32-key blocks: register 4g + e of sacc[kb] is key key0 + 32kb + 8g + 4h + e
     f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
+    for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int i = 0; i < 16; i++) sacc[kb][i] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < C::KK; kk++) {
+    for (int kk = 0; kk < C::KK; kk++) {  // the two key blocks' chains interleaved
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++) {
         const bf16x8 ka = *(const bf16x8*)(&ks[buf][(32 * kb + rj) * C::KStr + 16 * kk + 8 * h]);
         sacc[kb] = mfma32(ka, qb[kk], sacc[kb]);
       }
     }
 
-    if (need_mask) {
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
@@ -203,7 +208,11 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
     }
     if (t + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
-  }
+  };
+  // tiles entirely at or before the first query position need no mask
+  const int n_full = min(n_tiles, (t_min + 1) / kBN);
+  for (int t = 0; t < n_full; t++) tile(t, std::false_type());
+  for (int t = n_full; t < n_tiles; t++) tile(t, std::true_type());
 
   // epilogue: normalize and write O and LSE
   // lanes l and l ^ 32 hold the row's sums over different keys (with the same maximum)
