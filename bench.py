@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 80B-shaped prefill leg (full attention + token top-k)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the token-sparse decode layer sweep over batch sizes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (calibrates the "
                          "HBM byte counters of a profiler) and exit")
@@ -166,10 +168,13 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": b_full, "traffic": counter_traffic(wl.name)},
     }
-    if not args.no_prefill:
+    if not args.no_prefill or not args.no_sweep:
         del x, q, k, v, qs, kl, vl, gate
         torch.cuda.empty_cache()
+    if not args.no_prefill:
         out["prefill"] = prefill_leg(args)
+    if not args.no_sweep:
+        out["sparse_decode_sweep"] = sparse_sweep(wl)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, make_inputs(wl, device=dev, block_variant=True),
                                            args.cpu_seconds)
@@ -234,6 +239,44 @@ def prefill_leg(args):
             "useful_tflops": round(f_fa / ((t_fa + t_tk) * 1e-3) / 1e12, 1),
             "mfma_frac_full_attn": round(f_fa / (t_fa * 1e-3) / 2.5e15, 4),
             "peak_tflops": 2500.0, "reps": reps}
+
+
+def sparse_sweep(wl, batches=(8, 32, 128)):
+    """The token-sparse decode layer alone (7B decode shape: 32k context, 32/8 heads, d 128,
+    1024 + 128 keys per (b, u)) at several batch sizes, over synthetic sorted index sets:
+    gathered K+V bytes per second against the 8 TB/s HBM peak.  At the benchmark's batch of 8
+    the layer is latency-bound; larger batches show the kernel's bandwidth."""
+    import torch
+
+    from oracle_top_kv_amd import hs
+    from oracle_top_kv_amd.inputs import Workload, make_inputs, random_token_sets
+
+    res = {}
+    for B in batches:
+        w = Workload("sweep", B, 1, wl.kv_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, "bf16",
+                     n_sparse=1, seed=600 + B)
+        x = make_inputs(w, device=torch.device("cuda:0"))
+        idx, cnt = random_token_sets(B, w.n_kv_heads, w.kv_len, wl.k_global, wl.window,
+                                     seed=700 + B, device="cuda:0")
+        qs, k, v = x["q_sparse"][0], x["k"], x["v"]
+        for _ in range(3):
+            hs.sparse_attn_gather(qs, k, v, idx, cnt, kind="token")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            hs.sparse_attn_gather(qs, k, v, idx, cnt, kind="token")
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        byts = B * w.n_kv_heads * (wl.k_global + wl.window) * 2 * w.head_dim * 2
+        gbs = byts / (us * 1e-6) / 1e9
+        res[f"batch_{B}"] = {"us": round(us, 1), "GB_per_s": round(gbs, 1),
+                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
+        del x, idx, cnt, qs, k, v
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(wl, x, budget_s):

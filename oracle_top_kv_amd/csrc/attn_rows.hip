@@ -28,7 +28,6 @@
 namespace hs {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kStep = 32;  // keys per wave step
 constexpr int kMaxListEntries = 2048;  // list-mode entries staged per workgroup (64 steps)
 
@@ -38,8 +37,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, bool F32>
+// NW: waves per workgroup (4, or 8 for unsplit key lists of few row-sets)
+template <int D, bool F32, int NW>
 struct RaCfg {
+  static constexpr int kWaves = NW;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kTPR = kThreads / 16;  // merge threads per row
+  static constexpr int kCPT = D / kTPR;       // merge columns per thread
   static constexpr int kElem = F32 ? 4 : 2;
   static constexpr int kVStride = D + (F32 ? 4 : 16);  // LDS row stride (elements), padded
   static constexpr int kChunksPerRow = D * kElem / 16;
@@ -66,24 +70,25 @@ __device__ __forceinline__ int entry_pos(const RowAttnParams& p, int e, int L, l
 }
 
 // Result of one pass over a key source, as held by the merge thread of row r, columns
-// c0 .. c0 + D/16 - 1 (r = threadIdx.x / 16, c0 = (threadIdx.x % 16) * D/16): the row maximum
+// c0 .. c0 + CPT - 1 (r = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * CPT): the row maximum
 // M (log2 domain), the row sum L relative to M and the unnormalized output columns.
-template <int D>
+template <int CPT>
 struct PassOut {
   float M;
   double L;
-  float ov[D / 16];
+  float ov[CPT];
 };
 
 // One split of one row-set over one key source (K, V given explicitly so that the gated layer
 // can run its window branch over K', V' in the same workgroup).  Ends with the four waves
 // merged; `smem` and `pos_all` are free again once the caller has synchronized.
-template <int D, bool F32, int SRC>
+template <int D, bool F32, int SRC, int NW>
 __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* kmat,
                                             const void* vmat, int split, int steps_per_split,
                                             int b, int u, int j0, int nq, unsigned char* smem,
-                                            int* pos_all, PassOut<D>& out) {
-  using Cfg = RaCfg<D, F32>;
+                                            int* pos_all, PassOut<RaCfg<D, F32, NW>::kCPT>& out) {
+  using Cfg = RaCfg<D, F32, NW>;
+  constexpr int kWaves = NW;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rn = lane & 15;   // MFMA row / column index of this lane
@@ -155,7 +160,7 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   constexpr bool kList = (SRC == SRC_TOKEN || SRC == SRC_BLOCK);
   if constexpr (kList) {
     const int n_e = (step_end - step_begin) * kStep;
-    for (int i = threadIdx.x; i < n_e; i += 256)
+    for (int i = threadIdx.x; i < n_e; i += Cfg::kThreads)
       pos_all[i] = entry_pos<SRC>(p, step_begin * kStep + i, L, lo, t_last, list);
     __syncthreads();
   }
@@ -313,7 +318,7 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   }
   if (step < step_end) compute_step(step, ka0, ka1, va);
 
-  // ---- merge the 4 waves of this workgroup ----
+  // ---- merge the waves of this workgroup ----
   __syncthreads();
   float* cO = (float*)smem;                     // [kWaves][16][D]
   float* cM = cO + kWaves * 16 * D;             // [kWaves][16]
@@ -331,9 +336,9 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   }
   __syncthreads();
 
-  constexpr int CPT = D / 16;  // columns per thread
-  const int r = threadIdx.x >> 4;
-  const int c0 = (threadIdx.x & 15) * CPT;
+  constexpr int CPT = Cfg::kCPT;
+  const int r = threadIdx.x / Cfg::kTPR;
+  const int c0 = (threadIdx.x % Cfg::kTPR) * CPT;
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kWaves; w++) M = fmaxf(M, cM[w * 16 + r]);
@@ -356,17 +361,17 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   out.L = Ls;
 }
 
-template <int D>
-__device__ __forceinline__ float lse_of(const PassOut<D>& a) {
+template <int CPT>
+__device__ __forceinline__ float lse_of(const PassOut<CPT>& a) {
   return (a.L > 0.0) ? (float)(((double)a.M + log2(a.L)) * kLn2) : -INFINITY;
 }
 
 // GATED: the HySparse sparse layer in one workgroup when neither branch is split -- the block
 // (or token) branch over K, V, then the sliding-window branch over K', V' (p.k2, p.v2), each
 // normalized on its own and weighted by its sigmoid gate [P2 "Same query, two memories"].
-template <int D, bool F32, int SRC, bool GATED>
-__global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
-  using Cfg = RaCfg<D, F32>;
+template <int D, bool F32, int SRC, bool GATED, int NW>
+__global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
+  using Cfg = RaCfg<D, F32, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::kSmem];
   __shared__ int pos_all[kMaxListEntries];
 
@@ -383,12 +388,12 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
   const int nq = min(p.q_per_set, p.Tq - j0);
   const int nrows = nq * p.g;
 
-  PassOut<D> a;
-  attend_pass<D, F32, SRC>(p, p.k, p.v, split, p.steps_per_split, b, u, j0, nq, smem, pos_all, a);
+  constexpr int CPT = Cfg::kCPT;  // columns per merge thread
+  PassOut<CPT> a;
+  attend_pass<D, F32, SRC, NW>(p, p.k, p.v, split, p.steps_per_split, b, u, j0, nq, smem, pos_all, a);
 
-  constexpr int CPT = D / 16;  // columns per merge thread
-  const int r = threadIdx.x >> 4;
-  const int c0 = (threadIdx.x & 15) * CPT;
+  const int r = threadIdx.x / Cfg::kTPR;
+  const int c0 = (threadIdx.x % Cfg::kTPR) * CPT;
   const int jr = j0 + r / p.g;
   const int hr = u * p.g + r % p.g;
   const size_t ooff = (((size_t)b * p.Tq + jr) * p.Hq + hr) * D + c0;
@@ -396,8 +401,8 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowAttnParams p) {
   float inv = 0.f;
   if constexpr (GATED) {
     __syncthreads();  // merge buffers are reused by the window pass
-    PassOut<D> w;
-    attend_pass<D, F32, SRC_WINDOW>(p, p.k2, p.v2, 0, 1 << 30, b, u, j0, nq, smem, pos_all, w);
+    PassOut<CPT> w;
+    attend_pass<D, F32, SRC_WINDOW, NW>(p, p.k2, p.v2, 0, 1 << 30, b, u, j0, nq, smem, pos_all, w);
     if (r >= nrows) return;
     const float* z = p.gate + (((size_t)b * p.Tq + jr) * p.Hq + hr) * 2;
     const double sg = 1.0 / (1.0 + exp(-(double)z[0]));
@@ -515,21 +520,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   if (p.lse && c == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = (float)lse0;
 }
 
-template <int D, bool F32>
+template <int D, bool F32, int NW>
 hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
   const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu);
+  const int threads = 64 * NW;
   if (gated) {
     if (src == SRC_TOKEN)
-      row_attn_kernel<D, F32, SRC_TOKEN, true><<<grid, 256, 0, stream>>>(p);
+      row_attn_kernel<D, F32, SRC_TOKEN, true, NW><<<grid, threads, 0, stream>>>(p);
     else
-      row_attn_kernel<D, F32, SRC_BLOCK, true><<<grid, 256, 0, stream>>>(p);
+      row_attn_kernel<D, F32, SRC_BLOCK, true, NW><<<grid, threads, 0, stream>>>(p);
     return hipGetLastError();
   }
   switch (src) {
-    case SRC_RANGE: row_attn_kernel<D, F32, SRC_RANGE, false><<<grid, 256, 0, stream>>>(p); break;
-    case SRC_TOKEN: row_attn_kernel<D, F32, SRC_TOKEN, false><<<grid, 256, 0, stream>>>(p); break;
-    case SRC_BLOCK: row_attn_kernel<D, F32, SRC_BLOCK, false><<<grid, 256, 0, stream>>>(p); break;
-    case SRC_WINDOW: row_attn_kernel<D, F32, SRC_WINDOW, false><<<grid, 256, 0, stream>>>(p); break;
+    case SRC_RANGE: row_attn_kernel<D, F32, SRC_RANGE, false, NW><<<grid, threads, 0, stream>>>(p); break;
+    case SRC_TOKEN: row_attn_kernel<D, F32, SRC_TOKEN, false, NW><<<grid, threads, 0, stream>>>(p); break;
+    case SRC_BLOCK: row_attn_kernel<D, F32, SRC_BLOCK, false, NW><<<grid, threads, 0, stream>>>(p); break;
+    case SRC_WINDOW: row_attn_kernel<D, F32, SRC_WINDOW, false, NW><<<grid, threads, 0, stream>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -537,12 +543,17 @@ hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t
 }  // namespace
 
 hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
-                           hipStream_t stream, bool gated) {
+                           hipStream_t stream, bool gated, bool wide) {
+  if (wide) {  // 8 waves: bf16 only (the fp32 variants need more registers than that allows)
+    if (in_f32) return hipErrorInvalidValue;
+    return head_dim == 128 ? launch_ra<128, false, 8>(p, src, gated, stream)
+                           : launch_ra<64, false, 8>(p, src, gated, stream);
+  }
   if (head_dim == 128)
-    return in_f32 ? launch_ra<128, true>(p, src, gated, stream)
-                  : launch_ra<128, false>(p, src, gated, stream);
-  return in_f32 ? launch_ra<64, true>(p, src, gated, stream)
-                : launch_ra<64, false>(p, src, gated, stream);
+    return in_f32 ? launch_ra<128, true, 4>(p, src, gated, stream)
+                  : launch_ra<128, false, 4>(p, src, gated, stream);
+  return in_f32 ? launch_ra<64, true, 4>(p, src, gated, stream)
+                : launch_ra<64, false, 4>(p, src, gated, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream) {

@@ -61,9 +61,10 @@ struct CombineParams {
 };
 
 // gated: list source (token or block) then the window branch over k2, v2 in one workgroup,
-// combined with the sigmoid gates (requires n_split == 1).
+// combined with the sigmoid gates (requires n_split == 1).  wide: 8 waves per workgroup instead
+// of 4 (bf16 only), for unsplit key lists of few row-sets.
 hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
-                           hipStream_t stream, bool gated = false);
+                           hipStream_t stream, bool gated = false, bool wide = false);
 
 // Full causal attention for many queries per KV head (bf16): 256 (query, head) rows per
 // workgroup sharing LDS-staged K/V tiles.

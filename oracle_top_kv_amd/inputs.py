@@ -161,6 +161,24 @@ def make_inputs(wl: Workload, device="cpu", n_sparse: Optional[int] = None,
     return out
 
 
+def random_token_sets(batch: int, n_kv_heads: int, kv_len: int, k_global: int, window: int,
+                      seed: int, device="cpu"):
+    """Index sets of the token-sparse layer's shape for one decode query per (b, u) without running
+    the selection: k_global distinct positions drawn uniformly from 0 .. kv_len-window-1, sorted,
+    followed by the window kv_len-window .. kv_len-1.  Returns (idx int32 [B, 1, Hkv, k+w],
+    count int32 [B, 1, Hkv]).  Used to time the gather kernel over many batch sizes."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    r = torch.rand(batch, n_kv_heads, kv_len - window, device=device, generator=g)
+    top = r.topk(k_global, dim=-1).indices.sort(dim=-1).values.to(torch.int32)
+    win = torch.arange(kv_len - window, kv_len, device=device, dtype=torch.int32)
+    idx = torch.cat([top, win.expand(batch, n_kv_heads, window)], dim=-1)
+    idx = idx.reshape(batch, 1, n_kv_heads, k_global + window).contiguous()
+    cnt = torch.full((batch, 1, n_kv_heads), k_global + window, dtype=torch.int32, device=device)
+    return idx, cnt
+
+
 def to_numpy_f32(x: torch.Tensor):
     """Exact float32 copy on the host (bf16 widens exactly)."""
     return x.detach().float().cpu().numpy()

@@ -187,6 +187,11 @@ SPARSE_CASES = [
     ("decode_g4_token", Workload("dec", 3, 1, 6000, 32, 8, 128, "bf16", needles=8, seed=31)),
     ("decode_g16_token", Workload("d16", 2, 1, 2500, 64, 4, 128, "bf16", seed=32)),
     ("prefill_g4_token", Workload("pf", 1, 40, 1500, 8, 2, 128, "bf16", seed=33)),
+    # at least 96 (query, KV head) sets: one 8-wave workgroup per set, no split
+    ("prefill_g4_token_wide", Workload("pw", 1, 120, 2000, 8, 2, 128, "bf16", seed=35)),
+    ("decode_g4_token_wide", Workload("dw", 16, 1, 4000, 32, 8, 128, "bf16", seed=36)),
+    ("decode_g8_d64_token_wide", Workload("dw64", 12, 1, 3000, 64, 8, 64, "bf16",
+                                          k_global=500, window=64, seed=37)),
 ]
 
 
