@@ -28,9 +28,15 @@
  *     them [P2 engineering constraint 6: producer/consumer lifetime].
  *   - Workspace: every call takes a caller-owned device scratch buffer of at least
  *     hs_workspace_size(...) bytes (16-byte aligned); a smaller one returns HS_ERR_WORKSPACE.
- *   - Supported: head_dim in {64, 128}; g = Hq/Hkv integral; in_dtype bf16 or fp32; out_dtype
- *     bf16 or fp32.  Index-set selection (hs_oracle_topk, hs_block_score_topk) needs g in
- *     {4, 8, 16}.
+ *   - Supported: head_dim in {64, 128}; g = Hq/Hkv integral and at most 16; kv_len <= 2^30;
+ *     in_dtype bf16 or fp32; out_dtype bf16 or fp32.  Index-set selection (hs_oracle_topk,
+ *     hs_block_score_topk) needs g in {4, 8, 16}; block selection needs block a multiple of 16
+ *     and 1 <= n_blocks <= 64.  Anything else returns HS_ERR_UNSUPPORTED.
+ *   - Workspace sizes, for orientation: token selection with many query rows per KV head and
+ *     k_global <= 1024 keeps a 16 KiB candidate buffer per (b, t, u); with few rows it keeps
+ *     12 bytes per candidate key per (b, t, u) plus small histograms; split attention keeps
+ *     per-split partial rows (about 0.5 KiB each).  Full attention with many query rows and the
+ *     prefill-shaped block selection need none.
  */
 #ifndef HYSPARSE_H
 #define HYSPARSE_H
@@ -112,8 +118,8 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
 /* Sparse layer over the full layer's K, V and index set, with the layer's own queries q
  * [P2 "Cross-layer KV cache reuse", gather equations; P2 "Same query, two memories";
  * P4 section 3.3].
- *   kind == HS_IDX_TOKEN: idx [B, q_len, Hkv, idx_cap] token positions (ascending or not), the
- *     first count[b,j,u] entries valid; attention over exactly those keys.
+ *   kind == HS_IDX_TOKEN: idx [B, q_len, Hkv, idx_cap] distinct token positions (ascending or
+ *     not), the first count[b,j,u] entries valid; attention over exactly those keys.
  *   kind == HS_IDX_BLOCK: idx [B, q_len, Hkv, idx_cap] block ids, count valid; attention over
  *     the keys of those blocks (size `block`), masked causally inside a block that crosses t
  *     [P2 engineering constraint 4].

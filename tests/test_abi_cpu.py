@@ -88,6 +88,18 @@ def test_topk_argument_checks():
                             None) == hs.HS_ERR_UNSUPPORTED
 
 
+def test_block_topk_argument_checks():
+    L = hs.lib()
+    d = desc()  # g = 4
+    for block, n_blocks in ((48 + 8, 16), (64, 0), (64, 65)):
+        assert L.hs_block_score_topk(ctypes.byref(d), FAKE, FAKE, FAKE, block, n_blocks, FAKE, FAKE,
+                                     FAKE, 1 << 40, None) == hs.HS_ERR_UNSUPPORTED
+    d2 = desc(n_q_heads=4, n_kv_heads=2)  # g = 2
+    assert L.hs_block_score_topk(ctypes.byref(d2), FAKE, FAKE, FAKE, 64, 16, FAKE, FAKE, FAKE,
+                                 1 << 40, None) == hs.HS_ERR_UNSUPPORTED
+    assert L.hs_last_error().decode()
+
+
 def test_sparse_argument_checks():
     d = desc()
     L = hs.lib()

@@ -44,6 +44,10 @@ FULL_CASES = [
     ("prefill_bf16_g16_chunk", Workload("pf16", 1, 77, 3000, 32, 2, 128, "bf16", seed=15)),
     ("prefill_bf16_g8_d64_causal", Workload("pf8", 2, 300, 300, 16, 2, 64, "bf16", seed=16)),
     ("prefill_bf16_g4_causal_long", Workload("pf4", 1, 700, 700, 8, 2, 128, "bf16", seed=17)),
+    # group sizes outside the pages' models: 1 and 2 on the prefill kernel, 12 on the row kernel
+    ("prefill_bf16_g1", Workload("pg1", 1, 300, 500, 4, 4, 128, "bf16", seed=18)),
+    ("prefill_bf16_g2_d64", Workload("pg2", 2, 130, 400, 8, 4, 64, "bf16", seed=19)),
+    ("prefill_bf16_g12", Workload("pg12", 1, 40, 600, 24, 2, 128, "bf16", seed=20)),
 ]
 
 
@@ -192,6 +196,8 @@ SPARSE_CASES = [
     ("decode_g4_token_wide", Workload("dw", 16, 1, 4000, 32, 8, 128, "bf16", seed=36)),
     ("decode_g8_d64_token_wide", Workload("dw64", 12, 1, 3000, 64, 8, 64, "bf16",
                                           k_global=500, window=64, seed=37)),
+    ("decode_g1_token", Workload("dg1", 2, 1, 3000, 8, 8, 128, "bf16", seed=38)),
+    ("prefill_g2_token", Workload("pg2", 1, 30, 1500, 4, 2, 128, "bf16", seed=39)),
 ]
 
 
