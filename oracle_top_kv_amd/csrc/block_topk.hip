@@ -95,12 +95,8 @@ __global__ __launch_bounds__(256) void blk_score_kernel(BlockTopkParams p) {
   const long long key_begin = blk_begin * p.block;
   long long key_end = blk_end * p.block;
   if (key_end > t_last + 1) key_end = t_last + 1;
-  KTile<D, F32> cur, nxt;
-  long long tile = key_begin + 64LL * wave;
-  if (tile < key_end) load_k_tile<D, F32>(cur, p.k, kv_base, kv_row_stride, tile, p.Tk, rn, jg);
-  for (; tile < key_end; tile += 64LL * 4) {
-    if (tile + 256 < key_end)
-      load_k_tile<D, F32>(nxt, p.k, kv_base, kv_row_stride, tile + 256, p.Tk, rn, jg);
+  // one 64-key tile already in registers
+  auto score_tile = [&](const KTile<D, F32>& cur, long long tile) {
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
       const long long g0 = tile + 16 * kb;  // first key of the group
@@ -109,21 +105,28 @@ __global__ __launch_bounds__(256) void blk_score_kernel(BlockTopkParams p) {
       float v = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[e], p.scale_log2, -delta[e]));
-      if (G >= 2) v = fmaxf(v, __shfl_xor(v, 16, 64));
-      if (G >= 4) v = fmaxf(v, __shfl_xor(v, 32, 64));
+      if (G >= 2) v = max_xor16(v);
+      if (G >= 4) v = max_xor32(v);
       // causal: keys after this lane's query position do not count
       if (pos > t_own || pos >= key_end) v = -INFINITY;
       // max over the 16 keys of the group (lanes of one 16-lane row)
-      v = fmaxf(v, __shfl_xor(v, 1, 64));
-      v = fmaxf(v, __shfl_xor(v, 2, 64));
-      v = fmaxf(v, __shfl_xor(v, 4, 64));
-      v = fmaxf(v, __shfl_xor(v, 8, 64));
+      v = max16(v);
       const long long blk = g0 / p.block;
       if (owner && rn == 0 && g0 < key_end && g0 <= t_own)
         atomicMax(&bmax[jq_own][blk - blk_begin], float_key(v));
     }
+  };
+  // The loop always prefetches the next tile (the last tile is peeled off): with a conditional
+  // prefetch the compiler waits for the prefetched loads before computing each tile.
+  KTile<D, F32> cur, nxt;
+  long long tile = key_begin + 64LL * wave;
+  if (tile < key_end) load_k_tile<D, F32>(cur, p.k, kv_base, kv_row_stride, tile, p.Tk, rn, jg);
+  for (; tile + 256 < key_end; tile += 64LL * 4) {
+    load_k_tile<D, F32>(nxt, p.k, kv_base, kv_row_stride, tile + 256, p.Tk, rn, jg);
+    score_tile(cur, tile);
     cur = nxt;
   }
+  if (tile < key_end) score_tile(cur, tile);
   __syncthreads();
   for (int i = threadIdx.x; i < 4 * n_range; i += 256) {
     const int jq = i / n_range, rb = i % n_range;

@@ -65,17 +65,20 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// Exchanges between 16-lane rows with the gfx950 swap instructions (VALU, no LDS crossbar).
+// v_permlane16_swap(x, x) returns, in each lane, x of that lane and of the same lane in the
+// partner row (rows 0<->1, 2<->3); v_permlane32_swap(x, x) does the same for the two halves.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
 
-// max / sum over the 4 lanes {n, n+16, n+32, n+48} (one MFMA row spread over 4 lane groups)
-__device__ __forceinline__ float max4groups(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  return fmaxf(v, shfl_xor_f(v, 32));
-}
-__device__ __forceinline__ float sum4groups(float v) {
-  v += shfl_xor_f(v, 16);
-  return v + shfl_xor_f(v, 32);
-}
+// max over the 4 lanes {n, n+16, n+32, n+48} (one MFMA row spread over 4 lane groups)
+__device__ __forceinline__ float max4groups(float v) { return max_xor32(max_xor16(v)); }
 
 // Lane exchanges inside a 16-lane row with DPP (no LDS crossbar): quad_perm [1,0,3,2] and
 // [2,3,0,1], then the half-row and row mirrors.  After the four steps of max16 / min16_u64 every
