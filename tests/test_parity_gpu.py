@@ -93,6 +93,9 @@ TOPK_CASES = [
                                          k_global=1024, window=128, seed=25)),
     ("prefill_g8_d64_small_k", Workload("pf8", 2, 100, 3000, 16, 2, 64, "bf16", k_global=50,
                                         window=10, seed=26)),
+    # longer than 65536 keys: the multi-kernel boundary-list selection
+    ("decode_g4_70k", Workload("dl", 1, 1, 70000, 32, 8, 128, "bf16", k_global=300, window=64,
+                               needles=8, seed=27)),
 ]
 
 
