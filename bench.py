@@ -10,7 +10,8 @@ Inputs are generated on the GPU before timing and stay resident in HBM.
 
 Prints ONE JSON line.  `value` is the step's algorithmic HBM bytes (what the method must read: K
 and V once for full attention, K once for each scoring pass, the index-set rows of K and V for
-each sparse layer) divided by the step time (`ms_per_step_graph`: the same step replayed from a HIP graph).
+each sparse layer) divided by the step time (`ms_per_step_graph`: the same step replayed from a
+HIP graph).
 Per-stage times come from HIP events recorded on the stream the library launches on.
 """
 import argparse
