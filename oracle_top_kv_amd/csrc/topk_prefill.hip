@@ -172,7 +172,7 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
 
 // G: query heads per KV head (4, 8 or 16).  NE: block-list entries per lane (n_blocks <= 16 NE).
 template <int D, bool F32, bool BLOCK, int G, int NE>
-__global__ __launch_bounds__(kThreads, 2) void pf_select_kernel(PrefillSelectParams p) {
+__global__ __launch_bounds__(kThreads, F32 ? 1 : 2) void pf_select_kernel(PrefillSelectParams p) {
   using C = PsCfg<D, F32>;
   constexpr int NW = kThreads / 64;  // waves
   constexpr int HQ = G / 4;          // head quarters per query
