@@ -96,6 +96,13 @@ TOPK_CASES = [
     # longer than 65536 keys: the multi-kernel boundary-list selection
     ("decode_g4_70k", Workload("dl", 1, 1, 70000, 32, 8, 128, "bf16", k_global=300, window=64,
                                needles=8, seed=27)),
+    # degenerate budgets: no forced window; window only (k_global = 0)
+    ("decode_g4_no_window", Workload("dnw", 2, 1, 3000, 16, 4, 128, "bf16", k_global=200,
+                                     window=0, seed=28)),
+    ("prefill_g4_no_window", Workload("pnw", 1, 60, 900, 8, 2, 128, "bf16", k_global=100,
+                                      window=0, seed=29)),
+    ("prefill_g8_window_only", Workload("pwo", 1, 50, 700, 16, 2, 64, "bf16", k_global=0,
+                                        window=40, seed=30)),
 ]
 
 
@@ -167,6 +174,11 @@ BLOCK_CASES = [
                                        n_blocks=3, seed=56)),
     ("prefill_g4_b128_generic", Workload("bpg", 1, 30, 1500, 8, 2, 128, "bf16", block=128,
                                          n_blocks=5, seed=57)),
+    # more than 16 blocks per list (4 register entries per lane on the prefill path); the most
+    ("prefill_g4_b32_40blocks", Workload("bp40", 1, 70, 3000, 8, 2, 128, "bf16", block=32,
+                                         n_blocks=40, seed=58)),
+    ("decode_g8_b64_64blocks", Workload("bd64", 2, 1, 6000, 32, 4, 128, "bf16", block=64,
+                                        n_blocks=64, seed=59)),
 ]
 
 
@@ -279,3 +291,35 @@ def test_block_sparse_gated_swa_matches_oracle(name, wl):
     eo = max_abs(o.cpu().numpy(), o_ref)
     say(f"  max|dO| = {eo:.3e}")
     assert eo <= tol
+
+
+def test_sparse_token_empty_index_sets():
+    """Sets with count 0 attend over nothing: output 0 and LSE -inf; the other sets as usual."""
+    wl = Workload("emp", 2, 3, 1200, 8, 2, 128, "bf16", k_global=64, window=16, seed=60)
+    say(f"[sparse empty sets] {wl}")
+    x = make_inputs(wl)
+    qn, kn, vn = (to_numpy_f32(x[n]) for n in ("q", "k", "v"))
+    oi, oc = oracle.token_topk(qn, kn, None, wl.k_global, wl.window)
+    empty = np.zeros_like(oc, dtype=bool)
+    empty[1, 2, 0] = empty[0, 0, 1] = True
+    oc_gpu = oc.copy()
+    oc_gpu[empty] = 0
+    qs = x["q_sparse"][0]
+    o, lse = hs().sparse_attn_gather(to_dev(qs), to_dev(x["k"]), to_dev(x["v"]),
+                                     torch.from_numpy(oi).cuda(), torch.from_numpy(oc_gpu).cuda(),
+                                     kind="token", out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    o_ref, lse_ref = oracle.masked_attention(to_numpy_f32(qs), kn, vn, oi, oc)
+    g = wl.group
+    for b in range(wl.batch):
+        for j in range(wl.q_len):
+            for u in range(wl.n_kv_heads):
+                hs_ = slice(u * g, (u + 1) * g)
+                if empty[b, j, u]:
+                    assert (o[b, j, hs_] == 0).all()
+                    assert np.isneginf(lse[b, hs_, j]).all()
+                else:
+                    assert max_abs(o[b, j, hs_], o_ref[b, j, hs_]) <= TOL_BF16
+                    assert max_abs(lse[b, hs_, j], lse_ref[b, hs_, j]) <= 2e-6
+
