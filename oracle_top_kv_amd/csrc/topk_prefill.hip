@@ -98,6 +98,12 @@ __device__ __forceinline__ void wave_find_bin(const uint32_t* h, int k, int lane
   *bin_count = __shfl(my_cnt, src, 64);
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // Keep exactly the k largest of the n (> k) entries of `buf`; returns the new threshold theta
 // (entries >= theta are the ones kept, compacted to buf[0..k)).  Wave-wide.  If `sorted_pos`
 // is given, the kept positions (~low word) are also written there, unordered.
@@ -109,9 +115,28 @@ __device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k
     const int idx = lane + 64 * i;
     v[i] = idx < n ? ld_coherent(buf + idx) : 0ull;
   }
-  unsigned long long prefix = 0ull, pmask = 0ull;
+  // Start below the bits that all entries share: the entries are scores near the top of the
+  // row, so their leading bits coincide, and a histogram of them would send every lane's atomic
+  // to the same LDS bin.
+  unsigned long long vmin = ~0ull, vmax = 0ull;
+#pragma unroll
+  for (int i = 0; i < kNPL; i++) {
+    if (v[i] != 0ull) {
+      vmin = v[i] < vmin ? v[i] : vmin;
+      vmax = v[i] > vmax ? v[i] : vmax;
+    }
+  }
+  for (int m = 1; m < 64; m <<= 1) {
+    const unsigned long long a = shfl_xor_u64(vmin, m), c = shfl_xor_u64(vmax, m);
+    vmin = a < vmin ? a : vmin;
+    vmax = c > vmax ? c : vmax;
+  }
+  int start = 56;  // first 8-bit digit that holds a differing bit
+  if (vmin < vmax) start = ((63 - __clzll((long long)(vmin ^ vmax))) / 8) * 8;
+  unsigned long long pmask = start == 56 ? 0ull : ~((1ull << (start + 8)) - 1ull);
+  unsigned long long prefix = vmin & pmask;
   int kk = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (int shift = start; shift >= 0; shift -= 8) {
 #pragma unroll
     for (int q = 0; q < 4; q++) hist[4 * lane + q] = 0u;
     wave_sync_lds();
