@@ -232,40 +232,51 @@ def counter_traffic(workload):
 
 
 def prefill_leg(args):
-    """Full attention + token top-k on the 80B-shaped prefill chunk (4096 queries appended to a
-    131072-token cache, 64/4 heads, d 128, bf16): TFLOP/s of the full-attention flops plus the
-    score-recompute flops over the two calls' time, and of the full-attention flops alone."""
+    """Full attention + token top-k + one token-sparse layer on the 80B-shaped prefill chunk
+    (4096 queries appended to a 131072-token cache, 64/4 heads, d 128, bf16): TFLOP/s of the
+    full-attention flops plus the score-recompute flops over the first two calls' time, of the
+    full-attention flops alone, and the sparse layer's time with its logical gathered bytes
+    (every query's index-set rows; neighbouring queries share most of them in cache)."""
     import torch
 
     from oracle_top_kv_amd import costs, hs
     from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs
 
     wl = WORKLOADS["prefill_80b_128k"]
-    x = make_inputs(wl, device=torch.device("cuda:0"), n_sparse=0)
-    q, k, v = x["q"], x["k"], x["v"]
+    x = make_inputs(wl, device=torch.device("cuda:0"), n_sparse=1)
+    q, k, v, qs = x["q"], x["k"], x["v"], x["q_sparse"][0]
     for _ in range(2):
         _, lse = hs.full_attn_fwd(q, k, v)
-        hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+        idx, cnt = hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+        hs.sparse_attn_gather(qs, k, v, idx, cnt, kind="token")
     torch.cuda.synchronize()
     reps = 3
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
     for r in range(reps):
         ev[r][0].record()
         _, lse = hs.full_attn_fwd(q, k, v)
         ev[r][1].record()
-        hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+        idx, cnt = hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
         ev[r][2].record()
+        hs.sparse_attn_gather(qs, k, v, idx, cnt, kind="token")
+        ev[r][3].record()
     torch.cuda.synchronize()
     t_fa = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
     t_tk = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    t_sp = sum(e[2].elapsed_time(e[3]) for e in ev) / reps
     f_fa, f_sc = costs.full_attn_flops(wl), costs.score_flops(wl)
     tot = (f_fa + f_sc) / ((t_fa + t_tk) * 1e-3) / 1e12
+    b_sp = costs.token_gather_bytes(wl)  # rows each (b, t, u) gathers (mostly from cache)
+    f_sp = costs.sparse_flops(wl)
     return {"workload": wl.name, "full_attn_ms": round(t_fa, 3), "topk_ms": round(t_tk, 3),
             "full_attn_tflops": round(f_fa / (t_fa * 1e-3) / 1e12, 1),
             "topk_score_tflops": round(f_sc / (t_tk * 1e-3) / 1e12, 1),
             "full_attn_plus_topk_tflops": round(tot, 1),
             "useful_tflops": round(f_fa / ((t_fa + t_tk) * 1e-3) / 1e12, 1),
             "mfma_frac_full_attn": round(f_fa / (t_fa * 1e-3) / 2.5e15, 4),
+            "sparse_layer_ms": round(t_sp, 3),
+            "sparse_layer_logical_GB_per_s": round(b_sp / (t_sp * 1e-3) / 1e9, 1),
+            "sparse_layer_tflops": round(f_sp / (t_sp * 1e-3) / 1e12, 1),
             "peak_tflops": 2500.0, "reps": reps}
 
 

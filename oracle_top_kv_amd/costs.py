@@ -89,3 +89,8 @@ def block_gather_bytes(wl, elem_bytes=2):
     K', V' per (b, t, u) (upper bound at full blocks and a full window)."""
     rows = wl.n_blocks * wl.block + wl.window
     return wl.batch * wl.q_len * wl.n_kv_heads * rows * 2 * wl.head_dim * elem_bytes
+
+
+def sparse_flops(wl):
+    """Token-sparse layer: 4 d flops (QK and PV) per (query head, selected key)."""
+    return 4 * wl.head_dim * wl.n_q_heads * (token_gather_bytes(wl) // (2 * wl.head_dim * 2 * wl.n_kv_heads))
