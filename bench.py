@@ -11,7 +11,8 @@ Inputs are generated on the GPU before timing and stay resident in HBM.
 Prints ONE JSON line.  `value` is the step's algorithmic HBM bytes (what the method must read: K
 and V once for full attention, K once for each scoring pass, the index-set rows of K and V for
 each sparse layer) divided by the step time (`ms_per_step_graph`: the same step replayed from a
-HIP graph).
+HIP graph).  `step_stored_logits` times the same step with full attention keeping its logits
+and both selections reading them back instead of re-reading K (its own bytes and GB/s).
 Per-stage times come from HIP events recorded on the stream the library launches on.
 """
 import argparse
@@ -105,6 +106,28 @@ def main():
                               swa=(kl, vl, gate, wl.window))
         mark(5)
 
+    # The same step with the selection reading the logits that full attention stored, instead
+    # of recomputing them from Q and K (decode only: the logits are B * Hq * kv_len floats).
+    def step_logits(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        o, lse, lg = hs.full_attn_fwd_logits(q, k, v)
+        mark(1)
+        idx, cnt = hs.oracle_topk_from_logits(lg, lse, wl.n_kv_heads, wl.head_dim, wl.k_global,
+                                              wl.window)
+        mark(2)
+        for l in range(wl.n_sparse):
+            hs.sparse_attn_gather(qs[l], k, v, idx, cnt, kind="token")
+        mark(3)
+        bidx, bcnt = hs.block_topk_from_logits(lg, lse, wl.n_kv_heads, wl.head_dim, wl.block,
+                                               wl.n_blocks)
+        mark(4)
+        hs.sparse_attn_gather(qs[0], k, v, bidx, bcnt, kind="block", block=wl.block,
+                              swa=(kl, vl, gate, wl.window))
+        mark(5)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -150,6 +173,20 @@ def main():
     del graph
     ms_step = ms_step_eager
 
+    # the stored-logits step, timed the same way (eager)
+    for _ in range(args.warmup):
+        step_logits()
+    evl = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step_logits(evl[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step_logits = t_start.elapsed_time(t_end) / args.steps
+    stage_ms_logits = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evl) / args.steps
+                       for i, name in enumerate(stages)}
+
     # algorithmic bytes per stage
     b_full = costs.full_attn_kv_bytes(wl)                 # K and V read once
     b_score = costs.score_k_bytes(wl)                     # K read once per scoring pass
@@ -169,6 +206,20 @@ def main():
     stages_out["sparse_token"]["per_layer_gathered_bytes"] = b_tok
     dom = "full_attn"
     achieved = stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+
+    # stored-logits step: full attention also writes the logits; each selection reads them back
+    b_logits = costs.logit_bytes(wl)
+    stage_bytes_l = {"full_attn": b_full + b_logits, "token_topk": b_logits,
+                     "sparse_token": wl.n_sparse * b_tok, "block_topk": b_logits,
+                     "sparse_block_swa": b_blk}
+    total_bytes_l = sum(stage_bytes_l.values())
+    logits_out = {"ms_per_step": round(ms_step_logits, 4), "step_bytes": total_bytes_l,
+                  "GB_per_s": round(total_bytes_l / (ms_step_logits * 1e-3) / 1e9, 1),
+                  "speedup_vs_recompute": round(ms_step / ms_step_logits, 3), "stages": {}}
+    for n in stages:
+        gbs = stage_bytes_l[n] / (stage_ms_logits[n] * 1e-3) / 1e9
+        logits_out["stages"][n] = {"ms": round(stage_ms_logits[n], 4), "GB_per_s": round(gbs, 1),
+                                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
 
     out = {
         "metric": METRIC,
@@ -195,6 +246,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": b_full, "traffic": counter_traffic(wl.name)},
+        "step_stored_logits": logits_out,
     }
     if not args.no_prefill or not args.no_sweep:
         del x, q, k, v, qs, kl, vl, gate

@@ -64,8 +64,11 @@ typedef enum {
   HS_OP_FULL_ATTN = 0,   /* p0, p1 unused */
   HS_OP_ORACLE_TOPK = 1, /* p0 = k_global, p1 = window */
   HS_OP_BLOCK_TOPK = 2,  /* p0 = block, p1 = n_blocks */
-  HS_OP_SPARSE_ATTN = 3  /* p0 = number of keys per index set (token cap, or n_blocks*block);
+  HS_OP_SPARSE_ATTN = 3, /* p0 = number of keys per index set (token cap, or n_blocks*block);
                             p1 = SWA window (0: no SWA branch) */
+  HS_OP_FULL_ATTN_LOGITS = 4,       /* p0, p1 unused */
+  HS_OP_TOPK_FROM_LOGITS = 5,       /* p0 = k_global, p1 = window */
+  HS_OP_BLOCK_TOPK_FROM_LOGITS = 6  /* p0 = block, p1 = n_blocks */
 } hs_op;
 
 typedef struct {
@@ -132,6 +135,44 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
                                 const int32_t* count, int32_t idx_cap, int32_t block,
                                 const hs_swa_branch* swa, void* o, float* lse_opt, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/* ---- Selection from stored logits (decode) ------------------------------------------------
+ * With few query rows per call, full attention can keep the logits it computes, so that the
+ * index selection reads them back instead of recomputing them from Q and K.  The pages allow
+ * either way of getting the normalized scores: computing them once the LSE is known, in a
+ * second pass, or from values kept during the attention pass [P2 "Why normalize scores for
+ * TopK" and "Extracting block scores from exact attention"].  The result is the same index set;
+ * the traffic changes: per (b, t, u) the scores cost 4 g bytes per key written and read back,
+ * against 2 d bytes of K re-read per key.  Meant for decode (q_len of a few rows): the logit
+ * array holds B * q_len * Hq * kv_len floats. */
+
+/* hs_full_attn_fwd that also stores every dot product q_t . k_i it computes (fp32, before the
+ * 1/sqrt(d) scale) to logits: [B, q_len, Hq, kv_len] fp32, caller-owned, 4-byte aligned (16 for
+ * full-width stores).  Entries i <= t of query row t are the attention logits times sqrt(d);
+ * entries past t are unspecified (those of the last query row's range are written, larger ones
+ * not).  Always runs on the split row kernel, whatever q_len is; o and lse are bit-identical to
+ * what hs_full_attn_fwd returns for the same inputs on that kernel (q_len * g <= 16, or fp32
+ * inputs).  Workspace: hs_workspace_size(HS_OP_FULL_ATTN_LOGITS, ...). */
+hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const void* k,
+                                  const void* v, void* o, float* lse, float* logits, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* hs_oracle_topk with the scores taken from logits (as stored by hs_full_attn_fwd_logits for the
+ * same desc) and lse instead of Q and K: same index set, same layout and padding of idx and
+ * count.  desc->in_dtype is not used; head_dim sets the 1/sqrt(d) scale.  Any group size
+ * g <= 16.  Workspace: hs_workspace_size(HS_OP_TOPK_FROM_LOGITS, desc, k_global, window). */
+hs_status hs_oracle_topk_from_logits(const hs_attn_desc* desc, const float* logits,
+                                     const float* lse, int32_t k_global, int32_t window,
+                                     int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/* hs_block_score_topk with the block scores taken from logits and lse: same blocks, layout and
+ * padding.  Any group size g <= 16; block a multiple of 16; 1 <= n_blocks <= 64.  Workspace:
+ * hs_workspace_size(HS_OP_BLOCK_TOPK_FROM_LOGITS, desc, block, n_blocks). */
+hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logits,
+                                    const float* lse, int32_t block, int32_t n_blocks,
+                                    int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /* Bytes of workspace the call `op` needs for `desc` (p0, p1 as documented on hs_op).  Returns 0
  * for an invalid description (hs_last_error() says why). */

@@ -98,6 +98,18 @@ def full_attention(q, k, v, q_offset=None, rows=None):
     return o, lse
 
 
+def logit_row(q, k, b, j, h, q_offset=None):
+    """Scaled logits a_{t,i} = q.k_i / sqrt(d), i = 0..t, of one (b, j, h)."""
+    s = _shape(q, k, q_offset)
+    q, qp = _f32(q)
+    k, kp = _f32(k)
+    t = s.q_offset + j
+    a = np.empty(t + 1)
+    _check(lib().orc_logit_row(ctypes.byref(s), qp, kp, b, j, h,
+                               a.ctypes.data_as(ctypes.c_void_p)), "logit_row")
+    return a
+
+
 def prob_row(q, k, b, j, h, lse=None, q_offset=None):
     """Per-head normalized probabilities p_{t,i}, i = 0..t, of one (b, j, h)."""
     s = _shape(q, k, q_offset)

@@ -140,6 +140,17 @@ static void work_item(const work_list* w, int64_t it, int* b, int* j, int* h) {
   *j = w->rows ? w->rows[jr] : jr;
 }
 
+/* Logits a_{t,i}, i = 0..t, of one (b, j, h): the first step above, exported so that stored
+ * attention logits can be checked against it. */
+int orc_logit_row(const orc_shape* s, const float* q, const float* k, int b, int j, int h,
+                  double* a) {
+  if (!shape_ok(s) || !q || !k || !a) return ORC_EINVAL;
+  if (b < 0 || b >= s->batch || j < 0 || j >= s->q_len || h < 0 || h >= s->n_q_heads)
+    return ORC_EINVAL;
+  logits_row(s, q, k, b, j, h, a);
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* per-head probabilities                                                                      */
 /* ------------------------------------------------------------------------------------------ */

@@ -52,6 +52,10 @@ typedef struct {
 int orc_set_threads(int n);
 int orc_threads(void);
 
+/* Logits a_{t,i} = q_t . k_i / sqrt(d), i = 0..t, of one (b, j, h).  a must hold t+1 doubles. */
+int orc_logit_row(const orc_shape* s, const float* q, const float* k, int b, int j, int h,
+                  double* a);
+
 /* Per-head normalized probabilities p_{t,i} = exp(a_{t,i} - LSE_t), i = 0..t, for one
  * (b, j, h).  lse may be NULL (then LSE is recomputed from the row).  p must hold t+1 doubles. */
 int orc_prob_row(const orc_shape* s, const float* q, const float* k, const double* lse, int b,

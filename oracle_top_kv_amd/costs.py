@@ -94,3 +94,8 @@ def block_gather_bytes(wl, elem_bytes=2):
 def sparse_flops(wl):
     """Token-sparse layer: 4 d flops (QK and PV) per (query head, selected key)."""
     return 4 * wl.head_dim * wl.n_q_heads * (token_gather_bytes(wl) // (2 * wl.head_dim * 2 * wl.n_kv_heads))
+
+
+def logit_bytes(wl):
+    """Logits kept by full attention for the selections: one fp32 per (b, t, query head, key)."""
+    return 4 * wl.batch * wl.q_len * wl.n_q_heads * wl.kv_len

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -226,6 +227,60 @@ TkLayout tk_layout(const Shape& s, const TkGeom& t) {
 
 size_t tk_ws(const Shape& s, const TkGeom& t) { return tk_layout(s, t).total; }
 
+// Token selection from stored logits: one (b, t, u) row per workgroup and key chunk (chunks of
+// at least 1024 keys, multiples of 256); the selection passes are those of tk_geom.
+TkGeom tl_geom(const Shape& s) {
+  TkGeom t = tk_geom(s);
+  t.q_per_set = 1;
+  t.sets_per_bu = s.Tq;
+  long long want = (1024 + (long long)t.rows - 1) / (long long)t.rows;
+  const long long most = (s.Tk + 1023) / 1024;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  long long kps = (s.Tk + want - 1) / want;
+  kps = (kps + 255) / 256 * 256;
+  t.keys_per_split = (int)kps;
+  t.n_split = (int)((s.Tk + kps - 1) / kps);
+  return t;
+}
+
+// Decode-path parameters of the token selection (score pass from Q, K or from stored logits).
+hs::TopkDecodeParams tk_params(const Shape& s, const TkGeom& t, const float* lse, int k_global,
+                               int window, int32_t* idx, int32_t* count, void* ws) {
+  hs::TopkDecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.lse = lse;
+  p.B = s.B;
+  p.Tq = s.Tq;
+  p.Tk = s.Tk;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.g;
+  p.q_off = s.q_off;
+  p.k_global = k_global;
+  p.window = window;
+  p.q_per_set = t.q_per_set;
+  p.sets_per_bu = t.sets_per_bu;
+  p.n_split = t.n_split;
+  p.keys_per_split = t.keys_per_split;
+  p.sel_split = t.sel_split;
+  p.keys_per_sel = t.keys_per_sel;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  const TkLayout lay = tk_layout(s, t);
+  char* w = (char*)ws;
+  p.keys = (uint32_t*)(w + lay.keys);
+  p.hist = (uint32_t*)(w + lay.hist);
+  p.bcount = p.hist + t.rows * 2048;
+  p.blist = (unsigned long long*)(w + lay.blist);
+  p.above = (uint32_t*)(w + lay.above);
+  p.counts = (uint32_t*)(w + lay.counts);
+  p.state = (uint32_t*)(w + lay.state);
+  p.idx = idx;
+  p.cnt = count;
+  p.cap = k_global + window;
+  return p;
+}
+
 // Many query rows per KV head: selection streams over K tiles and stores no per-key score.
 bool use_prefill_select(const Shape& s, int k_global) {
   return (long long)s.Tq * s.g > 16 && (s.g == 4 || s.g == 8 || s.g == 16) &&
@@ -260,9 +315,9 @@ struct BkGeom {
   size_t rows;
 };
 
-BkGeom bk_geom(const Shape& s, int block, int n_blocks) {
+BkGeom bk_geom(const Shape& s, int block, int n_blocks, bool per_row = false) {
   BkGeom t;
-  t.q_per_set = 16 / s.g;
+  t.q_per_set = per_row ? 1 : 16 / s.g;
   t.sets_per_bu = (s.Tq + t.q_per_set - 1) / t.q_per_set;
   const long long n_sets = (long long)s.B * s.Hkv * t.sets_per_bu;
   const long long nblk = (s.Tk + block - 1) / block;
@@ -280,12 +335,13 @@ BkGeom bk_geom(const Shape& s, int block, int n_blocks) {
   return t;
 }
 
-hs_status bk_check(const Shape& s, int block, int n_blocks, BkGeom* g) {
+// per_row: selection from stored logits (one (b, t, u) row per workgroup, any group size)
+hs_status bk_check(const Shape& s, int block, int n_blocks, BkGeom* g, bool per_row = false) {
   if (block < 16 || block % 16) return fail(HS_ERR_UNSUPPORTED, "block %d: must be a multiple of 16", block);
   if (n_blocks < 1 || n_blocks > 64) return fail(HS_ERR_UNSUPPORTED, "n_blocks %d: must be 1..64", n_blocks);
-  if (s.g != 4 && s.g != 8 && s.g != 16)
+  if (!per_row && s.g != 4 && s.g != 8 && s.g != 16)
     return fail(HS_ERR_UNSUPPORTED, "block selection needs a GQA group of 4, 8 or 16 (got %d)", s.g);
-  *g = bk_geom(s, block, n_blocks);
+  *g = bk_geom(s, block, n_blocks, per_row);
   if ((long long)g->n_split * n_blocks > 4096)
     return fail(HS_ERR_UNSUPPORTED, "context too long for the block merge (%d splits)", g->n_split);
   return HS_OK;
@@ -335,6 +391,65 @@ size_t sparse_ws(const Shape& s, const SparseGeom& g, int window) {
   return b;
 }
 
+// Full attention on the row kernel (decode and short query blocks); logits != nullptr also
+// stores every computed dot product q.k to logits [B, Tq, Hq, Tk].
+hs_status row_full_attn(const Shape& s, const void* q, const void* k, const void* v, void* o,
+                        float* lse, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
+  const size_t need = g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hs::RowAttnParams p = ra_params(s, g);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.logits = logits;
+  p.logits_vec = logits && s.Tk % 4 == 0 && (uintptr_t)logits % 16 == 0;
+  p.final_direct = g.n_split == 1;
+  if (!p.final_direct) carve_partials(ws, g, s.D, &p.part_m, &p.part_l, &p.part_o);
+  hipStream_t hst = (hipStream_t)stream;
+  hipError_t e = hs::launch_row_attn(p, s.D, s.in_f32, hs::SRC_RANGE, hst);
+  if (e != hipSuccess) return hip_status(e, "full attention kernel");
+  if (!p.final_direct) {
+    hs::CombineParams c = combine_params(s, g, o, lse);
+    c.n_branch = 1;
+    c.m[0] = p.part_m;
+    c.l[0] = p.part_l;
+    c.po[0] = p.part_o;
+    c.n_split[0] = g.n_split;
+    e = hs::launch_combine(c, s.D, hst);
+    if (e != hipSuccess) return hip_status(e, "combine kernel");
+  }
+  return ok();
+}
+
+hs::BlockTopkParams bk_params(const Shape& s, const BkGeom& g, const float* lse, int block,
+                              int n_blocks, int32_t* blk_idx, int32_t* count, void* ws) {
+  hs::BlockTopkParams p;
+  memset(&p, 0, sizeof(p));
+  p.lse = lse;
+  p.B = s.B;
+  p.Tq = s.Tq;
+  p.Tk = s.Tk;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.g;
+  p.q_off = s.q_off;
+  p.block = block;
+  p.n_blocks = n_blocks;
+  p.q_per_set = g.q_per_set;
+  p.sets_per_bu = g.sets_per_bu;
+  p.n_split = g.n_split;
+  p.blocks_per_split = g.blocks_per_split;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  p.cand = (unsigned long long*)ws;
+  p.blk_idx = blk_idx;
+  p.cnt = count;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -374,6 +489,16 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
       if (p0 < 1 || p1 < 0) return 0;
       return sparse_ws(s, sparse_geom(s, p0, p1), p1);
     }
+    case HS_OP_FULL_ATTN_LOGITS: {
+      const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
+      return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+    }
+    case HS_OP_TOPK_FROM_LOGITS: return tk_ws(s, tl_geom(s));
+    case HS_OP_BLOCK_TOPK_FROM_LOGITS: {
+      BkGeom g;
+      if (bk_check(s, p0, p1, &g, true) != HS_OK) return 0;
+      return bk_ws(g, p1);
+    }
   }
   fail(HS_ERR_INVALID_ARG, "unknown op %d", (int)op);
   return 0;
@@ -404,33 +529,58 @@ hs_status hs_full_attn_fwd(const hs_attn_desc* desc, const void* q, const void* 
     pp.out_f32 = s.out_f32;
     return hip_status(hs::launch_prefill_attn(pp, s.D, (hipStream_t)stream), "prefill attention kernel");
   }
-  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
-  const size_t need = g.n_split > 1 ? partial_bytes(g, s.D) : 0;
-  if (need > 0 && (!ws || ws_bytes < need))
-    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  hs::RowAttnParams p = ra_params(s, g);
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.lse = lse;
-  p.final_direct = g.n_split == 1;
-  if (!p.final_direct) carve_partials(ws, g, s.D, &p.part_m, &p.part_l, &p.part_o);
-  hipStream_t hst = (hipStream_t)stream;
-  hipError_t e = hs::launch_row_attn(p, s.D, s.in_f32, hs::SRC_RANGE, hst);
-  if (e != hipSuccess) return hip_status(e, "full attention kernel");
-  if (!p.final_direct) {
-    hs::CombineParams c = combine_params(s, g, o, lse);
-    c.n_branch = 1;
-    c.m[0] = p.part_m;
-    c.l[0] = p.part_l;
-    c.po[0] = p.part_o;
-    c.n_split[0] = g.n_split;
-    e = hs::launch_combine(c, s.D, hst);
-    if (e != hipSuccess) return hip_status(e, "combine kernel");
-  }
-  return ok();
+  return row_full_attn(s, q, k, v, o, lse, nullptr, ws, ws_bytes, stream);
 }
+
+hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const void* k,
+                                  const void* v, void* o, float* lse, float* logits, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  if (!q || !k || !v || !o || !lse || !logits) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if ((uintptr_t)logits % 4) return fail(HS_ERR_INVALID_ARG, "logits must be 4-byte aligned");
+  return row_full_attn(s, q, k, v, o, lse, logits, ws, ws_bytes, stream);
+}
+
+hs_status hs_oracle_topk_from_logits(const hs_attn_desc* desc, const float* logits,
+                                     const float* lse, int32_t k_global, int32_t window,
+                                     int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  if (!logits || !lse || !idx || !count) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (k_global < 0 || window < 0) return fail(HS_ERR_INVALID_ARG, "k_global and window must be >= 0");
+  if ((long long)k_global + window < 1) return fail(HS_ERR_INVALID_ARG, "k_global + window must be >= 1");
+  const TkGeom t = tl_geom(s);
+  const size_t need = tk_ws(s, t);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hs::TopkDecodeParams p = tk_params(s, t, lse, k_global, window, idx, count, ws);
+  p.logits = logits;
+  return hip_status(hs::launch_topk_from_logits(p, (hipStream_t)stream), "token top-k kernels");
+}
+
+hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logits,
+                                    const float* lse, int32_t block, int32_t n_blocks,
+                                    int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  if (!logits || !lse || !blk_idx || !count) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  BkGeom g;
+  st = bk_check(s, block, n_blocks, &g, true);
+  if (st != HS_OK) return st;
+  const size_t need = bk_ws(g, n_blocks);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hs::BlockTopkParams p = bk_params(s, g, lse, block, n_blocks, blk_idx, count, ws);
+  p.logits = logits;
+  return hip_status(hs::launch_block_from_logits(p, (hipStream_t)stream), "block top-k kernels");
+}
+
 
 hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k, const float* lse,
                          int32_t k_global, int32_t window, int32_t* idx, int32_t* count, void* ws,
@@ -461,39 +611,9 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
   const size_t need = tk_ws(s, t);
   if (!ws || ws_bytes < need)
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  hs::TopkDecodeParams p;
-  memset(&p, 0, sizeof(p));
+  hs::TopkDecodeParams p = tk_params(s, t, lse, k_global, window, idx, count, ws);
   p.q = q;
   p.k = k;
-  p.lse = lse;
-  p.B = s.B;
-  p.Tq = s.Tq;
-  p.Tk = s.Tk;
-  p.Hq = s.Hq;
-  p.Hkv = s.Hkv;
-  p.g = s.g;
-  p.q_off = s.q_off;
-  p.k_global = k_global;
-  p.window = window;
-  p.q_per_set = t.q_per_set;
-  p.sets_per_bu = t.sets_per_bu;
-  p.n_split = t.n_split;
-  p.keys_per_split = t.keys_per_split;
-  p.sel_split = t.sel_split;
-  p.keys_per_sel = t.keys_per_sel;
-  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
-  const TkLayout lay = tk_layout(s, t);
-  char* w = (char*)ws;
-  p.keys = (uint32_t*)(w + lay.keys);
-  p.hist = (uint32_t*)(w + lay.hist);
-  p.bcount = p.hist + t.rows * 2048;
-  p.blist = (unsigned long long*)(w + lay.blist);
-  p.above = (uint32_t*)(w + lay.above);
-  p.counts = (uint32_t*)(w + lay.counts);
-  p.state = (uint32_t*)(w + lay.state);
-  p.idx = idx;
-  p.cnt = count;
-  p.cap = k_global + window;
   return hip_status(hs::launch_topk_decode(p, s.D, s.in_f32, (hipStream_t)stream),
                     "token top-k kernels");
 }
@@ -521,28 +641,9 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
   const size_t need = bk_ws(g, n_blocks);
   if (!ws || ws_bytes < need)
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  hs::BlockTopkParams p;
-  memset(&p, 0, sizeof(p));
+  hs::BlockTopkParams p = bk_params(s, g, lse, block, n_blocks, blk_idx, count, ws);
   p.q = q;
   p.k = k;
-  p.lse = lse;
-  p.B = s.B;
-  p.Tq = s.Tq;
-  p.Tk = s.Tk;
-  p.Hq = s.Hq;
-  p.Hkv = s.Hkv;
-  p.g = s.g;
-  p.q_off = s.q_off;
-  p.block = block;
-  p.n_blocks = n_blocks;
-  p.q_per_set = g.q_per_set;
-  p.sets_per_bu = g.sets_per_bu;
-  p.n_split = g.n_split;
-  p.blocks_per_split = g.blocks_per_split;
-  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
-  p.cand = (unsigned long long*)ws;
-  p.blk_idx = blk_idx;
-  p.cnt = count;
   return hip_status(hs::launch_block_topk(p, s.D, s.in_f32, (hipStream_t)stream),
                     "block top-k kernels");
 }

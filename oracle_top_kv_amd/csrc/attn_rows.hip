@@ -37,6 +37,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not wait for this
+// wave's global stores to be acknowledged (the stored logits need no ordering before the merge).
+__device__ __forceinline__ void workgroup_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // NW: waves per workgroup (4, or 8 for unsplit key lists of few row-sets)
 template <int D, bool F32, int NW>
 struct RaCfg {
@@ -53,6 +61,14 @@ struct RaCfg {
   static constexpr int kSmem =
       (kWaves * kVTileBytes > kCombineBytes ? kWaves * kVTileBytes : kCombineBytes);
 };
+
+// Logits kept by the full-attention pass are staged per wave in LDS and written out every
+// kLogitSteps steps: a global store issued between the loads of the software pipeline delays the
+// wait for every later load until the store is acknowledged (the vector memory counter is in
+// order), so few, large store bursts cost far less than two small stores per step.
+constexpr int kLogitSteps = 4;
+constexpr int kLogitRow = kLogitSteps * kStep + 4;  // floats per staged row (padded)
+constexpr int kLogitWaveBytes = 16 * kLogitRow * 4;
 
 template <int SRC>
 __device__ __forceinline__ int entry_pos(const RowAttnParams& p, int e, int L, long long lo,
@@ -81,8 +97,9 @@ struct PassOut {
 
 // One split of one row-set over one key source (K, V given explicitly so that the gated layer
 // can run its window branch over K', V' in the same workgroup).  Ends with the four waves
-// merged; `smem` and `pos_all` are free again once the caller has synchronized.
-template <int D, bool F32, int SRC, int NW>
+// merged; `smem` and `pos_all` are free again once the caller has synchronized.  LOGITS (range
+// mode only): every lane also stores the raw dot products q.k it computed to p.logits.
+template <int D, bool F32, int SRC, int NW, bool LOGITS = false>
 __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* kmat,
                                             const void* vmat, int split, int steps_per_split,
                                             int b, int u, int j0, int nq, unsigned char* smem,
@@ -153,6 +170,36 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   const int step_begin = split * steps_per_split;
   const int step_end = min(step_begin + steps_per_split, n_steps);
   unsigned char* vtile = smem + wave * Cfg::kVTileBytes;
+
+  // LOGITS: this wave's staging rows [16][kLogitRow] behind the V tiles, the number of steps
+  // staged so far and the first step of the current batch
+  float* lbuf = nullptr;
+  int l_count = 0, l_base = 0;
+  if constexpr (LOGITS) {
+    static_assert(SRC == SRC_RANGE, "logits are written by the full-attention pass only");
+    lbuf = (float*)(smem + kWaves * Cfg::kVTileBytes + wave * kLogitWaveBytes);
+  }
+  // Write the n staged steps l_base, l_base + kWaves, ... of this wave to the logit array
+  // [B, Tq, Hq, Tk]: 128-byte pieces (32 keys of one row), 16 bytes per lane.
+  auto flush_logits = [&](int n) {
+    wave_lds_sync();  // staged values written by every lane
+    const int chunks = nrows * n * 8;
+    for (int c = lane; c < chunks; c += 64) {
+      const int r = c / (n * 8), li = (c / 8) % n, qd = c % 8;
+      const int e0 = (l_base + li * kWaves) * kStep + 4 * qd;  // range mode: entry = position
+      float* dst = p.logits + (((size_t)b * p.Tq + (j0 + r / p.g)) * p.Hq + u * p.g + r % p.g) *
+                                  (size_t)p.Tk + e0;
+      const f32x4 val = *(const f32x4*)(lbuf + r * kLogitRow + li * kStep + 4 * qd);
+      if (p.logits_vec && e0 + 3 < L) {
+        *(f32x4*)dst = val;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          if (e0 + e < L) dst[e] = val[e];
+      }
+    }
+    wave_lds_sync();  // staging rows free again
+  };
 
   // Positions of this split's key-list entries.  List modes stage them in LDS once (so the
   // K/V loads of the next step can be issued without waiting on an index load); range modes
@@ -233,6 +280,18 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
         sacc[0] = mfma_f32(ka0[s2], qf[s2], sacc[0]);
         sacc[1] = mfma_f32(ka1[s2], qf[s2], sacc[1]);
       }
+    }
+
+    if constexpr (LOGITS) {
+      // lane (row rn, group jg) holds the dot products of entries 16 kb + 4 jg + e of the step;
+      // keys past a row's own position are written as well (the caller ignores them)
+      const int slot = l_count % kLogitSteps;
+      if (slot == 0) l_base = step;
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+        *(f32x4*)(lbuf + rn * kLogitRow + slot * kStep + 16 * kb + 4 * jg) = sacc[kb];
+      l_count++;
+      if (slot == kLogitSteps - 1) flush_logits(kLogitSteps);
     }
 
     // scale to the log2 domain and mask
@@ -317,9 +376,12 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
     for (int n = 0; n < VL; n++) va[n] = vn[n];
   }
   if (step < step_end) compute_step(step, ka0, ka1, va);
+  if constexpr (LOGITS) {
+    if (l_count % kLogitSteps) flush_logits(l_count % kLogitSteps);
+  }
 
   // ---- merge the waves of this workgroup ----
-  __syncthreads();
+  workgroup_lds_sync();
   float* cO = (float*)smem;                     // [kWaves][16][D]
   float* cM = cO + kWaves * 16 * D;             // [kWaves][16]
   double* cL = (double*)(cM + kWaves * 16);     // [kWaves][16]
@@ -334,7 +396,7 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
     cM[wave * 16 + rn] = m_run;
     cL[wave * 16 + rn] = ld;
   }
-  __syncthreads();
+  workgroup_lds_sync();
 
   constexpr int CPT = Cfg::kCPT;
   const int r = threadIdx.x / Cfg::kTPR;
@@ -369,10 +431,15 @@ __device__ __forceinline__ float lse_of(const PassOut<CPT>& a) {
 // GATED: the HySparse sparse layer in one workgroup when neither branch is split -- the block
 // (or token) branch over K, V, then the sliding-window branch over K', V' (p.k2, p.v2), each
 // normalized on its own and weighted by its sigmoid gate [P2 "Same query, two memories"].
-template <int D, bool F32, int SRC, bool GATED, int NW>
+template <int D, bool F32, int SRC, bool GATED, int NW, bool LOGITS = false>
 __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   using Cfg = RaCfg<D, F32, NW>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::kSmem];
+  // LOGITS: the logit staging rows of every wave follow the V tiles
+  constexpr int kSmemBytes =
+      LOGITS && NW * (Cfg::kVTileBytes + kLogitWaveBytes) > Cfg::kSmem
+          ? NW * (Cfg::kVTileBytes + kLogitWaveBytes)
+          : Cfg::kSmem;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
   __shared__ int pos_all[kMaxListEntries];
 
   // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
@@ -390,7 +457,8 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
 
   constexpr int CPT = Cfg::kCPT;  // columns per merge thread
   PassOut<CPT> a;
-  attend_pass<D, F32, SRC, NW>(p, p.k, p.v, split, p.steps_per_split, b, u, j0, nq, smem, pos_all, a);
+  attend_pass<D, F32, SRC, NW, LOGITS>(p, p.k, p.v, split, p.steps_per_split, b, u, j0, nq, smem,
+                                       pos_all, a);
 
   const int r = threadIdx.x / Cfg::kTPR;
   const int c0 = (threadIdx.x % Cfg::kTPR) * CPT;
@@ -524,6 +592,14 @@ template <int D, bool F32, int NW>
 hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
   const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu);
   const int threads = 64 * NW;
+  if (p.logits) {
+    if constexpr (NW == 4) {
+      if (src != SRC_RANGE || gated) return hipErrorInvalidValue;
+      row_attn_kernel<D, F32, SRC_RANGE, false, 4, true><<<grid, threads, 0, stream>>>(p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (gated) {
     if (src == SRC_TOKEN)
       row_attn_kernel<D, F32, SRC_TOKEN, true, NW><<<grid, threads, 0, stream>>>(p);

@@ -154,6 +154,71 @@ __global__ __launch_bounds__(256) void blk_score_kernel(BlockTopkParams p) {
   }
 }
 
+// Block scores from the raw dot products q.k that the full-attention pass stored
+// ([B, Tq, Hq, Tk] fp32): same key and same local top-n as blk_score_kernel, without reading Q
+// or K.  One workgroup per (row, block split); a thread per key, a 16-lane row per 16 keys.
+template <int G>
+__global__ __launch_bounds__(256) void blk_logit_score_kernel(BlockTopkParams p) {
+  __shared__ unsigned long long bkey[kMaxRange];
+  __shared__ uint32_t bmax[kMaxRange];
+  __shared__ float dsh[16];
+  const int split = blockIdx.x % p.n_split;
+  const int row = blockIdx.x / p.n_split;  // (b * Tq + j) * Hkv + u
+  const int u = row % p.Hkv;
+  const int j = (row / p.Hkv) % p.Tq;
+  const int b = row / (p.Hkv * p.Tq);
+  const long long t = p.q_off + j;
+  const long long blk_begin = (long long)split * p.blocks_per_split;
+  long long blk_end = blk_begin + p.blocks_per_split;
+  if (blk_end > t / p.block + 1) blk_end = t / p.block + 1;
+  const int n_range = blk_end > blk_begin ? (int)(blk_end - blk_begin) : 0;
+  for (int i = threadIdx.x; i < kMaxRange; i += 256) {
+    bkey[i] = 0ull;
+    bmax[i] = 0u;
+  }
+  if (threadIdx.x < G) {
+    const double l2 = (double)p.lse[((size_t)b * p.Hq + u * G + threadIdx.x) * p.Tq + j] * 1.4426950408889634;
+    const double C = rint((double)p.lse[((size_t)b * p.Hq + u * G) * p.Tq + j] * 1.4426950408889634);
+    dsh[threadIdx.x] = (float)(l2 - C);
+  }
+  __syncthreads();
+  float delta[G];
+#pragma unroll
+  for (int hh = 0; hh < G; hh++) delta[hh] = dsh[hh];
+  const long long key_begin = blk_begin * p.block;  // a multiple of 16
+  long long key_end = blk_end * p.block;
+  if (key_end > t + 1) key_end = t + 1;
+  const float* lg = p.logits + (((size_t)b * p.Tq + j) * p.Hq + (size_t)u * G) * p.Tk;
+  for (long long base = key_begin; base < key_end; base += 256) {
+    const long long pos = base + threadIdx.x;
+    float v = -INFINITY;
+    if (pos < key_end) {
+      float x[G];
+#pragma unroll
+      for (int hh = 0; hh < G; hh++) x[hh] = lg[(size_t)hh * p.Tk + pos];
+#pragma unroll
+      for (int hh = 0; hh < G; hh++) v = fmaxf(v, __builtin_fmaf(x[hh], p.scale_log2, -delta[hh]));
+    }
+    // max over the 16 keys of this lane row (they lie in one block: block % 16 == 0)
+    v = max16(v);
+    if ((threadIdx.x & 15) == 0 && pos < key_end)
+      atomicMax(&bmax[pos / p.block - blk_begin], float_key(v));
+  }
+  __syncthreads();
+  for (int rb = threadIdx.x; rb < n_range; rb += 256)
+    bkey[rb] = ((unsigned long long)bmax[rb] << 32) |
+               (unsigned long long)(0xFFFFFFFFu - (uint32_t)(blk_begin + rb));
+  __syncthreads();
+  unsigned long long* out = p.cand + ((size_t)row * p.n_split + split) * p.n_blocks;
+  for (int c = threadIdx.x; c < n_range; c += 256) {
+    const unsigned long long kc = bkey[c];
+    int rank = 0;
+    for (int o = 0; o < n_range; o++) rank += bkey[o] > kc;
+    if (rank < p.n_blocks) out[rank] = kc;
+  }
+  for (int s = n_range + threadIdx.x; s < p.n_blocks; s += 256) out[s] = 0ull;
+}
+
 __global__ __launch_bounds__(256) void blk_merge_kernel(BlockTopkParams p) {
   extern __shared__ unsigned long long cand[];  // n_split * n_blocks
   __shared__ int sel_ids[64];
@@ -198,7 +263,38 @@ hipError_t launch_blk(const BlockTopkParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int G>
+hipError_t launch_blk_logits(const BlockTopkParams& p, hipStream_t stream) {
+  const size_t rows = (size_t)p.B * p.Tq * p.Hkv;
+  blk_logit_score_kernel<G><<<dim3((unsigned)(p.n_split * rows)), 256, 0, stream>>>(p);
+  const size_t smem = (size_t)p.n_split * p.n_blocks * sizeof(unsigned long long);
+  blk_merge_kernel<<<dim3((unsigned)rows), 256, smem, stream>>>(p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_block_from_logits(const BlockTopkParams& p, hipStream_t stream) {
+  switch (p.g) {
+    case 1: return launch_blk_logits<1>(p, stream);
+    case 2: return launch_blk_logits<2>(p, stream);
+    case 3: return launch_blk_logits<3>(p, stream);
+    case 4: return launch_blk_logits<4>(p, stream);
+    case 5: return launch_blk_logits<5>(p, stream);
+    case 6: return launch_blk_logits<6>(p, stream);
+    case 7: return launch_blk_logits<7>(p, stream);
+    case 8: return launch_blk_logits<8>(p, stream);
+    case 9: return launch_blk_logits<9>(p, stream);
+    case 10: return launch_blk_logits<10>(p, stream);
+    case 11: return launch_blk_logits<11>(p, stream);
+    case 12: return launch_blk_logits<12>(p, stream);
+    case 13: return launch_blk_logits<13>(p, stream);
+    case 14: return launch_blk_logits<14>(p, stream);
+    case 15: return launch_blk_logits<15>(p, stream);
+    case 16: return launch_blk_logits<16>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_block_topk(const BlockTopkParams& p, int head_dim, bool in_f32,
                              hipStream_t stream) {

@@ -42,6 +42,9 @@ struct RowAttnParams {
   const void* k2;
   const void* v2;
   const float* gate;  // [B, Tq, Hq, 2]
+  // full attention (range mode, 4 waves) may also store its raw dot products q.k:
+  float* logits;   // [B, Tq, Hq, Tk] fp32, or null
+  int logits_vec;  // 16-byte stores allowed (Tk % 4 == 0 and an aligned base)
 };
 
 // Merge of split partials (one or two branches) into O and LSE; with two branches the sigmoid
@@ -106,9 +109,13 @@ struct TopkDecodeParams {
   int32_t* idx;  // [B, Tq, Hkv, cap]
   int32_t* cnt;  // [B, Tq, Hkv]
   int cap;
+  // selection from stored logits instead of Q, K (launch_topk_from_logits; n_split chunks of
+  // keys_per_split keys per (b, t, u) row, multiples of 256)
+  const float* logits;  // [B, Tq, Hq, Tk] raw dot products q.k
 };
 hipError_t launch_topk_decode(const TopkDecodeParams& p, int head_dim, bool in_f32,
                               hipStream_t stream);
+hipError_t launch_topk_from_logits(const TopkDecodeParams& p, hipStream_t stream);
 
 // ---- block scores + top-n blocks ----------------------------------------------------------
 struct BlockTopkParams {
@@ -124,9 +131,13 @@ struct BlockTopkParams {
   unsigned long long* cand;  // workspace [rows][n_split][n_blocks]
   int32_t* blk_idx;          // [B, Tq, Hkv, n_blocks]
   int32_t* cnt;              // [B, Tq, Hkv]
+  // selection from stored logits instead of Q, K (launch_block_from_logits; one (b, t, u) row
+  // per workgroup and split, at most 256 blocks per split)
+  const float* logits;  // [B, Tq, Hq, Tk] raw dot products q.k
 };
 hipError_t launch_block_topk(const BlockTopkParams& p, int head_dim, bool in_f32,
                              hipStream_t stream);
+hipError_t launch_block_from_logits(const BlockTopkParams& p, hipStream_t stream);
 
 // ---- selection for many queries per KV head (prefill), streamed tile by tile -----------------
 struct PrefillSelectParams {

@@ -149,6 +149,55 @@ __global__ __launch_bounds__(256) void tk_score_kernel(TopkDecodeParams p) {
   }
 }
 
+// ---- 1'. score from stored logits ---------------------------------------------------------
+// Same key as the score pass, from the raw dot products q.k that the full-attention pass stored
+// ([B, Tq, Hq, Tk] fp32), so neither Q nor K is read again.  One workgroup per (row, key chunk);
+// a thread per key reads the G head values of its key (coalesced across the wave per head).
+template <int G>
+__global__ __launch_bounds__(256) void tk_logit_score_kernel(TopkDecodeParams p) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ float dsh[16];
+  const int split = blockIdx.x % p.n_split;
+  const int row = blockIdx.x / p.n_split;  // (b * Tq + j) * Hkv + u
+  const int u = row % p.Hkv;
+  const int j = (row / p.Hkv) % p.Tq;
+  const int b = row / (p.Hkv * p.Tq);
+  for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = 0u;
+  if (threadIdx.x < G) {
+    // per-head shift LSE_h * log2(e) - C, C from the group's first head (as in the score pass)
+    const double l2 = (double)p.lse[((size_t)b * p.Hq + u * G + threadIdx.x) * p.Tq + j] * 1.4426950408889634;
+    const double C = rint((double)p.lse[((size_t)b * p.Hq + u * G) * p.Tq + j] * 1.4426950408889634);
+    dsh[threadIdx.x] = (float)(l2 - C);
+  }
+  __syncthreads();
+  float delta[G];
+#pragma unroll
+  for (int hh = 0; hh < G; hh++) delta[hh] = dsh[hh];
+  const long long t = p.q_off + j;
+  const long long k_begin = (long long)split * p.keys_per_split;
+  long long k_end = k_begin + p.keys_per_split;
+  if (k_end > t - p.window + 1) k_end = t - p.window + 1;  // candidates 0 .. t - w
+  const float* lg = p.logits + (((size_t)b * p.Tq + j) * p.Hq + (size_t)u * G) * p.Tk;
+  uint32_t* keys_row = p.keys + (size_t)row * p.Tk;
+  for (long long pos = k_begin + threadIdx.x; pos < k_end; pos += 256) {
+    float x[G];
+#pragma unroll
+    for (int hh = 0; hh < G; hh++) x[hh] = lg[(size_t)hh * p.Tk + pos];
+    float v = -INFINITY;
+#pragma unroll
+    for (int hh = 0; hh < G; hh++) v = fmaxf(v, __builtin_fmaf(x[hh], p.scale_log2, -delta[hh]));
+    const uint32_t key = float_key(v);
+    keys_row[pos] = key;
+    atomicAdd(&hist[key >> 21], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = p.hist + (size_t)row * kBins;
+  for (int i = threadIdx.x; i < kBins; i += 256) {
+    const uint32_t c = hist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
 // ---- selection ----------------------------------------------------------------------------
 struct RowSel {
   int k_eff;  // number of candidates to take
@@ -373,7 +422,41 @@ hipError_t launch_tk(const TopkDecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int G>
+hipError_t launch_tk_logits(const TopkDecodeParams& p, hipStream_t stream) {
+  const size_t rows = (size_t)p.B * p.Tq * p.Hkv;
+  const size_t zero_words = rows * kBins + rows;
+  zero_u32_kernel<<<(unsigned)((zero_words + 255) / 256 < 1024 ? (zero_words + 255) / 256 : 1024), 256, 0, stream>>>(p.hist, zero_words);
+  tk_logit_score_kernel<G><<<dim3((unsigned)(p.n_split * rows)), 256, 0, stream>>>(p);
+  tk_collect_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
+  tk_finalize_kernel<<<dim3((unsigned)rows), 256, p.sel_split * sizeof(uint32_t), stream>>>(p);
+  tk_write_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_topk_from_logits(const TopkDecodeParams& p, hipStream_t stream) {
+  switch (p.g) {
+    case 1: return launch_tk_logits<1>(p, stream);
+    case 2: return launch_tk_logits<2>(p, stream);
+    case 3: return launch_tk_logits<3>(p, stream);
+    case 4: return launch_tk_logits<4>(p, stream);
+    case 5: return launch_tk_logits<5>(p, stream);
+    case 6: return launch_tk_logits<6>(p, stream);
+    case 7: return launch_tk_logits<7>(p, stream);
+    case 8: return launch_tk_logits<8>(p, stream);
+    case 9: return launch_tk_logits<9>(p, stream);
+    case 10: return launch_tk_logits<10>(p, stream);
+    case 11: return launch_tk_logits<11>(p, stream);
+    case 12: return launch_tk_logits<12>(p, stream);
+    case 13: return launch_tk_logits<13>(p, stream);
+    case 14: return launch_tk_logits<14>(p, stream);
+    case 15: return launch_tk_logits<15>(p, stream);
+    case 16: return launch_tk_logits<16>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_topk_decode(const TopkDecodeParams& p, int head_dim, bool in_f32,
                               hipStream_t stream) {

@@ -17,8 +17,10 @@ HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE, HS_ERR_HIP = 0,
 HS_BF16, HS_F32 = 0, 1
 HS_IDX_TOKEN, HS_IDX_BLOCK = 0, 1
 HS_OP_FULL_ATTN, HS_OP_ORACLE_TOPK, HS_OP_BLOCK_TOPK, HS_OP_SPARSE_ATTN = 0, 1, 2, 3
+HS_OP_FULL_ATTN_LOGITS, HS_OP_TOPK_FROM_LOGITS, HS_OP_BLOCK_TOPK_FROM_LOGITS = 4, 5, 6
 
 EXPORTS = ["hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk", "hs_sparse_attn_gather",
+           "hs_full_attn_fwd_logits", "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
            "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
 
 
@@ -57,6 +59,9 @@ def lib():
         L.hs_block_score_topk.argtypes = [pd, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.hs_sparse_attn_gather.argtypes = [pd, vp, vp, vp, ctypes.c_int, vp, vp, i32, i32,
                                             ctypes.POINTER(SwaBranch), vp, vp, vp, sz, vp]
+        L.hs_full_attn_fwd_logits.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.hs_oracle_topk_from_logits.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.hs_block_topk_from_logits.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.hs_workspace_size.argtypes = [ctypes.c_int, pd, i32, i32]
         L.hs_workspace_size.restype = sz
         L.hs_status_string.restype = ctypes.c_char_p
@@ -64,7 +69,8 @@ def lib():
         L.hs_last_error.restype = ctypes.c_char_p
         L.hs_version.restype = ctypes.c_char_p
         for f in ("hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk",
-                  "hs_sparse_attn_gather"):
+                  "hs_sparse_attn_gather", "hs_full_attn_fwd_logits",
+                  "hs_oracle_topk_from_logits", "hs_block_topk_from_logits"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -131,6 +137,64 @@ def full_attn_fwd(q, k, v, q_offset=None, out_dtype=None):
     _check(lib().hs_full_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                   _ptr(lse), _ptr(ws), n, _stream(dev)), "hs_full_attn_fwd")
     return o, lse
+
+
+def full_attn_fwd_logits(q, k, v, q_offset=None, out_dtype=None):
+    """Full attention that also keeps its dot products q.k (decode).
+    Returns (o, lse, logits fp32 [B,Tq,Hq,Tk]); logits past a row's position are unspecified."""
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dev, dtype=q.dtype)
+    desc = make_desc(q, k, q_offset, out_dtype)
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
+    logits = torch.empty((q.shape[0], q.shape[1], q.shape[2], k.shape[1]), dtype=torch.float32,
+                         device=dev)
+    ws, n = workspace(HS_OP_FULL_ATTN_LOGITS, desc, device=dev)
+    _check(lib().hs_full_attn_fwd_logits(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                         _ptr(lse), _ptr(logits), _ptr(ws), n, _stream(dev)),
+           "hs_full_attn_fwd_logits")
+    return o, lse, logits
+
+
+def _logits_desc(logits, n_kv_heads, head_dim, q_offset):
+    B, Tq, Hq, Tk = logits.shape
+    return AttnDesc(B, Tq, Tk, Hq, int(n_kv_heads), int(head_dim),
+                    -1 if q_offset is None else int(q_offset), HS_F32, HS_F32)
+
+
+def oracle_topk_from_logits(logits, lse, n_kv_heads, head_dim, k_global, window, q_offset=None):
+    """oracle_topk from the logits kept by full_attn_fwd_logits. Returns (idx, count)."""
+    dev = logits.device
+    _need(logits, "logits", dev, dtype=torch.float32)
+    B, Tq, Hq, Tk = logits.shape
+    _need(lse, "lse", dev, dtype=torch.float32, shape=(B, Hq, Tq))
+    desc = _logits_desc(logits, n_kv_heads, head_dim, q_offset)
+    idx = torch.empty((B, Tq, n_kv_heads, k_global + window), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Tq, n_kv_heads), dtype=torch.int32, device=dev)
+    ws, n = workspace(HS_OP_TOPK_FROM_LOGITS, desc, k_global, window, device=dev)
+    _check(lib().hs_oracle_topk_from_logits(ctypes.byref(desc), _ptr(logits), _ptr(lse),
+                                            int(k_global), int(window), _ptr(idx), _ptr(cnt),
+                                            _ptr(ws), n, _stream(dev)),
+           "hs_oracle_topk_from_logits")
+    return idx, cnt
+
+
+def block_topk_from_logits(logits, lse, n_kv_heads, head_dim, block, n_blocks, q_offset=None):
+    """block_score_topk from the logits kept by full_attn_fwd_logits. Returns (blk_idx, count)."""
+    dev = logits.device
+    _need(logits, "logits", dev, dtype=torch.float32)
+    B, Tq, Hq, Tk = logits.shape
+    _need(lse, "lse", dev, dtype=torch.float32, shape=(B, Hq, Tq))
+    desc = _logits_desc(logits, n_kv_heads, head_dim, q_offset)
+    idx = torch.empty((B, Tq, n_kv_heads, n_blocks), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Tq, n_kv_heads), dtype=torch.int32, device=dev)
+    ws, n = workspace(HS_OP_BLOCK_TOPK_FROM_LOGITS, desc, block, n_blocks, device=dev)
+    _check(lib().hs_block_topk_from_logits(ctypes.byref(desc), _ptr(logits), _ptr(lse),
+                                           int(block), int(n_blocks), _ptr(idx), _ptr(cnt),
+                                           _ptr(ws), n, _stream(dev)),
+           "hs_block_topk_from_logits")
+    return idx, cnt
 
 
 def oracle_topk(q, k, lse, k_global, window, q_offset=None):

@@ -114,6 +114,40 @@ def test_sparse_argument_checks():
                                    None) == hs.HS_ERR_INVALID_ARG
 
 
+def test_logits_entry_points_argument_checks():
+    L = hs.lib()
+    d = desc(batch=8, kv_len=32768, n_q_heads=32, n_kv_heads=8)
+    # full attention with logits: NULL or misaligned logits, too small a workspace
+    assert L.hs_full_attn_fwd_logits(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                     1 << 40, None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_full_attn_fwd_logits(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     ctypes.c_void_p(0x1002), FAKE, 1 << 40, None) == \
+        hs.HS_ERR_INVALID_ARG
+    need = L.hs_workspace_size(hs.HS_OP_FULL_ATTN_LOGITS, ctypes.byref(d), 0, 0)
+    assert need == L.hs_workspace_size(hs.HS_OP_FULL_ATTN, ctypes.byref(d), 0, 0) > 0
+    assert L.hs_full_attn_fwd_logits(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     need - 1, None) == hs.HS_ERR_WORKSPACE
+    # token selection from logits: any group size is accepted; budgets are checked
+    need_tk = L.hs_workspace_size(hs.HS_OP_TOPK_FROM_LOGITS, ctypes.byref(d), 1024, 128)
+    assert need_tk > 0
+    assert L.hs_oracle_topk_from_logits(ctypes.byref(d), FAKE, FAKE, 1024, 128, FAKE, FAKE, FAKE,
+                                        need_tk - 1, None) == hs.HS_ERR_WORKSPACE
+    assert L.hs_oracle_topk_from_logits(ctypes.byref(d), FAKE, FAKE, -1, 128, FAKE, FAKE, FAKE,
+                                        1 << 40, None) == hs.HS_ERR_INVALID_ARG
+    assert L.hs_oracle_topk_from_logits(ctypes.byref(d), None, FAKE, 16, 4, FAKE, FAKE, FAKE,
+                                        1 << 40, None) == hs.HS_ERR_INVALID_ARG
+    d3 = desc(n_q_heads=6, n_kv_heads=2)  # g = 3
+    assert L.hs_workspace_size(hs.HS_OP_TOPK_FROM_LOGITS, ctypes.byref(d3), 16, 4) > 0
+    # block selection from logits: block and n_blocks checked, any group size accepted
+    for block, n_blocks in ((56, 16), (64, 0), (64, 65)):
+        assert L.hs_block_topk_from_logits(ctypes.byref(d), FAKE, FAKE, block, n_blocks, FAKE,
+                                           FAKE, FAKE, 1 << 40, None) == hs.HS_ERR_UNSUPPORTED
+    assert L.hs_workspace_size(hs.HS_OP_BLOCK_TOPK_FROM_LOGITS, ctypes.byref(d3), 64, 16) > 0
+    need_bk = L.hs_workspace_size(hs.HS_OP_BLOCK_TOPK_FROM_LOGITS, ctypes.byref(d), 64, 16)
+    assert L.hs_block_topk_from_logits(ctypes.byref(d), FAKE, FAKE, 64, 16, FAKE, FAKE, FAKE,
+                                       need_bk - 1, None) == hs.HS_ERR_WORKSPACE
+
+
 def test_status_strings():
     L = hs.lib()
     for s in (0, -1, -2, -3, -4):

@@ -104,6 +104,25 @@ def test_first_position_reads_first_value():
     assert np.array_equal(o[0, 0, 1], v[0, 0, 0].astype(np.float64))
 
 
+def test_logit_row_closed_form():
+    """q = c e_0 per head, k_i of KV head u = (i + 10 u) e_0: a_{t,i} = c (i + 10 u) / sqrt(d) for
+    i = 0..t, with u = h // g (a wrong head mapping, scale or causal length fails)."""
+    B, Tq, Tk, Hq, Hkv, d = 1, 3, 9, 4, 2, 16
+    q = np.zeros((B, Tq, Hq, d), np.float32)
+    k = np.zeros((B, Tk, Hkv, d), np.float32)
+    for h in range(Hq):
+        q[0, :, h, 0] = h + 1
+    for u in range(Hkv):
+        k[0, :, u, 0] = np.arange(Tk) + 10 * u
+    for j in range(Tq):
+        t = Tk - Tq + j
+        for h in range(Hq):
+            a = oracle.logit_row(q, k, 0, j, h)
+            assert a.shape == (t + 1,)
+            want = (h + 1) * (np.arange(t + 1) + 10 * (h // 2)) / math.sqrt(d)
+            assert np.max(np.abs(a - want)) < 1e-12
+
+
 def test_one_hot_values_read_back_probabilities():
     """V = identity rows: O[t, h, c] = p_{t,c}; and sum_i p_{t,i} = 1."""
     T, d = 16, 16
