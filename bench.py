@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 80B-shaped prefill leg (full attention + token top-k)")
+    ap.add_argument("--no-block-prefill", action="store_true",
+                    help="skip the 64k block-selection prefill leg (HySparse scoring pass)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the token-sparse decode layer sweep over batch sizes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -253,6 +255,8 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_prefill:
         out["prefill"] = prefill_leg(args)
+    if not args.no_block_prefill:
+        out["block_prefill"] = block_prefill_leg(args)
     if not args.no_sweep:
         out["sparse_decode_sweep"] = sparse_sweep(wl)
     if not args.no_cpu_baseline:
@@ -330,6 +334,47 @@ def prefill_leg(args):
             "sparse_layer_logical_GB_per_s": round(b_sp / (t_sp * 1e-3) / 1e9, 1),
             "sparse_layer_tflops": round(f_sp / (t_sp * 1e-3) / 1e12, 1),
             "peak_tflops": 2500.0, "reps": reps}
+
+
+def block_prefill_leg(args):
+    """HySparse scoring on the 64k block workload (batch 4, 65536-query causal prefill, 32/8
+    heads, d 128, bf16, blocks of 64, top 16): full attention followed by the block selection
+    pass, against the one-pass call that selects inside full attention.  TFLOP/s count the
+    full-attention flops (plus the recompute flops for the two-pass version)."""
+    import torch
+
+    from oracle_top_kv_amd import costs, hs
+    from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["block_7b_64k"]
+    x = make_inputs(wl, device=torch.device("cuda:0"), n_sparse=0)
+    q, k, v = x["q"], x["k"], x["v"]
+    _, lse = hs.full_attn_fwd(q, k, v)
+    hs.block_score_topk(q, k, lse, wl.block, wl.n_blocks)
+    hs.full_attn_block_topk(q, k, v, wl.block, wl.n_blocks)
+    torch.cuda.synchronize()
+    reps = 2
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record()
+        _, lse = hs.full_attn_fwd(q, k, v)
+        ev[r][1].record()
+        hs.block_score_topk(q, k, lse, wl.block, wl.n_blocks)
+        ev[r][2].record()
+        hs.full_attn_block_topk(q, k, v, wl.block, wl.n_blocks)
+        ev[r][3].record()
+    torch.cuda.synchronize()
+    t_fa = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    t_sel = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    t_one = sum(e[2].elapsed_time(e[3]) for e in ev) / reps
+    f_fa, f_sc = costs.full_attn_flops(wl), costs.score_flops(wl)
+    del x, q, k, v, lse
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "full_attn_ms": round(t_fa, 2), "block_select_ms": round(t_sel, 2),
+            "one_pass_ms": round(t_one, 2),
+            "two_pass_tflops": round((f_fa + f_sc) / ((t_fa + t_sel) * 1e-3) / 1e12, 1),
+            "one_pass_useful_tflops": round(f_fa / (t_one * 1e-3) / 1e12, 1),
+            "speedup_one_pass": round((t_fa + t_sel) / t_one, 3), "reps": reps}
 
 
 def sparse_sweep(wl, batches=(8, 32, 128)):

@@ -68,7 +68,8 @@ typedef enum {
                             p1 = SWA window (0: no SWA branch) */
   HS_OP_FULL_ATTN_LOGITS = 4,       /* p0, p1 unused */
   HS_OP_TOPK_FROM_LOGITS = 5,       /* p0 = k_global, p1 = window */
-  HS_OP_BLOCK_TOPK_FROM_LOGITS = 6  /* p0 = block, p1 = n_blocks */
+  HS_OP_BLOCK_TOPK_FROM_LOGITS = 6, /* p0 = block, p1 = n_blocks */
+  HS_OP_FULL_ATTN_BLOCK_TOPK = 7    /* p0 = block, p1 = n_blocks */
 } hs_op;
 
 typedef struct {
@@ -117,6 +118,24 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
                               const float* lse, int32_t block, int32_t n_blocks,
                               int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* Full attention and block-level oracle index in one call: the outputs of hs_full_attn_fwd
+ * (o, lse) and of hs_block_score_topk (blk_idx, count) for the same inputs.  The pages obtain
+ * the block scores inside the attention loop, from each tile's row maximum, and normalize them
+ * with the LSE at the end [P4 Algorithm 1; P2 "Extracting block scores from exact attention"].
+ * For prefill-shaped bf16 calls (the tiled prefill kernel: q_len * g > 16) with block == 64 and
+ * n_blocks <= 16 this is one pass: every (query, head) row keeps its best n blocks by raw logit
+ * maximum while the key tiles stream past (within one head p ranks like the logit), and the g
+ * rows of a query merge their lists once their LSEs are known.  Exact: a block among the
+ * group's best n is among the best n of the head attaining its group maximum.  No score matrix
+ * and no workspace.  Other shapes run the two calls one after the other (same limits as those;
+ * workspace: hs_workspace_size(HS_OP_FULL_ATTN_BLOCK_TOPK, desc, block, n_blocks)).  Index
+ * sets equal hs_block_score_topk's except where two blocks' scores tie to within fp32
+ * rounding (the logits come from a different MFMA tiling). */
+hs_status hs_full_attn_block_topk(const hs_attn_desc* desc, const void* q, const void* k,
+                                  const void* v, int32_t block, int32_t n_blocks, void* o,
+                                  float* lse, int32_t* blk_idx, int32_t* count, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* Sparse layer over the full layer's K, V and index set, with the layer's own queries q
  * [P2 "Cross-layer KV cache reuse", gather equations; P2 "Same query, two memories";

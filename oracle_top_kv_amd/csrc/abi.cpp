@@ -425,6 +425,44 @@ hs_status row_full_attn(const Shape& s, const void* q, const void* k, const void
   return ok();
 }
 
+hs::PrefillParams prefill_params(const Shape& s, const void* q, const void* k, const void* v,
+                                 void* o, float* lse) {
+  hs::PrefillParams pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.q = q;
+  pp.k = k;
+  pp.v = v;
+  pp.B = s.B;
+  pp.Tq = s.Tq;
+  pp.Tk = s.Tk;
+  pp.Hq = s.Hq;
+  pp.Hkv = s.Hkv;
+  pp.g = s.g;
+  pp.q_off = s.q_off;
+  pp.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  pp.o = o;
+  pp.lse = lse;
+  pp.out_f32 = s.out_f32;
+  return pp;
+}
+
+// Block selection inside the prefill attention pass: blocks of one 64-key tile, at most 16
+// blocks per list.
+bool fused_blocks(const Shape& s, int block, int n_blocks) {
+  return use_prefill_kernel(s) && block == 64 && n_blocks >= 1 && n_blocks <= 16;
+}
+
+// Workspace of hs_full_attn_block_topk: none when fused, else what the larger of its two
+// passes needs (they run one after the other and share it).
+size_t fused_blocks_ws(const Shape& s, int block, int n_blocks) {
+  if (fused_blocks(s, block, n_blocks)) return 0;
+  BkGeom g;
+  if (bk_check(s, block, n_blocks, &g) != HS_OK) return 0;
+  const size_t a = full_attn_ws(s);
+  const size_t b = use_prefill_blocks(s, block) ? 0 : bk_ws(g, n_blocks);
+  return a > b ? a : b;
+}
+
 hs::BlockTopkParams bk_params(const Shape& s, const BkGeom& g, const float* lse, int block,
                               int n_blocks, int32_t* blk_idx, int32_t* count, void* ws) {
   hs::BlockTopkParams p;
@@ -494,6 +532,7 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
       return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
     }
     case HS_OP_TOPK_FROM_LOGITS: return tk_ws(s, tl_geom(s));
+    case HS_OP_FULL_ATTN_BLOCK_TOPK: return fused_blocks_ws(s, p0, p1);
     case HS_OP_BLOCK_TOPK_FROM_LOGITS: {
       BkGeom g;
       if (bk_check(s, p0, p1, &g, true) != HS_OK) return 0;
@@ -511,25 +550,40 @@ hs_status hs_full_attn_fwd(const hs_attn_desc* desc, const void* q, const void* 
   if (st != HS_OK) return st;
   if (!q || !k || !v || !o || !lse) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
   if (use_prefill_kernel(s)) {
-    hs::PrefillParams pp;
-    memset(&pp, 0, sizeof(pp));
-    pp.q = q;
-    pp.k = k;
-    pp.v = v;
-    pp.B = s.B;
-    pp.Tq = s.Tq;
-    pp.Tk = s.Tk;
-    pp.Hq = s.Hq;
-    pp.Hkv = s.Hkv;
-    pp.g = s.g;
-    pp.q_off = s.q_off;
-    pp.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
-    pp.o = o;
-    pp.lse = lse;
-    pp.out_f32 = s.out_f32;
+    const hs::PrefillParams pp = prefill_params(s, q, k, v, o, lse);
     return hip_status(hs::launch_prefill_attn(pp, s.D, (hipStream_t)stream), "prefill attention kernel");
   }
   return row_full_attn(s, q, k, v, o, lse, nullptr, ws, ws_bytes, stream);
+}
+
+hs_status hs_full_attn_block_topk(const hs_attn_desc* desc, const void* q, const void* k,
+                                  const void* v, int32_t block, int32_t n_blocks, void* o,
+                                  float* lse, int32_t* blk_idx, int32_t* count, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  if (!q || !k || !v || !o || !lse || !blk_idx || !count)
+    return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (fused_blocks(s, block, n_blocks)) {
+    hs::PrefillParams pp = prefill_params(s, q, k, v, o, lse);
+    pp.blk_idx = blk_idx;
+    pp.blk_cnt = count;
+    pp.n_blocks = n_blocks;
+    return hip_status(hs::launch_prefill_attn(pp, s.D, (hipStream_t)stream),
+                      "prefill attention kernel with block selection");
+  }
+  // two passes: every argument of both is checked before the first launch
+  BkGeom g;
+  st = bk_check(s, block, n_blocks, &g);
+  if (st != HS_OK) return st;
+  const size_t need = fused_blocks_ws(s, block, n_blocks);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  st = hs_full_attn_fwd(desc, q, k, v, o, lse, ws, ws_bytes, stream);
+  if (st != HS_OK) return st;
+  return hs_block_score_topk(desc, q, k, lse, block, n_blocks, blk_idx, count, ws, ws_bytes,
+                             stream);
 }
 
 hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const void* k,

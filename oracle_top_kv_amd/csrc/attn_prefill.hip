@@ -15,6 +15,15 @@
 // K/V tiles are double-buffered: the next tile's rows are loaded into registers while the
 // current tile is computed, then stored to the other buffer; one barrier per tile.  Only tiles
 // that reach past the earliest query position of the workgroup apply the causal mask.
+//
+// BSEL: the HySparse block selection in the same pass, for blocks of 64 keys (one tile).  The
+// pages compute the block scores inside the attention loop from each tile's row maximum and
+// normalize them once the LSE is known [P4 Algorithm 1; P2 "Extracting block scores from exact
+// attention" and "Why normalize scores for TopK"].  Here no score matrix is stored: within one
+// head, p = exp(a - LSE) ranks like the raw logit a, so each row keeps its own best n blocks by
+// raw tile maximum as the tiles stream past (an exact running top-n); at the end the g rows of a
+// query merge their lists with the normalized scores.  The merge is exact: a block among the
+// group's best n is among the best n of the head that attains its group maximum.
 #include <type_traits>
 
 #include "hs_device.h"
@@ -49,14 +58,110 @@ struct PfCfg {
   static constexpr int LPT = kBN * CPR / kThreads;  // chunks per thread per tile (each of K and V)
 };
 
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Inverse of float_key.
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// LDS of the BSEL merge: per wave 32 rows x 16 list entries, then 16 x 16 kept entries and 16
+// selected ids.
+constexpr int kMergeCandBytes = (kThreads / 64) * 32 * 16 * 8;
+constexpr int kMergeBytes = kMergeCandBytes + (kThreads / 64) * (16 * 16 + 8) * 8;
+
+// BSEL epilogue of one wave (32 rows = 32/g whole queries, since g divides 32): normalize every
+// row's list with its LSE, then per query keep the best n of the union of its g lists, one
+// entry per block (its group maximum), and write them in ascending block order.  The score key
+// is the one of the selection kernels: a * scale_log2 - (LSE * log2(e) - C), C an integer per
+// query taken from its first head.  cand_all: 32 x 16 entries per wave; kept_all: 16 x 16
+// entries plus 16 ints per wave (LDS the tile loop no longer uses).
+template <int kSlots>
+__device__ __forceinline__ void select_blocks(const PrefillParams& p,
+                                              const unsigned long long (&bl)[kSlots],
+                                              float lse_row, unsigned long long* cand_all,
+                                              unsigned long long* kept_all, int wave, int lane,
+                                              int j0, int nq, int t_min, int b, int u) {
+  const int rj = lane & 31, h = lane >> 5;
+  const int hh = (wave * 32 + rj) % p.g;
+  unsigned long long* cand = cand_all + wave * (32 * 16);
+  unsigned long long* kept = kept_all + wave * (16 * 16 + 8);
+  int* sel = (int*)(kept + 16 * 16);
+  const float lse0 = __shfl(lse_row, (rj - hh) + 32 * h, 64);  // first head of this query
+  const double l2 = (double)lse_row * 1.4426950408889634;
+  const double Cq = rint((double)lse0 * 1.4426950408889634);
+  const float delta = (float)(l2 - Cq);
+#pragma unroll
+  for (int i = 0; i < kSlots; i++) {
+    const unsigned long long e = bl[i];
+    unsigned long long v = 0ull;  // empty slot
+    if ((e >> 32) != 0ull && e != ~0ull) {
+      const float sc = __builtin_fmaf(key_float((uint32_t)(e >> 32)), p.scale_log2, -delta);
+      v = ((unsigned long long)float_key(sc) << 32) | (e & 0xFFFFFFFFull);
+    }
+    cand[rj * 16 + kSlots * h + i] = v;
+  }
+  const int nc = p.g * 16;  // candidates per query
+  for (int qw = 0; qw < 32 / p.g; qw++) {
+    const int jq = (wave * 32) / p.g + qw;
+    if (jq >= nq) break;  // the same for the whole wave
+    wave_sync_lds();
+    const unsigned long long* cq = cand + qw * nc;
+    // one entry per block id: its largest value (equal values: the lowest index)
+    for (int c = lane; c < nc; c += 64) {
+      const unsigned long long v = cq[c];
+      bool keep = v != 0ull;
+      for (int o = 0; o < nc; o++) {
+        const unsigned long long w = cq[o];
+        keep = keep && !(o != c && (uint32_t)w == (uint32_t)v && (w > v || (w == v && o < c)));
+      }
+      kept[c] = keep ? v : 0ull;
+    }
+    if (lane < 16) sel[lane] = -1;
+    wave_sync_lds();
+    // the kept entries are distinct: the best n_take go to sel[] by rank
+    const int n_take = min((t_min + jq) / 64 + 1, p.n_blocks);
+    for (int c = lane; c < nc; c += 64) {
+      const unsigned long long v = kept[c];
+      if (v == 0ull) continue;
+      int rank = 0;
+      for (int o = 0; o < nc; o++) rank += kept[o] > v;
+      if (rank < n_take) sel[rank] = (int)(0xFFFFFFFFu - (uint32_t)v);
+    }
+    wave_sync_lds();
+    // ascending block order, -1 padding, count
+    const size_t row = ((size_t)b * p.Tq + j0 + jq) * p.Hkv + u;
+    if (lane < p.n_blocks) {
+      if (lane < n_take) {
+        const int id = sel[lane];
+        int pos = 0;
+        for (int o = 0; o < n_take; o++) pos += sel[o] < id;
+        p.blk_idx[row * p.n_blocks + pos] = id;
+      } else {
+        p.blk_idx[row * p.n_blocks + lane] = -1;
+      }
+    }
+    if (lane == 0) p.blk_cnt[row] = n_take;
+  }
+}
+
 // 32x32x16 layouts (wave64, lane l, h = l / 32):
 //   A[32 x 16]: row l % 32, k = 8h .. 8h + 7;   B[16 x 32]: column l % 32, k = 8h .. 8h + 7
 //   C[32 x 32]: column l % 32, register 4g + e holds row 8g + 4h + e (g, e = 0..3)
-template <int D>
+template <int D, bool BSEL>
 __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   using C = PfCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBN * C::KStr];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kBN * C::VStr];
+  // K/V tiles; BSEL reuses the same LDS for its merge after the last tile
+  constexpr int kTileBytes = 2 * kBN * (C::KStr + C::VStr) * 2;
+  constexpr int kSmemBytes = BSEL && kMergeBytes > kTileBytes ? kMergeBytes : kTileBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char pf_smem[kSmemBytes];
+  uint16_t (*ks)[kBN * C::KStr] = reinterpret_cast<uint16_t (*)[kBN * C::KStr]>(pf_smem);
+  uint16_t (*vs)[kBN * C::VStr] =
+      reinterpret_cast<uint16_t (*)[kBN * C::VStr]>(pf_smem + 2 * kBN * C::KStr * 2);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rj = lane & 31, h = lane >> 5;
@@ -122,6 +227,21 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
     }
   };
 
+  // BSEL: this row's best n blocks as (order-preserving raw maximum << 32 | ~block id); lane
+  // half h holds list slots 8h .. 8h+7.  An empty slot holds its own slot number (distinct, and
+  // below every real entry, whose upper half is never 0); slots past n_blocks hold ~0 and are
+  // never replaced.  thr = the list minimum (slot 0 at first), the same in both halves.
+  constexpr int kSlots = 8;
+  unsigned long long bl[BSEL ? kSlots : 1];
+  unsigned long long thr = 0ull;
+  if constexpr (BSEL) {
+#pragma unroll
+    for (int i = 0; i < kSlots; i++) {
+      const int slot = kSlots * h + i;
+      bl[i] = slot < p.n_blocks ? (unsigned long long)slot : ~0ull;
+    }
+  }
+
   load_tile(0);
   store_tile(0);
   __syncthreads();
@@ -163,6 +283,24 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
     mx = max_halves(mx);
+    if constexpr (BSEL) {
+      // block t = this tile: replace the list minimum when the tile's maximum beats it (equal
+      // maxima keep the earlier block); both halves of the row take the same branch
+      const unsigned long long cand =
+          ((unsigned long long)float_key(mx) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)t);
+      if (row_ok && mx != -INFINITY && cand > thr) {
+#pragma unroll
+        for (int i = 0; i < kSlots; i++) bl[i] = bl[i] == thr ? cand : bl[i];
+        unsigned long long m = bl[0];
+#pragma unroll
+        for (int i = 1; i < kSlots; i++) m = bl[i] < m ? bl[i] : m;
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)m, (uint32_t)m, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(m >> 32), (uint32_t)(m >> 32), false, false);
+        const unsigned long long m0 = ((unsigned long long)hi[0] << 32) | lo[0];
+        const unsigned long long m1 = ((unsigned long long)hi[1] << 32) | lo[1];
+        thr = m0 < m1 ? m0 : m1;
+      }
+    }
     const float m_new = fmaxf(m_run, mx * p.scale_log2);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
@@ -218,6 +356,10 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   // lanes l and l ^ 32 hold the row's sums over different keys (with the same maximum)
   double ld = (double)l_s - (double)l_c;
   ld += __shfl_xor(ld, 32, 64);
+  const float lse_row = ld > 0.0 ? (float)(((double)m_run + log2(ld)) * kLn2) : -INFINITY;
+  if constexpr (BSEL)
+    select_blocks(p, bl, lse_row, (unsigned long long*)pf_smem,
+                  (unsigned long long*)(pf_smem + kMergeCandBytes), wave, lane, j0, nq, t_min, b, u);
   if (!row_ok) return;
   const float inv = ld > 0.0 ? (float)(1.0 / ld) : 0.f;
   const size_t orow = (((size_t)b * p.Tq + j_row) * p.Hq + h_row) * D;
@@ -237,9 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
       }
     }
   }
-  if (h == 0)
-    p.lse[((size_t)b * p.Hq + h_row) * p.Tq + j_row] =
-        ld > 0.0 ? (float)(((double)m_run + log2(ld)) * kLn2) : -INFINITY;
+  if (h == 0) p.lse[((size_t)b * p.Hq + h_row) * p.Tq + j_row] = lse_row;
 }
 
 }  // namespace
@@ -248,10 +388,15 @@ hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t
   const int qpw = kRowsWG / p.g;
   const int n_qt = (p.Tq + qpw - 1) / qpw;
   const dim3 grid(p.B * p.Hkv * n_qt);
-  if (head_dim == 128)
-    pf_attn_kernel<128><<<grid, kThreads, 0, stream>>>(p);
-  else
-    pf_attn_kernel<64><<<grid, kThreads, 0, stream>>>(p);
+  const bool bsel = p.blk_idx != nullptr;
+  if (bsel && (p.n_blocks < 1 || p.n_blocks > 16 || 32 % p.g)) return hipErrorInvalidValue;
+  if (head_dim == 128) {
+    if (bsel) pf_attn_kernel<128, true><<<grid, kThreads, 0, stream>>>(p);
+    else pf_attn_kernel<128, false><<<grid, kThreads, 0, stream>>>(p);
+  } else {
+    if (bsel) pf_attn_kernel<64, true><<<grid, kThreads, 0, stream>>>(p);
+    else pf_attn_kernel<64, false><<<grid, kThreads, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

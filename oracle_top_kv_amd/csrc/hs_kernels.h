@@ -81,6 +81,10 @@ struct PrefillParams {
   void* o;
   float* lse;
   int out_f32;
+  // block selection in the same pass (blocks of 64 keys, n_blocks <= 16), or null
+  int32_t* blk_idx;  // [B, Tq, Hkv, n_blocks]
+  int32_t* blk_cnt;  // [B, Tq, Hkv]
+  int n_blocks;
 };
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);

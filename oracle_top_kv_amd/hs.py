@@ -18,9 +18,11 @@ HS_BF16, HS_F32 = 0, 1
 HS_IDX_TOKEN, HS_IDX_BLOCK = 0, 1
 HS_OP_FULL_ATTN, HS_OP_ORACLE_TOPK, HS_OP_BLOCK_TOPK, HS_OP_SPARSE_ATTN = 0, 1, 2, 3
 HS_OP_FULL_ATTN_LOGITS, HS_OP_TOPK_FROM_LOGITS, HS_OP_BLOCK_TOPK_FROM_LOGITS = 4, 5, 6
+HS_OP_FULL_ATTN_BLOCK_TOPK = 7
 
 EXPORTS = ["hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk", "hs_sparse_attn_gather",
            "hs_full_attn_fwd_logits", "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
+           "hs_full_attn_block_topk",
            "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
 
 
@@ -62,6 +64,8 @@ def lib():
         L.hs_full_attn_fwd_logits.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.hs_oracle_topk_from_logits.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.hs_block_topk_from_logits.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.hs_full_attn_block_topk.argtypes = [pd, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz,
+                                              vp]
         L.hs_workspace_size.argtypes = [ctypes.c_int, pd, i32, i32]
         L.hs_workspace_size.restype = sz
         L.hs_status_string.restype = ctypes.c_char_p
@@ -70,7 +74,8 @@ def lib():
         L.hs_version.restype = ctypes.c_char_p
         for f in ("hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk",
                   "hs_sparse_attn_gather", "hs_full_attn_fwd_logits",
-                  "hs_oracle_topk_from_logits", "hs_block_topk_from_logits"):
+                  "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
+                  "hs_full_attn_block_topk"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -137,6 +142,27 @@ def full_attn_fwd(q, k, v, q_offset=None, out_dtype=None):
     _check(lib().hs_full_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                   _ptr(lse), _ptr(ws), n, _stream(dev)), "hs_full_attn_fwd")
     return o, lse
+
+
+def full_attn_block_topk(q, k, v, block, n_blocks, q_offset=None, out_dtype=None):
+    """Full attention and the top n_blocks causal blocks in one call (one pass for prefill).
+    Returns (o, lse, blk_idx int32 [B,Tq,Hkv,n_blocks], count)."""
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dev, dtype=q.dtype)
+    desc = make_desc(q, k, q_offset, out_dtype)
+    B, Tq, Hq = q.shape[0], q.shape[1], q.shape[2]
+    Hkv = k.shape[2]
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Tq, Hkv, n_blocks), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
+    ws, n = workspace(HS_OP_FULL_ATTN_BLOCK_TOPK, desc, block, n_blocks, device=dev)
+    _check(lib().hs_full_attn_block_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                         int(block), int(n_blocks), _ptr(o), _ptr(lse), _ptr(idx),
+                                         _ptr(cnt), _ptr(ws), n, _stream(dev)),
+           "hs_full_attn_block_topk")
+    return o, lse, idx, cnt
 
 
 def full_attn_fwd_logits(q, k, v, q_offset=None, out_dtype=None):

@@ -205,6 +205,12 @@ def test_block_7b_64k_sampled_rows():
         _, lse = hs().full_attn_fwd(q, k, v)
     with Timer("block scores + top-16"):
         bidx, bcnt = hs().block_score_topk(q, k, lse, wl.block, wl.n_blocks)
+    with Timer("full attention with the block selection in the same pass"):
+        _, lse_f, bidx_f, bcnt_f = hs().full_attn_block_topk(q, k, v, wl.block, wl.n_blocks)
+    assert torch.equal(lse_f, lse)
+    n_diff = int((bidx_f != bidx).any(dim=-1).sum())
+    say(f"  one-pass selection: {n_diff} of {bidx.numel() // wl.n_blocks} rows differ from the "
+        "separate selection")
     rows = sample_rows(wl.q_len, seed=wl.seed)
     rows = sorted(set(rows) | {63, 64, 1023, 1024})
     say(f"  sampled rows {rows}")
@@ -223,6 +229,9 @@ def test_block_7b_64k_sampled_rows():
         ex = check_block_sets(bidx_g[b:b + 1], bcnt_g[b:b + 1], bi, bc, qn, kn, lse_ref,
                               wl.block, wl.q_offset, rows=rows)
         say(f"  b={b} block sets: near-tie differences excused {ex}")
+        ex = check_block_sets(bidx_f.cpu().numpy()[b:b + 1], bcnt_f.cpu().numpy()[b:b + 1], bi, bc,
+                              qn, kn, lse_ref, wl.block, wl.q_offset, rows=rows)
+        say(f"  b={b} one-pass block sets: near-tie differences excused {ex}")
         bidx_in[b, r] = torch.from_numpy(bi[0, rows]).cuda()
         bcnt_in[b, r] = torch.from_numpy(bc[0, rows]).cuda()
         refs[b] = (bi, bc)
