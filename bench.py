@@ -147,6 +147,8 @@ def main():
     ms_step_eager = t_start.elapsed_time(t_end) / args.steps
     stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                 for i, name in enumerate(stages)}
+    stage_all = {name: sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+                 for i, name in enumerate(stages)}
 
     # The same step captured once in a HIP graph and replayed (reported as ms_per_step_graph):
     # the library allocates nothing, never synchronizes and zero-fills with kernels, so every
@@ -203,7 +205,9 @@ def main():
     stages_out = {}
     for n in stages:
         gbs = stage_bytes[n] / (stage_ms[n] * 1e-3) / 1e9
-        stages_out[n] = {"ms": round(stage_ms[n], 4), "GB_per_s": round(gbs, 1),
+        v = stage_all[n]
+        stages_out[n] = {"ms": round(stage_ms[n], 4), "median_ms": round(v[len(v) // 2], 4),
+                         "min_ms": round(v[0], 4), "GB_per_s": round(gbs, 1),
                          "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
     stages_out["sparse_token"]["per_layer_gathered_bytes"] = b_tok
     dom = "full_attn"
@@ -250,11 +254,18 @@ def main():
                      "algorithmic_bytes": b_full, "traffic": counter_traffic(wl.name)},
         "step_stored_logits": logits_out,
     }
+    out["sparse_cold_cache"] = cold_sparse(wl, x, hs, costs)
+    peaks = measured_peaks()
+    out["measured_peaks"] = peaks
+    out["roofline"]["frac_of_measured_copy"] = round(achieved / peaks["copy_GB_per_s"], 4)
     if not args.no_prefill or not args.no_sweep:
         del x, q, k, v, qs, kl, vl, gate
         torch.cuda.empty_cache()
+    gemm = peaks["gemm_bf16_TFLOP_per_s"]
     if not args.no_prefill:
         out["prefill"] = prefill_leg(args)
+        out["prefill"]["full_attn_frac_of_measured_gemm"] = round(
+            out["prefill"]["full_attn_tflops"] / gemm, 4)
     if not args.no_block_prefill:
         out["block_prefill"] = block_prefill_leg(args)
     if not args.no_sweep:
@@ -262,6 +273,8 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, make_inputs(wl, device=dev, block_variant=True),
                                            args.cpu_seconds)
+        if not args.no_prefill:
+            out["cpu_baseline_prefill"] = cpu_baseline_prefill(out.get("prefill"))
     print(json.dumps(out), flush=True)
 
 
@@ -334,6 +347,78 @@ def prefill_leg(args):
             "sparse_layer_logical_GB_per_s": round(b_sp / (t_sp * 1e-3) / 1e9, 1),
             "sparse_layer_tflops": round(f_sp / (t_sp * 1e-3) / 1e12, 1),
             "peak_tflops": 2500.0, "reps": reps}
+
+
+def cold_sparse(wl, x, hs, costs, reps=10):
+    """One token-sparse layer and the gated block layer, each timed alone right after a 1 GiB
+    scrub write, so that neither the 256 MB last-level cache nor L2 holds the gathered rows (the
+    step's own numbers are warm: the layers run back to back after full attention)."""
+    import torch
+
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=x["q"].device)
+    _, lse = hs.full_attn_fwd(x["q"], x["k"], x["v"])
+    idx, cnt = hs.oracle_topk(x["q"], x["k"], lse, wl.k_global, wl.window)
+    bidx, bcnt = hs.block_score_topk(x["q"], x["k"], lse, wl.block, wl.n_blocks)
+    calls = {
+        "sparse_token": (lambda: hs.sparse_attn_gather(x["q_sparse"][0], x["k"], x["v"], idx, cnt,
+                                                       kind="token"),
+                         costs.token_gather_bytes(wl)),
+        "sparse_block_swa": (lambda: hs.sparse_attn_gather(
+            x["q_sparse"][0], x["k"], x["v"], bidx, bcnt, kind="block", block=wl.block,
+            swa=(x["k_loc"], x["v_loc"], x["gate"], wl.window)), costs.block_gather_bytes(wl)),
+    }
+    res = {}
+    for name, (fn, byts) in calls.items():
+        fn()
+        ts = []
+        for r in range(reps):
+            scrub.fill_(float(r))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        med = ts[len(ts) // 2]
+        res[name] = {"median_us": round(med, 1), "min_us": round(ts[0], 1),
+                     "GB_per_s": round(byts / (med * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(byts / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+                     "bytes": byts, "reps": reps}
+    del scrub
+    return res
+
+
+def measured_peaks():
+    """Peaks measured on this GPU with library kernels: a 1 GiB device copy (bytes read plus
+    written per second) and a large bf16 GEMM (dense MFMA, TFLOP/s)."""
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    t_copy = timed(lambda: b.copy_(a), 10)
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device="cuda:0")
+    y = torch.randn(m, m, dtype=torch.bfloat16, device="cuda:0")
+    t_mm = timed(lambda: torch.matmul(x, y), 10)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"copy_GB_per_s": round(2 * 4 * n / t_copy / 1e9, 1),
+            "gemm_bf16_TFLOP_per_s": round(2 * m ** 3 / t_mm / 1e12, 1),
+            "spec": {"hbm_GB_per_s": HBM_PEAK_GBS, "bf16_dense_TFLOP_per_s": 2500.0}}
 
 
 def block_prefill_leg(args):
@@ -449,6 +534,36 @@ def cpu_baseline(wl, x, budget_s):
     return {"value": round(done * per_b / t_used / 1e9, 4), "unit": "GB/s",
             "cores": oracle.threads(), "kind": "oracle",
             "sample": f"{done} of {wl.batch} batch entries, every stage, {t_used:.1f} s"}
+
+
+def cpu_baseline_prefill(gpu_prefill, n_rows=8):
+    """The oracle on a fixed sample of query rows of the 80B prefill chunk (full attention and
+    token top-k for rows spread over the 4096 queries, first and last included), extrapolated by
+    rows to the whole chunk and set against the GPU's time for the same two stages."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs, to_numpy_f32
+
+    wl = WORKLOADS["prefill_80b_128k"]
+    x = make_inputs(wl, device=torch.device("cuda:0"), n_sparse=0)
+    q, k, v = (to_numpy_f32(x[n]) for n in ("q", "k", "v"))
+    del x
+    torch.cuda.empty_cache()
+    rows = np.linspace(0, wl.q_len - 1, n_rows).round().astype(np.int32)
+    t0 = time.perf_counter()
+    _, lse = oracle.full_attention(q, k, v, rows=rows)
+    oracle.token_topk(q, k, lse, wl.k_global, wl.window, rows=rows)
+    t = time.perf_counter() - t0
+    est = t * wl.q_len / n_rows
+    out = {"kind": "oracle", "cores": oracle.threads(), "sample": f"{n_rows} of {wl.q_len} query "
+           f"rows of {wl.name}, full attention + token top-k, {t:.1f} s", "extrapolated_s": round(est, 1)}
+    if gpu_prefill:
+        gpu_s = (gpu_prefill["full_attn_ms"] + gpu_prefill["topk_ms"]) * 1e-3
+        out["gpu_s"] = round(gpu_s, 4)
+        out["gpu_speedup_extrapolated"] = round(est / gpu_s, 1)
+    return out
 
 
 if __name__ == "__main__":
