@@ -158,9 +158,16 @@ def token_topk(q, k, lse, k_global, window, cap=None, q_offset=None, rows=None):
     return idx, cnt
 
 
-def masked_attention(q, k, v, idx, count, q_offset=None, rows=None):
+def _opt_f32(x):
+    if x is None:
+        return None, None
+    return _f32(x)
+
+
+def masked_attention(q, k, v, idx, count, q_offset=None, rows=None, sink=None, out_gate=None):
     """Attention of q over k, v restricted to each row's index set (dense masked softmax).
-    Returns (o float64, lse float64)."""
+    sink: [Hq] per-head sink logits in the denominator; out_gate: [B,Tq,Hq] sigmoid output-gate
+    logits.  Returns (o float64, lse float64; lse includes the sink)."""
     s = _shape(q, k, q_offset)
     q, qp = _f32(q)
     k, kp = _f32(k)
@@ -170,9 +177,11 @@ def masked_attention(q, k, v, idx, count, q_offset=None, rows=None):
     o = np.full(q.shape, np.nan)
     lse = np.full((s.batch, s.n_q_heads, s.q_len), np.nan)
     rr, rp, nr = _rows(rows)
-    _check(lib().orc_masked_attention(ctypes.byref(s), qp, kp, vp, ip, cp, int(idx.shape[-1]),
-                                      o.ctypes.data_as(ctypes.c_void_p),
-                                      lse.ctypes.data_as(ctypes.c_void_p), rp, nr),
+    sk, skp = _opt_f32(sink)
+    og, ogp = _opt_f32(out_gate)
+    _check(lib().orc_masked_attention_ex(ctypes.byref(s), qp, kp, vp, ip, cp, int(idx.shape[-1]),
+                                         skp, ogp, o.ctypes.data_as(ctypes.c_void_p),
+                                         lse.ctypes.data_as(ctypes.c_void_p), rp, nr),
            "masked_attention")
     return o, lse
 
@@ -210,8 +219,10 @@ def block_topk(q, k, lse, block, n_blocks, q_offset=None, rows=None):
 
 
 def gated_block_swa(q, k, v, blk_idx, count, block, k_loc, v_loc, window, gate, q_offset=None,
-                    rows=None):
-    """HySparse sparse layer. Returns (o, o_glob, o_loc), all float64 [B,Tq,Hq,d]."""
+                    rows=None, sink=None, sink_loc=None, out_gate=None):
+    """HySparse sparse layer; sink / sink_loc: [Hq] sink logits of the two branches, out_gate:
+    [B,Tq,Hq] sigmoid output-gate logits on the gated sum.  Returns (o, o_glob, o_loc), all
+    float64 [B,Tq,Hq,d] (o_glob, o_loc: the normalized branches before the gates)."""
     s = _shape(q, k, q_offset)
     q, qp = _f32(q)
     k, kp = _f32(k)
@@ -225,9 +236,12 @@ def gated_block_swa(q, k, v, blk_idx, count, block, k_loc, v_loc, window, gate, 
     og = np.full(q.shape, np.nan)
     ol = np.full(q.shape, np.nan)
     rr, rp, nr = _rows(rows)
-    _check(lib().orc_gated_block_swa(ctypes.byref(s), qp, kp, vp, bp, cp, int(bi.shape[-1]),
-                                     int(block), klp, vlp, int(window), gp,
-                                     o.ctypes.data_as(ctypes.c_void_p),
+    sk, skp = _opt_f32(sink)
+    sl, slp = _opt_f32(sink_loc)
+    ogt, ogtp = _opt_f32(out_gate)
+    _check(lib().orc_gated_block_swa_ex(ctypes.byref(s), qp, kp, vp, bp, cp, int(bi.shape[-1]),
+                                        int(block), klp, vlp, int(window), gp, skp, slp, ogtp,
+                                        o.ctypes.data_as(ctypes.c_void_p),
                                      og.ctypes.data_as(ctypes.c_void_p),
                                      ol.ctypes.data_as(ctypes.c_void_p), rp, nr),
            "gated_block_swa")

@@ -303,9 +303,32 @@ int orc_token_topk(const orc_shape* s, const float* q, const float* k, const dou
  * index set [P2 "Cross-layer KV cache reuse" gather equations; P2 "Same query, two memories",
  * global-branch equation; P4 section 3.3].  Written as a dense masked softmax over all keys
  * 0..t (non-members at -inf), so no gather loop is involved. */
+/* ln(e^L + e^s): the denominator of a softmax whose keys give LSE L, with one more logit s
+ * that carries no value (the per-head sink).  sink == NULL: L unchanged. */
+static double with_sink(double L, const float* sink, int h) {
+  if (!sink) return L;
+  const double sv = (double)sink[h];
+  if (L == -INFINITY) return sv;
+  const double m = L > sv ? L : sv;
+  return m + log(exp(L - m) + exp(sv - m));
+}
+
+static double sigmoid(double z);
+
 int orc_masked_attention(const orc_shape* s, const float* q, const float* k, const float* v,
                          const int32_t* idx, const int32_t* count, int cap, double* o,
                          double* lse, const int32_t* rows, int n_rows) {
+  return orc_masked_attention_ex(s, q, k, v, idx, count, cap, NULL, NULL, o, lse, rows, n_rows);
+}
+
+/* Sparse layer with the options of the pages' sparse layers [P1 section 6.1: every sparse and
+ * SWA layer has a sigmoid output gate and a learnable per-head sink bias; P4 experimental setup:
+ * per-head sink bias in the manner of gpt-oss]: LSE' = ln(e^{s_h} + sum_{i in I} e^{a_i}),
+ * o = sigmoid(g) sum_{i in I} e^{a_i - LSE'} v_i. */
+int orc_masked_attention_ex(const orc_shape* s, const float* q, const float* k, const float* v,
+                            const int32_t* idx, const int32_t* count, int cap, const float* sink,
+                            const float* out_gate, double* o, double* lse, const int32_t* rows,
+                            int n_rows) {
   if (!shape_ok(s) || !q || !k || !v || !idx || !count || !o || cap < 1 ||
       !rows_ok(s, rows, n_rows))
     return ORC_EINVAL;
@@ -336,8 +359,13 @@ int orc_masked_attention(const orc_shape* s, const float* q, const float* k, con
         continue;
       }
       logits_row(s, q, k, b, j, h, a);
-      const double L = lse_of(a, keep, t + 1);
-      weighted_sum(s, v, b, u, a, keep, t + 1, L, o + q_at(s, b, j, h));
+      const double L = with_sink(lse_of(a, keep, t + 1), sink, h);
+      double* out = o + q_at(s, b, j, h);
+      weighted_sum(s, v, b, u, a, keep, t + 1, L, out);
+      if (out_gate) {
+        const double gv = sigmoid((double)out_gate[((int64_t)b * s->q_len + j) * s->n_q_heads + h]);
+        for (int c = 0; c < s->head_dim; c++) out[c] *= gv;
+      }
       if (lse) lse[lse_at(s, b, h, j)] = L;
     }
     free(a);
@@ -444,6 +472,18 @@ int orc_gated_block_swa(const orc_shape* s, const float* q, const float* k, cons
                         const float* k_loc, const float* v_loc, int window, const float* gate,
                         double* o, double* o_glob, double* o_loc, const int32_t* rows,
                         int n_rows) {
+  return orc_gated_block_swa_ex(s, q, k, v, blk_idx, count, n_blocks, block, k_loc, v_loc, window,
+                                gate, NULL, NULL, NULL, o, o_glob, o_loc, rows, n_rows);
+}
+
+/* The gated layer with a per-head sink in each branch and an output gate applied to the sum
+ * (same sources as orc_masked_attention_ex). */
+int orc_gated_block_swa_ex(const orc_shape* s, const float* q, const float* k, const float* v,
+                           const int32_t* blk_idx, const int32_t* count, int n_blocks, int block,
+                           const float* k_loc, const float* v_loc, int window, const float* gate,
+                           const float* sink, const float* sink_loc, const float* out_gate,
+                           double* o, double* o_glob, double* o_loc, const int32_t* rows,
+                           int n_rows) {
   if (!shape_ok(s) || !q || !k || !v || !blk_idx || !count || !k_loc || !v_loc || !gate || !o ||
       n_blocks < 1 || block < 1 || window < 1 || !rows_ok(s, rows, n_rows))
     return ORC_EINVAL;
@@ -484,18 +524,19 @@ int orc_gated_block_swa(const orc_shape* s, const float* q, const float* k, cons
       }
       /* global branch over the shared K, V */
       logits_row(s, q, k, b, j, h, a);
-      double L = lse_of(a, keep, t + 1);
+      double L = with_sink(lse_of(a, keep, t + 1), sink, h);
       weighted_sum(s, v, b, u, a, keep, t + 1, L, og);
       /* local branch over the layer's own K', V' */
       memset(keep, 0, (size_t)(t + 1));
       for (int64_t i = (t - window + 1 > 0 ? t - window + 1 : 0); i <= t; i++) keep[i] = 1;
       logits_row(s, q, k_loc, b, j, h, a);
-      L = lse_of(a, keep, t + 1);
+      L = with_sink(lse_of(a, keep, t + 1), sink_loc, h);
       weighted_sum(s, v_loc, b, u, a, keep, t + 1, L, ol);
       const float* z = gate + (((int64_t)b * s->q_len + j) * s->n_q_heads + h) * 2;
       const double gG = sigmoid((double)z[0]), gL = sigmoid((double)z[1]);
+      const double gO = out_gate ? sigmoid((double)out_gate[((int64_t)b * s->q_len + j) * s->n_q_heads + h]) : 1.0;
       double* out = o + q_at(s, b, j, h);
-      for (int c = 0; c < d; c++) out[c] = gG * og[c] + gL * ol[c];
+      for (int c = 0; c < d; c++) out[c] = gO * (gG * og[c] + gL * ol[c]);
       if (o_glob)
         for (int c = 0; c < d; c++) o_glob[q_at(s, b, j, h) + c] = og[c];
       if (o_loc)

@@ -81,6 +81,14 @@ int orc_masked_attention(const orc_shape* s, const float* q, const float* k, con
                          const int32_t* idx, const int32_t* count, int cap, double* o,
                          double* lse, const int32_t* rows, int n_rows);
 
+/* orc_masked_attention with a per-head sink logit (sink [Hq], NULL: none) in the softmax
+ * denominator, LSE = ln(e^{s_h} + sum_{i in I} e^{a_i}), and a sigmoid output gate
+ * (out_gate [B, Tq, Hq] logits, NULL: none) applied to the result. */
+int orc_masked_attention_ex(const orc_shape* s, const float* q, const float* k, const float* v,
+                            const int32_t* idx, const int32_t* count, int cap, const float* sink,
+                            const float* out_gate, double* o, double* lse, const int32_t* rows,
+                            int n_rows);
+
 /* Block score of every causal block r = 0..floor(t/B) for one (b, j, u):
  * max over heads of max over i in [rB, min(rB+B-1, t)] of p^h_{t,i}. */
 int orc_block_score_row(const orc_shape* s, const float* q, const float* k, const double* lse,
@@ -100,6 +108,15 @@ int orc_gated_block_swa(const orc_shape* s, const float* q, const float* k, cons
                         const float* k_loc, const float* v_loc, int window, const float* gate,
                         double* o, double* o_glob, double* o_loc, const int32_t* rows,
                         int n_rows);
+
+/* orc_gated_block_swa with a per-head sink in the global (sink) and local (sink_loc) branch and
+ * a sigmoid output gate on the gated sum; any of the three may be NULL. */
+int orc_gated_block_swa_ex(const orc_shape* s, const float* q, const float* k, const float* v,
+                           const int32_t* blk_idx, const int32_t* count, int n_blocks, int block,
+                           const float* k_loc, const float* v_loc, int window, const float* gate,
+                           const float* sink, const float* sink_loc, const float* out_gate,
+                           double* o, double* o_glob, double* o_loc, const int32_t* rows,
+                           int n_rows);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,12 @@ MUTANTS = [
      "for (int64_t i = (t - window > 0 ? t - window : 0); i <= t; i++) keep[i] = 1;\n      logits_row(s, q, k_loc"),
     ("mask_ignored", "if (keep && !keep[i]) continue;", "(void)keep;"),
     ("lse_log2", "return m + log(l);", "return m + log2(l);"),
+    ("sink_sign", "return m + log(exp(L - m) + exp(sv - m));",
+     "return m + log(exp(L - m) + exp(-sv - m));"),
+    ("sink_ignored_when_empty", "if (L == -INFINITY) return sv;", "if (L == -INFINITY) return L;"),
+    ("sink_local_in_global", "double L = with_sink(lse_of(a, keep, t + 1), sink, h);\n      weighted_sum(s, v, b, u, a, keep, t + 1, L, og);",
+     "double L = with_sink(lse_of(a, keep, t + 1), sink_loc, h);\n      weighted_sum(s, v, b, u, a, keep, t + 1, L, og);"),
+    ("out_gate_missing", "for (int c = 0; c < s->head_dim; c++) out[c] *= gv;", "(void)gv;"),
 ]
 
 

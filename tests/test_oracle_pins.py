@@ -413,6 +413,111 @@ def test_gate_special_cases():
     assert np.max(np.abs(o2 - sg * og2)) < 1e-15
 
 
+# ------------------------------------------------------------------------------------------
+# per-head sink bias and sigmoid output gate of the sparse layers
+# ------------------------------------------------------------------------------------------
+
+def _sink_setup(seed, T=40, Hq=4, Hkv=2, d=16, n_idx=12):
+    q = rnd((1, 1, Hq, d), seed)
+    k = rnd((1, T, Hkv, d), seed + 1)
+    v = rnd((1, T, Hkv, d), seed + 2)
+    r = np.random.default_rng(seed)
+    idx = np.full((1, 1, Hkv, n_idx), -1, np.int32)
+    for u in range(Hkv):
+        idx[0, 0, u] = np.sort(r.choice(T, n_idx, replace=False))
+    cnt = np.full((1, 1, Hkv), n_idx, np.int32)
+    return q, k, v, idx, cnt
+
+
+def test_sink_equals_an_extra_key_with_zero_value():
+    """A sink logit s_h is attention to one more key whose logit is s_h and whose value is 0:
+    build that key explicitly (k = s sqrt(d) q / |q|^2, one per head with g = 1, placed at
+    position 0) and compare with the plain masked attention of the oracle."""
+    T, H, d = 40, 3, 16
+    q, k, v, idx, cnt = _sink_setup(81, T=T, Hq=H, Hkv=H, d=d)
+    sink = np.array([0.7, 3.5, -2.0], np.float32)  # below, near and above the typical logits
+    o_s, lse_s = oracle.masked_attention(q, k, v, idx, cnt, sink=sink)
+    k2 = np.zeros((1, T + 1, H, d), np.float32)
+    v2 = np.zeros((1, T + 1, H, d), np.float32)
+    k2[0, 1:], v2[0, 1:] = k[0], v[0]
+    for h in range(H):
+        qh = q[0, 0, h].astype(np.float64)
+        k2[0, 0, h] = (sink[h] * math.sqrt(d) * qh / (qh @ qh)).astype(np.float32)
+    idx2 = np.concatenate([np.zeros((1, 1, H, 1), np.int32), idx + 1], axis=-1)
+    o_x, lse_x = oracle.masked_attention(q, k2, v2, idx2, cnt + 1)
+    assert np.max(np.abs(o_s - o_x)) < 1e-6
+    assert np.max(np.abs(lse_s - lse_x)) < 1e-6
+    o_n, lse_n = oracle.masked_attention(q, k, v, idx, cnt)
+    assert np.max(np.abs(o_s - o_n)) > 1e-3  # the sink matters here
+
+
+def test_sink_limits_and_identical_keys():
+    q, k, v, idx, cnt = _sink_setup(82)
+    o_n, lse_n = oracle.masked_attention(q, k, v, idx, cnt)
+    o_m, lse_m = oracle.masked_attention(q, k, v, idx, cnt,
+                                         sink=np.full(4, -np.inf, np.float32))
+    assert np.array_equal(o_m, o_n) and np.array_equal(lse_m, lse_n)
+    # identical keys: every logit is a, so o = n e^a / (e^s + n e^a) * mean(v over the set)
+    k1 = np.repeat(k[:, :1], k.shape[1], axis=1)
+    sink = np.array([0.3, -1.0, 2.0, 5.0], np.float32)
+    o, lse = oracle.masked_attention(q, k1, v, idx, cnt, sink=sink)
+    n = int(cnt[0, 0, 0])
+    for h in range(4):
+        u = h // 2
+        a = float(q[0, 0, h].astype(np.float64) @ k1[0, 0, u].astype(np.float64)) / 4.0
+        mean = v[0, idx[0, 0, u], u].astype(np.float64).mean(axis=0)
+        frac = n * math.exp(a) / (math.exp(float(sink[h])) + n * math.exp(a))
+        assert np.max(np.abs(o[0, 0, h] - frac * mean)) < 1e-12
+        assert abs(lse[0, h, 0] - math.log(math.exp(float(sink[h])) + n * math.exp(a))) < 1e-12
+    # an empty set: o = 0 and LSE = the sink
+    o0, l0 = oracle.masked_attention(q, k, v, np.full_like(idx, -1), np.zeros_like(cnt),
+                                     sink=sink)
+    assert np.all(o0 == 0) and np.allclose(l0[0, :, 0], sink, atol=0, rtol=0)
+
+
+def test_output_gate_scales_the_layer():
+    q, k, v, idx, cnt = _sink_setup(83)
+    g = rnd((1, 1, 4), 84, 2.0)
+    sink = np.array([0.1, 0.2, 0.3, 0.4], np.float32)
+    o, lse = oracle.masked_attention(q, k, v, idx, cnt, sink=sink)
+    og, lseg = oracle.masked_attention(q, k, v, idx, cnt, sink=sink, out_gate=g)
+    sg = 1 / (1 + np.exp(-g.astype(np.float64)))
+    assert np.max(np.abs(og - sg[..., None] * o)) < 1e-15
+    assert np.array_equal(lse, lseg)
+    wl, a, bi, bc = _gated_setup(73)
+    hq = a["qs"].shape[2]
+    s1, s2 = rnd((hq,), 85), rnd((hq,), 86)
+    gate_o = rnd(a["qs"].shape[:3], 87)
+    o3, og3, ol3 = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                                          a["v_loc"], wl.window, a["gate"], sink=s1, sink_loc=s2,
+                                          out_gate=gate_o)
+    z = a["gate"].astype(np.float64)
+    want = (1 / (1 + np.exp(-gate_o.astype(np.float64))))[..., None] * (
+        1 / (1 + np.exp(-z[..., 0:1])) * og3 + 1 / (1 + np.exp(-z[..., 1:2])) * ol3)
+    assert np.max(np.abs(o3 - want)) < 1e-14
+    # each branch is the masked attention of its own keys with its own sink: the block set
+    # expanded to its causal positions, and the window positions
+    cap = wl.n_blocks * wl.block
+    tok = np.full((1, wl.q_len, wl.n_kv_heads, cap), -1, np.int32)
+    tcnt = np.zeros((1, wl.q_len, wl.n_kv_heads), np.int32)
+    win = np.full((1, wl.q_len, wl.n_kv_heads, wl.window), -1, np.int32)
+    wcnt = np.zeros_like(tcnt)
+    for j in range(wl.q_len):
+        t = wl.q_offset + j
+        for u in range(wl.n_kv_heads):
+            pos = [i for r in sorted(bi[0, j, u, :bc[0, j, u]])
+                   for i in range(r * wl.block, min((r + 1) * wl.block, t + 1))]
+            tok[0, j, u, :len(pos)], tcnt[0, j, u] = pos, len(pos)
+            wp = list(range(max(0, t - wl.window + 1), t + 1))
+            win[0, j, u, :len(wp)], wcnt[0, j, u] = wp, len(wp)
+    og_ref, _ = oracle.masked_attention(a["qs"], a["k"], a["v"], tok, tcnt, sink=s1)
+    ol_ref, _ = oracle.masked_attention(a["qs"], a["k_loc"], a["v_loc"], win, wcnt, sink=s2)
+    assert np.max(np.abs(og3 - og_ref)) < 1e-13 and np.max(np.abs(ol3 - ol_ref)) < 1e-13
+    o_plain, og_p, ol_p = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block,
+                                                 a["k_loc"], a["v_loc"], wl.window, a["gate"])
+    assert np.max(np.abs(og3 - og_p)) > 1e-4 and np.max(np.abs(ol3 - ol_p)) > 1e-4
+
+
 def test_blocks_covering_prefix_and_wide_window_are_full_attention():
     """B * n_blocks >= t + 1 selects every causal block; w >= t + 1 with K' = K, V' = V makes
     the local branch full attention too."""
