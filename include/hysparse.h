@@ -119,6 +119,22 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
                               int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Options of a sparse layer (hs_sparse_attn_gather_ex); a NULL field is left out.
+ *   sink, sink_local: per-head sink logits of the global (token or block) branch and of the
+ *     sliding-window branch, fp32 [Hq], natural log.  The pages give every sparse and
+ *     sliding-window layer a learnable per-head sink bias in the manner of gpt-oss [P1 section
+ *     6.1; P4 experimental setup]; the reading taken is gpt-oss's: the sink s_h is one more logit in the
+ *     softmax denominator and carries no value, p_i = e^{a_i} / (e^{s_h} + sum_j e^{a_j}).  The
+ *     reported LSE includes it.  A row with no key then gets o = 0 and LSE = s_h.
+ *   out_gate: logits of the sigmoid output gate of those layers [P1 section 6.1], fp32
+ *     [B, q_len, Hq], one per (query, head) (the pages give no size; one scalar per head, like
+ *     the branch gates): o <- sigmoid(g) * o, applied last. */
+typedef struct {
+  const float* sink;
+  const float* sink_local;
+  const float* out_gate;
+} hs_sparse_opts;
+
 /* Full attention and block-level oracle index in one call: the outputs of hs_full_attn_fwd
  * (o, lse) and of hs_block_score_topk (blk_idx, count) for the same inputs.  The pages obtain
  * the block scores inside the attention loop, from each tile's row maximum, and normalize them
@@ -192,6 +208,14 @@ hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logit
                                     const float* lse, int32_t block, int32_t n_blocks,
                                     int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/* hs_sparse_attn_gather with options (opts may be NULL: then it is hs_sparse_attn_gather).
+ * sink_local requires swa.  Workspace: as hs_sparse_attn_gather (HS_OP_SPARSE_ATTN). */
+hs_status hs_sparse_attn_gather_ex(const hs_attn_desc* desc, const void* q, const void* k_full,
+                                   const void* v_full, hs_index_kind kind, const int32_t* idx,
+                                   const int32_t* count, int32_t idx_cap, int32_t block,
+                                   const hs_swa_branch* swa, const hs_sparse_opts* opts, void* o,
+                                   float* lse_opt, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace the call `op` needs for `desc` (p0, p1 as documented on hs_op).  Returns 0
  * for an invalid description (hs_last_error() says why). */

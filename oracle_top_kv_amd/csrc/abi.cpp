@@ -707,6 +707,18 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
                                 const int32_t* count, int32_t idx_cap, int32_t block,
                                 const hs_swa_branch* swa, void* o, float* lse_opt, void* ws,
                                 size_t ws_bytes, void* stream) {
+  return hs_sparse_attn_gather_ex(desc, q, k_full, v_full, kind, idx, count, idx_cap, block, swa,
+                                  nullptr, o, lse_opt, ws, ws_bytes, stream);
+}
+
+hs_status hs_sparse_attn_gather_ex(const hs_attn_desc* desc, const void* q, const void* k_full,
+                                   const void* v_full, hs_index_kind kind, const int32_t* idx,
+                                   const int32_t* count, int32_t idx_cap, int32_t block,
+                                   const hs_swa_branch* swa, const hs_sparse_opts* opts, void* o,
+                                   float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
+  const float* sink_g = opts ? opts->sink : nullptr;
+  const float* sink_l = opts ? opts->sink_local : nullptr;
+  const float* ogate = opts ? opts->out_gate : nullptr;
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
@@ -724,6 +736,8 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
     if (swa->window < 1) return fail(HS_ERR_INVALID_ARG, "sliding window must be >= 1");
     window = swa->window;
   }
+  if (sink_l && !swa)
+    return fail(HS_ERR_INVALID_ARG, "sink_local given without a sliding-window branch");
   const SparseGeom g = sparse_geom(s, keys, window);
   const size_t need = sparse_ws(s, g, window);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -741,6 +755,9 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
   pg.o = o;
   pg.lse = lse_opt;
   pg.final_direct = !g.combine;
+  pg.sink = sink_g;
+  pg.sink2 = sink_l;
+  pg.out_gate = ogate;
   const hs::KeySrc src = kind == HS_IDX_TOKEN ? hs::SRC_TOKEN : hs::SRC_BLOCK;
   if (g.fused) {
     pg.k2 = swa->k_local;
@@ -773,6 +790,9 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
   if (g.combine) {
     hs::CombineParams c = combine_params(s, g.glob, o, lse_opt);
     c.n_branch = window > 0 ? 2 : 1;
+    c.sink[0] = sink_g;
+    c.sink[1] = sink_l;
+    c.out_gate = ogate;
     c.m[0] = pg.part_m;
     c.l[0] = pg.part_l;
     c.po[0] = pg.part_o;

@@ -423,9 +423,34 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   out.L = Ls;
 }
 
-template <int CPT>
-__device__ __forceinline__ float lse_of(const PassOut<CPT>& a) {
-  return (a.L > 0.0) ? (float)(((double)a.M + log2(a.L)) * kLn2) : -INFINITY;
+// Normalization of one row from its maximum M (log2 domain) and its sum L relative to M, with
+// an optional per-head sink logit s (natural log): the softmax denominator becomes
+// e^s + sum_i e^a_i, and the sink itself carries no value (the learnable per-head sink bias of
+// the pages' sparse and sliding-window layers, P1 section 6.1 and P4 experimental setup, taken in the
+// gpt-oss form those pages refer to).  Returns the factor that turns the unnormalized output
+// (relative to M) into the output, scaled by `weight`, and the row's LSE including the sink.
+// Without a sink: factor = weight / L and LSE = (M + log2 L) ln 2, as before.
+struct RowNorm {
+  float factor;
+  float lse;
+};
+__device__ __forceinline__ RowNorm row_norm(float M, double L, const float* sink, int h,
+                                            double weight) {
+  const double s2 = sink ? (double)sink[h] * 1.4426950408889634 : -INFINITY;
+  const double mx = fmax((double)M, s2);
+  RowNorm n = {0.f, -INFINITY};
+  if (mx == -INFINITY) return n;  // no key and no sink
+  const double e = exp2((double)M - mx);  // 1 without a sink; 0 when the row has no key
+  const double Lp = L * e + (sink ? exp2(s2 - mx) : 0.0);
+  if (!(Lp > 0.0)) return n;
+  n.factor = (float)(weight * e / Lp);
+  n.lse = (float)((mx + log2(Lp)) * kLn2);
+  return n;
+}
+
+// Sigmoid output gate of (b, t, h), or 1 without one.
+__device__ __forceinline__ double out_gate_of(const float* g, size_t i) {
+  return g ? 1.0 / (1.0 + exp(-(double)g[i])) : 1.0;
 }
 
 // GATED: the HySparse sparse layer in one workgroup when neither branch is split -- the block
@@ -466,19 +491,21 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   const int hr = u * p.g + r % p.g;
   const size_t ooff = (((size_t)b * p.Tq + jr) * p.Hq + hr) * D + c0;
   float res[CPT];
-  float inv = 0.f;
+  float lse_row = -INFINITY;
   if constexpr (GATED) {
     __syncthreads();  // merge buffers are reused by the window pass
     PassOut<CPT> w;
     attend_pass<D, F32, SRC_WINDOW, NW>(p, p.k2, p.v2, 0, 1 << 30, b, u, j0, nq, smem, pos_all, w);
     if (r >= nrows) return;
     const float* z = p.gate + (((size_t)b * p.Tq + jr) * p.Hq + hr) * 2;
+    const double og = out_gate_of(p.out_gate, ((size_t)b * p.Tq + jr) * p.Hq + hr);
     const double sg = 1.0 / (1.0 + exp(-(double)z[0]));
     const double sl = 1.0 / (1.0 + exp(-(double)z[1]));
-    const float fg = a.L > 0.0 ? (float)(sg / a.L) : 0.f;
-    const float fl = w.L > 0.0 ? (float)(sl / w.L) : 0.f;
+    const RowNorm ng = row_norm(a.M, a.L, p.sink, hr, sg * og);
+    const RowNorm nl = row_norm(w.M, w.L, p.sink2, hr, sl * og);
 #pragma unroll
-    for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * fg + w.ov[c] * fl;
+    for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * ng.factor + w.ov[c] * nl.factor;
+    lse_row = ng.lse;
   } else {
     if (r >= nrows) return;
     if (!p.final_direct) {
@@ -492,9 +519,11 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
       for (int c = 0; c < CPT; c++) p.part_o[prow * D + c0 + c] = a.ov[c];
       return;
     }
-    inv = (a.L > 0.0) ? (float)(1.0 / a.L) : 0.f;
+    const RowNorm n =
+        row_norm(a.M, a.L, p.sink, hr, out_gate_of(p.out_gate, ((size_t)b * p.Tq + jr) * p.Hq + hr));
 #pragma unroll
-    for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * inv;
+    for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * n.factor;
+    lse_row = n.lse;
   }
   if (p.out_f32) {
     float* op = (float*)p.o + ooff;
@@ -505,7 +534,7 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
 #pragma unroll
     for (int c = 0; c < CPT; c++) op[c] = f2bf(res[c]);
   }
-  if (p.lse && c0 == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = lse_of(a);
+  if (p.lse && c0 == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = lse_row;
 }
 
 // ---- split / branch combine ---------------------------------------------------------------
@@ -535,6 +564,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 
   float out[4] = {0.f, 0.f, 0.f, 0.f};
   double lse0 = -INFINITY;
+  const double og = out_gate_of(p.out_gate, ((size_t)b * p.Tq + jr) * p.Hq + hr);
   for (int br = 0; br < p.n_branch; br++) {
     const int ns = p.n_split[br];
     const float* m = p.m[br];
@@ -564,15 +594,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
       for (int q = 0; q < SP; q++)
 #pragma unroll
         for (int e = 0; e < 4; e++) sum[e] += red[q][4 * c + e];
-      float wgt = 1.f;
+      double wgt = og;
       if (p.n_branch == 2) {
         const float z = p.gate[(((size_t)b * p.Tq + jr) * p.Hq + hr) * 2 + br];
-        wgt = (float)(1.0 / (1.0 + exp(-(double)z)));
+        wgt *= 1.0 / (1.0 + exp(-(double)z));
       }
-      const float inv = L > 0.0 ? (float)(wgt / L) : 0.f;
+      const RowNorm n = row_norm(M, L, p.sink[br], hr, wgt);
 #pragma unroll
-      for (int e = 0; e < 4; e++) out[e] += sum[e] * inv;
-      if (br == 0 && c == 0) lse0 = L > 0.0 ? ((double)M + log2(L)) * kLn2 : -INFINITY;
+      for (int e = 0; e < 4; e++) out[e] += sum[e] * n.factor;
+      if (br == 0 && c == 0) lse0 = n.lse;
     }
     __syncthreads();
   }

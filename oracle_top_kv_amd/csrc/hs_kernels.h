@@ -45,6 +45,11 @@ struct RowAttnParams {
   // full attention (range mode, 4 waves) may also store its raw dot products q.k:
   float* logits;   // [B, Tq, Hq, Tk] fp32, or null
   int logits_vec;  // 16-byte stores allowed (Tk % 4 == 0 and an aligned base)
+  // optional per-head sink logits (sink: this pass; sink2: the window branch of the gated
+  // one-pass layer) and sigmoid output-gate logits, applied when the output is final
+  const float* sink;      // [Hq] or null
+  const float* sink2;     // [Hq] or null
+  const float* out_gate;  // [B, Tq, Hq] or null
 };
 
 // Merge of split partials (one or two branches) into O and LSE; with two branches the sigmoid
@@ -61,6 +66,8 @@ struct CombineParams {
   void* o;
   float* lse;  // nullable; LSE of branch 0
   int out_f32;
+  const float* sink[2];   // per branch: [Hq] sink logits or null
+  const float* out_gate;  // [B, Tq, Hq] sigmoid output-gate logits or null
 };
 
 // gated: list source (token or block) then the window branch over k2, v2 in one workgroup,

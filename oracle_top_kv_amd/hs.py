@@ -22,7 +22,7 @@ HS_OP_FULL_ATTN_BLOCK_TOPK = 7
 
 EXPORTS = ["hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk", "hs_sparse_attn_gather",
            "hs_full_attn_fwd_logits", "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
-           "hs_full_attn_block_topk",
+           "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex",
            "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
 
 
@@ -36,6 +36,11 @@ class AttnDesc(ctypes.Structure):
 class SwaBranch(ctypes.Structure):
     _fields_ = [("k_local", ctypes.c_void_p), ("v_local", ctypes.c_void_p),
                 ("gate_logits", ctypes.c_void_p), ("window", ctypes.c_int32)]
+
+
+class SparseOpts(ctypes.Structure):
+    _fields_ = [("sink", ctypes.c_void_p), ("sink_local", ctypes.c_void_p),
+                ("out_gate", ctypes.c_void_p)]
 
 
 class HsError(RuntimeError):
@@ -66,6 +71,9 @@ def lib():
         L.hs_block_topk_from_logits.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.hs_full_attn_block_topk.argtypes = [pd, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz,
                                               vp]
+        L.hs_sparse_attn_gather_ex.argtypes = [pd, vp, vp, vp, ctypes.c_int, vp, vp, i32, i32,
+                                               ctypes.POINTER(SwaBranch),
+                                               ctypes.POINTER(SparseOpts), vp, vp, vp, sz, vp]
         L.hs_workspace_size.argtypes = [ctypes.c_int, pd, i32, i32]
         L.hs_workspace_size.restype = sz
         L.hs_status_string.restype = ctypes.c_char_p
@@ -75,7 +83,7 @@ def lib():
         for f in ("hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk",
                   "hs_sparse_attn_gather", "hs_full_attn_fwd_logits",
                   "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
-                  "hs_full_attn_block_topk"):
+                  "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -258,10 +266,12 @@ def block_score_topk(q, k, lse, block, n_blocks, q_offset=None):
 
 
 def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_offset=None,
-                       out_dtype=None, want_lse=False):
+                       out_dtype=None, want_lse=False, sink=None, sink_local=None, out_gate=None):
     """Sparse layer over the shared K, V and index set with the layer's own q.
     swa = (k_local, v_local, gate_logits fp32 [B,Tq,Hq,2], window) adds the gated sliding-window
-    branch.  Returns (o, lse or None)."""
+    branch.  sink / sink_local: fp32 [Hq] per-head sink logits of the global / window branch;
+    out_gate: fp32 [B,Tq,Hq] sigmoid output-gate logits (hs_sparse_attn_gather_ex).
+    Returns (o, lse or None)."""
     dev = q.device
     _need(q, "q", dev)
     _need(k, "k", dev, dtype=q.dtype)
@@ -286,10 +296,27 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
     lse = (torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
            if want_lse else None)
     ws, n = workspace(HS_OP_SPARSE_ATTN, desc, keys, window, device=dev)
-    _check(lib().hs_sparse_attn_gather(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), kind_code,
-                                       _ptr(idx), _ptr(count), int(cap), int(block),
-                                       ctypes.byref(sw) if sw is not None else None, _ptr(o),
-                                       _ptr(lse), _ptr(ws), n, _stream(dev)),
-           "hs_sparse_attn_gather")
+    if sink is None and sink_local is None and out_gate is None:
+        _check(lib().hs_sparse_attn_gather(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                           kind_code, _ptr(idx), _ptr(count), int(cap),
+                                           int(block),
+                                           ctypes.byref(sw) if sw is not None else None, _ptr(o),
+                                           _ptr(lse), _ptr(ws), n, _stream(dev)),
+               "hs_sparse_attn_gather")
+    else:
+        Hq = q.shape[2]
+        for t, nm, shp in ((sink, "sink", (Hq,)), (sink_local, "sink_local", (Hq,)),
+                           (out_gate, "out_gate", tuple(q.shape[:3]))):
+            if t is not None:
+                _need(t, nm, dev, dtype=torch.float32, shape=shp)
+        opts = SparseOpts(*(t.data_ptr() if t is not None else None
+                            for t in (sink, sink_local, out_gate)))
+        _check(lib().hs_sparse_attn_gather_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                              kind_code, _ptr(idx), _ptr(count), int(cap),
+                                              int(block),
+                                              ctypes.byref(sw) if sw is not None else None,
+                                              ctypes.byref(opts), _ptr(o), _ptr(lse), _ptr(ws),
+                                              n, _stream(dev)),
+               "hs_sparse_attn_gather_ex")
     del keep
     return o, lse

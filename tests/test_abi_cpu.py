@@ -148,6 +148,16 @@ def test_logits_entry_points_argument_checks():
                                        need_bk - 1, None) == hs.HS_ERR_WORKSPACE
 
 
+def test_sparse_options_argument_checks():
+    d = desc()
+    L = hs.lib()
+    opts = hs.SparseOpts(None, 0x1000, None)  # a window-branch sink without a window branch
+    assert L.hs_sparse_attn_gather_ex(ctypes.byref(d), FAKE, FAKE, FAKE, hs.HS_IDX_TOKEN, FAKE,
+                                      FAKE, 8, 64, None, ctypes.byref(opts), FAKE, None, FAKE,
+                                      1 << 40, None) == hs.HS_ERR_INVALID_ARG
+    assert "sink_local" in L.hs_last_error().decode()
+
+
 def test_status_strings():
     L = hs.lib()
     for s in (0, -1, -2, -3, -4):
