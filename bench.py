@@ -254,6 +254,7 @@ def main():
                      "algorithmic_bytes": b_full, "traffic": counter_traffic(wl.name)},
         "step_stored_logits": logits_out,
     }
+    out["step_paged"] = paged_step(wl, x, hs, args, logits_out["ms_per_step"])
     out["sparse_cold_cache"] = cold_sparse(wl, x, hs, costs)
     peaks = measured_peaks()
     out["measured_peaks"] = peaks
@@ -347,6 +348,58 @@ def prefill_leg(args):
             "sparse_layer_logical_GB_per_s": round(b_sp / (t_sp * 1e-3) / 1e9, 1),
             "sparse_layer_tflops": round(f_sp / (t_sp * 1e-3) / 1e12, 1),
             "peak_tflops": 2500.0, "reps": reps}
+
+
+def paged_step(wl, x, hs, args, ms_contiguous, page_size=64):
+    """The stored-logits decode step on a paged cache: K and V in shuffled 64-position pages
+    behind a block table, the window branch's own K', V' in a ring of `window` slots."""
+    import torch
+
+    B, T, Hkv, d = x["k"].shape
+    mp = (T + page_size - 1) // page_size
+    g = torch.Generator().manual_seed(17)
+    table = torch.randperm(B * mp, generator=g).view(B, mp).to(torch.int32).cuda()
+    inv = torch.empty(B * mp, dtype=torch.long)
+    inv[table.view(-1).cpu().long()] = torch.arange(B * mp)
+    inv = inv.cuda()
+
+    def pool(t):
+        p = t.view(B * mp, page_size, Hkv, d)  # logical page order (T is a multiple of 64)
+        return p[inv].contiguous()              # physical page table[b, lp] holds page (b, lp)
+
+    kp, vp = pool(x["k"]), pool(x["v"])
+    ring = wl.window
+    first = T - ring
+    kl = torch.zeros((B, ring, Hkv, d), dtype=x["k"].dtype, device="cuda")
+    vl = torch.zeros_like(kl)
+    pos = torch.arange(first, T, device="cuda")
+    kl[:, pos % ring] = x["k_loc"][:, first:]
+    vl[:, pos % ring] = x["v_loc"][:, first:]
+    pages = (table, T)
+    qs = x["q_sparse"]
+
+    def step():
+        o, lse, lg = hs.full_attn_fwd_paged(x["q"], kp, vp, table, T, logits=True)
+        idx, cnt = hs.oracle_topk_from_logits(lg, lse, Hkv, d, wl.k_global, wl.window)
+        for l in range(wl.n_sparse):
+            hs.sparse_attn_gather(qs[l], kp, vp, idx, cnt, kind="token", pages=pages)
+        bidx, bcnt = hs.block_topk_from_logits(lg, lse, Hkv, d, wl.block, wl.n_blocks)
+        hs.sparse_attn_gather(qs[0], kp, vp, bidx, bcnt, kind="block", block=wl.block,
+                              swa=(kl, vl, x["gate"], wl.window), local_ring=ring, pages=pages)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    del kp, vp, kl, vl
+    return {"ms_per_step": round(ms, 4), "page_size": page_size, "local_ring": ring,
+            "vs_contiguous_stored_logits": round(ms / ms_contiguous, 3)}
 
 
 def cold_sparse(wl, x, hs, costs, reps=10):

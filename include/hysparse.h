@@ -69,7 +69,8 @@ typedef enum {
   HS_OP_FULL_ATTN_LOGITS = 4,       /* p0, p1 unused */
   HS_OP_TOPK_FROM_LOGITS = 5,       /* p0 = k_global, p1 = window */
   HS_OP_BLOCK_TOPK_FROM_LOGITS = 6, /* p0 = block, p1 = n_blocks */
-  HS_OP_FULL_ATTN_BLOCK_TOPK = 7    /* p0 = block, p1 = n_blocks */
+  HS_OP_FULL_ATTN_BLOCK_TOPK = 7,   /* p0 = block, p1 = n_blocks */
+  HS_OP_FULL_ATTN_PAGED = 8         /* p0 = page_size */
 } hs_op;
 
 typedef struct {
@@ -133,7 +134,28 @@ typedef struct {
   const float* sink;
   const float* sink_local;
   const float* out_gate;
+  int32_t local_ring; /* 0: swa->k_local / v_local are position-indexed [B, kv_len, Hkv, d];
+                         > 0: they are rings [B, local_ring, Hkv, d] holding position t in slot
+                         t % local_ring (local_ring >= window), the layer's own small cache
+                         [P2 "Why the local branch cannot reuse the same KV": each sparse layer
+                         keeps its own K', V' only for a ring window of length w] */
 } hs_sparse_opts;
+
+/* Paged K / V cache (serving): K and V are pools [n_pages, page_size, Hkv, d]; the positions
+ * p * page_size .. (p + 1) * page_size - 1 of batch entry b live in the pool's page
+ * block_table[b * max_pages + p].  Index sets keep logical positions (token) or logical 64-key
+ * blocks, whatever the page size; the kernels translate every key position through the table
+ * while they load K / V, so no contiguous copy of the cache is made [P2 engineering constraints
+ * 2 and 3: logical blocks may span several physical pages, the block table translates them,
+ * and the kernel should consume it directly instead of copying to a temporary buffer].
+ * page_size: a power of two; max_pages * page_size >= kv_len.  Table entries outside
+ * [0, n_pages) are clamped into the pool (the result is then wrong, the read stays inside it). */
+typedef struct {
+  const int32_t* block_table; /* [B, max_pages] int32, device memory */
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t n_pages;
+} hs_kv_pages;
 
 /* Full attention and block-level oracle index in one call: the outputs of hs_full_attn_fwd
  * (o, lse) and of hs_block_score_topk (blk_idx, count) for the same inputs.  The pages obtain
@@ -208,6 +230,25 @@ hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logit
                                     const float* lse, int32_t block, int32_t n_blocks,
                                     int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/* hs_full_attn_fwd over a paged K / V cache (always the split row kernel: meant for decode),
+ * optionally keeping the logits like hs_full_attn_fwd_logits (logits may be NULL).  Same o, lse
+ * (and logits) as the contiguous call on the same logical cache.  Workspace:
+ * hs_workspace_size(HS_OP_FULL_ATTN_PAGED, desc, page_size, 0). */
+hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
+                                 const void* v_pool, const hs_kv_pages* pages, void* o, float* lse,
+                                 float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/* hs_sparse_attn_gather_ex over a paged K / V cache (token and block index sets address logical
+ * positions; the sliding-window branch keeps its own position-indexed or ring cache).  Same
+ * outputs as the contiguous call.  Workspace: HS_OP_SPARSE_ATTN, as the contiguous call. */
+hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
+                                      const void* v_pool, const hs_kv_pages* pages,
+                                      hs_index_kind kind, const int32_t* idx,
+                                      const int32_t* count, int32_t idx_cap, int32_t block,
+                                      const hs_swa_branch* swa, const hs_sparse_opts* opts,
+                                      void* o, float* lse_opt, void* ws, size_t ws_bytes,
+                                      void* stream);
 
 /* hs_sparse_attn_gather with options (opts may be NULL: then it is hs_sparse_attn_gather).
  * sink_local requires swa.  Workspace: as hs_sparse_attn_gather (HS_OP_SPARSE_ATTN). */

@@ -391,11 +391,43 @@ size_t sparse_ws(const Shape& s, const SparseGeom& g, int window) {
   return b;
 }
 
+// Geometry of full attention on the row kernel.  Paged K / V: a split's pages are staged in LDS,
+// so no split may span more than kMaxStagedPages of them.
+constexpr long long kMaxStagedPages = 2048;
+RaGeom fa_row_geom(const Shape& s, int page_size) {
+  long long max_steps = 1LL << 40;
+  if (page_size > 0) max_steps = ((kMaxStagedPages - 1) * page_size) / kStepKeys;
+  if (max_steps < 1) max_steps = 1;
+  return ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups, max_steps);
+}
+
+hs_status check_pages(const Shape& s, const hs_kv_pages* pg) {
+  if (!pg || !pg->block_table) return fail(HS_ERR_INVALID_ARG, "NULL page table");
+  const int P = pg->page_size;
+  if (P < 1 || (P & (P - 1)) || P > (1 << 20))
+    return fail(HS_ERR_INVALID_ARG, "page_size %d: must be a power of two (1 .. 2^20)", P);
+  if (pg->n_pages < 1) return fail(HS_ERR_INVALID_ARG, "n_pages must be >= 1");
+  if ((long long)pg->max_pages * P < s.Tk)
+    return fail(HS_ERR_INVALID_ARG, "max_pages %d x page_size %d < kv_len %d", pg->max_pages, P,
+                s.Tk);
+  if ((long long)pg->n_pages * P * s.Hkv * s.D > (1LL << 40))
+    return fail(HS_ERR_UNSUPPORTED, "page pool too large");
+  return HS_OK;
+}
+
+void set_pages(hs::RowAttnParams& p, const hs_kv_pages* pg) {
+  p.pages = pg->block_table;
+  p.page_size = pg->page_size;
+  p.max_pages = pg->max_pages;
+  p.n_pages = pg->n_pages;
+}
+
 // Full attention on the row kernel (decode and short query blocks); logits != nullptr also
 // stores every computed dot product q.k to logits [B, Tq, Hq, Tk].
 hs_status row_full_attn(const Shape& s, const void* q, const void* k, const void* v, void* o,
-                        float* lse, float* logits, void* ws, size_t ws_bytes, void* stream) {
-  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
+                        float* lse, float* logits, void* ws, size_t ws_bytes, void* stream,
+                        const hs_kv_pages* pages = nullptr) {
+  const RaGeom g = fa_row_geom(s, pages ? pages->page_size : 0);
   const size_t need = g.n_split > 1 ? partial_bytes(g, s.D) : 0;
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
@@ -407,6 +439,7 @@ hs_status row_full_attn(const Shape& s, const void* q, const void* k, const void
   p.lse = lse;
   p.logits = logits;
   p.logits_vec = logits && s.Tk % 4 == 0 && (uintptr_t)logits % 16 == 0;
+  if (pages) set_pages(p, pages);
   p.final_direct = g.n_split == 1;
   if (!p.final_direct) carve_partials(ws, g, s.D, &p.part_m, &p.part_l, &p.part_o);
   hipStream_t hst = (hipStream_t)stream;
@@ -528,7 +561,12 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
       return sparse_ws(s, sparse_geom(s, p0, p1), p1);
     }
     case HS_OP_FULL_ATTN_LOGITS: {
-      const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
+      const RaGeom g = fa_row_geom(s, 0);
+      return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+    }
+    case HS_OP_FULL_ATTN_PAGED: {
+      if (p0 < 1 || (p0 & (p0 - 1))) return 0;
+      const RaGeom g = fa_row_geom(s, p0);
       return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
     }
     case HS_OP_TOPK_FROM_LOGITS: return tk_ws(s, tl_geom(s));
@@ -595,6 +633,19 @@ hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const
   if (!q || !k || !v || !o || !lse || !logits) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
   if ((uintptr_t)logits % 4) return fail(HS_ERR_INVALID_ARG, "logits must be 4-byte aligned");
   return row_full_attn(s, q, k, v, o, lse, logits, ws, ws_bytes, stream);
+}
+
+hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
+                                 const void* v_pool, const hs_kv_pages* pages, void* o, float* lse,
+                                 float* logits, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  if (!q || !k_pool || !v_pool || !o || !lse) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  st = check_pages(s, pages);
+  if (st != HS_OK) return st;
+  if (logits && (uintptr_t)logits % 4) return fail(HS_ERR_INVALID_ARG, "logits must be 4-byte aligned");
+  return row_full_attn(s, q, k_pool, v_pool, o, lse, logits, ws, ws_bytes, stream, pages);
 }
 
 hs_status hs_oracle_topk_from_logits(const hs_attn_desc* desc, const float* logits,
@@ -716,12 +767,28 @@ hs_status hs_sparse_attn_gather_ex(const hs_attn_desc* desc, const void* q, cons
                                    const int32_t* count, int32_t idx_cap, int32_t block,
                                    const hs_swa_branch* swa, const hs_sparse_opts* opts, void* o,
                                    float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
+  return hs_sparse_attn_gather_paged(desc, q, k_full, v_full, nullptr, kind, idx, count, idx_cap,
+                                     block, swa, opts, o, lse_opt, ws, ws_bytes, stream);
+}
+
+hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, const void* k_full,
+                                      const void* v_full, const hs_kv_pages* pages,
+                                      hs_index_kind kind, const int32_t* idx,
+                                      const int32_t* count, int32_t idx_cap, int32_t block,
+                                      const hs_swa_branch* swa, const hs_sparse_opts* opts,
+                                      void* o, float* lse_opt, void* ws, size_t ws_bytes,
+                                      void* stream) {
   const float* sink_g = opts ? opts->sink : nullptr;
   const float* sink_l = opts ? opts->sink_local : nullptr;
   const float* ogate = opts ? opts->out_gate : nullptr;
+  const int ring = opts ? opts->local_ring : 0;
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
+  if (pages) {
+    st = check_pages(s, pages);
+    if (st != HS_OK) return st;
+  }
   if (!q || !k_full || !v_full || !idx || !count || !o)
     return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
   if (kind != HS_IDX_TOKEN && kind != HS_IDX_BLOCK) return fail(HS_ERR_INVALID_ARG, "unknown index kind");
@@ -738,6 +805,10 @@ hs_status hs_sparse_attn_gather_ex(const hs_attn_desc* desc, const void* q, cons
   }
   if (sink_l && !swa)
     return fail(HS_ERR_INVALID_ARG, "sink_local given without a sliding-window branch");
+  if (ring < 0 || (ring > 0 && !swa))
+    return fail(HS_ERR_INVALID_ARG, "local_ring %d: needs a sliding-window branch", ring);
+  if (ring > 0 && ring < window)
+    return fail(HS_ERR_INVALID_ARG, "local_ring %d shorter than the window %d", ring, window);
   const SparseGeom g = sparse_geom(s, keys, window);
   const size_t need = sparse_ws(s, g, window);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -758,6 +829,8 @@ hs_status hs_sparse_attn_gather_ex(const hs_attn_desc* desc, const void* q, cons
   pg.sink = sink_g;
   pg.sink2 = sink_l;
   pg.out_gate = ogate;
+  pg.ring = ring;
+  if (pages) set_pages(pg, pages);
   const hs::KeySrc src = kind == HS_IDX_TOKEN ? hs::SRC_TOKEN : hs::SRC_BLOCK;
   if (g.fused) {
     pg.k2 = swa->k_local;
@@ -782,6 +855,7 @@ hs_status hs_sparse_attn_gather_ex(const hs_attn_desc* desc, const void* q, cons
     pl.k = swa->k_local;
     pl.v = swa->v_local;
     pl.window = window;
+    pl.ring = ring;
     pl.final_direct = 0;
     carve_partials(w, g.loc, s.D, &pl.part_m, &pl.part_l, &pl.part_o);
     e = hs::launch_row_attn(pl, s.D, s.in_f32, hs::SRC_WINDOW, hst);

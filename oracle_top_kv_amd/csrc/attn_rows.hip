@@ -99,11 +99,15 @@ struct PassOut {
 // can run its window branch over K', V' in the same workgroup).  Ends with the four waves
 // merged; `smem` and `pos_all` are free again once the caller has synchronized.  LOGITS (range
 // mode only): every lane also stores the raw dot products q.k it computed to p.logits.
-template <int D, bool F32, int SRC, int NW, bool LOGITS = false>
+// PAGED (range and list modes): K and V are page pools [n_pages, page_size, Hkv, d] addressed
+// through the block table; `row_all` holds the split's physical rows (list modes).  The window
+// source reads a ring of p.ring slots (position t at slot t % ring) when p.ring > 0.
+template <int D, bool F32, int SRC, int NW, bool LOGITS = false, bool PAGED = false>
 __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* kmat,
                                             const void* vmat, int split, int steps_per_split,
                                             int b, int u, int j0, int nq, unsigned char* smem,
-                                            int* pos_all, PassOut<RaCfg<D, F32, NW>::kCPT>& out) {
+                                            int* pos_all, int* row_all,
+                                            PassOut<RaCfg<D, F32, NW>::kCPT>& out) {
   using Cfg = RaCfg<D, F32, NW>;
   constexpr int kWaves = NW;
   const int lane = threadIdx.x & 63;
@@ -203,14 +207,56 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
 
   // Positions of this split's key-list entries.  List modes stage them in LDS once (so the
   // K/V loads of the next step can be issued without waiting on an index load); range modes
-  // compute them.
+  // compute them.  PAGED: list modes also stage each entry's physical row; the range mode
+  // stages the physical page of every logical page the split touches.
   constexpr bool kList = (SRC == SRC_TOKEN || SRC == SRC_BLOCK);
+  static_assert(!PAGED || SRC == SRC_RANGE || kList, "the window source is never paged");
+  const int pg_shift = PAGED ? __ffs(p.page_size) - 1 : 0;
+  const int32_t* table = PAGED ? p.pages + (size_t)b * p.max_pages : nullptr;
+  auto phys_page = [&](int logical) -> int {
+    const int e = table[logical];
+    return e < 0 ? 0 : (e >= p.n_pages ? p.n_pages - 1 : e);  // stays inside the pool
+  };
+  int first_page = 0;
   if constexpr (kList) {
     const int n_e = (step_end - step_begin) * kStep;
-    for (int i = threadIdx.x; i < n_e; i += Cfg::kThreads)
-      pos_all[i] = entry_pos<SRC>(p, step_begin * kStep + i, L, lo, t_last, list);
+    for (int i = threadIdx.x; i < n_e; i += Cfg::kThreads) {
+      const int pos = entry_pos<SRC>(p, step_begin * kStep + i, L, lo, t_last, list);
+      pos_all[i] = pos;
+      if constexpr (PAGED) {
+        const int q = pos < 0 ? 0 : pos;
+        row_all[i] = (phys_page(q >> pg_shift) << pg_shift) | (q & (p.page_size - 1));
+      }
+    }
+    __syncthreads();
+  } else if constexpr (PAGED) {
+    if (step_begin < step_end) {
+      first_page = (int)((lo + (long long)step_begin * kStep) >> pg_shift);
+      const int last_page = (int)((lo + min((long long)step_end * kStep, (long long)L) - 1) >> pg_shift);
+      for (int i = threadIdx.x; i <= last_page - first_page; i += Cfg::kThreads)
+        pos_all[i] = phys_page(first_page + i);
+    }
     __syncthreads();
   }
+  // element offset of key entry i of a step (position pos >= 0, or -1: any valid row) in K / V
+  auto kv_off = [&](int step, int i, int pos) -> size_t {
+    if constexpr (PAGED && kList) {
+      return ((size_t)row_all[(step - step_begin) * kStep + i] * p.Hkv + u) * D;
+    } else if constexpr (PAGED) {
+      const int q = pos < 0 ? 0 : pos;  // past the end: any staged row
+      const int pg = (q >> pg_shift) - first_page;
+      const size_t row = ((size_t)pos_all[pg < 0 ? 0 : pg] << pg_shift) |
+                         (size_t)(q & (p.page_size - 1));
+      return (row * p.Hkv + u) * D;
+    } else if constexpr (SRC == SRC_WINDOW) {
+      if (pos < 0) pos = 0;
+      if (p.ring > 0) return (((size_t)b * p.ring + pos % p.ring) * p.Hkv + u) * D;
+      return kv_base + (size_t)pos * kv_row_stride;
+    } else {
+      if (pos < 0) pos = 0;
+      return kv_base + (size_t)pos * kv_row_stride;
+    }
+  };
   auto pos_of = [&](int step, int i) -> int {
     if constexpr (kList) {
       return pos_all[(step - step_begin) * kStep + i];
@@ -227,17 +273,18 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   using KReg = typename std::conditional<F32, float, u32x4>::type;
   auto load_step = [&](int step, KReg (&k0)[KK], KReg (&k1)[KK], u32x4 (&vr)[VL]) {
     const int pk0 = pos_of(step, rn), pk1 = pos_of(step, 16 + rn);
+    const size_t ko0 = kv_off(step, rn, pk0), ko1 = kv_off(step, 16 + rn, pk1);
     if constexpr (!F32) {
-      const uint16_t* kp0 = (const uint16_t*)kmat + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + 8 * jg;
-      const uint16_t* kp1 = (const uint16_t*)kmat + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + 8 * jg;
+      const uint16_t* kp0 = (const uint16_t*)kmat + ko0 + 8 * jg;
+      const uint16_t* kp1 = (const uint16_t*)kmat + ko1 + 8 * jg;
 #pragma unroll
       for (int kk = 0; kk < KK; kk++) {
         k0[kk] = *(const u32x4*)(kp0 + 32 * kk);
         k1[kk] = *(const u32x4*)(kp1 + 32 * kk);
       }
     } else {
-      const float* kp0 = (const float*)kmat + kv_base + (size_t)(pk0 < 0 ? 0 : pk0) * kv_row_stride + jg * KK;
-      const float* kp1 = (const float*)kmat + kv_base + (size_t)(pk1 < 0 ? 0 : pk1) * kv_row_stride + jg * KK;
+      const float* kp0 = (const float*)kmat + ko0 + jg * KK;
+      const float* kp1 = (const float*)kmat + ko1 + jg * KK;
 #pragma unroll
       for (int s2 = 0; s2 < KK; s2++) {
         k0[s2] = kp0[s2];
@@ -249,8 +296,7 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
       const int c = n * 64 + lane;
       const int e = c / Cfg::kChunksPerRow, qc = c % Cfg::kChunksPerRow;
       const int pv = pos_of(step, e);
-      const unsigned char* vp = (const unsigned char*)vmat +
-          (kv_base + (size_t)(pv < 0 ? 0 : pv) * kv_row_stride) * Cfg::kElem + qc * 16;
+      const unsigned char* vp = (const unsigned char*)vmat + kv_off(step, e, pv) * Cfg::kElem + qc * 16;
       vr[n] = ld_stream(vp);
     }
   };
@@ -456,7 +502,7 @@ __device__ __forceinline__ double out_gate_of(const float* g, size_t i) {
 // GATED: the HySparse sparse layer in one workgroup when neither branch is split -- the block
 // (or token) branch over K, V, then the sliding-window branch over K', V' (p.k2, p.v2), each
 // normalized on its own and weighted by its sigmoid gate [P2 "Same query, two memories"].
-template <int D, bool F32, int SRC, bool GATED, int NW, bool LOGITS = false>
+template <int D, bool F32, int SRC, bool GATED, int NW, bool LOGITS = false, bool PAGED = false>
 __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   using Cfg = RaCfg<D, F32, NW>;
   // LOGITS: the logit staging rows of every wave follow the V tiles
@@ -466,6 +512,7 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
           : Cfg::kSmem;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
   __shared__ int pos_all[kMaxListEntries];
+  __shared__ int row_all[PAGED && SRC != SRC_RANGE ? kMaxListEntries : 1];
 
   // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
   // workgroups reading the same positions of the Hkv interleaved heads run together (whole
@@ -482,8 +529,8 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
 
   constexpr int CPT = Cfg::kCPT;  // columns per merge thread
   PassOut<CPT> a;
-  attend_pass<D, F32, SRC, NW, LOGITS>(p, p.k, p.v, split, p.steps_per_split, b, u, j0, nq, smem,
-                                       pos_all, a);
+  attend_pass<D, F32, SRC, NW, LOGITS, PAGED>(p, p.k, p.v, split, p.steps_per_split, b, u, j0,
+                                              nq, smem, pos_all, row_all, a);
 
   const int r = threadIdx.x / Cfg::kTPR;
   const int c0 = (threadIdx.x % Cfg::kTPR) * CPT;
@@ -495,7 +542,8 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   if constexpr (GATED) {
     __syncthreads();  // merge buffers are reused by the window pass
     PassOut<CPT> w;
-    attend_pass<D, F32, SRC_WINDOW, NW>(p, p.k2, p.v2, 0, 1 << 30, b, u, j0, nq, smem, pos_all, w);
+    attend_pass<D, F32, SRC_WINDOW, NW>(p, p.k2, p.v2, 0, 1 << 30, b, u, j0, nq, smem, pos_all,
+                                        row_all, w);
     if (r >= nrows) return;
     const float* z = p.gate + (((size_t)b * p.Tq + jr) * p.Hq + hr) * 2;
     const double og = out_gate_of(p.out_gate, ((size_t)b * p.Tq + jr) * p.Hq + hr);
@@ -619,7 +667,38 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }
 
 template <int D, bool F32, int NW>
+hipError_t launch_ra_paged(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
+  const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu);
+  const int threads = 64 * NW;
+  if (gated) {
+    if (src == SRC_TOKEN)
+      row_attn_kernel<D, F32, SRC_TOKEN, true, NW, false, true><<<grid, threads, 0, stream>>>(p);
+    else if (src == SRC_BLOCK)
+      row_attn_kernel<D, F32, SRC_BLOCK, true, NW, false, true><<<grid, threads, 0, stream>>>(p);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  switch (src) {
+    case SRC_RANGE:
+      if constexpr (NW == 4) {
+        if (p.logits)
+          row_attn_kernel<D, F32, SRC_RANGE, false, 4, true, true><<<grid, threads, 0, stream>>>(p);
+        else
+          row_attn_kernel<D, F32, SRC_RANGE, false, 4, false, true><<<grid, threads, 0, stream>>>(p);
+        break;
+      }
+      return hipErrorInvalidValue;
+    case SRC_TOKEN: row_attn_kernel<D, F32, SRC_TOKEN, false, NW, false, true><<<grid, threads, 0, stream>>>(p); break;
+    case SRC_BLOCK: row_attn_kernel<D, F32, SRC_BLOCK, false, NW, false, true><<<grid, threads, 0, stream>>>(p); break;
+    default: return hipErrorInvalidValue;  // the window source is never paged
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool F32, int NW>
 hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
+  if (p.pages) return launch_ra_paged<D, F32, NW>(p, src, gated, stream);
   const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu);
   const int threads = 64 * NW;
   if (p.logits) {

@@ -50,6 +50,11 @@ struct RowAttnParams {
   const float* sink;      // [Hq] or null
   const float* sink2;     // [Hq] or null
   const float* out_gate;  // [B, Tq, Hq] or null
+  // paged K / V (range and list sources): pools [n_pages, page_size, Hkv, d], page of logical
+  // page lp of batch entry b = pages[b * max_pages + lp]; page_size a power of two
+  const int32_t* pages;
+  int page_size, max_pages, n_pages;
+  int ring;  // window source: K2 / V2 (or K / V) are rings [B, ring, Hkv, d], slot t % ring (0: none)
 };
 
 // Merge of split partials (one or two branches) into O and LSE; with two branches the sigmoid

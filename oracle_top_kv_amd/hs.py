@@ -18,11 +18,12 @@ HS_BF16, HS_F32 = 0, 1
 HS_IDX_TOKEN, HS_IDX_BLOCK = 0, 1
 HS_OP_FULL_ATTN, HS_OP_ORACLE_TOPK, HS_OP_BLOCK_TOPK, HS_OP_SPARSE_ATTN = 0, 1, 2, 3
 HS_OP_FULL_ATTN_LOGITS, HS_OP_TOPK_FROM_LOGITS, HS_OP_BLOCK_TOPK_FROM_LOGITS = 4, 5, 6
-HS_OP_FULL_ATTN_BLOCK_TOPK = 7
+HS_OP_FULL_ATTN_BLOCK_TOPK, HS_OP_FULL_ATTN_PAGED = 7, 8
 
 EXPORTS = ["hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk", "hs_sparse_attn_gather",
            "hs_full_attn_fwd_logits", "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
-           "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex",
+           "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex", "hs_full_attn_fwd_paged",
+           "hs_sparse_attn_gather_paged",
            "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
 
 
@@ -40,7 +41,12 @@ class SwaBranch(ctypes.Structure):
 
 class SparseOpts(ctypes.Structure):
     _fields_ = [("sink", ctypes.c_void_p), ("sink_local", ctypes.c_void_p),
-                ("out_gate", ctypes.c_void_p)]
+                ("out_gate", ctypes.c_void_p), ("local_ring", ctypes.c_int32)]
+
+
+class KvPages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
 
 
 class HsError(RuntimeError):
@@ -74,6 +80,11 @@ def lib():
         L.hs_sparse_attn_gather_ex.argtypes = [pd, vp, vp, vp, ctypes.c_int, vp, vp, i32, i32,
                                                ctypes.POINTER(SwaBranch),
                                                ctypes.POINTER(SparseOpts), vp, vp, vp, sz, vp]
+        pp = ctypes.POINTER(KvPages)
+        L.hs_full_attn_fwd_paged.argtypes = [pd, vp, vp, vp, pp, vp, vp, vp, vp, sz, vp]
+        L.hs_sparse_attn_gather_paged.argtypes = [pd, vp, vp, vp, pp, ctypes.c_int, vp, vp, i32,
+                                                  i32, ctypes.POINTER(SwaBranch),
+                                                  ctypes.POINTER(SparseOpts), vp, vp, vp, sz, vp]
         L.hs_workspace_size.argtypes = [ctypes.c_int, pd, i32, i32]
         L.hs_workspace_size.restype = sz
         L.hs_status_string.restype = ctypes.c_char_p
@@ -83,7 +94,8 @@ def lib():
         for f in ("hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk",
                   "hs_sparse_attn_gather", "hs_full_attn_fwd_logits",
                   "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
-                  "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex"):
+                  "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex",
+                  "hs_full_attn_fwd_paged", "hs_sparse_attn_gather_paged"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -150,6 +162,46 @@ def full_attn_fwd(q, k, v, q_offset=None, out_dtype=None):
     _check(lib().hs_full_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                   _ptr(lse), _ptr(ws), n, _stream(dev)), "hs_full_attn_fwd")
     return o, lse
+
+
+def _pages(k_pool, block_table, page_size, dev):
+    _need(block_table, "block_table", dev, dtype=torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages]")
+    return KvPages(block_table.data_ptr(), int(page_size), int(block_table.shape[1]),
+                   int(k_pool.shape[0]))
+
+
+def _paged_desc(q, k_pool, kv_len, q_offset, out_dtype):
+    B, Tq, Hq, d = q.shape
+    n_pages, P, Hkv, dk = k_pool.shape
+    if d != dk:
+        raise ValueError("q and the page pool disagree on head_dim")
+    out = q.dtype if out_dtype is None else out_dtype
+    return AttnDesc(B, Tq, int(kv_len), Hq, Hkv, d, -1 if q_offset is None else int(q_offset),
+                    _dtype_code(q.dtype), _dtype_code(out))
+
+
+def full_attn_fwd_paged(q, k_pool, v_pool, block_table, kv_len, logits=False, q_offset=None,
+                        out_dtype=None):
+    """Full attention over a paged cache: k_pool, v_pool [n_pages, page_size, Hkv, d],
+    block_table int32 [B, max_pages].  Returns (o, lse) or (o, lse, logits)."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, n, dev, dtype=q.dtype)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool shapes differ")
+    desc = _paged_desc(q, k_pool, kv_len, q_offset, out_dtype)
+    pg = _pages(k_pool, block_table, k_pool.shape[1], dev)
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
+    lg = (torch.empty((q.shape[0], q.shape[1], q.shape[2], int(kv_len)), dtype=torch.float32,
+                      device=dev) if logits else None)
+    ws, n = workspace(HS_OP_FULL_ATTN_PAGED, desc, k_pool.shape[1], device=dev)
+    _check(lib().hs_full_attn_fwd_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                        ctypes.byref(pg), _ptr(o), _ptr(lse), _ptr(lg), _ptr(ws),
+                                        n, _stream(dev)), "hs_full_attn_fwd_paged")
+    return (o, lse, lg) if logits else (o, lse)
 
 
 def full_attn_block_topk(q, k, v, block, n_blocks, q_offset=None, out_dtype=None):
@@ -266,19 +318,27 @@ def block_score_topk(q, k, lse, block, n_blocks, q_offset=None):
 
 
 def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_offset=None,
-                       out_dtype=None, want_lse=False, sink=None, sink_local=None, out_gate=None):
+                       out_dtype=None, want_lse=False, sink=None, sink_local=None, out_gate=None,
+                       local_ring=0, pages=None):
     """Sparse layer over the shared K, V and index set with the layer's own q.
     swa = (k_local, v_local, gate_logits fp32 [B,Tq,Hq,2], window) adds the gated sliding-window
-    branch.  sink / sink_local: fp32 [Hq] per-head sink logits of the global / window branch;
+    branch; local_ring > 0: k_local / v_local are rings [B, local_ring, Hkv, d].
+    sink / sink_local: fp32 [Hq] per-head sink logits of the global / window branch;
     out_gate: fp32 [B,Tq,Hq] sigmoid output-gate logits (hs_sparse_attn_gather_ex).
-    Returns (o, lse or None)."""
+    pages = (block_table int32 [B, max_pages], kv_len): k, v are page pools
+    [n_pages, page_size, Hkv, d] (hs_sparse_attn_gather_paged).  Returns (o, lse or None)."""
     dev = q.device
     _need(q, "q", dev)
     _need(k, "k", dev, dtype=q.dtype)
     _need(v, "v", dev, dtype=q.dtype)
     _need(idx, "idx", dev, dtype=torch.int32)
     _need(count, "count", dev, dtype=torch.int32, shape=idx.shape[:3])
-    desc = make_desc(q, k, q_offset, out_dtype)
+    if pages is not None:
+        desc = _paged_desc(q, k, pages[1], q_offset, out_dtype)
+        pg = _pages(k, pages[0], k.shape[1], dev)
+    else:
+        desc = make_desc(q, k, q_offset, out_dtype)
+        pg = None
     kind_code = HS_IDX_TOKEN if kind == "token" else HS_IDX_BLOCK
     cap = idx.shape[-1]
     keys = cap if kind_code == HS_IDX_TOKEN else cap * block
@@ -287,8 +347,10 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
     keep = []
     if swa is not None:
         kl, vl, gate, window = swa
-        _need(kl, "k_local", dev, dtype=q.dtype, shape=k.shape)
-        _need(vl, "v_local", dev, dtype=q.dtype, shape=k.shape)
+        loc_shape = ((q.shape[0], int(local_ring)) + tuple(k.shape[2:]) if local_ring
+                     else (q.shape[0], desc.kv_len) + tuple(k.shape[2:]))
+        _need(kl, "k_local", dev, dtype=q.dtype, shape=loc_shape)
+        _need(vl, "v_local", dev, dtype=q.dtype, shape=loc_shape)
         _need(gate, "gate_logits", dev, dtype=torch.float32, shape=tuple(q.shape[:3]) + (2,))
         sw = SwaBranch(kl.data_ptr(), vl.data_ptr(), gate.data_ptr(), int(window))
         keep = [kl, vl, gate]
@@ -296,7 +358,7 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
     lse = (torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
            if want_lse else None)
     ws, n = workspace(HS_OP_SPARSE_ATTN, desc, keys, window, device=dev)
-    if sink is None and sink_local is None and out_gate is None:
+    if sink is None and sink_local is None and out_gate is None and not local_ring and pg is None:
         _check(lib().hs_sparse_attn_gather(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                            kind_code, _ptr(idx), _ptr(count), int(cap),
                                            int(block),
@@ -310,13 +372,14 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
             if t is not None:
                 _need(t, nm, dev, dtype=torch.float32, shape=shp)
         opts = SparseOpts(*(t.data_ptr() if t is not None else None
-                            for t in (sink, sink_local, out_gate)))
-        _check(lib().hs_sparse_attn_gather_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
-                                              kind_code, _ptr(idx), _ptr(count), int(cap),
-                                              int(block),
-                                              ctypes.byref(sw) if sw is not None else None,
-                                              ctypes.byref(opts), _ptr(o), _ptr(lse), _ptr(ws),
-                                              n, _stream(dev)),
-               "hs_sparse_attn_gather_ex")
+                            for t in (sink, sink_local, out_gate)), int(local_ring))
+        _check(lib().hs_sparse_attn_gather_paged(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                                 ctypes.byref(pg) if pg is not None else None,
+                                                 kind_code, _ptr(idx), _ptr(count), int(cap),
+                                                 int(block),
+                                                 ctypes.byref(sw) if sw is not None else None,
+                                                 ctypes.byref(opts), _ptr(o), _ptr(lse),
+                                                 _ptr(ws), n, _stream(dev)),
+               "hs_sparse_attn_gather_paged")
     del keep
     return o, lse

@@ -1,0 +1,174 @@
+"""GPU parity of the paged K / V cache (hs_full_attn_fwd_paged, hs_sparse_attn_gather_paged) and
+of the ring-buffered sliding-window cache: the same logical cache laid out in shuffled pages
+(or a ring) must give bit-identical outputs to the contiguous calls, whose parity with the
+oracle the other tests establish; one decode pipeline is also checked against the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle_top_kv_amd.inputs import Workload, make_inputs, to_numpy_f32
+from parity_utils import TOL_BF16, check_token_sets, max_abs
+
+pytestmark = pytest.mark.gpu
+
+
+def hs():
+    from oracle_top_kv_amd import hs as _hs
+    return _hs
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def paged(t, page_size, seed, spare=3):
+    """[B, T, Hkv, d] -> (pool [n_pages, P, Hkv, d], block_table [B, max_pages]): every logical
+    page of every batch entry in its own physical page, in a shuffled order, with a few unused
+    pages in the pool (filled with large values that must never be read)."""
+    B, T, Hkv, d = t.shape
+    mp = (T + page_size - 1) // page_size
+    n = B * mp + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n, generator=g)[:B * mp].view(B, mp).to(torch.int32)
+    pool = torch.full((n, page_size, Hkv, d), 1e4, dtype=t.dtype, device=t.device)
+    for b in range(B):
+        for p in range(mp):
+            rows = t[b, p * page_size:(p + 1) * page_size]
+            pool[perm[b, p], :rows.shape[0]] = rows
+    return pool, perm.to(t.device)
+
+
+FA_CASES = [
+    ("decode_g4_p64", Workload("d4", 2, 1, 5000, 32, 8, 128, "bf16", seed=601), 64),
+    ("decode_g16_p16_ragged", Workload("d16", 2, 1, 3001, 64, 4, 128, "bf16", seed=602), 16),
+    ("short_block_d64_p256", Workload("sb", 2, 3, 777, 8, 2, 64, "bf16", seed=603), 256),
+    ("tiny_f32_p32", Workload("tf", 1, 64, 300, 4, 1, 64, "f32", seed=604), 32),
+    ("decode_p1", Workload("p1", 1, 1, 700, 16, 4, 128, "bf16", seed=605), 1),
+    # a long split: many pages staged per workgroup
+    ("decode_g4_70k_p16", Workload("dl", 1, 1, 70000, 32, 8, 128, "bf16", seed=606), 16),
+]
+
+
+@pytest.mark.parametrize("name,wl,P", FA_CASES, ids=[c[0] for c in FA_CASES])
+def test_paged_full_attention_equals_contiguous(name, wl, P):
+    say(f"[paged full attention] {name} {wl} page {P}")
+    x = make_inputs(wl, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    kp, table = paged(k, P, wl.seed)
+    vp, _ = paged(v, P, wl.seed)
+    o, lse, lg = hs().full_attn_fwd_logits(q, k, v, out_dtype=torch.float32)
+    o2, lse2, lg2 = hs().full_attn_fwd_paged(q, kp, vp, table, wl.kv_len, logits=True,
+                                             out_dtype=torch.float32)
+    o3, lse3 = hs().full_attn_fwd_paged(q, kp, vp, table, wl.kv_len, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(o, o3)
+    assert torch.equal(lse, lse3)
+    t = wl.q_offset + torch.arange(wl.q_len, device="cuda")
+    causal = (torch.arange(wl.kv_len, device="cuda")[None, :] <= t[:, None])[None, :, None, :]
+    assert torch.equal(lg.masked_fill(~causal, 0), lg2.masked_fill(~causal, 0))
+
+
+SPARSE_CASES = [
+    ("decode_g4_split_p64", Workload("s4", 2, 1, 6000, 32, 8, 128, "bf16", seed=611), 64),
+    ("decode_g4_wide_p16", Workload("sw", 16, 1, 3000, 32, 8, 128, "bf16", seed=612), 16),
+    ("prefill_g4_p32", Workload("sp", 1, 40, 1500, 8, 2, 128, "bf16", seed=613), 32),
+    ("decode_p1", Workload("s1", 1, 1, 900, 16, 4, 128, "bf16", k_global=200, window=32,
+                           seed=614), 1),
+]
+
+
+@pytest.mark.parametrize("name,wl,P", SPARSE_CASES, ids=[c[0] for c in SPARSE_CASES])
+def test_paged_sparse_token_equals_contiguous(name, wl, P):
+    say(f"[paged sparse token] {name} {wl} page {P}")
+    x = make_inputs(wl, device="cuda", n_sparse=1)
+    q, k, v, qs = x["q"], x["k"], x["v"], x["q_sparse"][0]
+    _, lse = hs().full_attn_fwd(q, k, v)
+    idx, cnt = hs().oracle_topk(q, k, lse, wl.k_global, wl.window) \
+        if wl.n_q_heads // wl.n_kv_heads in (4, 8, 16) else (None, None)
+    kp, table = paged(k, P, wl.seed)
+    vp, _ = paged(v, P, wl.seed)
+    g = torch.Generator().manual_seed(wl.seed)
+    sink = torch.randn(wl.n_q_heads, generator=g).cuda()
+    o, l1 = hs().sparse_attn_gather(qs, k, v, idx, cnt, kind="token", out_dtype=torch.float32,
+                                    want_lse=True, sink=sink)
+    o2, l2 = hs().sparse_attn_gather(qs, kp, vp, idx, cnt, kind="token", out_dtype=torch.float32,
+                                     want_lse=True, sink=sink, pages=(table, wl.kv_len))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(l1, l2)
+
+
+GATED_CASES = [
+    ("decode_g4_split_p64_ring", Workload("gd", 2, 1, 5000, 32, 8, 128, "bf16", block=64,
+                                          n_blocks=16, window=128, seed=621), 64, 160),
+    ("decode_g4_wide_p32", Workload("gw", 16, 1, 3000, 32, 8, 128, "bf16", block=64,
+                                    n_blocks=16, window=128, seed=622), 32, 0),
+    ("prefill_fused_p16_ring", Workload("gf", 1, 600, 1200, 16, 4, 128, "bf16", block=64,
+                                        n_blocks=4, window=32, seed=623), 16, 700),
+    ("prefill_split_p128", Workload("gp", 1, 70, 900, 8, 2, 128, "bf16", block=64, n_blocks=4,
+                                    window=32, seed=624), 128, 0),
+]
+
+
+def ring_of(t, ring, first):
+    """Position-indexed [B, T, Hkv, d] -> ring [B, ring, Hkv, d] holding positions >= first."""
+    out = torch.zeros((t.shape[0], ring) + tuple(t.shape[2:]), dtype=t.dtype, device=t.device)
+    for pos in range(first, t.shape[1]):
+        out[:, pos % ring] = t[:, pos]
+    return out
+
+
+@pytest.mark.parametrize("name,wl,P,ring", GATED_CASES, ids=[c[0] for c in GATED_CASES])
+def test_paged_gated_layer_equals_contiguous(name, wl, P, ring):
+    say(f"[paged gated] {name} {wl} page {P} ring {ring}")
+    x = make_inputs(wl, device="cuda", block_variant=True)
+    q, k, v, qs = x["q"], x["k"], x["v"], x["q_sparse"][0]
+    _, lse = hs().full_attn_fwd(q, k, v)
+    bi, bc = hs().block_score_topk(q, k, lse, wl.block, wl.n_blocks)
+    kp, table = paged(k, P, wl.seed)
+    vp, _ = paged(v, P, wl.seed)
+    g = torch.Generator().manual_seed(wl.seed)
+    s1, s2 = torch.randn(wl.n_q_heads, generator=g).cuda(), torch.randn(wl.n_q_heads, generator=g).cuda()
+    swa = (x["k_loc"], x["v_loc"], x["gate"], wl.window)
+    o, l1 = hs().sparse_attn_gather(qs, k, v, bi, bc, kind="block", block=wl.block, swa=swa,
+                                    out_dtype=torch.float32, want_lse=True, sink=s1,
+                                    sink_local=s2)
+    if ring:
+        first = wl.q_offset - wl.window + 1
+        assert ring >= wl.window + wl.q_len - 1
+        swa = (ring_of(x["k_loc"], ring, max(first, 0)), ring_of(x["v_loc"], ring, max(first, 0)),
+               x["gate"], wl.window)
+    o2, l2 = hs().sparse_attn_gather(qs, kp, vp, bi, bc, kind="block", block=wl.block, swa=swa,
+                                     out_dtype=torch.float32, want_lse=True, sink=s1,
+                                     sink_local=s2, local_ring=ring, pages=(table, wl.kv_len))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(l1, l2)
+
+
+def test_paged_decode_pipeline_matches_oracle():
+    """Paged full attention keeping the logits -> token selection from the logits -> a paged
+    sparse layer, against the oracle on the logical cache."""
+    wl = Workload("pipe", 2, 1, 6000, 32, 8, 128, "bf16", needles=8, seed=631)
+    x = make_inputs(wl, device="cuda", n_sparse=1)
+    kp, table = paged(x["k"], 64, 632)
+    vp, _ = paged(x["v"], 64, 632)
+    _, lse, lg = hs().full_attn_fwd_paged(x["q"], kp, vp, table, wl.kv_len, logits=True)
+    idx, cnt = hs().oracle_topk_from_logits(lg, lse, wl.n_kv_heads, wl.head_dim, wl.k_global,
+                                            wl.window)
+    o, _ = hs().sparse_attn_gather(x["q_sparse"][0], kp, vp, idx, cnt, kind="token",
+                                   out_dtype=torch.float32, pages=(table, wl.kv_len))
+    torch.cuda.synchronize()
+    qn, kn, vn = (to_numpy_f32(x[n]) for n in ("q", "k", "v"))
+    _, lse_ref = oracle.full_attention(qn, kn, vn)
+    oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
+    ex = check_token_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, qn, kn, lse_ref,
+                          wl.k_global, wl.window, wl.q_offset)
+    say(f"  near-tie differences excused: {ex}")
+    if ex == 0:
+        o_ref, _ = oracle.masked_attention(to_numpy_f32(x["q_sparse"][0]), kn, vn, oi, oc)
+        eo = max_abs(o.cpu().numpy(), o_ref)
+        say(f"  sparse layer max|dO| = {eo:.3e}")
+        assert eo <= TOL_BF16
