@@ -269,6 +269,7 @@ def main():
             out["prefill"]["full_attn_tflops"] / gemm, 4)
     if not args.no_block_prefill:
         out["block_prefill"] = block_prefill_leg(args)
+    out["mqa256_decode"] = mqa256_leg(args)
     if not args.no_sweep:
         out["sparse_decode_sweep"] = sparse_sweep(wl)
     if not args.no_cpu_baseline:
@@ -472,6 +473,52 @@ def measured_peaks():
     return {"copy_GB_per_s": round(2 * 4 * n / t_copy / 1e9, 1),
             "gemm_bf16_TFLOP_per_s": round(2 * m ** 3 / t_mm / 1e12, 1),
             "spec": {"hbm_GB_per_s": HBM_PEAK_GBS, "bf16_dense_TFLOP_per_s": 2500.0}}
+
+
+def mqa256_leg(args):
+    """HySparse2's own head shape (MQA, 64 query heads on one KV head, d 256) in decode, batch 8 at
+    32k context: full attention keeping its logits, token selection from them, 3 token-sparse
+    layers.  Full attention's GB/s counts K and V read once; the sparse layers' the gathered
+    rows."""
+    import torch
+
+    from oracle_top_kv_amd import costs, hs
+    from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["decode_mqa256_32k"]
+    x = make_inputs(wl, device=torch.device("cuda:0"))
+    q, k, v, qs = x["q"], x["k"], x["v"], x["q_sparse"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        m = (lambda i: e[i].record()) if e else (lambda i: None)
+        m(0)
+        _, lse, lg = hs.full_attn_fwd_logits(q, k, v)
+        m(1)
+        idx, cnt = hs.oracle_topk_from_logits(lg, lse, wl.n_kv_heads, wl.head_dim, wl.k_global,
+                                              wl.window)
+        m(2)
+        for l in range(wl.n_sparse):
+            hs.sparse_attn_gather(qs[l], k, v, idx, cnt, kind="token")
+        m(3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for s2 in range(args.steps):
+        step(ev[s2])
+    torch.cuda.synchronize()
+    t = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / args.steps for i in range(3)]
+    b_fa = costs.full_attn_kv_bytes(wl)
+    b_sp = costs.token_gather_bytes(wl)
+    del x, q, k, v, qs
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "ms_per_step": round(sum(t), 4),
+            "full_attn_ms": round(t[0], 4),
+            "full_attn_GB_per_s": round(b_fa / (t[0] * 1e-3) / 1e9, 1),
+            "full_attn_hbm_frac": round(b_fa / (t[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+            "token_select_ms": round(t[1], 4), "sparse_layers_ms": round(t[2], 4),
+            "sparse_GB_per_s": round(wl.n_sparse * b_sp / (t[2] * 1e-3) / 1e9, 1)}
 
 
 def block_prefill_leg(args):

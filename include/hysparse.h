@@ -28,10 +28,14 @@
  *     them [P2 engineering constraint 6: producer/consumer lifetime].
  *   - Workspace: every call takes a caller-owned device scratch buffer of at least
  *     hs_workspace_size(...) bytes (16-byte aligned); a smaller one returns HS_ERR_WORKSPACE.
- *   - Supported: head_dim in {64, 128}; g = Hq/Hkv integral and at most 16; kv_len <= 2^30;
- *     in_dtype bf16 or fp32; out_dtype bf16 or fp32.  Index-set selection (hs_oracle_topk,
- *     hs_block_score_topk) needs g in {4, 8, 16}; block selection needs block a multiple of 16
- *     and 1 <= n_blocks <= 64.  Anything else returns HS_ERR_UNSUPPORTED.
+ *   - Supported: head_dim in {64, 128} (fp32 or bf16 inputs) or 256 (bf16; the HySparse2 head
+ *     shape, MQA with 64 query heads of d 256 [P1 section 6.1]); g = Hq/Hkv integral and at
+ *     most 16, or 32, 48, 64 (run as chunks of 16 heads); kv_len <= 2^30; out_dtype bf16 or
+ *     fp32.  Index-set selection from Q and K (hs_oracle_topk, hs_block_score_topk) needs g in
+ *     {4, 8, 16} and head_dim <= 128; selection from stored logits takes every supported shape;
+ *     block selection needs block a multiple of 16 and 1 <= n_blocks <= 64.  head_dim 256 runs
+ *     on the decode-shaped kernels only (any q_len; the gated sparse layer as two branches plus
+ *     a combine).  Anything else returns HS_ERR_UNSUPPORTED.
  *   - Workspace sizes, for orientation: token selection with many query rows per KV head and
  *     k_global <= 1024 keeps a 16 KiB candidate buffer per (b, t, u); with few rows it keeps
  *     12 bytes per candidate key per (b, t, u) plus small histograms; split attention keeps

@@ -45,8 +45,8 @@ hs_status check_desc(const hs_attn_desc* d, Shape* s) {
   if (d->n_q_heads % d->n_kv_heads)
     return fail(HS_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
                 d->n_q_heads, d->n_kv_heads);
-  if (d->head_dim != 64 && d->head_dim != 128)
-    return fail(HS_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+    return fail(HS_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128 or 256)", d->head_dim);
   if ((d->in_dtype != HS_BF16 && d->in_dtype != HS_F32) ||
       (d->out_dtype != HS_BF16 && d->out_dtype != HS_F32))
     return fail(HS_ERR_INVALID_ARG, "unknown dtype");
@@ -55,8 +55,9 @@ hs_status check_desc(const hs_attn_desc* d, Shape* s) {
     return fail(HS_ERR_INVALID_ARG, "q_offset %lld with q_len %d does not fit kv_len %d", q_off,
                 d->q_len, d->kv_len);
   const int g = d->n_q_heads / d->n_kv_heads;
-  if (g > 16)
-    return fail(HS_ERR_UNSUPPORTED, "GQA group of %d query heads per KV head (at most 16)", g);
+  if (g > 64 || (g > 16 && g % 16))
+    return fail(HS_ERR_UNSUPPORTED,
+                "GQA group of %d query heads per KV head (at most 16, or 32, 48, 64)", g);
   // 32-bit position arithmetic inside the kernels
   if ((long long)d->kv_len > (1LL << 30))
     return fail(HS_ERR_UNSUPPORTED, "kv_len %d too large", d->kv_len);
@@ -83,12 +84,16 @@ struct RaGeom {
 
 // Splits of each row-set's key list: enough workgroups to fill the GPU (`target`), no split
 // shorter than `min_steps` 32-key steps, none longer than `max_steps`.
+// Heads per row-set and head chunks per query: groups of more than 16 heads run as chunks of 16.
+int heads_per_set(const Shape& s) { return s.g < 16 ? s.g : 16; }
+int chunks_per_query(const Shape& s) { return s.g / heads_per_set(s); }
+
 RaGeom ra_geom(const Shape& s, bool per_query, long long max_keys, int min_steps_per_split,
                long long target = kTargetWorkgroups, long long max_steps = 1LL << 40) {
   RaGeom g;
-  g.q_per_set = per_query ? 1 : (16 / s.g > 0 ? 16 / s.g : 1);
+  g.q_per_set = per_query ? 1 : 16 / heads_per_set(s);
   g.sets_per_bu = (s.Tq + g.q_per_set - 1) / g.q_per_set;
-  g.n_sets = s.B * s.Hkv * g.sets_per_bu;
+  g.n_sets = s.B * s.Hkv * g.sets_per_bu * chunks_per_query(s);
   const long long steps = (max_keys + kStepKeys - 1) / kStepKeys;
   long long want = (target + g.n_sets - 1) / g.n_sets;
   long long most = (steps + min_steps_per_split - 1) / min_steps_per_split;
@@ -127,6 +132,8 @@ hs::RowAttnParams ra_params(const Shape& s, const RaGeom& g) {
   p.Hq = s.Hq;
   p.Hkv = s.Hkv;
   p.g = s.g;
+  p.hpc = heads_per_set(s);
+  p.cpq = chunks_per_query(s);
   p.q_off = s.q_off;
   p.q_per_set = g.q_per_set;
   p.sets_per_bu = g.sets_per_bu;
@@ -145,6 +152,8 @@ hs::CombineParams combine_params(const Shape& s, const RaGeom& g, void* o, float
   c.Hq = s.Hq;
   c.Hkv = s.Hkv;
   c.g = s.g;
+  c.hpc = heads_per_set(s);
+  c.cpq = chunks_per_query(s);
   c.q_per_set = g.q_per_set;
   c.sets_per_bu = g.sets_per_bu;
   c.o = o;
@@ -162,8 +171,17 @@ hs_status hip_status(hipError_t e, const char* what) {
 constexpr long long kResidentWorkgroups = 512;  // 256 CUs x 2 workgroups of this kernel
 
 // Many queries per KV head (bf16): the LDS-tiled prefill kernel; otherwise the row kernel.
+// (A group of more than 16 heads needs at least 128 rows per KV head to fill half a workgroup;
+// with fewer, the row kernel's key splits do better.)
 bool use_prefill_kernel(const Shape& s) {
-  return !s.in_f32 && (long long)s.Tq * s.g > 16 && 256 % s.g == 0;
+  const long long rows = (long long)s.Tq * s.g;
+  return !s.in_f32 && s.D <= 128 && rows > 16 && (s.g <= 16 || rows >= 128) && 256 % s.g == 0;
+}
+
+// Kernels that read Q, K, V take head_dim 256 with bf16 inputs only.
+hs_status check_qkv_dtype(const Shape& s) {
+  if (s.D == 256 && s.in_f32) return fail(HS_ERR_UNSUPPORTED, "head_dim 256 needs bf16 inputs");
+  return HS_OK;
 }
 
 size_t full_attn_ws(const Shape& s) {
@@ -341,6 +359,9 @@ hs_status bk_check(const Shape& s, int block, int n_blocks, BkGeom* g, bool per_
   if (n_blocks < 1 || n_blocks > 64) return fail(HS_ERR_UNSUPPORTED, "n_blocks %d: must be 1..64", n_blocks);
   if (!per_row && s.g != 4 && s.g != 8 && s.g != 16)
     return fail(HS_ERR_UNSUPPORTED, "block selection needs a GQA group of 4, 8 or 16 (got %d)", s.g);
+  if (!per_row && s.D > 128)
+    return fail(HS_ERR_UNSUPPORTED, "block selection from Q and K takes head_dim 64 or 128; "
+                "use the stored-logits path");
   *g = bk_geom(s, block, n_blocks, per_row);
   if ((long long)g->n_split * n_blocks > 4096)
     return fail(HS_ERR_UNSUPPORTED, "context too long for the block merge (%d splits)", g->n_split);
@@ -373,13 +394,14 @@ SparseGeom sparse_geom(const Shape& s, long long keys_per_set, int window) {
   // (1152 keys per set): 5.3 TB/s at 1024 sets against 3.9 TB/s split; below about 96 sets the
   // work is latency-bound and the split version is slightly faster.
   const long long n_sets = (long long)g.glob.n_sets;
-  g.wide = !s.in_f32 && g.glob.n_split > 1 && keys_per_set <= 64LL * kStepKeys && n_sets >= 96;
+  g.wide = !s.in_f32 && s.D <= 128 && g.glob.n_split > 1 && keys_per_set <= 64LL * kStepKeys &&
+           n_sets >= 96;
   if (g.wide) {
     g.glob.steps_per_split = (int)((keys_per_set + kStepKeys - 1) / kStepKeys);
     g.glob.n_split = 1;
   }
   g.loc = ra_geom(s, true, window > 0 ? window : 1, 4);
-  g.fused = window > 0 && g.glob.n_split == 1 && g.loc.n_split == 1;
+  g.fused = window > 0 && s.D <= 128 && g.glob.n_split == 1 && g.loc.n_split == 1;
   g.combine = !g.fused && (window > 0 || g.glob.n_split > 1);
   return g;
 }
@@ -482,7 +504,8 @@ hs::PrefillParams prefill_params(const Shape& s, const void* q, const void* k, c
 // Block selection inside the prefill attention pass: blocks of one 64-key tile, at most 16
 // blocks per list.
 bool fused_blocks(const Shape& s, int block, int n_blocks) {
-  return use_prefill_kernel(s) && block == 64 && n_blocks >= 1 && n_blocks <= 16;
+  return use_prefill_kernel(s) && 32 % s.g == 0 && block == 64 && n_blocks >= 1 &&
+         n_blocks <= 16;
 }
 
 // Workspace of hs_full_attn_block_topk: none when fused, else what the larger of its two
@@ -546,7 +569,7 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
   switch (op) {
     case HS_OP_FULL_ATTN: return full_attn_ws(s);
     case HS_OP_ORACLE_TOPK: {
-      if (s.g != 4 && s.g != 8 && s.g != 16) return 0;
+      if ((s.g != 4 && s.g != 8 && s.g != 16) || s.D > 128) return 0;
       if (use_prefill_select(s, p0)) return tk_prefill_ws(s);
       return tk_ws(s, tk_geom(s));
     }
@@ -586,6 +609,8 @@ hs_status hs_full_attn_fwd(const hs_attn_desc* desc, const void* q, const void* 
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
+  st = check_qkv_dtype(s);
+  if (st != HS_OK) return st;
   if (!q || !k || !v || !o || !lse) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
   if (use_prefill_kernel(s)) {
     const hs::PrefillParams pp = prefill_params(s, q, k, v, o, lse);
@@ -600,6 +625,8 @@ hs_status hs_full_attn_block_topk(const hs_attn_desc* desc, const void* q, const
                                   size_t ws_bytes, void* stream) {
   Shape s;
   hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  st = check_qkv_dtype(s);
   if (st != HS_OK) return st;
   if (!q || !k || !v || !o || !lse || !blk_idx || !count)
     return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
@@ -630,6 +657,8 @@ hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
+  st = check_qkv_dtype(s);
+  if (st != HS_OK) return st;
   if (!q || !k || !v || !o || !lse || !logits) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
   if ((uintptr_t)logits % 4) return fail(HS_ERR_INVALID_ARG, "logits must be 4-byte aligned");
   return row_full_attn(s, q, k, v, o, lse, logits, ws, ws_bytes, stream);
@@ -640,6 +669,8 @@ hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const 
                                  float* logits, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  st = check_qkv_dtype(s);
   if (st != HS_OK) return st;
   if (!q || !k_pool || !v_pool || !o || !lse) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
   st = check_pages(s, pages);
@@ -698,6 +729,9 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
   if ((long long)k_global + window < 1) return fail(HS_ERR_INVALID_ARG, "k_global + window must be >= 1");
   if (s.g != 4 && s.g != 8 && s.g != 16)
     return fail(HS_ERR_UNSUPPORTED, "token selection needs a GQA group of 4, 8 or 16 (got %d)", s.g);
+  if (s.D > 128)
+    return fail(HS_ERR_UNSUPPORTED, "token selection from Q and K takes head_dim 64 or 128; "
+                "use the stored-logits path");
   if (use_prefill_select(s, k_global)) {
     const size_t need = tk_prefill_ws(s);
     if (!ws || ws_bytes < need)
@@ -784,6 +818,8 @@ hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, c
   const int ring = opts ? opts->local_ring : 0;
   Shape s;
   hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  st = check_qkv_dtype(s);
   if (st != HS_OK) return st;
   if (pages) {
     st = check_pages(s, pages);

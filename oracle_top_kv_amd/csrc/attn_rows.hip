@@ -105,8 +105,8 @@ struct PassOut {
 template <int D, bool F32, int SRC, int NW, bool LOGITS = false, bool PAGED = false>
 __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* kmat,
                                             const void* vmat, int split, int steps_per_split,
-                                            int b, int u, int j0, int nq, unsigned char* smem,
-                                            int* pos_all, int* row_all,
+                                            int b, int u, int hc, int j0, int nq,
+                                            unsigned char* smem, int* pos_all, int* row_all,
                                             PassOut<RaCfg<D, F32, NW>::kCPT>& out) {
   using Cfg = RaCfg<D, F32, NW>;
   constexpr int kWaves = NW;
@@ -114,7 +114,7 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   const int wave = threadIdx.x >> 6;
   const int rn = lane & 15;   // MFMA row / column index of this lane
   const int jg = lane >> 4;   // lane group 0..3
-  const int nrows = nq * p.g;
+  const int nrows = nq * p.hpc;  // a set: nq queries x the hpc heads of head chunk hc
   const long long t_first = p.q_off + j0;
   const long long t_last = p.q_off + j0 + nq - 1;
 
@@ -134,8 +134,8 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
 
   // this lane's row (for Q, masks and statistics)
   const bool row_ok = rn < nrows;
-  const int jq = row_ok ? rn / p.g : 0;
-  const int hh = row_ok ? rn % p.g : 0;
+  const int jq = row_ok ? rn / p.hpc : 0;
+  const int hh = hc * p.hpc + (row_ok ? rn % p.hpc : 0);
   const long long t_row = p.q_off + j0 + jq;
   const int h = u * p.g + hh;
   const long long lo_row = (SRC == SRC_WINDOW) ? t_row - p.window + 1 : 0;
@@ -191,7 +191,8 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
     for (int c = lane; c < chunks; c += 64) {
       const int r = c / (n * 8), li = (c / 8) % n, qd = c % 8;
       const int e0 = (l_base + li * kWaves) * kStep + 4 * qd;  // range mode: entry = position
-      float* dst = p.logits + (((size_t)b * p.Tq + (j0 + r / p.g)) * p.Hq + u * p.g + r % p.g) *
+      float* dst = p.logits + (((size_t)b * p.Tq + (j0 + r / p.hpc)) * p.Hq + u * p.g +
+                                hc * p.hpc + r % p.hpc) *
                                   (size_t)p.Tk + e0;
       const f32x4 val = *(const f32x4*)(lbuf + r * kLogitRow + li * kStep + 4 * qd);
       if (p.logits_vec && e0 + 3 < L) {
@@ -517,33 +518,37 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
   // workgroups reading the same positions of the Hkv interleaved heads run together (whole
   // [Hkv, d] rows of K and V are then consumed close in time).
-  const int u = blockIdx.x % p.Hkv;
-  const int split = (blockIdx.x / p.Hkv) % p.n_split;
-  const int bq = blockIdx.x / (p.Hkv * p.n_split);
+  // Head chunks (groups of more than 16 heads: 16 heads per set) vary fastest of all, so that
+  // the sets reading the same key list run together.
+  const int hc = blockIdx.x % p.cpq;
+  const int x = blockIdx.x / p.cpq;
+  const int u = x % p.Hkv;
+  const int split = (x / p.Hkv) % p.n_split;
+  const int bq = x / (p.Hkv * p.n_split);
   const int sq = bq % p.sets_per_bu;
   const int b = bq / p.sets_per_bu;
-  const int set = (b * p.Hkv + u) * p.sets_per_bu + sq;
+  const int set = ((b * p.Hkv + u) * p.sets_per_bu + sq) * p.cpq + hc;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);
-  const int nrows = nq * p.g;
+  const int nrows = nq * p.hpc;
 
   constexpr int CPT = Cfg::kCPT;  // columns per merge thread
   PassOut<CPT> a;
-  attend_pass<D, F32, SRC, NW, LOGITS, PAGED>(p, p.k, p.v, split, p.steps_per_split, b, u, j0,
-                                              nq, smem, pos_all, row_all, a);
+  attend_pass<D, F32, SRC, NW, LOGITS, PAGED>(p, p.k, p.v, split, p.steps_per_split, b, u, hc,
+                                              j0, nq, smem, pos_all, row_all, a);
 
   const int r = threadIdx.x / Cfg::kTPR;
   const int c0 = (threadIdx.x % Cfg::kTPR) * CPT;
-  const int jr = j0 + r / p.g;
-  const int hr = u * p.g + r % p.g;
+  const int jr = j0 + r / p.hpc;
+  const int hr = u * p.g + hc * p.hpc + r % p.hpc;
   const size_t ooff = (((size_t)b * p.Tq + jr) * p.Hq + hr) * D + c0;
   float res[CPT];
   float lse_row = -INFINITY;
   if constexpr (GATED) {
     __syncthreads();  // merge buffers are reused by the window pass
     PassOut<CPT> w;
-    attend_pass<D, F32, SRC_WINDOW, NW>(p, p.k2, p.v2, 0, 1 << 30, b, u, j0, nq, smem, pos_all,
-                                        row_all, w);
+    attend_pass<D, F32, SRC_WINDOW, NW>(p, p.k2, p.v2, 0, 1 << 30, b, u, hc, j0, nq, smem,
+                                        pos_all, row_all, w);
     if (r >= nrows) return;
     const float* z = p.gate + (((size_t)b * p.Tq + jr) * p.Hq + hr) * 2;
     const double og = out_gate_of(p.out_gate, ((size_t)b * p.Tq + jr) * p.Hq + hr);
@@ -557,7 +562,7 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   } else {
     if (r >= nrows) return;
     if (!p.final_direct) {
-      const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu;
+      const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu * p.cpq;
       const size_t prow = ((size_t)split * n_sets + set) * 16 + r;
       if (c0 == 0) {
         p.part_m[prow] = a.M;
@@ -598,15 +603,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int set = blockIdx.x / 16;
   const int r = blockIdx.x % 16;
   const size_t n_sets = gridDim.x / 16;
-  const int sq = set % p.sets_per_bu;
-  const int bu = set / p.sets_per_bu;
+  const int hc = set % p.cpq;
+  const int sq = (set / p.cpq) % p.sets_per_bu;
+  const int bu = set / (p.cpq * p.sets_per_bu);
   const int u = bu % p.Hkv;
   const int b = bu / p.Hkv;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);
-  if (r >= nq * p.g) return;  // whole workgroup leaves together
-  const int jr = j0 + r / p.g;
-  const int hr = u * p.g + r % p.g;
+  if (r >= nq * p.hpc) return;  // whole workgroup leaves together
+  const int jr = j0 + r / p.hpc;
+  const int hr = u * p.g + hc * p.hpc + r % p.hpc;
   const int c = threadIdx.x % NC;
   const int sl = threadIdx.x / NC;
 
@@ -668,7 +674,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 
 template <int D, bool F32, int NW>
 hipError_t launch_ra_paged(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
-  const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu);
+  const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu * p.cpq);
   const int threads = 64 * NW;
   if (gated) {
     if (src == SRC_TOKEN)
@@ -699,7 +705,7 @@ hipError_t launch_ra_paged(const RowAttnParams& p, KeySrc src, bool gated, hipSt
 template <int D, bool F32, int NW>
 hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
   if (p.pages) return launch_ra_paged<D, F32, NW>(p, src, gated, stream);
-  const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu);
+  const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu * p.cpq);
   const int threads = 64 * NW;
   if (p.logits) {
     if constexpr (NW == 4) {
@@ -734,6 +740,10 @@ hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, Ke
     return head_dim == 128 ? launch_ra<128, false, 8>(p, src, gated, stream)
                            : launch_ra<64, false, 8>(p, src, gated, stream);
   }
+  if (head_dim == 256) {  // bf16, 4 waves, one branch per launch (registers allow no more)
+    if (in_f32 || gated) return hipErrorInvalidValue;
+    return launch_ra<256, false, 4>(p, src, false, stream);
+  }
   if (head_dim == 128)
     return in_f32 ? launch_ra<128, true, 4>(p, src, gated, stream)
                   : launch_ra<128, false, 4>(p, src, gated, stream);
@@ -742,8 +752,10 @@ hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, Ke
 }
 
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.B * p.Hkv * p.sets_per_bu * 16);
-  if (head_dim == 128)
+  const dim3 grid(p.B * p.Hkv * p.sets_per_bu * p.cpq * 16);
+  if (head_dim == 256)
+    combine_kernel<256><<<grid, 256, 0, stream>>>(p);
+  else if (head_dim == 128)
     combine_kernel<128><<<grid, 256, 0, stream>>>(p);
   else
     combine_kernel<64><<<grid, 256, 0, stream>>>(p);

@@ -161,7 +161,7 @@ template <int G>
 __global__ __launch_bounds__(256) void blk_logit_score_kernel(BlockTopkParams p) {
   __shared__ unsigned long long bkey[kMaxRange];
   __shared__ uint32_t bmax[kMaxRange];
-  __shared__ float dsh[16];
+  __shared__ float dsh[64];
   const int split = blockIdx.x % p.n_split;
   const int row = blockIdx.x / p.n_split;  // (b * Tq + j) * Hkv + u
   const int u = row % p.Hkv;
@@ -292,6 +292,9 @@ hipError_t launch_block_from_logits(const BlockTopkParams& p, hipStream_t stream
     case 14: return launch_blk_logits<14>(p, stream);
     case 15: return launch_blk_logits<15>(p, stream);
     case 16: return launch_blk_logits<16>(p, stream);
+    case 32: return launch_blk_logits<32>(p, stream);
+    case 48: return launch_blk_logits<48>(p, stream);
+    case 64: return launch_blk_logits<64>(p, stream);
   }
   return hipErrorInvalidValue;
 }

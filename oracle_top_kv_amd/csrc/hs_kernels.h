@@ -24,6 +24,7 @@ struct RowAttnParams {
   int idx_cap, block;
   int window;  // window mode: each row sees positions t-window+1 .. t
   int B, Tq, Tk, Hq, Hkv, g;
+  int hpc, cpq;     // heads per row-set (min(g, 16)) and head chunks per query (g / hpc)
   long long q_off;
   int q_per_set;    // queries per row-set (range mode may pack several; list modes: 1)
   int sets_per_bu;  // row-sets per (b, u) = ceil(Tq / q_per_set)
@@ -67,6 +68,7 @@ struct CombineParams {
   int n_branch;
   const float* gate;  // [B, Tq, Hq, 2] (two branches)
   int B, Tq, Hq, Hkv, g;
+  int hpc, cpq;
   int q_per_set, sets_per_bu;
   void* o;
   float* lse;  // nullable; LSE of branch 0

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void tk_score_kernel(TopkDecodeParams p) {
 template <int G>
 __global__ __launch_bounds__(256) void tk_logit_score_kernel(TopkDecodeParams p) {
   __shared__ uint32_t hist[kBins];
-  __shared__ float dsh[16];
+  __shared__ float dsh[64];
   const int split = blockIdx.x % p.n_split;
   const int row = blockIdx.x / p.n_split;  // (b * Tq + j) * Hkv + u
   const int u = row % p.Hkv;
@@ -454,6 +454,9 @@ hipError_t launch_topk_from_logits(const TopkDecodeParams& p, hipStream_t stream
     case 14: return launch_tk_logits<14>(p, stream);
     case 15: return launch_tk_logits<15>(p, stream);
     case 16: return launch_tk_logits<16>(p, stream);
+    case 32: return launch_tk_logits<32>(p, stream);
+    case 48: return launch_tk_logits<48>(p, stream);
+    case 64: return launch_tk_logits<64>(p, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -78,6 +78,10 @@ WORKLOADS: Dict[str, Workload] = {
     # HySparse block variant at 64k, gated sliding-window branch with its own K'/V'
     "block_7b_64k": Workload("block_7b_64k", 4, 65536, 65536, 32, 8, 128, "bf16",
                              n_sparse=1, seed=505),
+    # HySparse2's own attention shape (MQA: 64 query heads on one KV head, d 256) in decode at
+    # 32k context, 16 needles, 1 full + 3 sparse layers
+    "decode_mqa256_32k": Workload("decode_mqa256_32k", 8, 1, 32768, 64, 1, 256, "bf16",
+                                  n_sparse=3, needles=16, needle_logit=8.0, seed=606),
 }
 
 

@@ -42,7 +42,9 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
     (dict(q_len=0), hs.HS_ERR_INVALID_ARG),
     (dict(q_offset=1024), hs.HS_ERR_INVALID_ARG),
     (dict(q_len=4, q_offset=1021), hs.HS_ERR_INVALID_ARG),
-    (dict(n_q_heads=64, n_kv_heads=1), hs.HS_ERR_UNSUPPORTED),
+    (dict(n_q_heads=40, n_kv_heads=2), hs.HS_ERR_UNSUPPORTED),   # g = 20: not a multiple of 16
+    (dict(n_q_heads=128, n_kv_heads=1), hs.HS_ERR_UNSUPPORTED),  # g = 128
+    (dict(head_dim=256, in_dtype=hs.HS_F32), hs.HS_ERR_UNSUPPORTED),
     (dict(in_dtype=7), hs.HS_ERR_INVALID_ARG),
 ])
 def test_full_attn_rejects_bad_descriptions(kw, status):
