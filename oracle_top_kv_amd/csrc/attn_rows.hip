@@ -29,6 +29,7 @@ namespace hs {
 namespace {
 
 constexpr int kStep = 32;  // keys per wave step
+constexpr int kXcds = 8;   // accelerator complex dies of MI355X (workgroups go round-robin)
 constexpr int kMaxListEntries = 2048;  // list-mode entries staged per workgroup (64 steps)
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -518,10 +519,22 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
   // workgroups reading the same positions of the Hkv interleaved heads run together (whole
   // [Hkv, d] rows of K and V are then consumed close in time).
-  // Head chunks (groups of more than 16 heads: 16 heads per set) vary fastest of all, so that
-  // the sets reading the same key list run together.
-  const int hc = blockIdx.x % p.cpq;
-  const int x = blockIdx.x / p.cpq;
+  // Head chunks (groups of more than 16 heads: 16 heads per set) of one key range read the
+  // same K and V rows: they are placed on the same XCD (consecutive workgroup ids go round-robin
+  // over the 8 XCDs, each with its own L2), so that the rows come from HBM once.
+  int hc = 0, x = blockIdx.x;
+  if (p.cpq > 1) {
+    const int n8 = kXcds * p.cpq;
+    const int full = (int)(gridDim.x / n8) * n8;
+    if ((int)blockIdx.x < full) {
+      const int grp = blockIdx.x / n8, within = blockIdx.x % n8;
+      hc = within / kXcds;
+      x = grp * kXcds + within % kXcds;
+    } else {
+      hc = (blockIdx.x - full) % p.cpq;
+      x = full / p.cpq + (blockIdx.x - full) / p.cpq;
+    }
+  }
   const int u = x % p.Hkv;
   const int split = (x / p.Hkv) % p.n_split;
   const int bq = x / (p.Hkv * p.n_split);
