@@ -41,6 +41,8 @@ def parse():
                     help="skip the 80B-shaped prefill leg (full attention + token top-k)")
     ap.add_argument("--no-block-prefill", action="store_true",
                     help="skip the 64k block-selection prefill leg (HySparse scoring pass)")
+    ap.add_argument("--no-long-decode", action="store_true",
+                    help="skip the 2^20-context decode leg (80B shape)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the token-sparse decode layer sweep over batch sizes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -270,6 +272,8 @@ def main():
     if not args.no_block_prefill:
         out["block_prefill"] = block_prefill_leg(args)
     out["mqa256_decode"] = mqa256_leg(args)
+    if not args.no_long_decode:
+        out["long_decode"] = long_decode_leg(args, cpu=not args.no_cpu_baseline)
     if not args.no_sweep:
         out["sparse_decode_sweep"] = sparse_sweep(wl)
     if not args.no_cpu_baseline:
@@ -473,6 +477,69 @@ def measured_peaks():
     return {"copy_GB_per_s": round(2 * 4 * n / t_copy / 1e9, 1),
             "gemm_bf16_TFLOP_per_s": round(2 * m ** 3 / t_mm / 1e12, 1),
             "spec": {"hbm_GB_per_s": HBM_PEAK_GBS, "bf16_dense_TFLOP_per_s": 2500.0}}
+
+
+def long_decode_leg(args, cpu=True):
+    """The 80B shape in decode at 2^20 context (batch 4, 64/4 heads, d 128, 16 clusters of 16
+    needles per KV head): full attention (K + V once: 8.59 GB), token top-k recomputed from Q and
+    K, and the 11 token-sparse layers (9.44 MB gathered each); with `cpu`, the oracle's time for
+    batch entry 0 (full attention + token top-k), scaled to the batch."""
+    import torch
+
+    from oracle_top_kv_amd import costs, hs
+    from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs, to_numpy_f32
+
+    wl = WORKLOADS["decode_80b_1m"]
+    x = make_inputs(wl, device=torch.device("cuda:0"), n_sparse=1)
+    q, k, v, qs = x["q"], x["k"], x["v"], x["q_sparse"][0]
+    reps = 5
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+
+    def step(e=None):
+        m = (lambda i: e[i].record()) if e else (lambda i: None)
+        m(0)
+        _, lse = hs.full_attn_fwd(q, k, v)
+        m(1)
+        idx, cnt = hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+        m(2)
+        for _ in range(wl.n_sparse):  # the layers' own Q' differ only in values
+            hs.sparse_attn_gather(qs, k, v, idx, cnt, kind="token")
+        m(3)
+
+    step()
+    torch.cuda.synchronize()
+    for r in range(reps):
+        step(ev[r])
+    torch.cuda.synchronize()
+    t = [sorted(e[i].elapsed_time(e[i + 1]) for e in ev)[reps // 2] for i in range(3)]
+    b_fa, b_sc, b_sp = costs.full_attn_kv_bytes(wl), costs.score_k_bytes(wl), costs.token_gather_bytes(wl)
+    out = {"workload": wl.name, "ms_per_step": round(sum(t), 4), "full_attn_ms": round(t[0], 4),
+           "full_attn_GB_per_s": round(b_fa / (t[0] * 1e-3) / 1e9, 1),
+           "full_attn_hbm_frac": round(b_fa / (t[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+           "token_topk_ms": round(t[1], 4),
+           "token_topk_GB_per_s": round(b_sc / (t[1] * 1e-3) / 1e9, 1),
+           "sparse_layers_ms": round(t[2], 4),
+           "sparse_per_layer_us": round(t[2] / wl.n_sparse * 1e3, 2),
+           "sparse_GB_per_s": round(wl.n_sparse * b_sp / (t[2] * 1e-3) / 1e9, 1),
+           "timing": "median of 5"}
+    if cpu:
+        import oracle
+        qn, kn, vn = (to_numpy_f32(x[n][0:1]) for n in ("q", "k", "v"))
+        del x, q, k, v, qs
+        torch.cuda.empty_cache()
+        t0 = time.perf_counter()
+        _, lse = oracle.full_attention(qn, kn, vn)
+        oracle.token_topk(qn, kn, lse, wl.k_global, wl.window)
+        tc = time.perf_counter() - t0
+        out["cpu_oracle"] = {"kind": "oracle", "cores": oracle.threads(),
+                             "sample": f"batch entry 0 of {wl.batch}, full attention + token "
+                                       f"top-k, {tc:.1f} s",
+                             "extrapolated_s": round(tc * wl.batch, 1),
+                             "gpu_s": round((t[0] + t[1]) * 1e-3, 5)}
+    else:
+        del x, q, k, v, qs
+        torch.cuda.empty_cache()
+    return out
 
 
 def mqa256_leg(args):
