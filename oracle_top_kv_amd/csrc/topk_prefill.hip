@@ -37,6 +37,9 @@ constexpr int kRowsWG = 256;
 constexpr int kBN = 64;
 constexpr int kBufCap = 2048;          // token candidates per query
 constexpr int kNPL = kBufCap / 64;     // buffer entries per lane during a compaction
+// Entries a compaction before the end may keep beyond k (the rest of the k-th entry's bin);
+// k + slack must leave room for a tile's appends (at most 64 per query).
+constexpr int kCompactSlack = 256;
 constexpr int kSortCap = 1024;         // largest k_global of the token mode
 constexpr int kMaxBlocks = 64;         // largest n_blocks
 
@@ -108,7 +111,8 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
 // (entries >= theta are the ones kept, compacted to buf[0..k)).  Wave-wide.  If `sorted_pos`
 // is given, the kept positions (~low word) are also written there, unordered.
 __device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k, int lane,
-                                           uint32_t* hist, int* kept_pos) {
+                                           uint32_t* hist, int* kept_pos, int slack,
+                                           int* kept_out) {
   unsigned long long v[kNPL];
 #pragma unroll
   for (int i = 0; i < kNPL; i++) {
@@ -152,6 +156,9 @@ __device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k
     kk = kr;
     wave_sync_lds();
     if (cnt == (uint32_t)kr) break;  // the bin is taken whole: V >= prefix selects exactly k
+    // A running threshold only has to stay at or below the k-th value: keeping the whole bin
+    // of the k-th entry (at most `slack` entries beyond k) ends the select after one pass.
+    if (slack > 0 && (int)cnt - kr <= slack) break;
   }
   const unsigned long long theta = prefix;
   int base = 0;
@@ -168,6 +175,7 @@ __device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k
     base += __popcll(bm);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // stores complete before reloads
+  *kept_out = base;
   return theta;
 }
 
@@ -358,10 +366,12 @@ __global__ __launch_bounds__(kThreads, F32 ? 1 : 2) void pf_select_kernel(Prefil
           for (int jj = 0; jj < 4; jj++) {
             const int n = __shfl(cnt[qg], 16 * jj, 64);
             if (n > kBufCap - kBN) {
-              const unsigned long long tnew =
-                  wave_compact(buf_of(4 * qg + jj), n, p.k_global, lane, whist[wave], nullptr);
+              int kept;
+              const unsigned long long tnew = wave_compact(buf_of(4 * qg + jj), n, p.k_global,
+                                                           lane, whist[wave], nullptr,
+                                                           kCompactSlack, &kept);
               if (jg == jj) {
-                cnt[qg] = p.k_global;
+                cnt[qg] = kept;
                 th[qg] = tnew;
                 const uint32_t hi = (uint32_t)(tnew >> 32);
                 thf[qg] = hi ? key_to_float(hi) : -INFINITY;
@@ -481,7 +491,8 @@ __global__ __launch_bounds__(kThreads, F32 ? 1 : 2) void pf_select_kernel(Prefil
         const int n = __shfl(cnt[qg], 16 * jj, 64);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // appends complete before reloads
         if (n > k_eff) {
-          wave_compact(bufq, n, k_eff, lane, whist[wave], sb);
+          int kept_final;
+          wave_compact(bufq, n, k_eff, lane, whist[wave], sb, 0, &kept_final);
         } else {
           for (int i = lane; i < n; i += 64)
             sb[i] = (int)(0xFFFFFFFFu - (uint32_t)(ld_coherent(bufq + i) & 0xFFFFFFFFull));
