@@ -35,6 +35,9 @@ namespace {
 constexpr int kRowsWG = 256;
 constexpr int kThreads = 512;
 constexpr int kBN = 64;
+constexpr float kLazy = 8.f;  // see the lazy rescale in the tile step
+constexpr int kBufferConfig = 0x00020000;  // buffer descriptor word 3 (gfx9 family: raw dwords)
+constexpr int kNonTemporal = 2;            // cache-policy bit of a buffer load: non-temporal
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -51,7 +54,9 @@ __device__ __forceinline__ float max_halves(float v) {
 template <int D>
 struct PfCfg {
   static constexpr int KStr = D + 8;    // K tile row stride (elements): conflict-free ds_read_b128
-  static constexpr int VStr = D + 16;   // V tile row stride: conflict-free transpose reads
+  // V tile row stride: a transpose read covers 4 rows x 2 column groups per 32 lanes; rows 16
+  // dwords apart (mod 64 banks) make it conflict-free
+  static constexpr int VStr = D + 32;
   static constexpr int KK = D / 16;     // MFMA steps over d
   static constexpr int DB = D / 32;     // 32-wide d blocks of O
   static constexpr int CPR = D / 8;     // 16-byte chunks per row
@@ -206,24 +211,71 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   const uint16_t* vbase = (const uint16_t*)p.v + ((size_t)b * p.Tk * p.Hkv + u) * D;
   const int n_tiles = (t_max + kBN) / kBN;  // tiles covering keys 0..t_max
 
-  u32x4 kreg[C::LPT], vreg[C::LPT];
-  auto load_tile = [&](int t) {
+  // K tiles run one tile ahead of V tiles: the step of tile t takes the softmax of S(t), computed
+  // in the previous step, while S(t+1) = K(t+1) Q^T runs on the matrix cores, then O += V(t) P(t).
+  // K(t) lives in K buffer t & 1 and V(t) in V buffer t & 1.  The step of tile t stores K(t+2)
+  // into K(t)'s buffer (last read by the previous step) and V(t+1) into V(t-1)'s buffer; the
+  // barrier ending the step publishes both.  Loads past the last tile read clamped rows, and the
+  // last step's S(t+1) is never used, so a step has no branch around its loads or MFMAs.
+  // Tile loads are raw buffer loads: the descriptor (scalar registers) holds the tile's first
+  // row and its number of valid rows (through t_max); rows past them read as zeros without a
+  // memory access (the causal mask covers them), so a thread's byte offset inside a tile is a
+  // constant and the loop does no address arithmetic.
+  const int row_bytes = p.Hkv * D * 2;
+  int voff[C::LPT];
 #pragma unroll
-    for (int i = 0; i < C::LPT; i++) {
-      const int c = threadIdx.x + kThreads * i;
-      const int row = c / C::CPR, ch = c % C::CPR;
-      const int key = min(t * kBN + row, t_max);  // rows past the last query are loaded but masked
-      kreg[i] = *(const u32x4*)(kbase + (size_t)key * kv_row_stride + ch * 8);
-      vreg[i] = ld_stream(vbase + (size_t)key * kv_row_stride + ch * 8);
-    }
+  for (int i = 0; i < C::LPT; i++) {
+    const int c = threadIdx.x + kThreads * i;
+    voff[i] = (c / C::CPR) * row_bytes + (c % C::CPR) * 16;
+  }
+  auto tile_rsrc = [&](const uint16_t* base, int t) {
+    const int valid = max(0, min(kBN, t_max + 1 - t * kBN));
+    const int n_rec = __builtin_amdgcn_readfirstlane(valid * row_bytes);  // uniform: scalar
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)t * kBN * kv_row_stride), 0,
+                                             n_rec, kBufferConfig);
   };
-  auto store_tile = [&](int buf) {
+  u32x4 kreg[C::LPT], vreg[C::LPT];
+  auto load_k = [&](int t) {
+    const auto rs = tile_rsrc(kbase, t);
+#pragma unroll
+    for (int i = 0; i < C::LPT; i++)
+      kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], 0, 0));
+  };
+  auto load_v = [&](int t) {  // V is read once: non-temporal
+    const auto rs = tile_rsrc(vbase, t);
+#pragma unroll
+    for (int i = 0; i < C::LPT; i++)
+      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], 0, kNonTemporal));
+  };
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::LPT; i++) {
       const int c = threadIdx.x + kThreads * i;
       const int row = c / C::CPR, ch = c % C::CPR;
       *(u32x4*)(&ks[buf][row * C::KStr + ch * 8]) = kreg[i];
+    }
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::LPT; i++) {
+      const int c = threadIdx.x + kThreads * i;
+      const int row = c / C::CPR, ch = c % C::CPR;
       *(u32x4*)(&vs[buf][row * C::VStr + ch * 8]) = vreg[i];
+    }
+  };
+  // S^T of tile t for the two 32-key blocks: register 4g + e of s[kb] is key 64t + 32kb + 8g + 4h + e
+  auto qk = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) s[kb][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; kk++) {  // the two key blocks' chains interleaved
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++) {
+        const bf16x8 ka = *(const bf16x8*)(&ks[t & 1][(32 * kb + rj) * C::KStr + 16 * kk + 8 * h]);
+        s[kb] = mfma32(ka, qb[kk], s[kb]);
+      }
     }
   };
 
@@ -242,46 +294,40 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
     }
   }
 
-  load_tile(0);
-  store_tile(0);
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  load_k(1);
+  store_k(1);
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0);  // Q loads done here, not inside the loop
-  // One 64-key tile; MASK: the tile reaches past the workgroup's first query position.
-  auto tile = [&](int t, auto mask_tag) {
+  f32x16 sa[2], sb[2];
+  qk(0, sa);
+  __syncthreads();  // the first step rewrites K buffer 0
+
+  // The step of tile t: S(t) in sc, S(t+1) into sn.  MASK: tile t reaches past the workgroup's
+  // first query position.
+  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], auto mask_tag)
+                  __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    load_k(t + 2);
+    load_v(t + 1);
     const int key0 = t * kBN;
-
-    // S^T for the two 32-key blocks: register 4g + e of sacc[kb] is key key0 + 32kb + 8g + 4h + e
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) sacc[kb][i] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < C::KK; kk++) {  // the two key blocks' chains interleaved
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++) {
-        const bf16x8 ka = *(const bf16x8*)(&ks[buf][(32 * kb + rj) * C::KStr + 16 * kk + 8 * h]);
-        sacc[kb] = mfma32(ka, qb[kk], sacc[kb]);
-      }
-    }
-
     if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int i = 0; i < 16; i++) {
           const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * h + (i % 4);
-          if (!row_ok || key > t_row) sacc[kb][i] = -INFINITY;
+          sc[kb][i] = (row_ok && key <= t_row) ? sc[kb][i] : -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kb][i], sacc[kb][i + 1]));
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[kb][i], sc[kb][i + 1]));
     mx = max_halves(mx);
     if constexpr (BSEL) {
       // block t = this tile: replace the list minimum when the tile's maximum beats it (equal
@@ -301,9 +347,20 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
         thr = m0 < m1 ? m0 : m1;
       }
     }
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // Lazy rescale: the exponent reference m_run moves only when a row maximum passes it by more
+    // than kLazy (log2 units); otherwise p = 2^(s - m_run) <= 2^kLazy, exact in fp32 and bf16, and
+    // O, l and the LSE refer to m_run consistently.
+    const float m_cand = mx * p.scale_log2;
+    if (__ballot(m_cand > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+      l_s *= alpha;
+      l_c *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; db++) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float psum = 0.f;
     bf16x8 pb[2][2];
 #pragma unroll
@@ -313,20 +370,13 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
         float x8[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          x8[i] = fast_exp2(__builtin_fmaf(sacc[kb][8 * s2 + i], p.scale_log2, -m_use));
+          x8[i] = fast_exp2(__builtin_fmaf(sc[kb][8 * s2 + i], p.scale_log2, -m_use));
           psum += x8[i];
         }
         pb[kb][s2] = pack_bf16x8(x8);
       }
     }
-    l_s *= alpha;
-    l_c *= alpha;
-    kahan_add(l_s, l_c, psum);
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {  // rescale only when some row maximum moved
-#pragma unroll
-      for (int db = 0; db < C::DB; db++) oacc[db] *= alpha;
-    }
+    qk(t + 1, sn);
 
     // O^T += V^T P^T over four 16-key steps; step (kb, s2) covers keys key0 + 32kb + 16s2 + {4h+e,
     // 8+4h+e}, the order in which pb[kb][s2] holds them
@@ -338,19 +388,52 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
 #pragma unroll
         for (int db = 0; db < C::DB; db++) {
           const int c0 = 32 * db + 16 * ((lane >> 4) & 1);
-          const uint16_t* a0 = &vs[buf][(kbase_row + ((lane & 15) >> 2)) * C::VStr + c0 + 4 * (lane & 3)];
+          const uint16_t* a0 = &vs[t & 1][(kbase_row + ((lane & 15) >> 2)) * C::VStr + c0 + 4 * (lane & 3)];
           const bf16x8 va = join_tr(lds_read_tr16(a0), lds_read_tr16(a0 + 8 * C::VStr));
           oacc[db] = mfma32(va, pb[kb][s2], oacc[db]);
         }
       }
     }
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    // one matrix instruction between every few vector ones: S(t+1) with the exponentials of
+    // S(t), then O += V(t) P(t) with the rest
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 14; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    }
+    kahan_add(l_s, l_c, psum);
+    store_k(t & 1);
+    store_v((t + 1) & 1);
     __syncthreads();
   };
-  // tiles entirely at or before the first query position need no mask
+  // tiles entirely at or before the first query position need no mask.  Two steps per loop
+  // trip, so that S(t) always sits in sa for even t and in sb for odd t; a tile without mask
+  // may run the masked step (the mask is then a no-op)
   const int n_full = min(n_tiles, (t_min + 1) / kBN);
-  for (int t = 0; t < n_full; t++) tile(t, std::false_type());
-  for (int t = n_full; t < n_tiles; t++) tile(t, std::true_type());
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    step(t, sa, sb, std::false_type());
+    step(t + 1, sb, sa, std::false_type());
+  }
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, sa, sb, std::true_type());
+    step(t + 1, sb, sa, std::true_type());
+  }
+  if (t < n_tiles) step(t, sa, sb, std::true_type());
 
   // epilogue: normalize and write O and LSE
   // lanes l and l ^ 32 hold the row's sums over different keys (with the same maximum)

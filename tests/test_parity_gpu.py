@@ -75,6 +75,48 @@ def test_full_attn_matches_oracle(name, wl):
         assert (diff <= np.maximum(TOL_BF16, ulp)).all()
 
 
+def logit_profile_inputs(wl, profile):
+    """Every query of a KV group is the same vector q0 and key i is s_i * sqrt(d) * q0 / |q0|^2,
+    so every head sees the logit s_i at key i (up to bf16 rounding of the key)."""
+    x = make_inputs(wl)
+    q, k = x["q"].clone(), x["k"].clone()
+    g = wl.n_q_heads // wl.n_kv_heads
+    s = torch.tensor([profile(i) for i in range(wl.kv_len)], dtype=torch.float64)
+    for b in range(wl.batch):
+        for u in range(wl.n_kv_heads):
+            q0 = q[b, 0, u * g].double()
+            q[b, :, u * g:(u + 1) * g] = q0.to(q.dtype)
+            dirv = wl.head_dim ** 0.5 * q0 / (q0 * q0).sum()
+            k[b, :, u] = (s[:, None] * dirv[None, :]).to(k.dtype)
+    return q, k, x["v"]
+
+
+PROFILES = {
+    # the maximum rises by about 32 log2 units along a row: the exponent reference of the
+    # prefill kernel is kept while it is within 8 of the maximum and moved several times
+    "linear_rise": lambda i: -8.0 + 22.0 * i / 2500,
+    # one jump of 20 after a long flat stretch
+    "step": lambda i: -8.0 if i < 1000 else 12.0,
+    # rises and falls: late keys far below the reference
+    "tent": lambda i: 14.0 - abs(i - 1200) * 0.02,
+}
+
+
+@pytest.mark.parametrize("profile", list(PROFILES), ids=list(PROFILES))
+def test_full_attn_moving_maximum(profile):
+    wl = Workload("mv", 1, 300, 2500, 8, 2, 128, "bf16", seed=41)
+    say(f"[full_attn moving maximum] {profile} {wl}")
+    q, k, v = logit_profile_inputs(wl, PROFILES[profile])
+    o, lse = hs().full_attn_fwd(to_dev(q), to_dev(k), to_dev(v), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.full_attention(to_numpy_f32(q), to_numpy_f32(k), to_numpy_f32(v))
+    eo = max_abs(o.cpu().numpy(), o_ref)
+    el = max_abs(lse.cpu().numpy(), lse_ref)
+    say(f"  max|dO| = {eo:.3e}  max|dLSE| = {el:.3e}  max LSE {np.abs(lse_ref).max():.2f}")
+    assert eo <= TOL_BF16
+    assert el <= 2e-6
+
+
 # ---- token top-k -------------------------------------------------------------------------
 
 TOPK_CASES = [
