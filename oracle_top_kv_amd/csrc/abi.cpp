@@ -184,10 +184,10 @@ hs_status check_qkv_dtype(const Shape& s) {
   return HS_OK;
 }
 
+size_t row_fa_ws(const Shape& s, int page_size);
 size_t full_attn_ws(const Shape& s) {
   if (use_prefill_kernel(s)) return 0;
-  const RaGeom g = ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups);
-  return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+  return row_fa_ws(s, 0);
 }
 
 // ---- token top-k ---------------------------------------------------------------------------
@@ -423,6 +423,39 @@ RaGeom fa_row_geom(const Shape& s, int page_size) {
   return ra_geom(s, false, s.q_off + s.Tq, 8, kResidentWorkgroups, max_steps);
 }
 
+// Groups of more than 16 heads per KV head (bf16, contiguous K / V): the group kernel, one
+// workgroup per (batch entry, KV head, query, key split) whose waves are the 16-head chunks and
+// share every 64-key step of K / V through LDS.  It always writes split partials.
+constexpr int kGroupStepKeys = 64;
+bool use_group_kernel(const Shape& s, bool paged) {
+  return s.g > 16 && !s.in_f32 && (s.D == 128 || s.D == 256) && !paged;
+}
+
+RaGeom group_geom(const Shape& s) {
+  RaGeom g;
+  g.q_per_set = 1;
+  g.sets_per_bu = s.Tq;
+  g.n_sets = s.B * s.Hkv * s.Tq * chunks_per_query(s);
+  const long long steps = (s.q_off + s.Tq + kGroupStepKeys - 1) / kGroupStepKeys;
+  const long long wgs = (long long)s.B * s.Hkv * s.Tq;
+  const long long target = s.D == 256 ? 256 : 512;  // LDS: one (d 256) or two workgroups per CU
+  long long want = (target + wgs - 1) / wgs;
+  const long long most = (steps + 7) / 8;  // no split shorter than 8 steps
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  g.steps_per_split = (int)((steps + want - 1) / want);
+  g.n_split = (int)((steps + g.steps_per_split - 1) / g.steps_per_split);
+  return g;
+}
+
+// Workspace of full attention on the row path (decode, short query blocks, stored logits,
+// paged caches).
+size_t row_fa_ws(const Shape& s, int page_size) {
+  if (use_group_kernel(s, page_size > 0)) return partial_bytes(group_geom(s), s.D);
+  const RaGeom g = fa_row_geom(s, page_size);
+  return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+}
+
 hs_status check_pages(const Shape& s, const hs_kv_pages* pg) {
   if (!pg || !pg->block_table) return fail(HS_ERR_INVALID_ARG, "NULL page table");
   const int P = pg->page_size;
@@ -449,8 +482,9 @@ void set_pages(hs::RowAttnParams& p, const hs_kv_pages* pg) {
 hs_status row_full_attn(const Shape& s, const void* q, const void* k, const void* v, void* o,
                         float* lse, float* logits, void* ws, size_t ws_bytes, void* stream,
                         const hs_kv_pages* pages = nullptr) {
-  const RaGeom g = fa_row_geom(s, pages ? pages->page_size : 0);
-  const size_t need = g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+  const bool group = use_group_kernel(s, pages != nullptr);
+  const RaGeom g = group ? group_geom(s) : fa_row_geom(s, pages ? pages->page_size : 0);
+  const size_t need = row_fa_ws(s, pages ? pages->page_size : 0);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   hs::RowAttnParams p = ra_params(s, g);
@@ -462,10 +496,11 @@ hs_status row_full_attn(const Shape& s, const void* q, const void* k, const void
   p.logits = logits;
   p.logits_vec = logits && s.Tk % 4 == 0 && (uintptr_t)logits % 16 == 0;
   if (pages) set_pages(p, pages);
-  p.final_direct = g.n_split == 1;
+  p.final_direct = !group && g.n_split == 1;
   if (!p.final_direct) carve_partials(ws, g, s.D, &p.part_m, &p.part_l, &p.part_o);
   hipStream_t hst = (hipStream_t)stream;
-  hipError_t e = hs::launch_row_attn(p, s.D, s.in_f32, hs::SRC_RANGE, hst);
+  hipError_t e = group ? hs::launch_group_attn(p, s.D, hst)
+                       : hs::launch_row_attn(p, s.D, s.in_f32, hs::SRC_RANGE, hst);
   if (e != hipSuccess) return hip_status(e, "full attention kernel");
   if (!p.final_direct) {
     hs::CombineParams c = combine_params(s, g, o, lse);
@@ -583,14 +618,10 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
       if (p0 < 1 || p1 < 0) return 0;
       return sparse_ws(s, sparse_geom(s, p0, p1), p1);
     }
-    case HS_OP_FULL_ATTN_LOGITS: {
-      const RaGeom g = fa_row_geom(s, 0);
-      return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
-    }
+    case HS_OP_FULL_ATTN_LOGITS: return row_fa_ws(s, 0);
     case HS_OP_FULL_ATTN_PAGED: {
       if (p0 < 1 || (p0 & (p0 - 1))) return 0;
-      const RaGeom g = fa_row_geom(s, p0);
-      return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+      return row_fa_ws(s, p0);
     }
     case HS_OP_TOPK_FROM_LOGITS: return tk_ws(s, tl_geom(s));
     case HS_OP_FULL_ATTN_BLOCK_TOPK: return fused_blocks_ws(s, p0, p1);

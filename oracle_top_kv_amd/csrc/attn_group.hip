@@ -1,0 +1,282 @@
+// attn_group.hip -- full attention of one query over a long key range for GQA groups of 32, 48
+// or 64 query heads per KV head (decode in HySparse2's head shape: 64 query heads on one KV
+// head, d = 256) [P2 "Extracting block scores from exact attention": a = q.k/sqrt(d),
+// p = softmax, o = sum p v; P1 section 4.2 and P5 model configuration for the head shape].
+//
+// One workgroup per (batch entry, KV head, query, key split) with one wave per 16-head chunk of
+// the group.  Every 64-key step of K and V is loaded once by the whole workgroup into LDS
+// (double-buffered, through buffer loads whose descriptors hold the step's first row and its
+// number of rows) and read there by every chunk: K and V cross HBM and L2 once, however many
+// heads share them.  Per wave the arithmetic is the row kernel's:
+//   S^T = K Q^T    v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 d from the LDS tile, B = Q^T
+//                  resident; lane (row n, group j) holds S[n][16kb + 4j .. 16kb + 4j + 3]
+//   online softmax in the log2 domain, Kahan-compensated row sums in the 4 lanes of a row
+//   O^T += V^T P^T B = P^T straight from the S^T accumulator, A = V^T read from the row-major
+//                  V tile with ds_read_b64_tr_b16 (keys in the accumulator's order)
+// LOGITS: the raw dot products q.k go to a [B, Tq, Hq, Tk] array, 16 bytes per lane per key
+// block (64 contiguous bytes per row).  Every workgroup writes split partials (row maximum, row
+// sum, unnormalized O); the combine kernel normalizes.
+#include "hs_device.h"
+#include "hs_kernels.h"
+
+namespace hs {
+namespace {
+
+constexpr int kGStep = 64;                   // keys per step
+constexpr int kBufferConfig = 0x00020000;    // buffer descriptor word 3 (gfx9 family: raw dwords)
+constexpr int kNonTemporal = 2;              // cache-policy bit of a buffer load: non-temporal
+
+template <int D>
+struct GaCfg {
+  static constexpr int KStr = D + 8;   // K tile row stride (elements): conflict-free b128 reads
+  static constexpr int VStr = D + 16;  // V tile row stride: conflict-free transpose reads
+  static constexpr int KK = D / 32;    // MFMA steps over d
+  static constexpr int DB = D / 16;    // 16-wide d blocks of O^T
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int kChunks = kGStep * CPR;  // 16-byte chunks per tile
+};
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D, int NW, bool LOGITS>
+__global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p) {
+  using C = GaCfg<D>;
+  constexpr int kThreads = 64 * NW;
+  constexpr int kPer = (C::kChunks + kThreads - 1) / kThreads;  // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][kGStep * C::KStr];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kGStep * C::VStr];
+
+  const int lane = threadIdx.x & 63, hc = threadIdx.x >> 6;  // wave = head chunk
+  const int rn = lane & 15, jg = lane >> 4;
+  // KV head fastest, then split, then (batch, query)
+  const int x = blockIdx.x;
+  const int u = x % p.Hkv;
+  const int split = (x / p.Hkv) % p.n_split;
+  const int bq = x / (p.Hkv * p.n_split);
+  const int j = bq % p.Tq;
+  const int b = bq / p.Tq;
+  const long long t_row = p.q_off + j;  // this query's position: keys 0 .. t_row
+  const int h = u * p.g + hc * 16 + rn;
+
+  const int n_steps = (int)((t_row + kGStep) / kGStep);
+  const int s0 = split * p.steps_per_split;
+  const int s1 = min(s0 + p.steps_per_split, n_steps);
+
+  // Q^T operand of this lane's row
+  bf16x8 qb[C::KK];
+  {
+    const uint16_t* qp = (const uint16_t*)p.q + (((size_t)b * p.Tq + j) * p.Hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; kk++)
+      qb[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * kk + 8 * jg));
+  }
+
+  // tile loads: thread chunk c = threadIdx.x + kThreads * i is row c / CPR, 16 bytes ch = c % CPR
+  const int row_bytes = p.Hkv * D * 2;
+  const size_t kv_row_stride = (size_t)p.Hkv * D;
+  const uint16_t* kbase = (const uint16_t*)p.k + ((size_t)b * p.Tk * p.Hkv + u) * D;
+  const uint16_t* vbase = (const uint16_t*)p.v + ((size_t)b * p.Tk * p.Hkv + u) * D;
+  int voff[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int c = threadIdx.x + kThreads * i;
+    voff[i] = (c / C::CPR) * row_bytes + (c % C::CPR) * 16;
+  }
+  // descriptor of step s: its first row and the rows through t_row (past them: zeros, masked);
+  // no rows at all for steps past this split (the prefetch runs two steps ahead)
+  auto rsrc = [&](const uint16_t* base, int s) {
+    const long long valid = s < s1 ? t_row + 1 - (long long)s * kGStep : 0;
+    const int rows = valid < 0 ? 0 : (valid > kGStep ? kGStep : (int)valid);
+    const int n_rec = __builtin_amdgcn_readfirstlane(rows * row_bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)s * kGStep * kv_row_stride), 0,
+                                             n_rec, kBufferConfig);
+  };
+  // two register sets (the two steps after the one being computed are both in flight), or one
+  // when a thread holds more than 8 chunks per step (2 waves, d 256: registers)
+  constexpr int kSets = kPer <= 8 ? 2 : 1;
+  u32x4 kreg[kSets][kPer], vreg[kSets][kPer];
+  auto load = [&](int s, int set) {
+    const auto rk = rsrc(kbase, s), rv = rsrc(vbase, s);
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      if (kPer * kThreads == C::kChunks || threadIdx.x + kThreads * i < C::kChunks) {
+        kreg[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[i], 0, 0));
+        vreg[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, kNonTemporal));
+      }
+    }
+  };
+  auto store = [&](int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int c = threadIdx.x + kThreads * i;
+      if (kPer * kThreads == C::kChunks || c < C::kChunks) {
+        const int row = c / C::CPR, ch = c % C::CPR;
+        *(u32x4*)&kt[buf][row * C::KStr + ch * 8] = kreg[set][i];
+        *(u32x4*)&vt[buf][row * C::VStr + ch * 8] = vreg[set][i];
+      }
+    }
+  };
+
+  float m_run = -INFINITY;
+  float l_s = 0.f, l_c = 0.f;
+  f32x4 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float* lrow = LOGITS ? p.logits + (((size_t)b * p.Tq + j) * p.Hq + h) * (size_t)p.Tk : nullptr;
+
+  auto compute = [&](int s, int buf) {
+    // S^T for the four 16-key blocks
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C::KK; kk++)
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        const bf16x8 ka = *(const bf16x8*)&kt[buf][(16 * kb + rn) * C::KStr + 32 * kk + 8 * jg];
+        sacc[kb] = mfma_bf16(ka, qb[kk], sacc[kb]);
+      }
+    const int key0 = s * kGStep;
+    if constexpr (LOGITS) {
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        const int e0 = key0 + 16 * kb + 4 * jg;
+        if (p.logits_vec) {
+          if (e0 < p.Tk) *(f32x4*)(lrow + e0) = sacc[kb];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (e0 + e < p.Tk) lrow[e0 + e] = sacc[kb][e];
+        }
+      }
+    }
+    float sv[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const long long key = key0 + 16 * kb + 4 * jg + e;
+        const float v = key <= t_row ? sacc[kb][e] * p.scale_log2 : -INFINITY;
+        sv[kb][e] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = max4groups(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      float p8[8];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; k2++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float pe = fast_exp2(sv[2 * half + k2][e] - m_use);
+          p8[4 * k2 + e] = pe;
+          psum += pe;
+        }
+      pb[half] = pack_bf16x8(p8);
+    }
+    l_s *= alpha;
+    l_c *= alpha;
+    kahan_add(l_s, l_c, psum);
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < C::DB; db++) oacc[db] *= alpha;
+    // O^T += V^T P^T, one MFMA per 32 keys (key blocks 2half, 2half + 1) and 16 columns
+#pragma unroll
+    for (int half = 0; half < 2; half++)
+#pragma unroll
+      for (int db = 0; db < C::DB; db++) {
+        const uint16_t* a0 = &vt[buf][(32 * half + 4 * jg + (rn >> 2)) * C::VStr + 16 * db + 4 * (rn & 3)];
+        const bf16x8 vop = join_tr(lds_read_tr16(a0), lds_read_tr16(a0 + 16 * C::VStr));
+        oacc[db] = mfma_bf16(vop, pb[half], oacc[db]);
+      }
+  };
+
+  // Step s is computed from LDS buffer (s - s0) & 1 while steps s + 1 and s + 2 are loading
+  // into the register sets; two steps per loop trip keep the sets' roles fixed.  With one set,
+  // only step s + 1 is loading.
+  if (s0 < s1) {
+    load(s0, 0);
+    store(0, 0);
+    lds_barrier();
+    if constexpr (kSets == 2) {
+      load(s0 + 1, 1);
+      int s = s0;
+      for (; s + 1 < s1; s += 2) {
+        load(s + 2, 0);
+        compute(s, 0);
+        store(1, 1);  // step s + 1
+        lds_barrier();
+        load(s + 3, 1);
+        compute(s + 1, 1);
+        if (s + 2 < s1) store(0, 0);  // step s + 2
+        lds_barrier();
+      }
+      if (s < s1) compute(s, 0);
+    } else {
+      for (int s = s0; s < s1; s++) {
+        const int buf = (s - s0) & 1;
+        load(s + 1, 0);
+        compute(s, buf);
+        if (s + 1 < s1) store(0, buf ^ 1);
+        lds_barrier();
+      }
+    }
+  }
+
+  // partials of this split: row maximum, row sum (the 4 lanes of the row summed), O^T
+  double ld = (double)l_s - (double)l_c;
+  ld += __shfl_xor(ld, 16, 64);
+  ld += __shfl_xor(ld, 32, 64);
+  const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu * p.cpq;
+  const int set = ((b * p.Hkv + u) * p.sets_per_bu + j) * p.cpq + hc;
+  const size_t prow = ((size_t)split * n_sets + set) * 16 + rn;
+  if (jg == 0) {
+    p.part_m[prow] = m_run;
+    p.part_l[prow] = ld;
+  }
+#pragma unroll
+  for (int db = 0; db < C::DB; db++) *(f32x4*)(p.part_o + prow * D + 16 * db + 4 * jg) = oacc[db];
+}
+
+template <int D, int NW>
+hipError_t launch_nw(const RowAttnParams& p, hipStream_t stream) {
+  const dim3 grid(p.n_split * p.B * p.Hkv * p.Tq);
+  if (p.logits)
+    group_attn_kernel<D, NW, true><<<grid, 64 * NW, 0, stream>>>(p);
+  else
+    group_attn_kernel<D, NW, false><<<grid, 64 * NW, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const RowAttnParams& p, hipStream_t stream) {
+  switch (p.cpq) {
+    case 2: return launch_nw<D, 2>(p, stream);
+    case 3: return launch_nw<D, 3>(p, stream);
+    case 4: return launch_nw<D, 4>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_group_attn(const RowAttnParams& p, int head_dim, hipStream_t stream) {
+  if (p.hpc != 16 || p.q_per_set != 1 || p.sets_per_bu != p.Tq || p.n_split < 1 || p.pages)
+    return hipErrorInvalidValue;
+  if (head_dim == 256) return launch_d<256>(p, stream);
+  if (head_dim == 128) return launch_d<128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hs

@@ -607,7 +607,10 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
 // One workgroup per (row-set, row).  Threads = SP split lanes x D/4 column chunks; each thread
 // folds every SP-th split of its 4 columns with weights 2^(m_s - M), then the split lanes are
 // summed in LDS.  Row sums are combined in fp64.
-template <int D>
+// BATCHED (more than two splits per thread): the loads of kBatch splits are issued before any
+// is used, here and below (a dependent load per split makes the combine a chain of round
+// trips); with at most two splits per thread the plain loops, with fewer registers, are faster.
+template <int D, bool BATCHED>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int NC = D / 4;         // column chunks of 4
   constexpr int SP = 256 / NC;      // split lanes
@@ -635,20 +638,51 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   for (int br = 0; br < p.n_branch; br++) {
     const int ns = p.n_split[br];
     const float* m = p.m[br];
-    // row maximum over splits (every thread, redundantly; ns is small)
+    // row maximum over splits (every thread, redundantly)
+    constexpr int kBatch = 8;
     float M = -INFINITY;
-    for (int s = 0; s < ns; s++) M = fmaxf(M, m[((size_t)s * n_sets + set) * 16 + r]);
+    if constexpr (!BATCHED) {
+      for (int s = 0; s < ns; s++) M = fmaxf(M, m[((size_t)s * n_sets + set) * 16 + r]);
+    } else {
+      for (int s = 0; s < ns; s += kBatch) {
+        float mb[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; i++)
+          mb[i] = s + i < ns ? m[((size_t)(s + i) * n_sets + set) * 16 + r] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kBatch; i++) M = fmaxf(M, mb[i]);
+      }
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     double lacc = 0.0;
-    if (M != -INFINITY) {
+    if (M != -INFINITY && !BATCHED) {
       for (int s = sl; s < ns; s += SP) {
         const size_t prow = ((size_t)s * n_sets + set) * 16 + r;
         const float ms = m[prow];
         if (ms == -INFINITY) continue;
-        const float f = fast_exp2(ms - M);
         const f32x4 o4 = *(const f32x4*)(p.po[br] + prow * D + 4 * c);
-        acc += f * o4;
+        acc += fast_exp2(ms - M) * o4;
         if (c == 0) lacc += exp2((double)ms - (double)M) * p.l[br][prow];
+      }
+    } else if (M != -INFINITY) {  // a split past the end reads split s, weighted 0
+      for (int s = sl; s < ns; s += kBatch * SP) {
+        float mb[kBatch];
+        f32x4 ob[kBatch];
+        double lb[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; i++) {
+          const int si = s + i * SP;
+          const size_t prow = ((size_t)(si < ns ? si : s) * n_sets + set) * 16 + r;
+          mb[i] = si < ns ? m[prow] : -INFINITY;
+          ob[i] = *(const f32x4*)(p.po[br] + prow * D + 4 * c);
+          lb[i] = c == 0 ? p.l[br][prow] : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; i++) {
+          if (mb[i] == -INFINITY) continue;
+          acc += fast_exp2(mb[i] - M) * ob[i];
+          if (c == 0) lacc += exp2((double)mb[i] - (double)M) * lb[i];
+        }
       }
     }
     *(f32x4*)&red[sl][4 * c] = acc;
@@ -764,14 +798,25 @@ hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, Ke
                 : launch_ra<64, false, 4>(p, src, gated, stream);
 }
 
+template <int D>
+void launch_combine_d(const CombineParams& p, dim3 grid, hipStream_t stream) {
+  constexpr int SP = 256 / (D / 4);  // split lanes of the kernel
+  int most = p.n_split[0];
+  if (p.n_branch == 2 && p.n_split[1] > most) most = p.n_split[1];
+  if (most > 2 * SP)
+    combine_kernel<D, true><<<grid, 256, 0, stream>>>(p);
+  else
+    combine_kernel<D, false><<<grid, 256, 0, stream>>>(p);
+}
+
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid(p.B * p.Hkv * p.sets_per_bu * p.cpq * 16);
   if (head_dim == 256)
-    combine_kernel<256><<<grid, 256, 0, stream>>>(p);
+    launch_combine_d<256>(p, grid, stream);
   else if (head_dim == 128)
-    combine_kernel<128><<<grid, 256, 0, stream>>>(p);
+    launch_combine_d<128>(p, grid, stream);
   else
-    combine_kernel<64><<<grid, 256, 0, stream>>>(p);
+    launch_combine_d<64>(p, grid, stream);
   return hipGetLastError();
 }
 

@@ -33,8 +33,13 @@ def to_dev(x):
 
 
 def row_kernel_route(wl):
-    """hs_full_attn_fwd runs the row kernel (the one that can keep logits) for these shapes."""
-    return wl.dtype == "f32" or wl.q_len * (wl.n_q_heads // wl.n_kv_heads) <= 16
+    """hs_full_attn_fwd runs the kernel that can keep logits (the row kernel, or the group kernel
+    for groups of more than 16 heads) for these shapes, i.e. not the prefill kernel."""
+    g = wl.n_q_heads // wl.n_kv_heads
+    rows = wl.q_len * g
+    prefill = (wl.dtype != "f32" and wl.head_dim <= 128 and rows > 16
+               and (g <= 16 or rows >= 128) and 256 % g == 0)
+    return not prefill
 
 
 LOGIT_CASES = [
@@ -46,6 +51,11 @@ LOGIT_CASES = [
     ("decode_g12", Workload("g12", 1, 1, 1999, 24, 2, 128, "bf16", seed=205)),
     ("tiny_f32_prefill", Workload("tiny", 1, 64, 300, 4, 1, 64, "f32", seed=206)),
     ("one_key", Workload("one", 1, 1, 1, 8, 2, 128, "bf16", seed=207)),
+    # groups of more than 16 heads (the group kernel): MQA d 256, an odd key count; 48 heads
+    # (three chunks) with two queries; 32 heads on two KV heads
+    ("mqa64_d256_odd", Workload("m", 1, 1, 2999, 64, 1, 256, "bf16", seed=208)),
+    ("g48_d128_two_queries", Workload("g48", 1, 2, 2001, 48, 1, 128, "bf16", seed=209)),
+    ("g32_d256_two_kv_heads", Workload("g32", 2, 1, 4000, 64, 2, 256, "bf16", seed=210)),
 ]
 
 
