@@ -383,10 +383,28 @@ struct SparseGeom {
   bool wide;     // few row-sets: one 8-wave workgroup per set instead of split key lists
   bool combine;  // split partials merged by the combine kernel
   bool fused;    // gated layer with unsplit branches: both in one workgroup, no partials
+  bool group;    // the global branch on the group kernel (groups of more than 16 heads)
 };
 
-SparseGeom sparse_geom(const Shape& s, long long keys_per_set, int window) {
+bool use_group_kernel(const Shape& s, bool paged);
+RaGeom group_list_geom(const Shape& s, long long keys_per_set);
+
+// The group kernel addresses a batch entry's K / V rows with 32-bit byte offsets.
+bool group_list_fits(const Shape& s) {
+  return (long long)s.Tk * s.Hkv * s.D * 2 < (1LL << 31);
+}
+
+SparseGeom sparse_geom(const Shape& s, long long keys_per_set, int window, bool paged = false) {
   SparseGeom g;
+  g.group = use_group_kernel(s, paged) && group_list_fits(s);
+  if (g.group) {
+    g.glob = group_list_geom(s, keys_per_set);
+    g.wide = false;
+    g.fused = false;
+    g.loc = ra_geom(s, true, window > 0 ? window : 1, 4);
+    g.combine = true;
+    return g;
+  }
   g.glob = ra_geom(s, true, keys_per_set, 4, kTargetWorkgroups, 64);
   // Decode-sized index sets (at most 64 steps of 32 keys): rather than splitting each list over
   // several workgroups and merging partials in a second kernel, one workgroup of 8 waves takes
@@ -448,6 +466,28 @@ RaGeom group_geom(const Shape& s) {
   return g;
 }
 
+// Index lists on the group kernel: 64-entry steps, at most 32 per split (staged in LDS), enough
+// workgroups to fill the GPU.
+RaGeom group_list_geom(const Shape& s, long long keys_per_set) {
+  RaGeom g;
+  g.q_per_set = 1;
+  g.sets_per_bu = s.Tq;
+  g.n_sets = s.B * s.Hkv * s.Tq * chunks_per_query(s);
+  const long long steps = (keys_per_set + kGroupStepKeys - 1) / kGroupStepKeys;
+  const long long wgs = (long long)s.B * s.Hkv * s.Tq;
+  const long long target = s.D == 256 ? 256 : 512;
+  long long want = (target + wgs - 1) / wgs;
+  if (want > steps) want = steps;
+  const long long least = (steps + 31) / 32;
+  if (want < least) want = least;
+  if (want < 1) want = 1;
+  g.steps_per_split = (int)((steps + want - 1) / want);
+  if (g.steps_per_split < 1) g.steps_per_split = 1;
+  g.n_split = (int)((steps + g.steps_per_split - 1) / g.steps_per_split);
+  if (g.n_split < 1) g.n_split = 1;
+  return g;
+}
+
 // Workspace of full attention on the row path (decode, short query blocks, stored logits,
 // paged caches).
 size_t row_fa_ws(const Shape& s, int page_size) {
@@ -499,7 +539,7 @@ hs_status row_full_attn(const Shape& s, const void* q, const void* k, const void
   p.final_direct = !group && g.n_split == 1;
   if (!p.final_direct) carve_partials(ws, g, s.D, &p.part_m, &p.part_l, &p.part_o);
   hipStream_t hst = (hipStream_t)stream;
-  hipError_t e = group ? hs::launch_group_attn(p, s.D, hst)
+  hipError_t e = group ? hs::launch_group_attn(p, s.D, hs::SRC_RANGE, hst)
                        : hs::launch_row_attn(p, s.D, s.in_f32, hs::SRC_RANGE, hst);
   if (e != hipSuccess) return hip_status(e, "full attention kernel");
   if (!p.final_direct) {
@@ -616,7 +656,11 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
     }
     case HS_OP_SPARSE_ATTN: {
       if (p0 < 1 || p1 < 0) return 0;
-      return sparse_ws(s, sparse_geom(s, p0, p1), p1);
+      // the paged call (row kernel) and the contiguous one (group kernel for groups of more
+      // than 16 heads) share this size
+      const size_t a = sparse_ws(s, sparse_geom(s, p0, p1, false), p1);
+      const size_t b = sparse_ws(s, sparse_geom(s, p0, p1, true), p1);
+      return a > b ? a : b;
     }
     case HS_OP_FULL_ATTN_LOGITS: return row_fa_ws(s, 0);
     case HS_OP_FULL_ATTN_PAGED: {
@@ -876,7 +920,7 @@ hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, c
     return fail(HS_ERR_INVALID_ARG, "local_ring %d: needs a sliding-window branch", ring);
   if (ring > 0 && ring < window)
     return fail(HS_ERR_INVALID_ARG, "local_ring %d shorter than the window %d", ring, window);
-  const SparseGeom g = sparse_geom(s, keys, window);
+  const SparseGeom g = sparse_geom(s, keys, window, pages != nullptr);
   const size_t need = sparse_ws(s, g, window);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
@@ -913,7 +957,8 @@ hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, c
     carve_partials(w, g.glob, s.D, &pg.part_m, &pg.part_l, &pg.part_o);
     w += partial_bytes(g.glob, s.D);
   }
-  hipError_t e = hs::launch_row_attn(pg, s.D, s.in_f32, src, hst, false, g.wide);
+  hipError_t e = g.group ? hs::launch_group_attn(pg, s.D, src, hst)
+                         : hs::launch_row_attn(pg, s.D, s.in_f32, src, hst, false, g.wide);
   if (e != hipSuccess) return hip_status(e, "sparse attention kernel");
   hs::RowAttnParams pl;
   if (window > 0) {

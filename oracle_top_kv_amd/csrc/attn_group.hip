@@ -13,9 +13,13 @@
 //   online softmax in the log2 domain, Kahan-compensated row sums in the 4 lanes of a row
 //   O^T += V^T P^T B = P^T straight from the S^T accumulator, A = V^T read from the row-major
 //                  V tile with ds_read_b64_tr_b16 (keys in the accumulator's order)
-// LOGITS: the raw dot products q.k go to a [B, Tq, Hq, Tk] array, 16 bytes per lane per key
-// block (64 contiguous bytes per row).  Every workgroup writes split partials (row maximum, row
-// sum, unnormalized O); the combine kernel normalizes.
+// Key sources: the contiguous range 0..t (full attention), or a token / block index list of
+// (b, t, u) (the sparse layers' global branch [P2 "Cross-layer KV cache reuse"; P2 "Same query,
+// two memories"]): a split's list positions are staged in LDS first, and each step gathers its
+// 64 rows straight into the shared tile (invalid entries read as zeros and are masked).
+// LOGITS (range only): the raw dot products q.k go to a [B, Tq, Hq, Tk] array, 16 bytes per
+// lane per key block (64 contiguous bytes per row).  Every workgroup writes split partials (row
+// maximum, row sum, unnormalized O); the combine kernel normalizes.
 #include "hs_device.h"
 #include "hs_kernels.h"
 
@@ -42,13 +46,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int D, int NW, bool LOGITS>
+constexpr int kMaxSplitEntries = 2048;  // list entries staged per workgroup (32 steps)
+
+template <int D, int NW, int SRC, bool LOGITS>
 __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p) {
   using C = GaCfg<D>;
+  static_assert(!LOGITS || SRC == SRC_RANGE, "logits come from the full-attention pass only");
+  constexpr bool kList = SRC == SRC_TOKEN || SRC == SRC_BLOCK;
   constexpr int kThreads = 64 * NW;
   constexpr int kPer = (C::kChunks + kThreads - 1) / kThreads;  // chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][kGStep * C::KStr];
   __shared__ __attribute__((aligned(16))) uint16_t vt[2][kGStep * C::VStr];
+  __shared__ int pos_all[kList ? kMaxSplitEntries : 1];
 
   const int lane = threadIdx.x & 63, hc = threadIdx.x >> 6;  // wave = head chunk
   const int rn = lane & 15, jg = lane >> 4;
@@ -62,9 +71,37 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
   const long long t_row = p.q_off + j;  // this query's position: keys 0 .. t_row
   const int h = u * p.g + hc * 16 + rn;
 
-  const int n_steps = (int)((t_row + kGStep) / kGStep);
+  // list modes: the (b, t, u) list and its number of keys L (blocks count block keys each)
+  const int32_t* list = nullptr;
+  int L = (int)(t_row + 1);
+  if constexpr (kList) {
+    const size_t lrow = ((size_t)b * p.Tq + j) * p.Hkv + u;
+    list = p.idx + lrow * p.idx_cap;
+    int c = p.cnt[lrow];
+    c = c < 0 ? 0 : (c > p.idx_cap ? p.idx_cap : c);
+    L = SRC == SRC_TOKEN ? c : c * p.block;
+  }
+  const int n_steps = (L + kGStep - 1) / kGStep;
   const int s0 = split * p.steps_per_split;
   const int s1 = min(s0 + p.steps_per_split, n_steps);
+  // position of list entry e (-1: none, past the count, or after t), as in the row kernel
+  auto entry_pos = [&](int e) -> int {
+    if (e >= L) return -1;
+    if constexpr (SRC == SRC_TOKEN) {
+      const int x = list[e];
+      return (x >= 0 && x <= t_row) ? x : -1;
+    } else {
+      const int blk = list[e / p.block];
+      if (blk < 0 || (long long)blk > t_row / p.block) return -1;
+      const long long x = (long long)blk * p.block + e % p.block;
+      return x <= t_row ? (int)x : -1;
+    }
+  };
+  if constexpr (kList) {
+    for (int i = threadIdx.x; i < (s1 - s0) * kGStep; i += kThreads)
+      pos_all[i] = entry_pos(s0 * kGStep + i);
+    __syncthreads();
+  }
 
   // Q^T operand of this lane's row
   bf16x8 qb[C::KK];
@@ -86,8 +123,17 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
     const int c = threadIdx.x + kThreads * i;
     voff[i] = (c / C::CPR) * row_bytes + (c % C::CPR) * 16;
   }
-  // descriptor of step s: its first row and the rows through t_row (past them: zeros, masked);
-  // no rows at all for steps past this split (the prefetch runs two steps ahead)
+  // list modes: one descriptor over this batch entry's rows of head u; a chunk's offset is its
+  // entry's position, or past the end (reads zeros) for no position
+  const int list_rec = (int)((long long)p.Tk * row_bytes - (long long)u * D * 2);
+  auto list_off = [&](int s, int i) -> int {
+    const int c = threadIdx.x + kThreads * i;
+    const int e = (s - s0) * kGStep + c / C::CPR;
+    const int pos = s < s1 ? pos_all[e] : -1;
+    return pos >= 0 ? pos * row_bytes + (c % C::CPR) * 16 : 0x7FFFFFF0;
+  };
+  // range mode: descriptor of step s: its first row and the rows through t_row (past them:
+  // zeros, masked); no rows at all for steps past this split (the prefetch runs two steps ahead)
   auto rsrc = [&](const uint16_t* base, int s) {
     const long long valid = s < s1 ? t_row + 1 - (long long)s * kGStep : 0;
     const int rows = valid < 0 ? 0 : (valid > kGStep ? kGStep : (int)valid);
@@ -100,12 +146,16 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
   constexpr int kSets = kPer <= 8 ? 2 : 1;
   u32x4 kreg[kSets][kPer], vreg[kSets][kPer];
   auto load = [&](int s, int set) {
-    const auto rk = rsrc(kbase, s), rv = rsrc(vbase, s);
+    const auto rk = kList ? __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, list_rec, kBufferConfig)
+                          : rsrc(kbase, s);
+    const auto rv = kList ? __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, list_rec, kBufferConfig)
+                          : rsrc(vbase, s);
 #pragma unroll
     for (int i = 0; i < kPer; i++) {
       if (kPer * kThreads == C::kChunks || threadIdx.x + kThreads * i < C::kChunks) {
-        kreg[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[i], 0, 0));
-        vreg[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, kNonTemporal));
+        const int off = kList ? list_off(s, i) : voff[i];
+        kreg[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        vreg[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kNonTemporal));
       }
     }
   };
@@ -161,8 +211,9 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const long long key = key0 + 16 * kb + 4 * jg + e;
-        const float v = key <= t_row ? sacc[kb][e] * p.scale_log2 : -INFINITY;
+        const int ke = 16 * kb + 4 * jg + e;  // entry of the step
+        const bool ok = kList ? pos_all[(s - s0) * kGStep + ke] >= 0 : (long long)key0 + ke <= t_row;
+        const float v = ok ? sacc[kb][e] * p.scale_log2 : -INFINITY;
         sv[kb][e] = v;
         mx = fmaxf(mx, v);
       }
@@ -250,32 +301,38 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
 }
 
 template <int D, int NW>
-hipError_t launch_nw(const RowAttnParams& p, hipStream_t stream) {
+hipError_t launch_nw(const RowAttnParams& p, KeySrc src, hipStream_t stream) {
   const dim3 grid(p.n_split * p.B * p.Hkv * p.Tq);
-  if (p.logits)
-    group_attn_kernel<D, NW, true><<<grid, 64 * NW, 0, stream>>>(p);
+  if (src == SRC_TOKEN)
+    group_attn_kernel<D, NW, SRC_TOKEN, false><<<grid, 64 * NW, 0, stream>>>(p);
+  else if (src == SRC_BLOCK)
+    group_attn_kernel<D, NW, SRC_BLOCK, false><<<grid, 64 * NW, 0, stream>>>(p);
+  else if (p.logits)
+    group_attn_kernel<D, NW, SRC_RANGE, true><<<grid, 64 * NW, 0, stream>>>(p);
   else
-    group_attn_kernel<D, NW, false><<<grid, 64 * NW, 0, stream>>>(p);
+    group_attn_kernel<D, NW, SRC_RANGE, false><<<grid, 64 * NW, 0, stream>>>(p);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const RowAttnParams& p, hipStream_t stream) {
+hipError_t launch_d(const RowAttnParams& p, KeySrc src, hipStream_t stream) {
   switch (p.cpq) {
-    case 2: return launch_nw<D, 2>(p, stream);
-    case 3: return launch_nw<D, 3>(p, stream);
-    case 4: return launch_nw<D, 4>(p, stream);
+    case 2: return launch_nw<D, 2>(p, src, stream);
+    case 3: return launch_nw<D, 3>(p, src, stream);
+    case 4: return launch_nw<D, 4>(p, src, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_group_attn(const RowAttnParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_group_attn(const RowAttnParams& p, int head_dim, KeySrc src, hipStream_t stream) {
   if (p.hpc != 16 || p.q_per_set != 1 || p.sets_per_bu != p.Tq || p.n_split < 1 || p.pages)
     return hipErrorInvalidValue;
-  if (head_dim == 256) return launch_d<256>(p, stream);
-  if (head_dim == 128) return launch_d<128>(p, stream);
+  if (src == SRC_WINDOW || (src != SRC_RANGE && p.logits)) return hipErrorInvalidValue;
+  if (src != SRC_RANGE && p.steps_per_split * kGStep > kMaxSplitEntries) return hipErrorInvalidValue;
+  if (head_dim == 256) return launch_d<256>(p, src, stream);
+  if (head_dim == 128) return launch_d<128>(p, src, stream);
   return hipErrorInvalidValue;
 }
 

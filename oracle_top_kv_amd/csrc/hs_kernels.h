@@ -83,11 +83,12 @@ struct CombineParams {
 hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
                            hipStream_t stream, bool gated = false, bool wide = false);
 
-// Full attention (range source, bf16, head_dim 128 or 256) for groups of 32, 48 or 64 heads:
-// one workgroup per (batch entry, KV head, query, split), one wave per 16-head chunk, K / V
-// steps shared through LDS; always writes split partials (hpc 16, q_per_set 1, sets_per_bu Tq);
-// optional logits as in the row kernel.
-hipError_t launch_group_attn(const RowAttnParams& p, int head_dim, hipStream_t stream);
+// Attention for groups of 32, 48 or 64 heads (bf16, head_dim 128 or 256) over a range (full
+// attention, optional logits as in the row kernel) or a token / block list (steps_per_split 64-key
+// steps of at most 2048 entries): one workgroup per (batch entry, KV head, query, split), one
+// wave per 16-head chunk, K / V steps shared through LDS; always writes split partials (hpc 16,
+// q_per_set 1, sets_per_bu Tq).  List offsets are 32-bit: Tk * Hkv * d * 2 below 2^31.
+hipError_t launch_group_attn(const RowAttnParams& p, int head_dim, KeySrc src, hipStream_t stream);
 
 // Full causal attention for many queries per KV head (bf16): 256 (query, head) rows per
 // workgroup sharing LDS-staged K/V tiles.

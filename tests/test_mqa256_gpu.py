@@ -128,15 +128,17 @@ def test_paged_mqa256_equals_contiguous():
     o2, lse2, lg2 = hs().full_attn_fwd_paged(x["q"], kp, vp, table, wl.kv_len, logits=True,
                                              out_dtype=torch.float32)
     idx, cnt = hs().oracle_topk_from_logits(lg, lse, 1, 256, wl.k_global, wl.window)
-    s1, _ = hs().sparse_attn_gather(x["q_sparse"][0], x["k"], x["v"], idx, cnt)
-    s2, _ = hs().sparse_attn_gather(x["q_sparse"][0], kp, vp, idx, cnt, pages=(table, wl.kv_len))
+    s1, _ = hs().sparse_attn_gather(x["q_sparse"][0], x["k"], x["v"], idx, cnt,
+                                    out_dtype=torch.float32)
+    s2, _ = hs().sparse_attn_gather(x["q_sparse"][0], kp, vp, idx, cnt, pages=(table, wl.kv_len),
+                                    out_dtype=torch.float32)
     torch.cuda.synchronize()
-    # the logits are the same dot products; full attention over a paged cache runs the row
-    # kernel, the contiguous call the group kernel: other split boundaries, so P is rounded to
-    # bf16 against other running maxima (the LSE sums fp32 exponentials)
+    # the logits are the same dot products; over a paged cache full attention and the sparse
+    # layer run the row kernel, the contiguous calls the group kernel: other split boundaries,
+    # so P is rounded to bf16 against other running maxima (the LSE sums fp32 exponentials)
     assert torch.equal(lg, lg2)
     assert (o - o2).abs().max().item() <= TOL_BF16 and (lse - lse2).abs().max().item() <= 2e-6
-    assert torch.equal(s1, s2)
+    assert (s1 - s2).abs().max().item() <= TOL_BF16
 
 
 def test_unsupported_combinations_are_rejected():
