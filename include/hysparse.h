@@ -211,9 +211,11 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
  * 1/sqrt(d) scale) to logits: [B, q_len, Hq, kv_len] fp32, caller-owned, 4-byte aligned (16 for
  * full-width stores).  Entries i <= t of query row t are the attention logits times sqrt(d);
  * entries past t are unspecified (those of the last query row's range are written, larger ones
- * not).  Always runs on the split row kernel, whatever q_len is; o and lse are bit-identical to
- * what hs_full_attn_fwd returns for the same inputs on that kernel (q_len * g <= 16, or fp32
- * inputs).  Workspace: hs_workspace_size(HS_OP_FULL_ATTN_LOGITS, ...). */
+ * not).  Always runs on the split row kernel (the group kernel for groups of 32-64 heads with
+ * bf16 inputs and head_dim 128 or 256), whatever q_len is; o and lse are bit-identical to what
+ * hs_full_attn_fwd returns for the same inputs on that kernel (whenever hs_full_attn_fwd does
+ * not take the prefill kernel: q_len * g <= 16, fp32 inputs, or groups above 16 with fewer than
+ * 128 query rows per KV head).  Workspace: hs_workspace_size(HS_OP_FULL_ATTN_LOGITS, ...). */
 hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const void* k,
                                   const void* v, void* o, float* lse, float* logits, void* ws,
                                   size_t ws_bytes, void* stream);
@@ -237,7 +239,9 @@ hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logit
 
 /* hs_full_attn_fwd over a paged K / V cache (always the split row kernel: meant for decode),
  * optionally keeping the logits like hs_full_attn_fwd_logits (logits may be NULL).  Same o, lse
- * (and logits) as the contiguous call on the same logical cache.  Workspace:
+ * (and logits) as the contiguous call on the same logical cache, bit for bit, except for groups
+ * of 32-64 heads, whose contiguous call runs the group kernel: there the logits are identical
+ * and o, lse agree to rounding (other split boundaries).  Workspace:
  * hs_workspace_size(HS_OP_FULL_ATTN_PAGED, desc, page_size, 0). */
 hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
                                  const void* v_pool, const hs_kv_pages* pages, void* o, float* lse,
@@ -245,7 +249,9 @@ hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const 
 
 /* hs_sparse_attn_gather_ex over a paged K / V cache (token and block index sets address logical
  * positions; the sliding-window branch keeps its own position-indexed or ring cache).  Same
- * outputs as the contiguous call.  Workspace: HS_OP_SPARSE_ATTN, as the contiguous call. */
+ * outputs as the contiguous call (bit for bit; to rounding for groups of 32-64 heads, whose
+ * contiguous call runs the group kernel).  Workspace: HS_OP_SPARSE_ATTN, as the contiguous
+ * call (that size covers both). */
 hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
                                       const void* v_pool, const hs_kv_pages* pages,
                                       hs_index_kind kind, const int32_t* idx,
