@@ -149,3 +149,46 @@ def test_unsupported_combinations_are_rejected():
         hs().oracle_topk(x["q"], x["k"], lse, 64, 16)  # Q/K selection: g and d too large
     with pytest.raises(hs().HsError):
         hs().block_score_topk(x["q"], x["k"], lse, 64, 4)
+
+
+@pytest.mark.parametrize("with_sink", [False, True], ids=["no_sink", "sink"])
+def test_group_kernel_empty_and_partial_index_sets(with_sink):
+    """Token sets of 64 heads on one KV head (the group kernel): a set with count 0 attends over
+    nothing (output 0; LSE -inf, or the sink when there is one), a set with a few entries and -1
+    padding inside its count as usual."""
+    wl = Workload("ge", 2, 2, 1500, 64, 1, 256, "bf16", k_global=200, window=32, seed=741)
+    x = make_inputs(wl, device="cuda", n_sparse=1)
+    qn, kn, vn = (to_numpy_f32(x[n]) for n in ("q", "k", "v"))
+    oi, oc = oracle.token_topk(qn, kn, None, wl.k_global, wl.window)
+    oc = oc.copy()
+    oc[1, 0, 0] = 0                       # empty set
+    # padding inside the count: the GPU skips those entries; the oracle, whose sets hold valid
+    # positions only, gets the same set without them
+    gi = oi.copy()
+    gi[0, 1, 0, 3:7] = -1
+    n = oc[0, 1, 0]
+    oi = oi.copy()
+    oi[0, 1, 0, :n - 4] = np.concatenate([oi[0, 1, 0, :3], oi[0, 1, 0, 7:n]])
+    oi[0, 1, 0, n - 4:] = -1
+    gc = oc.copy()
+    oc[0, 1, 0] = n - 4
+    sink = torch.randn(wl.n_q_heads, generator=torch.Generator().manual_seed(742)) if with_sink else None
+    qs = x["q_sparse"][0]
+    o, lse = hs().sparse_attn_gather(qs, x["k"], x["v"], torch.from_numpy(gi).cuda(),
+                                     torch.from_numpy(gc).cuda(), kind="token",
+                                     out_dtype=torch.float32, want_lse=True,
+                                     sink=None if sink is None else sink.cuda())
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    o_ref, lse_ref = oracle.masked_attention(to_numpy_f32(qs), kn, vn, oi, oc,
+                                             sink=None if sink is None else sink.numpy())
+    assert (o[1, 0] == 0).all()
+    if sink is None:
+        assert np.isneginf(lse[1, :, 0]).all()
+    else:
+        assert np.allclose(lse[1, :, 0], sink.numpy(), rtol=0, atol=1e-6)
+    keep = np.ones(o.shape[:2], dtype=bool)
+    keep[1, 0] = False
+    assert max_abs(o[keep], o_ref[keep]) <= TOL_BF16
+    lk = np.isfinite(lse_ref)
+    assert max_abs(lse[lk], lse_ref[lk]) <= 2e-6
