@@ -246,13 +246,15 @@ TkLayout tk_layout(const Shape& s, const TkGeom& t) {
 size_t tk_ws(const Shape& s, const TkGeom& t) { return tk_layout(s, t).total; }
 
 // Token selection from stored logits: one (b, t, u) row per workgroup and key chunk (chunks of
-// at least 1024 keys, multiples of 256); the selection passes are those of tk_geom.
+// at least 256 keys, multiples of 256: with few rows, e.g. MQA, a thread then reads the g head
+// values of one key instead of several keys one after the other); the selection passes are
+// those of tk_geom.
 TkGeom tl_geom(const Shape& s) {
   TkGeom t = tk_geom(s);
   t.q_per_set = 1;
   t.sets_per_bu = s.Tq;
   long long want = (1024 + (long long)t.rows - 1) / (long long)t.rows;
-  const long long most = (s.Tk + 1023) / 1024;
+  const long long most = (s.Tk + 255) / 256;
   if (want > most) want = most;
   if (want < 1) want = 1;
   long long kps = (s.Tk + want - 1) / want;
