@@ -164,3 +164,27 @@ def test_status_strings():
     L = hs.lib()
     for s in (0, -1, -2, -3, -4):
         assert L.hs_status_string(s).decode()
+
+
+def test_large_group_workspace_sizes():
+    """Groups of 64 heads on one KV head (d 256): full attention with and without logits runs the
+    group kernel (one size); the paged calls run the row kernel; the sparse size covers both
+    sparse paths; a workspace one byte short is refused before anything is enqueued."""
+    L = hs.lib()
+    d = desc(batch=8, kv_len=32768, n_q_heads=64, n_kv_heads=1, head_dim=256)
+    fa = L.hs_workspace_size(hs.HS_OP_FULL_ATTN, ctypes.byref(d), 0, 0)
+    assert fa > 0 and fa == L.hs_workspace_size(hs.HS_OP_FULL_ATTN_LOGITS, ctypes.byref(d), 0, 0)
+    assert L.hs_workspace_size(hs.HS_OP_FULL_ATTN_PAGED, ctypes.byref(d), 64, 0) > 0
+    sp = L.hs_workspace_size(hs.HS_OP_SPARSE_ATTN, ctypes.byref(d), 1152, 0)
+    sp_gated = L.hs_workspace_size(hs.HS_OP_SPARSE_ATTN, ctypes.byref(d), 1024, 128)
+    assert sp > 0 and sp_gated > 0
+    assert L.hs_full_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fa - 1,
+                              None) == hs.HS_ERR_WORKSPACE
+    assert L.hs_sparse_attn_gather(ctypes.byref(d), FAKE, FAKE, FAKE, hs.HS_IDX_TOKEN, FAKE, FAKE,
+                                   1152, 1, None, FAKE, None, FAKE, sp - 1,
+                                   None) == hs.HS_ERR_WORKSPACE
+    pages = hs.KvPages(0x1000, 64, 512, 4096)
+    assert L.hs_sparse_attn_gather_paged(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(pages),
+                                         hs.HS_IDX_TOKEN, FAKE, FAKE, 1152, 1, None, None, FAKE,
+                                         None, None, 0, None) == hs.HS_ERR_WORKSPACE
+    assert "workspace" in L.hs_last_error().decode()
