@@ -395,25 +395,26 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
       }
     }
     // one matrix instruction between every few vector ones: S(t+1) with the exponentials of
-    // S(t), then O += V(t) P(t) with the rest
+    // S(t), then O += V(t) P(t) with the rest (4 and 2 VALU per MFMA measured best: 3 to 8
+    // tried, and no hints at all 5 % slower)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 12; i++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 14; i++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
     kahan_add(l_s, l_c, psum);
     store_k(t & 1);
