@@ -281,6 +281,8 @@ def main():
                                            args.cpu_seconds)
         if not args.no_prefill:
             out["cpu_baseline_prefill"] = cpu_baseline_prefill(out.get("prefill"))
+        if not args.no_block_prefill:
+            out["cpu_baseline_block"] = cpu_baseline_block(out.get("block_prefill"))
     print(json.dumps(out), flush=True)
 
 
@@ -728,6 +730,38 @@ def cpu_baseline_prefill(gpu_prefill, n_rows=8):
            f"rows of {wl.name}, full attention + token top-k, {t:.1f} s", "extrapolated_s": round(est, 1)}
     if gpu_prefill:
         gpu_s = (gpu_prefill["full_attn_ms"] + gpu_prefill["topk_ms"]) * 1e-3
+        out["gpu_s"] = round(gpu_s, 4)
+        out["gpu_speedup_extrapolated"] = round(est / gpu_s, 1)
+    return out
+
+
+def cpu_baseline_block(gpu_block, n_rows=8):
+    """The oracle on a fixed sample of query rows of the 64k block workload (full attention and
+    the block top-16 for rows spread over the 65536 queries, first and last included, every
+    batch entry), extrapolated by rows and set against the GPU's one-pass time for both."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs, to_numpy_f32
+
+    wl = WORKLOADS["block_7b_64k"]
+    x = make_inputs(wl, device=torch.device("cuda:0"), n_sparse=0)
+    q, k, v = (to_numpy_f32(x[n]) for n in ("q", "k", "v"))
+    del x
+    torch.cuda.empty_cache()
+    rows = np.linspace(0, wl.q_len - 1, n_rows).round().astype(np.int32)
+    t0 = time.perf_counter()
+    _, lse = oracle.full_attention(q, k, v, rows=rows)
+    oracle.block_topk(q, k, lse, wl.block, wl.n_blocks, rows=rows)
+    t = time.perf_counter() - t0
+    # the sampled rows are spread evenly over the causal range, so their mean length is the mean
+    est = t * wl.q_len / n_rows
+    out = {"kind": "oracle", "cores": oracle.threads(), "sample": f"{n_rows} of {wl.q_len} query "
+           f"rows of {wl.name}, every batch entry, full attention + block top-{wl.n_blocks}, "
+           f"{t:.1f} s", "extrapolated_s": round(est, 1)}
+    if gpu_block:
+        gpu_s = gpu_block["one_pass_ms"] * 1e-3
         out["gpu_s"] = round(gpu_s, 4)
         out["gpu_speedup_extrapolated"] = round(est / gpu_s, 1)
     return out
