@@ -74,16 +74,17 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// LDS of the BSEL merge: per wave 32 rows x 16 list entries, then 16 x 16 kept entries and 16
-// selected ids.
+// LDS of the BSEL merge: per wave 32 rows x 16 list entries, then kKeptMax kept entries (one
+// query's whole union: g x 16 with g up to 32) and 16 selected ids.
+constexpr int kKeptMax = 32 * 16;
 constexpr int kMergeCandBytes = (kThreads / 64) * 32 * 16 * 8;
-constexpr int kMergeBytes = kMergeCandBytes + (kThreads / 64) * (16 * 16 + 8) * 8;
+constexpr int kMergeBytes = kMergeCandBytes + (kThreads / 64) * (kKeptMax + 8) * 8;
 
 // BSEL epilogue of one wave (32 rows = 32/g whole queries, since g divides 32): normalize every
 // row's list with its LSE, then per query keep the best n of the union of its g lists, one
 // entry per block (its group maximum), and write them in ascending block order.  The score key
 // is the one of the selection kernels: a * scale_log2 - (LSE * log2(e) - C), C an integer per
-// query taken from its first head.  cand_all: 32 x 16 entries per wave; kept_all: 16 x 16
+// query taken from its first head.  cand_all: 32 x 16 entries per wave; kept_all: kKeptMax
 // entries plus 16 ints per wave (LDS the tile loop no longer uses).
 template <int kSlots>
 __device__ __forceinline__ void select_blocks(const PrefillParams& p,
@@ -94,8 +95,8 @@ __device__ __forceinline__ void select_blocks(const PrefillParams& p,
   const int rj = lane & 31, h = lane >> 5;
   const int hh = (wave * 32 + rj) % p.g;
   unsigned long long* cand = cand_all + wave * (32 * 16);
-  unsigned long long* kept = kept_all + wave * (16 * 16 + 8);
-  int* sel = (int*)(kept + 16 * 16);
+  unsigned long long* kept = kept_all + wave * (kKeptMax + 8);
+  int* sel = (int*)(kept + kKeptMax);
   const float lse0 = __shfl(lse_row, (rj - hh) + 32 * h, 64);  // first head of this query
   const double l2 = (double)lse_row * 1.4426950408889634;
   const double Cq = rint((double)lse0 * 1.4426950408889634);

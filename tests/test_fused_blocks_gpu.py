@@ -50,6 +50,9 @@ CASES = [
                              seed=307)),
     ("fused_g16_causal_ragged", Workload("fr", 1, 333, 333, 32, 2, 128, "bf16", block=64,
                                          n_blocks=16, seed=308)),
+    # 32 heads per KV head: one query's rows fill a whole wave
+    ("fused_g32_n8", Workload("f32g", 1, 20, 1500, 64, 2, 128, "bf16", block=64, n_blocks=8,
+                              seed=309)),
     # two passes
     ("decode_g4_b64", Workload("d4", 2, 1, 9000, 32, 8, 128, "bf16", block=64, n_blocks=16,
                                seed=311)),
