@@ -216,32 +216,39 @@ __device__ __forceinline__ RowSel row_sel(const TopkDecodeParams& p, int row) {
 }
 
 // Scanning a 2048-bin histogram from the top bin down, find the bin that holds the k-th largest
-// element and the rank (1-based) of that element inside the bin.  Wave 0 does the scan with
-// lane shuffles; every thread of the workgroup must call it (it synchronizes).
-__device__ void find_bin(const uint32_t* h, int k, int* bin_out, int* k_out) {
+// element and the rank (1-based) of that element inside the bin.  Wave 0 searches in two
+// parallel steps: each lane sums a group of 32 bins and a scan over the lanes finds the group,
+// then 32 lanes take one bin each of that group and a second scan finds the bin.  Every thread
+// of the workgroup must call it (it synchronizes).  k is at least 1 and at most the total.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = __shfl_up(v, off, 64);
+    if (lane >= off) v += x;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void find_bin(const uint32_t* h, int k, int* bin_out, int* k_out) {
   __shared__ int res[2];
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int top = kBins - 32 * lane;  // lane owns bins [top-32, top), lane 0 the highest
     uint32_t s = 0;
+#pragma unroll
     for (int q = 1; q <= 32; q++) s += h[top - q];
-    uint32_t incl = s;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t x = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += x;
-    }
-    const uint32_t excl = incl - s;
-    if ((long long)excl < k && (long long)k <= (long long)incl) {
-      uint32_t cum = excl;
-      for (int q = 1; q <= 32; q++) {
-        const uint32_t c = h[top - q];
-        if ((long long)cum + c >= k) {
-          res[0] = top - q;
-          res[1] = k - (int)cum;
-          break;
-        }
-        cum += c;
-      }
+    const uint32_t incl = wave_incl_scan(s, lane);
+    const unsigned long long mg = __ballot(incl >= (uint32_t)k);
+    const int gl = mg ? __ffsll((long long)mg) - 1 : 63;  // the group holding the k-th
+    const uint32_t base = __shfl(incl - s, gl, 64);      // elements in higher groups
+    const int gtop = kBins - 32 * gl;
+    const uint32_t c = lane < 32 ? h[gtop - 1 - lane] : 0u;  // lane i: the group's i-th bin from the top
+    const uint32_t ci = wave_incl_scan(c, lane);
+    const unsigned long long mb = __ballot(lane < 32 && base + ci >= (uint32_t)k);
+    const int bl = mb ? __ffsll((long long)mb) - 1 : 31;
+    if (lane == bl) {
+      res[0] = gtop - 1 - bl;
+      res[1] = k - (int)(base + ci - c);
     }
   }
   __syncthreads();
@@ -255,11 +262,15 @@ __device__ void find_bin(const uint32_t* h, int k, int* bin_out, int* k_out) {
 __global__ __launch_bounds__(256) void tk_collect_kernel(TopkDecodeParams p) {
   __shared__ uint32_t scan[256];
   __shared__ uint32_t base_sh, above_sh;
+  __shared__ uint32_t hist[kBins];
   const int split = blockIdx.x, row = blockIdx.y;
   const RowSel rs = row_sel(p, row);
   if (rs.k_eff == 0) return;
+  // the bin search reads the histogram bin by bin: from LDS, not over the memory latency
+  for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = p.hist[(size_t)row * kBins + i];
+  __syncthreads();
   int b1, k1;
-  find_bin(p.hist + (size_t)row * kBins, rs.k_eff, &b1, &k1);
+  find_bin(hist, rs.k_eff, &b1, &k1);
   const long long k_begin = (long long)split * p.keys_per_sel;
   long long k_end = k_begin + p.keys_per_sel;
   if (k_end > rs.n_cand) k_end = rs.n_cand;
@@ -307,8 +318,10 @@ __global__ __launch_bounds__(256) void tk_finalize_kernel(TopkDecodeParams p) {
   const int row = blockIdx.x;
   const RowSel rs = row_sel(p, row);
   if (rs.k_eff == 0) return;
+  for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = p.hist[(size_t)row * kBins + i];
+  __syncthreads();
   int b1, k1;
-  find_bin(p.hist + (size_t)row * kBins, rs.k_eff, &b1, &k1);
+  find_bin(hist, rs.k_eff, &b1, &k1);  // ends with a barrier: hist is free again below
   const int m = (int)p.bcount[row];
   const unsigned long long* bl = p.blist + (size_t)row * p.Tk;
   if (m <= kStage) {
@@ -410,15 +423,167 @@ __global__ __launch_bounds__(256) void tk_write_kernel(TopkDecodeParams p) {
   }
 }
 
+// ---- 2-4 in one workgroup per row (rows of at most kSelMaxTiles tiles) --------------------
+// The row's keys are staged in LDS, one tile of kSelTile keys at a time (longer rows reload the
+// tile per pass).  Below the 11-bit bin b1 the remaining 21 key bits are resolved by two LDS
+// histograms (bits 20..10, then 9..0), which give the exact key threshold T and the number k3
+// of keys equal to T that are taken.  Keys equal to T are taken in position order, so the rule
+// is the same as the chain's: key > T, or key == T among the first k3 such keys (ties go to
+// the lower position).  The ordered compaction needs the counts of keys above T and equal to T
+// before each position: per lane over its 32 consecutive keys, then one scan over the wave's
+// lanes and one over the 16 waves.  Every pass is a short loop over LDS: the kernel runs once
+// per row, so its code is fetched cold and is kept small.  Positions past the row's
+// candidates are staged as key 0, which no finite score maps to (the smallest finite key is
+// 0x00800000), so 0 marks "no candidate" in every pass.
+constexpr int kSelThreads = 1024;
+constexpr int kSelKeys = 32;                       // keys per lane in the compaction
+constexpr int kSelTile = kSelThreads * kSelKeys;   // 32768 keys
+constexpr int kSelStride = kSelKeys + 1;           // LDS words per lane segment: conflict-free
+constexpr uint32_t kAllTies = 0xFFFFFFFFu;         // every key equal to T is taken
+
+__device__ __forceinline__ int sel_slot(int i) { return i + (i >> 5); }  // key i of a tile
+
+__global__ __launch_bounds__(kSelThreads) void tk_select_kernel(TopkDecodeParams p) {
+  __shared__ uint32_t tile_keys[kSelThreads * kSelStride];
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t wsum[kSelThreads / 64];  // per wave: above | ties << 16
+  const int row = blockIdx.x;
+  const RowSel rs = row_sel(p, row);
+  int32_t* out = p.idx + (size_t)row * p.cap;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {
+    // window positions after the k_eff selected candidates, then padding and the count
+    const long long w0 = rs.t - p.window + 1 > 0 ? rs.t - p.window + 1 : 0;
+    const int n_win = (int)(rs.t - w0 + 1);
+    for (int i = tid; i < p.cap - rs.k_eff; i += kSelThreads)
+      out[rs.k_eff + i] = i < n_win ? (int32_t)(w0 + i) : -1;
+    if (tid == 0) p.cnt[row] = rs.k_eff + n_win;
+  }
+  if (rs.k_eff == 0) return;
+  const int n_cand = (int)rs.n_cand;
+  const int n_tiles = (n_cand + kSelTile - 1) / kSelTile;
+  // buffer descriptor over the row's keys, its range rounded up to whole 16-byte loads (the
+  // at most 3 words past the row lie in the workspace): a load is wholly inside or returns 0
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.keys + (size_t)row * p.Tk), 0, ((n_cand + 3) & ~3) * 4, 0x00020000);
+  // stage tile `tile`: thread t loads keys 4096 r + 4 t .. + 3 of the tile (coalesced)
+  auto stage = [&](int tile) __attribute__((always_inline)) {
+    u32x4 v[kSelKeys / 4];
+#pragma unroll
+    for (int r = 0; r < kSelKeys / 4; r++)
+      v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rsrc, (tile * kSelTile + 4096 * r + 4 * tid) * 4, 0, 0));
+#pragma unroll
+    for (int r = 0; r < kSelKeys / 4; r++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int i = 4096 * r + 4 * tid + e;
+        tile_keys[sel_slot(i)] = tile * kSelTile + i < n_cand ? v[r][e] : 0u;
+      }
+  };
+  const uint32_t* my = tile_keys + tid * kSelStride;  // this lane's 32 consecutive keys
+
+  stage(0);
+  // the row's top-11-bit histogram, scanned from LDS
+  for (int i = tid; i < kBins; i += kSelThreads) hist[i] = p.hist[(size_t)row * kBins + i];
+  __syncthreads();
+  int b1, k1;
+  find_bin(hist, rs.k_eff, &b1, &k1);
+  uint32_t T = (uint32_t)b1 << 21, k3 = kAllTies;
+  bool more = hist[b1] != (uint32_t)k1;
+  // up to two radix levels: bits 20..10 under prefix b1, then bits 9..0 under prefix T >> 10
+  int k = k1;
+  for (int level = 0; level < 2 && more; level++) {
+    const int shift = level == 0 ? 10 : 0, hi = level == 0 ? 21 : 10;
+    const uint32_t prefix = T >> hi, mask = level == 0 ? 0x7FFu : 0x3FFu;
+    __syncthreads();  // every thread is done with hist
+    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int tile = 0; tile < n_tiles; tile++) {
+      if (tile > 0 || level > 0) {
+        if (n_tiles > 1) {
+          __syncthreads();
+          stage(tile);
+          __syncthreads();
+        }
+      }
+#pragma unroll 4
+      for (int j = 0; j < kSelKeys; j++) {
+        const uint32_t key = my[j];
+        if (key != 0u && (key >> hi) == prefix) atomicAdd(&hist[(key >> shift) & mask], 1u);
+      }
+    }
+    __syncthreads();
+    int bin, kb;
+    find_bin(hist, k, &bin, &kb);
+    T |= (uint32_t)bin << shift;
+    if (level == 1) k3 = (uint32_t)kb;
+    more = hist[bin] != (uint32_t)kb;
+    k = kb;
+  }
+
+  // ordered compaction
+  uint32_t carry_a = 0, carry_q = 0;  // keys above T and ties over earlier tiles
+  const uint32_t k_eff = (uint32_t)rs.k_eff;  // bounds every slot, whatever the keys hold
+  for (int tile = 0; tile < n_tiles; tile++) {
+    if (n_tiles > 1) {
+      __syncthreads();
+      stage(tile);
+      __syncthreads();
+    }
+    uint32_t c = 0;  // above | ties << 16 (a tile has 32768 keys)
+#pragma unroll 8
+    for (int j = 0; j < kSelKeys; j++) {
+      const uint32_t key = my[j];
+      c += (key > T ? 1u : 0u) + (key == T ? 0x10000u : 0u);
+    }
+    const uint32_t incl = wave_incl_scan(c, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = incl - c, total = 0;
+    for (int w = 0; w < kSelThreads / 64; w++) {
+      const uint32_t x = wsum[w];
+      if (w < wave) before += x;
+      total += x;
+    }
+    uint32_t ia = carry_a + (before & 0xFFFFu), iq = carry_q + (before >> 16);
+    carry_a += total & 0xFFFFu;
+    carry_q += total >> 16;
+    const int first = tile * kSelTile + kSelKeys * tid;
+#pragma unroll 4
+    for (int j = 0; j < kSelKeys; j++) {
+      const uint32_t key = my[j];
+      const uint32_t slot = ia + (iq < k3 ? iq : k3);
+      if ((key > T || (key == T && iq < k3)) && slot < k_eff) out[slot] = first + j;
+      ia += key > T;
+      iq += key == T;
+    }
+    __syncthreads();  // wsum is rewritten by the next tile
+  }
+}
+
+// Steps 2-4: one workgroup per row while a row spans at most kSelMaxTiles tiles (each
+// workgroup then reads its keys at most three times); longer rows, whose few workgroups would
+// leave most of the GPU idle, take the chain of collect / finalize / write over key chunks.
+constexpr int kSelMaxTiles = 4;
+
+void launch_select(const TopkDecodeParams& p, size_t rows, hipStream_t stream) {
+  if ((long long)p.Tk <= (long long)kSelMaxTiles * kSelTile) {
+    tk_select_kernel<<<dim3((unsigned)rows), kSelThreads, 0, stream>>>(p);
+    return;
+  }
+  tk_collect_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
+  tk_finalize_kernel<<<dim3((unsigned)rows), 256, p.sel_split * sizeof(uint32_t), stream>>>(p);
+  tk_write_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
+}
+
 template <int D, bool F32>
 hipError_t launch_tk(const TopkDecodeParams& p, hipStream_t stream) {
   const size_t rows = (size_t)p.B * p.Tq * p.Hkv;
   const size_t zero_words = rows * kBins + rows;  // first histograms, then boundary counters
   zero_u32_kernel<<<(unsigned)((zero_words + 255) / 256 < 1024 ? (zero_words + 255) / 256 : 1024), 256, 0, stream>>>(p.hist, zero_words);
   tk_score_kernel<D, F32><<<dim3(p.n_split * p.B * p.Hkv * p.sets_per_bu), 256, 0, stream>>>(p);
-  tk_collect_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
-  tk_finalize_kernel<<<dim3((unsigned)rows), 256, p.sel_split * sizeof(uint32_t), stream>>>(p);
-  tk_write_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
+  launch_select(p, rows, stream);
   return hipGetLastError();
 }
 
@@ -428,9 +593,7 @@ hipError_t launch_tk_logits(const TopkDecodeParams& p, hipStream_t stream) {
   const size_t zero_words = rows * kBins + rows;
   zero_u32_kernel<<<(unsigned)((zero_words + 255) / 256 < 1024 ? (zero_words + 255) / 256 : 1024), 256, 0, stream>>>(p.hist, zero_words);
   tk_logit_score_kernel<G><<<dim3((unsigned)(p.n_split * rows)), 256, 0, stream>>>(p);
-  tk_collect_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
-  tk_finalize_kernel<<<dim3((unsigned)rows), 256, p.sel_split * sizeof(uint32_t), stream>>>(p);
-  tk_write_kernel<<<dim3(p.sel_split, rows), 256, 0, stream>>>(p);
+  launch_select(p, rows, stream);
   return hipGetLastError();
 }
 

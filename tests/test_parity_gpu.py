@@ -135,9 +135,14 @@ TOPK_CASES = [
                                          k_global=1024, window=128, seed=25)),
     ("prefill_g8_d64_small_k", Workload("pf8", 2, 100, 3000, 16, 2, 64, "bf16", k_global=50,
                                         window=10, seed=26)),
-    # longer than 65536 keys: the multi-kernel boundary-list selection
+    # one workgroup per row over 3 and 4 key tiles of 32768 (ragged last tiles), and past
+    # 131072 keys the multi-kernel boundary-list selection
     ("decode_g4_70k", Workload("dl", 1, 1, 70000, 32, 8, 128, "bf16", k_global=300, window=64,
                                needles=8, seed=27)),
+    ("decode_g4_131k", Workload("d4t", 1, 1, 131072, 8, 2, 128, "bf16", k_global=1024,
+                                window=128, needles=8, seed=31)),
+    ("decode_g4_140k_chain", Workload("dch", 1, 1, 140000, 8, 2, 128, "bf16", k_global=1024,
+                                      window=128, needles=8, seed=32)),
     # degenerate budgets: no forced window; window only (k_global = 0)
     ("decode_g4_no_window", Workload("dnw", 2, 1, 3000, 16, 4, 128, "bf16", k_global=200,
                                      window=0, seed=28)),
