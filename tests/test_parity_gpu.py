@@ -143,6 +143,9 @@ TOPK_CASES = [
                                 window=128, needles=8, seed=31)),
     ("decode_g4_140k_chain", Workload("dch", 1, 1, 140000, 8, 2, 128, "bf16", k_global=1024,
                                       window=128, needles=8, seed=32)),
+    # fewer candidates than k: every candidate is taken
+    ("decode_g4_all_candidates", Workload("dall", 2, 1, 1000, 16, 4, 128, "bf16", k_global=1024,
+                                          window=128, seed=33)),
     # degenerate budgets: no forced window; window only (k_global = 0)
     ("decode_g4_no_window", Workload("dnw", 2, 1, 3000, 16, 4, 128, "bf16", k_global=200,
                                      window=0, seed=28)),
@@ -172,6 +175,33 @@ def test_oracle_topk_matches_oracle(name, wl):
             for u in range(wl.n_kv_heads):
                 sel = set(idx[b, -1, u, :cnt[b, -1, u]].cpu().tolist())
                 assert set(x["needle_pos"][b, u].tolist()) <= sel
+
+
+def test_decode_selection_ties_across_key_tiles():
+    """Exact ties spread over three 32768-key tiles of one decode row: the lowest positions win,
+    so the cut falls inside the second tile after all of the first tile's copies."""
+    wl = Workload("tiet", 1, 1, 70000, 8, 2, 128, "bf16", k_global=100, window=64, seed=62)
+    say("[topk ties across tiles]")
+    x = make_inputs(wl)
+    k = x["k"].clone()
+    qh = x["q"][0, -1, 0].float()
+    needle = (8.0 * 128 ** 0.5 * qh / (qh * qh).sum()).to(k.dtype)
+    copies = list(range(32700, 32820)) + list(range(65600, 65631))  # 68 + 52 + 31 copies
+    k[0, copies, 0] = needle
+    qn, kn = to_numpy_f32(x["q"]), to_numpy_f32(k)
+    q_d, k_d, v_d = to_dev(x["q"]), to_dev(k), to_dev(x["v"])
+    _, lse = hs().full_attn_fwd(q_d, k_d, v_d)
+    idx, cnt = hs().oracle_topk(q_d, k_d, lse, wl.k_global, wl.window)
+    torch.cuda.synchronize()
+    _, lse_ref = oracle.full_attention(qn, kn, to_numpy_f32(x["v"]))
+    oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    want = np.array(copies[:100])
+    assert np.array_equal(oi[0, 0, 0, :100], want)
+    assert np.array_equal(gi[0, 0, 0, :100], want)
+    excused = check_token_sets(gi, gc, oi, oc, qn, kn, lse_ref, wl.k_global, wl.window,
+                               wl.q_offset)
+    say(f"  near-tie differences excused: {excused}")
 
 
 @pytest.mark.parametrize("q_len", [1, 33])
