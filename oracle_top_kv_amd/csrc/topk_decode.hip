@@ -429,22 +429,21 @@ __global__ __launch_bounds__(256) void tk_write_kernel(TopkDecodeParams p) {
 // histograms (bits 20..10, then 9..0), which give the exact key threshold T and the number k3
 // of keys equal to T that are taken.  Keys equal to T are taken in position order, so the rule
 // is the same as the chain's: key > T, or key == T among the first k3 such keys (ties go to
-// the lower position).  The ordered compaction needs the counts of keys above T and equal to T
-// before each position: per lane over its 32 consecutive keys, then one scan over the wave's
-// lanes and one over the 16 waves.  Every pass is a short loop over LDS: the kernel runs once
-// per row, so its code is fetched cold and is kept small.  Positions past the row's
-// candidates are staged as key 0, which no finite score maps to (the smallest finite key is
-// 0x00800000), so 0 marks "no candidate" in every pass.
+// the lower position).  Each lane owns 32 consecutive keys of the tile: a pass reads them in 8
+// LDS loads and turns them into 32-bit masks (keys in the bin being refined; keys above T and
+// equal to T), so that the per-key work (histogram atomics, ordered writes) runs over set bits
+// only; slots come from mask popcounts plus one scan over the wave's lanes and one over the 16
+// waves.  The kernel has few workgroups (one per row), so its instruction count per key sets
+// its time.  Positions past the row's candidates are staged as key 0, which no finite score
+// maps to (the smallest finite key is 0x00800000) and which lies below every bin refined.
 constexpr int kSelThreads = 1024;
-constexpr int kSelKeys = 32;                       // keys per lane in the compaction
+constexpr int kSelKeys = 32;                       // keys per lane
 constexpr int kSelTile = kSelThreads * kSelKeys;   // 32768 keys
-constexpr int kSelStride = kSelKeys + 1;           // LDS words per lane segment: conflict-free
+constexpr int kSelStride = kSelKeys + 4;           // LDS words per lane: 16-byte reads, no conflicts
 constexpr uint32_t kAllTies = 0xFFFFFFFFu;         // every key equal to T is taken
 
-__device__ __forceinline__ int sel_slot(int i) { return i + (i >> 5); }  // key i of a tile
-
 __global__ __launch_bounds__(kSelThreads) void tk_select_kernel(TopkDecodeParams p) {
-  __shared__ uint32_t tile_keys[kSelThreads * kSelStride];
+  __shared__ __attribute__((aligned(16))) uint32_t tile_keys[kSelThreads * kSelStride];
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wsum[kSelThreads / 64];  // per wave: above | ties << 16
   const int row = blockIdx.x;
@@ -466,7 +465,8 @@ __global__ __launch_bounds__(kSelThreads) void tk_select_kernel(TopkDecodeParams
   // at most 3 words past the row lie in the workspace): a load is wholly inside or returns 0
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.keys + (size_t)row * p.Tk), 0, ((n_cand + 3) & ~3) * 4, 0x00020000);
-  // stage tile `tile`: thread t loads keys 4096 r + 4 t .. + 3 of the tile (coalesced)
+  // stage tile `tile`: thread t loads keys 4096 r + 4 t .. + 3 of the tile (coalesced) and
+  // stores them as key i at word 36 (i / 32) + i % 32
   auto stage = [&](int tile) __attribute__((always_inline)) {
     u32x4 v[kSelKeys / 4];
 #pragma unroll
@@ -474,14 +474,30 @@ __global__ __launch_bounds__(kSelThreads) void tk_select_kernel(TopkDecodeParams
       v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            rsrc, (tile * kSelTile + 4096 * r + 4 * tid) * 4, 0, 0));
 #pragma unroll
-    for (int r = 0; r < kSelKeys / 4; r++)
+    for (int r = 0; r < kSelKeys / 4; r++) {
+      const int i = 4096 * r + 4 * tid;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int i = 4096 * r + 4 * tid + e;
-        tile_keys[sel_slot(i)] = tile * kSelTile + i < n_cand ? v[r][e] : 0u;
-      }
+      for (int e = 0; e < 4; e++)
+        if (tile * kSelTile + i + e >= n_cand) v[r][e] = 0u;
+      *(u32x4*)(&tile_keys[(i >> 5) * kSelStride + (i & 31)]) = v[r];
+    }
   };
   const uint32_t* my = tile_keys + tid * kSelStride;  // this lane's 32 consecutive keys
+  auto mine = [&](uint32_t (&kk)[kSelKeys]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < kSelKeys / 4; m++) {
+      const u32x4 v = *(const u32x4*)(my + 4 * m);
+#pragma unroll
+      for (int e = 0; e < 4; e++) kk[4 * m + e] = v[e];
+    }
+  };
+  auto restage = [&](int tile) __attribute__((always_inline)) {
+    if (n_tiles > 1) {
+      __syncthreads();  // every lane is done with the previous tile
+      stage(tile);
+      __syncthreads();
+    }
+  };
 
   stage(0);
   // the row's top-11-bit histogram, scanned from LDS
@@ -500,17 +516,16 @@ __global__ __launch_bounds__(kSelThreads) void tk_select_kernel(TopkDecodeParams
     for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
     __syncthreads();
     for (int tile = 0; tile < n_tiles; tile++) {
-      if (tile > 0 || level > 0) {
-        if (n_tiles > 1) {
-          __syncthreads();
-          stage(tile);
-          __syncthreads();
-        }
-      }
-#pragma unroll 4
-      for (int j = 0; j < kSelKeys; j++) {
-        const uint32_t key = my[j];
-        if (key != 0u && (key >> hi) == prefix) atomicAdd(&hist[(key >> shift) & mask], 1u);
+      if (tile > 0 || level > 0) restage(tile);
+      uint32_t kk[kSelKeys];
+      mine(kk);
+      uint32_t in_bin = 0;
+#pragma unroll
+      for (int j = 0; j < kSelKeys; j++) in_bin |= ((kk[j] >> hi) == prefix ? 1u : 0u) << j;
+      while (in_bin) {
+        const int j = __builtin_ctz(in_bin);
+        in_bin &= in_bin - 1u;
+        atomicAdd(&hist[(my[j] >> shift) & mask], 1u);
       }
     }
     __syncthreads();
@@ -526,17 +541,16 @@ __global__ __launch_bounds__(kSelThreads) void tk_select_kernel(TopkDecodeParams
   uint32_t carry_a = 0, carry_q = 0;  // keys above T and ties over earlier tiles
   const uint32_t k_eff = (uint32_t)rs.k_eff;  // bounds every slot, whatever the keys hold
   for (int tile = 0; tile < n_tiles; tile++) {
-    if (n_tiles > 1) {
-      __syncthreads();
-      stage(tile);
-      __syncthreads();
-    }
-    uint32_t c = 0;  // above | ties << 16 (a tile has 32768 keys)
-#pragma unroll 8
+    restage(tile);
+    uint32_t kk[kSelKeys];
+    mine(kk);
+    uint32_t ma = 0, mq = 0;  // this lane's keys above T, equal to T
+#pragma unroll
     for (int j = 0; j < kSelKeys; j++) {
-      const uint32_t key = my[j];
-      c += (key > T ? 1u : 0u) + (key == T ? 0x10000u : 0u);
+      ma |= (kk[j] > T ? 1u : 0u) << j;
+      mq |= (kk[j] == T ? 1u : 0u) << j;
     }
+    const uint32_t c = (uint32_t)__popc(ma) + ((uint32_t)__popc(mq) << 16);  // tile: < 2^16 each
     const uint32_t incl = wave_incl_scan(c, lane);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
@@ -546,17 +560,18 @@ __global__ __launch_bounds__(kSelThreads) void tk_select_kernel(TopkDecodeParams
       if (w < wave) before += x;
       total += x;
     }
-    uint32_t ia = carry_a + (before & 0xFFFFu), iq = carry_q + (before >> 16);
+    const uint32_t ia = carry_a + (before & 0xFFFFu), iq = carry_q + (before >> 16);
     carry_a += total & 0xFFFFu;
     carry_q += total >> 16;
     const int first = tile * kSelTile + kSelKeys * tid;
-#pragma unroll 4
-    for (int j = 0; j < kSelKeys; j++) {
-      const uint32_t key = my[j];
-      const uint32_t slot = ia + (iq < k3 ? iq : k3);
-      if ((key > T || (key == T && iq < k3)) && slot < k_eff) out[slot] = first + j;
-      ia += key > T;
-      iq += key == T;
+    uint32_t todo = ma | mq;
+    while (todo) {
+      const int j = __builtin_ctz(todo);
+      todo &= todo - 1u;
+      const uint32_t below = (1u << j) - 1u;
+      const uint32_t qa = iq + (uint32_t)__popc(mq & below);  // ties before key j
+      const uint32_t slot = ia + (uint32_t)__popc(ma & below) + (qa < k3 ? qa : k3);
+      if ((((ma >> j) & 1u) || qa < k3) && slot < k_eff) out[slot] = first + j;
     }
     __syncthreads();  // wsum is rewritten by the next tile
   }
