@@ -38,7 +38,8 @@
  *     a combine).  Anything else returns HS_ERR_UNSUPPORTED.
  *   - Workspace sizes, for orientation: token selection with many query rows per KV head and
  *     k_global <= 1024 keeps a 16 KiB candidate buffer per (b, t, u); with few rows it keeps
- *     12 bytes per candidate key per (b, t, u) plus small histograms; split attention keeps
+ *     4 bytes per candidate key per (b, t, u) plus an 8 KiB histogram (12 bytes per key past
+ *     131072 keys, where a boundary list joins them); split attention keeps
  *     per-split partial rows (about 0.5 KiB each).  Full attention with many query rows and the
  *     prefill-shaped block selection need none.
  */

@@ -231,14 +231,16 @@ TkLayout tk_layout(const Shape& s, const TkGeom& t) {
   o += align_up(t.rows * (size_t)s.Tk * 4, 256);
   L.hist = o;  // histograms, then the boundary counters (zeroed together)
   o += align_up((t.rows * 2048 + t.rows) * 4, 256);
+  // the rest only for rows long enough to take the multi-kernel chain
+  const bool chain = hs::topk_decode_uses_chain(s.Tk);
   L.blist = o;
-  o += align_up(t.rows * (size_t)s.Tk * 8, 256);
+  o += chain ? align_up(t.rows * (size_t)s.Tk * 8, 256) : 0;
   L.above = o;
-  o += align_up(t.rows * (size_t)t.sel_split * 4, 256);
+  o += chain ? align_up(t.rows * (size_t)t.sel_split * 4, 256) : 0;
   L.counts = o;
-  o += align_up(t.rows * (size_t)t.sel_split * 4, 256);
+  o += chain ? align_up(t.rows * (size_t)t.sel_split * 4, 256) : 0;
   L.state = o;
-  o += align_up(t.rows * 2 * 4, 256);
+  o += chain ? align_up(t.rows * 2 * 4, 256) : 0;
   L.total = o;
   return L;
 }

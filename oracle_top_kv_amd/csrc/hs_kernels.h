@@ -140,6 +140,10 @@ struct TopkDecodeParams {
 };
 hipError_t launch_topk_decode(const TopkDecodeParams& p, int head_dim, bool in_f32,
                               hipStream_t stream);
+// Whether rows of Tk keys take the chain of collect / finalize / write over key chunks, which
+// needs the boundary list, the per-chunk counts and the threshold state; shorter rows are
+// selected by one workgroup per row, which needs only the keys and the histograms.
+bool topk_decode_uses_chain(long long Tk);
 hipError_t launch_topk_from_logits(const TopkDecodeParams& p, hipStream_t stream);
 
 // ---- block scores + top-n blocks ----------------------------------------------------------

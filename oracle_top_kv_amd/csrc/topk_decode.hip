@@ -583,7 +583,7 @@ __global__ __launch_bounds__(kSelThreads) void tk_select_kernel(TopkDecodeParams
 constexpr int kSelMaxTiles = 4;
 
 void launch_select(const TopkDecodeParams& p, size_t rows, hipStream_t stream) {
-  if ((long long)p.Tk <= (long long)kSelMaxTiles * kSelTile) {
+  if (!topk_decode_uses_chain(p.Tk)) {
     tk_select_kernel<<<dim3((unsigned)rows), kSelThreads, 0, stream>>>(p);
     return;
   }
@@ -613,6 +613,8 @@ hipError_t launch_tk_logits(const TopkDecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool topk_decode_uses_chain(long long Tk) { return Tk > (long long)kSelMaxTiles * kSelTile; }
 
 hipError_t launch_topk_from_logits(const TopkDecodeParams& p, hipStream_t stream) {
   switch (p.g) {

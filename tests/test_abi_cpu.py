@@ -78,6 +78,21 @@ def test_workspace_too_small_is_reported():
     assert rc == hs.HS_ERR_WORKSPACE
 
 
+def test_decode_topk_workspace_by_row_length():
+    """Decode token selection: rows of up to 131072 keys need the keys (4 bytes each) and the
+    histograms only; longer rows also hold the boundary list (8 bytes per key)."""
+    rows = 8 * 8
+    short = desc(batch=8, kv_len=32768, n_q_heads=32, n_kv_heads=8)
+    need = hs.lib().hs_workspace_size(hs.HS_OP_ORACLE_TOPK, ctypes.byref(short), 1024, 128)
+    assert rows * 32768 * 4 + rows * 2049 * 4 <= need <= rows * 32768 * 4 + rows * 2049 * 4 + 4096
+    edge = desc(batch=8, kv_len=131072, n_q_heads=32, n_kv_heads=8)
+    need = hs.lib().hs_workspace_size(hs.HS_OP_ORACLE_TOPK, ctypes.byref(edge), 1024, 128)
+    assert need < rows * 131072 * 5
+    long_ = desc(batch=8, kv_len=131073, n_q_heads=32, n_kv_heads=8)
+    need = hs.lib().hs_workspace_size(hs.HS_OP_ORACLE_TOPK, ctypes.byref(long_), 1024, 128)
+    assert need >= rows * 131073 * 12
+
+
 def test_topk_argument_checks():
     d = desc()
     L = hs.lib()
