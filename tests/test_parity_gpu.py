@@ -146,6 +146,12 @@ TOPK_CASES = [
     # fewer candidates than k: every candidate is taken
     ("decode_g4_all_candidates", Workload("dall", 2, 1, 1000, 16, 4, 128, "bf16", k_global=1024,
                                           window=128, seed=33)),
+    # decode rows with no candidates: window only (k_global = 0), and a context shorter than
+    # the window
+    ("decode_g4_window_only", Workload("dwo", 2, 1, 3000, 16, 4, 128, "bf16", k_global=0,
+                                       window=40, seed=34)),
+    ("decode_g4_short_context", Workload("dsc", 1, 1, 100, 8, 2, 128, "bf16", k_global=1024,
+                                         window=128, seed=35)),
     # degenerate budgets: no forced window; window only (k_global = 0)
     ("decode_g4_no_window", Workload("dnw", 2, 1, 3000, 16, 4, 128, "bf16", k_global=200,
                                      window=0, seed=28)),
