@@ -275,12 +275,18 @@ __global__ __launch_bounds__(256) void tk_collect_kernel(TopkDecodeParams p) {
   long long k_end = k_begin + p.keys_per_sel;
   if (k_end > rs.n_cand) k_end = rs.n_cand;
   const uint32_t* keys = p.keys + (size_t)row * p.Tk;
-  // pass 1: per-thread counts of keys above b1 and inside b1
+  // pass 1: per-thread counts of keys above b1 and inside b1 (8 loads in flight per trip)
   uint32_t above = 0, inside = 0;
-  for (long long i = k_begin + threadIdx.x; i < k_end; i += 256) {
-    const uint32_t d = keys[i] >> 21;
-    above += d > (uint32_t)b1;
-    inside += d == (uint32_t)b1;
+  for (long long i0 = k_begin + threadIdx.x; i0 < k_end; i0 += 8 * 256) {
+    uint32_t d[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) d[r] = i0 + 256 * r < k_end ? keys[i0 + 256 * r] >> 21 : 0u;
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const bool ok = i0 + 256 * r < k_end;
+      above += ok && d[r] > (uint32_t)b1;
+      inside += ok && d[r] == (uint32_t)b1;
+    }
   }
   // exclusive scan of `inside` over the workgroup; one global reservation per workgroup
   scan[threadIdx.x] = inside;
@@ -298,11 +304,17 @@ __global__ __launch_bounds__(256) void tk_collect_kernel(TopkDecodeParams p) {
   // pass 2: write this thread's boundary entries (key << 32 | ~position)
   unsigned long long* bl = p.blist + (size_t)row * p.Tk;
   uint32_t slot = base_sh + scan[threadIdx.x] - inside;
-  for (long long i = k_begin + threadIdx.x; i < k_end && inside; i += 256) {
-    const uint32_t key = keys[i];
-    if ((key >> 21) == (uint32_t)b1) {
-      bl[slot++] = ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
-      inside--;
+  for (long long i0 = k_begin + threadIdx.x; i0 < k_end && inside; i0 += 8 * 256) {
+    uint32_t kv[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) kv[r] = i0 + 256 * r < k_end ? keys[i0 + 256 * r] : 0u;
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const long long i = i0 + 256 * r;
+      if (i < k_end && (kv[r] >> 21) == (uint32_t)b1) {
+        bl[slot++] = ((unsigned long long)kv[r] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)i);
+        inside--;
+      }
     }
   }
   if (threadIdx.x == 0) p.above[(size_t)row * p.sel_split + split] = above_sh;
@@ -404,22 +416,31 @@ __global__ __launch_bounds__(256) void tk_write_kernel(TopkDecodeParams p) {
   if (k_end > rs.n_cand) k_end = rs.n_cand;
   const uint32_t* keys = p.keys + (size_t)row * p.Tk;
   const unsigned long long lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (long long i0 = k_begin; i0 < k_end; i0 += 256) {
-    const long long i = i0 + threadIdx.x;
-    const uint32_t key = i < k_end ? keys[i] : 0u;
-    const bool take = i < k_end && (key > T || (key == T && (uint32_t)i <= pos_star));
-    const unsigned long long bt = __ballot(take);
-    if (lane == 0) wsum[wave] = __popcll(bt);
-    __syncthreads();
-    uint32_t t_prev = 0, t_all = 0;
-    for (int w = 0; w < 4; w++) {
-      if (w < wave) t_prev += wsum[w];
-      t_all += wsum[w];
+  for (long long j0 = k_begin; j0 < k_end; j0 += 8 * 256) {
+    uint32_t kv[8];  // the next 8 rounds' keys, loaded together
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const long long i = j0 + 256 * r + threadIdx.x;
+      kv[r] = i < k_end ? keys[i] : 0u;
     }
-    const long long slot = off + t_prev + __popcll(bt & lower);
-    if (take && slot < rs.k_eff) out[slot] = (int32_t)i;
-    off += t_all;
-    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const long long i = j0 + 256 * r + threadIdx.x;
+      const uint32_t key = kv[r];
+      const bool take = i < k_end && (key > T || (key == T && (uint32_t)i <= pos_star));
+      const unsigned long long bt = __ballot(take);
+      if (lane == 0) wsum[wave] = __popcll(bt);
+      __syncthreads();
+      uint32_t t_prev = 0, t_all = 0;
+      for (int w = 0; w < 4; w++) {
+        if (w < wave) t_prev += wsum[w];
+        t_all += wsum[w];
+      }
+      const long long slot = off + t_prev + __popcll(bt & lower);
+      if (take && slot < rs.k_eff) out[slot] = (int32_t)i;
+      off += t_all;
+      __syncthreads();
+    }
   }
 }
 
