@@ -23,6 +23,10 @@
 //   4. write: ordered compaction per chunk (key > T, or key == T at a position <= the cut)
 //      into the index list, which is therefore ascending; the window positions follow; -1
 //      padding to the cap.
+// Rows of at most 131072 keys run steps 2-4 in one workgroup per row instead (tk_select_kernel:
+// the row's keys staged in LDS, two LDS radix levels below b1, then the same ordered
+// compaction); only longer rows, whose few workgroups would leave the GPU idle, take 2-4 as
+// separate kernels over key chunks.
 // All steps are exact: nothing is dropped by an approximation.
 #include "hs_device.h"
 #include "hs_kernels.h"
