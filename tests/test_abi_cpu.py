@@ -203,3 +203,21 @@ def test_large_group_workspace_sizes():
                                          hs.HS_IDX_TOKEN, FAKE, FAKE, 1152, 1, None, None, FAKE,
                                          None, None, 0, None) == hs.HS_ERR_WORKSPACE
     assert "workspace" in L.hs_last_error().decode()
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: without the built library every entry point raises instead of computing."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (f"import sys; sys.path.insert(0, {root!r})\n"
+            "from oracle_top_kv_amd import hs\n"
+            f"hs.LIB_PATH = {str(tmp_path / 'absent.so')!r}\n"
+            "try:\n"
+            "    hs.lib()\n"
+            "    print('loaded')\n"
+            "except RuntimeError as e:\n"
+            "    print('raised', 'missing' in str(e))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         timeout=300)
+    assert "raised True" in out.stdout, out.stdout + out.stderr
