@@ -183,6 +183,46 @@ def test_oracle_topk_matches_oracle(name, wl):
                 assert set(x["needle_pos"][b, u].tolist()) <= sel
 
 
+def _decode_sweep_cases():
+    """Seeded decode shapes for the token selection: contexts from a few hundred keys to past
+    131072 (one to five 32768-key tiles, ragged, and the tile edges themselves), every group
+    size of the decode path, budgets from 0 to past the candidate count, windows 0 to 128."""
+    tks = [300, 32768, 32769, 32896, 65536 + 3, 98304, 131072, 131200, 5000, 20000, 77777, 1200]
+    ks = [2000, 1024, 17, 1, 256, 1024, 1024, 1024, 2000, 300, 0, 64]
+    ws = [0, 128, 1, 64, 1, 128, 128, 0, 64, 1, 128, 128]
+    cases = []
+    for i, tk in enumerate(tks):
+        g = [4, 8, 16][i % 3]
+        hkv = [1, 2, 4][(i // 3) % 3]
+        tq = 2 if g <= 8 and i % 2 else 1
+        d = 64 if i % 4 == 3 else 128
+        k, w = ks[i], ws[i]
+        b = 1 + i % 3
+        name = f"sweep{i}_b{b}_tq{tq}_tk{tk}_g{g}_hkv{hkv}_d{d}_k{k}_w{w}"
+        cases.append((name, Workload(f"sw{i}", b, tq, tk, g * hkv, hkv, d, "bf16", k_global=k,
+                                     window=w, seed=400 + i)))
+    return cases
+
+
+SWEEP_CASES = _decode_sweep_cases()
+
+
+@pytest.mark.parametrize("name,wl", SWEEP_CASES, ids=[c[0] for c in SWEEP_CASES])
+def test_decode_token_selection_sweep(name, wl):
+    say(f"[topk sweep] {name}")
+    x = make_inputs(wl)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    _, lse = hs().full_attn_fwd(q, k, v, out_dtype=torch.float32)
+    idx, cnt = hs().oracle_topk(q, k, lse, wl.k_global, wl.window)
+    torch.cuda.synchronize()
+    qn, kn = to_numpy_f32(x["q"]), to_numpy_f32(x["k"])
+    _, lse_ref = oracle.full_attention(qn, kn, to_numpy_f32(x["v"]))
+    oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
+    excused = check_token_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, qn, kn, lse_ref,
+                               wl.k_global, wl.window, wl.q_offset)
+    say(f"  near-tie differences excused: {excused}")
+
+
 def test_decode_selection_ties_across_key_tiles():
     """Exact ties spread over three 32768-key tiles of one decode row: the lowest positions win,
     so the cut falls inside the second tile after all of the first tile's copies."""
