@@ -89,6 +89,24 @@ def test_full_attn_block_topk_matches_oracle(name, wl):
         say(f"  identical to the separate selection: {same}")
 
 
+# Seeded sweep of the one-pass form: every group size it takes (1-32), both head sizes, ragged
+# query counts, budgets 1-16, causal from position 0 and long prefixes.
+#            g   hkv  d    Tq   Tk    n   b
+SWEEP = [(1, 4, 128, 17, 900, 16, 1), (2, 2, 64, 61, 61, 3, 2), (4, 1, 128, 129, 2000, 1, 1),
+         (8, 2, 64, 33, 1500, 13, 1), (16, 1, 128, 300, 300, 8, 1), (32, 1, 128, 4, 2100, 16, 2),
+         (32, 2, 64, 9, 777, 5, 1), (16, 2, 64, 70, 3000, 16, 1), (8, 1, 128, 257, 257, 2, 1),
+         (4, 4, 64, 100, 1100, 11, 2), (2, 1, 128, 200, 1600, 7, 1), (1, 2, 64, 40, 4000, 16, 1)]
+SWEEP_CASES = [(f"sweep{i}_g{g}_hkv{h}_d{d}_tq{tq}_tk{tk}_n{n}_b{b}",
+                Workload(f"fs{i}", b, tq, tk, g * h, h, d, "bf16", block=64, n_blocks=n,
+                         seed=500 + i))
+               for i, (g, h, d, tq, tk, n, b) in enumerate(SWEEP)]
+
+
+@pytest.mark.parametrize("name,wl", SWEEP_CASES, ids=[c[0] for c in SWEEP_CASES])
+def test_full_attn_block_topk_sweep(name, wl):
+    test_full_attn_block_topk_matches_oracle(name, wl)
+
+
 def test_fused_block_selection_keeps_lower_block_on_exact_ties():
     """Blocks whose maxima are exactly equal (copied key rows): the lower block ids win, as in
     the oracle, although the running list sees the tied blocks one tile at a time."""
