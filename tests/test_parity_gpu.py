@@ -336,6 +336,16 @@ SPARSE_CASES = [
                                           k_global=500, window=64, seed=37)),
     ("decode_g1_token", Workload("dg1", 2, 1, 3000, 8, 8, 128, "bf16", seed=38)),
     ("prefill_g2_token", Workload("pg2", 1, 30, 1500, 4, 2, 128, "bf16", seed=39)),
+    # head size 256 on the row kernel, and groups of 32 / 64 heads (the group kernel) with
+    # several queries
+    ("decode_g8_d256_token", Workload("d256", 2, 1, 2000, 16, 2, 256, "bf16", k_global=300,
+                                      window=32, seed=40)),
+    ("prefill_g4_d256_token", Workload("p256", 1, 20, 900, 8, 2, 256, "bf16", k_global=200,
+                                       window=16, seed=41)),
+    ("decode_g32_d128_token", Workload("d32", 2, 1, 2500, 64, 2, 128, "bf16", k_global=400,
+                                       window=64, seed=42)),
+    ("prefill_g64_d256_token", Workload("p64", 1, 5, 1000, 64, 1, 256, "bf16", k_global=300,
+                                        window=32, seed=43)),
 ]
 
 
