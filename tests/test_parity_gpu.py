@@ -48,6 +48,11 @@ FULL_CASES = [
     ("prefill_bf16_g1", Workload("pg1", 1, 300, 500, 4, 4, 128, "bf16", seed=18)),
     ("prefill_bf16_g2_d64", Workload("pg2", 2, 130, 400, 8, 4, 64, "bf16", seed=19)),
     ("prefill_bf16_g12", Workload("pg12", 1, 40, 600, 24, 2, 128, "bf16", seed=20)),
+    # head size 256 with small groups: the 4-wave row kernel, also for prefill-shaped calls
+    ("decode_bf16_g4_d256", Workload("d256", 2, 1, 3000, 8, 2, 256, "bf16", seed=21)),
+    ("prefill_bf16_g8_d256", Workload("p256", 1, 30, 1200, 16, 2, 256, "bf16", seed=22)),
+    ("prefill_bf16_g16_d256_causal", Workload("p256c", 1, 150, 150, 16, 1, 256, "bf16",
+                                              seed=23)),
 ]
 
 
