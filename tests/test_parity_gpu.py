@@ -307,6 +307,11 @@ BLOCK_CASES = [
                                          n_blocks=40, seed=58)),
     ("decode_g8_b64_64blocks", Workload("bd64", 2, 1, 6000, 32, 4, 128, "bf16", block=64,
                                         n_blocks=64, seed=59)),
+    # blocks that are multiples of 16 but do not divide 64 (the generic path in both shapes)
+    ("decode_g4_b48", Workload("b48", 2, 1, 5000, 16, 4, 128, "bf16", block=48, n_blocks=20,
+                               seed=60)),
+    ("prefill_g8_b80_generic", Workload("b80", 1, 25, 2000, 16, 2, 64, "bf16", block=80,
+                                        n_blocks=9, seed=61)),
 ]
 
 
