@@ -640,9 +640,32 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const float* m = p.m[br];
     // row maximum over splits (every thread, redundantly)
     constexpr int kBatch = 8;
+    // unbatched: a thread folds at most two splits (sl and sl + SP); their loads are issued
+    // before the row maximum is known (a split past the end reads split 0, weighted 0)
+    float m2[2];
+    f32x4 o2[2];
+    double l2[2];
+    if constexpr (!BATCHED) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int s = sl + i * SP;
+        const size_t prow = ((size_t)(s < ns ? s : 0) * n_sets + set) * 16 + r;
+        m2[i] = m[prow];
+        o2[i] = *(const f32x4*)(p.po[br] + prow * D + 4 * c);
+        l2[i] = p.l[br][prow];
+        if (s >= ns) m2[i] = -INFINITY;
+      }
+    }
     float M = -INFINITY;
     if constexpr (!BATCHED) {
-      for (int s = 0; s < ns; s++) M = fmaxf(M, m[((size_t)s * n_sets + set) * 16 + r]);
+      int s = 0;
+      for (; s + 4 <= ns; s += 4) {  // four loads per wait
+        float mb[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) mb[i] = m[((size_t)(s + i) * n_sets + set) * 16 + r];
+        M = fmaxf(M, fmaxf(fmaxf(mb[0], mb[1]), fmaxf(mb[2], mb[3])));
+      }
+      for (; s < ns; s++) M = fmaxf(M, m[((size_t)s * n_sets + set) * 16 + r]);
     } else {
       for (int s = 0; s < ns; s += kBatch) {
         float mb[kBatch];
@@ -656,13 +679,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     double lacc = 0.0;
     if (M != -INFINITY && !BATCHED) {
-      for (int s = sl; s < ns; s += SP) {
-        const size_t prow = ((size_t)s * n_sets + set) * 16 + r;
-        const float ms = m[prow];
-        if (ms == -INFINITY) continue;
-        const f32x4 o4 = *(const f32x4*)(p.po[br] + prow * D + 4 * c);
-        acc += fast_exp2(ms - M) * o4;
-        if (c == 0) lacc += exp2((double)ms - (double)M) * p.l[br][prow];
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        if (m2[i] == -INFINITY) continue;
+        acc += fast_exp2(m2[i] - M) * o2[i];
+        if (c == 0) lacc += exp2((double)m2[i] - (double)M) * l2[i];
       }
     } else if (M != -INFINITY) {  // a split past the end reads split s, weighted 0
       for (int s = sl; s < ns; s += kBatch * SP) {
