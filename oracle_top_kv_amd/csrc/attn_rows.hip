@@ -645,6 +645,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     float m2[2];
     f32x4 o2[2];
     double l2[2];
+    // batched: the first batch of this thread's splits (sl, sl + SP, ...), likewise loaded
+    // before the row maximum
+    float mb0[BATCHED ? kBatch : 1];
+    f32x4 ob0[BATCHED ? kBatch : 1];
+    double lb0[BATCHED ? kBatch : 1];
+    if constexpr (BATCHED) {
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) {
+        const int si = sl + i * SP;
+        const size_t prow = ((size_t)(si < ns ? si : 0) * n_sets + set) * 16 + r;
+        mb0[i] = si < ns ? m[prow] : -INFINITY;
+        ob0[i] = *(const f32x4*)(p.po[br] + prow * D + 4 * c);
+        lb0[i] = c == 0 ? p.l[br][prow] : 0.0;
+      }
+    }
     if constexpr (!BATCHED) {
 #pragma unroll
       for (int i = 0; i < 2; i++) {
@@ -686,7 +701,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
         if (c == 0) lacc += exp2((double)m2[i] - (double)M) * l2[i];
       }
     } else if (M != -INFINITY) {  // a split past the end reads split s, weighted 0
-      for (int s = sl; s < ns; s += kBatch * SP) {
+#pragma unroll
+      for (int i = 0; i < kBatch; i++) {
+        if (mb0[i] == -INFINITY) continue;
+        acc += fast_exp2(mb0[i] - M) * ob0[i];
+        if (c == 0) lacc += exp2((double)mb0[i] - (double)M) * lb0[i];
+      }
+      for (int s = sl + kBatch * SP; s < ns; s += kBatch * SP) {
         float mb[kBatch];
         f32x4 ob[kBatch];
         double lb[kBatch];
