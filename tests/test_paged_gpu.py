@@ -48,6 +48,7 @@ FA_CASES = [
     ("short_block_d64_p256", Workload("sb", 2, 3, 777, 8, 2, 64, "bf16", seed=603), 256),
     ("tiny_f32_p32", Workload("tf", 1, 64, 300, 4, 1, 64, "f32", seed=604), 32),
     ("decode_p1", Workload("p1", 1, 1, 700, 16, 4, 128, "bf16", seed=605), 1),
+    ("decode_g4_d256_p32", Workload("d256", 2, 1, 2000, 8, 2, 256, "bf16", seed=607), 32),
     # a long split: many pages staged per workgroup
     ("decode_g4_70k_p16", Workload("dl", 1, 1, 70000, 32, 8, 128, "bf16", seed=606), 16),
 ]
