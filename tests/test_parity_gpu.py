@@ -412,6 +412,16 @@ GATED_CASES = [
                                   window=32, seed=44)),
     ("prefill_fused_f32_d64", Workload("gf32", 1, 520, 600, 16, 4, 64, "f32", block=16,
                                        n_blocks=6, window=20, seed=45)),
+    # other group and head sizes: 16, 8 with d 64 and blocks of 32, d 256 (two branches and a
+    # combine), and a 32-head group with two queries
+    ("decode_g16", Workload("g16", 2, 1, 3000, 64, 4, 128, "bf16", block=64, n_blocks=16,
+                            window=64, seed=46)),
+    ("decode_g8_d64_b32", Workload("g8", 3, 1, 2500, 16, 2, 64, "bf16", block=32, n_blocks=12,
+                                   window=48, seed=47)),
+    ("decode_g4_d256", Workload("g256", 2, 1, 2000, 8, 2, 256, "bf16", block=64, n_blocks=8,
+                                window=64, seed=48)),
+    ("g32_two_queries", Workload("g32", 1, 2, 2000, 64, 2, 128, "bf16", block=64, n_blocks=8,
+                                 window=64, seed=49)),
 ]
 
 
