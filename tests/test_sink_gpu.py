@@ -59,6 +59,14 @@ TOKEN_CASES = [
      ("sink", "out_gate")),
     ("tiny_f32", Workload("st", 1, 64, 512, 4, 1, 64, "f32", k_global=64, window=16, seed=506),
      ("sink", "out_gate")),
+    # other group and head sizes: 16 heads at d 64, d 256 on the row kernel, 64 heads at d 256
+    # (the group kernel)
+    ("decode_g16_d64", Workload("s16", 2, 1, 2500, 64, 4, 64, "bf16", k_global=300, window=32,
+                                seed=507), ("sink", "out_gate")),
+    ("decode_g4_d256", Workload("s256", 2, 1, 2000, 8, 2, 256, "bf16", k_global=300, window=32,
+                                seed=508), ("sink", "out_gate")),
+    ("mqa64_d256_two_queries", Workload("sm", 1, 2, 1500, 64, 1, 256, "bf16", k_global=200,
+                                        window=32, seed=509), ("sink", "out_gate")),
 ]
 
 
