@@ -81,6 +81,9 @@ typedef enum {
 typedef struct {
   int32_t batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim;
   int64_t q_offset;   /* absolute position of query row 0; -1 means kv_len - q_len */
+  float scale;        /* logit scale tau in a = tau q.k; 0 means 1/sqrt(head_dim) [P2 attention
+                         equations]; finite and >= 0.  The calls of one hybrid block (full layer,
+                         selection, sparse layers) must use the same value. */
   hs_dtype in_dtype;  /* element type of Q, K, V (and K', V') */
   hs_dtype out_dtype; /* element type of O */
 } hs_attn_desc;
@@ -96,7 +99,8 @@ typedef struct {
 } hs_swa_branch;
 
 /* Full causal GQA attention, the full-attention layer of a hybrid block:
- *   a_{t,i} = q_t.k_i / sqrt(d),  O_t = sum_{i<=t} softmax_i(a) v_i,  LSE_t = ln sum_{i<=t} e^a
+ *   a_{t,i} = tau q_t.k_i (tau = desc->scale, by default 1/sqrt(d)),
+ *   O_t = sum_{i<=t} softmax_i(a) v_i,  LSE_t = ln sum_{i<=t} e^a
  * [P2 "Extracting block scores from exact attention", attention equations; P4 section 3.2].
  * q, k, v: in_dtype.  o: [B, q_len, Hq, d] out_dtype.  lse: [B, Hq, q_len] fp32, required (the
  * index-selection calls normalize logits with it). */
@@ -116,7 +120,7 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
 
 /* Block-level oracle index of HySparse [P2 "Extracting block scores from exact attention",
  * block-score and TopK equations; P2 "GQA: the group shares one index set"; P4 section 3.2 and
- * Algorithm 1 with the exp its line 14 omits].  Per (b, t, u): S_r = max over heads h and keys
+ * Algorithm 1, with the exponential its block-score normalization omits].  Per (b, t, u): S_r = max over heads h and keys
  * i in [rB, min(rB+B-1, t)] of exp(a^h_{t,i} - LSE^h_t), for the causal blocks r <= t/B; the
  * n_blocks best by (S desc, r asc).  blk_idx: [B, q_len, Hkv, n_blocks] int32 ascending, -1
  * padded; count: [B, q_len, Hkv] = min(n_blocks, t/B + 1). */
@@ -141,7 +145,9 @@ typedef struct {
   const float* out_gate;
   int32_t local_ring; /* 0: swa->k_local / v_local are position-indexed [B, kv_len, Hkv, d];
                          > 0: they are rings [B, local_ring, Hkv, d] holding position t in slot
-                         t % local_ring (local_ring >= window), the layer's own small cache
+                         t % local_ring, with local_ring >= window + q_len - 1 (every position a
+                         call's rows read in its own slot; else HS_ERR_INVALID_ARG), the
+                         layer's own small cache
                          [P2 "Why the local branch cannot reuse the same KV": each sparse layer
                          keeps its own K', V' only for a ring window of length w] */
 } hs_sparse_opts;
@@ -209,7 +215,7 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
  * array holds B * q_len * Hq * kv_len floats. */
 
 /* hs_full_attn_fwd that also stores every dot product q_t . k_i it computes (fp32, before the
- * 1/sqrt(d) scale) to logits: [B, q_len, Hq, kv_len] fp32, caller-owned, 4-byte aligned (16 for
+ * scale tau) to logits: [B, q_len, Hq, kv_len] fp32, caller-owned, 4-byte aligned (16 for
  * full-width stores).  Entries i <= t of query row t are the attention logits times sqrt(d);
  * entries past t are unspecified (those of the last query row's range are written, larger ones
  * not).  Always runs on the split row kernel (the group kernel for groups of 32-64 heads with
@@ -223,7 +229,7 @@ hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const
 
 /* hs_oracle_topk with the scores taken from logits (as stored by hs_full_attn_fwd_logits for the
  * same desc) and lse instead of Q and K: same index set, same layout and padding of idx and
- * count.  desc->in_dtype is not used; head_dim sets the 1/sqrt(d) scale.  Any group size
+ * count.  desc->in_dtype is not used; desc->scale (0: 1/sqrt(head_dim)) scales the logits.  Any group size
  * g <= 16.  Workspace: hs_workspace_size(HS_OP_TOPK_FROM_LOGITS, desc, k_global, window). */
 hs_status hs_oracle_topk_from_logits(const hs_attn_desc* desc, const float* logits,
                                      const float* lse, int32_t k_global, int32_t window,

@@ -22,7 +22,8 @@ _lib = None
 class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("q_offset", ctypes.c_int64)]
+                ("head_dim", ctypes.c_int32), ("q_offset", ctypes.c_int64),
+                ("scale", ctypes.c_double)]
 
 
 def lib():
@@ -62,13 +63,14 @@ def _i32(x):
     return a, a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _shape(q, k, q_offset):
+def _shape(q, k, q_offset, scale=None):
+    """scale: the logit scale tau (None: 1/sqrt(d))."""
     B, Tq, Hq, d = q.shape
     Bk, Tk, Hkv, dk = k.shape
     assert B == Bk and d == dk, "q/k shapes disagree"
     if q_offset is None:
         q_offset = Tk - Tq
-    return Shape(B, Tq, Tk, Hq, Hkv, d, int(q_offset))
+    return Shape(B, Tq, Tk, Hq, Hkv, d, int(q_offset), 0.0 if scale is None else float(scale))
 
 
 def _rows(rows):
@@ -83,10 +85,10 @@ def _check(rc, what):
         raise ValueError(f"oracle {what} failed with code {rc}")
 
 
-def full_attention(q, k, v, q_offset=None, rows=None):
+def full_attention(q, k, v, q_offset=None, rows=None, scale=None):
     """Exact causal GQA attention. Returns (o float64 [B,Tq,Hq,d], lse float64 [B,Hq,Tq]).
     With ``rows`` only those query rows are computed (others are NaN)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
     v, vp = _f32(v)
@@ -98,9 +100,9 @@ def full_attention(q, k, v, q_offset=None, rows=None):
     return o, lse
 
 
-def logit_row(q, k, b, j, h, q_offset=None):
+def logit_row(q, k, b, j, h, q_offset=None, scale=None):
     """Scaled logits a_{t,i} = q.k_i / sqrt(d), i = 0..t, of one (b, j, h)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
     t = s.q_offset + j
@@ -110,9 +112,9 @@ def logit_row(q, k, b, j, h, q_offset=None):
     return a
 
 
-def prob_row(q, k, b, j, h, lse=None, q_offset=None):
+def prob_row(q, k, b, j, h, lse=None, q_offset=None, scale=None):
     """Per-head normalized probabilities p_{t,i}, i = 0..t, of one (b, j, h)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
     t = s.q_offset + j
@@ -125,9 +127,9 @@ def prob_row(q, k, b, j, h, lse=None, q_offset=None):
     return p
 
 
-def token_score_row(q, k, lse, b, j, u, q_offset=None):
+def token_score_row(q, k, lse, b, j, u, q_offset=None, scale=None):
     """Token scores max_{h in group u} p^h_{t,i}, i = 0..t, of one (b, j, u)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
     t = s.q_offset + j
@@ -140,9 +142,9 @@ def token_score_row(q, k, lse, b, j, u, q_offset=None):
     return out
 
 
-def token_topk(q, k, lse, k_global, window, cap=None, q_offset=None, rows=None):
+def token_topk(q, k, lse, k_global, window, cap=None, q_offset=None, rows=None, scale=None):
     """Forced window plus top-k_global outside it. Returns (idx int32 [B,Tq,Hkv,cap], count)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     cap = k_global + window if cap is None else cap
     q, qp = _f32(q)
     k, kp = _f32(k)
@@ -164,11 +166,12 @@ def _opt_f32(x):
     return _f32(x)
 
 
-def masked_attention(q, k, v, idx, count, q_offset=None, rows=None, sink=None, out_gate=None):
+def masked_attention(q, k, v, idx, count, q_offset=None, rows=None, sink=None, out_gate=None,
+                     scale=None):
     """Attention of q over k, v restricted to each row's index set (dense masked softmax).
     sink: [Hq] per-head sink logits in the denominator; out_gate: [B,Tq,Hq] sigmoid output-gate
     logits.  Returns (o float64, lse float64; lse includes the sink)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
     v, vp = _f32(v)
@@ -186,9 +189,9 @@ def masked_attention(q, k, v, idx, count, q_offset=None, rows=None, sink=None, o
     return o, lse
 
 
-def block_score_row(q, k, lse, b, j, u, block, q_offset=None):
+def block_score_row(q, k, lse, b, j, u, block, q_offset=None, scale=None):
     """Group-max block scores of the causal blocks 0..floor(t/B) of one (b, j, u)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
     t = s.q_offset + j
@@ -201,9 +204,9 @@ def block_score_row(q, k, lse, b, j, u, block, q_offset=None):
     return out
 
 
-def block_topk(q, k, lse, block, n_blocks, q_offset=None, rows=None):
+def block_topk(q, k, lse, block, n_blocks, q_offset=None, rows=None, scale=None):
     """Top n_blocks causal blocks. Returns (blk_idx int32 [B,Tq,Hkv,n_blocks] ascending, count)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
     lp = None
@@ -219,11 +222,11 @@ def block_topk(q, k, lse, block, n_blocks, q_offset=None, rows=None):
 
 
 def gated_block_swa(q, k, v, blk_idx, count, block, k_loc, v_loc, window, gate, q_offset=None,
-                    rows=None, sink=None, sink_loc=None, out_gate=None):
+                    rows=None, sink=None, sink_loc=None, out_gate=None, scale=None):
     """HySparse sparse layer; sink / sink_loc: [Hq] sink logits of the two branches, out_gate:
     [B,Tq,Hq] sigmoid output-gate logits on the gated sum.  Returns (o, o_glob, o_loc), all
     float64 [B,Tq,Hq,d] (o_glob, o_loc: the normalized branches before the gates)."""
-    s = _shape(q, k, q_offset)
+    s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
     v, vp = _f32(v)

@@ -48,6 +48,7 @@ static int shape_ok(const orc_shape* s) {
     return 0;
   if (s->n_q_heads % s->n_kv_heads) return 0;
   if (s->q_offset < 0 || s->q_offset + s->q_len > s->kv_len) return 0;
+  if (!(s->scale >= 0.0)) return 0;
   return 1;
 }
 
@@ -72,14 +73,15 @@ static int64_t set_at(const orc_shape* s, int b, int j, int u) {
   return ((int64_t)b * s->q_len + j) * s->n_kv_heads + u;
 }
 
-/* Logits of one (b, j, h) against keys 0..t:  a_{t,i} = q_t . k_i / sqrt(d)
- * [P2 "Extracting block scores from exact attention", scaled dot-product equation]. */
+/* Logits of one (b, j, h) against keys 0..t:  a_{t,i} = tau q_t . k_i with tau = 1/sqrt(d)
+ * [P2 "Extracting block scores from exact attention", scaled dot-product equation], or the
+ * caller's scale when one is given (a model may fold another constant into tau). */
 static void logits_row(const orc_shape* s, const float* q, const float* k, int b, int j, int h,
                        double* a) {
   const int d = s->head_dim;
   const int u = h / (s->n_q_heads / s->n_kv_heads);
   const int64_t t = s->q_offset + j;
-  const double tau = 1.0 / sqrt((double)d);
+  const double tau = s->scale > 0.0 ? s->scale : 1.0 / sqrt((double)d);
   const float* qr = q + q_at(s, b, j, h);
   for (int64_t i = 0; i <= t; i++) {
     const float* kr = k + kv_at(s, b, i, u);

@@ -46,13 +46,15 @@ extern "C" {
 typedef struct {
   int32_t batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim;
   int64_t q_offset; /* absolute position of query row 0; q_offset + q_len <= kv_len */
+  double scale;     /* logit scale tau; 0 means 1/sqrt(head_dim) */
 } orc_shape;
 
 /* Worker threads used by the parallel row loops (0 = OpenMP default). Returns the count in use. */
 int orc_set_threads(int n);
 int orc_threads(void);
 
-/* Logits a_{t,i} = q_t . k_i / sqrt(d), i = 0..t, of one (b, j, h).  a must hold t+1 doubles. */
+/* Logits a_{t,i} = tau q_t . k_i (tau = scale, or 1/sqrt(d) when scale is 0), i = 0..t, of one
+ * (b, j, h).  a must hold t+1 doubles. */
 int orc_logit_row(const orc_shape* s, const float* q, const float* k, int b, int j, int h,
                   double* a);
 

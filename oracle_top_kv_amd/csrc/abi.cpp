@@ -36,6 +36,7 @@ struct Shape {
   int B, Tq, Tk, Hq, Hkv, D, g;
   long long q_off;
   bool in_f32, out_f32;
+  float scale_log2;  // logit scale times log2(e): the kernels work in base 2
 };
 
 hs_status check_desc(const hs_attn_desc* d, Shape* s) {
@@ -54,6 +55,9 @@ hs_status check_desc(const hs_attn_desc* d, Shape* s) {
   if (q_off < 0 || q_off + d->q_len > d->kv_len)
     return fail(HS_ERR_INVALID_ARG, "q_offset %lld with q_len %d does not fit kv_len %d", q_off,
                 d->q_len, d->kv_len);
+  if (!(d->scale >= 0.f) || !std::isfinite(d->scale))
+    return fail(HS_ERR_INVALID_ARG, "scale %g: must be finite and >= 0 (0: 1/sqrt(head_dim))",
+                (double)d->scale);
   const int g = d->n_q_heads / d->n_kv_heads;
   if (g > 64 || (g > 16 && g % 16))
     return fail(HS_ERR_UNSUPPORTED,
@@ -71,6 +75,8 @@ hs_status check_desc(const hs_attn_desc* d, Shape* s) {
   s->q_off = q_off;
   s->in_f32 = d->in_dtype == HS_F32;
   s->out_f32 = d->out_dtype == HS_F32;
+  const double tau = d->scale > 0.f ? (double)d->scale : 1.0 / std::sqrt((double)d->head_dim);
+  s->scale_log2 = (float)(1.4426950408889634 * tau);
   return HS_OK;
 }
 
@@ -139,7 +145,7 @@ hs::RowAttnParams ra_params(const Shape& s, const RaGeom& g) {
   p.sets_per_bu = g.sets_per_bu;
   p.n_split = g.n_split;
   p.steps_per_split = g.steps_per_split;
-  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  p.scale_log2 = s.scale_log2;
   p.out_f32 = s.out_f32;
   return p;
 }
@@ -198,7 +204,7 @@ struct TkGeom {
 
 TkGeom tk_geom(const Shape& s) {
   TkGeom t;
-  t.q_per_set = 16 / s.g;
+  t.q_per_set = s.g <= 16 ? 16 / s.g : 1;  // query rows packed per 16-row score set
   t.sets_per_bu = (s.Tq + t.q_per_set - 1) / t.q_per_set;
   const long long n_sets = (long long)s.B * s.Hkv * t.sets_per_bu;
   // four workgroups per resident slot: measured 5 us faster than one round on the 7B decode step
@@ -287,7 +293,7 @@ hs::TopkDecodeParams tk_params(const Shape& s, const TkGeom& t, const float* lse
   p.keys_per_split = t.keys_per_split;
   p.sel_split = t.sel_split;
   p.keys_per_sel = t.keys_per_sel;
-  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  p.scale_log2 = s.scale_log2;
   const TkLayout lay = tk_layout(s, t);
   char* w = (char*)ws;
   p.keys = (uint32_t*)(w + lay.keys);
@@ -327,7 +333,7 @@ hs::PrefillSelectParams select_params(const Shape& s, const void* q, const void*
   p.Hkv = s.Hkv;
   p.g = s.g;
   p.q_off = s.q_off;
-  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  p.scale_log2 = s.scale_log2;
   return p;
 }
 
@@ -573,7 +579,7 @@ hs::PrefillParams prefill_params(const Shape& s, const void* q, const void* k, c
   pp.Hkv = s.Hkv;
   pp.g = s.g;
   pp.q_off = s.q_off;
-  pp.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  pp.scale_log2 = s.scale_log2;
   pp.o = o;
   pp.lse = lse;
   pp.out_f32 = s.out_f32;
@@ -616,7 +622,7 @@ hs::BlockTopkParams bk_params(const Shape& s, const BkGeom& g, const float* lse,
   p.sets_per_bu = g.sets_per_bu;
   p.n_split = g.n_split;
   p.blocks_per_split = g.blocks_per_split;
-  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  p.scale_log2 = s.scale_log2;
   p.cand = (unsigned long long*)ws;
   p.blk_idx = blk_idx;
   p.cnt = count;
@@ -922,8 +928,12 @@ hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, c
     return fail(HS_ERR_INVALID_ARG, "sink_local given without a sliding-window branch");
   if (ring < 0 || (ring > 0 && !swa))
     return fail(HS_ERR_INVALID_ARG, "local_ring %d: needs a sliding-window branch", ring);
-  if (ring > 0 && ring < window)
-    return fail(HS_ERR_INVALID_ARG, "local_ring %d shorter than the window %d", ring, window);
+  // the q_len rows of one call read positions q_offset - window + 1 .. q_offset + q_len - 1,
+  // which must sit in distinct ring slots
+  if (ring > 0 && (long long)ring < (long long)window + s.Tq - 1)
+    return fail(HS_ERR_INVALID_ARG,
+                "local_ring %d shorter than window + q_len - 1 = %lld (window %d, q_len %d)",
+                ring, (long long)window + s.Tq - 1, window, s.Tq);
   const SparseGeom g = sparse_geom(s, keys, window, pages != nullptr);
   const size_t need = sparse_ws(s, g, window);
   if (need > 0 && (!ws || ws_bytes < need))

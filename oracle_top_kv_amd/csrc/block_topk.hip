@@ -1,6 +1,7 @@
 // block_topk.hip -- HySparse block-level oracle index [P2 "Extracting block scores from exact
 // attention", block-score and TopK equations; P2 "GQA: the group shares one index set";
-// P4 section 3.2 and Algorithm 1, with the exp that its line 14 omits].
+// P4 section 3.2 and Algorithm 1, whose normalization of the block maximum needs the
+// exponential that the printed algorithm leaves out, as P2 points out].
 //
 // Block score of causal block r for query row (b, t, u):
 //   S_r = max_{h in group u} max_{i in [rB, min(rB+B-1, t)]} exp(a^h_{t,i} - LSE^h_t),

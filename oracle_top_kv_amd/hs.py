@@ -31,7 +31,7 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("q_offset", ctypes.c_int64),
-                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+                ("scale", ctypes.c_float), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int)]
 
 
 class SwaBranch(ctypes.Structure):
@@ -133,14 +133,19 @@ def _need(t, name, device, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def make_desc(q, k, q_offset=None, out_dtype=None):
+def make_desc(q, k, q_offset=None, out_dtype=None, scale=None):
     B, Tq, Hq, d = q.shape
     Bk, Tk, Hkv, dk = k.shape
     if B != Bk or d != dk:
         raise ValueError("q and k shapes disagree")
     out = q.dtype if out_dtype is None else out_dtype
     return AttnDesc(B, Tq, Tk, Hq, Hkv, d, -1 if q_offset is None else int(q_offset),
-                    _dtype_code(q.dtype), _dtype_code(out))
+                    _scale(scale), _dtype_code(q.dtype), _dtype_code(out))
+
+
+def _scale(scale):
+    """The descriptor's logit scale: 0 asks for the default 1/sqrt(head_dim)."""
+    return 0.0 if scale is None else float(scale)
 
 
 def workspace(op, desc, p0=0, p1=0, device=None):
@@ -150,12 +155,12 @@ def workspace(op, desc, p0=0, p1=0, device=None):
     return torch.empty(n, dtype=torch.uint8, device=device), n
 
 
-def full_attn_fwd(q, k, v, q_offset=None, out_dtype=None):
+def full_attn_fwd(q, k, v, q_offset=None, out_dtype=None, scale=None):
     """Full causal GQA attention. Returns (o [B,Tq,Hq,d], lse fp32 [B,Hq,Tq])."""
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, dev, dtype=q.dtype)
-    desc = make_desc(q, k, q_offset, out_dtype)
+    desc = make_desc(q, k, q_offset, out_dtype, scale)
     o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
     lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
     ws, n = workspace(HS_OP_FULL_ATTN, desc, device=dev)
@@ -172,18 +177,18 @@ def _pages(k_pool, block_table, page_size, dev):
                    int(k_pool.shape[0]))
 
 
-def _paged_desc(q, k_pool, kv_len, q_offset, out_dtype):
+def _paged_desc(q, k_pool, kv_len, q_offset, out_dtype, scale=None):
     B, Tq, Hq, d = q.shape
     n_pages, P, Hkv, dk = k_pool.shape
     if d != dk:
         raise ValueError("q and the page pool disagree on head_dim")
     out = q.dtype if out_dtype is None else out_dtype
     return AttnDesc(B, Tq, int(kv_len), Hq, Hkv, d, -1 if q_offset is None else int(q_offset),
-                    _dtype_code(q.dtype), _dtype_code(out))
+                    _scale(scale), _dtype_code(q.dtype), _dtype_code(out))
 
 
 def full_attn_fwd_paged(q, k_pool, v_pool, block_table, kv_len, logits=False, q_offset=None,
-                        out_dtype=None):
+                        out_dtype=None, scale=None):
     """Full attention over a paged cache: k_pool, v_pool [n_pages, page_size, Hkv, d],
     block_table int32 [B, max_pages].  Returns (o, lse) or (o, lse, logits)."""
     dev = q.device
@@ -191,7 +196,7 @@ def full_attn_fwd_paged(q, k_pool, v_pool, block_table, kv_len, logits=False, q_
         _need(t, n, dev, dtype=q.dtype)
     if v_pool.shape != k_pool.shape:
         raise ValueError("k_pool and v_pool shapes differ")
-    desc = _paged_desc(q, k_pool, kv_len, q_offset, out_dtype)
+    desc = _paged_desc(q, k_pool, kv_len, q_offset, out_dtype, scale)
     pg = _pages(k_pool, block_table, k_pool.shape[1], dev)
     o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
     lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
@@ -204,13 +209,13 @@ def full_attn_fwd_paged(q, k_pool, v_pool, block_table, kv_len, logits=False, q_
     return (o, lse, lg) if logits else (o, lse)
 
 
-def full_attn_block_topk(q, k, v, block, n_blocks, q_offset=None, out_dtype=None):
+def full_attn_block_topk(q, k, v, block, n_blocks, q_offset=None, out_dtype=None, scale=None):
     """Full attention and the top n_blocks causal blocks in one call (one pass for prefill).
     Returns (o, lse, blk_idx int32 [B,Tq,Hkv,n_blocks], count)."""
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, dev, dtype=q.dtype)
-    desc = make_desc(q, k, q_offset, out_dtype)
+    desc = make_desc(q, k, q_offset, out_dtype, scale)
     B, Tq, Hq = q.shape[0], q.shape[1], q.shape[2]
     Hkv = k.shape[2]
     o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
@@ -225,13 +230,13 @@ def full_attn_block_topk(q, k, v, block, n_blocks, q_offset=None, out_dtype=None
     return o, lse, idx, cnt
 
 
-def full_attn_fwd_logits(q, k, v, q_offset=None, out_dtype=None):
+def full_attn_fwd_logits(q, k, v, q_offset=None, out_dtype=None, scale=None):
     """Full attention that also keeps its dot products q.k (decode).
     Returns (o, lse, logits fp32 [B,Tq,Hq,Tk]); logits past a row's position are unspecified."""
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, dev, dtype=q.dtype)
-    desc = make_desc(q, k, q_offset, out_dtype)
+    desc = make_desc(q, k, q_offset, out_dtype, scale)
     o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
     lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
     logits = torch.empty((q.shape[0], q.shape[1], q.shape[2], k.shape[1]), dtype=torch.float32,
@@ -243,19 +248,20 @@ def full_attn_fwd_logits(q, k, v, q_offset=None, out_dtype=None):
     return o, lse, logits
 
 
-def _logits_desc(logits, n_kv_heads, head_dim, q_offset):
+def _logits_desc(logits, n_kv_heads, head_dim, q_offset, scale=None):
     B, Tq, Hq, Tk = logits.shape
     return AttnDesc(B, Tq, Tk, Hq, int(n_kv_heads), int(head_dim),
-                    -1 if q_offset is None else int(q_offset), HS_F32, HS_F32)
+                    -1 if q_offset is None else int(q_offset), _scale(scale), HS_F32, HS_F32)
 
 
-def oracle_topk_from_logits(logits, lse, n_kv_heads, head_dim, k_global, window, q_offset=None):
+def oracle_topk_from_logits(logits, lse, n_kv_heads, head_dim, k_global, window, q_offset=None,
+                            scale=None):
     """oracle_topk from the logits kept by full_attn_fwd_logits. Returns (idx, count)."""
     dev = logits.device
     _need(logits, "logits", dev, dtype=torch.float32)
     B, Tq, Hq, Tk = logits.shape
     _need(lse, "lse", dev, dtype=torch.float32, shape=(B, Hq, Tq))
-    desc = _logits_desc(logits, n_kv_heads, head_dim, q_offset)
+    desc = _logits_desc(logits, n_kv_heads, head_dim, q_offset, scale)
     idx = torch.empty((B, Tq, n_kv_heads, k_global + window), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, Tq, n_kv_heads), dtype=torch.int32, device=dev)
     ws, n = workspace(HS_OP_TOPK_FROM_LOGITS, desc, k_global, window, device=dev)
@@ -266,13 +272,14 @@ def oracle_topk_from_logits(logits, lse, n_kv_heads, head_dim, k_global, window,
     return idx, cnt
 
 
-def block_topk_from_logits(logits, lse, n_kv_heads, head_dim, block, n_blocks, q_offset=None):
+def block_topk_from_logits(logits, lse, n_kv_heads, head_dim, block, n_blocks, q_offset=None,
+                           scale=None):
     """block_score_topk from the logits kept by full_attn_fwd_logits. Returns (blk_idx, count)."""
     dev = logits.device
     _need(logits, "logits", dev, dtype=torch.float32)
     B, Tq, Hq, Tk = logits.shape
     _need(lse, "lse", dev, dtype=torch.float32, shape=(B, Hq, Tq))
-    desc = _logits_desc(logits, n_kv_heads, head_dim, q_offset)
+    desc = _logits_desc(logits, n_kv_heads, head_dim, q_offset, scale)
     idx = torch.empty((B, Tq, n_kv_heads, n_blocks), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, Tq, n_kv_heads), dtype=torch.int32, device=dev)
     ws, n = workspace(HS_OP_BLOCK_TOPK_FROM_LOGITS, desc, block, n_blocks, device=dev)
@@ -283,13 +290,13 @@ def block_topk_from_logits(logits, lse, n_kv_heads, head_dim, block, n_blocks, q
     return idx, cnt
 
 
-def oracle_topk(q, k, lse, k_global, window, q_offset=None):
+def oracle_topk(q, k, lse, k_global, window, q_offset=None, scale=None):
     """Forced window plus top-k_global tokens. Returns (idx int32 [B,Tq,Hkv,k+w], count)."""
     dev = q.device
     _need(q, "q", dev)
     _need(k, "k", dev, dtype=q.dtype)
     _need(lse, "lse", dev, dtype=torch.float32, shape=(q.shape[0], q.shape[2], q.shape[1]))
-    desc = make_desc(q, k, q_offset)
+    desc = make_desc(q, k, q_offset, scale=scale)
     B, Tq, Hkv = q.shape[0], q.shape[1], k.shape[2]
     idx = torch.empty((B, Tq, Hkv, k_global + window), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
@@ -300,13 +307,13 @@ def oracle_topk(q, k, lse, k_global, window, q_offset=None):
     return idx, cnt
 
 
-def block_score_topk(q, k, lse, block, n_blocks, q_offset=None):
+def block_score_topk(q, k, lse, block, n_blocks, q_offset=None, scale=None):
     """Top n_blocks causal blocks. Returns (blk_idx int32 [B,Tq,Hkv,n_blocks], count)."""
     dev = q.device
     _need(q, "q", dev)
     _need(k, "k", dev, dtype=q.dtype)
     _need(lse, "lse", dev, dtype=torch.float32, shape=(q.shape[0], q.shape[2], q.shape[1]))
-    desc = make_desc(q, k, q_offset)
+    desc = make_desc(q, k, q_offset, scale=scale)
     B, Tq, Hkv = q.shape[0], q.shape[1], k.shape[2]
     idx = torch.empty((B, Tq, Hkv, n_blocks), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
@@ -319,7 +326,7 @@ def block_score_topk(q, k, lse, block, n_blocks, q_offset=None):
 
 def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_offset=None,
                        out_dtype=None, want_lse=False, sink=None, sink_local=None, out_gate=None,
-                       local_ring=0, pages=None):
+                       local_ring=0, pages=None, scale=None):
     """Sparse layer over the shared K, V and index set with the layer's own q.
     swa = (k_local, v_local, gate_logits fp32 [B,Tq,Hq,2], window) adds the gated sliding-window
     branch; local_ring > 0: k_local / v_local are rings [B, local_ring, Hkv, d].
@@ -334,10 +341,10 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
     _need(idx, "idx", dev, dtype=torch.int32)
     _need(count, "count", dev, dtype=torch.int32, shape=idx.shape[:3])
     if pages is not None:
-        desc = _paged_desc(q, k, pages[1], q_offset, out_dtype)
+        desc = _paged_desc(q, k, pages[1], q_offset, out_dtype, scale)
         pg = _pages(k, pages[0], k.shape[1], dev)
     else:
-        desc = make_desc(q, k, q_offset, out_dtype)
+        desc = make_desc(q, k, q_offset, out_dtype, scale)
         pg = None
     kind_code = HS_IDX_TOKEN if kind == "token" else HS_IDX_BLOCK
     cap = idx.shape[-1]

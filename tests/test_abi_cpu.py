@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def desc(**kw):
     base = dict(batch=1, q_len=1, kv_len=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
-                q_offset=-1, in_dtype=hs.HS_BF16, out_dtype=hs.HS_BF16)
+                q_offset=-1, scale=0.0, in_dtype=hs.HS_BF16, out_dtype=hs.HS_BF16)
     base.update(kw)
     return hs.AttnDesc(**base)
 
@@ -221,3 +221,40 @@ def test_missing_library_fails_loudly(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                          timeout=300)
     assert "raised True" in out.stdout, out.stdout + out.stderr
+
+
+@pytest.mark.parametrize("scale", [-1.0, float("nan"), float("inf")])
+def test_bad_scale_rejected(scale):
+    d = desc(scale=scale)
+    assert hs.lib().hs_full_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                     None) == hs.HS_ERR_INVALID_ARG
+    assert "scale" in hs.lib().hs_last_error().decode()
+    assert hs.lib().hs_workspace_size(hs.HS_OP_FULL_ATTN, ctypes.byref(d), 0, 0) == 0
+
+
+def test_descriptor_layout_matches_header():
+    """The binding's descriptor has the header's field order: scale follows q_offset."""
+    names = [f[0] for f in hs.AttnDesc._fields_]
+    assert names == ["batch", "q_len", "kv_len", "n_q_heads", "n_kv_heads", "head_dim",
+                     "q_offset", "scale", "in_dtype", "out_dtype"]
+    assert hs.AttnDesc.scale.offset == 32 and ctypes.sizeof(hs.AttnDesc) == 48
+
+
+@pytest.mark.parametrize("q_len,ring,ok", [(1, 128, True), (1, 127, False), (4, 131, True),
+                                           (4, 130, False), (600, 727, True), (600, 726, False)])
+def test_ring_window_must_hold_every_position_of_the_call(q_len, ring, ok):
+    """A ring of local keys holds position t in slot t % ring; the q_len rows of one call read
+    window + q_len - 1 distinct positions, so a shorter ring is refused before any launch."""
+    L = hs.lib()
+    d = desc(q_len=q_len, kv_len=4096)
+    swa = hs.SwaBranch(0x1000, 0x1000, 0x1000, 128)
+    opts = hs.SparseOpts(None, None, None, ring)
+    # token lists of 4096 entries always take split partials, so a valid call needs workspace
+    rc = L.hs_sparse_attn_gather_ex(ctypes.byref(d), FAKE, FAKE, FAKE, hs.HS_IDX_TOKEN, FAKE,
+                                    FAKE, 4096, 1, ctypes.byref(swa), ctypes.byref(opts), FAKE,
+                                    None, FAKE, 0, None)
+    if ok:  # passes validation and stops at the missing workspace: nothing is enqueued
+        assert rc == hs.HS_ERR_WORKSPACE, (rc, L.hs_last_error().decode())
+    else:
+        assert rc == hs.HS_ERR_INVALID_ARG
+        assert "local_ring" in L.hs_last_error().decode()

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from oracle_top_kv_amd.inputs import Workload, make_inputs, to_numpy_f32
-from parity_utils import TOL_BF16, check_block_sets, check_token_sets, max_abs
+from parity_utils import LSE_TOL, TOL_BF16, check_block_sets, check_token_sets, max_abs
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_full_attention_and_logits_selection(name, wl):
     o_ref, lse_ref = oracle.full_attention(qn, kn, vn)
     eo, el = max_abs(o.cpu().numpy(), o_ref), max_abs(lse.cpu().numpy(), lse_ref)
     say(f"  full attention max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
-    assert eo <= TOL_BF16 and el <= 2e-6
+    assert eo <= TOL_BF16 and el <= LSE_TOL
     oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
     ex = check_token_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, qn, kn, lse_ref,
                           wl.k_global, wl.window, wl.q_offset)
@@ -83,7 +83,7 @@ def test_full_attention_and_logits_selection(name, wl):
     r_o, r_l = oracle.masked_attention(to_numpy_f32(qs), kn, vn, oi, oc, sink=sink.numpy())
     eo, el = max_abs(os_.cpu().numpy(), r_o), max_abs(ls_.cpu().numpy(), r_l)
     say(f"  token-sparse max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
-    assert eo <= TOL_BF16 and el <= 2e-6
+    assert eo <= TOL_BF16 and el <= LSE_TOL
 
 
 @pytest.mark.parametrize("name,wl", SHAPES[:3], ids=[s[0] for s in SHAPES[:3]])
@@ -115,7 +115,7 @@ def test_prefill_kernel_with_64_heads_per_kv_head():
     o_ref, lse_ref = oracle.full_attention(*(to_numpy_f32(x[n]) for n in ("q", "k", "v")))
     eo, el = max_abs(o.cpu().numpy(), o_ref), max_abs(lse.cpu().numpy(), lse_ref)
     say(f"[prefill g=64] max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
-    assert eo <= TOL_BF16 and el <= 2e-6
+    assert eo <= TOL_BF16 and el <= LSE_TOL
 
 
 def test_paged_mqa256_equals_contiguous():
@@ -137,7 +137,8 @@ def test_paged_mqa256_equals_contiguous():
     # layer run the row kernel, the contiguous calls the group kernel: other split boundaries,
     # so P is rounded to bf16 against other running maxima (the LSE sums fp32 exponentials)
     assert torch.equal(lg, lg2)
-    assert (o - o2).abs().max().item() <= TOL_BF16 and (lse - lse2).abs().max().item() <= 2e-6
+    assert (o - o2).abs().max().item() <= TOL_BF16
+    assert (lse - lse2).abs().max().item() <= LSE_TOL
     assert (s1 - s2).abs().max().item() <= TOL_BF16
 
 
@@ -191,4 +192,4 @@ def test_group_kernel_empty_and_partial_index_sets(with_sink):
     keep[1, 0] = False
     assert max_abs(o[keep], o_ref[keep]) <= TOL_BF16
     lk = np.isfinite(lse_ref)
-    assert max_abs(lse[lk], lse_ref[lk]) <= 2e-6
+    assert max_abs(lse[lk], lse_ref[lk]) <= LSE_TOL

@@ -12,7 +12,10 @@ SRC = os.path.join(ROOT, "oracle", "hs_oracle.c")
 
 # (name, exact snippet of the correct source, the planted mistake)
 MUTANTS = [
-    ("no_scale", "const double tau = 1.0 / sqrt((double)d);", "const double tau = 1.0;"),
+    ("no_scale", "const double tau = s->scale > 0.0 ? s->scale : 1.0 / sqrt((double)d);",
+     "const double tau = s->scale > 0.0 ? s->scale : 1.0;"),
+    ("given_scale_ignored", "const double tau = s->scale > 0.0 ? s->scale : 1.0 / sqrt((double)d);",
+     "const double tau = 1.0 / sqrt((double)d);"),
     ("head_mapping", "const int u = h / (s->n_q_heads / s->n_kv_heads);",
      "const int u = h % s->n_kv_heads;"),
     ("drops_diagonal", "const int64_t n = s->q_offset + j + 1;\n      logits_row",

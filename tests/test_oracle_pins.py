@@ -26,8 +26,9 @@ def rnd(shape, seed, scale=1.0):
     return (scale * torch.randn(shape, generator=g, dtype=torch.float32)).numpy()
 
 
-def sdpa_ref(q, k, v, q_offset, mask_fn=None):
-    """torch SDPA in float64 with GQA expanded by repeat_interleave and an explicit mask.
+def sdpa_ref(q, k, v, q_offset, mask_fn=None, scale=None):
+    """torch SDPA in float64 with GQA expanded by repeat_interleave and an explicit mask
+    (scale: SDPA's own scale argument; None is its default 1/sqrt(d)).
     Returns o [B,Tq,Hq,d] and lse [B,Hq,Tq] (lse from torch.logsumexp of the masked logits)."""
     B, Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[1], k.shape[2]
@@ -40,8 +41,8 @@ def sdpa_ref(q, k, v, q_offset, mask_fn=None):
     mask = ipos <= tpos
     if mask_fn is not None:
         mask = mask_fn(mask)  # [..., Tq, Tk] boolean, broadcastable to [B,Hq,Tq,Tk]
-    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
-    logits = (qt @ kt.transpose(-1, -2)) / math.sqrt(d)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    logits = (qt @ kt.transpose(-1, -2)) * (1.0 / math.sqrt(d) if scale is None else scale)
     logits = logits.masked_fill(~mask, float("-inf"))
     lse = torch.logsumexp(logits, dim=-1)
     return o.permute(0, 2, 1, 3).numpy(), lse.numpy()
@@ -71,6 +72,20 @@ def test_full_attention_matches_torch_sdpa(B, Tq, Tk, Hq, Hkv, d):
     o_ref, lse_ref = sdpa_ref(q, k, v, Tk - Tq)
     assert np.max(np.abs(o - o_ref)) < 1e-12
     assert np.max(np.abs(lse - lse_ref)) < 1e-12
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.4])
+def test_explicit_scale_matches_torch_sdpa(scale):
+    """A logit scale other than 1/sqrt(d) (the descriptor's scale) against SDPA's own scale
+    argument; the token and block rankings follow the same logits."""
+    q, k, v = rnd((2, 9, 4, 16), 61), rnd((2, 30, 2, 16), 62), rnd((2, 30, 2, 16), 63)
+    o, lse = oracle.full_attention(q, k, v, scale=scale)
+    o_ref, lse_ref = sdpa_ref(q, k, v, 21, scale=scale)
+    assert np.max(np.abs(o - o_ref)) < 1e-12
+    assert np.max(np.abs(lse - lse_ref)) < 1e-12
+    a = oracle.logit_row(q, k, 1, 8, 3, scale=scale)
+    ref = q[1, 8, 3].astype(np.float64) @ k[1, :30, 1].astype(np.float64).T * scale
+    assert np.max(np.abs(a - ref)) < 1e-12
 
 
 def test_full_attention_row_subset_leaves_others():
@@ -318,7 +333,7 @@ def test_masked_attention_rejects_out_of_range_index():
 
 def test_block_scores_match_algorithm1_route():
     """Store the per-block rowmax of the logits m~, then exp(m~ - m)/l with the row's global max
-    m and l = sum exp(a - m) (Algorithm 1 of the HySparse paper with the exp its line 14 omits,
+    m and l = sum exp(a - m) (Algorithm 1 of the HySparse paper, with the exponential its normalization step omits,
     as the part-1 notes point out).  The literal form (m~ - m)/l is negative and cannot match."""
     T, d, Bk = 200, 16, 16
     q, k = rnd((1, T, 3, d), 51), rnd((1, T, 1, d), 52)
