@@ -53,12 +53,21 @@ struct RaCfg {
   static constexpr int kThreads = 64 * NW;
   static constexpr int kTPR = kThreads / 16;  // merge threads per row
   static constexpr int kCPT = D / kTPR;       // merge columns per thread
+  // A merge thread's columns come in chunks of up to 4 consecutive ones, the chunks kTPR * kChunk
+  // columns apart: the kTPR threads of a row then read and write contiguous 16-byte pieces
+  // (conflict-free in LDS, coalesced in memory).
+  static constexpr int kChunk = kCPT < 4 ? kCPT : 4;
+  static constexpr int kOStride = D + 4;  // merge buffer row stride (floats)
+  __device__ static int col(int lr, int c) {
+    return ((c / kChunk) * kTPR + lr) * kChunk + c % kChunk;
+  }
   static constexpr int kElem = F32 ? 4 : 2;
   static constexpr int kVStride = D + (F32 ? 4 : 16);  // LDS row stride (elements), padded
   static constexpr int kChunksPerRow = D * kElem / 16;
   static constexpr int kVLoads = kStep * kChunksPerRow / 64;  // 16-byte V chunks per lane
   static constexpr int kVTileBytes = kStep * kVStride * kElem;
-  static constexpr int kCombineBytes = kWaves * 16 * D * 4 + kWaves * 16 * 4 + kWaves * 16 * 8;
+  static constexpr int kCombineBytes =
+      kWaves * 16 * kOStride * 4 + kWaves * 16 * 4 + kWaves * 16 * 8;
   static constexpr int kSmem =
       (kWaves * kVTileBytes > kCombineBytes ? kWaves * kVTileBytes : kCombineBytes);
 };
@@ -71,23 +80,26 @@ constexpr int kLogitSteps = 4;
 constexpr int kLogitRow = kLogitSteps * kStep + 4;  // floats per staged row (padded)
 constexpr int kLogitWaveBytes = 16 * kLogitRow * 4;
 
+// Position of key-list entry e (-1: none).  The list entry is read whether or not e is below the
+// list's length L (every entry below idx_cap, or idx_cap blocks, lies inside the caller's index
+// array), so that the entry loads need not wait for the count load.
 template <int SRC>
 __device__ __forceinline__ int entry_pos(const RowAttnParams& p, int e, int L, long long lo,
                                          long long t_last, const int32_t* list) {
-  if (e >= L) return -1;
-  if (SRC == SRC_RANGE || SRC == SRC_WINDOW) return (int)(lo + e);
+  if (SRC == SRC_RANGE || SRC == SRC_WINDOW) return e < L ? (int)(lo + e) : -1;
   if (SRC == SRC_TOKEN) {
-    const int x = list[e];
-    return (x >= 0 && x <= t_last) ? x : -1;
+    const int x = e < p.idx_cap ? list[e] : -1;
+    return (e < L && x >= 0 && x <= t_last) ? x : -1;
   }
-  const int blk = list[e / p.block];
-  if (blk < 0 || (long long)blk > t_last / p.block) return -1;
+  const int eb = e / p.block;
+  const int blk = eb < p.idx_cap ? list[eb] : -1;
+  if (e >= L || blk < 0 || (long long)blk > t_last / p.block) return -1;
   const long long x = (long long)blk * p.block + e % p.block;
   return x <= t_last ? (int)x : -1;
 }
 
 // Result of one pass over a key source, as held by the merge thread of row r, columns
-// c0 .. c0 + CPT - 1 (r = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * CPT): the row maximum
+// RaCfg::col(lr, c), c < CPT (r = threadIdx.x / TPR, lr = threadIdx.x % TPR): the row maximum
 // M (log2 domain), the row sum L relative to M and the unnormalized output columns.
 template <int CPT>
 struct PassOut {
@@ -221,7 +233,10 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   };
   int first_page = 0;
   if constexpr (kList) {
-    const int n_e = (step_end - step_begin) * kStep;
+    // the split's whole entry range (its length does not depend on the count, so the entry
+    // loads are issued together with the count load); entries past the list read as -1
+    const int n_e = steps_per_split * kStep < kMaxListEntries ? steps_per_split * kStep
+                                                                : kMaxListEntries;
     for (int i = threadIdx.x; i < n_e; i += Cfg::kThreads) {
       const int pos = entry_pos<SRC>(p, step_begin * kStep + i, L, lo, t_last, list);
       pos_all[i] = pos;
@@ -429,14 +444,15 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   }
 
   // ---- merge the waves of this workgroup ----
+  // (rows kOStride = D + 4 floats apart: the 16 rows' 16-byte writes of one column block fall in
+  // distinct bank groups)
   workgroup_lds_sync();
-  float* cO = (float*)smem;                     // [kWaves][16][D]
-  float* cM = cO + kWaves * 16 * D;             // [kWaves][16]
+  constexpr int OS = Cfg::kOStride;
+  float* cO = (float*)smem;                     // [kWaves][16][OS]
+  float* cM = cO + kWaves * 16 * OS;            // [kWaves][16]
   double* cL = (double*)(cM + kWaves * 16);     // [kWaves][16]
 #pragma unroll
-  for (int db = 0; db < D / 16; db++)
-#pragma unroll
-    for (int e = 0; e < 4; e++) cO[(wave * 16 + rn) * D + 16 * db + 4 * jg + e] = oacc[db][e];
+  for (int db = 0; db < D / 16; db++) *(f32x4*)&cO[(wave * 16 + rn) * OS + 16 * db + 4 * jg] = oacc[db];
   double ld = (double)l_s - (double)l_c;
   ld += __shfl_xor(ld, 16, 64);
   ld += __shfl_xor(ld, 32, 64);
@@ -448,7 +464,7 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
 
   constexpr int CPT = Cfg::kCPT;
   const int r = threadIdx.x / Cfg::kTPR;
-  const int c0 = (threadIdx.x % Cfg::kTPR) * CPT;
+  const int lr = threadIdx.x % Cfg::kTPR;
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kWaves; w++) M = fmaxf(M, cM[w * 16 + r]);
@@ -464,7 +480,7 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   for (int c = 0; c < CPT; c++) {
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) acc += f[w] * cO[(w * 16 + r) * D + c0 + c];
+    for (int w = 0; w < kWaves; w++) acc += f[w] * cO[(w * 16 + r) * OS + Cfg::col(lr, c)];
     out.ov[c] = acc;
   }
   out.M = M;
@@ -551,10 +567,10 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
                                               j0, nq, smem, pos_all, row_all, a);
 
   const int r = threadIdx.x / Cfg::kTPR;
-  const int c0 = (threadIdx.x % Cfg::kTPR) * CPT;
+  const int lr = threadIdx.x % Cfg::kTPR;
   const int jr = j0 + r / p.hpc;
   const int hr = u * p.g + hc * p.hpc + r % p.hpc;
-  const size_t ooff = (((size_t)b * p.Tq + jr) * p.Hq + hr) * D + c0;
+  const size_t orow = ((size_t)b * p.Tq + jr) * p.Hq + hr;  // (b, t, h) of this thread's row
   float res[CPT];
   float lse_row = -INFINITY;
   if constexpr (GATED) {
@@ -563,8 +579,8 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
     attend_pass<D, F32, SRC_WINDOW, NW>(p, p.k2, p.v2, 0, 1 << 30, b, u, hc, j0, nq, smem,
                                         pos_all, row_all, w);
     if (r >= nrows) return;
-    const float* z = p.gate + (((size_t)b * p.Tq + jr) * p.Hq + hr) * 2;
-    const double og = out_gate_of(p.out_gate, ((size_t)b * p.Tq + jr) * p.Hq + hr);
+    const float* z = p.gate + orow * 2;
+    const double og = out_gate_of(p.out_gate, orow);
     const double sg = 1.0 / (1.0 + exp(-(double)z[0]));
     const double sl = 1.0 / (1.0 + exp(-(double)z[1]));
     const RowNorm ng = row_norm(a.M, a.L, p.sink, hr, sg * og);
@@ -573,38 +589,40 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
     for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * ng.factor + w.ov[c] * nl.factor;
     lse_row = ng.lse;
   } else {
-    if (r >= nrows) return;
     if (!p.final_direct) {
       const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu * p.cpq;
       const size_t prow = ((size_t)split * n_sets + set) * 16 + r;
-      if (c0 == 0) {
-        p.part_m[prow] = a.M;
-        p.part_l[prow] = a.L;
+      if (r < nrows) {
+        if (lr == 0) {
+          p.part_m[prow] = a.M;
+          p.part_l[prow] = a.L;
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; c++) p.part_o[prow * D + Cfg::col(lr, c)] = a.ov[c];
       }
-#pragma unroll
-      for (int c = 0; c < CPT; c++) p.part_o[prow * D + c0 + c] = a.ov[c];
       return;
-    }
-    const RowNorm n =
-        row_norm(a.M, a.L, p.sink, hr, out_gate_of(p.out_gate, ((size_t)b * p.Tq + jr) * p.Hq + hr));
+    } else {
+      if (r >= nrows) return;
+      const RowNorm n = row_norm(a.M, a.L, p.sink, hr, out_gate_of(p.out_gate, orow));
 #pragma unroll
-    for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * n.factor;
-    lse_row = n.lse;
+      for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * n.factor;
+      lse_row = n.lse;
+    }
   }
   if (p.out_f32) {
-    float* op = (float*)p.o + ooff;
+    float* op = (float*)p.o + orow * D;
 #pragma unroll
-    for (int c = 0; c < CPT; c++) op[c] = res[c];
+    for (int c = 0; c < CPT; c++) op[Cfg::col(lr, c)] = res[c];
   } else {
-    uint16_t* op = (uint16_t*)p.o + ooff;
+    uint16_t* op = (uint16_t*)p.o + orow * D;
 #pragma unroll
-    for (int c = 0; c < CPT; c++) op[c] = f2bf(res[c]);
+    for (int c = 0; c < CPT; c++) op[Cfg::col(lr, c)] = f2bf(res[c]);
   }
-  if (p.lse && c0 == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = lse_row;
+  if (p.lse && lr == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = lse_row;
 }
 
 // ---- split / branch combine ---------------------------------------------------------------
-// One workgroup per (row-set, row).  Threads = SP split lanes x D/4 column chunks; each thread
+// One workgroup per (row-set, row), q_per_set * hpc rows per set.  Threads = SP split lanes x D/4 column chunks; each thread
 // folds every SP-th split of its 4 columns with weights 2^(m_s - M), then the split lanes are
 // summed in LDS.  Row sums are combined in fp64.
 // BATCHED (more than two splits per thread): the loads of kBatch splits are issued before any
@@ -616,9 +634,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int SP = 256 / NC;      // split lanes
   __shared__ float red[SP][D];
   __shared__ double redl[SP];
-  const int set = blockIdx.x / 16;
-  const int r = blockIdx.x % 16;
-  const size_t n_sets = gridDim.x / 16;
+  const int rps = p.q_per_set * p.hpc;  // rows of a full row-set (the grid has rps per set)
+  const int set = blockIdx.x / rps;
+  const int r = blockIdx.x % rps;
+  const size_t n_sets = gridDim.x / rps;
   const int hc = set % p.cpq;
   const int sq = (set / p.cpq) % p.sets_per_bu;
   const int bu = set / (p.cpq * p.sets_per_bu);
@@ -761,9 +780,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   if (p.lse && c == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = (float)lse0;
 }
 
+// Workgroups of a row-kernel launch: one per (row-set, split).
+unsigned ra_grid(const RowAttnParams& p) {
+  return (unsigned)((long long)p.B * p.Hkv * p.sets_per_bu * p.cpq * p.n_split);
+}
+
 template <int D, bool F32, int NW>
 hipError_t launch_ra_paged(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
-  const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu * p.cpq);
+  const dim3 grid(ra_grid(p));
   const int threads = 64 * NW;
   if (gated) {
     if (src == SRC_TOKEN)
@@ -794,7 +818,7 @@ hipError_t launch_ra_paged(const RowAttnParams& p, KeySrc src, bool gated, hipSt
 template <int D, bool F32, int NW>
 hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t stream) {
   if (p.pages) return launch_ra_paged<D, F32, NW>(p, src, gated, stream);
-  const dim3 grid(p.n_split * p.B * p.Hkv * p.sets_per_bu * p.cpq);
+  const dim3 grid(ra_grid(p));
   const int threads = 64 * NW;
   if (p.logits) {
     if constexpr (NW == 4) {
@@ -852,7 +876,8 @@ void launch_combine_d(const CombineParams& p, dim3 grid, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid(p.B * p.Hkv * p.sets_per_bu * p.cpq * 16);
+  // one workgroup per row of every row-set (a last, partial query chunk leaves some idle)
+  const dim3 grid(p.B * p.Hkv * p.sets_per_bu * p.cpq * p.q_per_set * p.hpc);
   if (head_dim == 256)
     launch_combine_d<256>(p, grid, stream);
   else if (head_dim == 128)

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from oracle_top_kv_amd.inputs import Workload, make_inputs, to_numpy_f32
-from parity_utils import LSE_TOL, TOL_BF16, TOL_F32, check_block_sets, check_token_sets, max_abs
+from parity_utils import LSE_TOL, lse_bound, TOL_BF16, TOL_F32, check_block_sets, check_token_sets, max_abs
 
 pytestmark = pytest.mark.gpu
 
@@ -119,7 +119,7 @@ def test_full_attn_moving_maximum(profile):
     el = max_abs(lse.cpu().numpy(), lse_ref)
     say(f"  max|dO| = {eo:.3e}  max|dLSE| = {el:.3e}  max LSE {np.abs(lse_ref).max():.2f}")
     assert eo <= TOL_BF16
-    assert el <= LSE_TOL
+    assert el <= lse_bound(lse_ref)
 
 
 # ---- token top-k -------------------------------------------------------------------------
@@ -486,7 +486,7 @@ SCALE_CASES = [
     ("prefill_g8_ragged", Workload("sc_pf", 1, 150, 900, 16, 2, 128, "bf16", k_global=128,
                                    window=32, block=64, n_blocks=4, seed=132), 0.11),
     ("tiny_f32", Workload("sc_t", 1, 64, 200, 4, 1, 64, "f32", k_global=32, window=8, block=16,
-                          n_blocks=4, seed=133), 0.3),
+                          n_blocks=4, seed=133), 0.09),
 ]
 
 
