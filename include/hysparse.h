@@ -275,6 +275,22 @@ hs_status hs_sparse_attn_gather_ex(const hs_attn_desc* desc, const void* q, cons
                                    const hs_swa_branch* swa, const hs_sparse_opts* opts, void* o,
                                    float* lse_opt, void* ws, size_t ws_bytes, void* stream);
 
+/* hs_sparse_attn_gather without a workspace argument, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same kernels and outputs, bit for bit, as hs_sparse_attn_gather with the same arguments; the
+ * split partials live in a device-resident scratch array that the library holds for the life of
+ * the process, one copy per device, 16 MiB each (a layer that needs more, i.e. more than
+ * hs_workspace_size(HS_OP_SPARSE_ATTN, ...) = 16 MiB, returns HS_ERR_WORKSPACE; decode-shaped
+ * layers of the pages' workloads need under 5 MiB).  Allocates nothing.  `stream` must belong to
+ * the current device.  Every call on a device shares that device's scratch: calls that overlap
+ * on one device (different streams, threads) race and must be serialized by the caller. */
+hs_status hs_sparse_attn_gather_noalloc(const hs_attn_desc* desc, const void* q,
+                                        const void* k_full, const void* v_full,
+                                        hs_index_kind kind, const int32_t* idx,
+                                        const int32_t* count, int32_t idx_cap, int32_t block,
+                                        const hs_swa_branch* swa, void* o, float* lse_opt,
+                                        void* stream);
+
 /* Bytes of workspace the call `op` needs for `desc` (p0, p1 as documented on hs_op).  Returns 0
  * for an invalid description (hs_last_error() says why). */
 size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t p1);

@@ -890,13 +890,18 @@ hs_status hs_sparse_attn_gather_ex(const hs_attn_desc* desc, const void* q, cons
                                      block, swa, opts, o, lse_opt, ws, ws_bytes, stream);
 }
 
-hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, const void* k_full,
-                                      const void* v_full, const hs_kv_pages* pages,
-                                      hs_index_kind kind, const int32_t* idx,
-                                      const int32_t* count, int32_t idx_cap, int32_t block,
-                                      const hs_swa_branch* swa, const hs_sparse_opts* opts,
-                                      void* o, float* lse_opt, void* ws, size_t ws_bytes,
-                                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Body of every sparse-layer entry point.  from_scratch: the workspace is the library's
+// device-resident scratch (the no-allocation entry point), fetched after validation.
+hs_status sparse_layer(const hs_attn_desc* desc, const void* q, const void* k_full,
+                       const void* v_full, const hs_kv_pages* pages, hs_index_kind kind,
+                       const int32_t* idx, const int32_t* count, int32_t idx_cap, int32_t block,
+                       const hs_swa_branch* swa, const hs_sparse_opts* opts, void* o,
+                       float* lse_opt, void* ws, size_t ws_bytes, void* stream,
+                       bool from_scratch) {
   const float* sink_g = opts ? opts->sink : nullptr;
   const float* sink_l = opts ? opts->sink_local : nullptr;
   const float* ogate = opts ? opts->out_gate : nullptr;
@@ -936,6 +941,16 @@ hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, c
                 ring, (long long)window + s.Tq - 1, window, s.Tq);
   const SparseGeom g = sparse_geom(s, keys, window, pages != nullptr);
   const size_t need = sparse_ws(s, g, window);
+  if (from_scratch) {
+    if (need > hs::kScratchBytes)
+      return fail(HS_ERR_WORKSPACE,
+                  "this layer needs %zu bytes of split partials; the no-allocation entry point "
+                  "holds at most %zu (use hs_sparse_attn_gather with a workspace)",
+                  need, hs::kScratchBytes);
+    hipError_t e = hs::scratch_buffer(&ws);
+    if (e != hipSuccess) return hip_status(e, "device scratch of the no-allocation entry point");
+    ws_bytes = hs::kScratchBytes;
+  }
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   hipStream_t hst = (hipStream_t)stream;
@@ -1008,6 +1023,31 @@ hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, c
     if (e != hipSuccess) return hip_status(e, "combine kernel");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_sparse_attn_gather_paged(const hs_attn_desc* desc, const void* q, const void* k_full,
+                                      const void* v_full, const hs_kv_pages* pages,
+                                      hs_index_kind kind, const int32_t* idx,
+                                      const int32_t* count, int32_t idx_cap, int32_t block,
+                                      const hs_swa_branch* swa, const hs_sparse_opts* opts,
+                                      void* o, float* lse_opt, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  return sparse_layer(desc, q, k_full, v_full, pages, kind, idx, count, idx_cap, block, swa, opts,
+                      o, lse_opt, ws, ws_bytes, stream, false);
+}
+
+hs_status hs_sparse_attn_gather_noalloc(const hs_attn_desc* desc, const void* q,
+                                        const void* k_full, const void* v_full,
+                                        hs_index_kind kind, const int32_t* idx,
+                                        const int32_t* count, int32_t idx_cap, int32_t block,
+                                        const hs_swa_branch* swa, void* o, float* lse_opt,
+                                        void* stream) {
+  return sparse_layer(desc, q, k_full, v_full, nullptr, kind, idx, count, idx_cap, block, swa,
+                      nullptr, o, lse_opt, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

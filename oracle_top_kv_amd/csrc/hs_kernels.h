@@ -190,4 +190,11 @@ int prefill_select_max_k();
 hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
                                  bool block_mode, hipStream_t stream);
 
+// ---- device-resident scratch of the no-allocation sparse-layer entry point ------------------
+// kScratchBytes of device memory held by the library for the life of the process, one copy per
+// device; scratch_buffer returns the current device's copy (its address is looked up once per
+// device).  Calls that use it and overlap on one device race.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+hipError_t scratch_buffer(void** ptr);
+
 }  // namespace hs

@@ -23,7 +23,7 @@ HS_OP_FULL_ATTN_BLOCK_TOPK, HS_OP_FULL_ATTN_PAGED = 7, 8
 EXPORTS = ["hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk", "hs_sparse_attn_gather",
            "hs_full_attn_fwd_logits", "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
            "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex", "hs_full_attn_fwd_paged",
-           "hs_sparse_attn_gather_paged",
+           "hs_sparse_attn_gather_paged", "hs_sparse_attn_gather_noalloc",
            "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
 
 
@@ -85,6 +85,8 @@ def lib():
         L.hs_sparse_attn_gather_paged.argtypes = [pd, vp, vp, vp, pp, ctypes.c_int, vp, vp, i32,
                                                   i32, ctypes.POINTER(SwaBranch),
                                                   ctypes.POINTER(SparseOpts), vp, vp, vp, sz, vp]
+        L.hs_sparse_attn_gather_noalloc.argtypes = [pd, vp, vp, vp, ctypes.c_int, vp, vp, i32,
+                                                    i32, ctypes.POINTER(SwaBranch), vp, vp, vp]
         L.hs_workspace_size.argtypes = [ctypes.c_int, pd, i32, i32]
         L.hs_workspace_size.restype = sz
         L.hs_status_string.restype = ctypes.c_char_p
@@ -95,7 +97,8 @@ def lib():
                   "hs_sparse_attn_gather", "hs_full_attn_fwd_logits",
                   "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
                   "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex",
-                  "hs_full_attn_fwd_paged", "hs_sparse_attn_gather_paged"):
+                  "hs_full_attn_fwd_paged", "hs_sparse_attn_gather_paged",
+                  "hs_sparse_attn_gather_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -389,4 +392,36 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
                                                  _ptr(ws), n, _stream(dev)),
                "hs_sparse_attn_gather_paged")
     del keep
+    return o, lse
+
+
+def sparse_attn_gather_noalloc(q, k, v, idx, count, o, lse=None, kind="token", block=64,
+                               swa=None, q_offset=None, scale=None):
+    """hs_sparse_attn_gather_noalloc: the sparse layer without a workspace, writing into the
+    caller's o [B,Tq,Hq,d] (and lse [B,Hq,Tq] fp32 when given).  Allocates nothing."""
+    dev = q.device
+    _need(q, "q", dev)
+    _need(k, "k", dev, dtype=q.dtype)
+    _need(v, "v", dev, dtype=q.dtype)
+    _need(idx, "idx", dev, dtype=torch.int32)
+    _need(count, "count", dev, dtype=torch.int32, shape=idx.shape[:3])
+    _need(o, "o", dev, shape=q.shape)
+    desc = make_desc(q, k, q_offset, o.dtype, scale)
+    if lse is not None:
+        _need(lse, "lse", dev, dtype=torch.float32, shape=(q.shape[0], q.shape[2], q.shape[1]))
+    sw = None
+    if swa is not None:
+        kl, vl, gate, window = swa
+        loc_shape = (q.shape[0], desc.kv_len) + tuple(k.shape[2:])
+        _need(kl, "k_local", dev, dtype=q.dtype, shape=loc_shape)
+        _need(vl, "v_local", dev, dtype=q.dtype, shape=loc_shape)
+        _need(gate, "gate_logits", dev, dtype=torch.float32, shape=tuple(q.shape[:3]) + (2,))
+        sw = SwaBranch(kl.data_ptr(), vl.data_ptr(), gate.data_ptr(), int(window))
+    kind_code = HS_IDX_TOKEN if kind == "token" else HS_IDX_BLOCK
+    _check(lib().hs_sparse_attn_gather_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                               kind_code, _ptr(idx), _ptr(count),
+                                               int(idx.shape[-1]), int(block),
+                                               ctypes.byref(sw) if sw is not None else None,
+                                               _ptr(o), _ptr(lse), _stream(dev)),
+           "hs_sparse_attn_gather_noalloc")
     return o, lse

@@ -106,6 +106,8 @@ int main() {
         hs_oracle_topk_from_logits(&y, FF, FF, 256, 64, FI, FI, F, big, nullptr);
         hs_block_topk_from_logits(&y, FF, FF, 64, 16, FI, FI, F, big, nullptr);
         hs_full_attn_fwd_logits(&y, F, F, F, F, FF, FF, F, big, nullptr);
+        hs_sparse_attn_gather_noalloc(&y, F, F, F, HS_IDX_TOKEN, FI, FI, 320, 64, nullptr, F, FF,
+                                      nullptr);
       }
     std::printf("valid calls exercised without a GPU\n");
   }
