@@ -60,5 +60,21 @@ def build(verbose=False, jobs=None):
     return SO
 
 
+PROBES_SRC = os.path.join(HERE, "probes", "ceilings.hip")
+PROBES_SO = os.path.join(HERE, "libhs_probes.so")
+
+
+def build_probes():
+    """The benchmark's measurement kernels (HBM read ceilings), a library of their own."""
+    tmp = PROBES_SO + ".tmp"
+    cmd = [HIPCC] + HIP_FLAGS + ["-shared", "-o", tmp, PROBES_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        print(r.stdout + r.stderr, file=sys.stderr)
+        raise RuntimeError("build of libhs_probes.so failed")
+    os.replace(tmp, PROBES_SO)
+    return PROBES_SO
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

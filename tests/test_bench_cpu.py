@@ -19,12 +19,14 @@ def test_more_than_one_gpu_is_refused():
 
 def test_counter_traffic_lookup():
     # the committed summary belongs to the decode workload and its listed sources
-    assert bench.counter_traffic("no_such_workload") is None
-    t = bench.counter_traffic("decode_7b_32k")
+    assert bench.counter_traffic("no_such_workload", "sparse_token") is None
+    assert bench.counter_traffic("decode_7b_32k", "no_such_stage") is None
     path = os.path.join(ROOT, "profiles", "decode_7b_32k_hbm_counters.md")
-    if t is not None:
-        text = open(path).read()
-        meta = json.loads(text.split("```json\n")[1].split("\n```")[0])
-        assert t == meta["traffic_bytes_per_launch"]
-        # traffic can only exceed the algorithmic bytes (re-reads), never undercut them much
-        assert t >= 0.99 * meta["algorithmic_bytes_per_launch"]
+    for stage in ("sparse_token", "full_attn"):
+        t = bench.counter_traffic("decode_7b_32k", stage)
+        if t is not None:
+            text = open(path).read()
+            meta = json.loads(text.split("```json\n")[1].split("\n```")[0])
+            assert t == meta["traffic_bytes_per_launch"][stage]
+            # traffic can only exceed the algorithmic bytes (re-reads), never undercut them much
+            assert t >= 0.99 * meta["algorithmic_bytes_per_launch"][stage]
