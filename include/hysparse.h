@@ -30,11 +30,16 @@
  *     hs_workspace_size(...) bytes (16-byte aligned); a smaller one returns HS_ERR_WORKSPACE.
  *   - Supported: head_dim in {64, 128} (fp32 or bf16 inputs) or 256 (bf16; the HySparse2 head
  *     shape, MQA with 64 query heads of d 256 [P1 section 6.1]); g = Hq/Hkv integral and at
- *     most 16, or 32, 48, 64 (run as chunks of 16 heads); kv_len <= 2^30; out_dtype bf16 or
- *     fp32.  Index-set selection from Q and K (hs_oracle_topk, hs_block_score_topk) needs g in
- *     {4, 8, 16} and head_dim <= 128; selection from stored logits takes every supported shape;
- *     block selection needs block a multiple of 16 and 1 <= n_blocks <= 64.  head_dim 256 runs
- *     on the decode-shaped kernels only (any q_len; the gated sparse layer as two branches plus
+ *     most 64 (groups above 16 heads run as chunks of 16, the last one short when g is not a
+ *     multiple of 16; the group shares one index set through the maximum over all its heads,
+ *     [P2 "Why GQA shares the index within a group"]); kv_len <= 2^30; out_dtype bf16 or fp32.
+ *     Block selection needs block a multiple of 16 and 1 <= n_blocks <= 64.  Index selection
+ *     from Q and K takes every such shape: many query rows with g <= 16 stream over K tiles
+ *     (groups padded to 4, 8 or 16 heads); few rows with g in {4, 8, 16} and head_dim <= 128
+ *     run the fused score passes; every other shape first computes the rows' raw logits into
+ *     the workspace (at most 8 GiB of them: B * q_len * Hq * kv_len * 4 bytes, else
+ *     HS_ERR_UNSUPPORTED) and selects from them like stored logits.  head_dim 256 attention
+ *     runs on the decode-shaped kernels (any q_len; the gated sparse layer as two branches plus
  *     a combine).  Anything else returns HS_ERR_UNSUPPORTED.
  *   - Workspace sizes, for orientation: token selection with many query rows per KV head and
  *     k_global <= 1024 keeps a 16 KiB candidate buffer per (b, t, u); with few rows it keeps
@@ -229,15 +234,15 @@ hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const
 
 /* hs_oracle_topk with the scores taken from logits (as stored by hs_full_attn_fwd_logits for the
  * same desc) and lse instead of Q and K: same index set, same layout and padding of idx and
- * count.  desc->in_dtype is not used; desc->scale (0: 1/sqrt(head_dim)) scales the logits.  Any group size
- * g <= 16.  Workspace: hs_workspace_size(HS_OP_TOPK_FROM_LOGITS, desc, k_global, window). */
+ * count.  desc->in_dtype is not used; desc->scale (0: 1/sqrt(head_dim)) scales the logits.
+ * Any group size g <= 64.  Workspace: hs_workspace_size(HS_OP_TOPK_FROM_LOGITS, desc, k_global, window). */
 hs_status hs_oracle_topk_from_logits(const hs_attn_desc* desc, const float* logits,
                                      const float* lse, int32_t k_global, int32_t window,
                                      int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
                                      void* stream);
 
 /* hs_block_score_topk with the block scores taken from logits and lse: same blocks, layout and
- * padding.  Any group size g <= 16; block a multiple of 16; 1 <= n_blocks <= 64.  Workspace:
+ * padding.  Any group size g <= 64; block a multiple of 16; 1 <= n_blocks <= 64.  Workspace:
  * hs_workspace_size(HS_OP_BLOCK_TOPK_FROM_LOGITS, desc, block, n_blocks). */
 hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logits,
                                     const float* lse, int32_t block, int32_t n_blocks,

@@ -59,9 +59,8 @@ hs_status check_desc(const hs_attn_desc* d, Shape* s) {
     return fail(HS_ERR_INVALID_ARG, "scale %g: must be finite and >= 0 (0: 1/sqrt(head_dim))",
                 (double)d->scale);
   const int g = d->n_q_heads / d->n_kv_heads;
-  if (g > 64 || (g > 16 && g % 16))
-    return fail(HS_ERR_UNSUPPORTED,
-                "GQA group of %d query heads per KV head (at most 16, or 32, 48, 64)", g);
+  if (g > 64)
+    return fail(HS_ERR_UNSUPPORTED, "GQA group of %d query heads per KV head (at most 64)", g);
   // 32-bit position arithmetic inside the kernels
   if ((long long)d->kv_len > (1LL << 30))
     return fail(HS_ERR_UNSUPPORTED, "kv_len %d too large", d->kv_len);
@@ -92,7 +91,7 @@ struct RaGeom {
 // shorter than `min_steps` 32-key steps, none longer than `max_steps`.
 // Heads per row-set and head chunks per query: groups of more than 16 heads run as chunks of 16.
 int heads_per_set(const Shape& s) { return s.g < 16 ? s.g : 16; }
-int chunks_per_query(const Shape& s) { return s.g / heads_per_set(s); }
+int chunks_per_query(const Shape& s) { return (s.g + heads_per_set(s) - 1) / heads_per_set(s); }
 
 RaGeom ra_geom(const Shape& s, bool per_query, long long max_keys, int min_steps_per_split,
                long long target = kTargetWorkgroups, long long max_steps = 1LL << 40) {
@@ -309,11 +308,57 @@ hs::TopkDecodeParams tk_params(const Shape& s, const TkGeom& t, const float* lse
   return p;
 }
 
+// Group sizes and head sizes the streamed prefill selection takes (the group sits in the rows of
+// one 256-row tile; smaller groups are padded to 4, 8 or 16 heads).
+bool prefill_select_shape(const Shape& s) { return s.g <= 16 && (s.D <= 128 || !s.in_f32); }
+
 // Many query rows per KV head: selection streams over K tiles and stores no per-key score.
 bool use_prefill_select(const Shape& s, int k_global) {
-  return (long long)s.Tq * s.g > 16 && (s.g == 4 || s.g == 8 || s.g == 16) &&
+  return (long long)s.Tq * s.g > 16 && prefill_select_shape(s) &&
          k_global <= hs::prefill_select_max_k();
 }
+
+// The fused decode score passes (score, key and histogram in one kernel over K tiles).
+bool fused_decode_score(const Shape& s) {
+  return (s.g == 4 || s.g == 8 || s.g == 16) && s.D <= 128;
+}
+
+// Selection for every other shape with few query rows: the raw logits of the rows are computed
+// into the workspace first, then selected like stored logits.  Bounded by their size.
+constexpr size_t kMaxLogitBytes = (size_t)8 << 30;
+size_t logit_bytes(const Shape& s) {
+  return align_up((size_t)s.B * s.Tq * s.Hq * (size_t)s.Tk * 4, 256);
+}
+bool logits_fit(const Shape& s) { return logit_bytes(s) <= kMaxLogitBytes; }
+
+hs::LogitsParams logits_params(const Shape& s, const void* q, const void* k, float* logits) {
+  hs::LogitsParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.B = s.B;
+  p.Tq = s.Tq;
+  p.Tk = s.Tk;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.g = s.g;
+  p.q_off = s.q_off;
+  p.logits = logits;
+  // key chunks of multiples of 256 keys, enough workgroups to fill the GPU
+  const long long wgs = (long long)s.B * s.Tq * s.Hkv * ((s.g + 15) / 16);
+  const long long keys = s.q_off + s.Tq;  // the longest row
+  long long want = (2048 + wgs - 1) / wgs;
+  const long long most = (keys + 255) / 256;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  long long kps = (keys + want - 1) / want;
+  kps = (kps + 255) / 256 * 256;
+  p.keys_per_split = (int)kps;
+  p.n_split = (int)((keys + kps - 1) / kps);
+  return p;
+}
+
+enum SelRoute { SEL_NONE, SEL_PREFILL, SEL_DECODE, SEL_LOGITS };
 
 size_t tk_prefill_ws(const Shape& s) {
   return align_up((size_t)s.B * s.Tq * s.Hkv * hs::prefill_select_buffer_cap() * 8, 256);
@@ -345,7 +390,7 @@ struct BkGeom {
 
 BkGeom bk_geom(const Shape& s, int block, int n_blocks, bool per_row = false) {
   BkGeom t;
-  t.q_per_set = per_row ? 1 : 16 / s.g;
+  t.q_per_set = (per_row || s.g > 16) ? 1 : 16 / s.g;  // query rows per 16-row score set
   t.sets_per_bu = (s.Tq + t.q_per_set - 1) / t.q_per_set;
   const long long n_sets = (long long)s.B * s.Hkv * t.sets_per_bu;
   const long long nblk = (s.Tk + block - 1) / block;
@@ -363,15 +408,11 @@ BkGeom bk_geom(const Shape& s, int block, int n_blocks, bool per_row = false) {
   return t;
 }
 
-// per_row: selection from stored logits (one (b, t, u) row per workgroup, any group size)
+// per_row: selection from logits (stored or computed; one (b, t, u) row per workgroup and
+// split, any group size)
 hs_status bk_check(const Shape& s, int block, int n_blocks, BkGeom* g, bool per_row = false) {
   if (block < 16 || block % 16) return fail(HS_ERR_UNSUPPORTED, "block %d: must be a multiple of 16", block);
   if (n_blocks < 1 || n_blocks > 64) return fail(HS_ERR_UNSUPPORTED, "n_blocks %d: must be 1..64", n_blocks);
-  if (!per_row && s.g != 4 && s.g != 8 && s.g != 16)
-    return fail(HS_ERR_UNSUPPORTED, "block selection needs a GQA group of 4, 8 or 16 (got %d)", s.g);
-  if (!per_row && s.D > 128)
-    return fail(HS_ERR_UNSUPPORTED, "block selection from Q and K takes head_dim 64 or 128; "
-                "use the stored-logits path");
   *g = bk_geom(s, block, n_blocks, per_row);
   if ((long long)g->n_split * n_blocks > 4096)
     return fail(HS_ERR_UNSUPPORTED, "context too long for the block merge (%d splits)", g->n_split);
@@ -380,11 +421,45 @@ hs_status bk_check(const Shape& s, int block, int n_blocks, BkGeom* g, bool per_
 
 // Many query rows per KV head and blocks that tile 64 keys: streamed running top-n.
 bool use_prefill_blocks(const Shape& s, int block) {
-  return (long long)s.Tq * s.g > 16 && 64 % block == 0;
+  return (long long)s.Tq * s.g > 16 && 64 % block == 0 && prefill_select_shape(s);
 }
 
 size_t bk_ws(const BkGeom& g, int n_blocks) {
   return align_up(g.rows * (size_t)g.n_split * n_blocks * 8, 256);
+}
+
+// Route of a token selection from Q and K.
+SelRoute token_route(const Shape& s, int k_global) {
+  if (use_prefill_select(s, k_global)) return SEL_PREFILL;
+  if (fused_decode_score(s)) return SEL_DECODE;
+  if (logits_fit(s)) return SEL_LOGITS;
+  return SEL_NONE;
+}
+
+// Route of a block selection from Q and K, with its merge geometry.
+hs_status block_route(const Shape& s, int block, int n_blocks, SelRoute* r, BkGeom* g) {
+  hs_status st = bk_check(s, block, n_blocks, g);
+  if (st != HS_OK) return st;
+  if (use_prefill_blocks(s, block)) {
+    *r = SEL_PREFILL;
+  } else if (fused_decode_score(s)) {
+    *r = SEL_DECODE;
+  } else if (logits_fit(s)) {
+    *r = SEL_LOGITS;
+    return bk_check(s, block, n_blocks, g, true);
+  } else {
+    *r = SEL_NONE;
+    return fail(HS_ERR_UNSUPPORTED, "block selection: %zu bytes of logits for this shape exceed "
+                "the %zu-byte bound of the route for this group and head size", logit_bytes(s),
+                kMaxLogitBytes);
+  }
+  return HS_OK;
+}
+
+size_t block_select_ws(SelRoute r, const Shape& s, const BkGeom& g, int n_blocks) {
+  if (r == SEL_PREFILL) return 0;
+  if (r == SEL_LOGITS) return logit_bytes(s) + bk_ws(g, n_blocks);
+  return bk_ws(g, n_blocks);
 }
 
 // ---- sparse attention ----------------------------------------------------------------------
@@ -598,9 +673,10 @@ bool fused_blocks(const Shape& s, int block, int n_blocks) {
 size_t fused_blocks_ws(const Shape& s, int block, int n_blocks) {
   if (fused_blocks(s, block, n_blocks)) return 0;
   BkGeom g;
-  if (bk_check(s, block, n_blocks, &g) != HS_OK) return 0;
+  SelRoute r;
+  if (block_route(s, block, n_blocks, &r, &g) != HS_OK) return 0;
   const size_t a = full_attn_ws(s);
-  const size_t b = use_prefill_blocks(s, block) ? 0 : bk_ws(g, n_blocks);
+  const size_t b = block_select_ws(r, s, g, n_blocks);
   return a > b ? a : b;
 }
 
@@ -654,15 +730,20 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
   switch (op) {
     case HS_OP_FULL_ATTN: return full_attn_ws(s);
     case HS_OP_ORACLE_TOPK: {
-      if ((s.g != 4 && s.g != 8 && s.g != 16) || s.D > 128) return 0;
-      if (use_prefill_select(s, p0)) return tk_prefill_ws(s);
-      return tk_ws(s, tk_geom(s));
+      switch (token_route(s, p0)) {
+        case SEL_PREFILL: return tk_prefill_ws(s);
+        case SEL_DECODE: return tk_ws(s, tk_geom(s));
+        case SEL_LOGITS: return logit_bytes(s) + tk_ws(s, tl_geom(s));
+        case SEL_NONE: break;
+      }
+      fail(HS_ERR_UNSUPPORTED, "token selection: no route for this shape");
+      return 0;
     }
     case HS_OP_BLOCK_TOPK: {
       BkGeom g;
-      if (bk_check(s, p0, p1, &g) != HS_OK) return 0;
-      if (use_prefill_blocks(s, p0)) return 0;
-      return bk_ws(g, p1);
+      SelRoute r;
+      if (block_route(s, p0, p1, &r, &g) != HS_OK) return 0;
+      return block_select_ws(r, s, g, p1);
     }
     case HS_OP_SPARSE_ATTN: {
       if (p0 < 1 || p1 < 0) return 0;
@@ -725,7 +806,8 @@ hs_status hs_full_attn_block_topk(const hs_attn_desc* desc, const void* q, const
   }
   // two passes: every argument of both is checked before the first launch
   BkGeom g;
-  st = bk_check(s, block, n_blocks, &g);
+  SelRoute r;
+  st = block_route(s, block, n_blocks, &r, &g);
   if (st != HS_OK) return st;
   const size_t need = fused_blocks_ws(s, block, n_blocks);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -809,15 +891,14 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
+  st = check_qkv_dtype(s);
+  if (st != HS_OK) return st;
   if (!q || !k || !lse || !idx || !count) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
   if (k_global < 0 || window < 0) return fail(HS_ERR_INVALID_ARG, "k_global and window must be >= 0");
   if ((long long)k_global + window < 1) return fail(HS_ERR_INVALID_ARG, "k_global + window must be >= 1");
-  if (s.g != 4 && s.g != 8 && s.g != 16)
-    return fail(HS_ERR_UNSUPPORTED, "token selection needs a GQA group of 4, 8 or 16 (got %d)", s.g);
-  if (s.D > 128)
-    return fail(HS_ERR_UNSUPPORTED, "token selection from Q and K takes head_dim 64 or 128; "
-                "use the stored-logits path");
-  if (use_prefill_select(s, k_global)) {
+  const SelRoute route = token_route(s, k_global);
+  hipStream_t hst = (hipStream_t)stream;
+  if (route == SEL_PREFILL) {
     const size_t need = tk_prefill_ws(s);
     if (!ws || ws_bytes < need)
       return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
@@ -828,18 +909,35 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
     p.tbuf = (unsigned long long*)ws;
     p.idx = idx;
     p.cnt = count;
-    return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, false, (hipStream_t)stream),
+    return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, false, hst),
                       "token selection kernel");
   }
-  const TkGeom t = tk_geom(s);
-  const size_t need = tk_ws(s, t);
+  if (route == SEL_DECODE) {
+    const TkGeom t = tk_geom(s);
+    const size_t need = tk_ws(s, t);
+    if (!ws || ws_bytes < need)
+      return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    hs::TopkDecodeParams p = tk_params(s, t, lse, k_global, window, idx, count, ws);
+    p.q = q;
+    p.k = k;
+    return hip_status(hs::launch_topk_decode(p, s.D, s.in_f32, hst), "token top-k kernels");
+  }
+  if (route == SEL_NONE)
+    return fail(HS_ERR_UNSUPPORTED, "token selection: %zu bytes of logits for this shape exceed "
+                "the %zu-byte bound of the route for this group and head size", logit_bytes(s),
+                kMaxLogitBytes);
+  // logits of the rows first, then the selection from them
+  const TkGeom t = tl_geom(s);
+  const size_t lb = logit_bytes(s);
+  const size_t need = lb + tk_ws(s, t);
   if (!ws || ws_bytes < need)
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  hs::TopkDecodeParams p = tk_params(s, t, lse, k_global, window, idx, count, ws);
-  p.q = q;
-  p.k = k;
-  return hip_status(hs::launch_topk_decode(p, s.D, s.in_f32, (hipStream_t)stream),
-                    "token top-k kernels");
+  float* logits = (float*)ws;
+  hipError_t e = hs::launch_logits(logits_params(s, q, k, logits), s.D, s.in_f32, hst);
+  if (e != hipSuccess) return hip_status(e, "logits kernel");
+  hs::TopkDecodeParams p = tk_params(s, t, lse, k_global, window, idx, count, (char*)ws + lb);
+  p.logits = logits;
+  return hip_status(hs::launch_topk_from_logits(p, hst), "token top-k kernels");
 }
 
 hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const void* k,
@@ -849,27 +947,40 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
+  st = check_qkv_dtype(s);
+  if (st != HS_OK) return st;
   if (!q || !k || !lse || !blk_idx || !count) return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
   BkGeom g;
-  st = bk_check(s, block, n_blocks, &g);
+  SelRoute route;
+  st = block_route(s, block, n_blocks, &route, &g);
   if (st != HS_OK) return st;
-  if (use_prefill_blocks(s, block)) {
+  hipStream_t hst = (hipStream_t)stream;
+  if (route == SEL_PREFILL) {
     hs::PrefillSelectParams p = select_params(s, q, k, lse);
     p.block = block;
     p.n_blocks = n_blocks;
     p.idx = blk_idx;
     p.cnt = count;
-    return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, true, (hipStream_t)stream),
+    return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, true, hst),
                       "block selection kernel");
   }
-  const size_t need = bk_ws(g, n_blocks);
+  const size_t need = block_select_ws(route, s, g, n_blocks);
   if (!ws || ws_bytes < need)
     return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  hs::BlockTopkParams p = bk_params(s, g, lse, block, n_blocks, blk_idx, count, ws);
-  p.q = q;
-  p.k = k;
-  return hip_status(hs::launch_block_topk(p, s.D, s.in_f32, (hipStream_t)stream),
-                    "block top-k kernels");
+  if (route == SEL_DECODE) {
+    hs::BlockTopkParams p = bk_params(s, g, lse, block, n_blocks, blk_idx, count, ws);
+    p.q = q;
+    p.k = k;
+    return hip_status(hs::launch_block_topk(p, s.D, s.in_f32, hst), "block top-k kernels");
+  }
+  // logits of the rows first, then the selection from them
+  const size_t lb = logit_bytes(s);
+  float* logits = (float*)ws;
+  hipError_t e = hs::launch_logits(logits_params(s, q, k, logits), s.D, s.in_f32, hst);
+  if (e != hipSuccess) return hip_status(e, "logits kernel");
+  hs::BlockTopkParams p = bk_params(s, g, lse, block, n_blocks, blk_idx, count, (char*)ws + lb);
+  p.logits = logits;
+  return hip_status(hs::launch_block_from_logits(p, hst), "block top-k kernels");
 }
 
 hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const void* k_full,

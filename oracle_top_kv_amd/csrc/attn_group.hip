@@ -69,7 +69,9 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
   const int j = bq % p.Tq;
   const int b = bq / p.Tq;
   const long long t_row = p.q_off + j;  // this query's position: keys 0 .. t_row
-  const int h = u * p.g + hc * 16 + rn;
+  // the last chunk of a group that is not a multiple of 16 heads has rows without a head
+  const bool row_ok = hc * 16 + rn < p.g;
+  const int h = u * p.g + hc * 16 + (row_ok ? rn : 0);
 
   // list modes: the (b, t, u) list and its number of keys L (blocks count block keys each)
   const int32_t* list = nullptr;
@@ -109,7 +111,8 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
     const uint16_t* qp = (const uint16_t*)p.q + (((size_t)b * p.Tq + j) * p.Hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < C::KK; kk++)
-      qb[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * kk + 8 * jg));
+      qb[kk] = __builtin_bit_cast(bf16x8, row_ok ? *(const u32x4*)(qp + 32 * kk + 8 * jg)
+                                                 : u32x4{0, 0, 0, 0});
   }
 
   // tile loads: thread chunk c = threadIdx.x + kThreads * i is row c / CPR, 16 bytes ch = c % CPR
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
         sacc[kb] = mfma_bf16(ka, qb[kk], sacc[kb]);
       }
     const int key0 = s * kGStep;
-    if constexpr (LOGITS) {
+    if (LOGITS && row_ok) {
 #pragma unroll
       for (int kb = 0; kb < 4; kb++) {
         const int e0 = key0 + 16 * kb + 4 * jg;

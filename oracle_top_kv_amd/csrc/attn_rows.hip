@@ -127,7 +127,8 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   const int wave = threadIdx.x >> 6;
   const int rn = lane & 15;   // MFMA row / column index of this lane
   const int jg = lane >> 4;   // lane group 0..3
-  const int nrows = nq * p.hpc;  // a set: nq queries x the hpc heads of head chunk hc
+  const int hcn = min(p.hpc, p.g - hc * p.hpc);  // heads of chunk hc (the last may be short)
+  const int nrows = nq * hcn;  // a set: nq queries x the heads of head chunk hc
   const long long t_first = p.q_off + j0;
   const long long t_last = p.q_off + j0 + nq - 1;
 
@@ -147,8 +148,8 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
 
   // this lane's row (for Q, masks and statistics)
   const bool row_ok = rn < nrows;
-  const int jq = row_ok ? rn / p.hpc : 0;
-  const int hh = hc * p.hpc + (row_ok ? rn % p.hpc : 0);
+  const int jq = row_ok ? rn / hcn : 0;
+  const int hh = hc * p.hpc + (row_ok ? rn % hcn : 0);
   const long long t_row = p.q_off + j0 + jq;
   const int h = u * p.g + hh;
   const long long lo_row = (SRC == SRC_WINDOW) ? t_row - p.window + 1 : 0;
@@ -204,8 +205,8 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
     for (int c = lane; c < chunks; c += 64) {
       const int r = c / (n * 8), li = (c / 8) % n, qd = c % 8;
       const int e0 = (l_base + li * kWaves) * kStep + 4 * qd;  // range mode: entry = position
-      float* dst = p.logits + (((size_t)b * p.Tq + (j0 + r / p.hpc)) * p.Hq + u * p.g +
-                                hc * p.hpc + r % p.hpc) *
+      float* dst = p.logits + (((size_t)b * p.Tq + (j0 + r / hcn)) * p.Hq + u * p.g +
+                                hc * p.hpc + r % hcn) *
                                   (size_t)p.Tk + e0;
       const f32x4 val = *(const f32x4*)(lbuf + r * kLogitRow + li * kStep + 4 * qd);
       if (p.logits_vec && e0 + 3 < L) {
@@ -559,7 +560,8 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   const int set = ((b * p.Hkv + u) * p.sets_per_bu + sq) * p.cpq + hc;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);
-  const int nrows = nq * p.hpc;
+  const int hcn = min(p.hpc, p.g - hc * p.hpc);  // heads of chunk hc (the last may be short)
+  const int nrows = nq * hcn;
 
   constexpr int CPT = Cfg::kCPT;  // columns per merge thread
   PassOut<CPT> a;
@@ -568,8 +570,8 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
 
   const int r = threadIdx.x / Cfg::kTPR;
   const int lr = threadIdx.x % Cfg::kTPR;
-  const int jr = j0 + r / p.hpc;
-  const int hr = u * p.g + hc * p.hpc + r % p.hpc;
+  const int jr = j0 + r / hcn;
+  const int hr = u * p.g + hc * p.hpc + r % hcn;
   const size_t orow = ((size_t)b * p.Tq + jr) * p.Hq + hr;  // (b, t, h) of this thread's row
   float res[CPT];
   float lse_row = -INFINITY;
@@ -645,9 +647,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int b = bu / p.Hkv;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);
-  if (r >= nq * p.hpc) return;  // whole workgroup leaves together
-  const int jr = j0 + r / p.hpc;
-  const int hr = u * p.g + hc * p.hpc + r % p.hpc;
+  const int hcn = min(p.hpc, p.g - hc * p.hpc);  // heads of chunk hc (the last may be short)
+  if (r >= nq * hcn) return;  // whole workgroup leaves together
+  const int jr = j0 + r / hcn;
+  const int hr = u * p.g + hc * p.hpc + r % hcn;
   const int c = threadIdx.x % NC;
   const int sl = threadIdx.x / NC;
 

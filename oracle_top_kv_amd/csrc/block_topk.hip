@@ -178,9 +178,12 @@ __global__ __launch_bounds__(256) void blk_logit_score_kernel(BlockTopkParams p)
     bmax[i] = 0u;
   }
   if (threadIdx.x < G) {
-    const double l2 = (double)p.lse[((size_t)b * p.Hq + u * G + threadIdx.x) * p.Tq + j] * 1.4426950408889634;
-    const double C = rint((double)p.lse[((size_t)b * p.Hq + u * G) * p.Tq + j] * 1.4426950408889634);
-    dsh[threadIdx.x] = (float)(l2 - C);
+    // per-head shift LSE_h * log2(e) - C, C from the group's first head (as in the score pass);
+    // heads past the group's g (G is the instantiated bound) never score
+    const int hh = threadIdx.x;
+    const double l2 = hh < p.g ? (double)p.lse[((size_t)b * p.Hq + u * p.g + hh) * p.Tq + j] * 1.4426950408889634 : 0.0;
+    const double C = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
+    dsh[threadIdx.x] = hh < p.g ? (float)(l2 - C) : INFINITY;
   }
   __syncthreads();
   float delta[G];
@@ -189,14 +192,14 @@ __global__ __launch_bounds__(256) void blk_logit_score_kernel(BlockTopkParams p)
   const long long key_begin = blk_begin * p.block;  // a multiple of 16
   long long key_end = blk_end * p.block;
   if (key_end > t + 1) key_end = t + 1;
-  const float* lg = p.logits + (((size_t)b * p.Tq + j) * p.Hq + (size_t)u * G) * p.Tk;
+  const float* lg = p.logits + (((size_t)b * p.Tq + j) * p.Hq + (size_t)u * p.g) * p.Tk;
   for (long long base = key_begin; base < key_end; base += 256) {
     const long long pos = base + threadIdx.x;
     float v = -INFINITY;
     if (pos < key_end) {
       float x[G];
 #pragma unroll
-      for (int hh = 0; hh < G; hh++) x[hh] = lg[(size_t)hh * p.Tk + pos];
+      for (int hh = 0; hh < G; hh++) x[hh] = hh < p.g ? lg[(size_t)hh * p.Tk + pos] : 0.f;
 #pragma unroll
       for (int hh = 0; hh < G; hh++) v = fmaxf(v, __builtin_fmaf(x[hh], p.scale_log2, -delta[hh]));
     }
@@ -297,6 +300,10 @@ hipError_t launch_block_from_logits(const BlockTopkParams& p, hipStream_t stream
     case 48: return launch_blk_logits<48>(p, stream);
     case 64: return launch_blk_logits<64>(p, stream);
   }
+  // other group sizes run on the next larger instantiation, the extra heads masked
+  if (p.g < 32) return launch_blk_logits<32>(p, stream);
+  if (p.g < 48) return launch_blk_logits<48>(p, stream);
+  if (p.g < 64) return launch_blk_logits<64>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -190,6 +190,17 @@ int prefill_select_max_k();
 hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
                                  bool block_mode, hipStream_t stream);
 
+// ---- raw logits of few query rows (selection for shapes outside the fused score passes) ----
+struct LogitsParams {
+  const void* q;
+  const void* k;
+  int B, Tq, Tk, Hq, Hkv, g;
+  long long q_off;
+  int n_split, keys_per_split;  // key chunk per workgroup (a multiple of 256)
+  float* logits;                // [B, Tq, Hq, Tk] fp32: entries 0..t of query row t
+};
+hipError_t launch_logits(const LogitsParams& p, int head_dim, bool in_f32, hipStream_t stream);
+
 // ---- device-resident scratch of the no-allocation sparse-layer entry point ------------------
 // kScratchBytes of device memory held by the library for the life of the process, one copy per
 // device; scratch_buffer returns the current device's copy (its address is looked up once per

@@ -168,10 +168,12 @@ __global__ __launch_bounds__(256) void tk_logit_score_kernel(TopkDecodeParams p)
   const int b = row / (p.Hkv * p.Tq);
   for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = 0u;
   if (threadIdx.x < G) {
-    // per-head shift LSE_h * log2(e) - C, C from the group's first head (as in the score pass)
-    const double l2 = (double)p.lse[((size_t)b * p.Hq + u * G + threadIdx.x) * p.Tq + j] * 1.4426950408889634;
-    const double C = rint((double)p.lse[((size_t)b * p.Hq + u * G) * p.Tq + j] * 1.4426950408889634);
-    dsh[threadIdx.x] = (float)(l2 - C);
+    // per-head shift LSE_h * log2(e) - C, C from the group's first head (as in the score pass);
+    // heads past the group's g (G is the instantiated bound) never score
+    const int hh = threadIdx.x;
+    const double l2 = hh < p.g ? (double)p.lse[((size_t)b * p.Hq + u * p.g + hh) * p.Tq + j] * 1.4426950408889634 : 0.0;
+    const double C = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
+    dsh[threadIdx.x] = hh < p.g ? (float)(l2 - C) : INFINITY;
   }
   __syncthreads();
   float delta[G];
@@ -181,12 +183,12 @@ __global__ __launch_bounds__(256) void tk_logit_score_kernel(TopkDecodeParams p)
   const long long k_begin = (long long)split * p.keys_per_split;
   long long k_end = k_begin + p.keys_per_split;
   if (k_end > t - p.window + 1) k_end = t - p.window + 1;  // candidates 0 .. t - w
-  const float* lg = p.logits + (((size_t)b * p.Tq + j) * p.Hq + (size_t)u * G) * p.Tk;
+  const float* lg = p.logits + (((size_t)b * p.Tq + j) * p.Hq + (size_t)u * p.g) * p.Tk;
   uint32_t* keys_row = p.keys + (size_t)row * p.Tk;
   for (long long pos = k_begin + threadIdx.x; pos < k_end; pos += 256) {
     float x[G];
 #pragma unroll
-    for (int hh = 0; hh < G; hh++) x[hh] = lg[(size_t)hh * p.Tk + pos];
+    for (int hh = 0; hh < G; hh++) x[hh] = hh < p.g ? lg[(size_t)hh * p.Tk + pos] : 0.f;
     float v = -INFINITY;
 #pragma unroll
     for (int hh = 0; hh < G; hh++) v = fmaxf(v, __builtin_fmaf(x[hh], p.scale_log2, -delta[hh]));
@@ -663,6 +665,10 @@ hipError_t launch_topk_from_logits(const TopkDecodeParams& p, hipStream_t stream
     case 48: return launch_tk_logits<48>(p, stream);
     case 64: return launch_tk_logits<64>(p, stream);
   }
+  // other group sizes run on the next larger instantiation, the extra heads masked
+  if (p.g < 32) return launch_tk_logits<32>(p, stream);
+  if (p.g < 48) return launch_tk_logits<48>(p, stream);
+  if (p.g < 64) return launch_tk_logits<64>(p, stream);
   return hipErrorInvalidValue;
 }
 

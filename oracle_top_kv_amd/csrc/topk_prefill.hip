@@ -203,9 +203,11 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// G: query heads per KV head (4, 8 or 16).  NE: block-list entries per lane (n_blocks <= 16 NE).
+// G: query heads per KV head in the row layout (4, 8 or 16); a group of p.g < G heads is padded
+// to G (the rows of heads p.g .. G-1 hold no query and never score).  NE: block-list entries per
+// lane (n_blocks <= 16 NE).
 template <int D, bool F32, bool BLOCK, int G, int NE>
-__global__ __launch_bounds__(kThreads, F32 ? 1 : 2) void pf_select_kernel(PrefillSelectParams p) {
+__global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_kernel(PrefillSelectParams p) {
   using C = PsCfg<D, F32>;
   constexpr int NW = kThreads / 64;  // waves
   constexpr int HQ = G / 4;          // head quarters per query
@@ -244,8 +246,9 @@ __global__ __launch_bounds__(kThreads, F32 ? 1 : 2) void pf_select_kernel(Prefil
       const int qg = rb / HQ, hq = rb % HQ;
       const int jq = wq0 + 4 * qg + rn / 4;
       const int hh = 4 * hq + rn % 4;
-      const bool ok = jq < nq;
-      const size_t qoff = (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + u * G + hh) * D;
+      const bool ok = jq < nq && hh < p.g;
+      const size_t qoff =
+          (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + u * p.g + (ok ? hh : 0)) * D;
       if constexpr (!F32) {
         const uint16_t* qp = (const uint16_t*)p.q + qoff;
 #pragma unroll
@@ -269,13 +272,14 @@ __global__ __launch_bounds__(kThreads, F32 ? 1 : 2) void pf_select_kernel(Prefil
       const int jq = wq0 + 4 * qg + jg;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        if (jq < nq) {
-          const int j = j0 + jq, hh = 4 * hq + e;
-          const double l2 = (double)p.lse[((size_t)b * p.Hq + u * G + hh) * p.Tq + j] * 1.4426950408889634;
-          const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * G) * p.Tq + j] * 1.4426950408889634);
+        const int hh = 4 * hq + e;
+        if (jq < nq && hh < p.g) {
+          const int j = j0 + jq;
+          const double l2 = (double)p.lse[((size_t)b * p.Hq + u * p.g + hh) * p.Tq + j] * 1.4426950408889634;
+          const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
           delta[rb][e] = (float)(l2 - Cq);
         } else {
-          delta[rb][e] = INFINITY;  // queries past the last one never score
+          delta[rb][e] = INFINITY;  // queries past the last one, padding heads: never score
         }
       }
     }
@@ -546,14 +550,18 @@ void launch_g(const PrefillSelectParams& p, dim3 grid, hipStream_t stream) {
   pf_select_kernel<D, F32, BLOCK, G, 1><<<grid, kThreads, 0, stream>>>(p);
 }
 
+// The row layout's group size: the group padded to 4, 8 or 16 heads.
+int layout_group(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
+
 template <int D, bool F32, bool BLOCK>
 void launch_dfb(const PrefillSelectParams& p, hipStream_t stream) {
-  const int qpw = kRowsWG / p.g;  // queries per workgroup
+  const int G = layout_group(p.g);
+  const int qpw = kRowsWG / G;  // queries per workgroup
   const int n_qt = (p.Tq + qpw - 1) / qpw;
   const dim3 grid(p.B * p.Hkv * n_qt);
-  if (p.g == 4)
+  if (G == 4)
     launch_g<D, F32, BLOCK, 4>(p, grid, stream);
-  else if (p.g == 8)
+  else if (G == 8)
     launch_g<D, F32, BLOCK, 8>(p, grid, stream);
   else
     launch_g<D, F32, BLOCK, 16>(p, grid, stream);
@@ -566,11 +574,14 @@ int prefill_select_max_k() { return kSortCap; }
 
 hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
                                  bool block_mode, hipStream_t stream) {
-  if (p.g != 4 && p.g != 8 && p.g != 16) return hipErrorInvalidValue;
+  if (p.g < 1 || p.g > 16) return hipErrorInvalidValue;
   if (block_mode && (p.block < 16 || p.block > 64 || (p.block & (p.block - 1)) ||
                      p.n_blocks < 1 || p.n_blocks > kMaxBlocks))
     return hipErrorInvalidValue;
-  if (head_dim == 128) {
+  if (head_dim == 256) {  // bf16 only
+    if (in_f32) return hipErrorInvalidValue;
+    if (block_mode) launch_dfb<256, false, true>(p, stream); else launch_dfb<256, false, false>(p, stream);
+  } else if (head_dim == 128) {
     if (in_f32) {
       if (block_mode) launch_dfb<128, true, true>(p, stream); else launch_dfb<128, true, false>(p, stream);
     } else {

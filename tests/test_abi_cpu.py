@@ -42,7 +42,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
     (dict(q_len=0), hs.HS_ERR_INVALID_ARG),
     (dict(q_offset=1024), hs.HS_ERR_INVALID_ARG),
     (dict(q_len=4, q_offset=1021), hs.HS_ERR_INVALID_ARG),
-    (dict(n_q_heads=40, n_kv_heads=2), hs.HS_ERR_UNSUPPORTED),   # g = 20: not a multiple of 16
+    (dict(n_q_heads=130, n_kv_heads=2), hs.HS_ERR_UNSUPPORTED),  # g = 65
     (dict(n_q_heads=128, n_kv_heads=1), hs.HS_ERR_UNSUPPORTED),  # g = 128
     (dict(head_dim=256, in_dtype=hs.HS_F32), hs.HS_ERR_UNSUPPORTED),
     (dict(in_dtype=7), hs.HS_ERR_INVALID_ARG),
@@ -100,9 +100,21 @@ def test_topk_argument_checks():
                             None) == hs.HS_ERR_INVALID_ARG
     assert L.hs_oracle_topk(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, 1 << 40,
                             None) == hs.HS_ERR_INVALID_ARG
-    d3 = desc(n_q_heads=6, n_kv_heads=2)  # g = 3
-    assert L.hs_oracle_topk(ctypes.byref(d3), FAKE, FAKE, FAKE, 16, 4, FAKE, FAKE, FAKE, 1 << 40,
-                            None) == hs.HS_ERR_UNSUPPORTED
+    # every group size up to 64 and head size 256 have a route; a workspace one byte short is
+    # refused before anything is enqueued
+    for kw in (dict(n_q_heads=6, n_kv_heads=2), dict(n_q_heads=48, n_kv_heads=2),
+               dict(n_q_heads=64, n_kv_heads=1, head_dim=256),
+               dict(q_len=64, n_q_heads=24, n_kv_heads=2),
+               dict(q_len=64, n_q_heads=64, n_kv_heads=1, head_dim=256)):
+        dk = desc(**kw)
+        need = L.hs_workspace_size(hs.HS_OP_ORACLE_TOPK, ctypes.byref(dk), 16, 4)
+        assert need > 0, kw
+        assert L.hs_oracle_topk(ctypes.byref(dk), FAKE, FAKE, FAKE, 16, 4, FAKE, FAKE, FAKE,
+                                need - 1, None) == hs.HS_ERR_WORKSPACE, kw
+        needb = L.hs_workspace_size(hs.HS_OP_BLOCK_TOPK, ctypes.byref(dk), 64, 16)
+        if needb > 0:
+            assert L.hs_block_score_topk(ctypes.byref(dk), FAKE, FAKE, FAKE, 64, 16, FAKE, FAKE,
+                                         FAKE, needb - 1, None) == hs.HS_ERR_WORKSPACE, kw
 
 
 def test_block_topk_argument_checks():
@@ -111,7 +123,8 @@ def test_block_topk_argument_checks():
     for block, n_blocks in ((48 + 8, 16), (64, 0), (64, 65)):
         assert L.hs_block_score_topk(ctypes.byref(d), FAKE, FAKE, FAKE, block, n_blocks, FAKE, FAKE,
                                      FAKE, 1 << 40, None) == hs.HS_ERR_UNSUPPORTED
-    d2 = desc(n_q_heads=4, n_kv_heads=2)  # g = 2
+    # head size 256 with fp32 inputs has no kernel
+    d2 = desc(head_dim=256, in_dtype=hs.HS_F32)
     assert L.hs_block_score_topk(ctypes.byref(d2), FAKE, FAKE, FAKE, 64, 16, FAKE, FAKE, FAKE,
                                  1 << 40, None) == hs.HS_ERR_UNSUPPORTED
     assert L.hs_last_error().decode()

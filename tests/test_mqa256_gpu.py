@@ -143,11 +143,15 @@ def test_paged_mqa256_equals_contiguous():
 
 
 def test_unsupported_combinations_are_rejected():
-    wl = Workload("rj", 1, 1, 500, 64, 1, 256, "bf16", seed=731)
+    """Head size 256 takes bf16 inputs only: fp32 calls are refused before any launch (the
+    selection calls included, which accept every group size and head size 256 in bf16)."""
+    wl = Workload("rj", 1, 1, 500, 64, 1, 256, "f32", seed=731)
     x = make_inputs(wl, device="cuda")
-    _, lse = hs().full_attn_fwd(x["q"], x["k"], x["v"])
+    lse = torch.zeros((1, 64, 1), dtype=torch.float32, device="cuda")
     with pytest.raises(hs().HsError):
-        hs().oracle_topk(x["q"], x["k"], lse, 64, 16)  # Q/K selection: g and d too large
+        hs().full_attn_fwd(x["q"], x["k"], x["v"])
+    with pytest.raises(hs().HsError):
+        hs().oracle_topk(x["q"], x["k"], lse, 64, 16)
     with pytest.raises(hs().HsError):
         hs().block_score_topk(x["q"], x["k"], lse, 64, 4)
 
