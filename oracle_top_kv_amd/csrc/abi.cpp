@@ -308,14 +308,24 @@ hs::TopkDecodeParams tk_params(const Shape& s, const TkGeom& t, const float* lse
   return p;
 }
 
-// Group sizes and head sizes the streamed prefill selection takes (the group sits in the rows of
-// one 256-row tile; smaller groups are padded to 4, 8 or 16 heads).
-bool prefill_select_shape(const Shape& s) { return s.g <= 16 && (s.D <= 128 || !s.in_f32); }
+// Group sizes and head sizes the streamed prefill selection takes: groups of up to 16 heads sit
+// in the rows of one 256-row tile (padded to 4, 8 or 16 heads); larger groups select per chunk
+// of 16 heads and merge the chunks' candidates.
+bool prefill_select_shape(const Shape& s) { return s.g <= 64 && (s.D <= 128 || !s.in_f32); }
+int select_chunks(const Shape& s) { return s.g <= 16 ? 1 : (s.g + 15) / 16; }
+size_t select_chunk_rows(const Shape& s) {
+  return (size_t)s.B * s.Tq * s.Hkv * select_chunks(s);
+}
+
+bool logits_fit(const Shape& s);
 
 // Many query rows per KV head: selection streams over K tiles and stores no per-key score.
+// Chunked groups (above 16 heads) need 16 queries to fill a tile's rows; with fewer, computed
+// logits serve them unless those would be too large.
 bool use_prefill_select(const Shape& s, int k_global) {
-  return (long long)s.Tq * s.g > 16 && prefill_select_shape(s) &&
-         k_global <= hs::prefill_select_max_k();
+  if (!prefill_select_shape(s) || k_global > hs::prefill_select_max_k()) return false;
+  if (s.g <= 16) return (long long)s.Tq * s.g > 16;
+  return s.Tq >= 16 || !logits_fit(s);
 }
 
 // The fused decode score passes (score, key and histogram in one kernel over K tiles).
@@ -360,8 +370,18 @@ hs::LogitsParams logits_params(const Shape& s, const void* q, const void* k, flo
 
 enum SelRoute { SEL_NONE, SEL_PREFILL, SEL_DECODE, SEL_LOGITS };
 
+// candidate buffers of the (chunk) rows, then, with chunks, their kept counts
 size_t tk_prefill_ws(const Shape& s) {
-  return align_up((size_t)s.B * s.Tq * s.Hkv * hs::prefill_select_buffer_cap() * 8, 256);
+  const size_t rows = select_chunk_rows(s);
+  const size_t buf = align_up(rows * hs::prefill_select_buffer_cap() * 8, 256);
+  return buf + (select_chunks(s) > 1 ? align_up(rows * 4, 256) : 0);
+}
+
+// block mode: nothing for a whole group; with chunks, their kept values and counts
+size_t bk_prefill_ws(const Shape& s, int n_blocks) {
+  if (select_chunks(s) == 1) return 0;
+  const size_t rows = select_chunk_rows(s);
+  return align_up(rows * (size_t)n_blocks * 8, 256) + align_up(rows * 4, 256);
 }
 
 hs::PrefillSelectParams select_params(const Shape& s, const void* q, const void* k,
@@ -379,6 +399,7 @@ hs::PrefillSelectParams select_params(const Shape& s, const void* q, const void*
   p.g = s.g;
   p.q_off = s.q_off;
   p.scale_log2 = s.scale_log2;
+  p.chunks = select_chunks(s);
   return p;
 }
 
@@ -421,7 +442,9 @@ hs_status bk_check(const Shape& s, int block, int n_blocks, BkGeom* g, bool per_
 
 // Many query rows per KV head and blocks that tile 64 keys: streamed running top-n.
 bool use_prefill_blocks(const Shape& s, int block) {
-  return (long long)s.Tq * s.g > 16 && 64 % block == 0 && prefill_select_shape(s);
+  if (64 % block || !prefill_select_shape(s)) return false;
+  if (s.g <= 16) return (long long)s.Tq * s.g > 16;
+  return s.Tq >= 16 || !logits_fit(s);
 }
 
 size_t bk_ws(const BkGeom& g, int n_blocks) {
@@ -457,7 +480,7 @@ hs_status block_route(const Shape& s, int block, int n_blocks, SelRoute* r, BkGe
 }
 
 size_t block_select_ws(SelRoute r, const Shape& s, const BkGeom& g, int n_blocks) {
-  if (r == SEL_PREFILL) return 0;
+  if (r == SEL_PREFILL) return bk_prefill_ws(s, n_blocks);
   if (r == SEL_LOGITS) return logit_bytes(s) + bk_ws(g, n_blocks);
   return bk_ws(g, n_blocks);
 }
@@ -907,6 +930,8 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
     p.window = window;
     p.cap = k_global + window;
     p.tbuf = (unsigned long long*)ws;
+    if (p.chunks > 1)
+      p.ccnt = (int32_t*)((char*)ws + align_up(select_chunk_rows(s) * hs::prefill_select_buffer_cap() * 8, 256));
     p.idx = idx;
     p.cnt = count;
     return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, false, hst),
@@ -955,18 +980,22 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
   st = block_route(s, block, n_blocks, &route, &g);
   if (st != HS_OK) return st;
   hipStream_t hst = (hipStream_t)stream;
+  const size_t need = block_select_ws(route, s, g, n_blocks);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if (route == SEL_PREFILL) {
     hs::PrefillSelectParams p = select_params(s, q, k, lse);
     p.block = block;
     p.n_blocks = n_blocks;
     p.idx = blk_idx;
     p.cnt = count;
+    if (p.chunks > 1) {
+      p.cvals = (unsigned long long*)ws;
+      p.ccnt = (int32_t*)((char*)ws + align_up(select_chunk_rows(s) * (size_t)n_blocks * 8, 256));
+    }
     return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, true, hst),
                       "block selection kernel");
   }
-  const size_t need = block_select_ws(route, s, g, n_blocks);
-  if (!ws || ws_bytes < need)
-    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if (route == SEL_DECODE) {
     hs::BlockTopkParams p = bk_params(s, g, lse, block, n_blocks, blk_idx, count, ws);
     p.q = q;

@@ -184,6 +184,13 @@ struct PrefillSelectParams {
   // outputs
   int32_t* idx;
   int32_t* cnt;
+  // groups of more than 16 heads: `chunks` chunks of 16 heads select on their own (rows of
+  // virtual KV head u * chunks + c), keeping their candidates with their values; a merge over the
+  // chunks gives the group's set (exact: a key among the group's best is among the best of the
+  // chunk that attains its group maximum).  chunks == 1: the group selects as a whole.
+  int chunks;
+  int32_t* ccnt;               // [B, Tq, Hkv * chunks] entries kept per chunk row
+  unsigned long long* cvals;   // block mode: [B, Tq, Hkv * chunks, n_blocks] kept values
 };
 int prefill_select_buffer_cap();
 int prefill_select_max_k();

@@ -226,9 +226,14 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
   // query 4qg+j, head 4hq+e.  The S = Q K^T output then gives lane (key, j) heads 4hq..4hq+3 of
   // query 4qg+j in every block of the group: the group maximum over all G heads is in-lane.
   const int n_qt = (p.Tq + QPW - 1) / QPW;
-  const int u = blockIdx.x % p.Hkv;
-  const int qt = n_qt - 1 - (int)((blockIdx.x / p.Hkv) % n_qt);
-  const int b = blockIdx.x / (p.Hkv * n_qt);
+  // rows of (virtual) KV head uv: chunk c of the group of KV head u (chunks == 1: the group)
+  const int HV = p.Hkv * p.chunks;
+  const int uv = blockIdx.x % HV;
+  const int u = uv / p.chunks, c = uv % p.chunks;
+  const int hbase = u * p.g + c * 16;                    // first query head of the rows
+  const int gc = p.chunks > 1 ? min(16, p.g - c * 16) : p.g;  // heads of the rows
+  const int qt = n_qt - 1 - (int)((blockIdx.x / HV) % n_qt);
+  const int b = blockIdx.x / (HV * n_qt);
   const int j0 = qt * QPW;
   const int nq = min(QPW, p.Tq - j0);
   const int tq0 = (int)p.q_off + j0;  // positions fit in 31 bits
@@ -246,9 +251,9 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
       const int qg = rb / HQ, hq = rb % HQ;
       const int jq = wq0 + 4 * qg + rn / 4;
       const int hh = 4 * hq + rn % 4;
-      const bool ok = jq < nq && hh < p.g;
+      const bool ok = jq < nq && hh < gc;
       const size_t qoff =
-          (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + u * p.g + (ok ? hh : 0)) * D;
+          (((size_t)b * p.Tq + j0 + (ok ? jq : 0)) * p.Hq + hbase + (ok ? hh : 0)) * D;
       if constexpr (!F32) {
         const uint16_t* qp = (const uint16_t*)p.q + qoff;
 #pragma unroll
@@ -273,9 +278,9 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int hh = 4 * hq + e;
-        if (jq < nq && hh < p.g) {
+        if (jq < nq && hh < gc) {
           const int j = j0 + jq;
-          const double l2 = (double)p.lse[((size_t)b * p.Hq + u * p.g + hh) * p.Tq + j] * 1.4426950408889634;
+          const double l2 = (double)p.lse[((size_t)b * p.Hq + hbase + hh) * p.Tq + j] * 1.4426950408889634;
           const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
           delta[rb][e] = (float)(l2 - Cq);
         } else {
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const unsigned long long qmask = 0xFFFFull << (16 * jg);  // lanes of this lane's query
   auto buf_of = [&](int wq) {
-    return p.tbuf + ((size_t)((size_t)b * p.Tq + j0 + wq0 + wq) * p.Hkv + u) * kBufCap;
+    return p.tbuf + ((size_t)((size_t)b * p.Tq + j0 + wq0 + wq) * HV + uv) * kBufCap;
   };
 
   if (n_tiles > 0) {
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
       const int jq = wq0 + wq;
       if (jq >= nq) break;
       const int t = tq0 + jq;
-      const long long row = ((long long)b * p.Tq + j0 + jq) * p.Hkv + u;
+      const long long row = ((long long)b * p.Tq + j0 + jq) * HV + uv;
       if constexpr (!BLOCK) {
         const int n_cand = max(t - p.window + 1, 0);
         const int k_eff = min(n_cand, p.k_global);
@@ -494,6 +499,13 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
         int* sb = sortbuf[wave];
         const int n = __shfl(cnt[qg], 16 * jj, 64);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // appends complete before reloads
+        if (p.chunks > 1) {  // keep the chunk's best k_eff values for the merge
+          int kept = n;
+          if (n > k_eff) wave_compact(bufq, n, k_eff, lane, whist[wave], nullptr, 0, &kept);
+          if (lane == 0) p.ccnt[row] = kept;
+          wave_sync_lds();
+          continue;
+        }
         if (n > k_eff) {
           int kept_final;
           wave_compact(bufq, n, k_eff, lane, whist[wave], sb, 0, &kept_final);
@@ -520,6 +532,11 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
       } else {
         const int n_take = min((t >> bshift) + 1, p.n_blocks);
         const unsigned long long* Lq = blist[wave * QW + wq];
+        if (p.chunks > 1) {  // the chunk's best n_take values for the merge
+          if (lane < n_take) p.cvals[(size_t)row * p.n_blocks + lane] = Lq[lane];
+          if (lane == 0) p.ccnt[row] = n_take;
+          continue;
+        }
         int32_t* out = p.idx + (size_t)row * p.n_blocks;
         // real entries occupy slots 0 .. n_take-1 (empties are replaced in slot order)
         if (lane < p.n_blocks) {
@@ -539,6 +556,176 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
   }
 }
 
+// ---- merge of the chunk rows of a group of more than 16 heads -------------------------------
+// Every key of the group's top k is among the top k of the chunk that attains its group maximum,
+// with its group score: the union of the chunk lists, each key at its largest listed value,
+// ranked by value, gives the group's set exactly.
+constexpr int kMergeCap = 4 * kSortCap;  // up to 4 chunks of k entries
+
+// Ascending bitonic sort of n (a power of two) 64-bit keys in LDS by the whole workgroup.
+__device__ void block_bitonic_u64(unsigned long long* a, int n) {
+  for (int kk = 2; kk <= n; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int i = threadIdx.x; i < n; i += kThreads) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const unsigned long long x = a[i], y = a[ixj];
+          if ((x > y) == ((i & kk) == 0)) {
+            a[i] = y;
+            a[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pos_of_value(unsigned long long v) {
+  return 0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull);
+}
+
+__global__ __launch_bounds__(kThreads) void pf_merge_tokens_kernel(PrefillSelectParams p) {
+  __shared__ unsigned long long a[kMergeCap];
+  __shared__ int n_sh;
+  const int row = blockIdx.x;  // (b * Tq + j) * Hkv + u
+  const int u = row % p.Hkv;
+  const int j = (row / p.Hkv) % p.Tq;
+  const int b = row / (p.Hkv * p.Tq);
+  const int t = (int)(p.q_off + j);
+  const int n_cand = max(t - p.window + 1, 0);
+  const int k_eff = min(n_cand, p.k_global);
+  const int HV = p.Hkv * p.chunks;
+  // gather the chunk lists; key (position << 32 | ~score bits): a position's largest value first
+  if (threadIdx.x == 0) n_sh = 0;
+  __syncthreads();
+  int base = 0;
+  for (int c = 0; c < p.chunks; c++) {
+    const size_t rv = ((size_t)b * p.Tq + j) * HV + (size_t)u * p.chunks + c;
+    const int n = p.ccnt[rv];
+    const unsigned long long* src = p.tbuf + rv * kBufCap;
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const unsigned long long v = src[i];
+      a[base + i] = ((unsigned long long)pos_of_value(v) << 32) |
+                    (unsigned long long)(0xFFFFFFFFu - (uint32_t)(v >> 32));
+    }
+    base += n;
+  }
+  int P = 1;
+  while (P < base) P <<= 1;
+  for (int i = base + threadIdx.x; i < P; i += kThreads) a[i] = ~0ull;
+  __syncthreads();
+  block_bitonic_u64(a, P);
+  // first entry of each position: back to its value; later ones (smaller values) and the
+  // padding: 0.  Stored complemented, so that an ascending sort ranks by value descending.
+  unsigned long long keep[kMergeCap / kThreads];
+#pragma unroll
+  for (int r = 0; r < kMergeCap / kThreads; r++) {
+    const int i = threadIdx.x + r * kThreads;
+    unsigned long long out = ~0ull;
+    if (i < base) {
+      const unsigned long long x = a[i];
+      const bool first = i == 0 || (a[i - 1] >> 32) != (x >> 32);
+      if (first) {
+        const uint32_t pos = (uint32_t)(x >> 32);
+        const uint32_t sc = 0xFFFFFFFFu - (uint32_t)(x & 0xFFFFFFFFull);
+        out = ~(((unsigned long long)sc << 32) | (unsigned long long)(0xFFFFFFFFu - pos));
+      }
+    }
+    keep[r] = out;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kMergeCap / kThreads; r++) {
+    const int i = threadIdx.x + r * kThreads;
+    if (i < P) a[i] = keep[r];
+  }
+  __syncthreads();
+  block_bitonic_u64(a, P);
+  // the k_eff best (lowest complemented values): their positions, sorted ascending
+  int M = 1;
+  while (M < k_eff) M <<= 1;
+  unsigned long long sel[kSortCap / kThreads];
+#pragma unroll
+  for (int r = 0; r < kSortCap / kThreads; r++) {
+    const int i = threadIdx.x + r * kThreads;
+    sel[r] = i < k_eff ? (unsigned long long)pos_of_value(~a[i]) : ~0ull;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kSortCap / kThreads; r++) {
+    const int i = threadIdx.x + r * kThreads;
+    if (i < M) a[i] = sel[r];
+  }
+  __syncthreads();
+  if (k_eff > 1) block_bitonic_u64(a, M);
+  const int w0 = max(t - p.window + 1, 0);
+  const int n_win = t - w0 + 1;
+  int32_t* out = p.idx + (size_t)row * p.cap;
+  for (int i = threadIdx.x; i < p.cap; i += kThreads) {
+    int32_t val = -1;
+    if (i < k_eff) val = (int32_t)a[i];
+    else if (i < k_eff + n_win) val = w0 + (i - k_eff);
+    out[i] = val;
+  }
+  if (threadIdx.x == 0) p.cnt[row] = k_eff + n_win;
+}
+
+__global__ __launch_bounds__(kThreads) void pf_merge_blocks_kernel(PrefillSelectParams p) {
+  __shared__ unsigned long long a[4 * kMaxBlocks];
+  __shared__ bool is_best[4 * kMaxBlocks];
+  __shared__ int sel[kMaxBlocks];
+  const int row = blockIdx.x;
+  const int u = row % p.Hkv;
+  const int j = (row / p.Hkv) % p.Tq;
+  const int b = row / (p.Hkv * p.Tq);
+  const int t = (int)(p.q_off + j);
+  const int bshift = __ffs(p.block) - 1;
+  const int n_take = min((t >> bshift) + 1, p.n_blocks);
+  const int HV = p.Hkv * p.chunks;
+  int n = 0;
+  for (int c = 0; c < p.chunks; c++) {
+    const size_t rv = ((size_t)b * p.Tq + j) * HV + (size_t)u * p.chunks + c;
+    const int m = p.ccnt[rv];
+    for (int i = threadIdx.x; i < m; i += kThreads) a[n + i] = p.cvals[rv * p.n_blocks + i];
+    n += m;
+  }
+  __syncthreads();
+  // each block at its largest listed value (the first of equal copies)
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const unsigned long long v = a[i];
+    const uint32_t id = pos_of_value(v);
+    bool best = true;
+    for (int o = 0; o < n; o++) {
+      const unsigned long long w = a[o];
+      if (pos_of_value(w) == id && (w > v || (w == v && o < i))) best = false;
+    }
+    is_best[i] = best;
+  }
+  __syncthreads();
+  // rank among those by value
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    if (!is_best[i]) continue;
+    const unsigned long long v = a[i];
+    int rank = 0;
+    for (int o = 0; o < n; o++) rank += is_best[o] && a[o] > v;
+    if (rank < n_take) sel[rank] = (int)pos_of_value(v);
+  }
+  __syncthreads();
+  int32_t* out = p.idx + (size_t)row * p.n_blocks;
+  for (int s2 = threadIdx.x; s2 < p.n_blocks; s2 += kThreads) {
+    if (s2 < n_take) {
+      const int id = sel[s2];
+      int pos = 0;
+      for (int o = 0; o < n_take; o++) pos += sel[o] < id;
+      out[pos] = id;
+    } else {
+      out[s2] = -1;
+    }
+  }
+  if (threadIdx.x == 0) p.cnt[row] = n_take;
+}
+
 template <int D, bool F32, bool BLOCK, int G>
 void launch_g(const PrefillSelectParams& p, dim3 grid, hipStream_t stream) {
   if constexpr (BLOCK) {
@@ -555,10 +742,10 @@ int layout_group(int g) { return g <= 4 ? 4 : (g <= 8 ? 8 : 16); }
 
 template <int D, bool F32, bool BLOCK>
 void launch_dfb(const PrefillSelectParams& p, hipStream_t stream) {
-  const int G = layout_group(p.g);
+  const int G = p.chunks > 1 ? 16 : layout_group(p.g);
   const int qpw = kRowsWG / G;  // queries per workgroup
   const int n_qt = (p.Tq + qpw - 1) / qpw;
-  const dim3 grid(p.B * p.Hkv * n_qt);
+  const dim3 grid(p.B * p.Hkv * p.chunks * n_qt);
   if (G == 4)
     launch_g<D, F32, BLOCK, 4>(p, grid, stream);
   else if (G == 8)
@@ -574,7 +761,9 @@ int prefill_select_max_k() { return kSortCap; }
 
 hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
                                  bool block_mode, hipStream_t stream) {
-  if (p.g < 1 || p.g > 16) return hipErrorInvalidValue;
+  if (p.g < 1 || p.g > 64 || p.chunks != (p.g + 15) / 16) return hipErrorInvalidValue;
+  if (p.chunks > 4 || (p.chunks > 1 && (!p.ccnt || (block_mode && !p.cvals)))) return hipErrorInvalidValue;
+  if (!block_mode && p.k_global > kSortCap) return hipErrorInvalidValue;
   if (block_mode && (p.block < 16 || p.block > 64 || (p.block & (p.block - 1)) ||
                      p.n_blocks < 1 || p.n_blocks > kMaxBlocks))
     return hipErrorInvalidValue;
@@ -593,6 +782,13 @@ hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, boo
     } else {
       if (block_mode) launch_dfb<64, false, true>(p, stream); else launch_dfb<64, false, false>(p, stream);
     }
+  }
+  if (p.chunks > 1) {  // one merge workgroup per (b, t, u)
+    const dim3 grid((unsigned)((long long)p.B * p.Tq * p.Hkv));
+    if (block_mode)
+      pf_merge_blocks_kernel<<<grid, kThreads, 0, stream>>>(p);
+    else
+      pf_merge_tokens_kernel<<<grid, kThreads, 0, stream>>>(p);
   }
   return hipGetLastError();
 }

@@ -68,6 +68,16 @@ CASES = [
                                     window=64, block=64, n_blocks=8, seed=1015)),
     ("tiny_f32_g3", Workload("t3", 1, 40, 200, 3, 1, 64, "f32", k_global=32, window=8,
                              block=16, n_blocks=4, seed=1016)),
+    # 16 queries and more with groups above 16 heads: the streamed selection per 16-head chunk
+    # and the exact merge of the chunks' candidates (shrunk HySparse2 prefill: MQA 64/1, d 256)
+    ("prefill_g24_chunks", Workload("pc24", 1, 40, 1600, 24, 1, 128, "bf16", k_global=200,
+                                    window=32, block=64, n_blocks=8, seed=1017)),
+    ("prefill_mqa64_d256_chunks", Workload("pcm", 1, 48, 3000, 64, 1, 256, "bf16",
+                                           k_global=512, window=64, block=64, n_blocks=16,
+                                           seed=1018)),
+    ("prefill_g40_d64_chunks_compactions", Workload("pc40", 1, 20, 6000, 40, 1, 64, "bf16",
+                                                    k_global=1024, window=128, block=32,
+                                                    n_blocks=16, seed=1019)),
 ]
 
 
