@@ -296,6 +296,8 @@ def main():
     if not args.no_block_prefill:
         out["block_prefill"] = block_prefill_leg(args)
     out["mqa256_decode"] = mqa256_leg(args)
+    if not args.no_prefill:
+        out["mqa256_prefill"] = mqa256_prefill_leg()
     if not args.no_long_decode:
         out["long_decode"] = long_decode_leg(args, cpu=not args.no_cpu_baseline)
     if not args.no_sweep:
@@ -444,6 +446,48 @@ def prefill_leg(args):
             "sparse_layer_logical_GB_per_s": round(b_sp / (t_sp * 1e-3) / 1e9, 1),
             "sparse_layer_tflops": round(f_sp / (t_sp * 1e-3) / 1e12, 1),
             "peak_tflops": 2500.0, "reps": reps}
+
+
+def mqa256_prefill_leg():
+    """HySparse2's own head shape (MQA: 64 query heads on one KV head, d 256) in prefill: a
+    4096-query chunk appended to a 131072-token cache.  Full attention on the tiled prefill
+    kernel (128 rows per workgroup), token top-k per 16-head chunk with the exact chunk merge
+    (no per-key score is stored), one token-sparse layer; TFLOP/s as in the 80B prefill leg."""
+    import torch
+
+    from oracle_top_kv_amd import costs, hs
+    from oracle_top_kv_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["prefill_mqa256_128k"]
+    x = make_inputs(wl, device=torch.device("cuda:0"), n_sparse=1)
+    q, k, v, qs = x["q"], x["k"], x["v"], x["q_sparse"][0]
+    _, lse = hs.full_attn_fwd(q, k, v)
+    idx, cnt = hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+    hs.sparse_attn_gather(qs, k, v, idx, cnt, kind="token")
+    torch.cuda.synchronize()
+    reps = 5
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record()
+        _, lse = hs.full_attn_fwd(q, k, v)
+        ev[r][1].record()
+        idx, cnt = hs.oracle_topk(q, k, lse, wl.k_global, wl.window)
+        ev[r][2].record()
+        hs.sparse_attn_gather(qs, k, v, idx, cnt, kind="token")
+        ev[r][3].record()
+    torch.cuda.synchronize()
+    t_fa, t_tk, t_sp = (sum(e[i].elapsed_time(e[i + 1]) for e in ev) / reps for i in range(3))
+    f_fa, f_sc = costs.full_attn_flops(wl), costs.score_flops(wl)
+    del x, q, k, v, qs, lse, idx, cnt
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "full_attn_ms": round(t_fa, 3), "topk_ms": round(t_tk, 3),
+            "full_attn_tflops": round(f_fa / (t_fa * 1e-3) / 1e12, 1),
+            "mfma_frac_full_attn": round(f_fa / (t_fa * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "topk_score_tflops": round(f_sc / (t_tk * 1e-3) / 1e12, 1),
+            "full_attn_plus_topk_tflops": round((f_fa + f_sc) / ((t_fa + t_tk) * 1e-3) / 1e12, 1),
+            "sparse_layer_ms": round(t_sp, 3),
+            "sparse_layer_logical_GB_per_s": round(rate(costs.token_gather_bytes(wl), t_sp), 1),
+            "reps": reps}
 
 
 def paged_step(wl, x, hs, args, ms_contiguous, page_size=64):

@@ -38,9 +38,10 @@
  *     (groups padded to 4, 8 or 16 heads); few rows with g in {4, 8, 16} and head_dim <= 128
  *     run the fused score passes; every other shape first computes the rows' raw logits into
  *     the workspace (at most 8 GiB of them: B * q_len * Hq * kv_len * 4 bytes, else
- *     HS_ERR_UNSUPPORTED) and selects from them like stored logits.  head_dim 256 attention
- *     runs on the decode-shaped kernels (any q_len; the gated sparse layer as two branches plus
- *     a combine).  Anything else returns HS_ERR_UNSUPPORTED.
+ *     HS_ERR_UNSUPPORTED) and selects from them like stored logits.  Full attention with many
+ *     query rows per KV head runs a tiled kernel (bf16; 256 rows per workgroup, 128 at head
+ *     size 256, which the group size must divide); the sparse layers at head size 256 run as
+ *     two branches plus a combine.  Anything else returns HS_ERR_UNSUPPORTED.
  *   - Workspace sizes, for orientation: token selection with many query rows per KV head and
  *     k_global <= 1024 keeps a 16 KiB candidate buffer per (b, t, u); with few rows it keeps
  *     4 bytes per candidate key per (b, t, u) plus an 8 KiB histogram (12 bytes per key past
@@ -224,10 +225,11 @@ hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const v
  * full-width stores).  Entries i <= t of query row t are the attention logits times sqrt(d);
  * entries past t are unspecified (those of the last query row's range are written, larger ones
  * not).  Always runs on the split row kernel (the group kernel for groups of 32-64 heads with
- * bf16 inputs and head_dim 128 or 256), whatever q_len is; o and lse are bit-identical to what
- * hs_full_attn_fwd returns for the same inputs on that kernel (whenever hs_full_attn_fwd does
- * not take the prefill kernel: q_len * g <= 16, fp32 inputs, or groups above 16 with fewer than
- * 128 query rows per KV head).  Workspace: hs_workspace_size(HS_OP_FULL_ATTN_LOGITS, ...). */
+ * bf16 inputs and head_dim 128 or 256; groups above 16 heads), whatever q_len is; o and lse are
+ * bit-identical to what hs_full_attn_fwd returns for the same inputs on that kernel (whenever
+ * hs_full_attn_fwd does not take the tiled prefill kernel: q_len * g <= 16, fp32 inputs, groups
+ * above 16 with fewer than 128 query rows per KV head, or groups that do not divide the tiled
+ * kernel's rows).  Workspace: hs_workspace_size(HS_OP_FULL_ATTN_LOGITS, ...). */
 hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const void* k,
                                   const void* v, void* o, float* lse, float* logits, void* ws,
                                   size_t ws_bytes, void* stream);

@@ -178,9 +178,11 @@ constexpr long long kResidentWorkgroups = 512;  // 256 CUs x 2 workgroups of thi
 // Many queries per KV head (bf16): the LDS-tiled prefill kernel; otherwise the row kernel.
 // (A group of more than 16 heads needs at least 128 rows per KV head to fill half a workgroup;
 // with fewer, the row kernel's key splits do better.)
+// (Head size 256 runs 128 rows per workgroup, smaller heads 256: the group must divide them.)
 bool use_prefill_kernel(const Shape& s) {
   const long long rows = (long long)s.Tq * s.g;
-  return !s.in_f32 && s.D <= 128 && rows > 16 && (s.g <= 16 || rows >= 128) && 256 % s.g == 0;
+  const int rows_wg = s.D > 128 ? 128 : 256;
+  return !s.in_f32 && rows > 16 && (s.g <= 16 || rows >= 128) && rows_wg % s.g == 0;
 }
 
 // Kernels that read Q, K, V take head_dim 256 with bf16 inputs only.
@@ -687,7 +689,7 @@ hs::PrefillParams prefill_params(const Shape& s, const void* q, const void* k, c
 // Block selection inside the prefill attention pass: blocks of one 64-key tile, at most 16
 // blocks per list.
 bool fused_blocks(const Shape& s, int block, int n_blocks) {
-  return use_prefill_kernel(s) && 32 % s.g == 0 && block == 64 && n_blocks >= 1 &&
+  return use_prefill_kernel(s) && s.D <= 128 && 32 % s.g == 0 && block == 64 && n_blocks >= 1 &&
          n_blocks <= 16;
 }
 

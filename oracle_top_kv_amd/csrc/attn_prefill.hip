@@ -32,9 +32,8 @@
 namespace hs {
 namespace {
 
-constexpr int kRowsWG = 256;
-constexpr int kThreads = 512;
-constexpr int kBN = 64;
+constexpr int kThreads = 512;  // 8 waves (head sizes up to 128; the block-selection merge)
+constexpr int kBN = 64;  // keys per tile (head sizes up to 128; the BSEL block size)
 constexpr float kLazy = 8.f;  // see the lazy rescale in the tile step
 constexpr int kBufferConfig = 0x00020000;  // buffer descriptor word 3 (gfx9 family: raw dwords)
 constexpr int kNonTemporal = 2;            // cache-policy bit of a buffer load: non-temporal
@@ -51,8 +50,16 @@ __device__ __forceinline__ float max_halves(float v) {
   return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
+// Head size 256 runs 4 waves (one per SIMD, so that each wave can hold 32 rows' O accumulators
+// of 256 columns, its Q operand and two S blocks): 128 rows per workgroup.  Smaller heads run 8
+// waves, 256 rows.
 template <int D>
 struct PfCfg {
+  static constexpr int NW = D > 128 ? 4 : 8;  // waves
+  static constexpr int Threads = 64 * NW;
+  static constexpr int RowsWG = 32 * NW;      // (query, head) rows per workgroup
+  static constexpr int BN = D > 128 ? 32 : kBN;  // keys per tile (256: registers)
+  static constexpr int KB = BN / 32;            // 32-key MFMA blocks per tile
   static constexpr int KStr = D + 8;    // K tile row stride (elements): conflict-free ds_read_b128
   // V tile row stride: a transpose read covers 4 rows x 2 column groups per 32 lanes; rows 16
   // dwords apart (mod 64 banks) make it conflict-free
@@ -60,7 +67,7 @@ struct PfCfg {
   static constexpr int KK = D / 16;     // MFMA steps over d
   static constexpr int DB = D / 32;     // 32-wide d blocks of O
   static constexpr int CPR = D / 8;     // 16-byte chunks per row
-  static constexpr int LPT = kBN * CPR / kThreads;  // chunks per thread per tile (each of K and V)
+  static constexpr int LPT = BN * CPR / Threads;  // chunks per thread per tile (each of K and V)
 };
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -159,19 +166,22 @@ __device__ __forceinline__ void select_blocks(const PrefillParams& p,
 //   A[32 x 16]: row l % 32, k = 8h .. 8h + 7;   B[16 x 32]: column l % 32, k = 8h .. 8h + 7
 //   C[32 x 32]: column l % 32, register 4g + e holds row 8g + 4h + e (g, e = 0..3)
 template <int D, bool BSEL>
-__global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
+__global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillParams p) {
   using C = PfCfg<D>;
+  static_assert(!BSEL || C::NW == 8, "the block-selection merge assumes 8 waves");
   // K/V tiles; BSEL reuses the same LDS for its merge after the last tile
-  constexpr int kTileBytes = 2 * kBN * (C::KStr + C::VStr) * 2;
+  constexpr int BN = C::BN, KB = C::KB;
+  static_assert(!BSEL || BN == 64, "blocks of one 64-key tile");
+  constexpr int kTileBytes = 2 * BN * (C::KStr + C::VStr) * 2;
   constexpr int kSmemBytes = BSEL && kMergeBytes > kTileBytes ? kMergeBytes : kTileBytes;
   __shared__ __attribute__((aligned(16))) unsigned char pf_smem[kSmemBytes];
-  uint16_t (*ks)[kBN * C::KStr] = reinterpret_cast<uint16_t (*)[kBN * C::KStr]>(pf_smem);
-  uint16_t (*vs)[kBN * C::VStr] =
-      reinterpret_cast<uint16_t (*)[kBN * C::VStr]>(pf_smem + 2 * kBN * C::KStr * 2);
+  uint16_t (*ks)[BN * C::KStr] = reinterpret_cast<uint16_t (*)[BN * C::KStr]>(pf_smem);
+  uint16_t (*vs)[BN * C::VStr] =
+      reinterpret_cast<uint16_t (*)[BN * C::VStr]>(pf_smem + 2 * BN * C::KStr * 2);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rj = lane & 31, h = lane >> 5;
-  const int qpw = kRowsWG / p.g;  // queries per workgroup
+  const int qpw = C::RowsWG / p.g;  // queries per workgroup
   const int n_qt = (p.Tq + qpw - 1) / qpw;
   // KV head fastest, then query tile (latest, i.e. longest, first), then batch
   const int u = blockIdx.x % p.Hkv;
@@ -210,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   const size_t kv_row_stride = (size_t)p.Hkv * D;
   const uint16_t* kbase = (const uint16_t*)p.k + ((size_t)b * p.Tk * p.Hkv + u) * D;
   const uint16_t* vbase = (const uint16_t*)p.v + ((size_t)b * p.Tk * p.Hkv + u) * D;
-  const int n_tiles = (t_max + kBN) / kBN;  // tiles covering keys 0..t_max
+  const int n_tiles = (t_max + BN) / BN;  // tiles covering keys 0..t_max
 
   // K tiles run one tile ahead of V tiles: the step of tile t takes the softmax of S(t), computed
   // in the previous step, while S(t+1) = K(t+1) Q^T runs on the matrix cores, then O += V(t) P(t).
@@ -226,13 +236,13 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   int voff[C::LPT];
 #pragma unroll
   for (int i = 0; i < C::LPT; i++) {
-    const int c = threadIdx.x + kThreads * i;
+    const int c = threadIdx.x + C::Threads * i;
     voff[i] = (c / C::CPR) * row_bytes + (c % C::CPR) * 16;
   }
   auto tile_rsrc = [&](const uint16_t* base, int t) {
-    const int valid = max(0, min(kBN, t_max + 1 - t * kBN));
+    const int valid = max(0, min(BN, t_max + 1 - t * BN));
     const int n_rec = __builtin_amdgcn_readfirstlane(valid * row_bytes);  // uniform: scalar
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)t * kBN * kv_row_stride), 0,
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)t * BN * kv_row_stride), 0,
                                              n_rec, kBufferConfig);
   };
   u32x4 kreg[C::LPT], vreg[C::LPT];
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::LPT; i++) {
-      const int c = threadIdx.x + kThreads * i;
+      const int c = threadIdx.x + C::Threads * i;
       const int row = c / C::CPR, ch = c % C::CPR;
       *(u32x4*)(&ks[buf][row * C::KStr + ch * 8]) = kreg[i];
     }
@@ -259,21 +269,21 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   auto store_v = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::LPT; i++) {
-      const int c = threadIdx.x + kThreads * i;
+      const int c = threadIdx.x + C::Threads * i;
       const int row = c / C::CPR, ch = c % C::CPR;
       *(u32x4*)(&vs[buf][row * C::VStr + ch * 8]) = vreg[i];
     }
   };
   // S^T of tile t for the two 32-key blocks: register 4g + e of s[kb] is key 64t + 32kb + 8g + 4h + e
-  auto qk = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
+  auto qk = [&](int t, f32x16 (&s)[KB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
+    for (int kb = 0; kb < KB; kb++)
 #pragma unroll
       for (int i = 0; i < 16; i++) s[kb][i] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < C::KK; kk++) {  // the two key blocks' chains interleaved
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++) {
+      for (int kb = 0; kb < KB; kb++) {
         const bf16x8 ka = *(const bf16x8*)(&ks[t & 1][(32 * kb + rj) * C::KStr + 16 * kk + 8 * h]);
         s[kb] = mfma32(ka, qb[kk], s[kb]);
       }
@@ -303,21 +313,21 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   store_k(1);
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0);  // Q loads done here, not inside the loop
-  f32x16 sa[2], sb[2];
+  f32x16 sa[KB], sb[KB];
   qk(0, sa);
   __syncthreads();  // the first step rewrites K buffer 0
 
   // The step of tile t: S(t) in sc, S(t+1) into sn.  MASK: tile t reaches past the workgroup's
   // first query position.
-  auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], auto mask_tag)
+  auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB], auto mask_tag)
                   __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     load_k(t + 2);
     load_v(t + 1);
-    const int key0 = t * kBN;
+    const int key0 = t * BN;
     if constexpr (MASK) {
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++)
+      for (int kb = 0; kb < KB; kb++)
 #pragma unroll
         for (int i = 0; i < 16; i++) {
           const int key = key0 + 32 * kb + 8 * (i / 4) + 4 * h + (i % 4);
@@ -326,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
+    for (int kb = 0; kb < KB; kb++)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[kb][i], sc[kb][i + 1]));
     mx = max_halves(mx);
@@ -363,9 +373,9 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float psum = 0.f;
-    bf16x8 pb[2][2];
+    bf16x8 pb[KB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
+    for (int kb = 0; kb < KB; kb++) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; s2++) {
         float x8[8];
@@ -382,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
     // O^T += V^T P^T over four 16-key steps; step (kb, s2) covers keys key0 + 32kb + 16s2 + {4h+e,
     // 8+4h+e}, the order in which pb[kb][s2] holds them
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
+    for (int kb = 0; kb < KB; kb++) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; s2++) {
         const int kbase_row = 32 * kb + 16 * s2 + 4 * h;
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
   // tiles entirely at or before the first query position need no mask.  Two steps per loop
   // trip, so that S(t) always sits in sa for even t and in sb for odd t; a tile without mask
   // may run the masked step (the mask is then a no-op)
-  const int n_full = min(n_tiles, (t_min + 1) / kBN);
+  const int n_full = min(n_tiles, (t_min + 1) / BN);
   int t = 0;
   for (; t + 1 < n_full; t += 2) {
     step(t, sa, sb, std::false_type());
@@ -470,12 +480,17 @@ __global__ __launch_bounds__(kThreads, 1) void pf_attn_kernel(PrefillParams p) {
 }  // namespace
 
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t stream) {
-  const int qpw = kRowsWG / p.g;
+  const int rows_wg = head_dim == 256 ? PfCfg<256>::RowsWG : PfCfg<128>::RowsWG;
+  if (rows_wg % p.g) return hipErrorInvalidValue;
+  const int qpw = rows_wg / p.g;
   const int n_qt = (p.Tq + qpw - 1) / qpw;
   const dim3 grid(p.B * p.Hkv * n_qt);
   const bool bsel = p.blk_idx != nullptr;
-  if (bsel && (p.n_blocks < 1 || p.n_blocks > 16 || 32 % p.g)) return hipErrorInvalidValue;
-  if (head_dim == 128) {
+  if (bsel && (p.n_blocks < 1 || p.n_blocks > 16 || 32 % p.g || head_dim > 128))
+    return hipErrorInvalidValue;
+  if (head_dim == 256) {
+    pf_attn_kernel<256, false><<<grid, PfCfg<256>::Threads, 0, stream>>>(p);
+  } else if (head_dim == 128) {
     if (bsel) pf_attn_kernel<128, true><<<grid, kThreads, 0, stream>>>(p);
     else pf_attn_kernel<128, false><<<grid, kThreads, 0, stream>>>(p);
   } else {

@@ -82,6 +82,9 @@ WORKLOADS: Dict[str, Workload] = {
     # 32k context, 16 needles, 1 full + 3 sparse layers
     "decode_mqa256_32k": Workload("decode_mqa256_32k", 8, 1, 32768, 64, 1, 256, "bf16",
                                   n_sparse=3, needles=16, needle_logit=8.0, seed=606),
+    # the same head shape in prefill: a 4096-query chunk appended to a 131072-token cache
+    "prefill_mqa256_128k": Workload("prefill_mqa256_128k", 1, 4096, 135168, 64, 1, 256, "bf16",
+                                    n_sparse=1, seed=707),
 }
 
 

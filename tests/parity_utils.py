@@ -18,13 +18,16 @@ LSE_TOL = 1e-6
 
 
 def lse_bound(lse_ref):
-    """Bound on |LSE_gpu - LSE_oracle|: 1e-6, or one fp32 ulp at the largest |LSE| when that is
-    coarser.  Below |LSE| = 16 (every workload of the pages' shape) the ulp is 9.5e-7 and the
-    bound is 1e-6; the stress profiles that push logits to 20 and more get the fp32 spacing of
-    their values (1.9e-6 in [16, 32)), which an fp32 result cannot beat."""
+    """Bound on |LSE_gpu - LSE_oracle|: 1e-6 while every |LSE| stays below 16 (every workload of
+    the pages' shape, where the fp32 spacing is 9.5e-7); beyond, for the stress profiles that push
+    logits to 20 and more, two fp32 ulps of the largest |LSE| (3.8e-6 in [16, 32)): the fp32
+    result holds at best half an ulp, and the fp32 dot product behind the largest logit (its raw
+    value sqrt(d) times larger) carries about one more."""
     m = float(np.max(np.abs(np.asarray(lse_ref, dtype=np.float64)[np.isfinite(lse_ref)]),
                      initial=0.0))
-    return max(LSE_TOL, float(np.spacing(np.float32(m))))
+    if m < 16.0:
+        return LSE_TOL
+    return 2.0 * float(np.spacing(np.float32(m)))
 
 
 def check_token_sets(gpu_idx, gpu_cnt, orc_idx, orc_cnt, q, k, lse, k_global, window, q_offset,

@@ -53,13 +53,16 @@ def test_full_attention_and_logits_selection(name, wl):
     bi, bc = hs().block_topk_from_logits(lg, lse, wl.n_kv_heads, wl.head_dim, wl.block,
                                          wl.n_blocks)
     torch.cuda.synchronize()
-    if wl.q_len * wl.n_q_heads // wl.n_kv_heads < 128 or wl.head_dim == 256:
-        assert torch.equal(o, o2) and torch.equal(lse, lse2)  # the same row kernel
+    if wl.q_len * wl.n_q_heads // wl.n_kv_heads < 128:
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)  # the same split kernel
     qn, kn, vn = (to_numpy_f32(x[n]) for n in ("q", "k", "v"))
     o_ref, lse_ref = oracle.full_attention(qn, kn, vn)
     eo, el = max_abs(o.cpu().numpy(), o_ref), max_abs(lse.cpu().numpy(), lse_ref)
     say(f"  full attention max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
     assert eo <= TOL_BF16 and el <= LSE_TOL
+    # without logits, many query rows run the tiled prefill kernel
+    eo2, el2 = max_abs(o2.cpu().numpy(), o_ref), max_abs(lse2.cpu().numpy(), lse_ref)
+    assert eo2 <= TOL_BF16 and el2 <= LSE_TOL
     oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window)
     ex = check_token_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, qn, kn, lse_ref,
                           wl.k_global, wl.window, wl.q_offset)

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from oracle_top_kv_amd.inputs import Workload, make_inputs, to_numpy_f32
-from parity_utils import LSE_TOL, lse_bound, TOL_BF16, TOL_F32, check_block_sets, check_token_sets, max_abs
+from parity_utils import (LSE_TOL, TOL_BF16, TOL_F32, check_block_sets, check_token_sets,
+                          lse_bound, max_abs)
 
 pytestmark = pytest.mark.gpu
 
@@ -556,3 +557,20 @@ def test_scale_is_applied_everywhere(name, wl, scale):
     es, eg = max_abs(so.cpu().numpy(), so_ref), max_abs(go.cpu().numpy(), go_ref)
     say(f"  token-sparse max|dO| = {es:.3e}  gated block layer max|dO| = {eg:.3e}")
     assert es <= tol and eg <= tol
+
+
+@pytest.mark.parametrize("profile", ["step", "linear_rise"])
+def test_full_attn_d256_prefill_moving_maximum(profile):
+    """Head size 256 on the tiled prefill kernel (128 rows per workgroup, 32-key tiles) with a
+    row maximum that moves by more than the lazy-rescale margin."""
+    wl = Workload("mv256", 1, 96, 2500, 16, 2, 256, "bf16", seed=43)
+    say(f"[full_attn d256 moving maximum] {profile} {wl}")
+    q, k, v = logit_profile_inputs(wl, PROFILES[profile])
+    o, lse = hs().full_attn_fwd(to_dev(q), to_dev(k), to_dev(v), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.full_attention(to_numpy_f32(q), to_numpy_f32(k), to_numpy_f32(v))
+    eo = max_abs(o.cpu().numpy(), o_ref)
+    el = max_abs(lse.cpu().numpy(), lse_ref)
+    say(f"  max|dO| = {eo:.3e}  max|dLSE| = {el:.3e}")
+    assert eo <= TOL_BF16
+    assert el <= lse_bound(lse_ref)
