@@ -169,8 +169,9 @@ def _opt_f32(x):
 def masked_attention(q, k, v, idx, count, q_offset=None, rows=None, sink=None, out_gate=None,
                      scale=None):
     """Attention of q over k, v restricted to each row's index set (dense masked softmax).
-    sink: [Hq] per-head sink logits in the denominator; out_gate: [B,Tq,Hq] sigmoid output-gate
-    logits.  Returns (o float64, lse float64; lse includes the sink)."""
+    sink: [Hq] per-head sink logits in the denominator; out_gate: sigmoid output-gate logits,
+    [B,Tq,Hq] (one per head) or [B,Tq,Hq,d] (one per channel).  Returns (o float64, lse float64;
+    lse includes the sink)."""
     s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
@@ -182,9 +183,11 @@ def masked_attention(q, k, v, idx, count, q_offset=None, rows=None, sink=None, o
     rr, rp, nr = _rows(rows)
     sk, skp = _opt_f32(sink)
     og, ogp = _opt_f32(out_gate)
-    _check(lib().orc_masked_attention_ex(ctypes.byref(s), qp, kp, vp, ip, cp, int(idx.shape[-1]),
-                                         skp, ogp, o.ctypes.data_as(ctypes.c_void_p),
-                                         lse.ctypes.data_as(ctypes.c_void_p), rp, nr),
+    fn = lib().orc_masked_attention_ex
+    if og is not None and og.ndim == q.ndim:
+        fn = lib().orc_masked_attention_ch
+    _check(fn(ctypes.byref(s), qp, kp, vp, ip, cp, int(idx.shape[-1]), skp, ogp,
+              o.ctypes.data_as(ctypes.c_void_p), lse.ctypes.data_as(ctypes.c_void_p), rp, nr),
            "masked_attention")
     return o, lse
 
@@ -223,9 +226,12 @@ def block_topk(q, k, lse, block, n_blocks, q_offset=None, rows=None, scale=None)
 
 def gated_block_swa(q, k, v, blk_idx, count, block, k_loc, v_loc, window, gate, q_offset=None,
                     rows=None, sink=None, sink_loc=None, out_gate=None, scale=None):
-    """HySparse sparse layer; sink / sink_loc: [Hq] sink logits of the two branches, out_gate:
-    [B,Tq,Hq] sigmoid output-gate logits on the gated sum.  Returns (o, o_glob, o_loc), all
-    float64 [B,Tq,Hq,d] (o_glob, o_loc: the normalized branches before the gates)."""
+    """HySparse sparse layer.  gate: the two branch-gate logits (zG, zL), [B,Tq,Hq,2] (per head)
+    or [B,Tq,Hq,2,d] (per channel); sink / sink_loc: [Hq] sink logits of the two branches;
+    out_gate: sigmoid output-gate logits on the gated sum, [B,Tq,Hq] or [B,Tq,Hq,d] (per-channel
+    gates come as a pair: both gate and out_gate per channel, or out_gate None).  Returns
+    (o, o_glob, o_loc), all float64 [B,Tq,Hq,d] (o_glob, o_loc: the normalized branches before
+    the gates)."""
     s = _shape(q, k, q_offset, scale)
     q, qp = _f32(q)
     k, kp = _f32(k)
@@ -242,10 +248,12 @@ def gated_block_swa(q, k, v, blk_idx, count, block, k_loc, v_loc, window, gate, 
     sk, skp = _opt_f32(sink)
     sl, slp = _opt_f32(sink_loc)
     ogt, ogtp = _opt_f32(out_gate)
-    _check(lib().orc_gated_block_swa_ex(ctypes.byref(s), qp, kp, vp, bp, cp, int(bi.shape[-1]),
-                                        int(block), klp, vlp, int(window), gp, skp, slp, ogtp,
-                                        o.ctypes.data_as(ctypes.c_void_p),
-                                     og.ctypes.data_as(ctypes.c_void_p),
-                                     ol.ctypes.data_as(ctypes.c_void_p), rp, nr),
+    per_channel = gt.ndim == q.ndim + 1
+    if ogt is not None and per_channel != (ogt.ndim == q.ndim):
+        raise ValueError("gated_block_swa: gate and out_gate must both be per head or per channel")
+    fn = lib().orc_gated_block_swa_ch if per_channel else lib().orc_gated_block_swa_ex
+    _check(fn(ctypes.byref(s), qp, kp, vp, bp, cp, int(bi.shape[-1]), int(block), klp, vlp,
+              int(window), gp, skp, slp, ogtp, o.ctypes.data_as(ctypes.c_void_p),
+              og.ctypes.data_as(ctypes.c_void_p), ol.ctypes.data_as(ctypes.c_void_p), rp, nr),
            "gated_block_swa")
     return o, og, ol

@@ -327,10 +327,44 @@ int orc_masked_attention(const orc_shape* s, const float* q, const float* k, con
  * SWA layer has a sigmoid output gate and a learnable per-head sink bias; P4 experimental setup:
  * per-head sink bias in the manner of gpt-oss]: LSE' = ln(e^{s_h} + sum_{i in I} e^{a_i}),
  * o = sigmoid(g) sum_{i in I} e^{a_i - LSE'} v_i. */
+/* Output gate of the sparse and sliding-window layers: one logit per (query, head) (out_gate,
+ * [B, Tq, Hq]) or one per channel (out_gate_ch, [B, Tq, Hq, d]) [P1 section 6.1 (gated
+ * attention); P2 "Two sigmoid gates, not one of two": a gate may act per head or per channel].
+ * Returns the factor of channel c; 1 without a gate. */
+static double out_gate_factor(const orc_shape* s, const float* out_gate, const float* out_gate_ch,
+                              int b, int j, int h, int c) {
+  const int64_t row = ((int64_t)b * s->q_len + j) * s->n_q_heads + h;
+  if (out_gate_ch) return sigmoid((double)out_gate_ch[row * s->head_dim + c]);
+  if (out_gate) return sigmoid((double)out_gate[row]);
+  return 1.0;
+}
+
+static int masked_attention(const orc_shape* s, const float* q, const float* k, const float* v,
+                            const int32_t* idx, const int32_t* count, int cap, const float* sink,
+                            const float* out_gate, const float* out_gate_ch, double* o,
+                            double* lse, const int32_t* rows, int n_rows);
+
 int orc_masked_attention_ex(const orc_shape* s, const float* q, const float* k, const float* v,
                             const int32_t* idx, const int32_t* count, int cap, const float* sink,
                             const float* out_gate, double* o, double* lse, const int32_t* rows,
                             int n_rows) {
+  return masked_attention(s, q, k, v, idx, count, cap, sink, out_gate, NULL, o, lse, rows,
+                          n_rows);
+}
+
+int orc_masked_attention_ch(const orc_shape* s, const float* q, const float* k, const float* v,
+                            const int32_t* idx, const int32_t* count, int cap, const float* sink,
+                            const float* out_gate_ch, double* o, double* lse,
+                            const int32_t* rows, int n_rows) {
+  if (!out_gate_ch) return ORC_EINVAL;
+  return masked_attention(s, q, k, v, idx, count, cap, sink, NULL, out_gate_ch, o, lse, rows,
+                          n_rows);
+}
+
+static int masked_attention(const orc_shape* s, const float* q, const float* k, const float* v,
+                            const int32_t* idx, const int32_t* count, int cap, const float* sink,
+                            const float* out_gate, const float* out_gate_ch, double* o,
+                            double* lse, const int32_t* rows, int n_rows) {
   if (!shape_ok(s) || !q || !k || !v || !idx || !count || !o || cap < 1 ||
       !rows_ok(s, rows, n_rows))
     return ORC_EINVAL;
@@ -364,10 +398,9 @@ int orc_masked_attention_ex(const orc_shape* s, const float* q, const float* k, 
       const double L = with_sink(lse_of(a, keep, t + 1), sink, h);
       double* out = o + q_at(s, b, j, h);
       weighted_sum(s, v, b, u, a, keep, t + 1, L, out);
-      if (out_gate) {
-        const double gv = sigmoid((double)out_gate[((int64_t)b * s->q_len + j) * s->n_q_heads + h]);
-        for (int c = 0; c < s->head_dim; c++) out[c] *= gv;
-      }
+      if (out_gate || out_gate_ch)
+        for (int c = 0; c < s->head_dim; c++)
+          out[c] *= out_gate_factor(s, out_gate, out_gate_ch, b, j, h, c);
       if (lse) lse[lse_at(s, b, h, j)] = L;
     }
     free(a);
@@ -478,6 +511,13 @@ int orc_gated_block_swa(const orc_shape* s, const float* q, const float* k, cons
                                 gate, NULL, NULL, NULL, o, o_glob, o_loc, rows, n_rows);
 }
 
+static int gated_block_swa(const orc_shape* s, const float* q, const float* k, const float* v,
+                           const int32_t* blk_idx, const int32_t* count, int n_blocks, int block,
+                           const float* k_loc, const float* v_loc, int window, const float* gate,
+                           const float* gate_ch, const float* sink, const float* sink_loc,
+                           const float* out_gate, const float* out_gate_ch, double* o,
+                           double* o_glob, double* o_loc, const int32_t* rows, int n_rows);
+
 /* The gated layer with a per-head sink in each branch and an output gate applied to the sum
  * (same sources as orc_masked_attention_ex). */
 int orc_gated_block_swa_ex(const orc_shape* s, const float* q, const float* k, const float* v,
@@ -486,8 +526,36 @@ int orc_gated_block_swa_ex(const orc_shape* s, const float* q, const float* k, c
                            const float* sink, const float* sink_loc, const float* out_gate,
                            double* o, double* o_glob, double* o_loc, const int32_t* rows,
                            int n_rows) {
-  if (!shape_ok(s) || !q || !k || !v || !blk_idx || !count || !k_loc || !v_loc || !gate || !o ||
-      n_blocks < 1 || block < 1 || window < 1 || !rows_ok(s, rows, n_rows))
+  if (!gate) return ORC_EINVAL;
+  return gated_block_swa(s, q, k, v, blk_idx, count, n_blocks, block, k_loc, v_loc, window, gate,
+                         NULL, sink, sink_loc, out_gate, NULL, o, o_glob, o_loc, rows, n_rows);
+}
+
+/* The gated layer with per-channel gates [P2 "Two sigmoid gates, not one of two": each gate may
+ * act per head or per channel]: o_c = sigmoid(zG_c) o_glob,c + sigmoid(zL_c) o_loc,c with
+ * gate_ch [B, Tq, Hq, 2, d] (the d logits of zG, then the d of zL), and an optional per-channel
+ * output gate out_gate_ch [B, Tq, Hq, d] on the sum. */
+int orc_gated_block_swa_ch(const orc_shape* s, const float* q, const float* k, const float* v,
+                           const int32_t* blk_idx, const int32_t* count, int n_blocks, int block,
+                           const float* k_loc, const float* v_loc, int window,
+                           const float* gate_ch, const float* sink, const float* sink_loc,
+                           const float* out_gate_ch, double* o, double* o_glob, double* o_loc,
+                           const int32_t* rows, int n_rows) {
+  if (!gate_ch) return ORC_EINVAL;
+  return gated_block_swa(s, q, k, v, blk_idx, count, n_blocks, block, k_loc, v_loc, window, NULL,
+                         gate_ch, sink, sink_loc, NULL, out_gate_ch, o, o_glob, o_loc, rows,
+                         n_rows);
+}
+
+static int gated_block_swa(const orc_shape* s, const float* q, const float* k, const float* v,
+                           const int32_t* blk_idx, const int32_t* count, int n_blocks, int block,
+                           const float* k_loc, const float* v_loc, int window, const float* gate,
+                           const float* gate_ch, const float* sink, const float* sink_loc,
+                           const float* out_gate, const float* out_gate_ch, double* o,
+                           double* o_glob, double* o_loc, const int32_t* rows, int n_rows) {
+  if (!shape_ok(s) || !q || !k || !v || !blk_idx || !count || !k_loc || !v_loc ||
+      (!gate && !gate_ch) || !o || n_blocks < 1 || block < 1 || window < 1 ||
+      !rows_ok(s, rows, n_rows))
     return ORC_EINVAL;
   const work_list w = make_work(s, rows, n_rows, s->n_q_heads);
   const int g = s->n_q_heads / s->n_kv_heads;
@@ -534,11 +602,14 @@ int orc_gated_block_swa_ex(const orc_shape* s, const float* q, const float* k, c
       logits_row(s, q, k_loc, b, j, h, a);
       L = with_sink(lse_of(a, keep, t + 1), sink_loc, h);
       weighted_sum(s, v_loc, b, u, a, keep, t + 1, L, ol);
-      const float* z = gate + (((int64_t)b * s->q_len + j) * s->n_q_heads + h) * 2;
-      const double gG = sigmoid((double)z[0]), gL = sigmoid((double)z[1]);
-      const double gO = out_gate ? sigmoid((double)out_gate[((int64_t)b * s->q_len + j) * s->n_q_heads + h]) : 1.0;
+      const int64_t row = ((int64_t)b * s->q_len + j) * s->n_q_heads + h;
       double* out = o + q_at(s, b, j, h);
-      for (int c = 0; c < d; c++) out[c] = gO * (gG * og[c] + gL * ol[c]);
+      for (int c = 0; c < d; c++) {
+        const double zG = gate_ch ? gate_ch[(row * 2 + 0) * d + c] : gate[row * 2 + 0];
+        const double zL = gate_ch ? gate_ch[(row * 2 + 1) * d + c] : gate[row * 2 + 1];
+        const double gO = out_gate_factor(s, out_gate, out_gate_ch, b, j, h, c);
+        out[c] = gO * (sigmoid(zG) * og[c] + sigmoid(zL) * ol[c]);
+      }
       if (o_glob)
         for (int c = 0; c < d; c++) o_glob[q_at(s, b, j, h) + c] = og[c];
       if (o_loc)

@@ -91,6 +91,13 @@ int orc_masked_attention_ex(const orc_shape* s, const float* q, const float* k, 
                             const float* out_gate, double* o, double* lse, const int32_t* rows,
                             int n_rows);
 
+/* orc_masked_attention_ex with a per-channel output gate out_gate_ch [B, Tq, Hq, d] (logits;
+ * channel c of the output is scaled by sigmoid(out_gate_ch[.., c])). */
+int orc_masked_attention_ch(const orc_shape* s, const float* q, const float* k, const float* v,
+                            const int32_t* idx, const int32_t* count, int cap, const float* sink,
+                            const float* out_gate_ch, double* o, double* lse,
+                            const int32_t* rows, int n_rows);
+
 /* Block score of every causal block r = 0..floor(t/B) for one (b, j, u):
  * max over heads of max over i in [rB, min(rB+B-1, t)] of p^h_{t,i}. */
 int orc_block_score_row(const orc_shape* s, const float* q, const float* k, const double* lse,
@@ -119,6 +126,16 @@ int orc_gated_block_swa_ex(const orc_shape* s, const float* q, const float* k, c
                            const float* sink, const float* sink_loc, const float* out_gate,
                            double* o, double* o_glob, double* o_loc, const int32_t* rows,
                            int n_rows);
+
+/* orc_gated_block_swa_ex with per-channel gates: gate_ch [B, Tq, Hq, 2, d] holds the d logits of
+ * zG then the d of zL for each (query, head); out_gate_ch [B, Tq, Hq, d] (or NULL) gates the sum
+ * per channel.  o_c = sigmoid(out_c) (sigmoid(zG_c) o_glob,c + sigmoid(zL_c) o_loc,c). */
+int orc_gated_block_swa_ch(const orc_shape* s, const float* q, const float* k, const float* v,
+                           const int32_t* blk_idx, const int32_t* count, int n_blocks, int block,
+                           const float* k_loc, const float* v_loc, int window,
+                           const float* gate_ch, const float* sink, const float* sink_loc,
+                           const float* out_gate_ch, double* o, double* o_glob, double* o_loc,
+                           const int32_t* rows, int n_rows);
 
 #ifdef __cplusplus
 }

@@ -30,8 +30,13 @@ MUTANTS = [
      "const double p = tmp[i];\n      if (p > score[i])"),
     ("block_boundary_shift", "if (p > bs[i / block]) bs[i / block] = p;",
      "if (p > bs[i > 0 ? (i - 1) / block : 0]) bs[i > 0 ? (i - 1) / block : 0] = p;"),
-    ("gates_swapped", "gG = sigmoid((double)z[0]), gL = sigmoid((double)z[1]);",
-     "gG = sigmoid((double)z[1]), gL = sigmoid((double)z[0]);"),
+    ("gates_swapped", "out[c] = gO * (sigmoid(zG) * og[c] + sigmoid(zL) * ol[c]);",
+     "out[c] = gO * (sigmoid(zL) * og[c] + sigmoid(zG) * ol[c]);"),
+    ("channel_gates_interleaved", "gate_ch[(row * 2 + 0) * d + c]",
+     "gate_ch[(row * d + c) * 2 + 0]"),
+    ("channel_gate_per_head", "gate_ch[(row * 2 + 1) * d + c]", "gate_ch[(row * 2 + 1) * d]"),
+    ("channel_out_gate_per_head", "out_gate_ch[row * s->head_dim + c]",
+     "out_gate_ch[row * s->head_dim]"),
     ("swa_window_too_wide",
      "for (int64_t i = (t - window + 1 > 0 ? t - window + 1 : 0); i <= t; i++) keep[i] = 1;\n      logits_row(s, q, k_loc",
      "for (int64_t i = (t - window > 0 ? t - window : 0); i <= t; i++) keep[i] = 1;\n      logits_row(s, q, k_loc"),
@@ -42,7 +47,8 @@ MUTANTS = [
     ("sink_ignored_when_empty", "if (L == -INFINITY) return sv;", "if (L == -INFINITY) return L;"),
     ("sink_local_in_global", "double L = with_sink(lse_of(a, keep, t + 1), sink, h);\n      weighted_sum(s, v, b, u, a, keep, t + 1, L, og);",
      "double L = with_sink(lse_of(a, keep, t + 1), sink_loc, h);\n      weighted_sum(s, v, b, u, a, keep, t + 1, L, og);"),
-    ("out_gate_missing", "for (int c = 0; c < s->head_dim; c++) out[c] *= gv;", "(void)gv;"),
+    ("out_gate_missing", "if (out_gate) return sigmoid((double)out_gate[row]);",
+     "if (out_gate) return 1.0;"),
 ]
 
 

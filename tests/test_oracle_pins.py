@@ -533,6 +533,67 @@ def test_output_gate_scales_the_layer():
     assert np.max(np.abs(og3 - og_p)) > 1e-4 and np.max(np.abs(ol3 - ol_p)) > 1e-4
 
 
+def test_per_channel_gates_select_branches_channel_by_channel():
+    """Per-channel gates (P2: a gate may act per head or per channel).  Logits of +-60 make each
+    sigmoid exactly 1 or below 1e-26, so every channel of the output is one branch's channel:
+    o_glob where zG_c = +60, zL_c = -60 and o_loc where the signs flip, in a pattern that differs
+    between channels, heads and queries.  The branches themselves are pinned to SDPA above."""
+    wl, a, bi, bc = _gated_setup(74)
+    B, Tq, Hq, d = a["qs"].shape
+    pick = (np.arange(Tq)[:, None, None] + 3 * np.arange(Hq)[None, :, None]
+            + np.arange(d)[None, None, :] * np.arange(1, d + 1)[None, None, :] // 2) % 2 == 0
+    pick = pick[None]  # [1, Tq, Hq, d]: True -> global branch
+    gch = np.empty((B, Tq, Hq, 2, d), np.float32)
+    gch[..., 0, :] = np.where(pick, 60.0, -60.0)
+    gch[..., 1, :] = np.where(pick, -60.0, 60.0)
+    o, og, ol = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                                       a["v_loc"], wl.window, gch)
+    assert np.max(np.abs(o - np.where(pick, og, ol))) < 1e-24
+    # equal channels reduce to the per-head gates bit for bit, with and without output gates
+    rep = np.repeat(a["gate"][..., None], d, axis=-1)
+    o1, _, _ = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                                      a["v_loc"], wl.window, rep)
+    o2, _, _ = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                                      a["v_loc"], wl.window, a["gate"])
+    assert np.array_equal(o1, o2)
+    gate_o = rnd(a["qs"].shape[:3], 75)
+    o3, _, _ = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                                      a["v_loc"], wl.window, rep,
+                                      out_gate=np.repeat(gate_o[..., None], d, axis=-1))
+    o4, _, _ = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                                      a["v_loc"], wl.window, a["gate"], out_gate=gate_o)
+    assert np.array_equal(o3, o4)
+    with pytest.raises(ValueError):
+        oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                               a["v_loc"], wl.window, rep, out_gate=gate_o)
+
+
+def test_per_channel_output_gate_closes_or_passes_each_channel():
+    """A per-channel output gate of +-60 keeps a channel whole or zeroes it (sigmoid exactly 1,
+    or below 1e-26) on both the token layer and the gated layer; the LSE is unchanged."""
+    q, k, v, idx, cnt = _sink_setup(88)
+    B, Tq, Hq, d = q.shape
+    open_ = ((np.arange(Hq)[:, None] * 5 + np.arange(d)[None, :] * 3) % 7 < 3)[None, None]
+    g = np.where(open_, 60.0, -60.0).astype(np.float32)
+    sink = np.array([0.1, 0.2, 0.3, 0.4], np.float32)
+    o, lse = oracle.masked_attention(q, k, v, idx, cnt, sink=sink)
+    oc, lsec = oracle.masked_attention(q, k, v, idx, cnt, sink=sink, out_gate=g)
+    assert np.max(np.abs(oc - np.where(open_, o, 0.0))) < 1e-24
+    assert np.array_equal(lse, lsec)
+    wl, a, bi, bc = _gated_setup(76)
+    d2 = a["qs"].shape[-1]
+    rep = np.repeat(a["gate"][..., None], d2, axis=-1)
+    sh = a["qs"].shape
+    open2 = ((np.arange(sh[1])[:, None, None] + np.arange(sh[2])[None, :, None] * 2
+              + np.arange(d2)[None, None, :]) % 3 == 0)[None]
+    g2 = np.where(open2, 60.0, -60.0).astype(np.float32)
+    o5, _, _ = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                                      a["v_loc"], wl.window, rep, out_gate=g2)
+    o6, _, _ = oracle.gated_block_swa(a["qs"], a["k"], a["v"], bi, bc, wl.block, a["k_loc"],
+                                      a["v_loc"], wl.window, a["gate"])
+    assert np.max(np.abs(o5 - np.where(open2, o6, 0.0))) < 1e-24
+
+
 def test_blocks_covering_prefix_and_wide_window_are_full_attention():
     """B * n_blocks >= t + 1 selects every causal block; w >= t + 1 with K' = K, V' = V makes
     the local branch full attention too."""
