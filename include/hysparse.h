@@ -100,7 +100,8 @@ typedef struct {
 typedef struct {
   const void* k_local;      /* [B, kv_len, Hkv, d], in_dtype; position-indexed */
   const void* v_local;      /* [B, kv_len, Hkv, d], in_dtype */
-  const float* gate_logits; /* [B, q_len, Hq, 2] fp32: (zG, zL); sigmoid applied inside */
+  const float* gate_logits; /* [B, q_len, Hq, 2] fp32: (zG, zL); sigmoid applied inside
+                               ([B, q_len, Hq, 2, d] with hs_sparse_opts.gates_per_channel) */
   int32_t window;           /* w >= 1: positions max(0, t-w+1) .. t */
 } hs_swa_branch;
 
@@ -144,7 +145,13 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
  *     reported LSE includes it.  A row with no key then gets o = 0 and LSE = s_h.
  *   out_gate: logits of the sigmoid output gate of those layers [P1 section 6.1], fp32
  *     [B, q_len, Hq], one per (query, head) (the pages give no size; one scalar per head, like
- *     the branch gates): o <- sigmoid(g) * o, applied last. */
+ *     the branch gates): o <- sigmoid(g) * o, applied last.
+ *   gates_per_channel: 0 (default) as above; 1: every gate acts per channel [P2 "Two sigmoid
+ *     gates, not one of two": the branch gates may act per head or per channel, combined by an
+ *     element-wise product], so swa->gate_logits is [B, q_len, Hq, 2, d] (the d logits of zG,
+ *     then the d of zL, for each (query, head)) and out_gate is [B, q_len, Hq, d]:
+ *     o_c = sigmoid(out_c) (sigmoid(zG_c) o_glob,c + sigmoid(zL_c) o_loc,c).  Other values:
+ *     HS_ERR_INVALID_ARG. */
 typedef struct {
   const float* sink;
   const float* sink_local;
@@ -156,6 +163,7 @@ typedef struct {
                          layer's own small cache
                          [P2 "Why the local branch cannot reuse the same KV": each sparse layer
                          keeps its own K', V' only for a ring window of length w] */
+  int32_t gates_per_channel;
 } hs_sparse_opts;
 
 /* Paged K / V cache (serving): K and V are pools [n_pages, page_size, Hkv, d]; the positions

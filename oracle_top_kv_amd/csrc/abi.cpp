@@ -1048,6 +1048,7 @@ hs_status sparse_layer(const hs_attn_desc* desc, const void* q, const void* k_fu
   const float* sink_l = opts ? opts->sink_local : nullptr;
   const float* ogate = opts ? opts->out_gate : nullptr;
   const int ring = opts ? opts->local_ring : 0;
+  const int gate_ch = opts ? opts->gates_per_channel : 0;
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
@@ -1073,6 +1074,8 @@ hs_status sparse_layer(const hs_attn_desc* desc, const void* q, const void* k_fu
   }
   if (sink_l && !swa)
     return fail(HS_ERR_INVALID_ARG, "sink_local given without a sliding-window branch");
+  if (gate_ch != 0 && gate_ch != 1)
+    return fail(HS_ERR_INVALID_ARG, "gates_per_channel must be 0 or 1, got %d", gate_ch);
   if (ring < 0 || (ring > 0 && !swa))
     return fail(HS_ERR_INVALID_ARG, "local_ring %d: needs a sliding-window branch", ring);
   // the q_len rows of one call read positions q_offset - window + 1 .. q_offset + q_len - 1,
@@ -1111,6 +1114,7 @@ hs_status sparse_layer(const hs_attn_desc* desc, const void* q, const void* k_fu
   pg.sink = sink_g;
   pg.sink2 = sink_l;
   pg.out_gate = ogate;
+  pg.gate_ch = gate_ch;
   pg.ring = ring;
   if (pages) set_pages(pg, pages);
   const hs::KeySrc src = kind == HS_IDX_TOKEN ? hs::SRC_TOKEN : hs::SRC_BLOCK;
@@ -1150,6 +1154,7 @@ hs_status sparse_layer(const hs_attn_desc* desc, const void* q, const void* k_fu
     c.sink[0] = sink_g;
     c.sink[1] = sink_l;
     c.out_gate = ogate;
+    c.gate_ch = gate_ch;
     c.m[0] = pg.part_m;
     c.l[0] = pg.part_l;
     c.po[0] = pg.part_o;

@@ -518,6 +518,10 @@ __device__ __forceinline__ double out_gate_of(const float* g, size_t i) {
   return g ? 1.0 / (1.0 + exp(-(double)g[i])) : 1.0;
 }
 
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return (float)(1.0 / (1.0 + exp(-(double)z)));
+}
+
 // GATED: the HySparse sparse layer in one workgroup when neither branch is split -- the block
 // (or token) branch over K, V, then the sliding-window branch over K', V' (p.k2, p.v2), each
 // normalized on its own and weighted by its sigmoid gate [P2 "Same query, two memories"].
@@ -581,15 +585,30 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
     attend_pass<D, F32, SRC_WINDOW, NW>(p, p.k2, p.v2, 0, 1 << 30, b, u, hc, j0, nq, smem,
                                         pos_all, row_all, w);
     if (r >= nrows) return;
-    const float* z = p.gate + orow * 2;
-    const double og = out_gate_of(p.out_gate, orow);
-    const double sg = 1.0 / (1.0 + exp(-(double)z[0]));
-    const double sl = 1.0 / (1.0 + exp(-(double)z[1]));
-    const RowNorm ng = row_norm(a.M, a.L, p.sink, hr, sg * og);
-    const RowNorm nl = row_norm(w.M, w.L, p.sink2, hr, sl * og);
+    if (p.gate_ch) {  // per-channel gates: (zG_c, zL_c) and the output gate of column c
+      const float* zg = p.gate + orow * 2 * D;
+      const float* og = p.out_gate ? p.out_gate + orow * D : nullptr;
+      const RowNorm ng = row_norm(a.M, a.L, p.sink, hr, 1.0);
+      const RowNorm nl = row_norm(w.M, w.L, p.sink2, hr, 1.0);
 #pragma unroll
-    for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * ng.factor + w.ov[c] * nl.factor;
-    lse_row = ng.lse;
+      for (int c = 0; c < CPT; c++) {
+        const int col = Cfg::col(lr, c);
+        const float go = og ? sigmoid_f(og[col]) : 1.f;
+        res[c] = go * (a.ov[c] * ng.factor * sigmoid_f(zg[col]) +
+                       w.ov[c] * nl.factor * sigmoid_f(zg[D + col]));
+      }
+      lse_row = ng.lse;
+    } else {
+      const float* z = p.gate + orow * 2;
+      const double og = out_gate_of(p.out_gate, orow);
+      const double sg = 1.0 / (1.0 + exp(-(double)z[0]));
+      const double sl = 1.0 / (1.0 + exp(-(double)z[1]));
+      const RowNorm ng = row_norm(a.M, a.L, p.sink, hr, sg * og);
+      const RowNorm nl = row_norm(w.M, w.L, p.sink2, hr, sl * og);
+#pragma unroll
+      for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * ng.factor + w.ov[c] * nl.factor;
+      lse_row = ng.lse;
+    }
   } else {
     if (!p.final_direct) {
       const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu * p.cpq;
@@ -605,10 +624,19 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
       return;
     } else {
       if (r >= nrows) return;
-      const RowNorm n = row_norm(a.M, a.L, p.sink, hr, out_gate_of(p.out_gate, orow));
+      if (p.gate_ch && p.out_gate) {  // per-channel output gate
+        const RowNorm n = row_norm(a.M, a.L, p.sink, hr, 1.0);
+        const float* og = p.out_gate + orow * D;
 #pragma unroll
-      for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * n.factor;
-      lse_row = n.lse;
+        for (int c = 0; c < CPT; c++)
+          res[c] = a.ov[c] * n.factor * sigmoid_f(og[Cfg::col(lr, c)]);
+        lse_row = n.lse;
+      } else {
+        const RowNorm n = row_norm(a.M, a.L, p.sink, hr, out_gate_of(p.out_gate, orow));
+#pragma unroll
+        for (int c = 0; c < CPT; c++) res[c] = a.ov[c] * n.factor;
+        lse_row = n.lse;
+      }
     }
   }
   if (p.out_f32) {
@@ -656,7 +684,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 
   float out[4] = {0.f, 0.f, 0.f, 0.f};
   double lse0 = -INFINITY;
-  const double og = out_gate_of(p.out_gate, ((size_t)b * p.Tq + jr) * p.Hq + hr);
+  const size_t orow = ((size_t)b * p.Tq + jr) * p.Hq + hr;
+  const double og = p.gate_ch ? 1.0 : out_gate_of(p.out_gate, orow);
+  float og_ch[4] = {1.f, 1.f, 1.f, 1.f};  // per-channel output gate of this thread's columns
+  if (p.gate_ch && p.out_gate && threadIdx.x < NC) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) og_ch[e] = sigmoid_f(p.out_gate[orow * D + 4 * c + e]);
+  }
   for (int br = 0; br < p.n_branch; br++) {
     const int ns = p.n_split[br];
     const float* m = p.m[br];
@@ -760,13 +794,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 #pragma unroll
         for (int e = 0; e < 4; e++) sum[e] += red[q][4 * c + e];
       double wgt = og;
-      if (p.n_branch == 2) {
-        const float z = p.gate[(((size_t)b * p.Tq + jr) * p.Hq + hr) * 2 + br];
+      if (p.n_branch == 2 && !p.gate_ch) {
+        const float z = p.gate[orow * 2 + br];
         wgt *= 1.0 / (1.0 + exp(-(double)z));
       }
       const RowNorm n = row_norm(M, L, p.sink[br], hr, wgt);
+      if (p.gate_ch) {
 #pragma unroll
-      for (int e = 0; e < 4; e++) out[e] += sum[e] * n.factor;
+        for (int e = 0; e < 4; e++) {
+          const float gb = p.n_branch == 2 ? sigmoid_f(p.gate[(orow * 2 + br) * D + 4 * c + e])
+                                           : 1.f;
+          out[e] += sum[e] * n.factor * gb * og_ch[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) out[e] += sum[e] * n.factor;
+      }
       if (br == 0 && c == 0) lse0 = n.lse;
     }
     __syncthreads();

@@ -51,6 +51,7 @@ struct RowAttnParams {
   const float* sink;      // [Hq] or null
   const float* sink2;     // [Hq] or null
   const float* out_gate;  // [B, Tq, Hq] or null
+  int gate_ch;  // gates per channel: gate [B, Tq, Hq, 2, D], out_gate [B, Tq, Hq, D]
   // paged K / V (range and list sources): pools [n_pages, page_size, Hkv, d], page of logical
   // page lp of batch entry b = pages[b * max_pages + lp]; page_size a power of two
   const int32_t* pages;
@@ -75,6 +76,7 @@ struct CombineParams {
   int out_f32;
   const float* sink[2];   // per branch: [Hq] sink logits or null
   const float* out_gate;  // [B, Tq, Hq] sigmoid output-gate logits or null
+  int gate_ch;  // gates per channel: gate [B, Tq, Hq, 2, D], out_gate [B, Tq, Hq, D]
 };
 
 // gated: list source (token or block) then the window branch over k2, v2 in one workgroup,

@@ -41,7 +41,8 @@ class SwaBranch(ctypes.Structure):
 
 class SparseOpts(ctypes.Structure):
     _fields_ = [("sink", ctypes.c_void_p), ("sink_local", ctypes.c_void_p),
-                ("out_gate", ctypes.c_void_p), ("local_ring", ctypes.c_int32)]
+                ("out_gate", ctypes.c_void_p), ("local_ring", ctypes.c_int32),
+                ("gates_per_channel", ctypes.c_int32)]
 
 
 class KvPages(ctypes.Structure):
@@ -335,8 +336,16 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
     branch; local_ring > 0: k_local / v_local are rings [B, local_ring, Hkv, d].
     sink / sink_local: fp32 [Hq] per-head sink logits of the global / window branch;
     out_gate: fp32 [B,Tq,Hq] sigmoid output-gate logits (hs_sparse_attn_gather_ex).
+    Per-channel gates: gate_logits [B,Tq,Hq,2,d] and / or out_gate [B,Tq,Hq,d] (both per channel
+    when both are given; sets hs_sparse_opts.gates_per_channel).
     pages = (block_table int32 [B, max_pages], kv_len): k, v are page pools
     [n_pages, page_size, Hkv, d] (hs_sparse_attn_gather_paged).  Returns (o, lse or None)."""
+    per_ch = [t.dim() == q.dim() + (1 if i == 0 else 0)
+              for i, t in enumerate((swa[2] if swa is not None else None, out_gate))
+              if t is not None]
+    if len(set(per_ch)) > 1:
+        raise ValueError("gate_logits and out_gate must both be per head or both per channel")
+    gate_ch = int(bool(per_ch) and per_ch[0])
     dev = q.device
     _need(q, "q", dev)
     _need(k, "k", dev, dtype=q.dtype)
@@ -361,14 +370,16 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
                      else (q.shape[0], desc.kv_len) + tuple(k.shape[2:]))
         _need(kl, "k_local", dev, dtype=q.dtype, shape=loc_shape)
         _need(vl, "v_local", dev, dtype=q.dtype, shape=loc_shape)
-        _need(gate, "gate_logits", dev, dtype=torch.float32, shape=tuple(q.shape[:3]) + (2,))
+        _need(gate, "gate_logits", dev, dtype=torch.float32,
+              shape=tuple(q.shape[:3]) + ((2, q.shape[3]) if gate_ch else (2,)))
         sw = SwaBranch(kl.data_ptr(), vl.data_ptr(), gate.data_ptr(), int(window))
         keep = [kl, vl, gate]
     o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
     lse = (torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
            if want_lse else None)
     ws, n = workspace(HS_OP_SPARSE_ATTN, desc, keys, window, device=dev)
-    if sink is None and sink_local is None and out_gate is None and not local_ring and pg is None:
+    if (sink is None and sink_local is None and out_gate is None and not local_ring and pg is None
+            and not gate_ch):
         _check(lib().hs_sparse_attn_gather(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                            kind_code, _ptr(idx), _ptr(count), int(cap),
                                            int(block),
@@ -378,11 +389,12 @@ def sparse_attn_gather(q, k, v, idx, count, kind="token", block=64, swa=None, q_
     else:
         Hq = q.shape[2]
         for t, nm, shp in ((sink, "sink", (Hq,)), (sink_local, "sink_local", (Hq,)),
-                           (out_gate, "out_gate", tuple(q.shape[:3]))):
+                           (out_gate, "out_gate",
+                            tuple(q.shape[:3]) + ((q.shape[3],) if gate_ch else ()))):
             if t is not None:
                 _need(t, nm, dev, dtype=torch.float32, shape=shp)
         opts = SparseOpts(*(t.data_ptr() if t is not None else None
-                            for t in (sink, sink_local, out_gate)), int(local_ring))
+                            for t in (sink, sink_local, out_gate)), int(local_ring), gate_ch)
         _check(lib().hs_sparse_attn_gather_paged(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                                  ctypes.byref(pg) if pg is not None else None,
                                                  kind_code, _ptr(idx), _ptr(count), int(cap),

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from oracle_top_kv_amd import hs
 
@@ -186,6 +187,26 @@ def test_sparse_options_argument_checks():
                                       FAKE, 8, 64, None, ctypes.byref(opts), FAKE, None, FAKE,
                                       1 << 40, None) == hs.HS_ERR_INVALID_ARG
     assert "sink_local" in L.hs_last_error().decode()
+    opts = hs.SparseOpts(None, None, None, 0, 2)  # gates_per_channel is 0 or 1
+    assert L.hs_sparse_attn_gather_ex(ctypes.byref(d), FAKE, FAKE, FAKE, hs.HS_IDX_TOKEN, FAKE,
+                                      FAKE, 8, 64, None, ctypes.byref(opts), FAKE, None, FAKE,
+                                      1 << 40, None) == hs.HS_ERR_INVALID_ARG
+    assert "gates_per_channel" in L.hs_last_error().decode()
+    names = [f[0] for f in hs.SparseOpts._fields_]
+    assert names == ["sink", "sink_local", "out_gate", "local_ring", "gates_per_channel"]
+    assert hs.SparseOpts.gates_per_channel.offset == 28 and ctypes.sizeof(hs.SparseOpts) == 32
+
+
+def test_gate_kinds_must_agree():
+    """Per-channel and per-head gates cannot be mixed in one call (the ABI has one flag); the
+    binding refuses before touching any device."""
+    q = torch.zeros(1, 1, 4, 16)
+    k = torch.zeros(1, 8, 2, 16)
+    idx = torch.zeros(1, 1, 2, 4, dtype=torch.int32)
+    cnt = torch.zeros(1, 1, 2, dtype=torch.int32)
+    swa = (k, k, torch.zeros(1, 1, 4, 2, 16), 4)
+    with pytest.raises(ValueError, match="per head or both per channel"):
+        hs.sparse_attn_gather(q, k, k, idx, cnt, swa=swa, out_gate=torch.zeros(1, 1, 4))
 
 
 def test_status_strings():

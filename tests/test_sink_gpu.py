@@ -1,7 +1,7 @@
 """GPU parity of the sparse-layer options (hs_sparse_attn_gather_ex): per-head sink logits of
-the global and sliding-window branches and the sigmoid output gate, against the CPU oracle,
-on every launch form of the sparse kernels (split + combine, one 8-wave workgroup per set, the
-gated layer in one workgroup, fp32 inputs).  Index sets are the oracle's own.
+the global and sliding-window branches and the sigmoid gates (per head or per channel), against
+the CPU oracle, on every launch form of the sparse kernels (split + combine, one 8-wave workgroup
+per set, the gated layer in one workgroup, fp32 inputs).  Index sets are the oracle's own.
 """
 import sys
 
@@ -123,6 +123,76 @@ def test_gated_layer_with_sinks_and_gate(name, wl):
         swa=(to_dev(x["k_loc"]), to_dev(x["v_loc"]), to_dev(x["gate"]), wl.window),
         out_dtype=torch.float32, sink=sink.cuda(), sink_local=sink_l.cuda(),
         out_gate=gate.cuda())
+    torch.cuda.synchronize()
+    eo = max_abs(o.cpu().numpy(), o_ref)
+    say(f"  max|dO| = {eo:.3e}")
+    assert eo <= (TOL_F32 if wl.dtype == "f32" else TOL_BF16)
+
+
+def channel_gates(wl, seed, n_branch_gates):
+    """Per-channel gate logits ~ N(0, 2): branch gates [B,Tq,Hq,2,d] (when n_branch_gates) and
+    the output gate [B,Tq,Hq,d]."""
+    g = torch.Generator().manual_seed(seed)
+    shp = (wl.batch, wl.q_len, wl.n_q_heads)
+    zg = (2.0 * torch.randn(shp + (2, wl.head_dim), generator=g)).float() \
+        if n_branch_gates else None
+    zo = (2.0 * torch.randn(shp + (wl.head_dim,), generator=g)).float()
+    return zg, zo
+
+
+CHANNEL_TOKEN_CASES = [c for c in TOKEN_CASES if c[0] in (
+    "decode_g4_split", "decode_g4_wide", "prefill_g4", "tiny_f32", "decode_g4_d256",
+    "mqa64_d256_two_queries")]
+
+
+@pytest.mark.parametrize("name,wl,which", CHANNEL_TOKEN_CASES,
+                         ids=[c[0] for c in CHANNEL_TOKEN_CASES])
+def test_sparse_token_with_per_channel_gate(name, wl, which):
+    """The output gate per channel (hs_sparse_opts.gates_per_channel) with a sink, on the split +
+    combine, 8-wave, fp32 and group-kernel forms."""
+    say(f"[sparse token channel gate] {name} {wl}")
+    x = make_inputs(wl, n_sparse=1)
+    qn, kn, vn = (to_numpy_f32(x[n]) for n in ("q", "k", "v"))
+    oi, oc = oracle.token_topk(qn, kn, None, wl.k_global, wl.window)
+    sink, _, _ = options(wl, wl.seed, ("sink",))
+    _, zo = channel_gates(wl, wl.seed + 1, False)
+    qs = x["q_sparse"][0]
+    o, lse = hs().sparse_attn_gather(
+        to_dev(qs), to_dev(x["k"]), to_dev(x["v"]), torch.from_numpy(oi).cuda(),
+        torch.from_numpy(oc).cuda(), kind="token", out_dtype=torch.float32, want_lse=True,
+        sink=sink.cuda(), out_gate=zo.cuda())
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.masked_attention(to_numpy_f32(qs), kn, vn, oi, oc,
+                                             sink=sink.numpy(), out_gate=zo.numpy())
+    eo, el = max_abs(o.cpu().numpy(), o_ref), max_abs(lse.cpu().numpy(), lse_ref)
+    say(f"  max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+    assert eo <= (TOL_F32 if wl.dtype == "f32" else TOL_BF16)
+    assert el <= LSE_TOL
+
+
+@pytest.mark.parametrize("name,wl", GATED_CASES, ids=[c[0] for c in GATED_CASES])
+@pytest.mark.parametrize("with_out_gate", [True, False], ids=["out_gate", "branch_only"])
+def test_gated_layer_with_per_channel_gates(name, wl, with_out_gate):
+    """Branch gates (zG_c, zL_c) and the output gate per channel, with sinks, on the two-branch
+    combine and on the one-workgroup gated layer."""
+    say(f"[gated channel gates] {name} {wl} out_gate={with_out_gate}")
+    x = make_inputs(wl, block_variant=True)
+    a = {n: to_numpy_f32(x[n]) for n in ("q", "k", "v", "k_loc", "v_loc")}
+    qs = x["q_sparse"][0]
+    bi, bc = oracle.block_topk(a["q"], a["k"], None, wl.block, wl.n_blocks)
+    sink, sink_l, _ = options(wl, wl.seed, ("sink", "sink_local"))
+    zg, zo = channel_gates(wl, wl.seed + 2, True)
+    zo = zo if with_out_gate else None
+    o_ref, _, _ = oracle.gated_block_swa(to_numpy_f32(qs), a["k"], a["v"], bi, bc, wl.block,
+                                         a["k_loc"], a["v_loc"], wl.window, zg.numpy(),
+                                         sink=sink.numpy(), sink_loc=sink_l.numpy(),
+                                         out_gate=np_or_none(zo))
+    o, _ = hs().sparse_attn_gather(
+        to_dev(qs), to_dev(x["k"]), to_dev(x["v"]), torch.from_numpy(bi).cuda(),
+        torch.from_numpy(bc).cuda(), kind="block", block=wl.block,
+        swa=(to_dev(x["k_loc"]), to_dev(x["v_loc"]), zg.cuda(), wl.window),
+        out_dtype=torch.float32, sink=sink.cuda(), sink_local=sink_l.cuda(),
+        out_gate=None if zo is None else zo.cuda())
     torch.cuda.synchronize()
     eo = max_abs(o.cpu().numpy(), o_ref)
     say(f"  max|dO| = {eo:.3e}")
