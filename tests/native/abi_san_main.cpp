@@ -85,6 +85,9 @@ int main() {
   x = make(1, 4, 1024, 8, 2, 128);
   CHECK(hs_sparse_attn_gather_ex(&x, F, F, F, HS_IDX_BLOCK, FI, FI, 16, 64, &swa, &opts, F,
                                  nullptr, F, 1 << 30, nullptr) == HS_ERR_INVALID_ARG);
+  hs_sparse_opts opts_ch = {nullptr, nullptr, nullptr, 0, 3};  // gates_per_channel is 0 or 1
+  CHECK(hs_sparse_attn_gather_ex(&x, F, F, F, HS_IDX_BLOCK, FI, FI, 16, 64, &swa, &opts_ch, F,
+                                 nullptr, F, 1 << 30, nullptr) == HS_ERR_INVALID_ARG);
   hs_kv_pages pages = {FI, 48, 32, 100};  // not a power of two
   CHECK(hs_full_attn_fwd_paged(&x, F, F, F, &pages, F, FF, nullptr, F, 1 << 30, nullptr) ==
         HS_ERR_INVALID_ARG);

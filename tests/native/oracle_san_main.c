@@ -66,6 +66,19 @@ int main(void) {
                             0) == ORC_OK);
   CHECK(orc_gated_block_swa_ex(&s, q, k, v, bidx, bcnt, nb, blk, kl, vl, w, gate, sink, sinkl, og,
                                o, NULL, NULL, rows, 2) == ORC_OK);
+  /* per-channel gates: [B, Tq, Hq, 2, d] branch logits and a [B, Tq, Hq, d] output gate */
+  {
+    float *gch = randn((size_t)B * Tq * Hq * 2 * d), *ogch = randn((size_t)B * Tq * Hq * d);
+    CHECK(orc_masked_attention_ch(&s, q, k, v, idx, cnt, cap, sink, ogch, o2, lse2, NULL, 0) ==
+          ORC_OK);
+    CHECK(orc_gated_block_swa_ch(&s, q, k, v, bidx, bcnt, nb, blk, kl, vl, w, gch, sink, sinkl,
+                                 ogch, o, o2, o3, NULL, 0) == ORC_OK);
+    CHECK(orc_gated_block_swa_ch(&s, q, k, v, bidx, bcnt, nb, blk, kl, vl, w, gch, NULL, NULL,
+                                 NULL, o, NULL, NULL, rows, 2) == ORC_OK);
+    CHECK(orc_masked_attention_ch(&s, q, k, v, idx, cnt, cap, sink, NULL, o2, lse2, NULL, 0) ==
+          ORC_EINVAL);
+    free(gch); free(ogch);
+  }
   /* a prefill from position 0 and a non-default scale (buffers of its own size) */
   {
     orc_shape s0 = {1, 40, 40, 4, 1, 8, 0, 0.3};
