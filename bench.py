@@ -873,12 +873,17 @@ def cpu_baseline_sparse(wl, x, budget_s):
     from oracle_top_kv_amd import costs
 
     layers, t_used = 0, 0.0
-    for b in range(x["q"].shape[0]):
-        q, k, v = _host(x["q"], b), _host(x["k"], b), _host(x["v"], b)
-        _, lse = oracle.full_attention(q, k, v)
-        idx, cnt = oracle.token_topk(q, k, lse, wl.k_global, wl.window)
-        for qs_l in x["q_sparse"]:
-            qs = _host(qs_l, b)
+    ent = {}  # per batch entry: host K, V, the sparse layers' queries and the index sets
+    n_b = x["q"].shape[0]
+    for it in range(64 * n_b):  # the batch entries in turn, until the budget is spent
+        b = it % n_b
+        if b not in ent:  # untimed
+            q, k, v = _host(x["q"], b), _host(x["k"], b), _host(x["v"], b)
+            _, lse = oracle.full_attention(q, k, v)
+            ent[b] = (k, v, [_host(qs_l, b) for qs_l in x["q_sparse"]],
+                      oracle.token_topk(q, k, lse, wl.k_global, wl.window))
+        k, v, q_sp, (idx, cnt) = ent[b]
+        for qs in q_sp:
             t0 = time.perf_counter()
             oracle.masked_attention(qs, k, v, idx, cnt)
             t_used += time.perf_counter() - t0
@@ -888,8 +893,8 @@ def cpu_baseline_sparse(wl, x, budget_s):
     per_layer_b = costs.token_gather_bytes(wl) / wl.batch  # one batch entry's layer
     return {"value": round(layers * per_layer_b / t_used / 1e9, 4), "unit": "GB/s",
             "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{layers} token-sparse layer runs over batch entries of {wl.name} "
-                      f"(one entry each), {t_used:.2f} s"}
+            "sample": f"{layers} token-sparse layer runs over the batch entries of {wl.name} "
+                      f"in turn (one entry each), {t_used:.2f} s of oracle time"}
 
 
 def cpu_baseline(wl, x, budget_s):

@@ -11,6 +11,7 @@ Workloads (sizes of the pages' two model families):
   prefill_80b_128k  4096 queries after 131072 cached keys, 64/4 heads    12 sampled rows
   decode_80b_1m     batch 4, 2^20 keys, 64/4 heads, clustered needles    batch entries 0 and 3
   block_7b_64k      batch 4, 65536-query causal prefill, 32/8 heads      sampled (b, row) pairs
+  prefill_mqa256_128k  4096 queries after 131072 keys, 64/1 heads, d 256  8 sampled rows
 """
 import sys
 
@@ -154,6 +155,44 @@ def test_prefill_80b_128k_sampled_rows():
         el = max_abs(ls_.cpu().numpy()[:, :, rows], r_l[:, :, rows])
         say(f"  sparse layer {layer}: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
         assert eo <= TOL_BF16 and el <= LSE_TOL
+
+
+def test_prefill_mqa256_128k_sampled_rows():
+    """HySparse2's head shape at the benchmark's prefill size: 64 query heads on one KV head,
+    d 256, 4096 queries after 131072 cached keys (prefill attention at d 256, the selection in
+    chunks of 16 heads with the exact merge, the sparse layer on the group kernel)."""
+    wl = WORKLOADS["prefill_mqa256_128k"]
+    say(f"[full size] {wl}")
+    x = make_inputs(wl, device="cuda", n_sparse=1)
+    q, k, v = x["q"], x["k"], x["v"]
+    o, lse = hs().full_attn_fwd(q, k, v, out_dtype=torch.float32)
+    idx, cnt = hs().oracle_topk(q, k, lse, wl.k_global, wl.window)
+    torch.cuda.synchronize()
+    rows = [0, 15, 16, 127, 128, 2047, 4094, 4095]
+    say(f"  sampled rows {rows}")
+    qn, kn, vn = host(q), host(k), host(v)
+    o_ref, lse_ref = oracle.full_attention(qn, kn, vn, rows=rows)
+    eo = max_abs(o.cpu().numpy()[:, rows], o_ref[:, rows])
+    el = max_abs(lse.cpu().numpy()[:, :, rows], lse_ref[:, :, rows])
+    say(f"  full attention: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+    assert eo <= TOL_BF16 and el <= LSE_TOL
+    oi, oc = oracle.token_topk(qn, kn, lse_ref, wl.k_global, wl.window, rows=rows)
+    ex = check_token_sets(idx.cpu().numpy(), cnt.cpu().numpy(), oi, oc, qn, kn, lse_ref,
+                          wl.k_global, wl.window, wl.q_offset, rows=rows)
+    say(f"  token sets: near-tie differences excused {ex}")
+    idx_in, cnt_in = idx.clone(), cnt.clone()
+    r = torch.tensor(rows, device="cuda")
+    idx_in[:, r] = torch.from_numpy(oi[:, rows]).cuda()
+    cnt_in[:, r] = torch.from_numpy(oc[:, rows]).cuda()
+    qs = x["q_sparse"][0]
+    os_, ls_ = hs().sparse_attn_gather(qs, k, v, idx_in, cnt_in, kind="token",
+                                       out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    r_o, r_l = oracle.masked_attention(host(qs), kn, vn, oi, oc, rows=rows)
+    eo = max_abs(os_.cpu().numpy()[:, rows], r_o[:, rows])
+    el = max_abs(ls_.cpu().numpy()[:, :, rows], r_l[:, :, rows])
+    say(f"  sparse layer: max|dO| = {eo:.3e} max|dLSE| = {el:.3e}")
+    assert eo <= TOL_BF16 and el <= LSE_TOL
 
 
 def test_decode_80b_1m_sampled_batch_entries():
