@@ -512,7 +512,8 @@ SparseGeom sparse_geom(const Shape& s, long long keys_per_set, int window, bool 
     g.wide = false;
     g.fused = false;
     g.loc = ra_geom(s, true, window > 0 ? window : 1, 4);
-    g.combine = true;
+    // unsplit lists without a window branch: the group kernel writes the output itself
+    g.combine = window > 0 || g.glob.n_split > 1;
     return g;
   }
   g.glob = ra_geom(s, true, keys_per_set, 4, kTargetWorkgroups, 64);
@@ -601,7 +602,10 @@ RaGeom group_list_geom(const Shape& s, long long keys_per_set) {
 // Workspace of full attention on the row path (decode, short query blocks, stored logits,
 // paged caches).
 size_t row_fa_ws(const Shape& s, int page_size) {
-  if (use_group_kernel(s, page_size > 0)) return partial_bytes(group_geom(s), s.D);
+  if (use_group_kernel(s, page_size > 0)) {
+    const RaGeom g = group_geom(s);
+    return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
+  }
   const RaGeom g = fa_row_geom(s, page_size);
   return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
 }
@@ -646,7 +650,7 @@ hs_status row_full_attn(const Shape& s, const void* q, const void* k, const void
   p.logits = logits;
   p.logits_vec = logits && s.Tk % 4 == 0 && (uintptr_t)logits % 16 == 0;
   if (pages) set_pages(p, pages);
-  p.final_direct = !group && g.n_split == 1;
+  p.final_direct = g.n_split == 1;
   if (!p.final_direct) carve_partials(ws, g, s.D, &p.part_m, &p.part_l, &p.part_o);
   hipStream_t hst = (hipStream_t)stream;
   hipError_t e = group ? hs::launch_group_attn(p, s.D, hs::SRC_RANGE, hst)

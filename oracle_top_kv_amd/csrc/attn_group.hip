@@ -18,8 +18,10 @@
 // two memories"]): a split's list positions are staged in LDS first, and each step gathers its
 // 64 rows straight into the shared tile (invalid entries read as zeros and are masked).
 // LOGITS (range only): the raw dot products q.k go to a [B, Tq, Hq, Tk] array, 16 bytes per
-// lane per key block (64 contiguous bytes per row).  Every workgroup writes split partials (row
-// maximum, row sum, unnormalized O); the combine kernel normalizes.
+// lane per key block (64 contiguous bytes per row).  With several splits every workgroup writes
+// split partials (row maximum, row sum, unnormalized O) and the combine kernel normalizes; with
+// one split (final_direct) the workgroup normalizes its rows itself (sink, output gate) and
+// writes O and the LSE.
 #include "hs_device.h"
 #include "hs_kernels.h"
 
@@ -288,10 +290,35 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
     }
   }
 
-  // partials of this split: row maximum, row sum (the 4 lanes of the row summed), O^T
+  // row sum (the 4 lanes of the row summed)
   double ld = (double)l_s - (double)l_c;
   ld += __shfl_xor(ld, 16, 64);
   ld += __shfl_xor(ld, 32, 64);
+  if (p.final_direct) {  // one split: normalize here (sink, output gate) and write O and LSE
+    if (!row_ok) return;
+    const size_t orow = ((size_t)b * p.Tq + j) * p.Hq + h;
+    const bool ch = p.gate_ch && p.out_gate;  // per-channel output gate
+    const RowNorm n = row_norm(m_run, ld, p.sink, h, ch ? 1.0 : out_gate_of(p.out_gate, orow));
+#pragma unroll
+    for (int db = 0; db < C::DB; db++) {
+      const int c0 = 16 * db + 4 * jg;  // this lane's 4 columns of row rn
+      float o4[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        o4[e] = oacc[db][e] * n.factor * (ch ? sigmoid_f(p.out_gate[orow * D + c0 + e]) : 1.f);
+      if (p.out_f32) {
+        *(f32x4*)((float*)p.o + orow * D + c0) = f32x4{o4[0], o4[1], o4[2], o4[3]};
+      } else {
+        uint16_t* op = (uint16_t*)p.o + orow * D + c0;
+        const uint32_t lo = (uint32_t)f2bf(o4[0]) | ((uint32_t)f2bf(o4[1]) << 16);
+        const uint32_t hi = (uint32_t)f2bf(o4[2]) | ((uint32_t)f2bf(o4[3]) << 16);
+        *(uint2*)op = make_uint2(lo, hi);
+      }
+    }
+    if (p.lse && jg == 0) p.lse[((size_t)b * p.Hq + h) * p.Tq + j] = n.lse;
+    return;
+  }
+  // partials of this split: row maximum, row sum, O^T
   const size_t n_sets = (size_t)p.B * p.Hkv * p.sets_per_bu * p.cpq;
   const int set = ((b * p.Hkv + u) * p.sets_per_bu + j) * p.cpq + hc;
   const size_t prow = ((size_t)split * n_sets + set) * 16 + rn;

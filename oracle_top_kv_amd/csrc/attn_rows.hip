@@ -488,40 +488,6 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   out.L = Ls;
 }
 
-// Normalization of one row from its maximum M (log2 domain) and its sum L relative to M, with
-// an optional per-head sink logit s (natural log): the softmax denominator becomes
-// e^s + sum_i e^a_i, and the sink itself carries no value (the learnable per-head sink bias of
-// the pages' sparse and sliding-window layers, P1 section 6.1 and P4 experimental setup, taken in the
-// gpt-oss form those pages refer to).  Returns the factor that turns the unnormalized output
-// (relative to M) into the output, scaled by `weight`, and the row's LSE including the sink.
-// Without a sink: factor = weight / L and LSE = (M + log2 L) ln 2, as before.
-struct RowNorm {
-  float factor;
-  float lse;
-};
-__device__ __forceinline__ RowNorm row_norm(float M, double L, const float* sink, int h,
-                                            double weight) {
-  const double s2 = sink ? (double)sink[h] * 1.4426950408889634 : -INFINITY;
-  const double mx = fmax((double)M, s2);
-  RowNorm n = {0.f, -INFINITY};
-  if (mx == -INFINITY) return n;  // no key and no sink
-  const double e = exp2((double)M - mx);  // 1 without a sink; 0 when the row has no key
-  const double Lp = L * e + (sink ? exp2(s2 - mx) : 0.0);
-  if (!(Lp > 0.0)) return n;
-  n.factor = (float)(weight * e / Lp);
-  n.lse = (float)((mx + log2(Lp)) * kLn2);
-  return n;
-}
-
-// Sigmoid output gate of (b, t, h), or 1 without one.
-__device__ __forceinline__ double out_gate_of(const float* g, size_t i) {
-  return g ? 1.0 / (1.0 + exp(-(double)g[i])) : 1.0;
-}
-
-__device__ __forceinline__ float sigmoid_f(float z) {
-  return (float)(1.0 / (1.0 + exp(-(double)z)));
-}
-
 // GATED: the HySparse sparse layer in one workgroup when neither branch is split -- the block
 // (or token) branch over K, V, then the sliding-window branch over K', V' (p.k2, p.v2), each
 // normalized on its own and weighted by its sigmoid gate [P2 "Same query, two memories"].
@@ -836,13 +802,17 @@ hipError_t launch_ra_paged(const RowAttnParams& p, KeySrc src, bool gated, hipSt
   const dim3 grid(ra_grid(p));
   const int threads = 64 * NW;
   if (gated) {
-    if (src == SRC_TOKEN)
-      row_attn_kernel<D, F32, SRC_TOKEN, true, NW, false, true><<<grid, threads, 0, stream>>>(p);
-    else if (src == SRC_BLOCK)
-      row_attn_kernel<D, F32, SRC_BLOCK, true, NW, false, true><<<grid, threads, 0, stream>>>(p);
-    else
-      return hipErrorInvalidValue;
-    return hipGetLastError();
+    if constexpr (D > 128) {
+      return hipErrorInvalidValue;  // registers: one branch per launch
+    } else {
+      if (src == SRC_TOKEN)
+        row_attn_kernel<D, F32, SRC_TOKEN, true, NW, false, true><<<grid, threads, 0, stream>>>(p);
+      else if (src == SRC_BLOCK)
+        row_attn_kernel<D, F32, SRC_BLOCK, true, NW, false, true><<<grid, threads, 0, stream>>>(p);
+      else
+        return hipErrorInvalidValue;
+      return hipGetLastError();
+    }
   }
   switch (src) {
     case SRC_RANGE:
@@ -875,11 +845,15 @@ hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t
     return hipErrorInvalidValue;
   }
   if (gated) {
-    if (src == SRC_TOKEN)
-      row_attn_kernel<D, F32, SRC_TOKEN, true, NW><<<grid, threads, 0, stream>>>(p);
-    else
-      row_attn_kernel<D, F32, SRC_BLOCK, true, NW><<<grid, threads, 0, stream>>>(p);
-    return hipGetLastError();
+    if constexpr (D > 128) {
+      return hipErrorInvalidValue;  // registers: one branch per launch
+    } else {
+      if (src == SRC_TOKEN)
+        row_attn_kernel<D, F32, SRC_TOKEN, true, NW><<<grid, threads, 0, stream>>>(p);
+      else
+        row_attn_kernel<D, F32, SRC_BLOCK, true, NW><<<grid, threads, 0, stream>>>(p);
+      return hipGetLastError();
+    }
   }
   switch (src) {
     case SRC_RANGE: row_attn_kernel<D, F32, SRC_RANGE, false, NW><<<grid, threads, 0, stream>>>(p); break;

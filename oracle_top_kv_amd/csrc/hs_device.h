@@ -123,4 +123,38 @@ __device__ __forceinline__ void kahan_add(float& s, float& c, float x) {
   s = t;
 }
 
+// Normalization of one row from its maximum M (log2 domain) and its sum L relative to M, with
+// an optional per-head sink logit s (natural log): the softmax denominator becomes
+// e^s + sum_i e^a_i, and the sink itself carries no value (the learnable per-head sink bias of
+// the pages' sparse and sliding-window layers, P1 section 6.1 and P4 experimental setup, taken
+// in the gpt-oss form those pages refer to).  Returns the factor that turns the unnormalized
+// output (relative to M) into the output, scaled by `weight`, and the row's LSE including the
+// sink.  Without a sink: factor = weight / L and LSE = (M + log2 L) ln 2.
+struct RowNorm {
+  float factor;
+  float lse;
+};
+__device__ __forceinline__ RowNorm row_norm(float M, double L, const float* sink, int h,
+                                            double weight) {
+  const double s2 = sink ? (double)sink[h] * 1.4426950408889634 : -INFINITY;
+  const double mx = fmax((double)M, s2);
+  RowNorm n = {0.f, -INFINITY};
+  if (mx == -INFINITY) return n;  // no key and no sink
+  const double e = exp2((double)M - mx);  // 1 without a sink; 0 when the row has no key
+  const double Lp = L * e + (sink ? exp2(s2 - mx) : 0.0);
+  if (!(Lp > 0.0)) return n;
+  n.factor = (float)(weight * e / Lp);
+  n.lse = (float)((mx + log2(Lp)) * kLn2);
+  return n;
+}
+
+// Sigmoid output gate of (b, t, h), or 1 without one.
+__device__ __forceinline__ double out_gate_of(const float* g, size_t i) {
+  return g ? 1.0 / (1.0 + exp(-(double)g[i])) : 1.0;
+}
+
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return (float)(1.0 / (1.0 + exp(-(double)z)));
+}
+
 }  // namespace hs

@@ -78,6 +78,9 @@ CASES = [
     ("prefill_g40_d64_chunks_compactions", Workload("pc40", 1, 20, 6000, 40, 1, 64, "bf16",
                                                     k_global=1024, window=128, block=32,
                                                     n_blocks=16, seed=1019)),
+    # enough queries that every list is unsplit: the group kernel writes the outputs itself
+    ("prefill_g40_unsplit", Workload("pd40", 1, 520, 1400, 40, 1, 128, "bf16", k_global=200,
+                                     window=32, block=64, n_blocks=8, seed=1021)),
 ]
 
 

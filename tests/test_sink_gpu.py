@@ -67,6 +67,9 @@ TOKEN_CASES = [
                                 seed=508), ("sink", "out_gate")),
     ("mqa64_d256_two_queries", Workload("sm", 1, 2, 1500, 64, 1, 256, "bf16", k_global=200,
                                         window=32, seed=509), ("sink", "out_gate")),
+    # 256 queries: unsplit lists, the group kernel normalizes and gates its rows itself
+    ("mqa64_d256_unsplit", Workload("smd", 1, 256, 1500, 64, 1, 256, "bf16", k_global=200,
+                                    window=32, seed=510), ("sink", "out_gate")),
 ]
 
 
@@ -142,7 +145,7 @@ def channel_gates(wl, seed, n_branch_gates):
 
 CHANNEL_TOKEN_CASES = [c for c in TOKEN_CASES if c[0] in (
     "decode_g4_split", "decode_g4_wide", "prefill_g4", "tiny_f32", "decode_g4_d256",
-    "mqa64_d256_two_queries")]
+    "mqa64_d256_two_queries", "mqa64_d256_unsplit")]
 
 
 @pytest.mark.parametrize("name,wl,which", CHANNEL_TOKEN_CASES,
