@@ -1120,6 +1120,7 @@ hs_status sparse_layer(const hs_attn_desc* desc, const void* q, const void* k_fu
   pg.out_gate = ogate;
   pg.gate_ch = gate_ch;
   pg.ring = ring;
+  pg.query_major = g.glob.sets_per_bu > 1;  // many queries: one (b, u)'s rows at a time
   if (pages) set_pages(pg, pages);
   const hs::KeySrc src = kind == HS_IDX_TOKEN ? hs::SRC_TOKEN : hs::SRC_BLOCK;
   if (g.fused) {

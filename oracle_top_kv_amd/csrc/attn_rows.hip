@@ -505,7 +505,9 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
 
   // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
   // workgroups reading the same positions of the Hkv interleaved heads run together (whole
-  // [Hkv, d] rows of K and V are then consumed close in time).
+  // [Hkv, d] rows of K and V are then consumed close in time).  query_major (index lists of
+  // many queries): query fastest, so that the workgroups resident at one time gather from the
+  // K and V of one (batch entry, KV head), which then stay in the last-level cache.
   // Head chunks (groups of more than 16 heads: 16 heads per set) of one key range read the
   // same K and V rows: they are placed on the same XCD (consecutive workgroup ids go round-robin
   // over the 8 XCDs, each with its own L2), so that the rows come from HBM once.
@@ -522,11 +524,20 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
       x = full / p.cpq + (blockIdx.x - full) / p.cpq;
     }
   }
-  const int u = x % p.Hkv;
-  const int split = (x / p.Hkv) % p.n_split;
-  const int bq = x / (p.Hkv * p.n_split);
-  const int sq = bq % p.sets_per_bu;
-  const int b = bq / p.sets_per_bu;
+  int u, split, sq, b;
+  if (p.query_major) {  // query fastest, then split, then (batch, KV head)
+    sq = x % p.sets_per_bu;
+    split = (x / p.sets_per_bu) % p.n_split;
+    const int bu = x / (p.sets_per_bu * p.n_split);
+    u = bu % p.Hkv;
+    b = bu / p.Hkv;
+  } else {
+    u = x % p.Hkv;
+    split = (x / p.Hkv) % p.n_split;
+    const int bq = x / (p.Hkv * p.n_split);
+    sq = bq % p.sets_per_bu;
+    b = bq / p.sets_per_bu;
+  }
   const int set = ((b * p.Hkv + u) * p.sets_per_bu + sq) * p.cpq + hc;
   const int j0 = sq * p.q_per_set;
   const int nq = min(p.q_per_set, p.Tq - j0);

@@ -57,6 +57,7 @@ struct RowAttnParams {
   const int32_t* pages;
   int page_size, max_pages, n_pages;
   int ring;  // window source: K2 / V2 (or K / V) are rings [B, ring, Hkv, d], slot t % ring (0: none)
+  int query_major;  // workgroup order: query fastest (else KV head fastest)
 };
 
 // Merge of split partials (one or two branches) into O and LSE; with two branches the sigmoid
