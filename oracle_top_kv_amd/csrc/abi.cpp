@@ -1137,9 +1137,6 @@ hs_status sparse_layer(const hs_attn_desc* desc, const void* q, const void* k_fu
     carve_partials(w, g.glob, s.D, &pg.part_m, &pg.part_l, &pg.part_o);
     w += partial_bytes(g.glob, s.D);
   }
-  hipError_t e = g.group ? hs::launch_group_attn(pg, s.D, src, hst)
-                         : hs::launch_row_attn(pg, s.D, s.in_f32, src, hst, false, g.wide);
-  if (e != hipSuccess) return hip_status(e, "sparse attention kernel");
   hs::RowAttnParams pl;
   if (window > 0) {
     pl = ra_params(s, g.loc);
@@ -1150,8 +1147,19 @@ hs_status sparse_layer(const hs_attn_desc* desc, const void* q, const void* k_fu
     pl.ring = ring;
     pl.final_direct = 0;
     carve_partials(w, g.loc, s.D, &pl.part_m, &pl.part_l, &pl.part_o);
-    e = hs::launch_row_attn(pl, s.D, s.in_f32, hs::SRC_WINDOW, hst);
-    if (e != hipSuccess) return hip_status(e, "sliding-window kernel");
+  }
+  hipError_t e;
+  if (window > 0 && !g.group && !g.wide) {  // both branches in one launch
+    e = hs::launch_row_attn_two(pg, pl, s.D, s.in_f32, src, hst);
+    if (e != hipSuccess) return hip_status(e, "sparse attention kernel (two branches)");
+  } else {
+    e = g.group ? hs::launch_group_attn(pg, s.D, src, hst)
+                : hs::launch_row_attn(pg, s.D, s.in_f32, src, hst, false, g.wide);
+    if (e != hipSuccess) return hip_status(e, "sparse attention kernel");
+    if (window > 0) {
+      e = hs::launch_row_attn(pl, s.D, s.in_f32, hs::SRC_WINDOW, hst);
+      if (e != hipSuccess) return hip_status(e, "sliding-window kernel");
+    }
   }
   if (g.combine) {
     hs::CombineParams c = combine_params(s, g.glob, o, lse_opt);

@@ -488,20 +488,25 @@ __device__ __forceinline__ void attend_pass(const RowAttnParams& p, const void* 
   out.L = Ls;
 }
 
+// LDS bytes of a row-kernel workgroup besides its position lists.
+template <int D, bool F32, int NW, bool LOGITS>
+constexpr int row_attn_smem_bytes() {
+  using Cfg = RaCfg<D, F32, NW>;
+  // LOGITS: the logit staging rows of every wave follow the V tiles
+  return LOGITS && NW * (Cfg::kVTileBytes + kLogitWaveBytes) > Cfg::kSmem
+             ? NW * (Cfg::kVTileBytes + kLogitWaveBytes)
+             : Cfg::kSmem;
+}
+
+// One workgroup of a row-kernel launch: workgroup `bid` of `nblocks`, with the LDS arrays of the
+// calling kernel (smem: row_attn_smem_bytes; pos_all, row_all: kMaxListEntries ints).
 // GATED: the HySparse sparse layer in one workgroup when neither branch is split -- the block
 // (or token) branch over K, V, then the sliding-window branch over K', V' (p.k2, p.v2), each
 // normalized on its own and weighted by its sigmoid gate [P2 "Same query, two memories"].
-template <int D, bool F32, int SRC, bool GATED, int NW, bool LOGITS = false, bool PAGED = false>
-__global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
+template <int D, bool F32, int SRC, bool GATED, int NW, bool LOGITS, bool PAGED>
+__device__ __forceinline__ void row_attn_wg(const RowAttnParams& p, int bid, int nblocks,
+                                            unsigned char* smem, int* pos_all, int* row_all) {
   using Cfg = RaCfg<D, F32, NW>;
-  // LOGITS: the logit staging rows of every wave follow the V tiles
-  constexpr int kSmemBytes =
-      LOGITS && NW * (Cfg::kVTileBytes + kLogitWaveBytes) > Cfg::kSmem
-          ? NW * (Cfg::kVTileBytes + kLogitWaveBytes)
-          : Cfg::kSmem;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
-  __shared__ int pos_all[kMaxListEntries];
-  __shared__ int row_all[PAGED && SRC != SRC_RANGE ? kMaxListEntries : 1];
 
   // Workgroup order: KV head fastest, then split, then (batch, query chunk), so that the
   // workgroups reading the same positions of the Hkv interleaved heads run together (whole
@@ -511,17 +516,17 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
   // Head chunks (groups of more than 16 heads: 16 heads per set) of one key range read the
   // same K and V rows: they are placed on the same XCD (consecutive workgroup ids go round-robin
   // over the 8 XCDs, each with its own L2), so that the rows come from HBM once.
-  int hc = 0, x = blockIdx.x;
+  int hc = 0, x = bid;
   if (p.cpq > 1) {
     const int n8 = kXcds * p.cpq;
-    const int full = (int)(gridDim.x / n8) * n8;
-    if ((int)blockIdx.x < full) {
-      const int grp = blockIdx.x / n8, within = blockIdx.x % n8;
+    const int full = (nblocks / n8) * n8;
+    if (bid < full) {
+      const int grp = bid / n8, within = bid % n8;
       hc = within / kXcds;
       x = grp * kXcds + within % kXcds;
     } else {
-      hc = (blockIdx.x - full) % p.cpq;
-      x = full / p.cpq + (blockIdx.x - full) / p.cpq;
+      hc = (bid - full) % p.cpq;
+      x = full / p.cpq + (bid - full) / p.cpq;
     }
   }
   int u, split, sq, b;
@@ -626,6 +631,34 @@ __global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
     for (int c = 0; c < CPT; c++) op[Cfg::col(lr, c)] = f2bf(res[c]);
   }
   if (p.lse && lr == 0) p.lse[((size_t)b * p.Hq + hr) * p.Tq + jr] = lse_row;
+}
+
+template <int D, bool F32, int SRC, bool GATED, int NW, bool LOGITS = false, bool PAGED = false>
+__global__ __launch_bounds__(64 * NW) void row_attn_kernel(RowAttnParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[row_attn_smem_bytes<D, F32, NW, LOGITS>()];
+  __shared__ int pos_all[kMaxListEntries];
+  __shared__ int row_all[PAGED && SRC != SRC_RANGE ? kMaxListEntries : 1];
+  row_attn_wg<D, F32, SRC, GATED, NW, LOGITS, PAGED>(p, blockIdx.x, gridDim.x, smem, pos_all,
+                                                     row_all);
+}
+
+// Both branches of a gated sparse layer whose lists are split, in one launch: the first
+// n_glob workgroups take the split token / block lists over K, V (pg), the others the sliding
+// window over K', V' (pl); all write split partials for the two-branch combine.  One launch
+// instead of two: the window branch's workgroups run beside the list branch's instead of after
+// them.
+template <int D, bool F32, int SRC, int NW, bool PAGED>
+__global__ __launch_bounds__(64 * NW) void row_attn_two_kernel(RowAttnParams pg, RowAttnParams pl,
+                                                               int n_glob) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[row_attn_smem_bytes<D, F32, NW, false>()];
+  __shared__ int pos_all[kMaxListEntries];
+  __shared__ int row_all[PAGED ? kMaxListEntries : 1];
+  if ((int)blockIdx.x < n_glob)
+    row_attn_wg<D, F32, SRC, false, NW, false, PAGED>(pg, blockIdx.x, n_glob, smem, pos_all,
+                                                      row_all);
+  else
+    row_attn_wg<D, F32, SRC_WINDOW, false, NW, false, false>(
+        pl, blockIdx.x - n_glob, gridDim.x - n_glob, smem, pos_all, row_all);
 }
 
 // ---- split / branch combine ---------------------------------------------------------------
@@ -875,7 +908,42 @@ hipError_t launch_ra(const RowAttnParams& p, KeySrc src, bool gated, hipStream_t
   return hipGetLastError();
 }
 
+template <int D, bool F32, bool PAGED>
+hipError_t launch_two(const RowAttnParams& pg, const RowAttnParams& pl, KeySrc src,
+                      hipStream_t stream) {
+  const int n_glob = (int)ra_grid(pg);
+  const dim3 grid(n_glob + ra_grid(pl));
+  if (src == SRC_TOKEN)
+    row_attn_two_kernel<D, F32, SRC_TOKEN, 4, PAGED><<<grid, 256, 0, stream>>>(pg, pl, n_glob);
+  else if (src == SRC_BLOCK)
+    row_attn_two_kernel<D, F32, SRC_BLOCK, 4, PAGED><<<grid, 256, 0, stream>>>(pg, pl, n_glob);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int D, bool F32>
+hipError_t launch_two_d(const RowAttnParams& pg, const RowAttnParams& pl, KeySrc src,
+                        hipStream_t stream) {
+  return pg.pages ? launch_two<D, F32, true>(pg, pl, src, stream)
+                  : launch_two<D, F32, false>(pg, pl, src, stream);
+}
+
 }  // namespace
+
+hipError_t launch_row_attn_two(const RowAttnParams& pg, const RowAttnParams& pl, int head_dim,
+                               bool in_f32, KeySrc src, hipStream_t stream) {
+  if (pg.final_direct || pl.final_direct || pl.pages) return hipErrorInvalidValue;
+  if (head_dim == 256) {
+    if (in_f32) return hipErrorInvalidValue;
+    return launch_two_d<256, false>(pg, pl, src, stream);
+  }
+  if (head_dim == 128)
+    return in_f32 ? launch_two_d<128, true>(pg, pl, src, stream)
+                  : launch_two_d<128, false>(pg, pl, src, stream);
+  return in_f32 ? launch_two_d<64, true>(pg, pl, src, stream)
+                : launch_two_d<64, false>(pg, pl, src, stream);
+}
 
 hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
                            hipStream_t stream, bool gated, bool wide) {

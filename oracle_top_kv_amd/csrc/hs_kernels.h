@@ -85,6 +85,11 @@ struct CombineParams {
 // of 4 (bf16 only), for unsplit key lists of few row-sets.
 hipError_t launch_row_attn(const RowAttnParams& p, int head_dim, bool in_f32, KeySrc src,
                            hipStream_t stream, bool gated = false, bool wide = false);
+// Both branches of a gated layer whose lists are split, in one launch of 4-wave workgroups: the
+// token / block lists of pg (src), then the sliding window of pl (window source, not paged); both
+// write split partials.
+hipError_t launch_row_attn_two(const RowAttnParams& pg, const RowAttnParams& pl, int head_dim,
+                               bool in_f32, KeySrc src, hipStream_t stream);
 
 // Attention for groups of 32, 48 or 64 heads (bf16, head_dim 128 or 256) over a range (full
 // attention, optional logits as in the row kernel) or a token / block list (steps_per_split 64-key
