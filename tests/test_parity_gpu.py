@@ -123,6 +123,24 @@ def test_full_attn_moving_maximum(profile):
     assert el <= lse_bound(lse_ref)
 
 
+@pytest.mark.parametrize("profile", list(PROFILES), ids=list(PROFILES))
+def test_full_attn_moving_maximum_row_kernel(profile):
+    """The same logit profiles on decode shapes (one and three queries, split key ranges): the
+    row kernel's online softmax and the split combine under a moving maximum."""
+    for wl in (Workload("mvd", 2, 1, 2500, 8, 2, 128, "bf16", seed=42),
+               Workload("mvd3", 1, 3, 2500, 16, 4, 64, "bf16", seed=43)):
+        say(f"[full_attn moving maximum, row kernel] {profile} {wl}")
+        q, k, v = logit_profile_inputs(wl, PROFILES[profile])
+        o, lse = hs().full_attn_fwd(to_dev(q), to_dev(k), to_dev(v), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.full_attention(to_numpy_f32(q), to_numpy_f32(k), to_numpy_f32(v))
+        eo = max_abs(o.cpu().numpy(), o_ref)
+        el = max_abs(lse.cpu().numpy(), lse_ref)
+        say(f"  max|dO| = {eo:.3e}  max|dLSE| = {el:.3e}")
+        assert eo <= TOL_BF16
+        assert el <= lse_bound(lse_ref)
+
+
 # ---- token top-k -------------------------------------------------------------------------
 
 TOPK_CASES = [
