@@ -34,14 +34,17 @@
  *     multiple of 16; the group shares one index set through the maximum over all its heads,
  *     [P2 "Why GQA shares the index within a group"]); kv_len <= 2^30; out_dtype bf16 or fp32.
  *     Block selection needs block a multiple of 16 and 1 <= n_blocks <= 64.  Index selection
- *     from Q and K takes every such shape: many query rows with g <= 16 stream over K tiles
- *     (groups padded to 4, 8 or 16 heads); few rows with g in {4, 8, 16} and head_dim <= 128
+ *     from Q and K takes every such shape: many query rows stream over K tiles (groups of up
+ *     to 16 heads padded to 4, 8 or 16; larger groups, given at least 16 queries, in chunks of
+ *     16 heads whose candidates are merged exactly); few rows with g in {4, 8, 16} and
+ *     head_dim <= 128
  *     run the fused score passes; every other shape first computes the rows' raw logits into
  *     the workspace (at most 8 GiB of them: B * q_len * Hq * kv_len * 4 bytes, else
  *     HS_ERR_UNSUPPORTED) and selects from them like stored logits.  Full attention with many
  *     query rows per KV head runs a tiled kernel (bf16; 256 rows per workgroup, 128 at head
- *     size 256, which the group size must divide); the sparse layers at head size 256 run as
- *     two branches plus a combine.  Anything else returns HS_ERR_UNSUPPORTED.
+ *     size 256, which the group size must divide); the gated sparse layer at head size 256
+ *     runs its two branches as split partials plus a combine.  Anything else returns
+ *     HS_ERR_UNSUPPORTED.
  *   - Workspace sizes, for orientation: token selection with many query rows per KV head and
  *     k_global <= 1024 keeps a 16 KiB candidate buffer per (b, t, u); with few rows it keeps
  *     4 bytes per candidate key per (b, t, u) plus an 8 KiB histogram (12 bytes per key past
