@@ -432,6 +432,17 @@ def prefill_leg(args):
     t_fa = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
     t_tk = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
     t_sp = sum(e[2].elapsed_time(e[3]) for e in ev) / reps
+    # the same two stages in one call: the selection starts at the tile-maximum bound
+    _, _, idx1, cnt1 = hs.full_attn_topk(q, k, v, wl.k_global, wl.window)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(idx1, idx) and torch.equal(cnt1, cnt))
+    ev1 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for r in range(reps):
+        ev1[r][0].record()
+        hs.full_attn_topk(q, k, v, wl.k_global, wl.window)
+        ev1[r][1].record()
+    torch.cuda.synchronize()
+    t_one = sum(e[0].elapsed_time(e[1]) for e in ev1) / reps
     f_fa, f_sc = costs.full_attn_flops(wl), costs.score_flops(wl)
     tot = (f_fa + f_sc) / ((t_fa + t_tk) * 1e-3) / 1e12
     b_sp = costs.token_gather_bytes(wl)  # rows each (b, t, u) gathers (mostly from cache)
@@ -440,6 +451,9 @@ def prefill_leg(args):
             "full_attn_tflops": round(f_fa / (t_fa * 1e-3) / 1e12, 1),
             "topk_score_tflops": round(f_sc / (t_tk * 1e-3) / 1e12, 1),
             "full_attn_plus_topk_tflops": round(tot, 1),
+            "one_call_full_attn_topk_ms": round(t_one, 3),
+            "one_call_full_attn_topk_tflops": round((f_fa + f_sc) / (t_one * 1e-3) / 1e12, 1),
+            "one_call_sets_identical": same,
             "useful_tflops": round(f_fa / ((t_fa + t_tk) * 1e-3) / 1e12, 1),
             "mfma_frac_full_attn": round(f_fa / (t_fa * 1e-3) / 2.5e15, 4),
             "sparse_layer_ms": round(t_sp, 3),

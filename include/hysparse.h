@@ -84,7 +84,8 @@ typedef enum {
   HS_OP_TOPK_FROM_LOGITS = 5,       /* p0 = k_global, p1 = window */
   HS_OP_BLOCK_TOPK_FROM_LOGITS = 6, /* p0 = block, p1 = n_blocks */
   HS_OP_FULL_ATTN_BLOCK_TOPK = 7,   /* p0 = block, p1 = n_blocks */
-  HS_OP_FULL_ATTN_PAGED = 8         /* p0 = page_size */
+  HS_OP_FULL_ATTN_PAGED = 8,        /* p0 = page_size */
+  HS_OP_FULL_ATTN_TOPK = 9          /* p0 = k_global, p1 = window */
 } hs_op;
 
 typedef struct {
@@ -202,6 +203,26 @@ hs_status hs_full_attn_block_topk(const hs_attn_desc* desc, const void* q, const
                                   const void* v, int32_t block, int32_t n_blocks, void* o,
                                   float* lse, int32_t* blk_idx, int32_t* count, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/* Full attention and token-level oracle index in one call: the outputs of hs_full_attn_fwd
+ * (o, lse) and of hs_oracle_topk (idx, count) for the same inputs, the same bit for bit.  For
+ * prefill-shaped bf16 calls of whole groups (q_len * g > 16, g <= 16, head_dim 64 or 128, the
+ * tiled prefill kernel) the attention pass also records every (query, head) row's largest logit
+ * in each 64-key tile, and the selection pass starts every (b, t, u) at the k-th largest tile
+ * score over the tiles lying before the window.  A tile's score is the largest score of its
+ * keys [P2 "Extracting block scores from exact attention": block score = maximum over the
+ * block's tokens], so these are the scores of k distinct candidates and the k-th candidate score
+ * is at least as large: only keys at or above the bound enter the candidate lists, and ranking
+ * needs no more than that [P2 "TopK only needs ranking"].  bound_margin (log2 units, finite) is
+ * subtracted from the bound to cover the two passes' different accumulation orders (1/64 is
+ * ample); a row whose bound still exceeds its k-th score collects fewer than k candidates and is
+ * selected again without it, so the index sets never depend on the bound or the margin (a
+ * negative margin only costs that second pass).  Other shapes run the two calls one after the
+ * other.  Workspace: hs_workspace_size(HS_OP_FULL_ATTN_TOPK, desc, k_global, window). */
+hs_status hs_full_attn_topk(const hs_attn_desc* desc, const void* q, const void* k, const void* v,
+                            int32_t k_global, int32_t window, float bound_margin, void* o,
+                            float* lse, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* Sparse layer over the full layer's K, V and index set, with the layer's own queries q
  * [P2 "Cross-layer KV cache reuse", gather equations; P2 "Same query, two memories";

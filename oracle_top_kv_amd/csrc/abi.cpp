@@ -14,6 +14,14 @@
 
 namespace {
 
+// Finite float test on the bit pattern: this file is built with -fno-honor-nans (for the
+// kernels' max operations), under which comparisons may assume that no operand is NaN.
+bool finite_bits(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  return (u & 0x7F800000u) != 0x7F800000u;
+}
+
 thread_local char g_err[512] = "";
 
 hs_status fail(hs_status s, const char* fmt, ...) {
@@ -55,7 +63,7 @@ hs_status check_desc(const hs_attn_desc* d, Shape* s) {
   if (q_off < 0 || q_off + d->q_len > d->kv_len)
     return fail(HS_ERR_INVALID_ARG, "q_offset %lld with q_len %d does not fit kv_len %d", q_off,
                 d->q_len, d->kv_len);
-  if (!(d->scale >= 0.f) || !std::isfinite(d->scale))
+  if (!finite_bits(d->scale) || d->scale < 0.f)
     return fail(HS_ERR_INVALID_ARG, "scale %g: must be finite and >= 0 (0: 1/sqrt(head_dim))",
                 (double)d->scale);
   const int g = d->n_q_heads / d->n_kv_heads;
@@ -709,6 +717,43 @@ size_t fused_blocks_ws(const Shape& s, int block, int n_blocks) {
   return a > b ? a : b;
 }
 
+// Workspace of a token selection from Q and K on its route (0 and an error: no route).
+size_t token_select_ws(const Shape& s, int k_global) {
+  switch (token_route(s, k_global)) {
+    case SEL_PREFILL: return tk_prefill_ws(s);
+    case SEL_DECODE: return tk_ws(s, tk_geom(s));
+    case SEL_LOGITS: return logit_bytes(s) + tk_ws(s, tl_geom(s));
+    case SEL_NONE: break;
+  }
+  fail(HS_ERR_UNSUPPORTED, "token selection: no route for this shape");
+  return 0;
+}
+
+// Token selection started at the tile-maximum bound: the tiled prefill attention kernel (head
+// sizes up to 128) and the prefill selection of whole groups.
+bool fused_tokens(const Shape& s, int k_global) {
+  return use_prefill_kernel(s) && s.D <= 128 && s.g <= 16 && k_global >= 1 &&
+         token_route(s, k_global) == SEL_PREFILL;
+}
+int tmax_stride(const Shape& s) {
+  const long long tiles = (s.Tk + 63) / 64;
+  return (int)((tiles + 15) / 16 * 16);
+}
+size_t tmax_bytes(const Shape& s) {
+  return align_up((size_t)s.B * s.Hq * s.Tq * (size_t)tmax_stride(s) * 2, 256);
+}
+size_t redo_bytes(const Shape& s) { return align_up((size_t)s.B * s.Tq * s.Hkv * 4, 256); }
+
+// Workspace of hs_full_attn_topk: tile maxima, candidate buffers and row flags when fused,
+// else what the larger of its two passes needs.
+size_t fused_tokens_ws(const Shape& s, int k_global) {
+  if (fused_tokens(s, k_global)) return tmax_bytes(s) + tk_prefill_ws(s) + redo_bytes(s);
+  const size_t a = full_attn_ws(s);
+  const size_t b = token_select_ws(s, k_global);
+  if (b == 0 && token_route(s, k_global) == SEL_NONE) return 0;
+  return a > b ? a : b;
+}
+
 hs::BlockTopkParams bk_params(const Shape& s, const BkGeom& g, const float* lse, int block,
                               int n_blocks, int32_t* blk_idx, int32_t* count, void* ws) {
   hs::BlockTopkParams p;
@@ -758,16 +803,8 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
   if (check_desc(desc, &s) != HS_OK) return 0;
   switch (op) {
     case HS_OP_FULL_ATTN: return full_attn_ws(s);
-    case HS_OP_ORACLE_TOPK: {
-      switch (token_route(s, p0)) {
-        case SEL_PREFILL: return tk_prefill_ws(s);
-        case SEL_DECODE: return tk_ws(s, tk_geom(s));
-        case SEL_LOGITS: return logit_bytes(s) + tk_ws(s, tl_geom(s));
-        case SEL_NONE: break;
-      }
-      fail(HS_ERR_UNSUPPORTED, "token selection: no route for this shape");
-      return 0;
-    }
+    case HS_OP_ORACLE_TOPK: return token_select_ws(s, p0);
+    case HS_OP_FULL_ATTN_TOPK: return fused_tokens_ws(s, p0);
     case HS_OP_BLOCK_TOPK: {
       BkGeom g;
       SelRoute r;
@@ -845,6 +882,62 @@ hs_status hs_full_attn_block_topk(const hs_attn_desc* desc, const void* q, const
   if (st != HS_OK) return st;
   return hs_block_score_topk(desc, q, k, lse, block, n_blocks, blk_idx, count, ws, ws_bytes,
                              stream);
+}
+
+hs_status hs_full_attn_topk(const hs_attn_desc* desc, const void* q, const void* k, const void* v,
+                            int32_t k_global, int32_t window, float bound_margin, void* o,
+                            float* lse, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                            void* stream) {
+  Shape s;
+  hs_status st = check_desc(desc, &s);
+  if (st != HS_OK) return st;
+  st = check_qkv_dtype(s);
+  if (st != HS_OK) return st;
+  if (!q || !k || !v || !o || !lse || !idx || !count)
+    return fail(HS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (k_global < 0 || window < 0) return fail(HS_ERR_INVALID_ARG, "k_global and window must be >= 0");
+  if ((long long)k_global + window < 1) return fail(HS_ERR_INVALID_ARG, "k_global + window must be >= 1");
+  if (!finite_bits(bound_margin)) return fail(HS_ERR_INVALID_ARG, "bound_margin must be finite");
+  if (token_route(s, k_global) == SEL_NONE)
+    return fail(HS_ERR_UNSUPPORTED, "token selection: no route for this shape");
+  const size_t need = fused_tokens_ws(s, k_global);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(HS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!fused_tokens(s, k_global)) {
+    st = hs_full_attn_fwd(desc, q, k, v, o, lse, ws, ws_bytes, stream);
+    if (st != HS_OK) return st;
+    return hs_oracle_topk(desc, q, k, lse, k_global, window, idx, count, ws, ws_bytes, stream);
+  }
+  hipStream_t hst = (hipStream_t)stream;
+  char* w = (char*)ws;
+  uint16_t* tmax = (uint16_t*)w;
+  unsigned long long* tbuf = (unsigned long long*)(w + tmax_bytes(s));
+  int32_t* redo = (int32_t*)(w + tmax_bytes(s) + tk_prefill_ws(s));
+  hs::PrefillParams pp = prefill_params(s, q, k, v, o, lse);
+  pp.tile_max = tmax;
+  pp.tmax_stride = tmax_stride(s);
+  hipError_t e = hs::launch_prefill_attn(pp, s.D, hst);
+  if (e != hipSuccess) return hip_status(e, "prefill attention kernel with tile maxima");
+  hs::PrefillSelectParams p = select_params(s, q, k, lse);
+  p.k_global = k_global;
+  p.window = window;
+  p.cap = k_global + window;
+  p.tbuf = tbuf;
+  p.idx = idx;
+  p.cnt = count;
+  p.tile_max = tmax;
+  p.tmax_stride = pp.tmax_stride;
+  p.bound_margin = bound_margin;
+  p.redo = redo;
+  e = hs::launch_prefill_select(p, s.D, false, false, hst);
+  if (e != hipSuccess) return hip_status(e, "token selection kernel from the tile-maximum bound");
+  // rows whose bound was above their k-th score, selected again without it
+  hs::PrefillSelectParams p2 = p;
+  p2.tile_max = nullptr;
+  p2.redo = nullptr;
+  p2.redo_only = redo;
+  return hip_status(hs::launch_prefill_select(p2, s.D, false, false, hst),
+                    "token selection kernel (second pass)");
 }
 
 hs_status hs_full_attn_fwd_logits(const hs_attn_desc* desc, const void* q, const void* k,

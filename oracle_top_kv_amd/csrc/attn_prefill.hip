@@ -76,6 +76,12 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// bf16 bits of x rounded toward -inf (a lower bound of x; -inf stays -inf).
+__device__ __forceinline__ uint16_t bf16_bits_down(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u >> 16) + ((u >> 31) && (u & 0xFFFFu) ? 1u : 0u));
+}
+
 // Inverse of float_key.
 __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
@@ -165,10 +171,14 @@ __device__ __forceinline__ void select_blocks(const PrefillParams& p,
 // 32x32x16 layouts (wave64, lane l, h = l / 32):
 //   A[32 x 16]: row l % 32, k = 8h .. 8h + 7;   B[16 x 32]: column l % 32, k = 8h .. 8h + 7
 //   C[32 x 32]: column l % 32, register 4g + e holds row 8g + 4h + e (g, e = 0..3)
-template <int D, bool BSEL>
+// TMAX: every row also records its raw logit maximum over each tile (bf16, rounded toward -inf),
+// two tiles per 4-byte store.
+template <int D, bool BSEL, bool TMAX = false>
 __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillParams p) {
   using C = PfCfg<D>;
   static_assert(!BSEL || C::NW == 8, "the block-selection merge assumes 8 waves");
+  static_assert(!TMAX || (!BSEL && C::BN == 64), "tile maxima: 64-key tiles, no block selection");
+
   // K/V tiles; BSEL reuses the same LDS for its merge after the last tile
   constexpr int BN = C::BN, KB = C::KB;
   static_assert(!BSEL || BN == 64, "blocks of one 64-key tile");
@@ -319,6 +329,7 @@ __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillPa
 
   // The step of tile t: S(t) in sc, S(t+1) into sn.  MASK: tile t reaches past the workgroup's
   // first query position.
+  float tmx_last = -INFINITY;  // TMAX: the row maximum of the last tile stepped
   auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB], auto mask_tag)
                   __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -340,6 +351,7 @@ __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillPa
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[kb][i], sc[kb][i + 1]));
     mx = max_halves(mx);
+    if constexpr (TMAX) tmx_last = mx;
     if constexpr (BSEL) {
       // block t = this tile: replace the list minimum when the tile's maximum beats it (equal
       // maxima keep the earlier block); both halves of the row take the same branch
@@ -432,6 +444,20 @@ __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillPa
     store_v((t + 1) & 1);
     __syncthreads();
   };
+  // TMAX: write the staged maxima of tiles tile0 .. tile0 + 15 (lane: row lane / 2, tiles
+  // tile0 + 8 (lane % 2) .. + 7; the row's slots past its last tile hold values of no tile)
+  // TMAX: lanes of the first half write their row's maxima of tiles t, t + 1 as one 4-byte store
+  uint16_t* tm_dst = nullptr;
+  if constexpr (TMAX) {
+    if (h == 0 && row_ok)
+      tm_dst = p.tile_max + (((size_t)b * p.Hq + h_row) * p.Tq + j_row) * p.tmax_stride;
+  }
+  auto put_tmax = [&](int t0, float m0, float m1) {
+    if constexpr (TMAX) {
+      if (tm_dst)
+        *(uint32_t*)(tm_dst + t0) = (uint32_t)bf16_bits_down(m0) | ((uint32_t)bf16_bits_down(m1) << 16);
+    }
+  };
   // tiles entirely at or before the first query position need no mask.  Two steps per loop
   // trip, so that S(t) always sits in sa for even t and in sb for odd t; a tile without mask
   // may run the masked step (the mask is then a no-op)
@@ -439,13 +465,20 @@ __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillPa
   int t = 0;
   for (; t + 1 < n_full; t += 2) {
     step(t, sa, sb, std::false_type());
+    const float m0 = tmx_last;
     step(t + 1, sb, sa, std::false_type());
+    put_tmax(t, m0, tmx_last);
   }
   for (; t + 1 < n_tiles; t += 2) {
     step(t, sa, sb, std::true_type());
+    const float m0 = tmx_last;
     step(t + 1, sb, sa, std::true_type());
+    put_tmax(t, m0, tmx_last);
   }
-  if (t < n_tiles) step(t, sa, sb, std::true_type());
+  if (t < n_tiles) {
+    step(t, sa, sb, std::true_type());
+    put_tmax(t, tmx_last, -INFINITY);  // the pair's second slot lies inside the padded row
+  }
 
   // epilogue: normalize and write O and LSE
   // lanes l and l ^ 32 hold the row's sums over different keys (with the same maximum)
@@ -488,6 +521,13 @@ hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t
   const bool bsel = p.blk_idx != nullptr;
   if (bsel && (p.n_blocks < 1 || p.n_blocks > 16 || 32 % p.g || head_dim > 128))
     return hipErrorInvalidValue;
+  if (p.tile_max) {  // tile maxima: head sizes 64 and 128, not with the block selection
+    if (bsel || head_dim > 128 || p.tmax_stride % 16 || p.tmax_stride < (p.Tk + kBN - 1) / kBN)
+      return hipErrorInvalidValue;
+    if (head_dim == 128) pf_attn_kernel<128, false, true><<<grid, kThreads, 0, stream>>>(p);
+    else pf_attn_kernel<64, false, true><<<grid, kThreads, 0, stream>>>(p);
+    return hipGetLastError();
+  }
   if (head_dim == 256) {
     pf_attn_kernel<256, false><<<grid, PfCfg<256>::Threads, 0, stream>>>(p);
   } else if (head_dim == 128) {

@@ -114,6 +114,10 @@ struct PrefillParams {
   int32_t* blk_idx;  // [B, Tq, Hkv, n_blocks]
   int32_t* blk_cnt;  // [B, Tq, Hkv]
   int n_blocks;
+  // or null: every row's raw logit maximum over each 64-key tile, as bf16 bits rounded toward
+  // -inf, [B, Hq, Tq, tmax_stride] (tmax_stride a multiple of 16 and >= the tiles of the row)
+  uint16_t* tile_max;
+  int tmax_stride;
 };
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
@@ -199,6 +203,15 @@ struct PrefillSelectParams {
   int chunks;
   int32_t* ccnt;               // [B, Tq, Hkv * chunks] entries kept per chunk row
   unsigned long long* cvals;   // block mode: [B, Tq, Hkv * chunks, n_blocks] kept values
+  // token mode, or null: the tile maxima of the full-attention pass (PrefillParams::tile_max),
+  // from which every row starts at a proven lower bound of its k-th score minus bound_margin;
+  // redo[row] (written for every chunk row) then flags the rows whose bound turned out too high
+  const uint16_t* tile_max;
+  int tmax_stride;
+  float bound_margin;
+  int32_t* redo;
+  // or null: only workgroups holding a row flagged here run (the rows' second pass)
+  const int32_t* redo_only;
 };
 int prefill_select_buffer_cap();
 int prefill_select_max_k();

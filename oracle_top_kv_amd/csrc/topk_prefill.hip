@@ -26,6 +26,8 @@
 // Block mode (blocks of 16, 32 or 64 keys): each query keeps its best n blocks in registers,
 // spread over the 16 lanes that hold its keys; at each block boundary the block's V replaces
 // the list minimum (found with four lane exchanges) when it is larger.
+#include <cstring>
+
 #include "hs_device.h"
 #include "hs_kernels.h"
 
@@ -57,9 +59,19 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Every global store this wave issued has completed before any later load is issued: a
+// workgroup-scope release fence alone orders the compiler but, with all of a workgroup's waves on
+// one CU, emits no wait for the stores, and the agent-scope reloads of other lanes' entries must
+// not overtake them.
+__device__ __forceinline__ void stores_done() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+}
+
 // Loads of data this kernel wrote earlier (candidate buffers): agent-scope atomic loads do not
-// return stale copies from the per-CU cache.  Callers first complete their own stores with a
-// workgroup-scope release fence.
+// return stale copies from the per-CU cache.  Callers first complete their own stores with
+// stores_done().
 __device__ __forceinline__ unsigned long long ld_coherent(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -107,18 +119,12 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Keep exactly the k largest of the n (> k) entries of `buf`; returns the new threshold theta
-// (entries >= theta are the ones kept, compacted to buf[0..k)).  Wave-wide.  If `sorted_pos`
-// is given, the kept positions (~low word) are also written there, unordered.
-__device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k, int lane,
-                                           uint32_t* hist, int* kept_pos, int slack,
-                                           int* kept_out) {
-  unsigned long long v[kNPL];
-#pragma unroll
-  for (int i = 0; i < kNPL; i++) {
-    const int idx = lane + 64 * i;
-    v[i] = idx < n ? ld_coherent(buf + idx) : 0ull;
-  }
+// Radix select over a wave's entries (kNPL per lane, 0 = empty; every nonzero entry distinct):
+// returns theta such that the entries >= theta are the k largest, or (slack > 0) at most k + slack
+// of the largest ones, all of the k largest among them.  At least k nonzero entries.  Wave-wide.
+__device__ __forceinline__ unsigned long long wave_select(const unsigned long long (&v)[kNPL],
+                                                          int k, int lane, uint32_t* hist,
+                                                          int slack) {
   // Start below the bits that all entries share: the entries are scores near the top of the
   // row, so their leading bits coincide, and a histogram of them would send every lane's atomic
   // to the same LDS bin.
@@ -160,7 +166,23 @@ __device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k
     // of the k-th entry (at most `slack` entries beyond k) ends the select after one pass.
     if (slack > 0 && (int)cnt - kr <= slack) break;
   }
-  const unsigned long long theta = prefix;
+  return prefix;
+}
+
+// Keep exactly the k largest of the n (> k) entries of `buf` (at most `slack` more, see
+// wave_select); returns the threshold theta (entries >= theta are the ones kept, compacted to
+// buf[0..kept)).  Wave-wide.  If `kept_pos` is given, the kept positions (~low word) are also
+// written there, unordered.
+__device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k, int lane,
+                                           uint32_t* hist, int* kept_pos, int slack,
+                                           int* kept_out) {
+  unsigned long long v[kNPL];
+#pragma unroll
+  for (int i = 0; i < kNPL; i++) {
+    const int idx = lane + 64 * i;
+    v[i] = idx < n ? ld_coherent(buf + idx) : 0ull;
+  }
+  const unsigned long long theta = wave_select(v, k, lane, hist, slack);
   int base = 0;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
@@ -174,7 +196,7 @@ __device__ unsigned long long wave_compact(unsigned long long* buf, int n, int k
     }
     base += __popcll(bm);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // stores complete before reloads
+  stores_done();  // the write-back is complete before anything reloads it
   *kept_out = base;
   return theta;
 }
@@ -203,6 +225,61 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// The k-th largest tile score of query row j (head rows hbase .. hbase + gc - 1 of KV head u)
+// over its tiles r0 .. r0 + nt - 1 (k <= nt <= 64 kNPL), minus bound_margin: a lower bound of the
+// row's k-th candidate score.  Wave-wide, uniform arguments; hist is scratch.
+__device__ __forceinline__ float tile_bound(const PrefillSelectParams& p, int b, int j, int u,
+                                            int hbase, int gc, int r0, int nt, int lane,
+                                            uint32_t* hist) {
+  const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
+  float sv[kNPL];  // tiles r0 + kNPL * lane + i
+#pragma unroll
+  for (int i = 0; i < kNPL; i++) sv[i] = -INFINITY;
+  // four heads per round: their 16 loads in flight together; chunks past the last tile, and
+  // heads past the group, load nothing
+  for (int h0 = 0; h0 < gc; h0 += 4) {
+    u32x4 raw[4][kNPL / 8];
+    float dl[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int hh = min(h0 + e, gc - 1);
+      const size_t hrow = ((size_t)b * p.Hq + hbase + hh) * p.Tq + j;
+      dl[e] = h0 + e < gc ? (float)((double)p.lse[hrow] * 1.4426950408889634 - Cq) : INFINITY;
+      const uint16_t* src = p.tile_max + hrow * p.tmax_stride + r0 + kNPL * lane;
+#pragma unroll
+      for (int c = 0; c < kNPL / 8; c++)
+        raw[e][c] = (h0 + e < gc && kNPL * lane + 8 * c < nt) ? *(const u32x4*)(src + 8 * c)
+                                                               : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+#pragma unroll
+      for (int i = 0; i < kNPL; i++) {
+        const uint32_t w = raw[e][i / 8][(i % 8) / 2];
+        const float x = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        sv[i] = fmaxf(sv[i], __builtin_fmaf(x, p.scale_log2, -dl[e]));
+      }
+    }
+  }
+  unsigned long long v[kNPL];
+#pragma unroll
+  for (int i = 0; i < kNPL; i++) {
+    const int r = kNPL * lane + i;
+    v[i] = r < nt ? (((unsigned long long)float_key(sv[i]) << 32) | (uint32_t)r) : 0ull;
+  }
+  const unsigned long long theta = wave_select(v, p.k_global, lane, hist, 0);
+  // the k entries >= theta are the k largest: their minimum is the k-th tile score
+  unsigned long long kth = ~0ull;
+#pragma unroll
+  for (int i = 0; i < kNPL; i++)
+    if (v[i] != 0ull && v[i] >= theta) kth = v[i] < kth ? v[i] : kth;
+  for (int m = 1; m < 64; m <<= 1) {
+    const unsigned long long y = shfl_xor_u64(kth, m);
+    kth = y < kth ? y : kth;
+  }
+  return key_to_float((uint32_t)(kth >> 32)) - p.bound_margin;
+}
+
 // G: query heads per KV head in the row layout (4, 8 or 16); a group of p.g < G heads is padded
 // to G (the rows of heads p.g .. G-1 hold no query and never score).  NE: block-list entries per
 // lane (n_blocks <= 16 NE).
@@ -219,7 +296,8 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
   __shared__ unsigned long long blist[BLOCK ? NW * QW : 1][BLOCK ? 16 * NE : 1];
   __shared__ int sortbuf[BLOCK ? 1 : NW][BLOCK ? 1 : kSortCap];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar
   const int rn = lane & 15, jg = lane >> 4;
   // Row packing, head-quarter major: the wave's 64 rows are 4 MFMA blocks; block rb holds heads
   // 4hq..4hq+3 of the 4 queries of query group qg (rb = qg * HQ + hq), MFMA row 4j+e being
@@ -239,6 +317,11 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
   const int tq0 = (int)p.q_off + j0;  // positions fit in 31 bits
   const int t_max = tq0 + nq - 1;
   const int wq0 = wave * QW;  // first workgroup query of this wave
+  if (p.redo_only) {  // second pass: only workgroups holding a flagged row (uniform decision)
+    bool any = false;
+    for (int jq = 0; jq < nq; jq++) any |= p.redo_only[((size_t)b * p.Tq + j0 + jq) * HV + uv] != 0;
+    if (!any) return;
+  }
 
   constexpr int KK = C::KK;
   bf16x8 qa[4][F32 ? 1 : KK];
@@ -268,7 +351,6 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
       }
     }
   };
-  load_q();
   float delta[4][4];
 #pragma unroll
   for (int rb = 0; rb < 4; rb++) {
@@ -351,6 +433,45 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
     return p.tbuf + ((size_t)((size_t)b * p.Tq + j0 + wq0 + wq) * HV + uv) * kBufCap;
   };
 
+  // Token mode with the full-attention pass's tile maxima: every query starts at a lower bound
+  // of its k-th score.  The group score's maximum over a tile is the maximum over the heads of
+  // the head's tile maximum normalized with its LSE, i.e. the score of one of the tile's keys;
+  // over n >= k tiles lying entirely at or before t - w (no forced-window key) the k-th largest
+  // of these maxima belongs to k distinct candidates, so at least k candidate scores reach it.
+  // The stored maxima are rounded down, bound_margin covers the two passes' different
+  // accumulation orders, and the count check at the end catches a bound that is still too high.
+  bool bounded[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; qg++) bounded[qg] = false;
+  if constexpr (!BLOCK) {
+    if (p.tile_max && p.k_global > 0) {
+#pragma unroll
+      for (int qg = 0; qg < QG; qg++) {
+        float bnd[4];  // the bounds of the query group's four queries (uniform)
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          bnd[jj] = -INFINITY;
+          const int jq = wq0 + 4 * qg + jj;
+          if (jq >= nq) continue;  // the same for the whole wave
+          const int t = tq0 + jq;
+          const int n_ct = max(t - p.window + 1, 0) / 64;  // tiles before the window
+          // the last at most 64 kNPL of them, from a multiple of 8 (16-byte loads)
+          const int r0 = ((max(n_ct - 64 * kNPL, 0) + 7) / 8) * 8;
+          const int nt = n_ct - r0;
+          if (nt < p.k_global) continue;
+          bnd[jj] = tile_bound(p, b, j0 + jq, u, hbase, gc, r0, nt, lane, whist[wave]);
+        }
+        const float bound = jg == 0 ? bnd[0] : jg == 1 ? bnd[1] : jg == 2 ? bnd[2] : bnd[3];
+        if (bound > -INFINITY) {
+          thf[qg] = bound;
+          th[qg] = (unsigned long long)float_key(bound) << 32;
+          bounded[qg] = true;
+        }
+      }
+    }
+  }
+  load_q();
+
   if (n_tiles > 0) {
     load_tile(0);
     store_tile(0);
@@ -381,9 +502,11 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
                                                            kCompactSlack, &kept);
               if (jg == jj) {
                 cnt[qg] = kept;
-                th[qg] = tnew;
-                const uint32_t hi = (uint32_t)(tnew >> 32);
-                thf[qg] = hi ? key_to_float(hi) : -INFINITY;
+                if (tnew > th[qg]) {  // a bin's lower edge can lie below a starting bound
+                  th[qg] = tnew;
+                  const uint32_t hi = (uint32_t)(tnew >> 32);
+                  thf[qg] = hi ? key_to_float(hi) : -INFINITY;
+                }
               }
             }
           }
@@ -394,6 +517,10 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
     }
     if (t + 1 < n_tiles) load_tile(t + 1);
 
+    // token mode: each block's scores and filter ballots; the appends run after the tile's
+    // matrix work, so the four blocks' instructions schedule without branches between them
+    float vk[4][BLOCK ? 1 : QG];
+    unsigned long long tk[4][BLOCK ? 1 : QG];
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
       f32x4 acc[4];
@@ -428,25 +555,9 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
           for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[rb][e], p.scale_log2, -delta[rb][e]));
         }
         if constexpr (!BLOCK) {
-          bool take = false;
-          if (q_ok[qg] && pos <= t_q[qg] - p.window && v >= thf[qg]) {
-            if (v > thf[qg]) {
-              take = true;
-            } else {  // equal to the float filter: decide on the exact 64-bit value
-              const unsigned long long V = ((unsigned long long)float_key(v) << 32) |
-                                           (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
-              take = V >= th[qg];
-            }
-          }
-          const unsigned long long bm = __ballot(take);
-          if (bm) {
-            if (take) {
-              const int slot = cnt[qg] + __popcll(bm & qmask & below);
-              buf_of(4 * qg + jg)[slot] = ((unsigned long long)float_key(v) << 32) |
-                                          (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
-            }
-            cnt[qg] += __popcll(bm & qmask);
-          }
+          // candidates at or above the float filter; appended after the tile's four blocks
+          vk[kb][qg] = v;
+          tk[kb][qg] = __ballot(q_ok[qg] && pos <= t_q[qg] - p.window && v >= thf[qg]);
         } else {
           // running maximum of the current block (keys past the query are masked)
           bmax[qg] = fmaxf(bmax[qg], (q_ok[qg] && pos <= t_q[qg]) ? v : -INFINITY);
@@ -466,6 +577,32 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
                 if (L[qg][e] == gmn) L[qg][e] = V;
             }
             bmax[qg] = -INFINITY;
+          }
+        }
+      }
+    }
+    if constexpr (!BLOCK) {
+      unsigned long long any = 0ull;
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int qg = 0; qg < QG; qg++) any |= tk[kb][qg];
+      if (any) {
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+          const int pos = key0 + 16 * kb + rn;
+#pragma unroll
+          for (int qg = 0; qg < QG; qg++) {
+            if (!tk[kb][qg]) continue;
+            const float v = vk[kb][qg];
+            const unsigned long long V = ((unsigned long long)float_key(v) << 32) |
+                                         (unsigned long long)(0xFFFFFFFFu - (uint32_t)pos);
+            bool take = (tk[kb][qg] >> lane) & 1ull;
+            // equal to the float filter: decide on the exact 64-bit value
+            if (take && v == thf[qg]) take = V >= th[qg];
+            const unsigned long long bm = __ballot(take);
+            if (take) buf_of(4 * qg + jg)[cnt[qg] + __popcll(bm & qmask & below)] = V;
+            cnt[qg] += __popcll(bm & qmask);
           }
         }
       }
@@ -498,7 +635,12 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
         unsigned long long* bufq = buf_of(wq);
         int* sb = sortbuf[wave];
         const int n = __shfl(cnt[qg], 16 * jj, 64);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // appends complete before reloads
+        if (p.redo) {  // a bound above the k-th score leaves fewer than k candidates: flag it
+          const bool redo = __shfl(bounded[qg] ? 1 : 0, 16 * jj, 64) != 0 && n < k_eff;
+          if (lane == 0) p.redo[row] = redo ? 1 : 0;
+          if (redo) continue;  // the second pass writes this row
+        }
+        stores_done();  // the last tile's appends are complete before the reloads
         if (p.chunks > 1) {  // keep the chunk's best k_eff values for the merge
           int kept = n;
           if (n > k_eff) wave_compact(bufq, n, k_eff, lane, whist[wave], nullptr, 0, &kept);
@@ -759,11 +901,24 @@ void launch_dfb(const PrefillSelectParams& p, hipStream_t stream) {
 int prefill_select_buffer_cap() { return kBufCap; }
 int prefill_select_max_k() { return kSortCap; }
 
+// Finite float test on the bit pattern (the build assumes no NaN operands in comparisons).
+static bool finite_host(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  return (u & 0x7F800000u) != 0x7F800000u;
+}
+
 hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, bool in_f32,
                                  bool block_mode, hipStream_t stream) {
   if (p.g < 1 || p.g > 64 || p.chunks != (p.g + 15) / 16) return hipErrorInvalidValue;
   if (p.chunks > 4 || (p.chunks > 1 && (!p.ccnt || (block_mode && !p.cvals)))) return hipErrorInvalidValue;
   if (!block_mode && p.k_global > kSortCap) return hipErrorInvalidValue;
+  // the tile-maximum bound and the second pass: token mode of whole groups (at most 16 heads)
+  if ((p.tile_max || p.redo || p.redo_only) && (block_mode || p.chunks > 1)) return hipErrorInvalidValue;
+  if (p.tile_max && (!p.redo || p.tmax_stride % 16 ||
+                     !finite_host(p.bound_margin) ||
+                     p.tmax_stride < (p.Tk + kBN - 1) / kBN))
+    return hipErrorInvalidValue;
   if (block_mode && (p.block < 16 || p.block > 64 || (p.block & (p.block - 1)) ||
                      p.n_blocks < 1 || p.n_blocks > kMaxBlocks))
     return hipErrorInvalidValue;

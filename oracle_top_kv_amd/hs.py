@@ -18,12 +18,12 @@ HS_BF16, HS_F32 = 0, 1
 HS_IDX_TOKEN, HS_IDX_BLOCK = 0, 1
 HS_OP_FULL_ATTN, HS_OP_ORACLE_TOPK, HS_OP_BLOCK_TOPK, HS_OP_SPARSE_ATTN = 0, 1, 2, 3
 HS_OP_FULL_ATTN_LOGITS, HS_OP_TOPK_FROM_LOGITS, HS_OP_BLOCK_TOPK_FROM_LOGITS = 4, 5, 6
-HS_OP_FULL_ATTN_BLOCK_TOPK, HS_OP_FULL_ATTN_PAGED = 7, 8
+HS_OP_FULL_ATTN_BLOCK_TOPK, HS_OP_FULL_ATTN_PAGED, HS_OP_FULL_ATTN_TOPK = 7, 8, 9
 
 EXPORTS = ["hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk", "hs_sparse_attn_gather",
            "hs_full_attn_fwd_logits", "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
            "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex", "hs_full_attn_fwd_paged",
-           "hs_sparse_attn_gather_paged", "hs_sparse_attn_gather_noalloc",
+           "hs_sparse_attn_gather_paged", "hs_sparse_attn_gather_noalloc", "hs_full_attn_topk",
            "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
 
 
@@ -78,6 +78,8 @@ def lib():
         L.hs_block_topk_from_logits.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.hs_full_attn_block_topk.argtypes = [pd, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz,
                                               vp]
+        L.hs_full_attn_topk.argtypes = [pd, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp, vp,
+                                        vp, sz, vp]
         L.hs_sparse_attn_gather_ex.argtypes = [pd, vp, vp, vp, ctypes.c_int, vp, vp, i32, i32,
                                                ctypes.POINTER(SwaBranch),
                                                ctypes.POINTER(SparseOpts), vp, vp, vp, sz, vp]
@@ -99,7 +101,7 @@ def lib():
                   "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
                   "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex",
                   "hs_full_attn_fwd_paged", "hs_sparse_attn_gather_paged",
-                  "hs_sparse_attn_gather_noalloc"):
+                  "hs_sparse_attn_gather_noalloc", "hs_full_attn_topk"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -231,6 +233,29 @@ def full_attn_block_topk(q, k, v, block, n_blocks, q_offset=None, out_dtype=None
                                          int(block), int(n_blocks), _ptr(o), _ptr(lse), _ptr(idx),
                                          _ptr(cnt), _ptr(ws), n, _stream(dev)),
            "hs_full_attn_block_topk")
+    return o, lse, idx, cnt
+
+
+def full_attn_topk(q, k, v, k_global, window, q_offset=None, out_dtype=None, scale=None,
+                   bound_margin=1.0 / 64):
+    """Full attention and the forced window plus top-k_global tokens in one call (prefill: the
+    selection starts at the tile-maximum bound).  Returns (o, lse, idx int32 [B,Tq,Hkv,k+w],
+    count), equal to full_attn_fwd followed by oracle_topk."""
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dev, dtype=q.dtype)
+    desc = make_desc(q, k, q_offset, out_dtype, scale)
+    B, Tq, Hq = q.shape[0], q.shape[1], q.shape[2]
+    Hkv = k.shape[2]
+    o = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Tq, Hkv, k_global + window), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
+    ws, n = workspace(HS_OP_FULL_ATTN_TOPK, desc, k_global, window, device=dev)
+    _check(lib().hs_full_attn_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), int(k_global),
+                                   int(window), float(bound_margin), _ptr(o), _ptr(lse),
+                                   _ptr(idx), _ptr(cnt), _ptr(ws), n, _stream(dev)),
+           "hs_full_attn_topk")
     return o, lse, idx, cnt
 
 

@@ -118,6 +118,33 @@ def test_topk_argument_checks():
                                          FAKE, needb - 1, None) == hs.HS_ERR_WORKSPACE, kw
 
 
+def test_full_attn_topk_argument_checks():
+    """The one-call full attention + token selection: bad k / window / margin and NULL pointers
+    are refused; prefill shapes of whole groups need the tile maxima and row flags beyond the
+    separate selection's buffers; a workspace one byte short is refused before any launch."""
+    L = hs.lib()
+    f = L.hs_full_attn_topk
+    d = desc(q_len=512, kv_len=8192)  # g = 4: the tiled prefill kernel and selection
+    for kg, w, m in ((-1, 128, 0.0), (0, 0, 0.0), (16, 16, float("nan")), (16, 16, float("inf"))):
+        assert f(ctypes.byref(d), FAKE, FAKE, FAKE, kg, w, m, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 1 << 40, None) == hs.HS_ERR_INVALID_ARG, (kg, w, m)
+    assert f(ctypes.byref(d), FAKE, FAKE, None, 16, 16, 0.0, FAKE, FAKE, FAKE, FAKE, FAKE,
+             1 << 40, None) == hs.HS_ERR_INVALID_ARG
+    need = L.hs_workspace_size(hs.HS_OP_FULL_ATTN_TOPK, ctypes.byref(d), 1024, 128)
+    sel = L.hs_workspace_size(hs.HS_OP_ORACLE_TOPK, ctypes.byref(d), 1024, 128)
+    tiles = (8192 + 63) // 64
+    assert need >= sel + 1 * 8 * 512 * ((tiles + 15) // 16 * 16) * 2 + 512 * 2 * 4, (need, sel)
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 1024, 128, 0.0, FAKE, FAKE, FAKE, FAKE, FAKE,
+             need - 1, None) == hs.HS_ERR_WORKSPACE
+    # decode rows: the two calls, whose larger workspace is the size
+    dd = desc(batch=2, kv_len=5000, n_q_heads=32, n_kv_heads=8)
+    need_d = L.hs_workspace_size(hs.HS_OP_FULL_ATTN_TOPK, ctypes.byref(dd), 64, 32)
+    assert need_d == max(L.hs_workspace_size(hs.HS_OP_FULL_ATTN, ctypes.byref(dd), 0, 0),
+                         L.hs_workspace_size(hs.HS_OP_ORACLE_TOPK, ctypes.byref(dd), 64, 32))
+    assert f(ctypes.byref(dd), FAKE, FAKE, FAKE, 64, 32, 0.0, FAKE, FAKE, FAKE, FAKE, FAKE,
+             need_d - 1, None) == hs.HS_ERR_WORKSPACE
+
+
 def test_block_topk_argument_checks():
     L = hs.lib()
     d = desc()  # g = 4
