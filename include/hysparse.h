@@ -206,10 +206,11 @@ hs_status hs_full_attn_block_topk(const hs_attn_desc* desc, const void* q, const
 
 /* Full attention and token-level oracle index in one call: the outputs of hs_full_attn_fwd
  * (o, lse) and of hs_oracle_topk (idx, count) for the same inputs, the same bit for bit.  For
- * prefill-shaped bf16 calls of whole groups (q_len * g > 16, g <= 16, head_dim 64 or 128, the
- * tiled prefill kernel) the attention pass also records every (query, head) row's largest logit
- * in each 64-key tile, and the selection pass starts every (b, t, u) at the k-th largest tile
- * score over the tiles lying before the window.  A tile's score is the largest score of its
+ * prefill-shaped bf16 calls with head_dim up to 128 (those on the tiled prefill attention kernel
+ * and the streamed prefill selection) the attention pass also records every (query, head) row's
+ * largest logit in each 64-key tile, and the selection pass starts every (b, t, u) (for groups of
+ * more than 16 heads every chunk of 16 heads) at the k-th largest tile score over the tiles
+ * lying before the window.  A tile's score is the largest score of its
  * keys [P2 "Extracting block scores from exact attention": block score = maximum over the
  * block's tokens], so these are the scores of k distinct candidates and the k-th candidate score
  * is at least as large: only keys at or above the bound enter the candidate lists, and ranking

@@ -730,19 +730,20 @@ size_t token_select_ws(const Shape& s, int k_global) {
 }
 
 // Token selection started at the tile-maximum bound: the tiled prefill attention kernel (head
-// sizes up to 128) and the prefill selection of whole groups.
+// sizes up to 128) and the streamed prefill selection (whole groups, or chunks of 16 heads).
 bool fused_tokens(const Shape& s, int k_global) {
-  return use_prefill_kernel(s) && s.D <= 128 && s.g <= 16 && k_global >= 1 &&
+  return use_prefill_kernel(s) && s.D <= 128 && k_global >= 1 &&
          token_route(s, k_global) == SEL_PREFILL;
 }
 int tmax_stride(const Shape& s) {
-  const long long tiles = (s.Tk + 63) / 64;
+  const long long bn = hs::prefill_tile_keys(s.D);
+  const long long tiles = (s.Tk + bn - 1) / bn;
   return (int)((tiles + 15) / 16 * 16);
 }
 size_t tmax_bytes(const Shape& s) {
   return align_up((size_t)s.B * s.Hq * s.Tq * (size_t)tmax_stride(s) * 2, 256);
 }
-size_t redo_bytes(const Shape& s) { return align_up((size_t)s.B * s.Tq * s.Hkv * 4, 256); }
+size_t redo_bytes(const Shape& s) { return align_up(select_chunk_rows(s) * 4, 256); }
 
 // Workspace of hs_full_attn_topk: tile maxima, candidate buffers and row flags when fused,
 // else what the larger of its two passes needs.
@@ -927,8 +928,11 @@ hs_status hs_full_attn_topk(const hs_attn_desc* desc, const void* q, const void*
   p.cnt = count;
   p.tile_max = tmax;
   p.tmax_stride = pp.tmax_stride;
+  p.tmax_tile = hs::prefill_tile_keys(s.D);
   p.bound_margin = bound_margin;
   p.redo = redo;
+  if (p.chunks > 1)
+    p.ccnt = (int32_t*)((char*)tbuf + align_up(select_chunk_rows(s) * hs::prefill_select_buffer_cap() * 8, 256));
   e = hs::launch_prefill_select(p, s.D, false, false, hst);
   if (e != hipSuccess) return hip_status(e, "token selection kernel from the tile-maximum bound");
   // rows whose bound was above their k-th score, selected again without it

@@ -177,7 +177,7 @@ template <int D, bool BSEL, bool TMAX = false>
 __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillParams p) {
   using C = PfCfg<D>;
   static_assert(!BSEL || C::NW == 8, "the block-selection merge assumes 8 waves");
-  static_assert(!TMAX || (!BSEL && C::BN == 64), "tile maxima: 64-key tiles, no block selection");
+  static_assert(!TMAX || !BSEL, "tile maxima: not with the block selection");
 
   // K/V tiles; BSEL reuses the same LDS for its merge after the last tile
   constexpr int BN = C::BN, KB = C::KB;
@@ -512,6 +512,8 @@ __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillPa
 
 }  // namespace
 
+int prefill_tile_keys(int head_dim) { return head_dim == 256 ? PfCfg<256>::BN : PfCfg<128>::BN; }
+
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t stream) {
   const int rows_wg = head_dim == 256 ? PfCfg<256>::RowsWG : PfCfg<128>::RowsWG;
   if (rows_wg % p.g) return hipErrorInvalidValue;
@@ -521,7 +523,9 @@ hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t
   const bool bsel = p.blk_idx != nullptr;
   if (bsel && (p.n_blocks < 1 || p.n_blocks > 16 || 32 % p.g || head_dim > 128))
     return hipErrorInvalidValue;
-  if (p.tile_max) {  // tile maxima: head sizes 64 and 128, not with the block selection
+  // tile maxima: head sizes up to 128 (at 256 the kernel has no registers to spare: the maxima
+  // cost a fifth of its time), not with the block selection
+  if (p.tile_max) {
     if (bsel || head_dim > 128 || p.tmax_stride % 16 || p.tmax_stride < (p.Tk + kBN - 1) / kBN)
       return hipErrorInvalidValue;
     if (head_dim == 128) pf_attn_kernel<128, false, true><<<grid, kThreads, 0, stream>>>(p);

@@ -114,11 +114,13 @@ struct PrefillParams {
   int32_t* blk_idx;  // [B, Tq, Hkv, n_blocks]
   int32_t* blk_cnt;  // [B, Tq, Hkv]
   int n_blocks;
-  // or null: every row's raw logit maximum over each 64-key tile, as bf16 bits rounded toward
-  // -inf, [B, Hq, Tq, tmax_stride] (tmax_stride a multiple of 16 and >= the tiles of the row)
+  // or null: every row's raw logit maximum over each key tile (prefill_tile_keys(head_dim)
+  // keys), as bf16 bits rounded toward -inf, [B, Hq, Tq, tmax_stride] (tmax_stride a multiple of
+  // 16 and >= the tiles of the row)
   uint16_t* tile_max;
   int tmax_stride;
 };
+int prefill_tile_keys(int head_dim);
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int head_dim, hipStream_t stream);
 
@@ -207,7 +209,7 @@ struct PrefillSelectParams {
   // from which every row starts at a proven lower bound of its k-th score minus bound_margin;
   // redo[row] (written for every chunk row) then flags the rows whose bound turned out too high
   const uint16_t* tile_max;
-  int tmax_stride;
+  int tmax_stride, tmax_tile;  // tile maxima per row, keys per tile
   float bound_margin;
   int32_t* redo;
   // or null: only workgroups holding a row flagged here run (the rows' second pass)

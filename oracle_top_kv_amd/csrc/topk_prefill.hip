@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
           const int jq = wq0 + 4 * qg + jj;
           if (jq >= nq) continue;  // the same for the whole wave
           const int t = tq0 + jq;
-          const int n_ct = max(t - p.window + 1, 0) / 64;  // tiles before the window
+          const int n_ct = max(t - p.window + 1, 0) / p.tmax_tile;  // tiles before the window
           // the last at most 64 kNPL of them, from a multiple of 8 (16-byte loads)
           const int r0 = ((max(n_ct - 64 * kNPL, 0) + 7) / 8) * 8;
           const int nt = n_ct - r0;
@@ -637,7 +637,10 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
         const int n = __shfl(cnt[qg], 16 * jj, 64);
         if (p.redo) {  // a bound above the k-th score leaves fewer than k candidates: flag it
           const bool redo = __shfl(bounded[qg] ? 1 : 0, 16 * jj, 64) != 0 && n < k_eff;
-          if (lane == 0) p.redo[row] = redo ? 1 : 0;
+          if (lane == 0) {
+            p.redo[row] = redo ? 1 : 0;
+            if (redo && p.chunks > 1) p.ccnt[row] = 0;  // the merge reads nothing of it
+          }
           if (redo) continue;  // the second pass writes this row
         }
         stores_done();  // the last tile's appends are complete before the reloads
@@ -738,6 +741,11 @@ __global__ __launch_bounds__(kThreads) void pf_merge_tokens_kernel(PrefillSelect
   const int n_cand = max(t - p.window + 1, 0);
   const int k_eff = min(n_cand, p.k_global);
   const int HV = p.Hkv * p.chunks;
+  if (p.redo_only) {  // second pass: only rows with a chunk row selected again
+    bool any = false;
+    for (int c = 0; c < p.chunks; c++) any |= p.redo_only[((size_t)b * p.Tq + j) * HV + u * p.chunks + c] != 0;
+    if (!any) return;
+  }
   // gather the chunk lists; key (position << 32 | ~score bits): a position's largest value first
   if (threadIdx.x == 0) n_sh = 0;
   __syncthreads();
@@ -913,11 +921,11 @@ hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, boo
   if (p.g < 1 || p.g > 64 || p.chunks != (p.g + 15) / 16) return hipErrorInvalidValue;
   if (p.chunks > 4 || (p.chunks > 1 && (!p.ccnt || (block_mode && !p.cvals)))) return hipErrorInvalidValue;
   if (!block_mode && p.k_global > kSortCap) return hipErrorInvalidValue;
-  // the tile-maximum bound and the second pass: token mode of whole groups (at most 16 heads)
-  if ((p.tile_max || p.redo || p.redo_only) && (block_mode || p.chunks > 1)) return hipErrorInvalidValue;
-  if (p.tile_max && (!p.redo || p.tmax_stride % 16 ||
+  // the tile-maximum bound and the second pass: token mode
+  if ((p.tile_max || p.redo || p.redo_only) && block_mode) return hipErrorInvalidValue;
+  if (p.tile_max && (!p.redo || p.tmax_stride % 16 || p.tmax_tile < 16 ||
                      !finite_host(p.bound_margin) ||
-                     p.tmax_stride < (p.Tk + kBN - 1) / kBN))
+                     p.tmax_stride < (p.Tk + p.tmax_tile - 1) / p.tmax_tile))
     return hipErrorInvalidValue;
   if (block_mode && (p.block < 16 || p.block > 64 || (p.block & (p.block - 1)) ||
                      p.n_blocks < 1 || p.n_blocks > kMaxBlocks))

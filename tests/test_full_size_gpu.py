@@ -141,6 +141,15 @@ def test_prefill_80b_128k_sampled_rows():
                           wl.k_global, wl.window, wl.q_offset, rows=rows)
     say(f"  token sets: near-tie differences excused {ex}")
 
+    # the same two stages in one call (selection started at the tile-maximum bound): O, LSE and
+    # every row's index set identical to the two calls'
+    o1, lse1, idx1, cnt1 = hs().full_attn_topk(q, k, v, wl.k_global, wl.window,
+                                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o) and torch.equal(lse1, lse)
+    assert torch.equal(cnt1, cnt) and torch.equal(idx1, idx)
+    del o1, lse1, idx1, cnt1
+
     # sparse layers: the sampled rows carry the oracle's sets in the GPU's index input
     idx_in, cnt_in = idx.clone(), cnt.clone()
     r = torch.tensor(rows, device="cuda")

@@ -1,8 +1,8 @@
 """GPU parity of hs_full_attn_topk: full attention and the token-level oracle index in one call.
-On prefill shapes of whole groups the attention pass records every row's per-tile logit maximum
-and the selection starts each (b, t, u) at the k-th largest tile score before the window (a
-lower bound of its k-th candidate score); elsewhere the call is full attention followed by the
-separate selection.
+On prefill shapes the attention pass records every row's per-tile logit maximum and the
+selection starts each (b, t, u), or each chunk of 16 heads of a larger group, at the k-th
+largest tile score before the window (a lower bound of its k-th candidate score); elsewhere the
+call is full attention followed by the separate selection.
 
 O and LSE must equal hs_full_attn_fwd's bit for bit; index sets must equal the separate
 hs_oracle_topk's exactly (the bound only decides which keys enter the candidate lists, never
@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from oracle_top_kv_amd.inputs import Workload, make_inputs, to_numpy_f32
-from parity_utils import LSE_TOL, TOL_BF16, check_token_sets, max_abs
+from parity_utils import LSE_TOL, TOL_BF16, TOL_F32, check_token_sets, max_abs
 
 pytestmark = pytest.mark.gpu
 
@@ -52,10 +52,19 @@ CASES = [
     # k of the 80B workload: 1024 candidates of a 70k context (1090 tiles before the window)
     ("g16_k1024", Workload("tk", 1, 32, 70000, 16, 1, 128, "bf16", k_global=1024, window=128,
                            seed=708)),
-    # not the fused route: decode rows, and fp32 inputs
+    # groups of more than 16 heads: a bound per chunk of 16 heads, chunk lists merged
+    ("g32_chunks", Workload("tg", 1, 64, 4000, 64, 2, 128, "bf16", k_global=16, window=16,
+                            seed=712)),
+    ("mqa64_d128", Workload("tq", 1, 32, 5000, 64, 1, 128, "bf16", k_global=24, window=32,
+                            seed=713)),
+    # not the fused route: decode rows, fp32 inputs, a group the tiled kernel does not divide,
+    # HySparse2's head shape (64 query heads on one KV head) at d 256
+    ("mqa64_d256", Workload("tq2", 1, 32, 5000, 64, 1, 256, "bf16", k_global=24, window=32,
+                            seed=716)),
     ("decode_g4", Workload("td", 2, 1, 5000, 32, 8, 128, "bf16", k_global=64, window=32,
                            seed=709)),
     ("f32_g4", Workload("tf", 1, 200, 1500, 8, 2, 64, "f32", k_global=16, window=16, seed=710)),
+    ("g24", Workload("t24", 1, 40, 3000, 48, 2, 128, "bf16", k_global=16, window=16, seed=714)),
 ]
 
 
@@ -74,7 +83,8 @@ def run_case(wl, margin=1.0 / 64, oracle_rows=None):
     qn, kn = to_numpy_f32(x["q"]), to_numpy_f32(x["k"])
     o_ref, lse_ref = oracle.full_attention(qn, kn, to_numpy_f32(x["v"]), rows=oracle_rows)
     rows = list(range(wl.q_len)) if oracle_rows is None else list(oracle_rows)
-    assert max_abs(o.cpu().numpy()[:, rows], o_ref[:, rows]) <= TOL_BF16
+    tol = TOL_F32 if wl.dtype == "f32" else TOL_BF16
+    assert max_abs(o.cpu().numpy()[:, rows], o_ref[:, rows]) <= tol
     assert max_abs(lse.cpu().numpy()[:, :, rows], lse_ref[:, :, rows]) <= LSE_TOL
     return qn, kn, lse_ref, idx.cpu().numpy(), cnt.cpu().numpy()
 
@@ -90,10 +100,16 @@ def test_full_attn_topk_matches_separate_calls_and_oracle(name, wl):
     say(f"  near-tie differences excused: {excused}")
 
 
+MARGIN_SHAPES = [Workload("tm", 1, 96, 4000, 16, 2, 128, "bf16", k_global=24, window=16, seed=711),
+                 Workload("tm64", 1, 32, 5000, 64, 1, 128, "bf16", k_global=24, window=32,
+                          seed=715)]
+
+
 @pytest.mark.parametrize("margin", [-64.0, 8.0, 0.0])
-def test_bound_margin_never_changes_the_sets(margin):
-    """A bound pushed far above every k-th score (negative margin: each bounded row collects fewer
-    than k candidates and takes the second pass), a weak one, and none: the same sets."""
-    wl = Workload("tm", 1, 96, 4000, 16, 2, 128, "bf16", k_global=24, window=16, seed=711)
+@pytest.mark.parametrize("wl", MARGIN_SHAPES, ids=["g16", "mqa64_chunks"])
+def test_bound_margin_never_changes_the_sets(margin, wl):
+    """A bound pushed far above every k-th score (negative margin: each bounded row, or chunk
+    row, collects fewer than k candidates and takes the second pass, and the chunk merge runs
+    again for it), a weak one, and none: the same sets."""
     say(f"[bound margin {margin}] {wl}")
-    run_case(wl, margin=margin, oracle_rows=[0, 47, 95])
+    run_case(wl, margin=margin, oracle_rows=[0, wl.q_len // 2, wl.q_len - 1])
