@@ -4,7 +4,7 @@
 // p = softmax, o = sum p v; P1 section 4.2 and P5 model configuration for the head shape].
 //
 // One workgroup per (batch entry, KV head, query, key split) with one wave per 16-head chunk of
-// the group.  Every 64-key step of K and V is loaded once by the whole workgroup into LDS
+// the group (two over a contiguous key range at d 256, each taking half of every step's keys).  Every 64-key step of K and V is loaded once by the whole workgroup into LDS
 // (double-buffered, through buffer loads whose descriptors hold the step's first row and its
 // number of rows) and read there by every chunk: K and V cross HBM and L2 once, however many
 // heads share them.  Per wave the arithmetic is the row kernel's:
@@ -50,18 +50,33 @@ __device__ __forceinline__ void lds_barrier() {
 
 constexpr int kMaxSplitEntries = 2048;  // list entries staged per workgroup (32 steps)
 
+// Waves per 16-head chunk: over a contiguous key range at d 256, each chunk of a group of 32 or
+// 64 heads has two waves, one per 32-key half of every step (two waves per SIMD at 64 heads, so
+// that one covers the other's LDS and MFMA latencies; registers allow no more, and with 48 heads
+// six waves would spill); the halves are merged at the end.  Index lists keep one wave per
+// chunk: their splits are one or two steps long, too short to repay the merge.
+template <int D, int NW, int SRC>
+constexpr int key_halves() {
+  return D == 256 && NW % 2 == 0 && SRC == SRC_RANGE ? 2 : 1;
+}
+
 template <int D, int NW, int SRC, bool LOGITS>
-__global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p) {
+__global__ __launch_bounds__((64 * NW * key_halves<D, NW, SRC>()), 1) void group_attn_kernel(RowAttnParams p) {
   using C = GaCfg<D>;
   static_assert(!LOGITS || SRC == SRC_RANGE, "logits come from the full-attention pass only");
   constexpr bool kList = SRC == SRC_TOKEN || SRC == SRC_BLOCK;
-  constexpr int kThreads = 64 * NW;
+  constexpr int KH = key_halves<D, NW, SRC>();
+  constexpr int kKeys = kGStep / KH;  // keys of a step per wave
+  constexpr int kKB = kKeys / 16;     // 16-key blocks per wave and step
+  constexpr int kThreads = 64 * NW * KH;
   constexpr int kPer = (C::kChunks + kThreads - 1) / kThreads;  // chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][kGStep * C::KStr];
   __shared__ __attribute__((aligned(16))) uint16_t vt[2][kGStep * C::VStr];
   __shared__ int pos_all[kList ? kMaxSplitEntries : 1];
 
-  const int lane = threadIdx.x & 63, hc = threadIdx.x >> 6;  // wave = head chunk
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hc = wave % NW, kh = wave / NW;  // head chunk, key half
   const int rn = lane & 15, jg = lane >> 4;
   // KV head fastest, then split, then (batch, query)
   const int x = blockIdx.x;
@@ -185,21 +200,22 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
   float* lrow = LOGITS ? p.logits + (((size_t)b * p.Tq + j) * p.Hq + h) * (size_t)p.Tk : nullptr;
 
   auto compute = [&](int s, int buf) {
-    // S^T for the four 16-key blocks
-    f32x4 sacc[4];
+    // S^T for this wave's 16-key blocks (keys kKeys * kh .. of the step)
+    const int kw = kKeys * kh;
+    f32x4 sacc[kKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < kKB; kb++) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < C::KK; kk++)
 #pragma unroll
-      for (int kb = 0; kb < 4; kb++) {
-        const bf16x8 ka = *(const bf16x8*)&kt[buf][(16 * kb + rn) * C::KStr + 32 * kk + 8 * jg];
+      for (int kb = 0; kb < kKB; kb++) {
+        const bf16x8 ka = *(const bf16x8*)&kt[buf][(kw + 16 * kb + rn) * C::KStr + 32 * kk + 8 * jg];
         sacc[kb] = mfma_bf16(ka, qb[kk], sacc[kb]);
       }
-    const int key0 = s * kGStep;
+    const int key0 = s * kGStep + kw;
     if (LOGITS && row_ok) {
 #pragma unroll
-      for (int kb = 0; kb < 4; kb++) {
+      for (int kb = 0; kb < kKB; kb++) {
         const int e0 = key0 + 16 * kb + 4 * jg;
         if (p.logits_vec) {
           if (e0 < p.Tk) *(f32x4*)(lrow + e0) = sacc[kb];
@@ -210,14 +226,15 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
         }
       }
     }
-    float sv[4][4];
+    float sv[kKB][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++)
+    for (int kb = 0; kb < kKB; kb++)
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const int ke = 16 * kb + 4 * jg + e;  // entry of the step
-        const bool ok = kList ? pos_all[(s - s0) * kGStep + ke] >= 0 : (long long)key0 + ke <= t_row;
+        const int ke = kw + 16 * kb + 4 * jg + e;  // entry of the step
+        const bool ok = kList ? pos_all[(s - s0) * kGStep + ke] >= 0
+                              : (long long)s * kGStep + ke <= t_row;
         const float v = ok ? sacc[kb][e] * p.scale_log2 : -INFINITY;
         sv[kb][e] = v;
         mx = fmaxf(mx, v);
@@ -227,9 +244,9 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     float psum = 0.f;
-    bf16x8 pb[2];
+    bf16x8 pb[kKB / 2];
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
+    for (int half = 0; half < kKB / 2; half++) {
       float p8[8];
 #pragma unroll
       for (int k2 = 0; k2 < 2; k2++)
@@ -249,10 +266,11 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
     for (int db = 0; db < C::DB; db++) oacc[db] *= alpha;
     // O^T += V^T P^T, one MFMA per 32 keys (key blocks 2half, 2half + 1) and 16 columns
 #pragma unroll
-    for (int half = 0; half < 2; half++)
+    for (int half = 0; half < kKB / 2; half++)
 #pragma unroll
       for (int db = 0; db < C::DB; db++) {
-        const uint16_t* a0 = &vt[buf][(32 * half + 4 * jg + (rn >> 2)) * C::VStr + 16 * db + 4 * (rn & 3)];
+        const uint16_t* a0 =
+            &vt[buf][(kw + 32 * half + 4 * jg + (rn >> 2)) * C::VStr + 16 * db + 4 * (rn & 3)];
         const bf16x8 vop = join_tr(lds_read_tr16(a0), lds_read_tr16(a0 + 16 * C::VStr));
         oacc[db] = mfma_bf16(vop, pb[half], oacc[db]);
       }
@@ -294,6 +312,36 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
   double ld = (double)l_s - (double)l_c;
   ld += __shfl_xor(ld, 16, 64);
   ld += __shfl_xor(ld, 32, 64);
+  if constexpr (KH == 2) {
+    // the second key half's maximum, row sum and O^T go through the (now free) V tiles, lane by
+    // lane in the accumulator layout, to the first half's wave of the same head chunk
+    static_assert(NW * (C::DB + 1) * 64 * 16 <= (int)sizeof(vt), "merge buffer");
+    f32x4* xo = (f32x4*)&vt[0][0] + hc * (C::DB + 1) * 64;
+    lds_barrier();  // every wave is done with the tiles
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < C::DB; db++) xo[db * 64 + lane] = oacc[db];
+      const unsigned long long lb = (unsigned long long)__double_as_longlong(ld);
+      xo[C::DB * 64 + lane] = f32x4{m_run, __uint_as_float((uint32_t)lb),
+                                    __uint_as_float((uint32_t)(lb >> 32)), 0.f};
+    }
+    lds_barrier();
+    if (kh == 1) return;
+    // (elements converted by value: a bit cast applied to an element of a vector reads the
+    // vector's first element here)
+    const f32x4 x = xo[C::DB * 64 + lane];
+    const float m1 = x[0];
+    const double l1 = __longlong_as_double((long long)((unsigned long long)__float_as_uint(x[1]) |
+                                                       ((unsigned long long)__float_as_uint(x[2]) << 32)));
+    const float M = fmaxf(m_run, m1);
+    const float f0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
+    const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+    ld = (m_run == -INFINITY ? 0.0 : exp2((double)m_run - (double)M) * ld) +
+         (m1 == -INFINITY ? 0.0 : exp2((double)m1 - (double)M) * l1);
+#pragma unroll
+    for (int db = 0; db < C::DB; db++) oacc[db] = oacc[db] * f0 + xo[db * 64 + lane] * f1;
+    m_run = M;
+  }
   if (p.final_direct) {  // one split: normalize here (sink, output gate) and write O and LSE
     if (!row_ok) return;
     const size_t orow = ((size_t)b * p.Tq + j) * p.Hq + h;
@@ -333,14 +381,16 @@ __global__ __launch_bounds__(64 * NW, 1) void group_attn_kernel(RowAttnParams p)
 template <int D, int NW>
 hipError_t launch_nw(const RowAttnParams& p, KeySrc src, hipStream_t stream) {
   const dim3 grid(p.n_split * p.B * p.Hkv * p.Tq);
+  constexpr int kListThreads = 64 * NW * key_halves<D, NW, SRC_TOKEN>();
+  constexpr int kRangeThreads = 64 * NW * key_halves<D, NW, SRC_RANGE>();
   if (src == SRC_TOKEN)
-    group_attn_kernel<D, NW, SRC_TOKEN, false><<<grid, 64 * NW, 0, stream>>>(p);
+    group_attn_kernel<D, NW, SRC_TOKEN, false><<<grid, kListThreads, 0, stream>>>(p);
   else if (src == SRC_BLOCK)
-    group_attn_kernel<D, NW, SRC_BLOCK, false><<<grid, 64 * NW, 0, stream>>>(p);
+    group_attn_kernel<D, NW, SRC_BLOCK, false><<<grid, kListThreads, 0, stream>>>(p);
   else if (p.logits)
-    group_attn_kernel<D, NW, SRC_RANGE, true><<<grid, 64 * NW, 0, stream>>>(p);
+    group_attn_kernel<D, NW, SRC_RANGE, true><<<grid, kRangeThreads, 0, stream>>>(p);
   else
-    group_attn_kernel<D, NW, SRC_RANGE, false><<<grid, 64 * NW, 0, stream>>>(p);
+    group_attn_kernel<D, NW, SRC_RANGE, false><<<grid, kRangeThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
