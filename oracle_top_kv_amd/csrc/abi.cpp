@@ -263,19 +263,18 @@ TkLayout tk_layout(const Shape& s, const TkGeom& t) {
 size_t tk_ws(const Shape& s, const TkGeom& t) { return tk_layout(s, t).total; }
 
 // Token selection from stored logits: one (b, t, u) row per workgroup and key chunk (chunks of
-// at least 256 keys, multiples of 256: with few rows, e.g. MQA, a thread then reads the g head
-// values of one key instead of several keys one after the other); the selection passes are
-// those of tk_geom.
+// whole 1024-key passes: a thread reads 4 consecutive keys of every head per pass); the
+// selection passes are those of tk_geom.
 TkGeom tl_geom(const Shape& s) {
   TkGeom t = tk_geom(s);
   t.q_per_set = 1;
   t.sets_per_bu = s.Tq;
   long long want = (1024 + (long long)t.rows - 1) / (long long)t.rows;
-  const long long most = (s.Tk + 255) / 256;
+  const long long most = (s.Tk + 1023) / 1024;
   if (want > most) want = most;
   if (want < 1) want = 1;
   long long kps = (s.Tk + want - 1) / want;
-  kps = (kps + 255) / 256 * 256;
+  kps = (kps + 1023) / 1024 * 1024;
   t.keys_per_split = (int)kps;
   t.n_split = (int)((s.Tk + kps - 1) / kps);
   return t;

@@ -149,7 +149,7 @@ struct TopkDecodeParams {
   int32_t* cnt;  // [B, Tq, Hkv]
   int cap;
   // selection from stored logits instead of Q, K (launch_topk_from_logits; n_split chunks of
-  // keys_per_split keys per (b, t, u) row, multiples of 256)
+  // keys_per_split keys per (b, t, u) row, multiples of 1024)
   const float* logits;  // [B, Tq, Hq, Tk] raw dot products q.k
 };
 hipError_t launch_topk_decode(const TopkDecodeParams& p, int head_dim, bool in_f32,

@@ -154,9 +154,26 @@ __global__ __launch_bounds__(256) void tk_score_kernel(TopkDecodeParams p) {
 }
 
 // ---- 1'. score from stored logits ---------------------------------------------------------
+// Histogram increments of a wave, bin `bin` for the lanes with `take` (every lane of the wave
+// active): the lanes that share the first taking lane's bin add with one atomic, the others
+// one each.  A chunk's keys crowd into few bins, so most increments take the first path.
+__device__ __forceinline__ void hist_add_wave(uint32_t* hist, uint32_t bin, bool take, int lane) {
+  const unsigned long long act = __ballot(take);
+  if (act == 0ull) return;
+  const int first = __ffsll((long long)act) - 1;
+  const uint32_t fb = __shfl(bin, first);
+  const bool same = take && bin == fb;
+  const unsigned long long m = __ballot(same);
+  if (lane == first) atomicAdd(&hist[fb], (uint32_t)__popcll(m));
+  if (take && !same) atomicAdd(&hist[bin], 1u);
+}
+
 // Same key as the score pass, from the raw dot products q.k that the full-attention pass stored
-// ([B, Tq, Hq, Tk] fp32), so neither Q nor K is read again.  One workgroup per (row, key chunk);
-// a thread per key reads the G head values of its key (coalesced across the wave per head).
+// ([B, Tq, Hq, Tk] fp32), so neither Q nor K is read again.  One workgroup per (row, key chunk).
+// With 16-byte aligned rows (Tk a multiple of 4) and chunks of whole 1024-key passes, a thread
+// takes 4 consecutive keys per pass and reads each head's 4 values with one 16-byte load (a
+// wave reads 1 KB of a head row per load, a workgroup 4 KB), heads in groups of 16; otherwise a
+// thread per key reads the G head values of its key (coalesced across the wave per head).
 template <int G>
 __global__ __launch_bounds__(256) void tk_logit_score_kernel(TopkDecodeParams p) {
   __shared__ uint32_t hist[kBins];
@@ -185,6 +202,36 @@ __global__ __launch_bounds__(256) void tk_logit_score_kernel(TopkDecodeParams p)
   if (k_end > t - p.window + 1) k_end = t - p.window + 1;  // candidates 0 .. t - w
   const float* lg = p.logits + (((size_t)b * p.Tq + j) * p.Hq + (size_t)u * p.g) * p.Tk;
   uint32_t* keys_row = p.keys + (size_t)row * p.Tk;
+  const bool vec = (p.Tk & 3) == 0 && (p.keys_per_split & 1023) == 0 &&
+                   ((uintptr_t)p.logits & 15) == 0 && ((uintptr_t)p.keys & 15) == 0;
+  if (vec) {
+    constexpr int HC = G < 16 ? G : 16;  // heads per load group
+    const int lane = threadIdx.x & 63;
+    for (long long base = k_begin; base < k_end; base += 1024) {  // uniform trip count
+      const long long pos = base + 4 * threadIdx.x;
+      const bool in = pos < k_end;  // then pos + 3 < Tk (Tk and pos multiples of 4)
+      float v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int c0 = 0; c0 < G; c0 += HC) {
+        f32x4 x[HC];
+#pragma unroll
+        for (int i = 0; i < HC; i++)
+          x[i] = (in && c0 + i < p.g) ? *(const f32x4*)(lg + (size_t)(c0 + i) * p.Tk + pos)
+                                      : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < HC; i++)
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            v[e] = fmaxf(v[e], __builtin_fmaf(x[i][e], p.scale_log2, -delta[c0 + i]));
+      }
+      uint32_t key[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) key[e] = float_key(v[e]);
+      if (in) *(uint4*)(keys_row + pos) = make_uint4(key[0], key[1], key[2], key[3]);
+#pragma unroll
+      for (int e = 0; e < 4; e++) hist_add_wave(hist, key[e] >> 21, in && pos + e < k_end, lane);
+    }
+  } else {
   for (long long pos = k_begin + threadIdx.x; pos < k_end; pos += 256) {
     float x[G];
 #pragma unroll
@@ -195,6 +242,7 @@ __global__ __launch_bounds__(256) void tk_logit_score_kernel(TopkDecodeParams p)
     const uint32_t key = float_key(v);
     keys_row[pos] = key;
     atomicAdd(&hist[key >> 21], 1u);
+  }
   }
   __syncthreads();
   uint32_t* gh = p.hist + (size_t)row * kBins;
