@@ -284,15 +284,40 @@ hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logit
                                     int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
                                     void* stream);
 
-/* hs_full_attn_fwd over a paged K / V cache (always the split row kernel: meant for decode),
- * optionally keeping the logits like hs_full_attn_fwd_logits (logits may be NULL).  Same o, lse
- * (and logits) as the contiguous call on the same logical cache, bit for bit, except for groups
- * of 32-64 heads, whose contiguous call runs the group kernel: there the logits are identical
- * and o, lse agree to rounding (other split boundaries).  Workspace:
- * hs_workspace_size(HS_OP_FULL_ATTN_PAGED, desc, page_size, 0). */
+/* hs_full_attn_fwd over a paged K / V cache, optionally keeping the logits like
+ * hs_full_attn_fwd_logits (logits may be NULL).  Decode and prefill take different kernels, as
+ * the pages require of a paged cache [P2 engineering constraints 2 and 3]:
+ *   - logits == NULL, a prefill shape (one that hs_full_attn_fwd runs on the tiled prefill
+ *     kernel) and page_size >= the kernel's key tile (64 keys; 32 at head_dim 256): the tiled
+ *     prefill kernel, which reads each key tile from its page (a page holds whole tiles); o and
+ *     lse are bit-identical to hs_full_attn_fwd's for the same logical cache.
+ *   - otherwise the split row kernel (meant for decode), which translates every key: same o,
+ *     lse (and logits) as the contiguous call on that kernel, bit for bit, except for groups of
+ *     32-64 heads, whose contiguous call runs the group kernel: there the logits are identical
+ *     and o, lse agree to rounding (other split boundaries).
+ * Workspace: hs_workspace_size(HS_OP_FULL_ATTN_PAGED, desc, page_size, 0) (0 on the prefill
+ * kernel). */
 hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
                                  const void* v_pool, const hs_kv_pages* pages, void* o, float* lse,
                                  float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/* hs_oracle_topk and hs_block_score_topk over a paged K cache (prefill over a paged cache):
+ * the same index sets as the contiguous calls on the same logical cache, bit for bit, from the
+ * streamed prefill selection, which reads every 64-key tile of K from its page.  Prefill shapes
+ * only (those the contiguous calls run on that selection: many query rows per KV head), with
+ * page_size >= 64 (pages hold whole tiles); other shapes or smaller pages: HS_ERR_UNSUPPORTED
+ * (decode selects from the logits that hs_full_attn_fwd_paged keeps, which never read the
+ * pages) [P2 engineering constraints 2 and 3: the block table is consumed by the kernel; prefill
+ * and decode have their own implementations].  NULL pages: HS_ERR_INVALID_ARG.  Workspace: as
+ * the contiguous call (HS_OP_ORACLE_TOPK / HS_OP_BLOCK_TOPK). */
+hs_status hs_oracle_topk_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
+                               const hs_kv_pages* pages, const float* lse, int32_t k_global,
+                               int32_t window, int32_t* idx, int32_t* count, void* ws,
+                               size_t ws_bytes, void* stream);
+hs_status hs_block_score_topk_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
+                                    const hs_kv_pages* pages, const float* lse, int32_t block,
+                                    int32_t n_blocks, int32_t* blk_idx, int32_t* count, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* hs_sparse_attn_gather_ex over a paged K / V cache (token and block index sets address logical
  * positions; the sliding-window branch keeps its own position-indexed or ring cache).  Same

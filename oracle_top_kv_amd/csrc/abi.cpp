@@ -617,6 +617,15 @@ size_t row_fa_ws(const Shape& s, int page_size) {
   return g.n_split > 1 ? partial_bytes(g, s.D) : 0;
 }
 
+// Pages of the paged selection calls hold whole 64-key tiles of the streamed selection.
+constexpr int kPagedSelectMinPage = 64;
+
+// Paged full attention of a prefill shape without stored logits runs on the tiled prefill
+// kernel when a page holds whole key tiles; everything else on the row kernel.
+bool paged_prefill_attn(const Shape& s, const float* logits, int page_size) {
+  return !logits && use_prefill_kernel(s) && page_size >= hs::prefill_tile_keys(s.D);
+}
+
 hs_status check_pages(const Shape& s, const hs_kv_pages* pg) {
   if (!pg || !pg->block_table) return fail(HS_ERR_INVALID_ARG, "NULL page table");
   const int P = pg->page_size;
@@ -822,6 +831,7 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
     case HS_OP_FULL_ATTN_LOGITS: return row_fa_ws(s, 0);
     case HS_OP_FULL_ATTN_PAGED: {
       if (p0 < 1 || (p0 & (p0 - 1))) return 0;
+      // the size of the row kernel's call, which also covers the logits form of the call
       return row_fa_ws(s, p0);
     }
     case HS_OP_TOPK_FROM_LOGITS: return tk_ws(s, tl_geom(s));
@@ -968,6 +978,15 @@ hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const 
   st = check_pages(s, pages);
   if (st != HS_OK) return st;
   if (logits && (uintptr_t)logits % 4) return fail(HS_ERR_INVALID_ARG, "logits must be 4-byte aligned");
+  if (paged_prefill_attn(s, logits, pages->page_size)) {
+    hs::PrefillParams pp = prefill_params(s, q, k_pool, v_pool, o, lse);
+    pp.pages = pages->block_table;
+    pp.page_shift = __builtin_ctz((unsigned)pages->page_size);
+    pp.max_pages = pages->max_pages;
+    pp.n_pages = pages->n_pages;
+    return hip_status(hs::launch_prefill_attn(pp, s.D, (hipStream_t)stream),
+                      "paged prefill attention kernel");
+  }
   return row_full_attn(s, q, k_pool, v_pool, o, lse, logits, ws, ws_bytes, stream, pages);
 }
 
@@ -1010,9 +1029,36 @@ hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logit
 }
 
 
-hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k, const float* lse,
-                         int32_t k_global, int32_t window, int32_t* idx, int32_t* count, void* ws,
-                         size_t ws_bytes, void* stream) {
+namespace {
+
+// The paged selection calls take the streamed prefill route only (the decode-shaped routes
+// select from logits that full attention keeps, which never read the pages), on pages that
+// hold whole 64-key tiles.
+hs_status check_paged_select(const Shape& s, const hs_kv_pages* pages, SelRoute route) {
+  hs_status st = check_pages(s, pages);
+  if (st != HS_OK) return st;
+  if (pages->page_size < kPagedSelectMinPage)
+    return fail(HS_ERR_UNSUPPORTED, "paged selection: page_size %d below %d (pages must hold "
+                "whole 64-key tiles)", pages->page_size, kPagedSelectMinPage);
+  if (route != SEL_PREFILL)
+    return fail(HS_ERR_UNSUPPORTED, "paged selection takes prefill shapes (many query rows per "
+                "KV head); for decode keep the logits (hs_full_attn_fwd_paged with logits) and "
+                "select from them");
+  return HS_OK;
+}
+
+void set_select_pages(hs::PrefillSelectParams& p, const hs_kv_pages* pages) {
+  if (!pages) return;
+  p.pages = pages->block_table;
+  p.page_shift = __builtin_ctz((unsigned)pages->page_size);
+  p.max_pages = pages->max_pages;
+  p.n_pages = pages->n_pages;
+}
+
+hs_status token_select(const hs_attn_desc* desc, const void* q, const void* k,
+                       const hs_kv_pages* pages, const float* lse, int32_t k_global,
+                       int32_t window, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                       void* stream) {
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
@@ -1022,6 +1068,10 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
   if (k_global < 0 || window < 0) return fail(HS_ERR_INVALID_ARG, "k_global and window must be >= 0");
   if ((long long)k_global + window < 1) return fail(HS_ERR_INVALID_ARG, "k_global + window must be >= 1");
   const SelRoute route = token_route(s, k_global);
+  if (pages) {
+    st = check_paged_select(s, pages, route);
+    if (st != HS_OK) return st;
+  }
   hipStream_t hst = (hipStream_t)stream;
   if (route == SEL_PREFILL) {
     const size_t need = tk_prefill_ws(s);
@@ -1036,6 +1086,7 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
       p.ccnt = (int32_t*)((char*)ws + align_up(select_chunk_rows(s) * hs::prefill_select_buffer_cap() * 8, 256));
     p.idx = idx;
     p.cnt = count;
+    set_select_pages(p, pages);
     return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, false, hst),
                       "token selection kernel");
   }
@@ -1067,10 +1118,10 @@ hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k,
   return hip_status(hs::launch_topk_from_logits(p, hst), "token top-k kernels");
 }
 
-hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const void* k,
-                              const float* lse, int32_t block, int32_t n_blocks,
-                              int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
-                              void* stream) {
+hs_status block_select(const hs_attn_desc* desc, const void* q, const void* k,
+                       const hs_kv_pages* pages, const float* lse, int32_t block,
+                       int32_t n_blocks, int32_t* blk_idx, int32_t* count, void* ws,
+                       size_t ws_bytes, void* stream) {
   Shape s;
   hs_status st = check_desc(desc, &s);
   if (st != HS_OK) return st;
@@ -1081,6 +1132,10 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
   SelRoute route;
   st = block_route(s, block, n_blocks, &route, &g);
   if (st != HS_OK) return st;
+  if (pages) {
+    st = check_paged_select(s, pages, route);
+    if (st != HS_OK) return st;
+  }
   hipStream_t hst = (hipStream_t)stream;
   const size_t need = block_select_ws(route, s, g, n_blocks);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -1095,6 +1150,7 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
       p.cvals = (unsigned long long*)ws;
       p.ccnt = (int32_t*)((char*)ws + align_up(select_chunk_rows(s) * (size_t)n_blocks * 8, 256));
     }
+    set_select_pages(p, pages);
     return hip_status(hs::launch_prefill_select(p, s.D, s.in_f32, true, hst),
                       "block selection kernel");
   }
@@ -1112,6 +1168,41 @@ hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const voi
   hs::BlockTopkParams p = bk_params(s, g, lse, block, n_blocks, blk_idx, count, (char*)ws + lb);
   p.logits = logits;
   return hip_status(hs::launch_block_from_logits(p, hst), "block top-k kernels");
+}
+
+}  // namespace
+
+hs_status hs_oracle_topk(const hs_attn_desc* desc, const void* q, const void* k, const float* lse,
+                         int32_t k_global, int32_t window, int32_t* idx, int32_t* count, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return token_select(desc, q, k, nullptr, lse, k_global, window, idx, count, ws, ws_bytes,
+                      stream);
+}
+
+hs_status hs_oracle_topk_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
+                               const hs_kv_pages* pages, const float* lse, int32_t k_global,
+                               int32_t window, int32_t* idx, int32_t* count, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!pages) return fail(HS_ERR_INVALID_ARG, "NULL page table");
+  return token_select(desc, q, k_pool, pages, lse, k_global, window, idx, count, ws, ws_bytes,
+                      stream);
+}
+
+hs_status hs_block_score_topk(const hs_attn_desc* desc, const void* q, const void* k,
+                              const float* lse, int32_t block, int32_t n_blocks,
+                              int32_t* blk_idx, int32_t* count, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return block_select(desc, q, k, nullptr, lse, block, n_blocks, blk_idx, count, ws, ws_bytes,
+                      stream);
+}
+
+hs_status hs_block_score_topk_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
+                                    const hs_kv_pages* pages, const float* lse, int32_t block,
+                                    int32_t n_blocks, int32_t* blk_idx, int32_t* count, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (!pages) return fail(HS_ERR_INVALID_ARG, "NULL page table");
+  return block_select(desc, q, k_pool, pages, lse, block, n_blocks, blk_idx, count, ws, ws_bytes,
+                      stream);
 }
 
 hs_status hs_sparse_attn_gather(const hs_attn_desc* desc, const void* q, const void* k_full,

@@ -173,7 +173,9 @@ __device__ __forceinline__ void select_blocks(const PrefillParams& p,
 //   C[32 x 32]: column l % 32, register 4g + e holds row 8g + 4h + e (g, e = 0..3)
 // TMAX: every row also records its raw logit maximum over each tile (bf16, rounded toward -inf),
 // two tiles per 4-byte store.
-template <int D, bool BSEL, bool TMAX = false>
+// PAGED: K and V are page pools addressed through the block table; a page holds whole tiles,
+// so only each tile's first row changes (one scalar table read per tile).
+template <int D, bool BSEL, bool TMAX = false, bool PAGED = false>
 __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillParams p) {
   using C = PfCfg<D>;
   static_assert(!BSEL || C::NW == 8, "the block-selection merge assumes 8 waves");
@@ -228,8 +230,9 @@ __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillPa
     for (int i = 0; i < 16; i++) oacc[db][i] = 0.f;
 
   const size_t kv_row_stride = (size_t)p.Hkv * D;
-  const uint16_t* kbase = (const uint16_t*)p.k + ((size_t)b * p.Tk * p.Hkv + u) * D;
-  const uint16_t* vbase = (const uint16_t*)p.v + ((size_t)b * p.Tk * p.Hkv + u) * D;
+  const size_t b_rows = PAGED ? 0 : (size_t)b * p.Tk;  // a pool has no batch dimension
+  const uint16_t* kbase = (const uint16_t*)p.k + (b_rows * p.Hkv + u) * D;
+  const uint16_t* vbase = (const uint16_t*)p.v + (b_rows * p.Hkv + u) * D;
   const int n_tiles = (t_max + BN) / BN;  // tiles covering keys 0..t_max
 
   // K tiles run one tile ahead of V tiles: the step of tile t takes the softmax of S(t), computed
@@ -252,8 +255,17 @@ __global__ __launch_bounds__(PfCfg<D>::Threads, 1) void pf_attn_kernel(PrefillPa
   auto tile_rsrc = [&](const uint16_t* base, int t) {
     const int valid = max(0, min(BN, t_max + 1 - t * BN));
     const int n_rec = __builtin_amdgcn_readfirstlane(valid * row_bytes);  // uniform: scalar
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)t * BN * kv_row_stride), 0,
-                                             n_rec, kBufferConfig);
+    size_t row0 = (size_t)t * BN;
+    if constexpr (PAGED) {
+      // the tile's page (a tile past the last one, read as zeros, takes the last key's page so
+      // that the table index stays inside the batch entry's row of the table)
+      const int key0 = min(t * BN, t_max);
+      int e = p.pages[(size_t)b * p.max_pages + (key0 >> p.page_shift)];
+      e = min(max(e, 0), p.n_pages - 1);
+      row0 = ((size_t)e << p.page_shift) + (key0 & ((1 << p.page_shift) - 1));
+    }
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * kv_row_stride), 0, n_rec,
+                                             kBufferConfig);
   };
   u32x4 kreg[C::LPT], vreg[C::LPT];
   auto load_k = [&](int t) {
@@ -526,10 +538,22 @@ hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t
   // tile maxima: head sizes up to 128 (at 256 the kernel has no registers to spare: the maxima
   // cost a fifth of its time), not with the block selection
   if (p.tile_max) {
-    if (bsel || head_dim > 128 || p.tmax_stride % 16 || p.tmax_stride < (p.Tk + kBN - 1) / kBN)
+    if (bsel || p.pages || head_dim > 128 || p.tmax_stride % 16 || p.tmax_stride < (p.Tk + kBN - 1) / kBN)
       return hipErrorInvalidValue;
     if (head_dim == 128) pf_attn_kernel<128, false, true><<<grid, kThreads, 0, stream>>>(p);
     else pf_attn_kernel<64, false, true><<<grid, kThreads, 0, stream>>>(p);
+    return hipGetLastError();
+  }
+  if (p.pages) {  // plain attention only; pages hold whole tiles
+    if (bsel || (1 << p.page_shift) < prefill_tile_keys(head_dim) || p.page_shift > 20 ||
+        p.max_pages < 1 || p.n_pages < 1)
+      return hipErrorInvalidValue;
+    if (head_dim == 256)
+      pf_attn_kernel<256, false, false, true><<<grid, PfCfg<256>::Threads, 0, stream>>>(p);
+    else if (head_dim == 128)
+      pf_attn_kernel<128, false, false, true><<<grid, kThreads, 0, stream>>>(p);
+    else
+      pf_attn_kernel<64, false, false, true><<<grid, kThreads, 0, stream>>>(p);
     return hipGetLastError();
   }
   if (head_dim == 256) {

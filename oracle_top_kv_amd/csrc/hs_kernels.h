@@ -119,6 +119,11 @@ struct PrefillParams {
   // 16 and >= the tiles of the row)
   uint16_t* tile_max;
   int tmax_stride;
+  // or null: k, v are page pools [n_pages, 1 << page_shift, Hkv, D] and position i of batch
+  // entry b lives in page pages[b * max_pages + (i >> page_shift)]; pages hold whole key tiles
+  // (1 << page_shift >= prefill_tile_keys(head_dim)), so a tile is one contiguous run of rows
+  const int32_t* pages;
+  int page_shift, max_pages, n_pages;
 };
 int prefill_tile_keys(int head_dim);
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, hipStream_t stream);
@@ -214,6 +219,10 @@ struct PrefillSelectParams {
   int32_t* redo;
   // or null: only workgroups holding a row flagged here run (the rows' second pass)
   const int32_t* redo_only;
+  // or null: k is a page pool [n_pages, 1 << page_shift, Hkv, D] addressed through the block
+  // table as in PrefillParams; pages hold whole 64-key tiles (page_shift >= 6)
+  const int32_t* pages;
+  int page_shift, max_pages, n_pages;
 };
 int prefill_select_buffer_cap();
 int prefill_select_max_k();

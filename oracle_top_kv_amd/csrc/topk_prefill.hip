@@ -405,18 +405,30 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
   const int bshift = BLOCK ? __ffs(p.block) - 1 : 0;  // blocks of 16, 32 or 64 keys
 
   const size_t kv_row_stride = (size_t)p.Hkv * D;
-  const unsigned char* kbase =
-      (const unsigned char*)p.k + ((size_t)b * p.Tk * p.Hkv + u) * D * C::Elem;
+  // a page pool (p.pages) has no batch dimension
+  const size_t b_rows = p.pages ? 0 : (size_t)b * p.Tk;
+  const unsigned char* kbase = (const unsigned char*)p.k + (b_rows * p.Hkv + u) * D * C::Elem;
   const int key_last = BLOCK ? t_max : t_max - p.window;  // last key any query needs
   const int n_tiles = key_last < 0 ? 0 : key_last / kBN + 1;
   u32x4 kreg[C::LPT];
   auto load_tile = [&](int t) {
+    // the tile's first key (clamped like its rows) and where its row sits in memory: the cache
+    // row itself, or its row in the page pool (pages hold whole 64-key tiles, so the tile's keys
+    // follow it in the same page); a uniform, scalar computation
+    const int key0 = min(t * kBN, key_last);
+    size_t row0 = (size_t)key0;
+    if (p.pages) {
+      int e = p.pages[(size_t)b * p.max_pages + (key0 >> p.page_shift)];
+      e = min(max(e, 0), p.n_pages - 1);
+      row0 = ((size_t)e << p.page_shift) + (key0 & ((1 << p.page_shift) - 1));
+    }
+    const unsigned char* tbase = kbase + row0 * kv_row_stride * C::Elem;
 #pragma unroll
     for (int i = 0; i < C::LPT; i++) {
       const int c = threadIdx.x + kThreads * i;
       const int row = c / C::CPR, ch = c % C::CPR;
       const int key = min(t * kBN + row, key_last);
-      kreg[i] = *(const u32x4*)(kbase + ((size_t)key * kv_row_stride) * C::Elem + ch * 16);
+      kreg[i] = *(const u32x4*)(tbase + ((size_t)(key - key0) * kv_row_stride) * C::Elem + ch * 16);
     }
   };
   auto store_tile = [&](int buf) {
@@ -929,6 +941,9 @@ hipError_t launch_prefill_select(const PrefillSelectParams& p, int head_dim, boo
     return hipErrorInvalidValue;
   if (block_mode && (p.block < 16 || p.block > 64 || (p.block & (p.block - 1)) ||
                      p.n_blocks < 1 || p.n_blocks > kMaxBlocks))
+    return hipErrorInvalidValue;
+  if (p.pages && ((1 << p.page_shift) < kBN || p.page_shift > 20 || p.max_pages < 1 ||
+                  p.n_pages < 1))
     return hipErrorInvalidValue;
   if (head_dim == 256) {  // bf16 only
     if (in_f32) return hipErrorInvalidValue;

@@ -24,7 +24,7 @@ EXPORTS = ["hs_full_attn_fwd", "hs_oracle_topk", "hs_block_score_topk", "hs_spar
            "hs_full_attn_fwd_logits", "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
            "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex", "hs_full_attn_fwd_paged",
            "hs_sparse_attn_gather_paged", "hs_sparse_attn_gather_noalloc", "hs_full_attn_topk",
-           "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
+           "hs_oracle_topk_paged", "hs_block_score_topk_paged", "hs_workspace_size", "hs_status_string", "hs_last_error", "hs_version"]
 
 
 class AttnDesc(ctypes.Structure):
@@ -85,6 +85,8 @@ def lib():
                                                ctypes.POINTER(SparseOpts), vp, vp, vp, sz, vp]
         pp = ctypes.POINTER(KvPages)
         L.hs_full_attn_fwd_paged.argtypes = [pd, vp, vp, vp, pp, vp, vp, vp, vp, sz, vp]
+        L.hs_oracle_topk_paged.argtypes = [pd, vp, vp, pp, vp, i32, i32, vp, vp, vp, sz, vp]
+        L.hs_block_score_topk_paged.argtypes = [pd, vp, vp, pp, vp, i32, i32, vp, vp, vp, sz, vp]
         L.hs_sparse_attn_gather_paged.argtypes = [pd, vp, vp, vp, pp, ctypes.c_int, vp, vp, i32,
                                                   i32, ctypes.POINTER(SwaBranch),
                                                   ctypes.POINTER(SparseOpts), vp, vp, vp, sz, vp]
@@ -101,7 +103,8 @@ def lib():
                   "hs_oracle_topk_from_logits", "hs_block_topk_from_logits",
                   "hs_full_attn_block_topk", "hs_sparse_attn_gather_ex",
                   "hs_full_attn_fwd_paged", "hs_sparse_attn_gather_paged",
-                  "hs_sparse_attn_gather_noalloc", "hs_full_attn_topk"):
+                  "hs_sparse_attn_gather_noalloc", "hs_full_attn_topk", "hs_oracle_topk_paged",
+                  "hs_block_score_topk_paged"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -319,37 +322,57 @@ def block_topk_from_logits(logits, lse, n_kv_heads, head_dim, block, n_blocks, q
     return idx, cnt
 
 
-def oracle_topk(q, k, lse, k_global, window, q_offset=None, scale=None):
-    """Forced window plus top-k_global tokens. Returns (idx int32 [B,Tq,Hkv,k+w], count)."""
+def _select_desc(q, k, lse, q_offset, scale, pages):
     dev = q.device
     _need(q, "q", dev)
     _need(k, "k", dev, dtype=q.dtype)
     _need(lse, "lse", dev, dtype=torch.float32, shape=(q.shape[0], q.shape[2], q.shape[1]))
-    desc = make_desc(q, k, q_offset, scale=scale)
+    if pages is None:
+        return make_desc(q, k, q_offset, scale=scale), None
+    desc = _paged_desc(q, k, pages[1], q_offset, q.dtype, scale)
+    return desc, _pages(k, pages[0], k.shape[1], dev)
+
+
+def oracle_topk(q, k, lse, k_global, window, q_offset=None, scale=None, pages=None):
+    """Forced window plus top-k_global tokens. Returns (idx int32 [B,Tq,Hkv,k+w], count).
+    pages = (block_table int32 [B, max_pages], kv_len): k is a page pool [n_pages, page_size,
+    Hkv, d] (hs_oracle_topk_paged; prefill shapes)."""
+    dev = q.device
+    desc, pg = _select_desc(q, k, lse, q_offset, scale, pages)
     B, Tq, Hkv = q.shape[0], q.shape[1], k.shape[2]
     idx = torch.empty((B, Tq, Hkv, k_global + window), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
     ws, n = workspace(HS_OP_ORACLE_TOPK, desc, k_global, window, device=dev)
-    _check(lib().hs_oracle_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), int(k_global),
-                                int(window), _ptr(idx), _ptr(cnt), _ptr(ws), n, _stream(dev)),
-           "hs_oracle_topk")
+    if pg is None:
+        _check(lib().hs_oracle_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse),
+                                    int(k_global), int(window), _ptr(idx), _ptr(cnt), _ptr(ws), n,
+                                    _stream(dev)), "hs_oracle_topk")
+    else:
+        _check(lib().hs_oracle_topk_paged(ctypes.byref(desc), _ptr(q), _ptr(k), ctypes.byref(pg),
+                                          _ptr(lse), int(k_global), int(window), _ptr(idx),
+                                          _ptr(cnt), _ptr(ws), n, _stream(dev)),
+               "hs_oracle_topk_paged")
     return idx, cnt
 
 
-def block_score_topk(q, k, lse, block, n_blocks, q_offset=None, scale=None):
-    """Top n_blocks causal blocks. Returns (blk_idx int32 [B,Tq,Hkv,n_blocks], count)."""
+def block_score_topk(q, k, lse, block, n_blocks, q_offset=None, scale=None, pages=None):
+    """Top n_blocks causal blocks. Returns (blk_idx int32 [B,Tq,Hkv,n_blocks], count).
+    pages: as oracle_topk (hs_block_score_topk_paged)."""
     dev = q.device
-    _need(q, "q", dev)
-    _need(k, "k", dev, dtype=q.dtype)
-    _need(lse, "lse", dev, dtype=torch.float32, shape=(q.shape[0], q.shape[2], q.shape[1]))
-    desc = make_desc(q, k, q_offset, scale=scale)
+    desc, pg = _select_desc(q, k, lse, q_offset, scale, pages)
     B, Tq, Hkv = q.shape[0], q.shape[1], k.shape[2]
     idx = torch.empty((B, Tq, Hkv, n_blocks), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, Tq, Hkv), dtype=torch.int32, device=dev)
     ws, n = workspace(HS_OP_BLOCK_TOPK, desc, block, n_blocks, device=dev)
-    _check(lib().hs_block_score_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), int(block),
-                                     int(n_blocks), _ptr(idx), _ptr(cnt), _ptr(ws), n,
-                                     _stream(dev)), "hs_block_score_topk")
+    if pg is None:
+        _check(lib().hs_block_score_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse),
+                                         int(block), int(n_blocks), _ptr(idx), _ptr(cnt),
+                                         _ptr(ws), n, _stream(dev)), "hs_block_score_topk")
+    else:
+        _check(lib().hs_block_score_topk_paged(ctypes.byref(desc), _ptr(q), _ptr(k),
+                                               ctypes.byref(pg), _ptr(lse), int(block),
+                                               int(n_blocks), _ptr(idx), _ptr(cnt), _ptr(ws), n,
+                                               _stream(dev)), "hs_block_score_topk_paged")
     return idx, cnt
 
 

@@ -6,6 +6,7 @@ Outputs given identical index sets: max-abs 1e-2 for bf16 inputs, 1e-5 for fp32 
 output compared is requested in fp32).  LSE: max-abs 1e-6.
 """
 import numpy as np
+import torch
 
 import oracle
 
@@ -91,3 +92,20 @@ def check_block_sets(gpu_idx, gpu_cnt, orc_idx, orc_cnt, q, k, lse, block, q_off
 
 def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
+
+
+def paged(t, page_size, seed, spare=3):
+    """[B, T, Hkv, d] -> (pool [n_pages, P, Hkv, d], block_table [B, max_pages]): every logical
+    page of every batch entry in its own physical page, in a shuffled order, with a few unused
+    pages in the pool (filled with large values that must never be read)."""
+    B, T, Hkv, d = t.shape
+    mp = (T + page_size - 1) // page_size
+    n = B * mp + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n, generator=g)[:B * mp].view(B, mp).to(torch.int32)
+    pool = torch.full((n, page_size, Hkv, d), 1e4, dtype=t.dtype, device=t.device)
+    for b in range(B):
+        for p in range(mp):
+            rows = t[b, p * page_size:(p + 1) * page_size]
+            pool[perm[b, p], :rows.shape[0]] = rows
+    return pool, perm.to(t.device)

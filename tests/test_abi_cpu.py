@@ -319,3 +319,38 @@ def test_ring_window_must_hold_every_position_of_the_call(q_len, ring, ok):
     else:
         assert rc == hs.HS_ERR_INVALID_ARG
         assert "local_ring" in L.hs_last_error().decode()
+
+
+@pytest.mark.parametrize("which", ["token", "block"])
+def test_paged_selection_argument_checks(which):
+    """The paged selection calls take prefill shapes on pages of at least 64 positions; a
+    decode shape, small pages or a missing table are refused before any launch (a valid call
+    stops at the missing workspace)."""
+    L = hs.lib()
+
+    def call(d, pages, ws_bytes=0):
+        pg = None if pages is None else ctypes.byref(pages)
+        if which == "token":
+            return L.hs_oracle_topk_paged(ctypes.byref(d), FAKE, FAKE, pg, FAKE, 1024, 128, FAKE,
+                                          FAKE, FAKE if ws_bytes else None, ws_bytes, None)
+        return L.hs_block_score_topk_paged(ctypes.byref(d), FAKE, FAKE, pg, FAKE, 64, 16, FAKE,
+                                           FAKE, FAKE if ws_bytes else None, ws_bytes, None)
+
+    prefill = desc(q_len=512, kv_len=8192, n_q_heads=16, n_kv_heads=4)
+    good = hs.KvPages(0x1000, 64, 128, 128)
+    # token candidates, and the chunk lists of a 32-head group's blocks, need a workspace (a
+    # 16-head group's block selection needs none: that valid call would launch, so it is not made)
+    wide = prefill if which == "token" else desc(q_len=512, kv_len=8192, n_q_heads=64,
+                                                 n_kv_heads=2)
+    assert call(wide, good) == hs.HS_ERR_WORKSPACE, L.hs_last_error().decode()
+    assert call(prefill, None) == hs.HS_ERR_INVALID_ARG
+    small = hs.KvPages(0x1000, 32, 256, 256)
+    assert call(prefill, small) == hs.HS_ERR_UNSUPPORTED
+    assert "page_size" in L.hs_last_error().decode()
+    decode = desc(q_len=1, kv_len=8192, n_q_heads=16, n_kv_heads=4)
+    assert call(decode, good) == hs.HS_ERR_UNSUPPORTED
+    assert "prefill" in L.hs_last_error().decode()
+    short = hs.KvPages(0x1000, 64, 100, 128)  # 100 pages of 64 < 8192 positions
+    assert call(prefill, short) == hs.HS_ERR_INVALID_ARG
+    npo2 = hs.KvPages(0x1000, 96, 128, 128)
+    assert call(prefill, npo2) == hs.HS_ERR_INVALID_ARG

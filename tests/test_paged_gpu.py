@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from oracle_top_kv_amd.inputs import Workload, make_inputs, to_numpy_f32
-from parity_utils import LSE_TOL, TOL_BF16, check_token_sets, max_abs
+from parity_utils import LSE_TOL, TOL_BF16, check_token_sets, max_abs, paged
 
 pytestmark = pytest.mark.gpu
 
@@ -25,23 +25,6 @@ def hs():
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def paged(t, page_size, seed, spare=3):
-    """[B, T, Hkv, d] -> (pool [n_pages, P, Hkv, d], block_table [B, max_pages]): every logical
-    page of every batch entry in its own physical page, in a shuffled order, with a few unused
-    pages in the pool (filled with large values that must never be read)."""
-    B, T, Hkv, d = t.shape
-    mp = (T + page_size - 1) // page_size
-    n = B * mp + spare
-    g = torch.Generator().manual_seed(seed)
-    perm = torch.randperm(n, generator=g)[:B * mp].view(B, mp).to(torch.int32)
-    pool = torch.full((n, page_size, Hkv, d), 1e4, dtype=t.dtype, device=t.device)
-    for b in range(B):
-        for p in range(mp):
-            rows = t[b, p * page_size:(p + 1) * page_size]
-            pool[perm[b, p], :rows.shape[0]] = rows
-    return pool, perm.to(t.device)
 
 
 FA_CASES = [
