@@ -443,6 +443,7 @@ def prefill_leg(args):
         ev1[r][1].record()
     torch.cuda.synchronize()
     t_one = sum(e[0].elapsed_time(e[1]) for e in ev1) / reps
+    paged = paged_prefill(wl, q, k, v, qs, idx, cnt, hs, reps)
     f_fa, f_sc = costs.full_attn_flops(wl), costs.score_flops(wl)
     tot = (f_fa + f_sc) / ((t_fa + t_tk) * 1e-3) / 1e12
     b_sp = costs.token_gather_bytes(wl)  # rows each (b, t, u) gathers (mostly from cache)
@@ -459,7 +460,53 @@ def prefill_leg(args):
             "sparse_layer_ms": round(t_sp, 3),
             "sparse_layer_logical_GB_per_s": round(b_sp / (t_sp * 1e-3) / 1e9, 1),
             "sparse_layer_tflops": round(f_sp / (t_sp * 1e-3) / 1e12, 1),
+            "paged": dict(paged, vs_contiguous={
+                "full_attn": round(paged["full_attn_ms"] / t_fa, 3),
+                "topk": round(paged["topk_ms"] / t_tk, 3),
+                "sparse_layer": round(paged["sparse_layer_ms"] / t_sp, 3)}),
             "peak_tflops": 2500.0, "reps": reps}
+
+
+def paged_prefill(wl, q, k, v, qs, idx, cnt, hs, reps, page_size=64):
+    """Full attention, token top-k and one token-sparse layer of a prefill chunk over a paged
+    cache: K and V in shuffled 64-position pages behind a block table (the tiled attention and
+    the streamed selection read each key tile from its page).  Checks that the index sets equal
+    the contiguous calls' (idx, cnt)."""
+    import torch
+
+    B, T, Hkv, d = k.shape
+    mp = (T + page_size - 1) // page_size
+    g = torch.Generator().manual_seed(19)
+    table = torch.randperm(B * mp, generator=g).view(B, mp).to(torch.int32)
+    inv = torch.empty(B * mp, dtype=torch.long)
+    inv[table.view(-1).long()] = torch.arange(B * mp)
+    table, inv = table.cuda(), inv.cuda()
+
+    def pool(t):
+        p = t.view(B * mp, page_size, Hkv, d)  # logical page order (T is a multiple of 64)
+        return p[inv].contiguous()              # physical page table[b, lp] holds page (b, lp)
+
+    kp, vp = pool(k), pool(v)
+    pages = (table, T)
+    _, lse = hs.full_attn_fwd_paged(q, kp, vp, table, T)
+    pi, pc = hs.oracle_topk(q, kp, lse, wl.k_global, wl.window, pages=pages)
+    hs.sparse_attn_gather(qs, kp, vp, pi, pc, kind="token", pages=pages)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(pi, idx) and torch.equal(pc, cnt))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record()
+        _, lse = hs.full_attn_fwd_paged(q, kp, vp, table, T)
+        ev[r][1].record()
+        pi, pc = hs.oracle_topk(q, kp, lse, wl.k_global, wl.window, pages=pages)
+        ev[r][2].record()
+        hs.sparse_attn_gather(qs, kp, vp, pi, pc, kind="token", pages=pages)
+        ev[r][3].record()
+    torch.cuda.synchronize()
+    t = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / reps for i in range(3)]
+    del kp, vp
+    return {"page_size": page_size, "full_attn_ms": round(t[0], 3), "topk_ms": round(t[1], 3),
+            "sparse_layer_ms": round(t[2], 3), "sets_identical_to_contiguous": same}
 
 
 def mqa256_prefill_leg():

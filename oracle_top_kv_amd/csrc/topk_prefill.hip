@@ -44,6 +44,7 @@ constexpr int kNPL = kBufCap / 64;     // buffer entries per lane during a compa
 constexpr int kCompactSlack = 256;
 constexpr int kSortCap = 1024;         // largest k_global of the token mode
 constexpr int kMaxBlocks = 64;         // largest n_blocks
+constexpr int kBufferConfig = 0x00020000;  // buffer descriptor word 3 (gfx9 family: raw dwords)
 
 template <int D, bool F32>
 struct PsCfg {
@@ -411,24 +412,30 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
   const int key_last = BLOCK ? t_max : t_max - p.window;  // last key any query needs
   const int n_tiles = key_last < 0 ? 0 : key_last / kBN + 1;
   u32x4 kreg[C::LPT];
+  // Tile loads are raw buffer loads: the descriptor (scalar registers) holds the tile's first row
+  // and its number of rows through key_last; rows past them read as zeros without a memory access
+  // (no query takes them: they lie past every query's last candidate), so a thread's byte offset
+  // inside a tile is a constant and the loop does no address arithmetic.
+  const int row_bytes = (int)(kv_row_stride * C::Elem);
   auto load_tile = [&](int t) {
-    // the tile's first key (clamped like its rows) and where its row sits in memory: the cache
-    // row itself, or its row in the page pool (pages hold whole 64-key tiles, so the tile's keys
-    // follow it in the same page); a uniform, scalar computation
-    const int key0 = min(t * kBN, key_last);
+    // the tile's first row: the cache row itself, or its row in the page pool (pages hold whole
+    // 64-key tiles, so the tile's keys follow it in the same page)
+    const int key0 = t * kBN;  // t < n_tiles: key0 <= key_last
     size_t row0 = (size_t)key0;
     if (p.pages) {
       int e = p.pages[(size_t)b * p.max_pages + (key0 >> p.page_shift)];
       e = min(max(e, 0), p.n_pages - 1);
       row0 = ((size_t)e << p.page_shift) + (key0 & ((1 << p.page_shift) - 1));
     }
-    const unsigned char* tbase = kbase + row0 * kv_row_stride * C::Elem;
+    const int valid = min(kBN, key_last + 1 - key0);
+    const int n_rec = __builtin_amdgcn_readfirstlane(valid * row_bytes);  // uniform: scalar
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + row0 * kv_row_stride * C::Elem),
+                                                      0, n_rec, kBufferConfig);
 #pragma unroll
     for (int i = 0; i < C::LPT; i++) {
       const int c = threadIdx.x + kThreads * i;
-      const int row = c / C::CPR, ch = c % C::CPR;
-      const int key = min(t * kBN + row, key_last);
-      kreg[i] = *(const u32x4*)(tbase + ((size_t)(key - key0) * kv_row_stride) * C::Elem + ch * 16);
+      const int voff = (c / C::CPR) * row_bytes + (c % C::CPR) * 16;
+      kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
     }
   };
   auto store_tile = [&](int buf) {
@@ -593,6 +600,10 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
         }
       }
     }
+    // the next tile's rows into the other buffer (last read before the previous barrier) before
+    // the appends: loads and stores share one in-order counter, so waiting for these loads after
+    // the appends' stores would also wait for every append to be acknowledged
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
     if constexpr (!BLOCK) {
       unsigned long long any = 0ull;
 #pragma unroll
@@ -619,7 +630,6 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
         }
       }
     }
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 
