@@ -352,7 +352,14 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
       }
     }
   };
-  float delta[4][4];
+  // Row score in log2 units, shifted by a per-query constant Cq (a whole number, the same for the
+  // query's heads, so the group maximum and every comparison are unchanged):
+  //   tau log2(e) q.k - (LSE log2(e) - Cq) = tau log2(e) (q.k - delta / (tau log2(e))).
+  // The matrix unit starts each row's accumulator at -delta / (tau log2(e)), so a tile's scores
+  // need only the maximum over the group's rows and one multiply per key.  The start value is
+  // rounded once from double; a start below -1e30 (a vanishing scale: every score then ties) is
+  // clamped, so no finite score overflows.
+  float cinit[4][4];
 #pragma unroll
   for (int rb = 0; rb < 4; rb++) {
     const int qg = rb / HQ, hq = rb % HQ;
@@ -365,9 +372,9 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
           const int j = j0 + jq;
           const double l2 = (double)p.lse[((size_t)b * p.Hq + hbase + hh) * p.Tq + j] * 1.4426950408889634;
           const double Cq = rint((double)p.lse[((size_t)b * p.Hq + u * p.g) * p.Tq + j] * 1.4426950408889634);
-          delta[rb][e] = (float)(l2 - Cq);
+          cinit[rb][e] = (float)fmax(-(l2 - Cq) / (double)p.scale_log2, -1e30);
         } else {
-          delta[rb][e] = INFINITY;  // queries past the last one, padding heads: never score
+          cinit[rb][e] = -INFINITY;  // queries past the last one, padding heads: never score
         }
       }
     }
@@ -544,7 +551,8 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
     for (int kb = 0; kb < 4; kb++) {
       f32x4 acc[4];
 #pragma unroll
-      for (int rb = 0; rb < 4; rb++) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < 4; rb++)
+        acc[rb] = f32x4{cinit[rb][0], cinit[rb][1], cinit[rb][2], cinit[rb][3]};
       if constexpr (!F32) {
         const uint16_t* kt = (const uint16_t*)ktile[buf];
 #pragma unroll
@@ -566,13 +574,14 @@ __global__ __launch_bounds__(kThreads, (F32 || D > 128) ? 1 : 2) void pf_select_
       const int pos = g0 + rn;
 #pragma unroll
       for (int qg = 0; qg < QG; qg++) {
-        float v = -INFINITY;
+        float m = -INFINITY;
 #pragma unroll
         for (int hq = 0; hq < HQ; hq++) {
           const int rb = qg * HQ + hq;
 #pragma unroll
-          for (int e = 0; e < 4; e++) v = fmaxf(v, __builtin_fmaf(acc[rb][e], p.scale_log2, -delta[rb][e]));
+          for (int e = 0; e < 4; e++) m = fmaxf(m, acc[rb][e]);
         }
+        const float v = m * p.scale_log2;
         if constexpr (!BLOCK) {
           // candidates at or above the float filter; appended after the tile's four blocks
           vk[kb][qg] = v;
