@@ -91,6 +91,17 @@ int main() {
   hs_kv_pages pages = {FI, 48, 32, 100};  // not a power of two
   CHECK(hs_full_attn_fwd_paged(&x, F, F, F, &pages, F, FF, nullptr, F, 1 << 30, nullptr) ==
         HS_ERR_INVALID_ARG);
+  // paged selection: prefill shapes on pages of at least 64 positions only
+  hs_kv_pages small = {FI, 32, 128, 256};
+  x = make(1, 512, 4096, 16, 4, 128);
+  CHECK(hs_oracle_topk_paged(&x, F, F, &small, FF, 256, 64, FI, FI, F, 1 << 30, nullptr) ==
+        HS_ERR_UNSUPPORTED);
+  CHECK(hs_block_score_topk_paged(&x, F, F, nullptr, FF, 64, 16, FI, FI, F, 1 << 30, nullptr) ==
+        HS_ERR_INVALID_ARG);
+  hs_kv_pages p64 = {FI, 64, 64, 64};
+  x = make(1, 1, 4096, 16, 4, 128);
+  CHECK(hs_oracle_topk_paged(&x, F, F, &p64, FF, 256, 64, FI, FI, F, 1 << 30, nullptr) ==
+        HS_ERR_UNSUPPORTED);
 
   // valid calls reach their launch, which fails without a GPU; never run with one visible
   int n_dev = 0;
@@ -111,6 +122,10 @@ int main() {
         hs_full_attn_fwd_logits(&y, F, F, F, F, FF, FF, F, big, nullptr);
         hs_sparse_attn_gather_noalloc(&y, F, F, F, HS_IDX_TOKEN, FI, FI, 320, 64, nullptr, F, FF,
                                       nullptr);
+        hs_kv_pages pg = {FI, 64, 47, 200};
+        hs_full_attn_fwd_paged(&y, F, F, F, &pg, F, FF, nullptr, F, big, nullptr);
+        hs_oracle_topk_paged(&y, F, F, &pg, FF, 256, 64, FI, FI, F, big, nullptr);
+        hs_block_score_topk_paged(&y, F, F, &pg, FF, 64, 16, FI, FI, F, big, nullptr);
       }
     std::printf("valid calls exercised without a GPU\n");
   }
