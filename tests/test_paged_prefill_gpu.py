@@ -39,6 +39,12 @@ CASES = [
                              needles=4, seed=703), 256),
     ("mqa64_d256_p64", Workload("ppm", 1, 32, 3000, 64, 1, 256, "bf16", k_global=256,
                                 window=64, needles=4, seed=704), 64),
+    # two chunks of 16 heads and their exact merge; blocks of 32 keys
+    ("g32_d128_p128_blk32", Workload("pp32", 1, 40, 4100, 64, 2, 128, "bf16", k_global=384,
+                                     window=64, block=32, n_blocks=24, needles=6, seed=707), 128),
+    # just past the prefill route's threshold (20 rows per KV head), pages of one tile
+    ("g4_d64_few_queries_p64", Workload("ppf", 3, 5, 1900, 8, 2, 64, "bf16", k_global=200,
+                                        window=16, needles=3, seed=708), 64),
 ]
 
 
