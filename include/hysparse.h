@@ -84,7 +84,8 @@ typedef enum {
   HS_OP_TOPK_FROM_LOGITS = 5,       /* p0 = k_global, p1 = window */
   HS_OP_BLOCK_TOPK_FROM_LOGITS = 6, /* p0 = block, p1 = n_blocks */
   HS_OP_FULL_ATTN_BLOCK_TOPK = 7,   /* p0 = block, p1 = n_blocks */
-  HS_OP_FULL_ATTN_PAGED = 8,        /* p0 = page_size */
+  HS_OP_FULL_ATTN_PAGED = 8,        /* p0 = page_size; p1 = 1 when the call keeps the logits,
+                                       else 0 (a prefill shape without logits needs none) */
   HS_OP_FULL_ATTN_TOPK = 9          /* p0 = k_global, p1 = window */
 } hs_op;
 
@@ -295,8 +296,8 @@ hs_status hs_block_topk_from_logits(const hs_attn_desc* desc, const float* logit
  *     lse (and logits) as the contiguous call on that kernel, bit for bit, except for groups of
  *     32-64 heads, whose contiguous call runs the group kernel: there the logits are identical
  *     and o, lse agree to rounding (other split boundaries).
- * Workspace: hs_workspace_size(HS_OP_FULL_ATTN_PAGED, desc, page_size, 0) (0 on the prefill
- * kernel). */
+ * Workspace: hs_workspace_size(HS_OP_FULL_ATTN_PAGED, desc, page_size, logits != NULL) (0 on
+ * the prefill kernel). */
 hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const void* k_pool,
                                  const void* v_pool, const hs_kv_pages* pages, void* o, float* lse,
                                  float* logits, void* ws, size_t ws_bytes, void* stream);

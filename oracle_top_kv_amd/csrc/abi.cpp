@@ -622,8 +622,8 @@ constexpr int kPagedSelectMinPage = 64;
 
 // Paged full attention of a prefill shape without stored logits runs on the tiled prefill
 // kernel when a page holds whole key tiles; everything else on the row kernel.
-bool paged_prefill_attn(const Shape& s, const float* logits, int page_size) {
-  return !logits && use_prefill_kernel(s) && page_size >= hs::prefill_tile_keys(s.D);
+bool paged_prefill_attn(const Shape& s, bool with_logits, int page_size) {
+  return !with_logits && use_prefill_kernel(s) && page_size >= hs::prefill_tile_keys(s.D);
 }
 
 hs_status check_pages(const Shape& s, const hs_kv_pages* pg) {
@@ -830,9 +830,16 @@ size_t hs_workspace_size(hs_op op, const hs_attn_desc* desc, int32_t p0, int32_t
     }
     case HS_OP_FULL_ATTN_LOGITS: return row_fa_ws(s, 0);
     case HS_OP_FULL_ATTN_PAGED: {
-      if (p0 < 1 || (p0 & (p0 - 1))) return 0;
-      // the size of the row kernel's call, which also covers the logits form of the call
-      return row_fa_ws(s, p0);
+      if (p0 < 1 || (p0 & (p0 - 1))) {
+        fail(HS_ERR_INVALID_ARG, "page_size %d: must be a power of two", p0);
+        return 0;
+      }
+      if (p1 != 0 && p1 != 1) {
+        fail(HS_ERR_INVALID_ARG, "p1 %d: 1 when the call keeps the logits, else 0", p1);
+        return 0;
+      }
+      // the tiled prefill kernel needs none; the row kernel its split partials
+      return paged_prefill_attn(s, p1 == 1, p0) ? 0 : row_fa_ws(s, p0);
     }
     case HS_OP_TOPK_FROM_LOGITS: return tk_ws(s, tl_geom(s));
     case HS_OP_FULL_ATTN_BLOCK_TOPK: return fused_blocks_ws(s, p0, p1);
@@ -978,7 +985,7 @@ hs_status hs_full_attn_fwd_paged(const hs_attn_desc* desc, const void* q, const 
   st = check_pages(s, pages);
   if (st != HS_OK) return st;
   if (logits && (uintptr_t)logits % 4) return fail(HS_ERR_INVALID_ARG, "logits must be 4-byte aligned");
-  if (paged_prefill_attn(s, logits, pages->page_size)) {
+  if (paged_prefill_attn(s, logits != nullptr, pages->page_size)) {
     hs::PrefillParams pp = prefill_params(s, q, k_pool, v_pool, o, lse);
     pp.pages = pages->block_table;
     pp.page_shift = __builtin_ctz((unsigned)pages->page_size);

@@ -211,7 +211,8 @@ def full_attn_fwd_paged(q, k_pool, v_pool, block_table, kv_len, logits=False, q_
     lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=dev)
     lg = (torch.empty((q.shape[0], q.shape[1], q.shape[2], int(kv_len)), dtype=torch.float32,
                       device=dev) if logits else None)
-    ws, n = workspace(HS_OP_FULL_ATTN_PAGED, desc, k_pool.shape[1], device=dev)
+    ws, n = workspace(HS_OP_FULL_ATTN_PAGED, desc, k_pool.shape[1], 1 if logits else 0,
+                      device=dev)
     _check(lib().hs_full_attn_fwd_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                         ctypes.byref(pg), _ptr(o), _ptr(lse), _ptr(lg), _ptr(ws),
                                         n, _stream(dev)), "hs_full_attn_fwd_paged")

@@ -354,3 +354,17 @@ def test_paged_selection_argument_checks(which):
     assert call(prefill, short) == hs.HS_ERR_INVALID_ARG
     npo2 = hs.KvPages(0x1000, 96, 128, 128)
     assert call(prefill, npo2) == hs.HS_ERR_INVALID_ARG
+
+
+def test_paged_full_attention_workspace_by_route():
+    """Paged full attention of a prefill shape without logits runs on the tiled prefill kernel
+    (no workspace); with logits, or on pages smaller than a key tile, on the row kernel (split
+    partials); p1 other than 0 or 1 is refused."""
+    L = hs.lib()
+    d = desc(q_len=4096, kv_len=135168, n_q_heads=64, n_kv_heads=4)
+    assert L.hs_workspace_size(hs.HS_OP_FULL_ATTN_PAGED, ctypes.byref(d), 64, 0) == 0
+    assert L.hs_workspace_size(hs.HS_OP_FULL_ATTN_PAGED, ctypes.byref(d), 64, 1) > 0
+    assert L.hs_workspace_size(hs.HS_OP_FULL_ATTN_PAGED, ctypes.byref(d), 16, 0) > 0
+    assert L.hs_workspace_size(hs.HS_OP_FULL_ATTN_PAGED, ctypes.byref(d), 64, 2) == 0
+    assert "p1" in L.hs_last_error().decode()
+    assert L.hs_workspace_size(hs.HS_OP_FULL_ATTN_PAGED, ctypes.byref(d), 48, 0) == 0
